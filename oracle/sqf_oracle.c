@@ -1,0 +1,534 @@
+/*
+ * sqf_oracle.c -- plain, slow, scalar CPU oracle for the outlier-separated
+ * dual-path GEMM (SQ-format / OSC).
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the parity reference.  Only the
+ * test suite, the smoke check and the benchmark's CPU-baseline leg may load
+ * it.  It shares no code, header, table or constant with the GPU library.
+ *
+ * Sources (cited by page title and section):
+ *   [SQF-art]  SQ-format press article (91haoming.cn), sections numbered
+ *              二 (two selection strategies), 三 (hardware: two paths, mask
+ *              code), 五 (static strategy), 九 (technical details).
+ *   [SQF-abs]  "SQ-format: A Unified Sparse-Quantized Hardware-friendly Data
+ *              Format for LLMs", abstract.
+ *   [OSC-abs]  "OSC: Hardware Efficient W4A4 Quantization via Outlier
+ *              Separation in Channel Dimension", abstract and the section
+ *              on the method framework.
+ *
+ * Everything is written as scalar loops, in the order the method states it.
+ * Floating point: quantisation decisions are taken in fp32 (the precision
+ * the kernels use, so both sides decide integer codes identically); sums
+ * and the final output are formed in fp64.  Build flags:
+ *   -O2 -fno-fast-math -ffp-contract=off -fopenmp
+ *
+ * Conventions where the pages are silent (each is a stated reading):
+ *   - symmetric quantisation to [-Q, Q] with Q = 7 (int4) or 127 (int8);
+ *     the int4 code 0x8 (-8) is never produced by quantisation and is the
+ *     reserved "high precision here" mark of the weight-side format;
+ *   - inv = Q / absmax as one fp32 division, code = clamp(rint(v*inv)),
+ *     scale = absmax / Q as one fp32 division; absmax 0 gives codes 0 and
+ *     scale 0;
+ *   - ties in any ranking go to the lower index;
+ *   - packed int4: slot 2i in the low nibble of byte i, slot 2i+1 in the
+ *     high nibble; rows zero-padded to their leading dimension.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_F32 0
+#define ORC_BF16 1
+#define ORC_FP8 2
+#define ORC_I8 3
+#define ORC_I4 4
+
+/* ------------------------------------------------------------------ */
+/* Number formats                                                      */
+/* ------------------------------------------------------------------ */
+
+static float f32_from_bits(uint32_t b) {
+  float f;
+  memcpy(&f, &b, 4);
+  return f;
+}
+static uint32_t bits_from_f32(float f) {
+  uint32_t b;
+  memcpy(&b, &f, 4);
+  return b;
+}
+
+/* bf16 -> fp32 is exact: the bf16 pattern is the top half of the fp32 one. */
+double orc_bf16_to_double(uint16_t h) { return (double)f32_from_bits((uint32_t)h << 16); }
+
+/* fp32 -> bf16, round to nearest, ties to even mantissa.  Finite inputs. */
+uint16_t orc_bf16_from_float(float v) {
+  uint32_t b = bits_from_f32(v);
+  uint32_t upper = b >> 16, lower = b & 0xFFFFu;
+  if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u))) upper += 1u;
+  return (uint16_t)upper;
+}
+
+/* OCP FP8 E4M3 ("fn" variant): 1 sign, 4 exponent bits (bias 7), 3 mantissa
+ * bits, no infinities, 0x7F / 0xFF are NaN, largest finite 448 (0x7E).  The
+ * value of a non-negative code is computed from that definition. */
+double orc_e4m3_to_double(uint8_t c) {
+  int s = c >> 7, e = (c >> 3) & 0xF, m = c & 7;
+  double v;
+  if (e == 0)
+    v = ldexp((double)m / 8.0, -6); /* subnormal: 0.m * 2^(1-7) */
+  else
+    v = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return s ? -v : v;
+}
+
+/* fp32 -> E4M3, round to nearest with ties to the even code, saturating to
+ * +-448.  Written as a search over every finite non-negative code, which is
+ * the definition of round-to-nearest rather than a bit trick. */
+uint8_t orc_e4m3_from_float(float v) {
+  double a = fabs((double)v);
+  int best = 0;
+  double best_err = a; /* code 0 has value 0 */
+  for (int c = 1; c <= 0x7E; ++c) {
+    double err = fabs(orc_e4m3_to_double((uint8_t)c) - a);
+    if (err < best_err || (err == best_err && (c & 1) == 0 && (best & 1) == 1)) {
+      best = c;
+      best_err = err;
+    }
+  }
+  if (a > 448.0) best = 0x7E; /* saturate */
+  return (uint8_t)(best | ((v < 0.0f && best != 0) ? 0x80 : 0));
+}
+
+/* Signed int4 nibble -> code.  0x8 is the reserved mark; it contributes 0 to
+ * the dense low-precision product [SQF-art section 三: the low part is
+ * consumed by ordinary matrix units, the marked positions by a separate
+ * gather of high-precision values]. */
+static int nib_code(uint8_t nib) {
+  nib &= 0xF;
+  if (nib == 0x8) return 0;
+  return (nib & 0x8) ? (int)nib - 16 : (int)nib;
+}
+
+/* ------------------------------------------------------------------ */
+/* Step: symmetric quantisation of one vector                          */
+/* ------------------------------------------------------------------ */
+
+/* Quantise v[0..len) symmetrically to [-q, q].  Per-token for activations,
+ * per-output-channel for weights.  fmt selects the code type: ORC_I4 / ORC_I8
+ * give integer codes clamp(rint(v*inv)); ORC_FP8 gives E4M3 codes of v*inv
+ * (q = 448).  Returns the scale; codes[i] receives the signed integer code
+ * (int formats) or the raw E4M3 byte (fp8). */
+float orc_quantize_vec(const float* v, int64_t len, int fmt, int32_t* codes) {
+  int q = fmt == ORC_I4 ? 7 : (fmt == ORC_I8 ? 127 : 448);
+  float a = 0.0f;
+  for (int64_t i = 0; i < len; ++i) {
+    float t = fabsf(v[i]);
+    if (t > a) a = t;
+  }
+  if (a == 0.0f) {
+    for (int64_t i = 0; i < len; ++i) codes[i] = 0;
+    return 0.0f;
+  }
+  float inv = (float)q / a;
+  for (int64_t i = 0; i < len; ++i) {
+    float p = v[i] * inv;
+    if (fmt == ORC_FP8) {
+      codes[i] = orc_e4m3_from_float(p);
+    } else {
+      float r = rintf(p);
+      if (r > (float)q) r = (float)q;
+      if (r < (float)-q) r = (float)-q;
+      codes[i] = (int32_t)r;
+    }
+  }
+  return a / (float)q;
+}
+
+/* ------------------------------------------------------------------ */
+/* Step a0: static outlier-channel selection                           */
+/* ------------------------------------------------------------------ */
+
+static const double* g_sort_score;
+static int cmp_rank(const void* pa, const void* pb) {
+  int32_t a = *(const int32_t*)pa, b = *(const int32_t*)pb;
+  double sa = g_sort_score[a], sb = g_sort_score[b];
+  if (sa > sb) return -1;
+  if (sa < sb) return 1;
+  return a < b ? -1 : (a > b ? 1 : 0);
+}
+static int cmp_i32(const void* pa, const void* pb) {
+  int32_t a = *(const int32_t*)pa, b = *(const int32_t*)pb;
+  return a < b ? -1 : (a > b ? 1 : 0);
+}
+
+/* Channel importance from calibration data [SQF-art sections 二 and 五: mean
+ * activation per channel weighted by the channel's contribution through the
+ * weights; chosen offline so no online top-k is needed] and [OSC-abs: outlier
+ * channels identified offline, token-persistent].
+ *   score_c = (sum_m |x[m,c]| / m_cal) * sqrt(sum_n W[c,n]^2)
+ * sums in fp64 in index order.  hdiag_c = (float) sum_m x[m,c]^2 (the
+ * diagonal of X^T X, used by the weight-side score).  The k_out best channels
+ * (score descending, lower index first on ties) are the outliers; idx lists
+ * them ascending; map[c] = low slot j >= 0, or -(t+1) for outlier slot t.
+ * score / hdiag may be NULL. */
+void orc_select_channels(const float* x_cal, int64_t m_cal, int64_t k, const float* w, int64_t n,
+                         int64_t k_out, int32_t* idx, int32_t* map, double* score_out,
+                         float* hdiag_out) {
+  double* score = (double*)malloc(sizeof(double) * (size_t)(k > 0 ? k : 1));
+  for (int64_t c = 0; c < k; ++c) {
+    double sa = 0.0, s2 = 0.0, sw = 0.0;
+    for (int64_t m = 0; m < m_cal; ++m) {
+      double x = (double)x_cal[m * k + c];
+      sa += fabs(x);
+      s2 += x * x;
+    }
+    for (int64_t j = 0; j < n; ++j) {
+      double t = (double)w[c * n + j];
+      sw += t * t;
+    }
+    double mean_abs = sa / (double)m_cal;
+    score[c] = mean_abs * sqrt(sw);
+    if (score_out) score_out[c] = score[c];
+    if (hdiag_out) hdiag_out[c] = (float)s2;
+  }
+  int32_t* order = (int32_t*)malloc(sizeof(int32_t) * (size_t)(k > 0 ? k : 1));
+  for (int64_t c = 0; c < k; ++c) order[c] = (int32_t)c;
+  g_sort_score = score;
+  qsort(order, (size_t)k, sizeof(int32_t), cmp_rank);
+  for (int64_t t = 0; t < k_out; ++t) idx[t] = order[t];
+  qsort(idx, (size_t)k_out, sizeof(int32_t), cmp_i32);
+  for (int64_t c = 0; c < k; ++c) map[c] = 0;
+  for (int64_t t = 0; t < k_out; ++t) map[idx[t]] = (int32_t)(-(t + 1));
+  int32_t j = 0;
+  for (int64_t c = 0; c < k; ++c)
+    if (map[c] >= 0) map[c] = j++;
+  free(order);
+  free(score);
+}
+
+/* ------------------------------------------------------------------ */
+/* Packing helpers                                                     */
+/* ------------------------------------------------------------------ */
+
+static void pack_i4_row(const int32_t* codes, int64_t len, uint8_t* row, int64_t ldk) {
+  memset(row, 0, (size_t)ldk);
+  for (int64_t j = 0; j < len; ++j) {
+    uint8_t nib = (uint8_t)(codes[j] & 0xF);
+    if (j & 1)
+      row[j >> 1] |= (uint8_t)(nib << 4);
+    else
+      row[j >> 1] |= nib;
+  }
+}
+
+/* Store one branch vector (the outlier slots of a row) in the branch format. */
+static float store_branch_row(const float* vals, int64_t k_out, int fmt, void* dst_row,
+                              int64_t ldo, int32_t* tmp) {
+  float scale = 1.0f;
+  if (fmt == ORC_BF16) {
+    uint16_t* d = (uint16_t*)dst_row;
+    for (int64_t t = 0; t < ldo; ++t) d[t] = t < k_out ? orc_bf16_from_float(vals[t]) : 0;
+    return scale;
+  }
+  scale = orc_quantize_vec(vals, k_out, fmt, tmp);
+  uint8_t* d = (uint8_t*)dst_row;
+  for (int64_t t = 0; t < ldo; ++t) d[t] = t < k_out ? (uint8_t)(tmp[t] & 0xFF) : 0;
+  return scale;
+}
+
+/* ------------------------------------------------------------------ */
+/* Step a1: weight format (outlier-channel split, OSC-style)          */
+/* ------------------------------------------------------------------ */
+
+/* For every output channel nn: the values W[c, nn] of the low channels, in
+ * slot order, are quantised per output channel to int4 and packed
+ * (w_low[nn][ldk]); the outlier-channel values form the branch row
+ * w_out[nn][ldo] in bf16 (no scale), FP8 or int8 (scale s_wo[nn]).
+ * [OSC-abs: low-precision 4-bit path plus a high-precision branch over the
+ * outlier channels.] */
+void orc_pack_weights(const float* w, int64_t k, int64_t n, const int32_t* map, int64_t k_low,
+                      int64_t k_out, int64_t ldk, int64_t ldo, int branch_fmt, uint8_t* w_low,
+                      float* s_w, void* w_out, float* s_wo) {
+  float* lo = (float*)malloc(sizeof(float) * (size_t)(k_low + 1));
+  float* hi = (float*)malloc(sizeof(float) * (size_t)(k_out + 1));
+  int32_t* codes = (int32_t*)malloc(sizeof(int32_t) * (size_t)(k + 1));
+  size_t esz = branch_fmt == ORC_BF16 ? 2 : 1;
+  for (int64_t nn = 0; nn < n; ++nn) {
+    for (int64_t c = 0; c < k; ++c) {
+      int32_t s = map[c];
+      float v = w[c * n + nn];
+      if (s >= 0)
+        lo[s] = v;
+      else
+        hi[-s - 1] = v;
+    }
+    s_w[nn] = orc_quantize_vec(lo, k_low, ORC_I4, codes);
+    pack_i4_row(codes, k_low, w_low + nn * ldk, ldk);
+    if (ldo > 0) {
+      float sc = store_branch_row(hi, k_out, branch_fmt, (uint8_t*)w_out + (size_t)nn * ldo * esz,
+                                  ldo, codes);
+      if (s_wo) s_wo[nn] = sc;
+    } else if (s_wo) {
+      s_wo[nn] = 0.0f;
+    }
+  }
+  free(codes);
+  free(hi);
+  free(lo);
+}
+
+/* ------------------------------------------------------------------ */
+/* Step a1 (weight-side SQ-format): int4 with a reserved mask code     */
+/* ------------------------------------------------------------------ */
+
+/* Weight-side SQ-format for one output channel, generic in the low bit
+ * width (bits = 2 or 4).  [SQF-art section 九: the format is a quantised
+ * dense matrix, a sparse high-precision matrix and a mask; symmetric
+ * quantisation leaves the largest unsigned code unused and that code marks
+ * the high-precision positions; the positions are the top fraction of each
+ * bank by an importance score built from the weight and the Hessian
+ * diagonal.]  The bank is the whole row here.
+ *   key_j = w_j^2 * hdiag_j in fp64 (orders exactly like |w_j| * sqrt(hdiag_j))
+ * The nnz largest keys (lower slot first on ties) are kept at high
+ * precision: int8 per-row quantisation of those values in ascending slot
+ * order -> v8[0..nnz), scale *s8.  The remaining slots are quantised to
+ * [-(2^(bits-1)-1), 2^(bits-1)-1] with their own scale *s_low; the kept
+ * slots receive the reserved code 2^(bits-1) (as an unsigned field).
+ * codes_out[j] holds the unsigned field value of slot j. */
+void orc_sq_row(const float* wrow, const float* hdiag, int64_t k_low, int64_t nnz, int bits,
+                uint8_t* codes_out, int8_t* v8, float* s8, float* s_low) {
+  double* key = (double*)malloc(sizeof(double) * (size_t)(k_low + 1));
+  int32_t* order = (int32_t*)malloc(sizeof(int32_t) * (size_t)(k_low + 1));
+  uint8_t* keep = (uint8_t*)calloc((size_t)(k_low + 1), 1);
+  float* tmp = (float*)malloc(sizeof(float) * (size_t)(k_low + 1));
+  int32_t* codes = (int32_t*)malloc(sizeof(int32_t) * (size_t)(k_low + 1));
+  for (int64_t j = 0; j < k_low; ++j) {
+    double wj = (double)wrow[j];
+    key[j] = wj * wj * (double)hdiag[j];
+    order[j] = (int32_t)j;
+  }
+  g_sort_score = key;
+  qsort(order, (size_t)k_low, sizeof(int32_t), cmp_rank);
+  for (int64_t i = 0; i < nnz; ++i) keep[order[i]] = 1;
+  /* high-precision values, ascending slot order */
+  int64_t c = 0;
+  for (int64_t j = 0; j < k_low; ++j)
+    if (keep[j]) tmp[c++] = wrow[j];
+  *s8 = orc_quantize_vec(tmp, nnz, ORC_I8, codes);
+  for (int64_t i = 0; i < nnz; ++i) v8[i] = (int8_t)codes[i];
+  /* low-precision part over the remaining slots */
+  int q = (1 << (bits - 1)) - 1;
+  float a = 0.0f;
+  for (int64_t j = 0; j < k_low; ++j)
+    if (!keep[j] && fabsf(wrow[j]) > a) a = fabsf(wrow[j]);
+  float inv = a == 0.0f ? 0.0f : (float)q / a;
+  *s_low = a == 0.0f ? 0.0f : a / (float)q;
+  uint32_t field_mask = (1u << bits) - 1u;
+  for (int64_t j = 0; j < k_low; ++j) {
+    if (keep[j]) {
+      codes_out[j] = (uint8_t)(1u << (bits - 1)); /* reserved mark */
+    } else {
+      int32_t cq = 0;
+      if (a != 0.0f) {
+        float r = rintf(wrow[j] * inv);
+        if (r > (float)q) r = (float)q;
+        if (r < (float)-q) r = (float)-q;
+        cq = (int32_t)r;
+      }
+      codes_out[j] = (uint8_t)((uint32_t)cq & field_mask);
+    }
+  }
+  free(codes);
+  free(tmp);
+  free(keep);
+  free(order);
+  free(key);
+}
+
+/* Weight-side SQ-format for a whole weight matrix with a static outlier
+ * channel split on the activation side: low slots -> int4 codes with the
+ * reserved mark + int8 sparse values (sq_val[nn][nnz], scale s_w8); outlier
+ * channels -> int8 branch rows w_out[nn][ldo] with scale s_wo. */
+void orc_pack_weights_sq(const float* w, int64_t k, int64_t n, const int32_t* map,
+                         const float* hdiag_k, int64_t k_low, int64_t k_out, int64_t ldk,
+                         int64_t ldo, int64_t nnz, uint8_t* w_low, float* s_w4, int8_t* sq_val,
+                         float* s_w8, int8_t* w_out, float* s_wo) {
+  float* lo = (float*)malloc(sizeof(float) * (size_t)(k_low + 1));
+  float* hlo = (float*)malloc(sizeof(float) * (size_t)(k_low + 1));
+  float* hi = (float*)malloc(sizeof(float) * (size_t)(k_out + 1));
+  uint8_t* fields = (uint8_t*)malloc((size_t)(k_low + 1));
+  int32_t* codes = (int32_t*)malloc(sizeof(int32_t) * (size_t)(k + 1));
+  for (int64_t c = 0; c < k; ++c)
+    if (map[c] >= 0) hlo[map[c]] = hdiag_k[c];
+  for (int64_t nn = 0; nn < n; ++nn) {
+    for (int64_t c = 0; c < k; ++c) {
+      int32_t s = map[c];
+      float v = w[c * n + nn];
+      if (s >= 0)
+        lo[s] = v;
+      else
+        hi[-s - 1] = v;
+    }
+    orc_sq_row(lo, hlo, k_low, nnz, 4, fields, sq_val + nn * nnz, &s_w8[nn], &s_w4[nn]);
+    uint8_t* row = w_low + nn * ldk;
+    memset(row, 0, (size_t)ldk);
+    for (int64_t j = 0; j < k_low; ++j)
+      row[j >> 1] |= (uint8_t)((j & 1) ? (fields[j] << 4) : fields[j]);
+    if (ldo > 0) {
+      s_wo[nn] = store_branch_row(hi, k_out, ORC_I8, (uint8_t*)w_out + nn * ldo, ldo, codes);
+    } else {
+      s_wo[nn] = 0.0f;
+    }
+  }
+  free(codes);
+  free(fields);
+  free(hi);
+  free(hlo);
+  free(lo);
+}
+
+/* ------------------------------------------------------------------ */
+/* Step a2: per-token quantisation and outlier extraction             */
+/* ------------------------------------------------------------------ */
+
+/* For every token m: the low channels (slot order) are quantised per token to
+ * int4 (low_fmt ORC_I4, packed, ldk bytes per row) or int8 (ORC_I8, one byte
+ * per slot); the outlier channels are gathered into the compact dense
+ * branch row x_out[m][ldo] (bf16, or FP8 / int8 with a per-token scale).
+ * [OSC-abs: structured sub-tensor extraction gathers the scattered outlier
+ * channels online into a compact dense tensor.]  x is fp32 (x_fmt ORC_F32)
+ * or bf16 bit patterns (ORC_BF16), row stride ldx elements. */
+void orc_quantize_split_act(const void* x, int x_fmt, int64_t m, int64_t k, int64_t ldx,
+                            const int32_t* map, int64_t k_low, int64_t k_out, int64_t ldk,
+                            int64_t ldo, int low_fmt, int branch_fmt, uint8_t* x_low, float* s_x,
+                            void* x_out, float* s_xo) {
+  float* row = (float*)malloc(sizeof(float) * (size_t)(k + 1));
+  float* lo = (float*)malloc(sizeof(float) * (size_t)(k_low + 1));
+  float* hi = (float*)malloc(sizeof(float) * (size_t)(k_out + 1));
+  int32_t* codes = (int32_t*)malloc(sizeof(int32_t) * (size_t)(k + 1));
+  size_t esz = branch_fmt == ORC_BF16 ? 2 : 1;
+  for (int64_t mm = 0; mm < m; ++mm) {
+    for (int64_t c = 0; c < k; ++c) {
+      if (x_fmt == ORC_BF16)
+        row[c] = (float)orc_bf16_to_double(((const uint16_t*)x)[mm * ldx + c]);
+      else
+        row[c] = ((const float*)x)[mm * ldx + c];
+    }
+    for (int64_t c = 0; c < k; ++c) {
+      if (map[c] >= 0)
+        lo[map[c]] = row[c];
+      else
+        hi[-map[c] - 1] = row[c];
+    }
+    s_x[mm] = orc_quantize_vec(lo, k_low, low_fmt, codes);
+    uint8_t* dst = x_low + mm * ldk;
+    if (low_fmt == ORC_I4) {
+      pack_i4_row(codes, k_low, dst, ldk);
+    } else {
+      memset(dst, 0, (size_t)ldk);
+      for (int64_t j = 0; j < k_low; ++j) dst[j] = (uint8_t)(codes[j] & 0xFF);
+    }
+    if (ldo > 0) {
+      float sc = store_branch_row(hi, k_out, branch_fmt, (uint8_t*)x_out + (size_t)mm * ldo * esz,
+                                  ldo, codes);
+      if (s_xo) s_xo[mm] = sc;
+    } else if (s_xo) {
+      s_xo[mm] = 0.0f;
+    }
+  }
+  free(codes);
+  free(hi);
+  free(lo);
+  free(row);
+}
+
+/* ------------------------------------------------------------------ */
+/* Steps a3-a5 (and the weight-side masked path): the dual GEMM        */
+/* ------------------------------------------------------------------ */
+
+static double branch_val(const void* base, int64_t ld, int64_t r, int64_t t, int fmt) {
+  if (fmt == ORC_BF16) return orc_bf16_to_double(((const uint16_t*)base)[r * ld + t]);
+  uint8_t b = ((const uint8_t*)base)[r * ld + t];
+  if (fmt == ORC_FP8) return orc_e4m3_to_double(b);
+  return (double)(int8_t)b;
+}
+
+/* Decoded low code of slot j of a packed (int4) or byte (int8) row. */
+static int low_code(const uint8_t* row, int64_t j, int fmt) {
+  if (fmt == ORC_I8) return (int)(int8_t)row[j];
+  uint8_t b = row[j >> 1];
+  return nib_code((j & 1) ? (uint8_t)(b >> 4) : b);
+}
+
+/* y[r][nn] for the token rows listed in rows[0..nr) (row r of the outputs is
+ * token rows[r]) and every output channel nn < n:
+ *   acc_low = sum_j qx[j] * qw[j]            (exact integer, mark -> 0)
+ *   acc_sp  = sum_i qx[pos_i] * v8[i]         (weight-side format only; pos_i
+ *                                              = i-th marked slot of the row)
+ *   acc_o   = sum_t xo[t] * wo[t]             (branch; integer for int8,
+ *                                              fp64 for bf16 / FP8)
+ *   y = s_x*s_w*acc_low [+ s_x*s_w8*acc_sp] + (s_xo*s_wo)*acc_o
+ * formed in fp64 and rounded once to fp32.  [SQF-art section 三: two parallel
+ * paths whose results are summed; OSC method framework: result fusion.]
+ * x_low_fmt: ORC_I4 (packed) or ORC_I8.  branch_fmt: ORC_BF16 / ORC_FP8 /
+ * ORC_I8 (the bf16 branch has no scales).  sq_nnz > 0 selects the
+ * weight-side format (w_low holds marks, sq_val/s_w8 the sparse values).
+ * Debug accumulators (NULL to skip) are int64 [nr][n]; acc_o is only filled
+ * for an int8 branch. */
+void orc_dual_gemm(int64_t n, int64_t k_low, int64_t k_out, const int64_t* rows, int64_t nr,
+                   const uint8_t* x_low, int64_t ldk_x, int x_low_fmt, const float* s_x,
+                   const void* x_out, int64_t ldo, int branch_fmt, const float* s_xo,
+                   const uint8_t* w_low, int64_t ldk_w, const float* s_w, const void* w_out,
+                   const float* s_wo, int64_t sq_nnz, const int8_t* sq_val, const float* s_w8,
+                   float* y, int64_t ldy, int64_t* acc_low_dbg, int64_t* acc_sp_dbg,
+                   int64_t* acc_o_dbg) {
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int64_t r = 0; r < nr; ++r) {
+    for (int64_t nn = 0; nn < n; ++nn) {
+      int64_t mm = rows[r];
+      const uint8_t* xr = x_low + mm * ldk_x;
+      const uint8_t* wr = w_low + nn * ldk_w;
+      int64_t acc = 0, acc_sp = 0, acc_o_i = 0;
+      double acc_o = 0.0;
+      int64_t i_sp = 0;
+      for (int64_t j = 0; j < k_low; ++j) {
+        int qx = low_code(xr, j, x_low_fmt);
+        if (sq_nnz > 0) {
+          uint8_t b = wr[j >> 1];
+          uint8_t nib = (uint8_t)(((j & 1) ? (b >> 4) : b) & 0xF);
+          if (nib == 0x8) {
+            acc_sp += (int64_t)qx * (int64_t)sq_val[nn * sq_nnz + i_sp];
+            ++i_sp;
+            continue;
+          }
+        }
+        acc += (int64_t)qx * (int64_t)low_code(wr, j, ORC_I4);
+      }
+      for (int64_t t = 0; t < k_out; ++t) {
+        if (branch_fmt == ORC_I8) {
+          acc_o_i += (int64_t)(int8_t)((const uint8_t*)x_out)[mm * ldo + t] *
+                     (int64_t)(int8_t)((const uint8_t*)w_out)[nn * ldo + t];
+        } else {
+          acc_o += branch_val(x_out, ldo, mm, t, branch_fmt) *
+                   branch_val(w_out, ldo, nn, t, branch_fmt);
+        }
+      }
+      double br;
+      if (branch_fmt == ORC_BF16)
+        br = acc_o;
+      else if (branch_fmt == ORC_FP8)
+        br = ((double)s_xo[mm] * (double)s_wo[nn]) * acc_o;
+      else
+        br = ((double)s_xo[mm] * (double)s_wo[nn]) * (double)acc_o_i;
+      if (k_out == 0) br = 0.0;
+      double low = (double)s_x[mm] * (double)s_w[nn] * (double)acc;
+      if (sq_nnz > 0) low += (double)s_x[mm] * (double)s_w8[nn] * (double)acc_sp;
+      y[r * ldy + nn] = (float)(low + br);
+      if (acc_low_dbg) acc_low_dbg[r * n + nn] = acc;
+      if (acc_sp_dbg) acc_sp_dbg[r * n + nn] = acc_sp;
+      if (acc_o_dbg) acc_o_dbg[r * n + nn] = acc_o_i;
+    }
+  }
+}
