@@ -35,7 +35,7 @@ F32, BF16, FP8, I8, I4 = 0, 1, 2, 3, 4
 _FMT = {"f32": F32, "bf16": BF16, "fp8": FP8, "i8": I8, "i4": I4}
 
 K_ALIGN_LOW = 256  # low slots are padded to a multiple of this
-K_ALIGN_OUT = 64  # branch slots are padded to a multiple of this
+K_ALIGN_OUT_BYTES = 128  # branch rows are padded to a multiple of 128 bytes
 
 
 def build(force: bool = True) -> str:
@@ -101,8 +101,9 @@ def pad_k_low(k_low: int) -> int:
     return -(-k_low // K_ALIGN_LOW) * K_ALIGN_LOW
 
 
-def pad_k_out(k_out: int) -> int:
-    return -(-k_out // K_ALIGN_OUT) * K_ALIGN_OUT
+def pad_k_out(k_out: int, branch: str = "bf16") -> int:
+    step = K_ALIGN_OUT_BYTES // (2 if branch == "bf16" else 1)
+    return -(-k_out // step) * step
 
 
 # ---------------------------------------------------------------- formats
@@ -155,7 +156,7 @@ def pack_weights(w: np.ndarray, mp: np.ndarray, branch: str = "bf16"):
     k_out = int((mp < 0).sum())
     k_low = k - k_out
     ldk = pad_k_low(k_low) // 2
-    ldo = pad_k_out(k_out)
+    ldo = pad_k_out(k_out, branch)
     w_low = np.zeros((n, max(ldk, 1)), dtype=np.uint8)[:, :ldk].copy()
     s_w = np.zeros(n, dtype=np.float32)
     w_out = np.zeros((n, ldo), dtype=_branch_dtype(branch))
@@ -189,7 +190,7 @@ def pack_weights_sq(w: np.ndarray, mp: np.ndarray, hdiag: np.ndarray, nnz: int):
     k_out = int((mp < 0).sum())
     k_low = k - k_out
     ldk = pad_k_low(k_low) // 2
-    ldo = pad_k_out(k_out)
+    ldo = pad_k_out(k_out, "i8")
     w_low = np.zeros((n, ldk), dtype=np.uint8)
     s_w4 = np.zeros(n, dtype=np.float32)
     sq_val = np.zeros((n, max(nnz, 1)), dtype=np.int8)
@@ -216,7 +217,7 @@ def quantize_split_act(x: np.ndarray, mp: np.ndarray, low: str = "i4", branch: s
     k_out = int((mp < 0).sum())
     k_low = k - k_out
     ldk = pad_k_low(k_low) // (2 if low == "i4" else 1)
-    ldo = pad_k_out(k_out)
+    ldo = pad_k_out(k_out, branch)
     x_low = np.zeros((m, ldk), dtype=np.uint8)
     s_x = np.zeros(m, dtype=np.float32)
     x_out = np.zeros((m, ldo), dtype=_branch_dtype(branch))

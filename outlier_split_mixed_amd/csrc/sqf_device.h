@@ -1,0 +1,90 @@
+// sqf_device.h -- device helpers shared by the gfx950 kernels of libsqf.
+//
+// Number-format conversions are written from the formats' definitions:
+//   bf16: the top 16 bits of an fp32 pattern, rounded to nearest-even.
+//   E4M3 (OCP): 1 sign, 4 exponent bits with bias 7, 3 mantissa bits, largest
+//   finite 448, no infinities.  A value is rounded by scaling it with the
+//   power-of-two quantum of its binade and rounding half to even.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sqf {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+// Status codes mirrored from the public header (kept in sync by the host code).
+enum : int { kBF16 = 1, kFP8 = 2, kI8 = 3, kI4X2 = 4, kF32 = 0 };
+
+__device__ __forceinline__ uint32_t f32_bits(float f) { return __float_as_uint(f); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  uint32_t b = __float_as_uint(f);
+  uint32_t lsb = (b >> 16) & 1u;
+  return (b + 0x7FFFu + lsb) >> 16;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// fp32 -> OCP E4M3 byte, nearest-even, saturating to +-448.  A value that
+// rounds to zero gives +0 (0x00) whatever its sign.
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float v) {
+  float a = fabsf(v);
+  uint32_t code;
+  if (a >= 464.0f) {
+    code = 0x7E;  // beyond the midpoint to the (absent) next value: saturate
+  } else {
+    int e = (int)((__float_as_uint(a) >> 23) & 0xFF) - 127;  // binade of a (a > 0)
+    if (a < 0.015625f) {  // below 2^-6: subnormal quantum 2^-9
+      code = (uint32_t)rintf(a * 512.0f);  // 0..8; 8 encodes 2^-6 exactly
+    } else {
+      // quantum 2^(e-3); q in [8, 16]; q == 16 carries into the next binade
+      float q = rintf(a * __uint_as_float((uint32_t)(127 + 3 - e) << 23));
+      code = (uint32_t)((e + 7) << 3) + ((uint32_t)q - 8u);
+    }
+    if (code > 0x7E) code = 0x7E;
+  }
+  if (code != 0 && v < 0.0f) code |= 0x80u;
+  return code;
+}
+
+// Wave-wide max of a non-negative float (order independent, exact).
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// Inclusive prefix sum across the wave (Hillis-Steele over shuffles).
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    int t = __shfl_up(v, off, kWave);
+    if (lane >= off) v += t;
+  }
+  return v;
+}
+
+// Symmetric quantisation helpers: inv = q / a (IEEE fp32 division), code =
+// clamp(rint(v * inv), -q, q).  a == 0 -> inv = 0 -> every code 0.
+__device__ __forceinline__ float quant_inv(float a, float q) { return a == 0.0f ? 0.0f : q / a; }
+__device__ __forceinline__ float quant_scale(float a, float q) { return a == 0.0f ? 0.0f : a / q; }
+__device__ __forceinline__ int quant_code(float v, float inv, float q) {
+  float r = rintf(v * inv);
+  r = fminf(fmaxf(r, -q), q);
+  return (int)r;
+}
+
+}  // namespace sqf

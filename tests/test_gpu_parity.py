@@ -1,0 +1,233 @@
+"""GPU parity at small and ragged sizes: every stage of the HIP path, called
+through the C ABI, against the CPU oracle on the same seeded inputs.
+
+Bit-exact: outlier set, channel map, fp64 scores, hdiag, packed int4 bytes,
+fp32 scale patterns, branch codes, int32 low-path accumulators.  Tolerance:
+per row, max |y_gpu - y_oracle| <= 1e-3 * max |y_oracle|.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from outlier_split_mixed_amd import synth
+
+from harness import assert_rows_close, f32_bits_equal, run_layer, x_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sqf():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    from outlier_split_mixed_amd import sqf as mod
+
+    return mod
+
+
+def _ragged(m=300, k=1000, n=520, n_scaled=37, seed=77, factor="loguniform"):
+    return synth.draw_layer("ragged", seed, 0, m, k, n, 128, n_scaled, factor=factor)
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+def test_tiny_fp32_input(sqf):
+    lay = synth.tiny()
+    st, _ = run_layer(sqf, lay, lay.k_out, x_dtype="f32")
+    _print("tiny", st)
+
+
+@pytest.mark.parametrize("tile", ["0", "1", "2"])
+def test_ragged_every_tile_config(sqf, tile):
+    """M, N and K_low are not multiples of any tile; K_out is not a multiple of 64."""
+    lay = _ragged()
+    os.environ["SQF_GEMM_TILE"] = tile
+    try:
+        st, _ = run_layer(sqf, lay, lay.k_out)
+    finally:
+        del os.environ["SQF_GEMM_TILE"]
+    _print("ragged tile", tile, st)
+
+
+@pytest.mark.parametrize("branch", ["bf16", "fp8"])
+def test_ragged_branch_types(sqf, branch):
+    lay = _ragged(m=257, k=1536, n=384, n_scaled=96, seed=78)
+    st, _ = run_layer(sqf, lay, lay.k_out, branch=branch)
+    _print("branch", branch, st)
+
+
+def test_no_outliers_is_w4a4(sqf):
+    lay = _ragged(m=130, k=512, n=200, n_scaled=0, seed=79, factor=1.0)
+    st, _ = run_layer(sqf, lay, 0)
+    _print("k_out=0", st)
+
+
+@pytest.mark.parametrize("branch", ["bf16", "fp8"])
+def test_all_outliers_is_branch_gemm(sqf, branch):
+    lay = _ragged(m=96, k=256, n=136, n_scaled=16, seed=80)
+    st, _ = run_layer(sqf, lay, lay.k, branch=branch)
+    _print("k_out=k", branch, st)
+
+
+def test_outlier_fraction_one_half(sqf):
+    lay = _ragged(m=200, k=2048, n=256, n_scaled=128, seed=81)
+    st, _ = run_layer(sqf, lay, 1024)
+    _print("f=1/2", st)
+
+
+def test_zero_token_rows_and_single_row(sqf):
+    lay = _ragged(m=65, k=512, n=96, n_scaled=32, seed=82)
+    lay.x[5] = 0.0  # every channel zero: scale 0, codes 0
+    lay.x[9, :] = 0.0
+    lay.x[9, lay.scaled] = 3.0  # low channels zero, outliers non-zero
+    st, _ = run_layer(sqf, lay, lay.k_out)
+    one = synth.draw_layer("one", 83, 0, 1, 512, 64, 64, 32)
+    run_layer(sqf, one, one.k_out)
+
+
+def test_m_zero_is_a_no_op(sqf):
+    acts = sqf.alloc_acts(0, 480, 32)
+    w = sqf.alloc_weights(512, 64, 32)
+    x = torch.zeros((0, 512), dtype=torch.bfloat16, device="cuda")
+    mp = torch.zeros(512, dtype=torch.int32, device="cuda")
+    sqf.sqf_quantize_split_act(x, mp, acts)
+    y = sqf.sqf_dual_gemm(acts, w)
+    assert y.shape == (0, 64)
+
+
+def test_deterministic_and_canary(sqf):
+    """Two runs are bitwise equal; bytes past every output's extent are untouched."""
+    lay = _ragged(m=190, k=768, n=200, n_scaled=48, seed=84)
+    x_cal = torch.from_numpy(lay.x_cal).cuda()
+    w = torch.from_numpy(lay.w).cuda()
+    idx, mp, _, _ = sqf.sqf_select_channels(x_cal, w, lay.k_out)
+    wts = sqf.sqf_pack_weights(w, mp)
+    _, _, xt = x_inputs(lay, "bf16")
+    acts = sqf.alloc_acts(lay.m, lay.k - lay.k_out, lay.k_out)
+    canary = 0x5A
+    # y with a wider leading dimension: the columns past n must stay untouched
+    ldy = lay.n + 24
+    ys = []
+    for _ in range(2):
+        big = torch.full((lay.m + 3, ldy), float("nan"), device="cuda")
+        sqf.sqf_quantize_split_act(xt, mp, acts)
+        y = big[: lay.m]
+        sqf.sqf_dual_gemm(acts, wts, y=y)
+        torch.cuda.synchronize()
+        b = big.cpu().numpy()
+        assert np.isnan(b[:, lay.n:]).all() and np.isnan(b[lay.m:]).all()
+        ys.append(b[: lay.m, : lay.n].copy())
+    assert np.array_equal(ys[0].view(np.uint32), ys[1].view(np.uint32))
+    # activation buffers carved from a larger canary-filled allocation
+    ldk, ldo = acts.ldk, acts.ldo
+    raw = torch.full((lay.m * ldk + 4096,), canary, dtype=torch.uint8, device="cuda")
+    acts.t["x_low"] = raw[: lay.m * ldk].view(lay.m, ldk)
+    sqf.sqf_quantize_split_act(xt, mp, acts)
+    torch.cuda.synchronize()
+    assert (raw[lay.m * ldk:].cpu().numpy() == canary).all()
+
+
+def test_sq_weight_side_small(sqf):
+    """Weight-side SQ-format: int8 activations, int4 weights with reserved
+    marks, int8 sparse values, int8 branch; three exact accumulators."""
+    lay = _ragged(m=140, k=1280, n=300, n_scaled=80, seed=85)
+    k_out = lay.k_out
+    k_low = lay.k - k_out
+    nnz = k_low // 8
+    x_cal = torch.from_numpy(lay.x_cal).cuda()
+    w = torch.from_numpy(lay.w).cuda()
+    idx, mp, score, hdiag = sqf.sqf_select_channels(x_cal, w, k_out)
+    wts = sqf.sqf_pack_weights(w, mp, branch="i8", hdiag=hdiag, sq_nnz=nnz)
+    ox, ofmt, xt = x_inputs(lay, "bf16")
+    acts = sqf.alloc_acts(lay.m, k_low, k_out, low="i8", branch="i8")
+    sqf.sqf_quantize_split_act(xt, mp, acts)
+    y, al, asp, ao = sqf.sqf_dual_gemm(acts, wts, debug=True)
+    torch.cuda.synchronize()
+    o_idx, o_mp, _, o_hd = oracle.select_channels(lay.x_cal, lay.w, k_out)
+    assert np.array_equal(mp.cpu().numpy(), o_mp)
+    o_w = oracle.pack_weights_sq(lay.w, o_mp, o_hd, nnz)
+    assert np.array_equal(wts.t["w_low"][0].cpu().numpy(), o_w["w_low"])
+    assert np.array_equal(wts.t["sq_val"].cpu().numpy(), o_w["sq_val"])
+    assert f32_bits_equal(wts.t["s_w"][0].cpu().numpy(), o_w["s_w"])
+    assert f32_bits_equal(wts.t["s_w8"].cpu().numpy(), o_w["s_w8"])
+    assert np.array_equal(wts.t["w_out"][0].cpu().numpy().view(np.int8), o_w["w_out"])
+    assert f32_bits_equal(wts.t["s_wo"][0].cpu().numpy(), o_w["s_wo"])
+    # tile offsets: marks before each 256-slot tile, from the oracle's bytes
+    nib = np.stack([o_w["w_low"] & 0xF, o_w["w_low"] >> 4], -1).reshape(lay.n, -1)
+    marks = np.concatenate([np.zeros((lay.n, 1), np.int64), np.cumsum(nib == 8, 1)], 1)
+    want = marks[:, ::256]
+    assert np.array_equal(wts.t["sq_tile_off"].cpu().numpy(), want)
+    o_a = oracle.quantize_split_act(ox, o_mp, low="i8", branch="i8", x_fmt=ofmt)
+    assert np.array_equal(acts.t["x_low"].cpu().numpy(), o_a["x_low"])
+    assert np.array_equal(acts.t["x_out"].cpu().numpy(), o_a["x_out"])
+    assert f32_bits_equal(acts.t["s_x"].cpu().numpy(), o_a["s_x"])
+    assert f32_bits_equal(acts.t["s_xo"].cpu().numpy(), o_a["s_xo"])
+    o_y, o_al, o_asp, o_ao = oracle.dual_gemm(o_a, o_w, debug=True)
+    assert np.array_equal(al.cpu().numpy().astype(np.int64), o_al)
+    assert np.array_equal(asp.cpu().numpy().astype(np.int64), o_asp)
+    assert np.array_equal(ao.cpu().numpy().astype(np.int64), o_ao)
+    assert_rows_close(y.cpu().numpy(), o_y, "sq small")
+
+
+def _moe_small(experts=6, tokens=96, topk=2, hidden=512, inter=256, seed=86):
+    return synth.qwen3_moe(seed=seed, experts=experts, tokens=tokens, topk=topk, hidden=hidden,
+                           inter=inter, cal_rows=64)
+
+
+@pytest.mark.parametrize("branch", ["bf16", "fp8"])
+def test_grouped_small_with_empty_group(sqf, branch):
+    moe = _moe_small()
+    lays = moe.up
+    # force one empty expert group
+    lays[2] = synth.Layer(name="empty", m=0, k=lays[2].k, n=lays[2].n, k_out=lays[2].k_out,
+                          x=lays[2].x[:0], x_cal=lays[2].x_cal, w=lays[2].w,
+                          scaled=lays[2].scaled)
+    _grouped_check(sqf, lays, branch)
+
+
+def _grouped_check(sqf, lays, branch, rows_per_group=None):
+    g = len(lays)
+    k, n, k_out = lays[0].k, lays[0].n, lays[0].k_out
+    counts = [l.m for l in lays]
+    off = np.zeros(g + 1, np.int64)
+    off[1:] = np.cumsum(counts)
+    maps, wst = [], []
+    for l in lays:
+        idx, mp, _, _ = sqf.sqf_select_channels(torch.from_numpy(l.x_cal).cuda(),
+                                                torch.from_numpy(l.w).cuda(), k_out)
+        maps.append(mp)
+    maps_t = torch.stack(maps)
+    w_all = torch.from_numpy(np.stack([l.w for l in lays])).cuda()
+    wts = sqf.sqf_pack_weights(w_all, maps_t, branch=branch)
+    x = np.concatenate([l.x for l in lays])
+    bits = synth.to_bf16_bits(x)
+    xt = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+    row_off = torch.from_numpy(off).cuda()
+    acts = sqf.alloc_acts(int(off[-1]), k - k_out, k_out, branch=branch)
+    sqf.sqf_quantize_split_act_grouped(xt, row_off, maps_t, acts)
+    y, acc = sqf.sqf_dual_gemm_grouped(acts, wts, row_off, debug=True)
+    torch.cuda.synchronize()
+    yg, ag = y.cpu().numpy(), acc.cpu().numpy().astype(np.int64)
+    xl, xo = acts.t["x_low"].cpu().numpy(), acts.t["x_out"].cpu().numpy()
+    for e, l in enumerate(lays):
+        o_idx, o_mp, _, _ = oracle.select_channels(l.x_cal, l.w, k_out)
+        assert np.array_equal(maps_t[e].cpu().numpy(), o_mp)
+        o_w = oracle.pack_weights(l.w, o_mp, branch=branch)
+        assert np.array_equal(wts.t["w_low"][e].cpu().numpy(), o_w["w_low"])
+        if l.m == 0:
+            continue
+        r0, r1 = off[e], off[e + 1]
+        o_a = oracle.quantize_split_act(bits[r0:r1], o_mp, branch=branch, x_fmt="bf16")
+        assert np.array_equal(xl[r0:r1], o_a["x_low"])
+        assert np.array_equal(xo[r0:r1].view(o_a["x_out"].dtype), o_a["x_out"])
+        rows = None if rows_per_group is None else np.unique(
+            np.linspace(0, l.m - 1, min(rows_per_group, l.m)).astype(np.int64))
+        o_y, o_acc, _, _ = oracle.dual_gemm(o_a, o_w, rows=rows, debug=True)
+        sel = np.arange(l.m) if rows is None else rows
+        assert np.array_equal(ag[r0:r1][sel], o_acc), f"expert {e} accumulators"
+        assert_rows_close(yg[r0:r1][sel], o_y, f"expert {e}")
