@@ -88,6 +88,8 @@ def _declare(lib):
     lib.orc_e4m3_from_float.restype = ctypes.c_uint8
     lib.orc_e4m3_to_double.argtypes = [ctypes.c_uint8]
     lib.orc_e4m3_to_double.restype = ctypes.c_double
+    lib.orc_num_threads.argtypes = []
+    lib.orc_num_threads.restype = ctypes.c_int
 
 
 def _p(a):
@@ -104,6 +106,11 @@ def pad_k_low(k_low: int) -> int:
 def pad_k_out(k_out: int, branch: str = "bf16") -> int:
     step = K_ALIGN_OUT_BYTES // (2 if branch == "bf16" else 1)
     return -(-k_out // step) * step
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_load().orc_num_threads())
 
 
 # ---------------------------------------------------------------- formats

@@ -34,6 +34,7 @@
  *     high nibble; rows zero-padded to their leading dimension.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -532,3 +533,6 @@ void orc_dual_gemm(int64_t n, int64_t k_low, int64_t k_out, const int64_t* rows,
     }
   }
 }
+
+/* Threads the OpenMP loops above use (reported with CPU timings). */
+int orc_num_threads(void) { return omp_get_max_threads(); }

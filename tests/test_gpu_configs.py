@@ -1,0 +1,126 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times.  Every stage before the GEMM is compared in full (bit-exact);
+the GEMM's int32 accumulators and fp32 outputs are compared on a sample of
+token rows (first, last and random rows, all output channels), which the
+oracle computes one by one.
+
+Workloads (seeded, synthetic):
+* tiny: M=64, K=N=256, fp32 input, 16 outliers.
+* Llama-3-8B-shaped prefill linears: M=2048; 4096->4096, 4096->14336, 14336->4096.
+* Llama-3-70B-shaped prefill linears: M=4096; 8192->8192, 8192->28672,
+  28672->8192 at outlier fraction 1/16; fractions 1/2, 1/4, 1/8 as well on
+  the 8192->8192 shape.
+* Qwen3-30B-A3B-shaped expert GEMMs: 128 experts, 8192 tokens routed top-8,
+  2048->768 (up) and 768->2048 (down); bf16 branch, E4M3 branch on the down
+  projection at 1/16 and with every channel in the branch.
+* Weight-side SQ-format on 4096->14336, M=2048.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from outlier_split_mixed_amd import synth
+
+from harness import assert_rows_close, f32_bits_equal, run_layer, sample_rows, x_inputs
+from test_gpu_parity import _grouped_check
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sqf():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    from outlier_split_mixed_amd import sqf as mod
+
+    return mod
+
+
+def _log(*a):
+    print(*a, flush=True)
+
+
+@pytest.mark.parametrize("layer", [0, 1, 2])
+def test_llama3_8b_layers(sqf, layer):
+    lay = synth.llama3_8b(layer)
+    st, _ = run_layer(sqf, lay, lay.k_out, rows=sample_rows(lay.m, 12, seed=layer))
+    _log(lay.name, st)
+
+
+@pytest.mark.parametrize("layer", [0, 1, 2])
+def test_llama3_70b_layers_f16(sqf, layer):
+    lay = synth.llama3_70b(layer, 16)
+    st, _ = run_layer(sqf, lay, lay.k_out, rows=sample_rows(lay.m, 8, seed=10 + layer))
+    _log(lay.name, "1/16", st)
+
+
+@pytest.mark.parametrize("frac", [2, 4, 8])
+def test_llama3_70b_fraction_sweep(sqf, frac):
+    lay = synth.llama3_70b(0, frac)
+    st, _ = run_layer(sqf, lay, lay.k_out, rows=sample_rows(lay.m, 8, seed=20 + frac))
+    _log(lay.name, f"1/{frac}", st)
+
+
+@pytest.fixture(scope="module")
+def moe():
+    return synth.qwen3_moe()
+
+
+def test_moe_up_bf16(sqf, moe):
+    _grouped_check(sqf, moe.up, "bf16", rows_per_group=3)
+    _log("moe up bf16 ok")
+
+
+def test_moe_down_bf16(sqf, moe):
+    _grouped_check(sqf, moe.down, "bf16", rows_per_group=3)
+    _log("moe down bf16 ok")
+
+
+def test_moe_down_fp8(sqf, moe):
+    _grouped_check(sqf, moe.down, "fp8", rows_per_group=3)
+    _log("moe down fp8 ok")
+
+
+def test_moe_down_fp8_every_channel(sqf, moe):
+    """The literal whole-input FP8 fallback: every channel in the E4M3 branch."""
+    lays = []
+    for l in moe.down[:16]:
+        l2 = synth.Layer(name=l.name, m=l.m, k=l.k, n=l.n, k_out=l.k, x=l.x, x_cal=l.x_cal,
+                         w=l.w, scaled=l.scaled)
+        lays.append(l2)
+    _grouped_check(sqf, lays, "fp8", rows_per_group=3)
+    _log("moe down fp8 f=1 ok")
+
+
+def test_sq_weight_side_full(sqf):
+    lay = synth.sq_weight()
+    k_out = lay.k_out
+    k_low = lay.k - k_out
+    nnz = k_low // 8
+    x_cal = torch.from_numpy(lay.x_cal).cuda()
+    w = torch.from_numpy(lay.w).cuda()
+    idx, mp, score, hdiag = sqf.sqf_select_channels(x_cal, w, k_out)
+    wts = sqf.sqf_pack_weights(w, mp, branch="i8", hdiag=hdiag, sq_nnz=nnz)
+    ox, ofmt, xt = x_inputs(lay, "bf16")
+    acts = sqf.alloc_acts(lay.m, k_low, k_out, low="i8", branch="i8")
+    sqf.sqf_quantize_split_act(xt, mp, acts)
+    y, al, asp, ao = sqf.sqf_dual_gemm(acts, wts, debug=True)
+    torch.cuda.synchronize()
+    o_idx, o_mp, _, o_hd = oracle.select_channels(lay.x_cal, lay.w, k_out)
+    assert np.array_equal(mp.cpu().numpy(), o_mp)
+    assert f32_bits_equal(hdiag.cpu().numpy(), o_hd)
+    o_w = oracle.pack_weights_sq(lay.w, o_mp, o_hd, nnz)
+    assert np.array_equal(wts.t["w_low"][0].cpu().numpy(), o_w["w_low"])
+    assert np.array_equal(wts.t["sq_val"].cpu().numpy(), o_w["sq_val"])
+    assert f32_bits_equal(wts.t["s_w8"].cpu().numpy(), o_w["s_w8"])
+    o_a = oracle.quantize_split_act(ox, o_mp, low="i8", branch="i8", x_fmt=ofmt)
+    assert np.array_equal(acts.t["x_low"].cpu().numpy(), o_a["x_low"])
+    assert np.array_equal(acts.t["x_out"].cpu().numpy(), o_a["x_out"])
+    rows = sample_rows(lay.m, 8, seed=40)
+    o_y, o_al, o_asp, o_ao = oracle.dual_gemm(o_a, o_w, rows=rows, debug=True)
+    assert np.array_equal(al.cpu().numpy()[rows].astype(np.int64), o_al)
+    assert np.array_equal(asp.cpu().numpy()[rows].astype(np.int64), o_asp)
+    assert np.array_equal(ao.cpu().numpy()[rows].astype(np.int64), o_ao)
+    assert_rows_close(y.cpu().numpy()[rows], o_y, "sq full")
+    _log("sq full ok")
