@@ -48,58 +48,61 @@ __device__ __forceinline__ void unpack_i4x32(const uint4 q, v4i& lo, v4i& hi) {
   hi[3] = (int)(q.w & 0xF0F0F0F0u);
 }
 
-template <int BM, int BN, int NT>
-struct StageLoader {
-  static constexpr int PIECES = (BM + BN) * 8;  // 16-byte pieces per stage
-  static constexpr int L = PIECES / NT;
-  static_assert(PIECES % NT == 0, "pieces must divide evenly");
-  static_assert((BM * 8) % NT == 0, "A/B split must fall on a load boundary");
-  static constexpr int LA = BM * 8 / NT;
-  uint32_t off[L];   // byte offset of the piece inside its operand (stage 0)
-  int lds_idx[L];    // fragment-order LDS index (uint4 units)
+// Direct global -> LDS loader.  One stage of a tile is (BM + BN) rows x 128
+// bytes = (BM + BN) / 8 fragments of 1 KiB; fragment (rowblock rb, half f)
+// holds, for lane l, the 16 bytes at row rb*16 + l%16, byte f*64 + (l/16)*16
+// of the stage.  One global_load_lds_dwordx4 fills one fragment: lane l's
+// 16 bytes land at LDS base + 16*l, which is exactly fragment order.  Each
+// wave owns PW consecutive fragments; PW divides the A fragment count, so a
+// wave loads either A rows or B rows only.
+template <int BM, int BN, int NW>
+struct DmaLoader {
+  static constexpr int FRAGS = (BM + BN) / 8;
+  static constexpr int PW = FRAGS / NW;
+  static constexpr int AFR = BM / 8;
+  static_assert(FRAGS % NW == 0 && AFR % PW == 0, "fragments must split evenly over waves");
+  uint32_t off[PW];
+  bool is_a;
+  int q0;
 
-  __device__ __forceinline__ void init(int tid, int64_t a_row0, int64_t a_rows_end, int64_t b_row0,
-                                       int64_t b_rows_end, int64_t ld) {
+  __device__ __forceinline__ void init(int wave, int lane, int64_t a_row0, int64_t a_end,
+                                       int64_t b_row0, int64_t b_end, int64_t ld) {
+    q0 = wave * PW;
+    is_a = q0 < AFR;
 #pragma unroll
-    for (int i = 0; i < L; ++i) {
-      int e = tid + i * NT;
-      int r = e >> 3, p = e & 7;
-      int64_t grow;
-      int rr;
-      if (i < LA) {
-        rr = r;
-        grow = a_row0 + rr;
-        if (grow > a_rows_end - 1) grow = a_rows_end - 1;
-      } else {
-        rr = r - BM;
-        grow = b_row0 + rr;
-        if (grow > b_rows_end - 1) grow = b_rows_end - 1;
-      }
-      off[i] = (uint32_t)(grow * ld + p * 16);
-      lds_idx[i] = (i < LA ? 0 : BM * 8) + (((rr >> 4) * 2 + (p >> 2)) * 64 + (p & 3) * 16 + (rr & 15));
+    for (int i = 0; i < PW; ++i) {
+      const int q = q0 + i;
+      const int ql = is_a ? q : q - AFR;
+      const int r = (ql >> 1) * 16 + (lane & 15);
+      int64_t grow = (is_a ? a_row0 : b_row0) + r;
+      const int64_t lim = (is_a ? a_end : b_end) - 1;
+      if (grow > lim) grow = lim;
+      off[i] = (uint32_t)(grow * ld + (ql & 1) * 64 + (lane >> 4) * 16);
     }
   }
-  __device__ __forceinline__ void load(uint4 (&buf)[L], const uint8_t* a, const uint8_t* b,
-                                       uint32_t stage_off) const {
+  __device__ __forceinline__ void issue(const uint8_t* a, const uint8_t* b, uint32_t stage_off,
+                                        uint8_t* lds_stage) const {
+    const uint8_t* base = is_a ? a : b;
 #pragma unroll
-    for (int i = 0; i < L; ++i) {
-      const uint8_t* base = i < LA ? a : b;
-      buf[i] = *(const uint4*)(base + off[i] + stage_off);
+    for (int i = 0; i < PW; ++i) {
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(base + off[i] + stage_off),
+          (__attribute__((address_space(3))) void*)(lds_stage + (q0 + i) * 1024), 16, 0, 0);
     }
-  }
-  __device__ __forceinline__ void store(const uint4 (&buf)[L], uint4* lds) const {
-#pragma unroll
-    for (int i = 0; i < L; ++i) lds[lds_idx[i]] = buf[i];
   }
 };
 
+// Wait until this wave's outstanding global (and LDS-DMA) loads have landed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 template <int BM, int BN, int WGM, int WGN, int BR, bool GROUPED, bool DEBUG, int GROUP_M>
 __global__ __launch_bounds__(WGM* WGN * 64) void k_dual_gemm(GemmArgs p) {
-  constexpr int NT = WGM * WGN * 64;
+  constexpr int NW = WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 16, TN = WN / 16;
+  constexpr int STAGE = (BM + BN) * 128;
   static_assert(TM >= 1 && TN >= 1, "wave tile too small");
-  __shared__ uint4 smem[2][(BM + BN) * 8];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
@@ -153,8 +156,7 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_dual_gemm(GemmArgs p) {
   const int64_t m0 = m_begin + tm * BM;
   const int64_t n0 = tn * BN;
 
-  StageLoader<BM, BN, NT> ld;
-  uint4 pre[StageLoader<BM, BN, NT>::L];
+  DmaLoader<BM, BN, NW> ld;
 
   v4i acc[TM][TN];
 #pragma unroll
@@ -164,33 +166,35 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_dual_gemm(GemmArgs p) {
 
   // ---------------- low path: int4 x int4 on int8 MFMA ----------------
   if (p.s_low > 0) {
-    ld.init(tid, m0, m_end, n0, p.n, p.ldk);
-    ld.load(pre, p.x_low, w_low, 0);
-    ld.store(pre, smem[0]);
-    __syncthreads();
+    ld.init(wave, lane, m0, m_end, n0, p.n, p.ldk);
+    ld.issue(p.x_low, w_low, 0, smem);
     for (int s = 0; s < p.s_low; ++s) {
-      const int b = s & 1;
-      if (s + 1 < p.s_low) ld.load(pre, p.x_low, w_low, (uint32_t)(s + 1) * 128u);
-      const uint4* As = smem[b];
-      const uint4* Bs = smem[b] + BM * 8;
+      wait_vmem();
+      __syncthreads();  // stage s landed everywhere; stage s-1's buffer is free
+      if (s + 1 < p.s_low) ld.issue(p.x_low, w_low, (uint32_t)(s + 1) * 128u, smem + ((s + 1) & 1) * STAGE);
+      const v4i* As = (const v4i*)(smem + (s & 1) * STAGE);
+      const v4i* Bs = As + BM * 8;
 #pragma unroll
       for (int f = 0; f < 2; ++f) {
         v4i b0[TN], b1[TN];
 #pragma unroll
-        for (int j = 0; j < TN; ++j) unpack_i4x32(Bs[((wn * TN + j) * 2 + f) * 64 + lane], b0[j], b1[j]);
+        for (int j = 0; j < TN; ++j) {
+          const v4i q = Bs[((wn * TN + j) * 2 + f) * 64 + lane];
+          unpack_i4x32(make_uint4(q[0], q[1], q[2], q[3]), b0[j], b1[j]);
+        }
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
           v4i a0, a1;
-          unpack_i4x32(As[((wm * TM + i) * 2 + f) * 64 + lane], a0, a1);
+          const v4i q = As[((wm * TM + i) * 2 + f) * 64 + lane];
+          unpack_i4x32(make_uint4(q[0], q[1], q[2], q[3]), a0, a1);
 #pragma unroll
-          for (int j = 0; j < TN; ++j) {
+          for (int j = 0; j < TN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1[j], acc[i][j], 0, 0, 0);
-          }
         }
       }
-      if (s + 1 < p.s_low) ld.store(pre, smem[b ^ 1]);
-      __syncthreads();
     }
   }
 
@@ -238,23 +242,23 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_dual_gemm(GemmArgs p) {
       for (int j = 0; j < TN; ++j) c2[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
   }
   if (p.s_out > 0) {
-    ld.init(tid, m0, m_end, n0, p.n, p.ldo_b);
-    ld.load(pre, p.x_out, w_out, 0);
-    ld.store(pre, smem[0]);
-    __syncthreads();
+    __syncthreads();  // every wave is done with the low path's last buffer
+    ld.init(wave, lane, m0, m_end, n0, p.n, p.ldo_b);
+    ld.issue(p.x_out, w_out, 0, smem);
     for (int s = 0; s < p.s_out; ++s) {
-      const int b = s & 1;
-      if (s + 1 < p.s_out) ld.load(pre, p.x_out, w_out, (uint32_t)(s + 1) * 128u);
-      const uint4* As = smem[b];
-      const uint4* Bs = smem[b] + BM * 8;
+      wait_vmem();
+      __syncthreads();
+      if (s + 1 < p.s_out) ld.issue(p.x_out, w_out, (uint32_t)(s + 1) * 128u, smem + ((s + 1) & 1) * STAGE);
+      const v4i* As = (const v4i*)(smem + (s & 1) * STAGE);
+      const v4i* Bs = As + BM * 8;
 #pragma unroll
       for (int f = 0; f < 2; ++f) {
-        uint4 bq[TN];
+        v4i bq[TN];
 #pragma unroll
         for (int j = 0; j < TN; ++j) bq[j] = Bs[((wn * TN + j) * 2 + f) * 64 + lane];
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-          uint4 aq = As[((wm * TM + i) * 2 + f) * 64 + lane];
+          const v4i aq = As[((wm * TM + i) * 2 + f) * 64 + lane];
 #pragma unroll
           for (int j = 0; j < TN; ++j) {
             if constexpr (BR == kBF16) {
@@ -262,18 +266,16 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_dual_gemm(GemmArgs p) {
                                                                 __builtin_bit_cast(v8bf, bq[j]),
                                                                 c[i][j], 0, 0, 0);
             } else {
-              long a_lo = (long)(((uint64_t)aq.y << 32) | aq.x);
-              long a_hi = (long)(((uint64_t)aq.w << 32) | aq.z);
-              long b_lo = (long)(((uint64_t)bq[j].y << 32) | bq[j].x);
-              long b_hi = (long)(((uint64_t)bq[j].w << 32) | bq[j].z);
+              long a_lo = (long)(((uint64_t)(uint32_t)aq[1] << 32) | (uint32_t)aq[0]);
+              long a_hi = (long)(((uint64_t)(uint32_t)aq[3] << 32) | (uint32_t)aq[2]);
+              long b_lo = (long)(((uint64_t)(uint32_t)bq[j][1] << 32) | (uint32_t)bq[j][0]);
+              long b_hi = (long)(((uint64_t)(uint32_t)bq[j][3] << 32) | (uint32_t)bq[j][2]);
               c2[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a_lo, b_lo, c2[i][j], 0, 0, 0);
               c2[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a_hi, b_hi, c2[i][j], 0, 0, 0);
             }
           }
         }
       }
-      if (s + 1 < p.s_out) ld.store(pre, smem[b ^ 1]);
-      __syncthreads();
     }
   }
 
