@@ -48,43 +48,42 @@ __device__ __forceinline__ void unpack_i4x32(const uint4 q, v4i& lo, v4i& hi) {
   hi[3] = (int)(q.w & 0xF0F0F0F0u);
 }
 
-// Direct global -> LDS loader.  One stage of a tile is (BM + BN) rows x 128
-// bytes = (BM + BN) / 8 fragments of 1 KiB; fragment (rowblock rb, half f)
-// holds, for lane l, the 16 bytes at row rb*16 + l%16, byte f*64 + (l/16)*16
-// of the stage.  One global_load_lds_dwordx4 fills one fragment: lane l's
-// 16 bytes land at LDS base + 16*l, which is exactly fragment order.  Each
-// wave owns PW consecutive fragments; PW divides the A fragment count, so a
-// wave loads either A rows or B rows only.
+// Direct global -> LDS loader.  One stage of a tile is (BM + BN) rows x 64
+// bytes (128 int4 slots, or 32 bf16, or 64 E4M3) = (BM + BN) / 16 fragments
+// of 1 KiB; fragment rb holds, for lane l, the 16 bytes at row rb*16 + l%16,
+// byte (l/16)*16 of the stage.  One global_load_lds_dwordx4 fills one
+// fragment: lane l's 16 bytes land at LDS base + 16*l, which is exactly the
+// order the MFMA operands are read back in.  Each wave owns PW consecutive
+// fragments (A rows first, then B rows).
 template <int BM, int BN, int NW>
 struct DmaLoader {
-  static constexpr int FRAGS = (BM + BN) / 8;
+  static constexpr int FRAGS = (BM + BN) / 16;
   static constexpr int PW = FRAGS / NW;
-  static constexpr int AFR = BM / 8;
-  static_assert(FRAGS % NW == 0 && AFR % PW == 0, "fragments must split evenly over waves");
+  static constexpr int AFR = BM / 16;
+  static_assert(FRAGS % NW == 0, "fragments must split evenly over waves");
   uint32_t off[PW];
-  bool is_a;
   int q0;
 
   __device__ __forceinline__ void init(int wave, int lane, int64_t a_row0, int64_t a_end,
                                        int64_t b_row0, int64_t b_end, int64_t ld) {
     q0 = wave * PW;
-    is_a = q0 < AFR;
 #pragma unroll
     for (int i = 0; i < PW; ++i) {
-      const int q = q0 + i;
+      const int q = q0 + i;  // wave-uniform: A fragment if q < AFR
+      const bool is_a = q < AFR;
       const int ql = is_a ? q : q - AFR;
-      const int r = (ql >> 1) * 16 + (lane & 15);
+      const int r = ql * 16 + (lane & 15);
       int64_t grow = (is_a ? a_row0 : b_row0) + r;
       const int64_t lim = (is_a ? a_end : b_end) - 1;
       if (grow > lim) grow = lim;
-      off[i] = (uint32_t)(grow * ld + (ql & 1) * 64 + (lane >> 4) * 16);
+      off[i] = (uint32_t)(grow * ld + (lane >> 4) * 16);
     }
   }
   __device__ __forceinline__ void issue(const uint8_t* a, const uint8_t* b, uint32_t stage_off,
                                         uint8_t* lds_stage) const {
-    const uint8_t* base = is_a ? a : b;
 #pragma unroll
     for (int i = 0; i < PW; ++i) {
+      const uint8_t* base = (q0 + i) < AFR ? a : b;
       __builtin_amdgcn_global_load_lds(
           (const __attribute__((address_space(1))) void*)(base + off[i] + stage_off),
           (__attribute__((address_space(3))) void*)(lds_stage + (q0 + i) * 1024), 16, 0, 0);
@@ -92,17 +91,53 @@ struct DmaLoader {
   }
 };
 
-// Wait until this wave's outstanding global (and LDS-DMA) loads have landed.
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt bits [3:0] and [15:14]; expcnt and
+// lgkmcnt left at their maximum, i.e. not waited on).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 
-template <int BM, int BN, int WGM, int WGN, int BR, bool GROUPED, bool DEBUG, int GROUP_M>
-__global__ __launch_bounds__(WGM* WGN * 64) void k_dual_gemm(GemmArgs p) {
+// Workgroup barrier that does not drain outstanding loads.  __syncthreads()
+// carries a workgroup fence, and the fence makes the compiler wait for every
+// outstanding LDS-DMA load (they count as LDS writes), which would cap the
+// ring at one stage in flight.  Here the caller has already waited for the
+// stage it needs (vmcnt), every LDS read of the previous stage has been
+// consumed by an MFMA (so it has completed), and the empty asm statements
+// keep the compiler from moving LDS accesses across the barrier.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Ring of NB stage buffers: at the top of step s the stages s .. s+NB-2 have
+// been issued; wait for stage s (the newer ones may stay in flight), barrier,
+// then refill the buffer freed by step s-1 with stage s+NB-1.
+template <int NB, int PW>
+__device__ __forceinline__ void ring_wait(int s, int S) {
+  static_assert(NB >= 2 && NB <= 4, "ring depth");
+  const int ahead = (S - 1 - s) < (NB - 2) ? (S - 1 - s) : (NB - 2);
+  if (NB >= 4 && ahead >= 2) wait_vmcnt<2 * PW>();
+  else if (NB >= 3 && ahead >= 1) wait_vmcnt<PW>();
+  else wait_vmcnt<0>();
+  stage_barrier();
+}
+
+// NB: stage ring depth.  OCC: blocks meant to share a CU (sets the register
+// budget so that OCC * WGM * WGN waves fit: 2 waves per SIMD either way).
+template <int BM, int BN, int WGM, int WGN, int NB, int OCC, int BR, bool GROUPED, bool DEBUG,
+          int GROUP_M>
+__global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_dual_gemm(GemmArgs p) {
   constexpr int NW = WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 16, TN = WN / 16;
-  constexpr int STAGE = (BM + BN) * 128;
+  constexpr int STAGE = (BM + BN) * 64;      // bytes per stage buffer
+  constexpr int PW = DmaLoader<BM, BN, NW>::PW;
   static_assert(TM >= 1 && TN >= 1, "wave tile too small");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+  static_assert(NB * STAGE * OCC <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NB * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
@@ -165,35 +200,35 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_dual_gemm(GemmArgs p) {
     for (int j = 0; j < TN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
   // ---------------- low path: int4 x int4 on int8 MFMA ----------------
-  if (p.s_low > 0) {
+  const int S = p.s_low;
+  if (S > 0) {
     ld.init(wave, lane, m0, m_end, n0, p.n, p.ldk);
-    ld.issue(p.x_low, w_low, 0, smem);
-    for (int s = 0; s < p.s_low; ++s) {
-      wait_vmem();
-      __syncthreads();  // stage s landed everywhere; stage s-1's buffer is free
-      if (s + 1 < p.s_low) ld.issue(p.x_low, w_low, (uint32_t)(s + 1) * 128u, smem + ((s + 1) & 1) * STAGE);
-      const v4i* As = (const v4i*)(smem + (s & 1) * STAGE);
-      const v4i* Bs = As + BM * 8;
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        v4i b0[TN], b1[TN];
+    for (int t = 0; t < NB - 1; ++t)
+      if (t < S) ld.issue(p.x_low, w_low, (uint32_t)t * 64u, smem + t * STAGE);
+    for (int s = 0; s < S; ++s) {
+      ring_wait<NB, PW>(s, S);
+      if (s + NB - 1 < S)
+        ld.issue(p.x_low, w_low, (uint32_t)(s + NB - 1) * 64u, smem + ((s + NB - 1) % NB) * STAGE);
+      const v4i* As = (const v4i*)(smem + (s % NB) * STAGE);
+      const v4i* Bs = As + BM * 4;
+      v4i b0[TN], b1[TN];
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const v4i q = Bs[((wn * TN + j) * 2 + f) * 64 + lane];
-          unpack_i4x32(make_uint4(q[0], q[1], q[2], q[3]), b0[j], b1[j]);
-        }
+      for (int j = 0; j < TN; ++j) {
+        const v4i q = Bs[(wn * TN + j) * 64 + lane];
+        unpack_i4x32(make_uint4(q[0], q[1], q[2], q[3]), b0[j], b1[j]);
+      }
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          v4i a0, a1;
-          const v4i q = As[((wm * TM + i) * 2 + f) * 64 + lane];
-          unpack_i4x32(make_uint4(q[0], q[1], q[2], q[3]), a0, a1);
+      for (int i = 0; i < TM; ++i) {
+        v4i a0, a1;
+        const v4i q = As[(wm * TM + i) * 64 + lane];
+        unpack_i4x32(make_uint4(q[0], q[1], q[2], q[3]), a0, a1);
 #pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0[j], acc[i][j], 0, 0, 0);
 #pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1[j], acc[i][j], 0, 0, 0);
-        }
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1[j], acc[i][j], 0, 0, 0);
       }
     }
   }
@@ -241,38 +276,43 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_dual_gemm(GemmArgs p) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) c2[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
   }
-  if (p.s_out > 0) {
-    __syncthreads();  // every wave is done with the low path's last buffer
+  const int SO = p.s_out;
+  if (SO > 0) {
+    __syncthreads();  // every wave is done with the low path's buffers
     ld.init(wave, lane, m0, m_end, n0, p.n, p.ldo_b);
-    ld.issue(p.x_out, w_out, 0, smem);
-    for (int s = 0; s < p.s_out; ++s) {
-      wait_vmem();
-      __syncthreads();
-      if (s + 1 < p.s_out) ld.issue(p.x_out, w_out, (uint32_t)(s + 1) * 128u, smem + ((s + 1) & 1) * STAGE);
-      const v4i* As = (const v4i*)(smem + (s & 1) * STAGE);
-      const v4i* Bs = As + BM * 8;
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        v4i bq[TN];
+    for (int t = 0; t < NB - 1; ++t)
+      if (t < SO) ld.issue(p.x_out, w_out, (uint32_t)t * 64u, smem + t * STAGE);
+    for (int s = 0; s < SO; ++s) {
+      ring_wait<NB, PW>(s, SO);
+      if (s + NB - 1 < SO)
+        ld.issue(p.x_out, w_out, (uint32_t)(s + NB - 1) * 64u, smem + ((s + NB - 1) % NB) * STAGE);
+      const v4i* As = (const v4i*)(smem + (s % NB) * STAGE);
+      const v4i* Bs = As + BM * 4;
+      v4i bq[TN];
 #pragma unroll
-        for (int j = 0; j < TN; ++j) bq[j] = Bs[((wn * TN + j) * 2 + f) * 64 + lane];
+      for (int j = 0; j < TN; ++j) bq[j] = Bs[(wn * TN + j) * 64 + lane];
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          const v4i aq = As[((wm * TM + i) * 2 + f) * 64 + lane];
+      for (int i = 0; i < TM; ++i) {
+        const v4i aq = As[(wm * TM + i) * 64 + lane];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          if constexpr (BR == kBF16) {
+            c[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, aq),
+                                                              __builtin_bit_cast(v8bf, bq[j]),
+                                                              c[i][j], 0, 0, 0);
+          } else {
+            long a_lo = (long)(((uint64_t)(uint32_t)aq[1] << 32) | (uint32_t)aq[0]);
+            long b_lo = (long)(((uint64_t)(uint32_t)bq[j][1] << 32) | (uint32_t)bq[j][0]);
+            c2[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a_lo, b_lo, c2[i][j], 0, 0, 0);
+          }
+        }
+        if constexpr (BR == kFP8) {
 #pragma unroll
           for (int j = 0; j < TN; ++j) {
-            if constexpr (BR == kBF16) {
-              c[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, aq),
-                                                                __builtin_bit_cast(v8bf, bq[j]),
-                                                                c[i][j], 0, 0, 0);
-            } else {
-              long a_lo = (long)(((uint64_t)(uint32_t)aq[1] << 32) | (uint32_t)aq[0]);
-              long a_hi = (long)(((uint64_t)(uint32_t)aq[3] << 32) | (uint32_t)aq[2]);
-              long b_lo = (long)(((uint64_t)(uint32_t)bq[j][1] << 32) | (uint32_t)bq[j][0]);
-              long b_hi = (long)(((uint64_t)(uint32_t)bq[j][3] << 32) | (uint32_t)bq[j][2]);
-              c2[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a_lo, b_lo, c2[i][j], 0, 0, 0);
-              c2[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a_hi, b_hi, c2[i][j], 0, 0, 0);
-            }
+            long a_hi = (long)(((uint64_t)(uint32_t)aq[3] << 32) | (uint32_t)aq[2]);
+            long b_hi = (long)(((uint64_t)(uint32_t)bq[j][3] << 32) | (uint32_t)bq[j][2]);
+            c2[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a_hi, b_hi, c2[i][j], 0, 0, 0);
           }
         }
       }
@@ -305,7 +345,7 @@ __global__ __launch_bounds__(WGM* WGN * 64) void k_dual_gemm(GemmArgs p) {
 }
 
 // ------------------------------------------------------------------ launch
-template <int BM, int BN, int WGM, int WGN, int BR, bool GROUPED, bool DEBUG>
+template <int BM, int BN, int WGM, int WGN, int NB, int OCC, int BR, bool GROUPED, bool DEBUG>
 static hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   int64_t tiles_n = (a.n + BN - 1) / BN;
   int64_t blocks;
@@ -314,7 +354,7 @@ static hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   else
     blocks = ((a.m + BM - 1) / BM) * tiles_n;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((k_dual_gemm<BM, BN, WGM, WGN, BR, GROUPED, DEBUG, 8>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((k_dual_gemm<BM, BN, WGM, WGN, NB, OCC, BR, GROUPED, DEBUG, 8>), dim3((unsigned)blocks),
                      dim3(WGM * WGN * 64), 0, s, a);
   return hipGetLastError();
 }
@@ -325,16 +365,20 @@ static hipError_t launch_br(const GemmArgs& a, int cfg, hipStream_t s) {
   if (BR == kFP8 && cfg == 0) cfg = 1;
   switch (cfg) {
     case 0:
-      if constexpr (BR != kFP8) return launch_cfg<256, 256, 2, 4, BR, GROUPED, DEBUG>(a, s);
+      if constexpr (BR != kFP8) return launch_cfg<256, 256, 2, 4, 4, 1, BR, GROUPED, DEBUG>(a, s);
       [[fallthrough]];
     case 1:
-      return launch_cfg<128, 128, 2, 2, BR, GROUPED, DEBUG>(a, s);
+      return launch_cfg<128, 128, 2, 2, 4, 2, BR, GROUPED, DEBUG>(a, s);
+    case 3:
+      if constexpr (BR != kFP8) return launch_cfg<256, 128, 2, 2, 3, 2, BR, GROUPED, DEBUG>(a, s);
+      return launch_cfg<128, 128, 2, 2, 4, 2, BR, GROUPED, DEBUG>(a, s);
     default:
-      return launch_cfg<64, 64, 2, 2, BR, GROUPED, DEBUG>(a, s);
+      return launch_cfg<64, 64, 2, 2, 4, 2, BR, GROUPED, DEBUG>(a, s);
   }
 }
 
-// cfg: 0 = 256x256 (8 waves), 1 = 128x128 (4 waves), 2 = 64x64 (4 waves).
+// cfg: 0 = 256x256 (8 waves), 1 = 128x128 (4 waves), 2 = 64x64 (4 waves),
+// 3 = 256x128 (4 waves, two blocks per CU).
 hipError_t launch_dual_gemm(const GemmArgs& a, int branch, bool grouped, bool debug, int cfg,
                             hipStream_t s) {
   if (branch == kFP8) {

@@ -51,7 +51,7 @@ int pick_cfg(int64_t m, int64_t n, int32_t branch) {
   const char* env = getenv("SQF_GEMM_TILE");
   const int forced = env ? atoi(env) : -1;
   int cfg;
-  if (forced >= 0 && forced <= 2)
+  if (forced >= 0 && forced <= 3)
     cfg = forced;
   else if (((m + 255) / 256) * ((n + 255) / 256) >= 448)
     cfg = 0;
@@ -287,7 +287,7 @@ sqf_status sqf_dual_gemm(const sqf_acts* a, const sqf_weights* w, float* y, int6
   const int64_t ldo_b = w->ldo * branch_esz(w->branch);
   sqf::GemmArgs ga{a->x_low, a->s_x, (const uint8_t*)a->x_out, a->s_xo, w->w_low, w->s_w,
                    (const uint8_t*)w->w_out, w->s_wo, y, acc_low_dbg, nullptr, a->m, w->n, w->ldk,
-                   ldo_b, ldy, 0, 0, 0, (int32_t)(w->ldk / 128), (int32_t)(ldo_b / 128), 1};
+                   ldo_b, ldy, 0, 0, 0, (int32_t)(w->ldk / 64), (int32_t)(ldo_b / 64), 1};
   return hip_status(sqf::launch_dual_gemm(ga, w->branch, false, debug,
                                           pick_cfg(a->m, w->n, w->branch), (hipStream_t)stream),
                     who);
@@ -309,7 +309,7 @@ sqf_status sqf_dual_gemm_grouped(const sqf_acts* a, const sqf_weights* w, int64_
   sqf::GemmArgs ga{a->x_low, a->s_x, (const uint8_t*)a->x_out, a->s_xo, w->w_low, w->s_w,
                    (const uint8_t*)w->w_out, w->s_wo, y, acc_low_dbg, row_off, a->m, w->n,
                    w->ldk, ldo_b, ldy, w->n * w->ldk, w->n * ldo_b, w->n,
-                   (int32_t)(w->ldk / 128), (int32_t)(ldo_b / 128), (int32_t)groups};
+                   (int32_t)(w->ldk / 64), (int32_t)(ldo_b / 64), (int32_t)groups};
   return hip_status(sqf::launch_dual_gemm(ga, w->branch, true, acc_low_dbg != nullptr, 1,
                                           (hipStream_t)stream),
                     who);

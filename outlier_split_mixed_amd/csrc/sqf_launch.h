@@ -47,7 +47,7 @@ struct GemmArgs {
   const int64_t* row_off;  // grouped: [groups+1]
   int64_t m, n, ldk, ldo_b, ldy;
   int64_t w_stride_low, w_stride_out, w_stride_s;  // per-group strides (bytes, bytes, elems)
-  int32_t s_low, s_out, groups;
+  int32_t s_low, s_out, groups;  // 64-byte K stages of the low / branch operands
 };
 
 struct SqArgs {
