@@ -117,7 +117,7 @@ __device__ __forceinline__ void stage_barrier() {
 // then refill the buffer freed by step s-1 with stage s+NB-1.
 template <int NB, int PW>
 __device__ __forceinline__ void ring_wait(int s, int S) {
-  static_assert(NB >= 2 && NB <= 4, "ring depth");
+  static_assert(NB >= 2 && NB <= 5, "ring depth");
   const int ahead = (S - 1 - s) < (NB - 2) ? (S - 1 - s) : (NB - 2);
   if (NB >= 4 && ahead >= 2) wait_vmcnt<2 * PW>();
   else if (NB >= 3 && ahead >= 1) wait_vmcnt<PW>();
@@ -199,71 +199,108 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_du
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
+  // Stage pipeline (both loops below).  Stage t lives in ring buffer t % NB.
+  // A step computes its stage in two halves.  Between them it waits for stage
+  // s+1 to land, crosses the barrier, refills the ring (stage s+NB-1 goes into
+  // the buffer of stage s-1, which every wave has finished with) and issues
+  // the LDS reads of stage s+1's B fragments and first A fragment; the second
+  // half's MFMAs then hide that latency.  The rest of stage s+1's A fragments
+  // are read at its start, behind the MFMAs on the prefetched first one.
+  auto mid_sync = [&](int s, int S_, const uint8_t* a, const uint8_t* b) {
+    // stages s+2 .. s+NB-2 may stay in flight
+    const int ahead = (S_ - 2 - s) < (NB - 3) ? (S_ - 2 - s) : (NB - 3);
+    if (NB >= 5 && ahead >= 2) wait_vmcnt<2 * PW>();
+    else if (NB >= 4 && ahead >= 1) wait_vmcnt<PW>();
+    else wait_vmcnt<0>();
+    stage_barrier();
+    if (s + NB - 1 < S_) ld.issue(a, b, (uint32_t)(s + NB - 1) * 64u, smem + ((s + NB - 1) % NB) * STAGE);
+  };
+  auto start = [&](int S_, const uint8_t* a, const uint8_t* b) {
+#pragma unroll
+    for (int t = 0; t < NB - 1; ++t)
+      if (t < S_) ld.issue(a, b, (uint32_t)t * 64u, smem + t * STAGE);
+    const int ahead = (S_ - 1) < (NB - 2) ? (S_ - 1) : (NB - 2);
+    if (NB >= 5 && ahead >= 3) wait_vmcnt<3 * PW>();
+    else if (NB >= 4 && ahead >= 2) wait_vmcnt<2 * PW>();
+    else if (NB >= 3 && ahead >= 1) wait_vmcnt<PW>();
+    else wait_vmcnt<0>();
+    stage_barrier();
+  };
+  v4i PB[TN], PA0;  // prefetched fragments of the next stage
+  auto prefetch = [&](int buf) {
+    const v4i* As = (const v4i*)(smem + buf * STAGE);
+    const v4i* Bs = As + BM * 4;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) PB[j] = Bs[(wn * TN + j) * 64 + lane];
+    PA0 = As[(wm * TM) * 64 + lane];
+  };
+
   // ---------------- low path: int4 x int4 on int8 MFMA ----------------
   const int S = p.s_low;
   if (S > 0) {
     ld.init(wave, lane, m0, m_end, n0, p.n, p.ldk);
-#pragma unroll
-    for (int t = 0; t < NB - 1; ++t)
-      if (t < S) ld.issue(p.x_low, w_low, (uint32_t)t * 64u, smem + t * STAGE);
+    start(S, p.x_low, w_low);
+    prefetch(0);
     for (int s = 0; s < S; ++s) {
-      ring_wait<NB, PW>(s, S);
-      if (s + NB - 1 < S)
-        ld.issue(p.x_low, w_low, (uint32_t)(s + NB - 1) * 64u, smem + ((s + NB - 1) % NB) * STAGE);
       const v4i* As = (const v4i*)(smem + (s % NB) * STAGE);
-      const v4i* Bs = As + BM * 4;
-      v4i b0[TN], b1[TN];
+      v4i A[TM], Bq[TN];
+      A[0] = PA0;
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const v4i q = Bs[(wn * TN + j) * 64 + lane];
-        unpack_i4x32(make_uint4(q[0], q[1], q[2], q[3]), b0[j], b1[j]);
-      }
+      for (int i = 1; i < TM; ++i) A[i] = As[(wm * TM + i) * 64 + lane];
+      // keep the reads at the top of the stage: their latency then overlaps
+      // the MFMAs on the prefetched fragments instead of stalling each use
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        v4i a0, a1;
-        const v4i q = As[(wm * TM + i) * 64 + lane];
-        unpack_i4x32(make_uint4(q[0], q[1], q[2], q[3]), a0, a1);
+      for (int j = 0; j < TN; ++j) Bq[j] = PB[j];
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0[j], acc[i][j], 0, 0, 0);
+      for (int half = 0; half < 2; ++half) {
+        if (half == 1 && s + 1 < S) {
+          mid_sync(s, S, p.x_low, w_low);
+          prefetch((s + 1) % NB);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        v4i bb[TN];
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < TN; ++j) {
+          const uint32_t x = (uint32_t)Bq[j][2 * half], y = (uint32_t)Bq[j][2 * half + 1];
+          bb[j] = v4i{(int)((x << 4) & 0xF0F0F0F0u), (int)(x & 0xF0F0F0F0u),
+                      (int)((y << 4) & 0xF0F0F0F0u), (int)(y & 0xF0F0F0F0u)};
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const uint32_t x = (uint32_t)A[i][2 * half], y = (uint32_t)A[i][2 * half + 1];
+          const v4i aa = v4i{(int)((x << 4) & 0xF0F0F0F0u), (int)(x & 0xF0F0F0F0u),
+                             (int)((y << 4) & 0xF0F0F0F0u), (int)(y & 0xF0F0F0F0u)};
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aa, bb[j], acc[i][j], 0, 0, 0);
+        }
       }
     }
   }
 
   // ---------------- epilogue part 1: exact int32 -> scaled fp32 ----------------
-  const int lr = (lane >> 4) * 4;  // first of the 4 rows this lane holds in a 16x16 tile
-  const int lc = lane & 15;
-  int64_t rows[TM][4];
-  int64_t cols[TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) rows[i][r] = m0 + wm * WM + i * 16 + lr + r;
-#pragma unroll
-  for (int j = 0; j < TN; ++j) cols[j] = n0 + wn * WN + j * 16 + lc;
-
-  float swv[TN];
-#pragma unroll
-  for (int j = 0; j < TN; ++j) swv[j] = s_w[cols[j] < p.n ? cols[j] : p.n - 1];
-
+  // Lane l holds rows 4*(l/16)+r (r < 4) and column l%16 of each 16x16 tile.
+  // Row and column indices fit in 32 bits (the host limits operand sizes).
+  const int row0 = (int)(m0 - m_begin) + wm * WM + (lane >> 4) * 4;  // tile-local to the group
+  const int col0 = (int)n0 + wn * WN + (lane & 15);
+  const int mrows = (int)(m_end - m_begin), ncols = (int)p.n;
+  const float* s_x = p.s_x + m_begin;
   v4f c[TM][TN];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    float sxv[4];
+  for (int j = 0; j < TN; ++j) {
+    const int col = col0 + j * 16;
+    const float sw = s_w[col < ncols ? col : ncols - 1] * 0.00390625f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sxv[r] = p.s_x[rows[i][r] < m_end ? rows[i][r] : m_end - 1];
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
+    for (int i = 0; i < TM; ++i) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
+        const int row = row0 + i * 16 + r;
         if constexpr (DEBUG) {
-          if (rows[i][r] < m_end && cols[j] < p.n)
-            p.acc_dbg[rows[i][r] * p.n + cols[j]] = acc[i][j][r] >> 8;
+          if (row < mrows && col < ncols)
+            p.acc_dbg[(m_begin + row) * p.n + col] = acc[i][j][r] >> 8;
         }
-        c[i][j][r] = (float)acc[i][j][r] * (sxv[r] * swv[j] * 0.00390625f);
+        c[i][j][r] = (float)acc[i][j][r] * (s_x[row < mrows ? row : mrows - 1] * sw);
       }
     }
   }
@@ -278,41 +315,45 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_du
   }
   const int SO = p.s_out;
   if (SO > 0) {
-    __syncthreads();  // every wave is done with the low path's buffers
+    stage_barrier();  // every wave is done with the low path's buffers
     ld.init(wave, lane, m0, m_end, n0, p.n, p.ldo_b);
-#pragma unroll
-    for (int t = 0; t < NB - 1; ++t)
-      if (t < SO) ld.issue(p.x_out, w_out, (uint32_t)t * 64u, smem + t * STAGE);
+    start(SO, p.x_out, w_out);
+    prefetch(0);
     for (int s = 0; s < SO; ++s) {
-      ring_wait<NB, PW>(s, SO);
-      if (s + NB - 1 < SO)
-        ld.issue(p.x_out, w_out, (uint32_t)(s + NB - 1) * 64u, smem + ((s + NB - 1) % NB) * STAGE);
       const v4i* As = (const v4i*)(smem + (s % NB) * STAGE);
-      const v4i* Bs = As + BM * 4;
-      v4i bq[TN];
+      v4i A[TM], Bq[TN];
+      A[0] = PA0;
 #pragma unroll
-      for (int j = 0; j < TN; ++j) bq[j] = Bs[(wn * TN + j) * 64 + lane];
+      for (int i = 1; i < TM; ++i) A[i] = As[(wm * TM + i) * 64 + lane];
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const v4i aq = As[(wm * TM + i) * 64 + lane];
+      for (int j = 0; j < TN; ++j) Bq[j] = PB[j];
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          if constexpr (BR == kBF16) {
-            c[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, aq),
-                                                              __builtin_bit_cast(v8bf, bq[j]),
-                                                              c[i][j], 0, 0, 0);
-          } else {
-            long a_lo = (long)(((uint64_t)(uint32_t)aq[1] << 32) | (uint32_t)aq[0]);
-            long b_lo = (long)(((uint64_t)(uint32_t)bq[j][1] << 32) | (uint32_t)bq[j][0]);
-            c2[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a_lo, b_lo, c2[i][j], 0, 0, 0);
-          }
+      for (int half = 0; half < 2; ++half) {
+        if (half == 1 && s + 1 < SO) {
+          mid_sync(s, SO, p.x_out, w_out);
+          prefetch((s + 1) % NB);
         }
-        if constexpr (BR == kFP8) {
+        // bf16: one MFMA (K = 32) per fragment, the halves split the rows;
+        // E4M3: two MFMAs (K = 32 each) per fragment, the halves split K.
+        if constexpr (BR == kBF16) {
 #pragma unroll
-          for (int j = 0; j < TN; ++j) {
-            long a_hi = (long)(((uint64_t)(uint32_t)aq[3] << 32) | (uint32_t)aq[2]);
-            long b_hi = (long)(((uint64_t)(uint32_t)bq[j][3] << 32) | (uint32_t)bq[j][2]);
-            c2[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a_hi, b_hi, c2[i][j], 0, 0, 0);
+          for (int ii = 0; ii < (TM + 1) / 2; ++ii) {
+            const int i = half * ((TM + 1) / 2) + ii;
+            if (i >= TM) break;
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+              c[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(v8bf, A[i]), __builtin_bit_cast(v8bf, Bq[j]), c[i][j], 0, 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < TM; ++i) {
+            const long a8 = (long)(((uint64_t)(uint32_t)A[i][2 * half + 1] << 32) | (uint32_t)A[i][2 * half]);
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+              const long b8 = (long)(((uint64_t)(uint32_t)Bq[j][2 * half + 1] << 32) | (uint32_t)Bq[j][2 * half]);
+              c2[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a8, b8, c2[i][j], 0, 0, 0);
+            }
           }
         }
       }
@@ -320,25 +361,22 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_du
   }
 
   // ---------------- epilogue part 2: fuse and store ----------------
-  float swo[TN];
-  if constexpr (BR == kFP8) {
-#pragma unroll
-    for (int j = 0; j < TN; ++j) swo[j] = s_wo[cols[j] < p.n ? cols[j] : p.n - 1];
-  }
+  float* y = p.y + m_begin * p.ldy;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int64_t row = rows[i][r];
-      if (row >= m_end) continue;
+      const int row = row0 + i * 16 + r;
+      if (row >= mrows) continue;
       float sxo = 0.f;
-      if constexpr (BR == kFP8) sxo = p.s_xo[row];
+      if constexpr (BR == kFP8) sxo = p.s_xo[m_begin + row];
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        if (cols[j] >= p.n) continue;
+        const int col = col0 + j * 16;
+        if (col >= ncols) continue;
         float v = c[i][j][r];
-        if constexpr (BR == kFP8) v += (sxo * swo[j]) * c2[i][j][r];
-        p.y[row * p.ldy + cols[j]] = v;
+        if constexpr (BR == kFP8) v += (sxo * s_wo[col]) * c2[i][j][r];
+        y[(int64_t)row * p.ldy + col] = v;
       }
     }
   }
