@@ -8,97 +8,159 @@
 // the per-token low-precision activation path of both pages.
 //
 // Memory plan (HBM-bound kernel): each row is read once with 16-byte loads per
-// lane (8 channels), the channel map comes from L2 (the same [k] array for
-// every row) and is kept in registers while a block walks several rows.
-// Codes are scattered into an LDS staging row by slot, then read back in slot
-// order and written with 16-byte stores, so every HBM write is coalesced.
-// The absmax is a wave max over shuffles followed by a cross-wave max in LDS.
+// lane (8 channels); the next row is loaded while the current one is
+// processed.  The channel map is read once per block and condensed to one
+// word per 8-channel chunk.  Codes are scattered into an LDS staging row by
+// slot, then read back in slot order and written with 16-byte stores, so every
+// HBM write is coalesced.  The absmax is a wave max over shuffles followed by
+// a cross-wave max in LDS; block barriers wait for LDS traffic only.
+#include <cstdlib>
+
 #include "sqf_device.h"
 #include "sqf_launch.h"
 
 namespace sqf {
 
+// Barrier for LDS hand-offs only: waits for this wave's LDS operations, then
+// s_barrier.  Unlike __syncthreads() it does not wait for outstanding global
+// loads, so the next row's prefetch stays in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt untouched
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <int XT, int LOW, int BR, bool GROUPED, int NT, int CPT>
 __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
   extern __shared__ uint8_t sm[];
-  // LDS: [pad_lo] code bytes | [ldo * esz] branch codes | reduction scratch
   constexpr int ESZ = BR == kBF16 ? 2 : 1;
   constexpr int NW = NT / 64;
+  constexpr int OPT = 4;  // outlier channels gathered per thread per pass
+  // LDS: [pad_lo + 16] code bytes (the last 16 are a dump slot written by
+  // outlier lanes) | [k_out] int32 outlier channel list | reduction scratch
   uint8_t* codes = sm;
-  uint8_t* bcodes = sm + p.pad_lo;
-  float* red = (float*)(sm + ((p.pad_lo + p.ldo * ESZ + 15) & ~(int64_t)15));
+  const int dump_lo = (int)p.pad_lo;
+  int32_t* oidx = (int32_t*)(sm + p.pad_lo + 16);
+  float* red = (float*)(sm + p.pad_lo + 16 + ((p.k_out * 4 + 15) & ~(int64_t)15));
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const float qlow = LOW == kI4X2 ? 7.0f : 127.0f;
   const float qhi = BR == kFP8 ? 448.0f : 127.0f;
+  const int k_out = (int)p.k_out;
 
   // padding slots are never written by the scatter below: zero them once
   for (int64_t j = p.k_low + tid; j < p.pad_lo; j += NT) codes[j] = 0;
-  for (int64_t t = p.k_out * ESZ + tid; t < p.ldo * ESZ; t += NT) bcodes[t] = 0;
 
-  int32_t mreg[CPT][8];
-  int cached_group = -1;
-
-  for (int64_t m = blockIdx.x; m < p.m; m += gridDim.x) {
-    int g = 0;
-    if constexpr (GROUPED) {
-      int lo = 0, hi = p.groups;  // largest g with row_off[g] <= m
-      while (hi - lo > 1) {
-        int mid = (lo + hi) >> 1;
-        if (p.row_off[mid] <= m) lo = mid; else hi = mid;
-      }
-      g = lo;
-    }
-    if (g != cached_group) {
-      const int32_t* mp = p.map + (int64_t)g * p.k;
-#pragma unroll
-      for (int i = 0; i < CPT; ++i) {
-        int64_t c8 = ((int64_t)tid + (int64_t)i * NT) * 8;
-        if (c8 < p.k) {
-          int4 u0 = *(const int4*)(mp + c8);
-          int4 u1 = *(const int4*)(mp + c8 + 4);
-          mreg[i][0] = u0.x; mreg[i][1] = u0.y; mreg[i][2] = u0.z; mreg[i][3] = u0.w;
-          mreg[i][4] = u1.x; mreg[i][5] = u1.y; mreg[i][6] = u1.z; mreg[i][7] = u1.w;
-        }
-      }
-      cached_group = g;
-    }
-    // ---- load the row (16 B per lane per chunk) ----
-    float v[CPT][8];
+  // One word per 8-channel chunk: (low slots before the chunk) << 8 | mask of
+  // the chunk's outlier channels.  The outlier channel list goes to LDS.
+  uint32_t cw[CPT];
+  auto load_map = [&](int g) {
+    const int32_t* mp = p.map + (int64_t)g * p.k;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      int64_t c8 = ((int64_t)tid + (int64_t)i * NT) * 8;
+      const int64_t c8 = ((int64_t)tid + (int64_t)i * NT) * 8;
+      cw[i] = 0;
       if (c8 < p.k) {
-        if constexpr (XT == kBF16) {
-          uint4 u = *(const uint4*)((const uint16_t*)p.x + m * p.ldx + c8);
-          uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+        const int4 u0 = *(const int4*)(mp + c8);
+        const int4 u1 = *(const int4*)(mp + c8 + 4);
+        const int m8[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+        uint32_t mask = 0;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            v[i][2 * e] = __uint_as_float(w4[e] << 16);
-            v[i][2 * e + 1] = __uint_as_float(w4[e] & 0xFFFF0000u);
-          }
-        } else {
-          const float* xr = (const float*)p.x + m * p.ldx + c8;
-          float4 a = *(const float4*)xr, b = *(const float4*)(xr + 4);
-          v[i][0] = a.x; v[i][1] = a.y; v[i][2] = a.z; v[i][3] = a.w;
-          v[i][4] = b.x; v[i][5] = b.y; v[i][6] = b.z; v[i][7] = b.w;
+        for (int e = 0; e < 8; ++e) {
+          mask |= (m8[e] < 0 ? 1u : 0u) << e;
+          if (m8[e] < 0) oidx[-m8[e] - 1] = (int32_t)(c8 + e);
+        }
+        const int64_t before = m8[0] >= 0 ? m8[0] : c8 - (-m8[0] - 1);
+        cw[i] = ((uint32_t)before << 8) | mask;
+      }
+    }
+  };
+  // one map for every row: load it once, outside the row loop (a load inside
+  // the loop would make every iteration wait for all outstanding loads)
+  int cached_group = -1;
+  if constexpr (!GROUPED) load_map(0);
+
+  // raw row words: 4 per chunk for bf16, 8 for fp32; the next row's words are
+  // loaded while the current row is processed
+  constexpr int WPC = XT == kBF16 ? 4 : 8;
+  typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+  auto load_raw = [&](int64_t row, uint32_t (&r)[CPT][WPC]) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int64_t c8 = ((int64_t)tid + (int64_t)i * NT) * 8;
+      if (c8 < p.k) {
+        const v4u* src = XT == kBF16 ? (const v4u*)((const uint16_t*)p.x + row * p.ldx + c8)
+                                     : (const v4u*)((const float*)p.x + row * p.ldx + c8);
+#pragma unroll
+        for (int h = 0; h < WPC / 4; ++h) {
+          const v4u u = src[h];
+          r[i][4 * h] = u[0]; r[i][4 * h + 1] = u[1]; r[i][4 * h + 2] = u[2]; r[i][4 * h + 3] = u[3];
         }
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[i][e] = 0.0f;
+        for (int w = 0; w < WPC; ++w) r[i][w] = 0;
       }
     }
-    // ---- absmax over low (and outlier) channels ----
+  };
+  auto val = [&](const uint32_t (&r)[CPT][WPC], int i, int e) -> float {
+    if constexpr (XT == kBF16) {
+      const uint32_t w = r[i][e >> 1];
+      return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+    } else {
+      return __uint_as_float(r[i][e]);
+    }
+  };
+  auto xval = [&](int64_t row, int c) -> float {
+    if constexpr (XT == kBF16) return __uint_as_float((uint32_t)((const uint16_t*)p.x)[row * p.ldx + c] << 16);
+    else return ((const float*)p.x)[row * p.ldx + c];
+  };
+  uint32_t raw[CPT][WPC], nxt[CPT][WPC];
+  if (blockIdx.x < p.m) load_raw(blockIdx.x, raw);
+  lds_barrier();  // outlier list and padding in place
+
+  for (int64_t m = blockIdx.x; m < p.m; m += gridDim.x) {
+    if constexpr (GROUPED) {
+      int lo = 0, hi = p.groups;  // largest g with row_off[g] <= m
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (p.row_off[mid] <= m) lo = mid; else hi = mid;
+      }
+      if (lo != cached_group) {
+        lds_barrier();  // nobody still reads the previous group's outlier list
+        load_map(lo);
+        cached_group = lo;
+        lds_barrier();
+      }
+    }
+    // ---- outlier channels: gathered from the row (cache-resident).  Issued
+    // before the next-row prefetch: loads retire in order, so waiting for
+    // these does not wait for the prefetch. ----
+    float ov[OPT];
+#pragma unroll
+    for (int u = 0; u < OPT; ++u) {
+      const int t = tid + u * NT;
+      ov[u] = t < k_out ? xval(m, oidx[t]) : 0.0f;
+    }
+    if (m + gridDim.x < p.m) load_raw(m + gridDim.x, nxt);
+    // Register pressure: the chunk words are constant across rows and the
+    // decoded values are needed twice; without these opaque redefinitions the
+    // compiler keeps every derived value live across the whole loop.
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) asm volatile("" : "+v"(cw[i]));
+    // ---- absmax over the low channels (and the outlier channels) ----
     float alo = 0.0f, ahi = 0.0f;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      int64_t c8 = ((int64_t)tid + (int64_t)i * NT) * 8;
-      if (c8 < p.k) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float t = fabsf(v[i][e]);
-          if (mreg[i][e] >= 0) alo = fmaxf(alo, t); else ahi = fmaxf(ahi, t);
-        }
+      for (int e = 0; e < 8; ++e) {
+        const float t = fabsf(val(raw, i, e));
+        alo = fmaxf(alo, ((cw[i] >> e) & 1u) ? 0.0f : t);
       }
+    }
+    if constexpr (BR != kBF16) {
+#pragma unroll
+      for (int u = 0; u < OPT; ++u) ahi = fmaxf(ahi, fabsf(ov[u]));
+      for (int t = OPT * NT + tid; t < k_out; t += NT) ahi = fmaxf(ahi, fabsf(xval(m, oidx[t])));
     }
     alo = wave_max(alo);
     if constexpr (BR != kBF16) ahi = wave_max(ahi);
@@ -106,7 +168,7 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
       red[wv] = alo;
       red[NW + wv] = ahi;
     }
-    __syncthreads();
+    lds_barrier();
     alo = red[0];
     ahi = red[NW];
 #pragma unroll
@@ -120,30 +182,46 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
       p.s_x[m] = quant_scale(alo, qlow);
       if constexpr (BR != kBF16) p.s_xo[m] = quant_scale(ahi, qhi);
     }
-    // ---- codes -> LDS staging row ----
+    // ---- branch row: coalesced direct stores, zero padding up to ldo ----
+    uint8_t* xo = p.x_out + m * p.ldo * ESZ;
+#pragma unroll
+    for (int u = 0; u < OPT; ++u) {
+      const int t = tid + u * NT;
+      if (t < k_out) {
+        if constexpr (BR == kBF16) ((uint16_t*)xo)[t] = (uint16_t)bf16_rne(ov[u]);
+        else if constexpr (BR == kFP8) xo[t] = (uint8_t)e4m3_rne_sat(ov[u] * inv_hi);
+        else xo[t] = (uint8_t)quant_code(ov[u], inv_hi, qhi);
+      }
+    }
+    for (int t = OPT * NT + tid; t < k_out; t += NT) {  // outliers beyond the registers
+      const float x = xval(m, oidx[t]);
+      if constexpr (BR == kBF16) ((uint16_t*)xo)[t] = (uint16_t)bf16_rne(x);
+      else if constexpr (BR == kFP8) xo[t] = (uint8_t)e4m3_rne_sat(x * inv_hi);
+      else xo[t] = (uint8_t)quant_code(x, inv_hi, qhi);
+    }
+    for (int64_t t = k_out + tid; t < p.ldo; t += NT) {
+      if constexpr (BR == kBF16) ((uint16_t*)xo)[t] = 0;
+      else xo[t] = 0;
+    }
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+#pragma unroll
+      for (int w = 0; w < WPC; ++w) asm volatile("" : "+v"(raw[i][w]));
+    // ---- low codes -> LDS staging row (outlier lanes write a dump slot) ----
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      int64_t c8 = ((int64_t)tid + (int64_t)i * NT) * 8;
+      const int64_t c8 = ((int64_t)tid + (int64_t)i * NT) * 8;
       if (c8 < p.k) {
+        int slot = (int)(cw[i] >> 8);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          int32_t s = mreg[i][e];
-          if (s >= 0) {
-            codes[s] = (uint8_t)quant_code(v[i][e], inv_lo, qlow);
-          } else {
-            int t = -s - 1;
-            if constexpr (BR == kBF16) {
-              ((uint16_t*)bcodes)[t] = (uint16_t)bf16_rne(v[i][e]);
-            } else if constexpr (BR == kFP8) {
-              bcodes[t] = (uint8_t)e4m3_rne_sat(v[i][e] * inv_hi);
-            } else {
-              bcodes[t] = (uint8_t)quant_code(v[i][e], inv_hi, qhi);
-            }
-          }
+          const bool out = (cw[i] >> e) & 1u;
+          codes[out ? dump_lo : slot] = (uint8_t)quant_code(val(raw, i, e), inv_lo, qlow);
+          slot += out ? 0 : 1;
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
     // ---- LDS -> packed HBM rows, 16-byte stores ----
     const int64_t ngrp = p.ldk / 16;
     uint8_t* xl = p.x_low + m * p.ldk;
@@ -166,10 +244,11 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
       }
       *(uint4*)(xl + q * 16) = o;
     }
-    const int64_t ogrp = p.ldo * ESZ / 16;
-    uint8_t* xo = p.x_out + m * p.ldo * ESZ;
-    for (int64_t q = tid; q < ogrp; q += NT) *(uint4*)(xo + q * 16) = *(const uint4*)(bcodes + q * 16);
-    __syncthreads();
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+#pragma unroll
+      for (int w = 0; w < WPC; ++w) raw[i][w] = nxt[i][w];
   }
 }
 
@@ -205,9 +284,11 @@ static hipError_t launch_br(const ActArgs& a, int br, int64_t grid, size_t lds, 
 
 hipError_t launch_act_split(const ActArgs& a, int x_dtype, int low, int branch, bool grouped,
                             hipStream_t s) {
-  const int esz = branch == kBF16 ? 2 : 1;
-  size_t lds = (size_t)((a.pad_lo + a.ldo * esz + 15) & ~(int64_t)15) + 2 * 16 * sizeof(float);
-  int64_t grid = a.m < 2048 ? a.m : 2048;
+  size_t lds = (size_t)(a.pad_lo + 16 + ((a.k_out * 4 + 15) & ~(int64_t)15)) + 2 * 16 * sizeof(float);
+  // rows per block: SQF_ACT_GRID overrides the grid size (tuning aid)
+  const char* env = getenv("SQF_ACT_GRID");
+  const int64_t cap = env ? atoll(env) : 1024;
+  int64_t grid = a.m < cap ? a.m : cap;
   if (grid <= 0) return hipSuccess;
   if (x_dtype == kBF16) {
     if (low == kI4X2)

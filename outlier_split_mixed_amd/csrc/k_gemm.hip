@@ -191,7 +191,32 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_du
   const int64_t m0 = m_begin + tm * BM;
   const int64_t n0 = tn * BN;
 
-  DmaLoader<BM, BN, NW> ld;
+  // One stage stream: stages 0 .. S-1 are the low path (packed int4, stride
+  // ldk), stages S .. S+SO-1 the branch (stride ldo_b).  Both run through the
+  // same ring, so the branch's first stages are already in flight when the
+  // low path ends and no pipeline restarts between them.
+  const int S = p.s_low, SO = p.s_out, ST = S + SO;
+  // per-lane row offsets of this wave's fragments for both operand streams
+  // (selected per stage with wave-uniform selects, no control flow)
+  DmaLoader<BM, BN, NW> ld_lo, ld_br;
+  ld_lo.init(wave, lane, m0, m_end, n0, p.n, p.ldk);
+  ld_br.init(wave, lane, m0, m_end, n0, p.n, p.ldo_b);
+  auto issue = [&](int t) {
+    const bool lo = t < S;
+    const uint8_t* a = lo ? p.x_low : p.x_out;
+    const uint8_t* b = lo ? w_low : w_out;
+    const uint32_t so = (uint32_t)(lo ? t : t - S) * 64u;
+    uint8_t* buf = smem + (t % NB) * STAGE;
+#pragma unroll
+    for (int i = 0; i < PW; ++i) {
+      const int q = ld_lo.q0 + i;
+      const uint8_t* base = q < DmaLoader<BM, BN, NW>::AFR ? a : b;
+      const uint32_t off = lo ? ld_lo.off[i] : ld_br.off[i];
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(base + off + so),
+          (__attribute__((address_space(3))) void*)(buf + q * 1024), 16, 0, 0);
+    }
+  };
 
   v4i acc[TM][TN];
 #pragma unroll
@@ -199,87 +224,88 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_du
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
-  // Stage pipeline (both loops below).  Stage t lives in ring buffer t % NB.
-  // A step computes its stage in two halves.  Between them it waits for stage
-  // s+1 to land, crosses the barrier, refills the ring (stage s+NB-1 goes into
-  // the buffer of stage s-1, which every wave has finished with) and issues
-  // the LDS reads of stage s+1's B fragments and first A fragment; the second
-  // half's MFMAs then hide that latency.  The rest of stage s+1's A fragments
-  // are read at its start, behind the MFMAs on the prefetched first one.
-  auto mid_sync = [&](int s, int S_, const uint8_t* a, const uint8_t* b) {
-    // stages s+2 .. s+NB-2 may stay in flight
-    const int ahead = (S_ - 2 - s) < (NB - 3) ? (S_ - 2 - s) : (NB - 3);
-    if (NB >= 5 && ahead >= 2) wait_vmcnt<2 * PW>();
-    else if (NB >= 4 && ahead >= 1) wait_vmcnt<PW>();
-    else wait_vmcnt<0>();
-    stage_barrier();
-    if (s + NB - 1 < S_) ld.issue(a, b, (uint32_t)(s + NB - 1) * 64u, smem + ((s + NB - 1) % NB) * STAGE);
-  };
-  auto start = [&](int S_, const uint8_t* a, const uint8_t* b) {
-#pragma unroll
-    for (int t = 0; t < NB - 1; ++t)
-      if (t < S_) ld.issue(a, b, (uint32_t)t * 64u, smem + t * STAGE);
-    const int ahead = (S_ - 1) < (NB - 2) ? (S_ - 1) : (NB - 2);
-    if (NB >= 5 && ahead >= 3) wait_vmcnt<3 * PW>();
-    else if (NB >= 4 && ahead >= 2) wait_vmcnt<2 * PW>();
-    else if (NB >= 3 && ahead >= 1) wait_vmcnt<PW>();
-    else wait_vmcnt<0>();
-    stage_barrier();
-  };
+  // Pipeline.  Stage t lives in ring buffer t % NB.  A step computes its
+  // stage in two halves.  Between them it waits for stage t+1 to land,
+  // crosses the barrier, refills the ring (stage t+NB-1 goes into the buffer
+  // of stage t-1, which every wave has finished with) and issues the LDS
+  // reads of stage t+1's B fragments and first A fragment; the second half's
+  // MFMAs then hide that latency.  The rest of stage t+1's A fragments are
+  // read at its start, behind the MFMAs on the prefetched first one.
   v4i PB[TN], PA0;  // prefetched fragments of the next stage
-  auto prefetch = [&](int buf) {
-    const v4i* As = (const v4i*)(smem + buf * STAGE);
+  auto prefetch = [&](int t) {
+    const v4i* As = (const v4i*)(smem + (t % NB) * STAGE);
     const v4i* Bs = As + BM * 4;
 #pragma unroll
     for (int j = 0; j < TN; ++j) PB[j] = Bs[(wn * TN + j) * 64 + lane];
     PA0 = As[(wm * TM) * 64 + lane];
   };
+  auto mid_sync = [&](int t) {
+    // stages t+2 .. t+NB-2 may stay in flight
+    const int ahead = (ST - 2 - t) < (NB - 3) ? (ST - 2 - t) : (NB - 3);
+    if (NB >= 5 && ahead >= 2) wait_vmcnt<2 * PW>();
+    else if (NB >= 4 && ahead >= 1) wait_vmcnt<PW>();
+    else wait_vmcnt<0>();
+    stage_barrier();
+    if (t + NB - 1 < ST) issue(t + NB - 1);
+    prefetch(t + 1);
+  };
+  // stage t's A fragments 1.. from LDS (fragment 0 and B were prefetched)
+  auto load_stage = [&](int t, v4i (&A)[TM], v4i (&Bq)[TN]) {
+    const v4i* As = (const v4i*)(smem + (t % NB) * STAGE);
+    A[0] = PA0;
+#pragma unroll
+    for (int i = 1; i < TM; ++i) A[i] = As[(wm * TM + i) * 64 + lane];
+    // keep the reads at the top of the stage: their latency then overlaps
+    // the MFMAs on the prefetched fragments instead of stalling each use
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) Bq[j] = PB[j];
+  };
+
+  // prime the ring
+#pragma unroll
+  for (int t = 0; t < NB - 1; ++t)
+    if (t < ST) issue(t);
+  {
+    const int ahead = (ST - 1) < (NB - 2) ? (ST - 1) : (NB - 2);
+    if (NB >= 5 && ahead >= 3) wait_vmcnt<3 * PW>();
+    else if (NB >= 4 && ahead >= 2) wait_vmcnt<2 * PW>();
+    else if (NB >= 3 && ahead >= 1) wait_vmcnt<PW>();
+    else wait_vmcnt<0>();
+    stage_barrier();
+    prefetch(0);
+  }
 
   // ---------------- low path: int4 x int4 on int8 MFMA ----------------
-  const int S = p.s_low;
-  if (S > 0) {
-    ld.init(wave, lane, m0, m_end, n0, p.n, p.ldk);
-    start(S, p.x_low, w_low);
-    prefetch(0);
-    for (int s = 0; s < S; ++s) {
-      const v4i* As = (const v4i*)(smem + (s % NB) * STAGE);
-      v4i A[TM], Bq[TN];
-      A[0] = PA0;
+  for (int t = 0; t < S; ++t) {
+    v4i A[TM], Bq[TN];
+    load_stage(t, A, Bq);
 #pragma unroll
-      for (int i = 1; i < TM; ++i) A[i] = As[(wm * TM + i) * 64 + lane];
-      // keep the reads at the top of the stage: their latency then overlaps
-      // the MFMAs on the prefetched fragments instead of stalling each use
-      __builtin_amdgcn_sched_barrier(0);
+    for (int half = 0; half < 2; ++half) {
+      if (half == 1 && t + 1 < ST) {
+        mid_sync(t);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      v4i bb[TN];
 #pragma unroll
-      for (int j = 0; j < TN; ++j) Bq[j] = PB[j];
+      for (int j = 0; j < TN; ++j) {
+        const uint32_t x = (uint32_t)Bq[j][2 * half], y = (uint32_t)Bq[j][2 * half + 1];
+        bb[j] = v4i{(int)((x << 4) & 0xF0F0F0F0u), (int)(x & 0xF0F0F0F0u),
+                    (int)((y << 4) & 0xF0F0F0F0u), (int)(y & 0xF0F0F0F0u)};
+      }
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        if (half == 1 && s + 1 < S) {
-          mid_sync(s, S, p.x_low, w_low);
-          prefetch((s + 1) % NB);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        v4i bb[TN];
+      for (int i = 0; i < TM; ++i) {
+        const uint32_t x = (uint32_t)A[i][2 * half], y = (uint32_t)A[i][2 * half + 1];
+        const v4i aa = v4i{(int)((x << 4) & 0xF0F0F0F0u), (int)(x & 0xF0F0F0F0u),
+                           (int)((y << 4) & 0xF0F0F0F0u), (int)(y & 0xF0F0F0F0u)};
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const uint32_t x = (uint32_t)Bq[j][2 * half], y = (uint32_t)Bq[j][2 * half + 1];
-          bb[j] = v4i{(int)((x << 4) & 0xF0F0F0F0u), (int)(x & 0xF0F0F0F0u),
-                      (int)((y << 4) & 0xF0F0F0F0u), (int)(y & 0xF0F0F0F0u)};
-        }
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          const uint32_t x = (uint32_t)A[i][2 * half], y = (uint32_t)A[i][2 * half + 1];
-          const v4i aa = v4i{(int)((x << 4) & 0xF0F0F0F0u), (int)(x & 0xF0F0F0F0u),
-                             (int)((y << 4) & 0xF0F0F0F0u), (int)(y & 0xF0F0F0F0u)};
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aa, bb[j], acc[i][j], 0, 0, 0);
-        }
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aa, bb[j], acc[i][j], 0, 0, 0);
       }
     }
   }
 
-  // ---------------- epilogue part 1: exact int32 -> scaled fp32 ----------------
+  // ---------------- exact int32 -> scaled fp32 ----------------
   // Lane l holds rows 4*(l/16)+r (r < 4) and column l%16 of each 16x16 tile.
   // Row and column indices fit in 32 bits (the host limits operand sizes).
   const int row0 = (int)(m0 - m_begin) + wm * WM + (lane >> 4) * 4;  // tile-local to the group
@@ -313,47 +339,35 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_du
 #pragma unroll
       for (int j = 0; j < TN; ++j) c2[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
   }
-  const int SO = p.s_out;
-  if (SO > 0) {
-    stage_barrier();  // every wave is done with the low path's buffers
-    ld.init(wave, lane, m0, m_end, n0, p.n, p.ldo_b);
-    start(SO, p.x_out, w_out);
-    prefetch(0);
-    for (int s = 0; s < SO; ++s) {
-      const v4i* As = (const v4i*)(smem + (s % NB) * STAGE);
-      v4i A[TM], Bq[TN];
-      A[0] = PA0;
+  for (int t = S; t < ST; ++t) {
+    v4i A[TM], Bq[TN];
+    load_stage(t, A, Bq);
 #pragma unroll
-      for (int i = 1; i < TM; ++i) A[i] = As[(wm * TM + i) * 64 + lane];
+    for (int half = 0; half < 2; ++half) {
+      if (half == 1 && t + 1 < ST) {
+        mid_sync(t);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // bf16: one MFMA (K = 32) per fragment, the halves split the rows;
+      // E4M3: two MFMAs (K = 32 each) per fragment, the halves split K.
+      if constexpr (BR == kBF16) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j) Bq[j] = PB[j];
+        for (int ii = 0; ii < (TM + 1) / 2; ++ii) {
+          const int i = half * ((TM + 1) / 2) + ii;
+          if (i >= TM) break;
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        if (half == 1 && s + 1 < SO) {
-          mid_sync(s, SO, p.x_out, w_out);
-          prefetch((s + 1) % NB);
+          for (int j = 0; j < TN; ++j)
+            c[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(v8bf, A[i]), __builtin_bit_cast(v8bf, Bq[j]), c[i][j], 0, 0, 0);
         }
-        // bf16: one MFMA (K = 32) per fragment, the halves split the rows;
-        // E4M3: two MFMAs (K = 32 each) per fragment, the halves split K.
-        if constexpr (BR == kBF16) {
+      } else {
 #pragma unroll
-          for (int ii = 0; ii < (TM + 1) / 2; ++ii) {
-            const int i = half * ((TM + 1) / 2) + ii;
-            if (i >= TM) break;
+        for (int i = 0; i < TM; ++i) {
+          const long a8 = (long)(((uint64_t)(uint32_t)A[i][2 * half + 1] << 32) | (uint32_t)A[i][2 * half]);
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
-              c[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  __builtin_bit_cast(v8bf, A[i]), __builtin_bit_cast(v8bf, Bq[j]), c[i][j], 0, 0, 0);
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < TM; ++i) {
-            const long a8 = (long)(((uint64_t)(uint32_t)A[i][2 * half + 1] << 32) | (uint32_t)A[i][2 * half]);
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-              const long b8 = (long)(((uint64_t)(uint32_t)Bq[j][2 * half + 1] << 32) | (uint32_t)Bq[j][2 * half]);
-              c2[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a8, b8, c2[i][j], 0, 0, 0);
-            }
+          for (int j = 0; j < TN; ++j) {
+            const long b8 = (long)(((uint64_t)(uint32_t)Bq[j][2 * half + 1] << 32) | (uint32_t)Bq[j][2 * half]);
+            c2[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a8, b8, c2[i][j], 0, 0, 0);
           }
         }
       }
