@@ -173,6 +173,8 @@ def main():
     ap.add_argument("--sweep", action="store_true", help="also time outlier fractions 1/2..1/16")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=128)
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="after timing, copy a buffer of this many bytes (counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -248,6 +250,15 @@ def main():
                 del r
                 torch.cuda.empty_cache()
         out["sweep"] = sweep
+    if args.copy_bytes:
+        # plain device copy of a known size: the reference that scales the
+        # memory-traffic counters of a profiled run to bytes
+        src = torch.empty(args.copy_bytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = args.copy_bytes
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(runs, args.cpu_rows)
     print(json.dumps(out), flush=True)
