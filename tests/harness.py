@@ -69,6 +69,8 @@ def run_layer(sqf, lay, k_out, branch="bf16", x_dtype="bf16", rows=None, check_s
     sqf.sqf_quantize_split_act(xt, mp, acts)
     out = sqf.sqf_dual_gemm(acts, wts, debug=debug)
     y, acc = (out[0], out[1]) if debug else (out, None)
+    # the launch that timing uses (no accumulator dump) is checked as well
+    y_fast = sqf.sqf_dual_gemm(acts, wts) if debug else y
     torch.cuda.synchronize()
     del w, x_cal
     # ---------------- oracle ----------------
@@ -103,5 +105,7 @@ def run_layer(sqf, lay, k_out, branch="bf16", x_dtype="bf16", rows=None, check_s
         ag = acc.cpu().numpy()[rows].astype(np.int64)
         assert np.array_equal(ag, o_acc), "int32 low accumulators differ"
     stats["max_rel_err"] = assert_rows_close(yg, o_y, lay.name)
+    if debug:
+        assert_rows_close(y_fast.cpu().numpy()[rows], o_y, lay.name + " (no debug outputs)")
     stats["rows_checked"] = len(rows)
     return stats, y

@@ -106,6 +106,7 @@ def test_sq_weight_side_full(sqf):
     acts = sqf.alloc_acts(lay.m, k_low, k_out, low="i8", branch="i8")
     sqf.sqf_quantize_split_act(xt, mp, acts)
     y, al, asp, ao = sqf.sqf_dual_gemm(acts, wts, debug=True)
+    y_fast = sqf.sqf_dual_gemm(acts, wts)
     torch.cuda.synchronize()
     o_idx, o_mp, _, o_hd = oracle.select_channels(lay.x_cal, lay.w, k_out)
     assert np.array_equal(mp.cpu().numpy(), o_mp)
@@ -123,4 +124,5 @@ def test_sq_weight_side_full(sqf):
     assert np.array_equal(asp.cpu().numpy()[rows].astype(np.int64), o_asp)
     assert np.array_equal(ao.cpu().numpy()[rows].astype(np.int64), o_ao)
     assert_rows_close(y.cpu().numpy()[rows], o_y, "sq full")
+    assert_rows_close(y_fast.cpu().numpy()[rows], o_y, "sq full (no debug outputs)")
     _log("sq full ok")

@@ -211,8 +211,10 @@ def _grouped_check(sqf, lays, branch, rows_per_group=None):
     acts = sqf.alloc_acts(int(off[-1]), k - k_out, k_out, branch=branch)
     sqf.sqf_quantize_split_act_grouped(xt, row_off, maps_t, acts)
     y, acc = sqf.sqf_dual_gemm_grouped(acts, wts, row_off, debug=True)
+    y_fast = sqf.sqf_dual_gemm_grouped(acts, wts, row_off)
     torch.cuda.synchronize()
     yg, ag = y.cpu().numpy(), acc.cpu().numpy().astype(np.int64)
+    yf = y_fast.cpu().numpy()
     xl, xo = acts.t["x_low"].cpu().numpy(), acts.t["x_out"].cpu().numpy()
     for e, l in enumerate(lays):
         o_idx, o_mp, _, _ = oracle.select_channels(l.x_cal, l.w, k_out)
@@ -231,3 +233,4 @@ def _grouped_check(sqf, lays, branch, rows_per_group=None):
         sel = np.arange(l.m) if rows is None else rows
         assert np.array_equal(ag[r0:r1][sel], o_acc), f"expert {e} accumulators"
         assert_rows_close(yg[r0:r1][sel], o_y, f"expert {e}")
+        assert_rows_close(yf[r0:r1][sel], o_y, f"expert {e} (no debug outputs)")
