@@ -79,16 +79,6 @@ struct DmaLoader {
       off[i] = (uint32_t)(grow * ld + (lane >> 4) * 16);
     }
   }
-  __device__ __forceinline__ void issue(const uint8_t* a, const uint8_t* b, uint32_t stage_off,
-                                        uint8_t* lds_stage) const {
-#pragma unroll
-    for (int i = 0; i < PW; ++i) {
-      const uint8_t* base = (q0 + i) < AFR ? a : b;
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(base + off[i] + stage_off),
-          (__attribute__((address_space(3))) void*)(lds_stage + (q0 + i) * 1024), 16, 0, 0);
-    }
-  }
 };
 
 // s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt bits [3:0] and [15:14]; expcnt and
@@ -97,6 +87,32 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// One 16-byte-per-lane global -> LDS DMA (global_load_lds_dwordx4): lane l's
+// 16 bytes land at LDS byte address lds + 16*l.  Written as a two-instruction
+// asm block rather than the compiler builtin because the builtin is a FLAT
+// instruction that also counts as an LDS access, and while one is outstanding
+// the compiler's wait insertion can only wait for every LDS read at once
+// (lgkmcnt(0)); the ring keeps DMAs outstanding across the whole K loop.  The
+// block has no register outputs; completion is tracked by the explicit vmcnt
+// waits of the ring (wait_vmcnt), and the "memory" clobber keeps the compiler
+// from moving LDS accesses across it.
+__device__ __forceinline__ void dma_16B(const uint8_t* base, uint32_t voff, uint32_t lds) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds);
+  // base: wave-uniform 64-bit address (SGPR pair); voff: per-lane byte offset.
+  // M0 holds the LDS base; one wait state separates its write from the DMA.
+  asm volatile(
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(base), "{m0}"(m0v)
+      : "memory");
+}
+
+// Byte address of a __shared__ object inside the workgroup's LDS.
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
 // Workgroup barrier that does not drain outstanding loads.  __syncthreads()
@@ -139,7 +155,9 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_du
   static_assert(NB * STAGE * OCC <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NB * STAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave index, provably uniform (operand bases and LDS addresses stay scalar)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WGN, wn = wave % WGN;
   const int64_t tiles_n = (p.n + BN - 1) / BN;
 
@@ -201,20 +219,19 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_du
   DmaLoader<BM, BN, NW> ld_lo, ld_br;
   ld_lo.init(wave, lane, m0, m_end, n0, p.n, p.ldk);
   ld_br.init(wave, lane, m0, m_end, n0, p.n, p.ldo_b);
+  const uint32_t smem_lds = lds_offset(smem);
   auto issue = [&](int t) {
     const bool lo = t < S;
     const uint8_t* a = lo ? p.x_low : p.x_out;
     const uint8_t* b = lo ? w_low : w_out;
     const uint32_t so = (uint32_t)(lo ? t : t - S) * 64u;
-    uint8_t* buf = smem + (t % NB) * STAGE;
+    const uint32_t buf = smem_lds + (uint32_t)((t % NB) * STAGE);
 #pragma unroll
     for (int i = 0; i < PW; ++i) {
-      const int q = ld_lo.q0 + i;
+      const int q = ld_lo.q0 + i;  // wave-uniform
       const uint8_t* base = q < DmaLoader<BM, BN, NW>::AFR ? a : b;
       const uint32_t off = lo ? ld_lo.off[i] : ld_br.off[i];
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(base + off + so),
-          (__attribute__((address_space(3))) void*)(buf + q * 1024), 16, 0, 0);
+      dma_16B(base, off + so, buf + (uint32_t)(q * 1024));
     }
   };
 
@@ -228,9 +245,12 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_du
   // stage in two halves.  Between them it waits for stage t+1 to land,
   // crosses the barrier, refills the ring (stage t+NB-1 goes into the buffer
   // of stage t-1, which every wave has finished with) and issues the LDS
-  // reads of stage t+1's B fragments and first A fragment; the second half's
-  // MFMAs then hide that latency.  The rest of stage t+1's A fragments are
-  // read at its start, behind the MFMAs on the prefetched first one.
+  // reads of stage t+1's B fragments and first A fragment into PB / PA0; the
+  // second half's MFMAs then hide that latency.  The rest of stage t+1's A
+  // fragments are read at its start, behind the MFMAs on the prefetched
+  // first one.  The low path widens PB and PA0 completely at the top of a
+  // step, so the registers are free again before mid_sync refills them and
+  // the loop carries them without a copy (and without a wait) at its end.
   v4i PB[TN], PA0;  // prefetched fragments of the next stage
   auto prefetch = [&](int t) {
     const v4i* As = (const v4i*)(smem + (t % NB) * STAGE);
@@ -250,17 +270,33 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_du
     prefetch(t + 1);
   };
   // stage t's A fragments 1.. from LDS (fragment 0 and B were prefetched)
-  auto load_stage = [&](int t, v4i (&A)[TM], v4i (&Bq)[TN]) {
+  auto load_a = [&](int t, v4i (&A)[TM]) {
     const v4i* As = (const v4i*)(smem + (t % NB) * STAGE);
-    A[0] = PA0;
 #pragma unroll
     for (int i = 1; i < TM; ++i) A[i] = As[(wm * TM + i) * 64 + lane];
     // keep the reads at the top of the stage: their latency then overlaps
     // the MFMAs on the prefetched fragments instead of stalling each use
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) Bq[j] = PB[j];
   };
+  // int4 pairs (two dwords = 16 codes) -> 16 * int8 (four dwords)
+  auto widen = [](uint32_t x, uint32_t y) {
+    return v4i{(int)((x << 4) & 0xF0F0F0F0u), (int)(x & 0xF0F0F0F0u),
+               (int)((y << 4) & 0xF0F0F0F0u), (int)(y & 0xF0F0F0F0u)};
+  };
+
+  // The epilogue's arguments are read with scalar loads.  If one of them were
+  // still outstanding during the K loop, the LDS read counter could no longer
+  // be waited on in order and every LDS wait there would become a full
+  // drain, so they are made to land here.
+  {
+    const float* y_ = p.y;
+    const float* sx_ = p.s_x;
+    const float* sxo_ = p.s_xo;
+    int32_t* dbg_ = p.acc_dbg;
+    const int64_t ldy_ = p.ldy, n_ = p.n;
+    asm volatile("" ::"s"(y_), "s"(sx_), "s"(sxo_), "s"(dbg_), "s"(ldy_), "s"(n_), "s"(s_w),
+                 "s"(s_wo));
+  }
 
   // prime the ring
 #pragma unroll
@@ -278,29 +314,30 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_du
 
   // ---------------- low path: int4 x int4 on int8 MFMA ----------------
   for (int t = 0; t < S; ++t) {
-    v4i A[TM], Bq[TN];
-    load_stage(t, A, Bq);
+    v4i A[TM], bw[2][TN], a0w[2];
+    load_a(t, A);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bw[h][j] = widen((uint32_t)PB[j][2 * h], (uint32_t)PB[j][2 * h + 1]);
+      a0w[h] = widen((uint32_t)PA0[2 * h], (uint32_t)PA0[2 * h + 1]);
+    }
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      if (half == 1 && t + 1 < ST) {
+      // unconditional, also on the last stage (the prefetch then reads a
+      // ring buffer whose contents go unused): a conditional refill would
+      // keep the old PB / PA0 alive beside the new ones
+      if (half == 1) {
         mid_sync(t);
         __builtin_amdgcn_sched_barrier(0);
       }
-      v4i bb[TN];
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const uint32_t x = (uint32_t)Bq[j][2 * half], y = (uint32_t)Bq[j][2 * half + 1];
-        bb[j] = v4i{(int)((x << 4) & 0xF0F0F0F0u), (int)(x & 0xF0F0F0F0u),
-                    (int)((y << 4) & 0xF0F0F0F0u), (int)(y & 0xF0F0F0F0u)};
-      }
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        const uint32_t x = (uint32_t)A[i][2 * half], y = (uint32_t)A[i][2 * half + 1];
-        const v4i aa = v4i{(int)((x << 4) & 0xF0F0F0F0u), (int)(x & 0xF0F0F0F0u),
-                           (int)((y << 4) & 0xF0F0F0F0u), (int)(y & 0xF0F0F0F0u)};
+        const v4i aa = i == 0 ? a0w[half]
+                              : widen((uint32_t)A[i][2 * half], (uint32_t)A[i][2 * half + 1]);
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aa, bb[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aa, bw[half][j], acc[i][j], 0, 0, 0);
       }
     }
   }
@@ -341,7 +378,10 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_du
   }
   for (int t = S; t < ST; ++t) {
     v4i A[TM], Bq[TN];
-    load_stage(t, A, Bq);
+    A[0] = PA0;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) Bq[j] = PB[j];
+    load_a(t, A);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       if (half == 1 && t + 1 < ST) {
@@ -366,7 +406,8 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_du
           const long a8 = (long)(((uint64_t)(uint32_t)A[i][2 * half + 1] << 32) | (uint32_t)A[i][2 * half]);
 #pragma unroll
           for (int j = 0; j < TN; ++j) {
-            const long b8 = (long)(((uint64_t)(uint32_t)Bq[j][2 * half + 1] << 32) | (uint32_t)Bq[j][2 * half]);
+            const long b8 =
+                (long)(((uint64_t)(uint32_t)Bq[j][2 * half + 1] << 32) | (uint32_t)Bq[j][2 * half]);
             c2[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a8, b8, c2[i][j], 0, 0, 0);
           }
         }
