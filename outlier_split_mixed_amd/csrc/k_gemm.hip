@@ -23,12 +23,14 @@
 // because it carries its own scales.
 //
 // Tiles.  A block computes BM x BN outputs with WGM x WGN waves; each wave a
-// (TM*16) x (TN*16) sub-tile.  One K stage is 128 bytes of every row (256
-// int4 slots, or 64 bf16, or 128 E4M3).  LDS holds each stage in "fragment
-// order": the 16 bytes lane l feeds to the MFMA for a 16-row block are
-// stored at index (rowblock*2 + f)*64 + l, so every ds_read_b128 of a wave is
-// one contiguous, conflict-free 1 KiB read.  Stages are double buffered with
-// register prefetch.  The block -> tile map is XCD-aware: consecutive
+// (TM*16) x (TN*16) sub-tile.  K advances in 64-byte steps of every operand
+// row (128 int4 slots, 32 bf16 or 64 E4M3), and operands move from global
+// memory to LDS in pairs of steps: one global_load_lds_dwordx4 brings 8 full
+// 128-byte row segments, so every request it makes is a whole cache line
+// (16 half lines per instruction cost markedly more).  LDS holds two pair
+// buffers; the 16-byte chunks of each row are XOR-swizzled on the way in, so
+// that the ds_read_b128 that feeds an MFMA operand (16 rows x one chunk)
+// touches distinct banks.  The block -> tile map is XCD-aware: consecutive
 // hardware block ids go to different XCDs, so they are remapped to give every
 // XCD a contiguous run of logical tiles, then rastered in groups of GROUP_M
 // tile rows to share operand panels in each XCD's L2.
@@ -37,30 +39,23 @@
 
 namespace sqf {
 
-__device__ __forceinline__ void unpack_i4x32(const uint4 q, v4i& lo, v4i& hi) {
-  lo[0] = (int)((q.x << 4) & 0xF0F0F0F0u);
-  lo[1] = (int)(q.x & 0xF0F0F0F0u);
-  lo[2] = (int)((q.y << 4) & 0xF0F0F0F0u);
-  lo[3] = (int)(q.y & 0xF0F0F0F0u);
-  hi[0] = (int)((q.z << 4) & 0xF0F0F0F0u);
-  hi[1] = (int)(q.z & 0xF0F0F0F0u);
-  hi[2] = (int)((q.w << 4) & 0xF0F0F0F0u);
-  hi[3] = (int)(q.w & 0xF0F0F0F0u);
-}
+// Direct global -> LDS loader for one pair of K steps.  A pair buffer holds
+// (BM + BN) / 16 row blocks of 2 KiB: 16 rows x 128 bytes (two steps of 64).
+// Half h of block rb (rows rb*16 + 8h .. +7) is filled by one DMA: lane l
+// brings row 8h + l/8, chunk (l%8) ^ swz(h, l/8) of the 128 bytes, and lands
+// at byte 16*l of that half (LDS offset rb*2048 + h*1024 + 16*l).  Reading it
+// back: chunk C of row R sits at (R/8)*1024 + (R%8)*128 + 16*(C ^ swz(R/8, R%8)).
+// swz(h, r) = r ^ 2h makes the 16 rows x one chunk of an MFMA operand read
+// hit 16 distinct 16-byte bank groups (and any 8 consecutive lanes distinct
+// ones).  Each wave owns PW consecutive halves (A rows first, then B rows).
+__host__ __device__ constexpr int pair_swz(int h, int r) { return r ^ (2 * h); }
 
-// Direct global -> LDS loader.  One stage of a tile is (BM + BN) rows x 64
-// bytes (128 int4 slots, or 32 bf16, or 64 E4M3) = (BM + BN) / 16 fragments
-// of 1 KiB; fragment rb holds, for lane l, the 16 bytes at row rb*16 + l%16,
-// byte (l/16)*16 of the stage.  One global_load_lds_dwordx4 fills one
-// fragment: lane l's 16 bytes land at LDS base + 16*l, which is exactly the
-// order the MFMA operands are read back in.  Each wave owns PW consecutive
-// fragments (A rows first, then B rows).
 template <int BM, int BN, int NW>
 struct DmaLoader {
-  static constexpr int FRAGS = (BM + BN) / 16;
-  static constexpr int PW = FRAGS / NW;
-  static constexpr int AFR = BM / 16;
-  static_assert(FRAGS % NW == 0, "fragments must split evenly over waves");
+  static constexpr int HALVES = (BM + BN) / 8;  // DMAs per pair buffer
+  static constexpr int PW = HALVES / NW;
+  static constexpr int AH = BM / 8;  // halves holding A rows
+  static_assert(HALVES % NW == 0, "DMAs must split evenly over waves");
   uint32_t off[PW];
   int q0;
 
@@ -69,18 +64,17 @@ struct DmaLoader {
     q0 = wave * PW;
 #pragma unroll
     for (int i = 0; i < PW; ++i) {
-      const int q = q0 + i;  // wave-uniform: A fragment if q < AFR
-      const bool is_a = q < AFR;
-      const int ql = is_a ? q : q - AFR;
-      const int r = ql * 16 + (lane & 15);
-      int64_t grow = (is_a ? a_row0 : b_row0) + r;
+      const int q = q0 + i;  // wave-uniform: A rows if q < AH
+      const bool is_a = q < AH;
+      const int ql = is_a ? q : q - AH;  // half index within the operand
+      const int rl = lane >> 3;
+      int64_t grow = (is_a ? a_row0 : b_row0) + ql * 8 + rl;
       const int64_t lim = (is_a ? a_end : b_end) - 1;
       if (grow > lim) grow = lim;
-      off[i] = (uint32_t)(grow * ld + (lane >> 4) * 16);
+      off[i] = (uint32_t)(grow * ld + ((lane & 7) ^ pair_swz(ql & 1, rl)) * 16);
     }
   }
 };
-
 // s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt bits [3:0] and [15:14]; expcnt and
 // lgkmcnt left at their maximum, i.e. not waited on).
 template <int N>
@@ -119,41 +113,27 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
 // carries a workgroup fence, and the fence makes the compiler wait for every
 // outstanding LDS-DMA load (they count as LDS writes), which would cap the
 // ring at one stage in flight.  Here the caller has already waited for the
-// stage it needs (vmcnt), every LDS read of the previous stage has been
-// consumed by an MFMA (so it has completed), and the empty asm statements
-// keep the compiler from moving LDS accesses across the barrier.
+// stage it needs (vmcnt) and for its own LDS reads (lgkmcnt), and the empty
+// asm statements keep the compiler from moving LDS accesses across the
+// barrier.
 __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
 
-// Ring of NB stage buffers: at the top of step s the stages s .. s+NB-2 have
-// been issued; wait for stage s (the newer ones may stay in flight), barrier,
-// then refill the buffer freed by step s-1 with stage s+NB-1.
-template <int NB, int PW>
-__device__ __forceinline__ void ring_wait(int s, int S) {
-  static_assert(NB >= 2 && NB <= 5, "ring depth");
-  const int ahead = (S - 1 - s) < (NB - 2) ? (S - 1 - s) : (NB - 2);
-  if (NB >= 4 && ahead >= 2) wait_vmcnt<2 * PW>();
-  else if (NB >= 3 && ahead >= 1) wait_vmcnt<PW>();
-  else wait_vmcnt<0>();
-  stage_barrier();
-}
-
-// NB: stage ring depth.  OCC: blocks meant to share a CU (sets the register
-// budget so that OCC * WGM * WGN waves fit: 2 waves per SIMD either way).
-template <int BM, int BN, int WGM, int WGN, int NB, int OCC, int BR, bool GROUPED, bool DEBUG,
-          int GROUP_M>
+// OCC: blocks meant to share a CU (sets the register budget so that
+// OCC * WGM * WGN waves fit: 2 waves per SIMD either way).
+template <int BM, int BN, int WGM, int WGN, int OCC, int BR, bool GROUPED, bool DEBUG, int GROUP_M>
 __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_dual_gemm(GemmArgs p) {
   constexpr int NW = WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 16, TN = WN / 16;
-  constexpr int STAGE = (BM + BN) * 64;      // bytes per stage buffer
+  constexpr int PAIR = (BM + BN) * 128;  // bytes per pair buffer
   constexpr int PW = DmaLoader<BM, BN, NW>::PW;
   static_assert(TM >= 1 && TN >= 1, "wave tile too small");
-  static_assert(NB * STAGE * OCC <= 160 * 1024, "LDS budget");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NB * STAGE];
+  static_assert(2 * PAIR * OCC <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(2048))) uint8_t smem[2 * PAIR];
 
   const int tid = threadIdx.x, lane = tid & 63;
   // wave index, provably uniform (operand bases and LDS addresses stay scalar)
@@ -209,30 +189,45 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_du
   const int64_t m0 = m_begin + tm * BM;
   const int64_t n0 = tn * BN;
 
-  // One stage stream: stages 0 .. S-1 are the low path (packed int4, stride
-  // ldk), stages S .. S+SO-1 the branch (stride ldo_b).  Both run through the
-  // same ring, so the branch's first stages are already in flight when the
-  // low path ends and no pipeline restarts between them.
+  // One stream of K steps: steps 0 .. S-1 are the low path (packed int4,
+  // stride ldk), steps S .. S+SO-1 the branch (stride ldo_b).  S and SO are
+  // even (rows are padded to 128 bytes), so a pair never mixes the two, and
+  // both run through the same two pair buffers: the branch's first pair is
+  // already in flight when the low path ends.
   const int S = p.s_low, SO = p.s_out, ST = S + SO;
-  // per-lane row offsets of this wave's fragments for both operand streams
-  // (selected per stage with wave-uniform selects, no control flow)
+  // per-lane row offsets of this wave's DMAs for both operand streams
+  // (selected per pair with wave-uniform selects, no control flow)
   DmaLoader<BM, BN, NW> ld_lo, ld_br;
   ld_lo.init(wave, lane, m0, m_end, n0, p.n, p.ldk);
   ld_br.init(wave, lane, m0, m_end, n0, p.n, p.ldo_b);
   const uint32_t smem_lds = lds_offset(smem);
-  auto issue = [&](int t) {
+  // pair q = steps 2q, 2q+1 -> pair buffer q % 2
+  auto issue = [&](int q) {
+    const int t = 2 * q;
     const bool lo = t < S;
     const uint8_t* a = lo ? p.x_low : p.x_out;
     const uint8_t* b = lo ? w_low : w_out;
     const uint32_t so = (uint32_t)(lo ? t : t - S) * 64u;
-    const uint32_t buf = smem_lds + (uint32_t)((t % NB) * STAGE);
+    const uint32_t buf = smem_lds + (uint32_t)((q & 1) * PAIR);
 #pragma unroll
     for (int i = 0; i < PW; ++i) {
-      const int q = ld_lo.q0 + i;  // wave-uniform
-      const uint8_t* base = q < DmaLoader<BM, BN, NW>::AFR ? a : b;
+      const int h = ld_lo.q0 + i;  // wave-uniform
+      const uint8_t* base = h < DmaLoader<BM, BN, NW>::AH ? a : b;
       const uint32_t off = lo ? ld_lo.off[i] : ld_br.off[i];
-      dma_16B(base, off + so, buf + (uint32_t)(q * 1024));
+      dma_16B(base, off + so, buf + (uint32_t)(h * 1024));
     }
+  };
+  // this lane's read offset inside a 2 KiB row block for step parity `sub`:
+  // row R = lane % 16, chunk C = lane / 16 + 4 * sub
+  uint32_t rd_off[2];
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub) {
+    const int R = lane & 15, C = (lane >> 4) + 4 * sub;
+    rd_off[sub] = (uint32_t)((R >> 3) * 1024 + (R & 7) * 128 + 16 * (C ^ pair_swz(R >> 3, R & 7)));
+  }
+  // the operand fragment of row block rb for step t
+  auto frag = [&](int t, int rb) -> v4i {
+    return *(const v4i*)(smem + ((t >> 1) & 1) * PAIR + rb * 2048 + rd_off[t & 1]);
   };
 
   v4i acc[TM][TN];
@@ -241,40 +236,40 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_du
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
-  // Pipeline.  Stage t lives in ring buffer t % NB.  A step computes its
-  // stage in two halves.  Between them it waits for stage t+1 to land,
-  // crosses the barrier, refills the ring (stage t+NB-1 goes into the buffer
-  // of stage t-1, which every wave has finished with) and issues the LDS
-  // reads of stage t+1's B fragments and first A fragment into PB / PA0; the
-  // second half's MFMAs then hide that latency.  The rest of stage t+1's A
-  // fragments are read at its start, behind the MFMAs on the prefetched
-  // first one.  The low path widens PB and PA0 completely at the top of a
-  // step, so the registers are free again before mid_sync refills them and
-  // the loop carries them without a copy (and without a wait) at its end.
-  v4i PB[TN], PA0;  // prefetched fragments of the next stage
+  // Pipeline.  A step computes its 64 bytes of K in two halves.  Between
+  // them, mid_sync issues the LDS reads of step t+1's B fragments and first A
+  // fragment into PB / PA0 (the second half's MFMAs hide their latency); the
+  // rest of step t+1's A fragments are read at its start, behind the MFMAs on
+  // the prefetched first one.  At the end of a pair (odd t) mid_sync first
+  // waits for the next pair to land, crosses the barrier, and refills the
+  // buffer of the pair just finished (every wave holds all of it in
+  // registers by then) with the pair after next.  The low path widens PB and
+  // PA0 completely at the top of a step, so the registers are free again
+  // before mid_sync refills them and the loop carries them without a copy.
+  v4i PB[TN], PA0;  // prefetched fragments of the next step
   auto prefetch = [&](int t) {
-    const v4i* As = (const v4i*)(smem + (t % NB) * STAGE);
-    const v4i* Bs = As + BM * 4;
 #pragma unroll
-    for (int j = 0; j < TN; ++j) PB[j] = Bs[(wn * TN + j) * 64 + lane];
-    PA0 = As[(wm * TM) * 64 + lane];
+    for (int j = 0; j < TN; ++j) PB[j] = frag(t, BM / 16 + wn * TN + j);
+    PA0 = frag(t, wm * TM);
   };
   auto mid_sync = [&](int t) {
-    // stages t+2 .. t+NB-2 may stay in flight
-    const int ahead = (ST - 2 - t) < (NB - 3) ? (ST - 2 - t) : (NB - 3);
-    if (NB >= 5 && ahead >= 2) wait_vmcnt<2 * PW>();
-    else if (NB >= 4 && ahead >= 1) wait_vmcnt<PW>();
-    else wait_vmcnt<0>();
-    stage_barrier();
-    if (t + NB - 1 < ST) issue(t + NB - 1);
+    if (t & 1) {
+      // only the next pair (t+1, t+2) can be in flight here
+      wait_vmcnt<0>();
+      // every LDS read of this pair has returned (the bf16 branch reads the
+      // second half's fragments before this point but uses them after it)
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      stage_barrier();
+      const int q = (t >> 1) + 2;
+      if (2 * q < ST) issue(q);
+    }
     prefetch(t + 1);
   };
-  // stage t's A fragments 1.. from LDS (fragment 0 and B were prefetched)
+  // step t's A fragments 1.. from LDS (fragment 0 and B were prefetched)
   auto load_a = [&](int t, v4i (&A)[TM]) {
-    const v4i* As = (const v4i*)(smem + (t % NB) * STAGE);
 #pragma unroll
-    for (int i = 1; i < TM; ++i) A[i] = As[(wm * TM + i) * 64 + lane];
-    // keep the reads at the top of the stage: their latency then overlaps
+    for (int i = 1; i < TM; ++i) A[i] = frag(t, wm * TM + i);
+    // keep the reads at the top of the step: their latency then overlaps
     // the MFMAs on the prefetched fragments instead of stalling each use
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -298,19 +293,16 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_du
                  "s"(s_wo));
   }
 
-  // prime the ring
-#pragma unroll
-  for (int t = 0; t < NB - 1; ++t)
-    if (t < ST) issue(t);
-  {
-    const int ahead = (ST - 1) < (NB - 2) ? (ST - 1) : (NB - 2);
-    if (NB >= 5 && ahead >= 3) wait_vmcnt<3 * PW>();
-    else if (NB >= 4 && ahead >= 2) wait_vmcnt<2 * PW>();
-    else if (NB >= 3 && ahead >= 1) wait_vmcnt<PW>();
-    else wait_vmcnt<0>();
-    stage_barrier();
-    prefetch(0);
+  // prime: both pair buffers, wait for the first
+  issue(0);
+  if (ST > 2) {
+    issue(1);
+    wait_vmcnt<PW>();
+  } else {
+    wait_vmcnt<0>();
   }
+  stage_barrier();
+  prefetch(0);
 
   // ---------------- low path: int4 x int4 on int8 MFMA ----------------
   for (int t = 0; t < S; ++t) {
@@ -324,8 +316,8 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_du
     }
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      // unconditional, also on the last stage (the prefetch then reads a
-      // ring buffer whose contents go unused): a conditional refill would
+      // unconditional, also on the last step (the prefetch then reads a
+      // pair buffer whose contents go unused): a conditional refill would
       // keep the old PB / PA0 alive beside the new ones
       if (half == 1) {
         mid_sync(t);
@@ -438,7 +430,7 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_du
 }
 
 // ------------------------------------------------------------------ launch
-template <int BM, int BN, int WGM, int WGN, int NB, int OCC, int BR, bool GROUPED, bool DEBUG>
+template <int BM, int BN, int WGM, int WGN, int OCC, int BR, bool GROUPED, bool DEBUG>
 static hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   int64_t tiles_n = (a.n + BN - 1) / BN;
   int64_t blocks;
@@ -447,31 +439,30 @@ static hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   else
     blocks = ((a.m + BM - 1) / BM) * tiles_n;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((k_dual_gemm<BM, BN, WGM, WGN, NB, OCC, BR, GROUPED, DEBUG, 8>), dim3((unsigned)blocks),
-                     dim3(WGM * WGN * 64), 0, s, a);
+  hipLaunchKernelGGL((k_dual_gemm<BM, BN, WGM, WGN, OCC, BR, GROUPED, DEBUG, 8>),
+                     dim3((unsigned)blocks), dim3(WGM * WGN * 64), 0, s, a);
   return hipGetLastError();
 }
 
 template <int BR, bool GROUPED, bool DEBUG>
 static hipError_t launch_br(const GemmArgs& a, int cfg, hipStream_t s) {
+  // expert groups hold a few hundred rows each: 128x128 tiles only
+  if constexpr (GROUPED) return launch_cfg<128, 128, 2, 2, 2, BR, GROUPED, DEBUG>(a, s);
   // an E4M3 branch keeps a second accumulator set: no 256x256 tile for it
   if (BR == kFP8 && cfg == 0) cfg = 1;
   switch (cfg) {
     case 0:
-      if constexpr (BR != kFP8) return launch_cfg<256, 256, 2, 4, 4, 1, BR, GROUPED, DEBUG>(a, s);
+      if constexpr (BR != kFP8) return launch_cfg<256, 256, 2, 4, 1, BR, GROUPED, DEBUG>(a, s);
       [[fallthrough]];
     case 1:
-      return launch_cfg<128, 128, 2, 2, 4, 2, BR, GROUPED, DEBUG>(a, s);
-    case 3:
-      if constexpr (BR != kFP8) return launch_cfg<256, 128, 2, 2, 3, 2, BR, GROUPED, DEBUG>(a, s);
-      return launch_cfg<128, 128, 2, 2, 4, 2, BR, GROUPED, DEBUG>(a, s);
+      return launch_cfg<128, 128, 2, 2, 2, BR, GROUPED, DEBUG>(a, s);
     default:
-      return launch_cfg<64, 64, 2, 2, 4, 2, BR, GROUPED, DEBUG>(a, s);
+      return launch_cfg<64, 64, 2, 2, 2, BR, GROUPED, DEBUG>(a, s);
   }
 }
 
-// cfg: 0 = 256x256 (8 waves), 1 = 128x128 (4 waves), 2 = 64x64 (4 waves),
-// 3 = 256x128 (4 waves, two blocks per CU).
+// cfg: 0 = 256x256 (8 waves), 1 = 128x128 (4 waves, two blocks per CU),
+// 2 = 64x64 (4 waves, two blocks per CU).
 hipError_t launch_dual_gemm(const GemmArgs& a, int branch, bool grouped, bool debug, int cfg,
                             hipStream_t s) {
   if (branch == kFP8) {

@@ -51,7 +51,7 @@ int pick_cfg(int64_t m, int64_t n, int32_t branch) {
   const char* env = getenv("SQF_GEMM_TILE");
   const int forced = env ? atoi(env) : -1;
   int cfg;
-  if (forced >= 0 && forced <= 4)
+  if (forced >= 0 && forced <= 2)
     cfg = forced;
   else if (((m + 255) / 256) * ((n + 255) / 256) >= 448)
     cfg = 0;

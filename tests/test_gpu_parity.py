@@ -42,7 +42,7 @@ def test_tiny_fp32_input(sqf):
     _print("tiny", st)
 
 
-@pytest.mark.parametrize("tile", ["0", "1", "2", "3"])
+@pytest.mark.parametrize("tile", ["0", "1", "2"])
 def test_ragged_every_tile_config(sqf, tile):
     """M, N and K_low are not multiples of any tile; K_out is not a multiple of 64."""
     lay = _ragged()
