@@ -409,21 +409,51 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_du
 
   // ---------------- epilogue part 2: fuse and store ----------------
   float* y = p.y + m_begin * p.ldy;
+  auto fused = [&](int i, int j, int r, int row, int col) {
+    float v = c[i][j][r];
+    if constexpr (BR == kFP8) v += (p.s_xo[m_begin + row] * s_wo[col]) * c2[i][j][r];
+    return v;
+  };
+  const int wrow0 = (int)(m0 - m_begin) + wm * WM, wcol0 = (int)n0 + wn * WN;
+  const bool whole = wrow0 + WM <= mrows && wcol0 + WN <= ncols && (p.ldy & 3) == 0 &&
+                     (((uintptr_t)p.y) & 15) == 0;
+  if (whole) {
+    // Row-contiguous stores: each 16-row slice of the wave tile goes through
+    // this wave's part of the pair buffer the K loop no longer uses (the one
+    // that held pair NP-2; no DMA targets it any more), padded by 4 floats
+    // per row so that both the 4-byte writes and the 16-byte reads are free
+    // of bank conflicts, and leaves as 16-byte stores of whole row segments.
+    constexpr int LDW = WN + 4;
+    static_assert(NW * 16 * LDW * 4 <= PAIR, "staging fits the free pair buffer");
+    float* stg = (float*)(smem + ((ST >> 1) & 1) * PAIR) + wave * (16 * LDW);
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
+    for (int i = 0; i < TM; ++i) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = row0 + i * 16 + r;
-      if (row >= mrows) continue;
-      float sxo = 0.f;
-      if constexpr (BR == kFP8) sxo = p.s_xo[m_begin + row];
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int col = col0 + j * 16;
-        if (col >= ncols) continue;
-        float v = c[i][j][r];
-        if constexpr (BR == kFP8) v += (sxo * s_wo[col]) * c2[i][j][r];
-        y[(int64_t)row * p.ldy + col] = v;
+        for (int r = 0; r < 4; ++r)
+          stg[((lane >> 4) * 4 + r) * LDW + j * 16 + (lane & 15)] =
+              fused(i, j, r, row0 + i * 16 + r, col0 + j * 16);
+#pragma unroll
+      for (int k = 0; k < WN / 16; ++k) {
+        const int idx = k * 64 + lane, rr = idx / (WN / 4), c4 = idx % (WN / 4);
+        const v4f v = *(const v4f*)(stg + rr * LDW + 4 * c4);
+        *(v4f*)(y + (int64_t)(wrow0 + i * 16 + rr) * p.ldy + wcol0 + 4 * c4) = v;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = row0 + i * 16 + r;
+        if (row >= mrows) continue;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int col = col0 + j * 16;
+          if (col >= ncols) continue;
+          y[(int64_t)row * p.ldy + col] = fused(i, j, r, row, col);
+        }
       }
     }
   }
@@ -446,18 +476,22 @@ static hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
 
 template <int BR, bool GROUPED, bool DEBUG>
 static hipError_t launch_br(const GemmArgs& a, int cfg, hipStream_t s) {
-  // expert groups hold a few hundred rows each: 128x128 tiles only
-  if constexpr (GROUPED) return launch_cfg<128, 128, 2, 2, 2, BR, GROUPED, DEBUG>(a, s);
-  // an E4M3 branch keeps a second accumulator set: no 256x256 tile for it
-  if (BR == kFP8 && cfg == 0) cfg = 1;
-  switch (cfg) {
-    case 0:
-      if constexpr (BR != kFP8) return launch_cfg<256, 256, 2, 4, 1, BR, GROUPED, DEBUG>(a, s);
-      [[fallthrough]];
-    case 1:
-      return launch_cfg<128, 128, 2, 2, 2, BR, GROUPED, DEBUG>(a, s);
-    default:
-      return launch_cfg<64, 64, 2, 2, 2, BR, GROUPED, DEBUG>(a, s);
+  if constexpr (GROUPED) {
+    // expert groups hold a few hundred rows each: 128x128 tiles only
+    (void)cfg;
+    return launch_cfg<128, 128, 2, 2, 2, BR, GROUPED, DEBUG>(a, s);
+  } else {
+    // an E4M3 branch keeps a second accumulator set: no 256x256 tile for it
+    if (BR == kFP8 && cfg == 0) cfg = 1;
+    switch (cfg) {
+      case 0:
+        if constexpr (BR != kFP8) return launch_cfg<256, 256, 2, 4, 1, BR, GROUPED, DEBUG>(a, s);
+        [[fallthrough]];
+      case 1:
+        return launch_cfg<128, 128, 2, 2, 2, BR, GROUPED, DEBUG>(a, s);
+      default:
+        return launch_cfg<64, 64, 2, 2, 2, BR, GROUPED, DEBUG>(a, s);
+    }
   }
 }
 
