@@ -202,9 +202,8 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_du
   ld_br.init(wave, lane, m0, m_end, n0, p.n, p.ldo_b);
   const uint32_t smem_lds = lds_offset(smem);
   // pair q = steps 2q, 2q+1 -> pair buffer q % 2
-  auto issue = [&](int q) {
+  auto issue_from = [&](int q, bool lo) {
     const int t = 2 * q;
-    const bool lo = t < S;
     const uint8_t* a = lo ? p.x_low : p.x_out;
     const uint8_t* b = lo ? w_low : w_out;
     const uint32_t so = (uint32_t)(lo ? t : t - S) * 64u;
@@ -217,6 +216,9 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_du
       dma_16B(base, off + so, buf + (uint32_t)(h * 1024));
     }
   };
+  auto issue = [&](int q) { issue_from(q, 2 * q < S); };
+  // branch pairs only (lets the low path's offsets die after its loop)
+  auto issue_br = [&](int q) { issue_from(q, false); };
   // this lane's read offset inside a 2 KiB row block for step parity `sub`:
   // row R = lane % 16, chunk C = lane / 16 + 4 * sub
   uint32_t rd_off[2];
@@ -368,42 +370,68 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_du
 #pragma unroll
       for (int j = 0; j < TN; ++j) c2[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
   }
-  for (int t = S; t < ST; ++t) {
-    v4i A[TM], Bq[TN];
-    A[0] = PA0;
+  // The branch keeps the whole next step in registers: a bf16 step has half
+  // the MFMA work of an int4 step, too little to hide the LDS reads of its
+  // own A fragments.  CUR holds step t, NXT is read during step t; at the
+  // start of an odd step (the second of a pair) the pair sync runs first, so
+  // the reads of the following pair's first step come after its barrier.
+  auto read_step = [&](int t, v4i (&A)[TM], v4i (&B)[TN]) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j) Bq[j] = PB[j];
-    load_a(t, A);
+    for (int i = 0; i < TM; ++i) A[i] = frag(t, wm * TM + i);
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      if (half == 1 && t + 1 < ST) {
-        mid_sync(t);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // bf16: one MFMA (K = 32) per fragment, the halves split the rows;
-      // E4M3: two MFMAs (K = 32 each) per fragment, the halves split K.
-      if constexpr (BR == kBF16) {
+    for (int j = 0; j < TN; ++j) B[j] = frag(t, BM / 16 + wn * TN + j);
+  };
+  auto br_mfma = [&](const v4i (&A)[TM], const v4i (&B)[TN]) {
+    if constexpr (BR == kBF16) {
 #pragma unroll
-        for (int ii = 0; ii < (TM + 1) / 2; ++ii) {
-          const int i = half * ((TM + 1) / 2) + ii;
-          if (i >= TM) break;
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-          for (int j = 0; j < TN; ++j)
-            c[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(v8bf, A[i]), __builtin_bit_cast(v8bf, Bq[j]), c[i][j], 0, 0, 0);
-        }
-      } else {
+        for (int j = 0; j < TN; ++j)
+          c[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(v8bf, A[i]), __builtin_bit_cast(v8bf, B[j]), c[i][j], 0, 0, 0);
+    } else {
+      // E4M3: two MFMAs (K = 32 each) per 16-byte fragment
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-          const long a8 = (long)(((uint64_t)(uint32_t)A[i][2 * half + 1] << 32) | (uint32_t)A[i][2 * half]);
+          const long a8 = (long)(((uint64_t)(uint32_t)A[i][2 * h + 1] << 32) | (uint32_t)A[i][2 * h]);
 #pragma unroll
           for (int j = 0; j < TN; ++j) {
-            const long b8 =
-                (long)(((uint64_t)(uint32_t)Bq[j][2 * half + 1] << 32) | (uint32_t)Bq[j][2 * half]);
+            const long b8 = (long)(((uint64_t)(uint32_t)B[j][2 * h + 1] << 32) | (uint32_t)B[j][2 * h]);
             c2[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a8, b8, c2[i][j], 0, 0, 0);
           }
         }
+    }
+  };
+  auto br_sync = [&](int t) {
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    stage_barrier();
+    const int q = (t >> 1) + 2;
+    if (2 * q < ST) issue_br(q);
+  };
+  if (S < ST) {
+    // S is even: the branch starts on a pair boundary with step S's B and
+    // first A fragment already prefetched
+    v4i A0[TM], B0[TN], A1[TM], B1[TN];
+    A0[0] = PA0;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) B0[j] = PB[j];
+#pragma unroll
+    for (int i = 1; i < TM; ++i) A0[i] = frag(S, wm * TM + i);
+    for (int t = S; t < ST; t += 2) {
+      // even step t: its successor is in the same pair
+      read_step(t + 1, A1, B1);
+      br_mfma(A0, B0);
+      __builtin_amdgcn_sched_barrier(0);
+      // odd step t+1: sync for the next pair, then read its first step
+      if (t + 2 < ST) {
+        br_sync(t + 1);
+        read_step(t + 2, A0, B0);
       }
+      br_mfma(A1, B1);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
