@@ -7,13 +7,29 @@
 // scattered outlier channels are coalesced online into one dense tensor) and
 // the per-token low-precision activation path of both pages.
 //
-// Memory plan (HBM-bound kernel): each row is read once with 16-byte loads per
-// lane (8 channels); the next row is loaded while the current one is
-// processed.  The channel map is read once per block and condensed to one
-// word per 8-channel chunk.  Codes are scattered into an LDS staging row by
-// slot, then read back in slot order and written with 16-byte stores, so every
-// HBM write is coalesced.  The absmax is a wave max over shuffles followed by
-// a cross-wave max in LDS; block barriers wait for LDS traffic only.
+// Memory plan (HBM-bound kernel): a block owns a row at a time; each lane
+// reads 16 bytes (8 channels, one "chunk") per load and the next row is loaded
+// while the current one is processed.  The channel map is static, so it is
+// condensed once per block into per-chunk constants: the number of low slots
+// before the chunk, the chunk's outlier mask, the absmax mask and two byte-
+// permute selectors that drop the chunk's outlier codes.
+//
+// Arithmetic per chunk:
+//   absmax   |x| of bf16 data is compared as 15-bit integers, two channels per
+//            packed u16 max (integer order equals float order for |x|);
+//   codes    y = fl(x * inv) + 1.5 * 2^23 rounds fl(x * inv) to the nearest
+//            integer, ties to even (the addition's own rounding), and leaves
+//            that integer in the low mantissa bits: the low byte of y's bit
+//            pattern is the two's complement code.  |fl(x * inv)| <= Q(1+2^-23)
+//            because the absmax covers every low channel, so no clamp is
+//            needed;
+//   packing  the code bytes are compacted with byte permutes, nibble-packed
+//            in registers and OR-ed (two LDS atomics per chunk) into a zeroed
+//            LDS image of the packed row at the chunk's slot offset.
+// The image is read back with 16-byte loads, stored coalesced to HBM and
+// re-zeroed.  Two images and two reduction slots alternate between rows, so
+// a row needs two barriers (absmax, image complete); the barriers wait for
+// LDS traffic only, never for the next row's loads.
 #include <cstdlib>
 
 #include "sqf_device.h"
@@ -31,47 +47,83 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// v_perm_b32: byte j of the result is byte sel.byte[j] of the pool {hi, lo}
+// (0..3 = lo's bytes, 4..7 = hi's bytes, 0x0C = zero).
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+constexpr float kRoundMagic = 12582912.0f;  // 1.5 * 2^23
+
+// Bytes of the image row beyond ldk that the OR of a chunk's upper part may
+// touch (always with zero data at the very end of the row).
+constexpr int kImgSlack = 16;
+
 template <int XT, int LOW, int BR, bool GROUPED, int NT, int CPT>
 __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
   extern __shared__ uint8_t sm[];
   constexpr int ESZ = BR == kBF16 ? 2 : 1;
   constexpr int NW = NT / 64;
   constexpr int OPT = 4;  // outlier channels gathered per thread per pass
-  // LDS: [pad_lo + 16] code bytes (the last 16 are a dump slot written by
-  // outlier lanes) | [k_out] int32 outlier channel list | reduction scratch
-  uint8_t* codes = sm;
-  const int dump_lo = (int)p.pad_lo;
-  int32_t* oidx = (int32_t*)(sm + p.pad_lo + 16);
-  float* red = (float*)(sm + p.pad_lo + 16 + ((p.k_out * 4 + 15) & ~(int64_t)15));
+  constexpr int WPC = XT == kBF16 ? 4 : 8;  // raw words per 8-channel chunk
+  const int64_t ldk = p.ldk;
+  const int img_bytes = (int)ldk + kImgSlack;  // a multiple of 16
+  // LDS: image[2][ldk + slack] | outlier channel list int32[k_out] |
+  // reduction slots float[2][2 * NW]
+  uint8_t* img0 = sm;
+  int32_t* oidx = (int32_t*)(sm + 2 * img_bytes);
+  float* red = (float*)(sm + 2 * img_bytes + ((p.k_out * 4 + 15) & ~(int64_t)15));
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const float qlow = LOW == kI4X2 ? 7.0f : 127.0f;
   const float qhi = BR == kFP8 ? 448.0f : 127.0f;
   const int k_out = (int)p.k_out;
 
-  // padding slots are never written by the scatter below: zero them once
-  for (int64_t j = p.k_low + tid; j < p.pad_lo; j += NT) codes[j] = 0;
+  // both images start zeroed
+  for (int j = tid * 16; j < 2 * img_bytes; j += NT * 16) *(uint4*)(img0 + j) = make_uint4(0, 0, 0, 0);
 
-  // One word per 8-channel chunk: (low slots before the chunk) << 8 | mask of
-  // the chunk's outlier channels.  The outlier channel list goes to LDS.
-  uint32_t cw[CPT];
+  // Per-chunk constants (chunk i of this thread = channels 8*(tid + i*NT) ..+7):
+  //   cw   (low slots before the chunk) << 8 | outlier mask (bit e = channel e)
+  //   am   absmax masks: 0x7FFF per low channel's bf16 half, 0 for outliers
+  //   sel  byte-permute selectors taking the low channels' code bytes, in
+  //        order, to bytes 0.. of the compacted pair (zero beyond them)
+  uint32_t cw[CPT], sel0[CPT], sel1[CPT], am[CPT][XT == kBF16 ? 4 : 1];
   auto load_map = [&](int g) {
     const int32_t* mp = p.map + (int64_t)g * p.k;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int64_t c8 = ((int64_t)tid + (int64_t)i * NT) * 8;
-      cw[i] = 0;
+      uint32_t mask = 0xFFu, before = 0;
       if (c8 < p.k) {
         const int4 u0 = *(const int4*)(mp + c8);
         const int4 u1 = *(const int4*)(mp + c8 + 4);
         const int m8[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-        uint32_t mask = 0;
+        mask = 0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           mask |= (m8[e] < 0 ? 1u : 0u) << e;
           if (m8[e] < 0) oidx[-m8[e] - 1] = (int32_t)(c8 + e);
         }
-        const int64_t before = m8[0] >= 0 ? m8[0] : c8 - (-m8[0] - 1);
-        cw[i] = ((uint32_t)before << 8) | mask;
+        before = (uint32_t)(m8[0] >= 0 ? m8[0] : c8 - (-m8[0] - 1));
+      }
+      cw[i] = (before << 8) | mask;
+      uint64_t sel = 0x0C0C0C0C0C0C0C0Cull;
+      int j = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (!((mask >> e) & 1u)) {
+          sel = (sel & ~(0xFFull << (8 * j))) | ((uint64_t)e << (8 * j));
+          ++j;
+        }
+      }
+      sel0[i] = (uint32_t)sel;
+      sel1[i] = (uint32_t)(sel >> 32);
+      if constexpr (XT == kBF16) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          am[i][d] = (((mask >> (2 * d)) & 1u) ? 0u : 0x7FFFu) |
+                     (((mask >> (2 * d + 1)) & 1u) ? 0u : 0x7FFF0000u);
+      } else {
+        am[i][0] = mask;
       }
     }
   };
@@ -80,9 +132,6 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
   int cached_group = -1;
   if constexpr (!GROUPED) load_map(0);
 
-  // raw row words: 4 per chunk for bf16, 8 for fp32; the next row's words are
-  // loaded while the current row is processed
-  constexpr int WPC = XT == kBF16 ? 4 : 8;
   typedef uint32_t v4u __attribute__((ext_vector_type(4)));
   auto load_raw = [&](int64_t row, uint32_t (&r)[CPT][WPC]) {
 #pragma unroll
@@ -102,6 +151,7 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
       }
     }
   };
+  // fp32 value of channel e of chunk i
   auto val = [&](const uint32_t (&r)[CPT][WPC], int i, int e) -> float {
     if constexpr (XT == kBF16) {
       const uint32_t w = r[i][e >> 1];
@@ -116,9 +166,13 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
   };
   uint32_t raw[CPT][WPC], nxt[CPT][WPC];
   if (blockIdx.x < p.m) load_raw(blockIdx.x, raw);
-  lds_barrier();  // outlier list and padding in place
+  lds_barrier();  // outlier list and zeroed images in place
 
-  for (int64_t m = blockIdx.x; m < p.m; m += gridDim.x) {
+  int it = 0;
+  for (int64_t m = blockIdx.x; m < p.m; m += gridDim.x, ++it) {
+    const int buf = it & 1;
+    uint8_t* img = img0 + buf * img_bytes;
+    float* rd = red + buf * 2 * NW;
     if constexpr (GROUPED) {
       int lo = 0, hi = p.groups;  // largest g with row_off[g] <= m
       while (hi - lo > 1) {
@@ -142,20 +196,36 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
       ov[u] = t < k_out ? xval(m, oidx[t]) : 0.0f;
     }
     if (m + gridDim.x < p.m) load_raw(m + gridDim.x, nxt);
-    // Register pressure: the chunk words are constant across rows and the
-    // decoded values are needed twice; without these opaque redefinitions the
+    // Register pressure: the per-chunk constants are row-invariant and the
+    // raw words are read twice; without these opaque redefinitions the
     // compiler keeps every derived value live across the whole loop.
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) asm volatile("" : "+v"(cw[i]));
-    // ---- absmax over the low channels (and the outlier channels) ----
-    float alo = 0.0f, ahi = 0.0f;
-#pragma unroll
     for (int i = 0; i < CPT; ++i) {
+      asm volatile("" : "+v"(cw[i]), "+v"(sel0[i]), "+v"(sel1[i]));
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float t = fabsf(val(raw, i, e));
-        alo = fmaxf(alo, ((cw[i] >> e) & 1u) ? 0.0f : t);
-      }
+      for (int d = 0; d < (XT == kBF16 ? 4 : 1); ++d) asm volatile("" : "+v"(am[i][d]));
+    }
+    // ---- absmax over the low channels (and the outlier channels) ----
+    float alo, ahi = 0.0f;
+    if constexpr (XT == kBF16) {
+      typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+      u16x2 mx = {0, 0};
+#pragma unroll
+      for (int i = 0; i < CPT; ++i)
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, raw[i][d] & am[i][d]));
+      alo = __uint_as_float((uint32_t)(mx[0] > mx[1] ? mx[0] : mx[1]) << 16);
+    } else {
+      uint32_t mx = 0;
+#pragma unroll
+      for (int i = 0; i < CPT; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t t = ((am[i][0] >> e) & 1u) ? 0u : (raw[i][e] & 0x7FFFFFFFu);
+          mx = mx > t ? mx : t;
+        }
+      alo = __uint_as_float(mx);
     }
     if constexpr (BR != kBF16) {
 #pragma unroll
@@ -165,16 +235,16 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
     alo = wave_max(alo);
     if constexpr (BR != kBF16) ahi = wave_max(ahi);
     if (lane == 0) {
-      red[wv] = alo;
-      red[NW + wv] = ahi;
+      rd[wv] = alo;
+      rd[NW + wv] = ahi;
     }
-    lds_barrier();
-    alo = red[0];
-    ahi = red[NW];
+    lds_barrier();  // (A) partial maxima in place
+    alo = rd[0];
+    ahi = rd[NW];
 #pragma unroll
     for (int w = 1; w < NW; ++w) {
-      alo = fmaxf(alo, red[w]);
-      ahi = fmaxf(ahi, red[NW + w]);
+      alo = fmaxf(alo, rd[w]);
+      ahi = fmaxf(ahi, rd[NW + w]);
     }
     const float inv_lo = quant_inv(alo, qlow);
     const float inv_hi = BR == kBF16 ? 0.0f : quant_inv(ahi, qhi);
@@ -207,44 +277,54 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
     for (int i = 0; i < CPT; ++i)
 #pragma unroll
       for (int w = 0; w < WPC; ++w) asm volatile("" : "+v"(raw[i][w]));
-    // ---- low codes -> LDS staging row (outlier lanes write a dump slot) ----
+    // ---- low codes: compacted, packed and OR-ed into the image row ----
+    uint32_t* im = (uint32_t*)img;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int64_t c8 = ((int64_t)tid + (int64_t)i * NT) * 8;
       if (c8 < p.k) {
-        int slot = (int)(cw[i] >> 8);
+        // code byte e = low byte of fl(fl(x_e * inv) + 1.5*2^23); the product
+        // must be rounded on its own (a fused multiply-add would round the
+        // exact product instead and differ at ties)
+        uint32_t y[8];
+        {
+#pragma clang fp contract(off)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const bool out = (cw[i] >> e) & 1u;
-          codes[out ? dump_lo : slot] = (uint8_t)quant_code(val(raw, i, e), inv_lo, qlow);
-          slot += out ? 0 : 1;
+          for (int e = 0; e < 8; ++e) {
+            const float prod = val(raw, i, e) * inv_lo;
+            y[e] = __float_as_uint(prod + kRoundMagic);
+          }
+        }
+        const uint32_t d0 = perm(y[1], y[0], 0x0C0C0400u) | (perm(y[3], y[2], 0x0C0C0400u) << 16);
+        const uint32_t d1 = perm(y[5], y[4], 0x0C0C0400u) | (perm(y[7], y[6], 0x0C0C0400u) << 16);
+        // the low channels' codes, in order, then zero bytes
+        const uint32_t q0 = perm(d1, d0, sel0[i]), q1 = perm(d1, d0, sel1[i]);
+        const uint32_t before = cw[i] >> 8;
+        if constexpr (LOW == kI4X2) {
+          const uint32_t t0 = q0 & 0x0F0F0F0Fu, t1 = q1 & 0x0F0F0F0Fu;
+          const uint32_t u0 = t0 | (t0 >> 4), u1 = t1 | (t1 >> 4);
+          const uint32_t w = perm(u1, u0, 0x06040200u);  // 8 nibbles, slot order
+          const uint64_t v = (uint64_t)w << (4 * (before & 7u));
+          atomicOr(im + (before >> 3), (uint32_t)v);
+          atomicOr(im + (before >> 3) + 1, (uint32_t)(v >> 32));
+        } else {
+          const uint32_t sh = 8 * (before & 3u);
+          const uint64_t lo = (uint64_t)q0 << sh;
+          const uint64_t hi = (uint64_t)q1 << sh;
+          atomicOr(im + (before >> 2), (uint32_t)lo);
+          atomicOr(im + (before >> 2) + 1, (uint32_t)(lo >> 32) | (uint32_t)hi);
+          atomicOr(im + (before >> 2) + 2, (uint32_t)(hi >> 32));
         }
       }
     }
-    lds_barrier();
-    // ---- LDS -> packed HBM rows, 16-byte stores ----
-    const int64_t ngrp = p.ldk / 16;
-    uint8_t* xl = p.x_low + m * p.ldk;
-    for (int64_t q = tid; q < ngrp; q += NT) {
-      uint4 o;
-      if constexpr (LOW == kI4X2) {
-        const uint32_t* src = (const uint32_t*)(codes + q * 32);
-        uint32_t ow[4];
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          uint32_t t0 = src[2 * h] & 0x0F0F0F0Fu, t1 = src[2 * h + 1] & 0x0F0F0F0Fu;
-          uint32_t s0 = t0 | (t0 >> 4), s1 = t1 | (t1 >> 4);
-          uint32_t p0 = (s0 & 0xFFu) | ((s0 >> 8) & 0xFF00u);
-          uint32_t p1 = (s1 & 0xFFu) | ((s1 >> 8) & 0xFF00u);
-          ow[h] = p0 | (p1 << 16);
-        }
-        o = make_uint4(ow[0], ow[1], ow[2], ow[3]);
-      } else {
-        o = *(const uint4*)(codes + q * 16);
-      }
-      *(uint4*)(xl + q * 16) = o;
+    lds_barrier();  // (B) the image row is complete
+    // ---- image -> packed HBM row (16-byte stores), then re-zero it ----
+    uint8_t* xl = p.x_low + m * ldk;
+    for (int64_t q = tid; q < ldk / 16; q += NT) {
+      *(uint4*)(xl + q * 16) = *(const uint4*)(img + q * 16);
+      *(uint4*)(img + q * 16) = make_uint4(0, 0, 0, 0);
     }
-    lds_barrier();
+    if (tid == 0) *(uint4*)(img + ldk) = make_uint4(0, 0, 0, 0);  // slack
 #pragma unroll
     for (int i = 0; i < CPT; ++i)
 #pragma unroll
@@ -282,9 +362,13 @@ static hipError_t launch_br(const ActArgs& a, int br, int64_t grid, size_t lds, 
   return launch_shape<XT, LOW, kI8, GROUPED>(a, grid, lds, s);
 }
 
+size_t act_split_lds_bytes(int64_t ldk, int64_t k_out) {
+  return (size_t)(2 * (ldk + kImgSlack) + ((k_out * 4 + 15) & ~(int64_t)15) + 2 * 2 * 16 * sizeof(float));
+}
+
 hipError_t launch_act_split(const ActArgs& a, int x_dtype, int low, int branch, bool grouped,
                             hipStream_t s) {
-  size_t lds = (size_t)(a.pad_lo + 16 + ((a.k_out * 4 + 15) & ~(int64_t)15)) + 2 * 16 * sizeof(float);
+  const size_t lds = act_split_lds_bytes(a.ldk, a.k_out);
   // rows per block: SQF_ACT_GRID overrides the grid size (tuning aid)
   const char* env = getenv("SQF_ACT_GRID");
   const int64_t cap = env ? atoll(env) : 1024;

@@ -159,7 +159,7 @@ sqf_status quantize_common(const void* x, int32_t x_dtype, int64_t ldx, int64_t 
   if (k % 8 != 0 || k > 65536)
     return fail(SQF_ERR_SHAPE, "%s: k=%lld must be a multiple of 8 and <= 65536", who,
                 (long long)k);
-  if (sqf_pad_k_low(a->k_low) + 16 + (a->k_out * 4 + 15) / 16 * 16 + 128 > 160 * 1024)
+  if (sqf::act_split_lds_bytes(a->ldk, a->k_out) > 160 * 1024)
     return fail(SQF_ERR_SHAPE, "%s: k_low=%lld, k_out=%lld exceed the kernel's LDS staging", who,
                 (long long)a->k_low, (long long)a->k_out);
   if (ldx < k || ldx % 8 != 0)

@@ -76,6 +76,8 @@ hipError_t launch_select(const float* x_cal, int64_t m_cal, int64_t k, const flo
 hipError_t launch_pack(const PackArgs& a, int branch, int groups, hipStream_t s);
 hipError_t launch_act_split(const ActArgs& a, int x_dtype, int low, int branch, bool grouped,
                             hipStream_t s);
+// dynamic LDS bytes the activation kernel needs for one block
+size_t act_split_lds_bytes(int64_t ldk, int64_t k_out);
 // cfg: 0 = 256x256 tiles (8 waves), 1 = 128x128 (4 waves), 2 = 64x64 (4 waves)
 hipError_t launch_dual_gemm(const GemmArgs& a, int branch, bool grouped, bool debug, int cfg,
                             hipStream_t s);
