@@ -333,8 +333,13 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
 }
 
 template <int XT, int LOW, int BR, bool GROUPED, int NT, int CPT>
-static hipError_t launch_one(const ActArgs& a, int64_t grid, size_t lds, hipStream_t s) {
+static hipError_t launch_one(const ActArgs& a, int64_t cap, size_t lds, hipStream_t s) {
   auto kern = k_act_split<XT, LOW, BR, GROUPED, NT, CPT>;
+  // about 16 waves per CU over the 256 CUs; each block walks a strided set
+  // of rows, so the per-block setup (the channel map) is amortised
+  int64_t grid = (int64_t)256 * 16 * 64 / NT;
+  if (cap > 0) grid = cap;
+  if (grid > a.m) grid = a.m;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)lds);
@@ -345,21 +350,21 @@ static hipError_t launch_one(const ActArgs& a, int64_t grid, size_t lds, hipStre
 }
 
 template <int XT, int LOW, int BR, bool GROUPED>
-static hipError_t launch_shape(const ActArgs& a, int64_t grid, size_t lds, hipStream_t s) {
+static hipError_t launch_shape(const ActArgs& a, int64_t cap, size_t lds, hipStream_t s) {
   const int64_t chunks = a.k / 8;
-  if (chunks <= 256) return launch_one<XT, LOW, BR, GROUPED, 256, 1>(a, grid, lds, s);
-  if (chunks <= 512) return launch_one<XT, LOW, BR, GROUPED, 256, 2>(a, grid, lds, s);
-  if (chunks <= 1024) return launch_one<XT, LOW, BR, GROUPED, 256, 4>(a, grid, lds, s);
-  if (chunks <= 2048) return launch_one<XT, LOW, BR, GROUPED, 512, 4>(a, grid, lds, s);
-  if (chunks <= 4096) return launch_one<XT, LOW, BR, GROUPED, 1024, 4>(a, grid, lds, s);
-  return launch_one<XT, LOW, BR, GROUPED, 1024, 8>(a, grid, lds, s);
+  if (chunks <= 256) return launch_one<XT, LOW, BR, GROUPED, 256, 1>(a, cap, lds, s);
+  if (chunks <= 512) return launch_one<XT, LOW, BR, GROUPED, 256, 2>(a, cap, lds, s);
+  if (chunks <= 1024) return launch_one<XT, LOW, BR, GROUPED, 256, 4>(a, cap, lds, s);
+  if (chunks <= 2048) return launch_one<XT, LOW, BR, GROUPED, 512, 4>(a, cap, lds, s);
+  if (chunks <= 4096) return launch_one<XT, LOW, BR, GROUPED, 1024, 4>(a, cap, lds, s);
+  return launch_one<XT, LOW, BR, GROUPED, 1024, 8>(a, cap, lds, s);
 }
 
 template <int XT, int LOW, bool GROUPED>
-static hipError_t launch_br(const ActArgs& a, int br, int64_t grid, size_t lds, hipStream_t s) {
-  if (br == kBF16) return launch_shape<XT, LOW, kBF16, GROUPED>(a, grid, lds, s);
-  if (br == kFP8) return launch_shape<XT, LOW, kFP8, GROUPED>(a, grid, lds, s);
-  return launch_shape<XT, LOW, kI8, GROUPED>(a, grid, lds, s);
+static hipError_t launch_br(const ActArgs& a, int br, int64_t cap, size_t lds, hipStream_t s) {
+  if (br == kBF16) return launch_shape<XT, LOW, kBF16, GROUPED>(a, cap, lds, s);
+  if (br == kFP8) return launch_shape<XT, LOW, kFP8, GROUPED>(a, cap, lds, s);
+  return launch_shape<XT, LOW, kI8, GROUPED>(a, cap, lds, s);
 }
 
 size_t act_split_lds_bytes(int64_t ldk, int64_t k_out) {
@@ -369,23 +374,22 @@ size_t act_split_lds_bytes(int64_t ldk, int64_t k_out) {
 hipError_t launch_act_split(const ActArgs& a, int x_dtype, int low, int branch, bool grouped,
                             hipStream_t s) {
   const size_t lds = act_split_lds_bytes(a.ldk, a.k_out);
-  // rows per block: SQF_ACT_GRID overrides the grid size (tuning aid)
+  // SQF_ACT_GRID overrides the number of blocks (tuning aid)
   const char* env = getenv("SQF_ACT_GRID");
-  const int64_t cap = env ? atoll(env) : 1024;
-  int64_t grid = a.m < cap ? a.m : cap;
-  if (grid <= 0) return hipSuccess;
+  const int64_t cap = env ? atoll(env) : 0;
+  if (a.m <= 0) return hipSuccess;
   if (x_dtype == kBF16) {
     if (low == kI4X2)
-      return grouped ? launch_br<kBF16, kI4X2, true>(a, branch, grid, lds, s)
-                     : launch_br<kBF16, kI4X2, false>(a, branch, grid, lds, s);
-    return grouped ? launch_br<kBF16, kI8, true>(a, branch, grid, lds, s)
-                   : launch_br<kBF16, kI8, false>(a, branch, grid, lds, s);
+      return grouped ? launch_br<kBF16, kI4X2, true>(a, branch, cap, lds, s)
+                     : launch_br<kBF16, kI4X2, false>(a, branch, cap, lds, s);
+    return grouped ? launch_br<kBF16, kI8, true>(a, branch, cap, lds, s)
+                   : launch_br<kBF16, kI8, false>(a, branch, cap, lds, s);
   }
   if (low == kI4X2)
-    return grouped ? launch_br<kF32, kI4X2, true>(a, branch, grid, lds, s)
-                   : launch_br<kF32, kI4X2, false>(a, branch, grid, lds, s);
-  return grouped ? launch_br<kF32, kI8, true>(a, branch, grid, lds, s)
-                 : launch_br<kF32, kI8, false>(a, branch, grid, lds, s);
+    return grouped ? launch_br<kF32, kI4X2, true>(a, branch, cap, lds, s)
+                   : launch_br<kF32, kI4X2, false>(a, branch, cap, lds, s);
+  return grouped ? launch_br<kF32, kI8, true>(a, branch, cap, lds, s)
+                 : launch_br<kF32, kI8, false>(a, branch, cap, lds, s);
 }
 
 }  // namespace sqf
