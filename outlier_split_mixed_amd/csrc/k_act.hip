@@ -164,12 +164,29 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
     if constexpr (XT == kBF16) return __uint_as_float((uint32_t)((const uint16_t*)p.x)[row * p.ldx + c] << 16);
     else return ((const float*)p.x)[row * p.ldx + c];
   };
-  uint32_t raw[CPT][WPC], nxt[CPT][WPC];
-  if (blockIdx.x < p.m) load_raw(blockIdx.x, raw);
+  // Rows of a block: a strided set (one map for all rows), or, for expert
+  // groups, a contiguous run, so that the group (and its map) rarely changes
+  // between consecutive rows of a block.
+  int64_t m_first = blockIdx.x, m_stop = p.m, m_step = gridDim.x;
+  if constexpr (GROUPED) {
+    const int64_t per = (p.m + gridDim.x - 1) / gridDim.x;
+    m_first = (int64_t)blockIdx.x * per;
+    m_stop = m_first + per < p.m ? m_first + per : p.m;
+    m_step = 1;
+  }
+  // rows in flight ahead of the current one: enough bytes per thread to hide
+  // HBM latency when a row is only a few chunks per thread
+  constexpr int PF = CPT >= 4 ? 1 : 4 / CPT;
+  // ring of PF + 1 row buffers; the row loop below is unrolled PF + 1 times so
+  // that every buffer index is static (no register moves, which would wait
+  // for the loads still in flight)
+  uint32_t ring[PF + 1][CPT][WPC];
+#pragma unroll
+  for (int f = 0; f < PF; ++f)
+    if (m_first + f * m_step < m_stop) load_raw(m_first + f * m_step, ring[f]);
   lds_barrier();  // outlier list and zeroed images in place
 
-  int it = 0;
-  for (int64_t m = blockIdx.x; m < p.m; m += gridDim.x, ++it) {
+  auto row_body = [&](int64_t m, int it, uint32_t (&raw)[CPT][WPC]) {
     const int buf = it & 1;
     uint8_t* img = img0 + buf * img_bytes;
     float* rd = red + buf * 2 * NW;
@@ -195,7 +212,6 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
       const int t = tid + u * NT;
       ov[u] = t < k_out ? xval(m, oidx[t]) : 0.0f;
     }
-    if (m + gridDim.x < p.m) load_raw(m + gridDim.x, nxt);
     // Register pressure: the per-chunk constants are row-invariant and the
     // raw words are read twice; without these opaque redefinitions the
     // compiler keeps every derived value live across the whole loop.
@@ -325,10 +341,19 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
       *(uint4*)(img + q * 16) = make_uint4(0, 0, 0, 0);
     }
     if (tid == 0) *(uint4*)(img + ldk) = make_uint4(0, 0, 0, 0);  // slack
+  };
+
+  int it = 0;
+  for (int64_t m = m_first; m < m_stop;) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i)
-#pragma unroll
-      for (int w = 0; w < WPC; ++w) raw[i][w] = nxt[i][w];
+    for (int u = 0; u <= PF; ++u) {
+      if (m >= m_stop) break;
+      // refill the buffer the previous row used with the row PF ahead
+      if (m + PF * m_step < m_stop) load_raw(m + PF * m_step, ring[(u + PF) % (PF + 1)]);
+      row_body(m, it, ring[u]);
+      m += m_step;
+      ++it;
+    }
   }
 }
 
@@ -352,6 +377,7 @@ static hipError_t launch_one(const ActArgs& a, int64_t cap, size_t lds, hipStrea
 template <int XT, int LOW, int BR, bool GROUPED>
 static hipError_t launch_shape(const ActArgs& a, int64_t cap, size_t lds, hipStream_t s) {
   const int64_t chunks = a.k / 8;
+  if (chunks <= 128) return launch_one<XT, LOW, BR, GROUPED, 128, 1>(a, cap, lds, s);
   if (chunks <= 256) return launch_one<XT, LOW, BR, GROUPED, 256, 1>(a, cap, lds, s);
   if (chunks <= 512) return launch_one<XT, LOW, BR, GROUPED, 256, 2>(a, cap, lds, s);
   if (chunks <= 1024) return launch_one<XT, LOW, BR, GROUPED, 256, 4>(a, cap, lds, s);

@@ -42,6 +42,15 @@ def test_tiny_fp32_input(sqf):
     _print("tiny", st)
 
 
+@pytest.mark.parametrize("k", [512, 40960])
+def test_row_width_extremes(sqf, k):
+    """The narrowest and widest rows the activation kernel lays out differently
+    (one 8-channel chunk per thread, and eight), ragged M and N."""
+    lay = synth.draw_layer("wide", 1010, k, 37, k, 72, 96, k // 16)
+    st, _ = run_layer(sqf, lay, lay.k_out)
+    _print("row width", k, st)
+
+
 @pytest.mark.parametrize("tile", ["0", "1", "2"])
 def test_ragged_every_tile_config(sqf, tile):
     """M, N and K_low are not multiples of any tile; K_out is not a multiple of 64."""
