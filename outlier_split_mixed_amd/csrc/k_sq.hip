@@ -9,36 +9,125 @@
 //   acc_sp [m,n] = sum_i qx[m,pos_i(n)] * v8[n,i]   (i-th marked slot of row n)
 //   acc_o  [m,n] = sum_t xo[m,t] * wo[n,t]          (int8 outlier-channel branch)
 //   y = s_x*(s_w4*acc_low + s_w8*acc_sp) + s_xo*s_wo*acc_o
-// Activations are int8 per token.  The "gather unit" is realised while a
-// stage of W is staged into LDS: each packed 16-byte piece of a row is
-// decoded into an int8 low tile (marks -> 0) and a dense int8 tile holding the
-// row's sparse values at their marked slots (0 elsewhere).  The index of a
-// marked slot's value is the row's mark count before the stage (precomputed
-// per 256-slot tile) plus the count before it inside the stage, found with a
-// shuffle scan across the 8 lanes that share the row.  Both tiles then feed
-// v_mfma_i32_16x16x64_i8 with the same A fragment.
+//
+// gfx950 mapping.  The "gather unit" is the decode of each K stage of W into
+// LDS, done once per block: a 128-slot stage of a W row becomes
+//   * an int4 low tile with the marks cleared to 0 (SWAR: a nibble is the
+//     mark iff its top bit is set and its low three bits are zero), widened
+//     to int8 at MFMA time with the x16 trick (w << 4 & 0xF0.. and
+//     w & 0xF0..), which puts a group of 8 slots in the order 0,2,4,6,1,3,5,7;
+//   * an int8 tile holding the row's sparse values at their marked slots
+//     (zero elsewhere), in that same slot order.  Only the marked slots (1/8)
+//     are written: a lane walks the marks of its 64 slots with find-first-set
+//     and copies each value from the row's value window, which was fetched
+//     into LDS with the stage (the row's running value index is carried from
+//     stage to stage, so the window is known before the stage is decoded).
+// The int8 activations are written to LDS with the same slot permutation, so
+// both tiles feed v_mfma_i32_16x16x64_i8 with one A fragment.  The low
+// accumulator carries the x16 factor (|acc| <= 16*127*7*k_low < 2^31 for the
+// k_low the host accepts); it is removed exactly in the epilogue.  Global
+// loads of stage s+1 are issued right after stage s is in LDS, so their
+// latency hides behind stage s's MFMAs; two blocks share a CU.
 #include "sqf_device.h"
 #include "sqf_launch.h"
 
 namespace sqf {
 
-__device__ __forceinline__ int lds_frag_idx(int r, int f, int g) {
-  return ((r >> 4) * 4 + f) * 64 + g * 16 + (r & 15);
+namespace {
+
+// LDS barrier that does not wait for outstanding global loads.
+__device__ __forceinline__ void lds_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// byte position, inside a lane's 16-byte MFMA operand, of slot k (0..15) in
+// the widened order 0,2,4,6,1,3,5,7 | 8,10,12,14,9,11,13,15
+__device__ __forceinline__ int perm_pos(int k) {
+  return (k & 8) + ((k & 1) ? 4 + ((k & 7) >> 1) : ((k & 7) >> 1));
+}
+
+}  // namespace
+
 template <bool DEBUG>
-__global__ __launch_bounds__(256) void k_sq_gemm(SqArgs p) {
+__global__ __launch_bounds__(256, 2) void k_sq_gemm(SqArgs p) {
   constexpr int BM = 128, BN = 128, TM = 4, TN = 4;
-  __shared__ uint4 sA[BM * 16];
-  __shared__ uint4 sL[BN * 16];
-  __shared__ uint4 sS[BN * 16];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // stage = 128 low slots: A 128 B / row, W 64 B / row
+  __shared__ uint4 sA[BM * 8];            // [rb][f][lane] x 16 B (permuted slot order)
+  __shared__ uint2 sL[BN * 8];            // [rb][f][lane] x 8 B (clean int4)
+  __shared__ uint4 sS[BN * 8];            // [rb][f][lane] x 16 B (values at marks)
+  __shared__ __attribute__((aligned(16))) uint8_t sV[BN * 64 + 16];  // value windows (+ read slack)
+  __shared__ uint2 sSel[256];  // expand selectors per 8-slot mark mask
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int64_t tiles_n = (p.n + BN - 1) / BN;
-  const int64_t tm = blockIdx.x % ((p.m + BM - 1) / BM), tn = blockIdx.x / ((p.m + BM - 1) / BM);
-  if (tn >= tiles_n) return;
+  const int64_t tiles_m = (p.m + BM - 1) / BM;
+  const int64_t tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
+  if (tn * BN >= p.n) return;
   const int64_t m0 = tm * BM, n0 = tn * BN;
-  const int64_t ntile1 = p.ldkw / 128 + 1;
+  const int nst = (int)(p.ldkw / 64);  // 128-slot stages (ldkw is a multiple of 128)
+
+  // this thread's share of a stage: row r (of A and of W), half h = K64 chunk
+  const int r = tid >> 1, h = tid & 1;
+  const int64_t ga = (m0 + r < p.m ? m0 + r : p.m - 1);
+  const int64_t gn = (n0 + r < p.n ? n0 + r : p.n - 1);
+  const uint8_t* arow = p.x_low + ga * p.ldkx + h * 64;
+  const uint8_t* wrow = p.w_low + gn * p.ldkw + h * 32;
+  const int8_t* vrow = p.sq_val + gn * p.nnz;
+  const int64_t vtotal = p.n * p.nnz;  // bytes in the value buffer
+  // byte offset of the buffer start past the previous 16-byte boundary
+  const int vmis = (int)((uintptr_t)p.sq_val & 15);
+  const int rb = r >> 4, rr = r & 15;
+
+  // Expand selectors: for the mark mask m of an 8-slot group, byte p of the
+  // group's operand bytes (slot order 0,2,4,6,1,3,5,7) takes value number
+  // rank(slot) (a byte of the pool {hi, lo} of the group's values) if the
+  // slot is marked, else zero (selector 0x0C).
+  {
+    const int m = tid;  // 256 threads, 256 masks
+    uint32_t sel[2] = {0, 0};
+#pragma unroll
+    for (int pp = 0; pp < 8; ++pp) {
+      const int sl = pp < 4 ? 2 * pp : 2 * (pp - 4) + 1;
+      const uint32_t b = ((m >> sl) & 1) ? (uint32_t)__builtin_popcount(m & ((1 << sl) - 1)) : 0x0Cu;
+      sel[pp >> 2] |= b << (8 * (pp & 3));
+    }
+    sSel[m] = make_uint2(sel[0], sel[1]);
+    if (tid < 4) ((uint32_t*)(sV + BN * 64))[tid] = 0;
+    lds_sync();
+  }
+
+  // prefetched global data of one stage
+  uint4 ra[4], rw[2], rv[2];
+  int vi = 0;         // row r's value index at the current stage
+  int win_valid = 0;  // bytes of the fetched window that lie inside the buffer
+  int64_t win_lo = 0; // buffer offset of the window's first byte (may be < 0)
+  auto fetch = [&](int s) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ra[q] = *(const uint4*)(arow + s * 128 + q * 16);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) rw[q] = *(const uint4*)(wrow + s * 64 + q * 16);
+    // value window [win_lo, win_lo + 64) (16-byte aligned addresses) holding
+    // row r's values from vi on; this lane brings its half (32 bytes)
+    const int64_t a0 = gn * p.nnz + vi;
+    win_lo = ((a0 + vmis) & ~(int64_t)15) - vmis;
+    // whole 16-byte blocks inside the buffer (the rest is read byte by byte)
+    const int64_t room = vtotal - win_lo;
+    win_valid = room > 0 ? (int)(room < 64 ? room : 64) & ~15 : 0;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int off = h * 32 + q * 16;
+      rv[q] = (off + 16 <= win_valid && win_lo + off >= 0)
+                  ? *(const uint4*)(p.sq_val + win_lo + off) : make_uint4(0, 0, 0, 0);
+    }
+  };
 
   v4i acc[TM][TN], acs[TM][TN];
 #pragma unroll
@@ -46,120 +135,143 @@ __global__ __launch_bounds__(256) void k_sq_gemm(SqArgs p) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = acs[i][j] = v4i{0, 0, 0, 0};
 
-  for (int s = 0; s < p.s_low; ++s) {
-    // A: 128 rows x 256 bytes, fragment order (4 K64 chunks per stage)
+  if (nst > 0) fetch(0);
+  for (int s = 0; s < nst; ++s) {
+    // ---- A: 64 bytes (chunk h of row r) in the widened slot order ----
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      int e = tid + i * 256, r = e >> 4, pc = e & 15;
-      int64_t gr = m0 + r < p.m ? m0 + r : p.m - 1;
-      sA[lds_frag_idx(r, pc >> 2, pc & 3)] = *(const uint4*)(p.x_low + gr * p.ldkx + s * 256 + pc * 16);
+    for (int g = 0; g < 4; ++g) {
+      const uint4 u = ra[g];
+      sA[(rb * 2 + h) * 64 + g * 16 + rr] =
+          make_uint4(perm(u.y, u.x, 0x06040200u), perm(u.y, u.x, 0x07050301u),
+                     perm(u.w, u.z, 0x06040200u), perm(u.w, u.z, 0x07050301u));
     }
-    // W: 128 rows x 128 packed bytes -> low tile + sparse tile
+    // ---- value window of row r ----
+    *(uint4*)(sV + r * 64 + h * 32) = rv[0];
+    *(uint4*)(sV + r * 64 + h * 32 + 16) = rv[1];
+    // ---- W: 64 slots (chunk h of row r): clean low tile, marks ----
+    uint32_t wd[8], mk[8];
+    int cnt = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int e = tid + i * 256, r = e >> 3, pc = e & 7;
-      int64_t gn = n0 + r < p.n ? n0 + r : p.n - 1;
-      uint4 q = *(const uint4*)(p.w_low + gn * p.ldkw + s * 128 + pc * 16);
-      uint32_t qw[4] = {q.x, q.y, q.z, q.w};
-      int marks = 0;
+    for (int q = 0; q < 2; ++q) {
+      const uint32_t d4[4] = {rw[q].x, rw[q].y, rw[q].z, rw[q].w};
 #pragma unroll
-      for (int h = 0; h < 4; ++h)
-#pragma unroll
-        for (int b = 0; b < 8; ++b) marks += ((qw[h] >> (4 * b)) & 0xF) == 0x8;
-      int incl = marks;  // inclusive scan across the 8 lanes of this row
-#pragma unroll
-      for (int off = 1; off < 8; off <<= 1) {
-        int t = __shfl_up(incl, off, 8);
-        if ((lane & 7) >= off) incl += t;
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t x = d4[e];
+        const uint32_t nz = ((x & 0x77777777u) + 0x77777777u) & 0x88888888u;
+        const uint32_t m8 = x & 0x88888888u & ~nz;  // bit 3 of each marked nibble
+        mk[q * 4 + e] = m8;
+        wd[q * 4 + e] = x & ~((m8 - (m8 >> 3)) | m8);
+        cnt += __builtin_popcount(m8);
       }
-      int vi = p.tile_off[gn * ntile1 + s] + incl - marks;
-      const int8_t* vals = p.sq_val + gn * p.nnz;
-      uint32_t lo[8], sp[8];
-#pragma unroll
-      for (int h = 0; h < 8; ++h) lo[h] = sp[h] = 0;
-#pragma unroll
-      for (int h = 0; h < 4; ++h)
-#pragma unroll
-        for (int b = 0; b < 8; ++b) {
-          uint32_t nib = (qw[h] >> (4 * b)) & 0xF;
-          int slot = h * 8 + b;  // 0..31 inside the piece
-          uint32_t lb, sb = 0;
-          if (nib == 0x8) {
-            lb = 0;
-            sb = vi < p.nnz ? (uint8_t)vals[vi] : 0u;  // marks beyond nnz: malformed input
-            ++vi;
-          } else {
-            lb = (uint8_t)(int8_t)((int)(nib << 28) >> 28);
-          }
-          lo[slot >> 2] |= lb << ((slot & 3) * 8);
-          sp[slot >> 2] |= sb << ((slot & 3) * 8);
-        }
-      // slots 32*pc .. +31 of the stage: K64 chunk f = pc/2, byte groups g, g+1
-      int f = pc >> 1, g = (pc & 1) * 2;
-      sL[lds_frag_idx(r, f, g)] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-      sL[lds_frag_idx(r, f, g + 1)] = make_uint4(lo[4], lo[5], lo[6], lo[7]);
-      sS[lds_frag_idx(r, f, g)] = make_uint4(sp[0], sp[1], sp[2], sp[3]);
-      sS[lds_frag_idx(r, f, g + 1)] = make_uint4(sp[4], sp[5], sp[6], sp[7]);
     }
-    __syncthreads();
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      v4i bl[TN], bs[TN];
+    for (int g = 0; g < 4; ++g)
+      sL[(rb * 2 + h) * 64 + g * 16 + rr] = make_uint2(wd[2 * g], wd[2 * g + 1]);
+    uint4* srow = sS + (rb * 2 + h) * 64 + rr;  // this lane's sparse-tile bytes
+    // marks of the first half of the row precede this lane's (partner lane ^ 1)
+    const int cnt_other = __shfl_xor(cnt, 1, 64);
+    const int v0 = vi + (h ? cnt_other : 0);         // value index of this lane's first mark
+    const int wo0 = (int)(gn * p.nnz + v0 - win_lo);  // its offset in the value window
+    // ---- sparse tile: every 8-slot group expanded from its values at once ----
+    {
+      const uint32_t* vw = (const uint32_t*)sV;
+      int pre = 0;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        // byte offset of the group's first value; past the row's window the
+        // bytes are not used (those lanes take the path below), so the read
+        // only has to stay inside the array
+        const int off = min(r * 64 + wo0 + pre, r * 64 + 64);
+        const uint32_t d0 = vw[off >> 2], d1 = vw[(off >> 2) + 1], d2 = vw[(off >> 2) + 2];
+        const uint32_t lo = __builtin_amdgcn_alignbyte(d1, d0, off & 3);
+        const uint32_t hi = __builtin_amdgcn_alignbyte(d2, d1, off & 3);
+        uint32_t x = mk[d] >> 3;  // mark bits at 4i -> bit i
+        x = (x | (x >> 3)) & 0x03030303u;
+        x = (x | (x >> 6)) & 0x000F000Fu;
+        x = (x | (x >> 12)) & 0xFFu;
+        const uint2 sl = sSel[x];
+        *(uint2*)((uint8_t*)(srow + (d >> 1) * 16) + (d & 1) * 8) = make_uint2(perm(hi, lo, sl.x), perm(hi, lo, sl.y));
+        pre += __builtin_popcount(mk[d]);
+      }
+    }
+    // rare: values beyond the window (or more marks than values) -> one by one
+    if (wo0 + cnt > win_valid || v0 + cnt > p.nnz) {
+      int j = 0;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        uint32_t m8 = mk[d];
+        while (m8) {
+          const int k = d * 8 + (__builtin_ctz(m8) >> 2);
+          m8 &= m8 - 1;
+          const int8_t v = v0 + j >= p.nnz ? (int8_t)0 : vrow[v0 + j];
+          ((uint8_t*)(srow + (k >> 4) * 16))[perm_pos(k & 15)] = (uint8_t)v;
+          ++j;
+        }
+      }
+    }
+    vi += cnt + cnt_other;
+    lds_sync();
+    // ---- next stage's global data (its latency hides behind the MFMAs) ----
+    if (s + 1 < nst) fetch(s + 1);
+    // ---- MFMAs: two K64 chunks ----
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      v4i a[TM];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) a[i] = __builtin_bit_cast(v4i, sA[((wm * TM + i) * 2 + f) * 64 + lane]);
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        bl[j] = __builtin_bit_cast(v4i, sL[(((wn * TN + j) * 4) + f) * 64 + lane]);
-        bs[j] = __builtin_bit_cast(v4i, sS[(((wn * TN + j) * 4) + f) * 64 + lane]);
-      }
+        const int idx = ((wn * TN + j) * 2 + f) * 64 + lane;
+        const uint2 x = sL[idx];
+        const v4i bl = v4i{(int)((x.x << 4) & 0xF0F0F0F0u), (int)(x.x & 0xF0F0F0F0u),
+                           (int)((x.y << 4) & 0xF0F0F0F0u), (int)(x.y & 0xF0F0F0F0u)};
+        const v4i bs = __builtin_bit_cast(v4i, sS[idx]);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        v4i a = __builtin_bit_cast(v4i, sA[(((wm * TM + i) * 4) + f) * 64 + lane]);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bl[j], acc[i][j], 0, 0, 0);
-          acs[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bs[j], acs[i][j], 0, 0, 0);
+        for (int i = 0; i < TM; ++i) {
+          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], bl, acc[i][j], 0, 0, 0);
+          acs[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], bs, acs[i][j], 0, 0, 0);
         }
       }
     }
-    __syncthreads();
+    lds_sync();
   }
 
+  // ---- low + masked parts -> fp32 partial (the low accumulator is x16) ----
+  // (the fp32 partial reuses the low accumulator's registers)
   const int lr = (lane >> 4) * 4, lc = lane & 15;
-  float part[TM][TN][4];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        int64_t row = m0 + wm * 64 + i * 16 + lr + r, col = n0 + wn * 64 + j * 16 + lc;
-        int64_t rc = row < p.m ? row : p.m - 1, cc = col < p.n ? col : p.n - 1;
+      for (int q = 0; q < 4; ++q) {
+        const int64_t row = m0 + wm * 64 + i * 16 + lr + q, col = n0 + wn * 64 + j * 16 + lc;
+        const int64_t rc = row < p.m ? row : p.m - 1, cc = col < p.n ? col : p.n - 1;
+        const int32_t lo = acc[i][j][q] >> 4;
         if (DEBUG && row < p.m && col < p.n) {
-          p.dbg_low[row * p.n + col] = acc[i][j][r];
-          p.dbg_sp[row * p.n + col] = acs[i][j][r];
+          p.dbg_low[row * p.n + col] = lo;
+          p.dbg_sp[row * p.n + col] = acs[i][j][q];
         }
-        part[i][j][r] = p.s_x[rc] * (p.s_w4[cc] * (float)acc[i][j][r] + p.s_w8[cc] * (float)acs[i][j][r]);
-        acs[i][j][r] = 0;
+        acc[i][j][q] = __float_as_int(p.s_x[rc] * (p.s_w4[cc] * (float)lo + p.s_w8[cc] * (float)acs[i][j][q]));
+        acs[i][j][q] = 0;
       }
 
-  // int8 branch (outlier channels), 128 bytes per row per stage
+  // ---- int8 branch (outlier channels), 128 bytes per row per stage ----
   for (int s = 0; s < p.s_out; ++s) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int e = tid + i * 256, r = e >> 3, pc = e & 7;
-      int64_t gr = m0 + r < p.m ? m0 + r : p.m - 1;
-      sA[lds_frag_idx(r, pc >> 2, pc & 3)] = *(const uint4*)(p.x_out + gr * p.ldo + s * 128 + pc * 16);
-      int64_t gn = n0 + r < p.n ? n0 + r : p.n - 1;
-      sL[lds_frag_idx(r, pc >> 2, pc & 3)] = *(const uint4*)(p.w_out + gn * p.ldo + s * 128 + pc * 16);
+    for (int q = 0; q < 4; ++q) {
+      sA[(rb * 2 + h) * 64 + q * 16 + rr] = *(const uint4*)(p.x_out + ga * p.ldo + s * 128 + h * 64 + q * 16);
+      sS[(rb * 2 + h) * 64 + q * 16 + rr] = *(const uint4*)(p.w_out + gn * p.ldo + s * 128 + h * 64 + q * 16);
     }
     __syncthreads();
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
       v4i b[TN];
 #pragma unroll
-      for (int j = 0; j < TN; ++j) b[j] = __builtin_bit_cast(v4i, sL[(((wn * TN + j) * 4) + f) * 64 + lane]);
+      for (int j = 0; j < TN; ++j) b[j] = __builtin_bit_cast(v4i, sS[((wn * TN + j) * 2 + f) * 64 + lane]);
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        v4i a = __builtin_bit_cast(v4i, sA[(((wm * TM + i) * 4) + f) * 64 + lane]);
+        const v4i a = __builtin_bit_cast(v4i, sA[((wm * TM + i) * 2 + f) * 64 + lane]);
 #pragma unroll
         for (int j = 0; j < TN; ++j)
           acs[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[j], acs[i][j], 0, 0, 0);
@@ -173,12 +285,12 @@ __global__ __launch_bounds__(256) void k_sq_gemm(SqArgs p) {
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        int64_t row = m0 + wm * 64 + i * 16 + lr + r, col = n0 + wn * 64 + j * 16 + lc;
+      for (int q = 0; q < 4; ++q) {
+        const int64_t row = m0 + wm * 64 + i * 16 + lr + q, col = n0 + wn * 64 + j * 16 + lc;
         if (row >= p.m || col >= p.n) continue;
-        if (DEBUG) p.dbg_o[row * p.n + col] = acs[i][j][r];
-        float v = part[i][j][r];
-        if (p.s_out > 0) v += (p.s_xo[row] * p.s_wo[col]) * (float)acs[i][j][r];
+        if (DEBUG) p.dbg_o[row * p.n + col] = acs[i][j][q];
+        float v = __int_as_float(acc[i][j][q]);
+        if (p.s_out > 0) v += (p.s_xo[row] * p.s_wo[col]) * (float)acs[i][j][q];
         p.y[row * p.ldy + col] = v;
       }
 }

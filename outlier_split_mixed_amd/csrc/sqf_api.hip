@@ -38,6 +38,8 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // The low path sums int4 products scaled by 256 in int32: 49 * 256 * k_low
 // must stay below 2^31.
 constexpr int64_t kMaxKLow = 171000;
+// weight-side format: |acc| <= 16 * 127 * 7 * k_low < 2^31
+constexpr int64_t kMaxKLowSq = 150000;
 // Kernels address operands with 32-bit byte offsets.
 constexpr int64_t kMaxOperandBytes = ((int64_t)1 << 31) - 1;
 
@@ -277,6 +279,10 @@ sqf_status sqf_dual_gemm(const sqf_acts* a, const sqf_weights* w, float* y, int6
   if (a->m == 0) return SQF_OK;
   const bool debug = acc_low_dbg || acc_sp_dbg || acc_out_dbg;
   if (w->sq_nnz > 0) {
+    // int8 activations x (16 x int4 weights) in an int32 accumulator
+    if (w->k_low > kMaxKLowSq)
+      return fail(SQF_ERR_UNSUPPORTED, "%s: k_low=%lld exceeds %lld for the weight-side format", who,
+                  (long long)w->k_low, (long long)kMaxKLowSq);
     if (debug && !(acc_low_dbg && acc_sp_dbg && acc_out_dbg))
       return fail(SQF_ERR_INVALID_ARG, "%s: the weight-side debug path writes all three accumulators", who);
     sqf::SqArgs sa{a->x_low, a->s_x, (const uint8_t*)a->x_out, a->s_xo, w->w_low, w->s_w,
