@@ -168,11 +168,21 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
   // groups, a contiguous run, so that the group (and its map) rarely changes
   // between consecutive rows of a block.
   int64_t m_first = blockIdx.x, m_stop = p.m, m_step = gridDim.x;
+  int g_cur = 0;      // group of the current row (expert groups)
+  int64_t g_end = 0;  // first row after it
   if constexpr (GROUPED) {
     const int64_t per = (p.m + gridDim.x - 1) / gridDim.x;
     m_first = (int64_t)blockIdx.x * per;
     m_stop = m_first + per < p.m ? m_first + per : p.m;
     m_step = 1;
+    // largest g with row_off[g] <= m_first, once per block
+    int lo = 0, hi = p.groups;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (p.row_off[mid] <= m_first) lo = mid; else hi = mid;
+    }
+    g_cur = lo;
+    g_end = p.row_off[lo + 1];
   }
   // rows in flight ahead of the current one: enough bytes per thread to hide
   // HBM latency when a row is only a few chunks per thread
@@ -191,15 +201,15 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
     uint8_t* img = img0 + buf * img_bytes;
     float* rd = red + buf * 2 * NW;
     if constexpr (GROUPED) {
-      int lo = 0, hi = p.groups;  // largest g with row_off[g] <= m
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (p.row_off[mid] <= m) lo = mid; else hi = mid;
+      // rows of a block are contiguous: advance to the group holding m
+      while (m >= g_end) {
+        ++g_cur;
+        g_end = p.row_off[g_cur + 1];
       }
-      if (lo != cached_group) {
+      if (g_cur != cached_group) {
         lds_barrier();  // nobody still reads the previous group's outlier list
-        load_map(lo);
-        cached_group = lo;
+        load_map(g_cur);
+        cached_group = g_cur;
         lds_barrier();
       }
     }

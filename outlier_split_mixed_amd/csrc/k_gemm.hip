@@ -153,20 +153,44 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_du
   const float* s_w = p.s_w;
   const float* s_wo = p.s_wo;
   if constexpr (GROUPED) {
-    // walk the groups: group g owns ceil(rows_g / BM) * tiles_n tiles
-    int64_t base = 0;
-    int g = 0;
-    for (; g < p.groups; ++g) {
-      int64_t r0 = p.row_off[g], r1 = p.row_off[g + 1];
-      int64_t t = ((r1 - r0 + BM - 1) / BM) * tiles_n;
-      if (lid < base + t) {
-        m_begin = r0;
-        m_end = r1;
-        break;
+    // Group g owns ceil(rows_g / BM) * tiles_n tiles, in group order.  The
+    // block finds the group of its tile cooperatively: each thread counts the
+    // tiles of one group, a block-wide prefix sum turns the counts into tile
+    // ranges, and the thread whose range holds the tile publishes it.
+    __shared__ int64_t s_part[NW];
+    __shared__ int64_t s_found[2];  // group, first tile of the group
+    if (tid == 0) s_found[0] = -1;
+    int64_t carry = 0;
+    for (int g0 = 0; g0 < p.groups; g0 += NW * 64) {
+      const int g = g0 + tid;
+      int64_t cnt = 0;
+      if (g < p.groups) cnt = ((p.row_off[g + 1] - p.row_off[g] + BM - 1) / BM) * tiles_n;
+      int64_t incl = cnt;  // inclusive prefix within the wave
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int64_t t = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += t;
       }
-      base += t;
+      if (lane == 63) s_part[wave] = incl;
+      __syncthreads();
+      int64_t before = carry;
+      for (int w = 0; w < wave; ++w) before += s_part[w];
+      int64_t chunk = 0;
+      for (int w = 0; w < NW; ++w) chunk += s_part[w];
+      const int64_t lo_t = before + incl - cnt;
+      if (g < p.groups && lid >= lo_t && lid < lo_t + cnt) {
+        s_found[0] = g;
+        s_found[1] = lo_t;
+      }
+      carry += chunk;
+      __syncthreads();
+      if (s_found[0] >= 0) break;
     }
-    if (g == p.groups) return;
+    if (s_found[0] < 0) return;  // beyond the last tile
+    const int g = (int)s_found[0];
+    const int64_t base = s_found[1];
+    m_begin = p.row_off[g];
+    m_end = p.row_off[g + 1];
     int64_t local = lid - base;
     int64_t tiles_m = (m_end - m_begin + BM - 1) / BM;
     tm = local % tiles_m;
@@ -505,8 +529,10 @@ static hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
 template <int BR, bool GROUPED, bool DEBUG>
 static hipError_t launch_br(const GemmArgs& a, int cfg, hipStream_t s) {
   if constexpr (GROUPED) {
-    // expert groups hold a few hundred rows each: 128x128 tiles only
-    (void)cfg;
+    // expert groups hold a few hundred rows each: 256x256 or 128x128 tiles
+    if (BR != kFP8 && cfg == 0) {
+      if constexpr (BR != kFP8) return launch_cfg<256, 256, 2, 4, 1, BR, GROUPED, DEBUG>(a, s);
+    }
     return launch_cfg<128, 128, 2, 2, 2, BR, GROUPED, DEBUG>(a, s);
   } else {
     // an E4M3 branch keeps a second accumulator set: no 256x256 tile for it

@@ -314,12 +314,17 @@ sqf_status sqf_dual_gemm_grouped(const sqf_acts* a, const sqf_weights* w, int64_
   if (w->sq_nnz > 0) return fail(SQF_ERR_UNSUPPORTED, "%s: channel-split format only", who);
   if (a->m == 0) return SQF_OK;
   const int64_t ldo_b = w->ldo * branch_esz(w->branch);
-  // 128x128 tiles: expert groups hold a few hundred rows each
+  // 256x256 tiles when the groups average 384 rows or more (bf16 branch),
+  // else 128x128; SQF_GEMM_TILE=0/1 forces one
   sqf::GemmArgs ga{a->x_low, a->s_x, (const uint8_t*)a->x_out, a->s_xo, w->w_low, w->s_w,
                    (const uint8_t*)w->w_out, w->s_wo, y, acc_low_dbg, row_off, a->m, w->n,
                    w->ldk, ldo_b, ldy, w->n * w->ldk, w->n * ldo_b, w->n,
                    (int32_t)(w->ldk / 64), (int32_t)(ldo_b / 64), (int32_t)groups};
-  return hip_status(sqf::launch_dual_gemm(ga, w->branch, true, acc_low_dbg != nullptr, 1,
+  const char* env = getenv("SQF_GEMM_TILE");
+  int cfg = (a->m / groups >= 384) ? 0 : 1;
+  if (env && (atoi(env) == 0 || atoi(env) == 1)) cfg = atoi(env);
+  if (w->branch == SQF_FP8_E4M3) cfg = 1;
+  return hip_status(sqf::launch_dual_gemm(ga, w->branch, true, acc_low_dbg != nullptr, cfg,
                                           (hipStream_t)stream),
                     who);
 }

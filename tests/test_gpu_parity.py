@@ -188,15 +188,20 @@ def _moe_small(experts=6, tokens=96, topk=2, hidden=512, inter=256, seed=86):
                            inter=inter, cal_rows=64)
 
 
-@pytest.mark.parametrize("branch", ["bf16", "fp8"])
-def test_grouped_small_with_empty_group(sqf, branch):
+@pytest.mark.parametrize("branch,tile", [("bf16", "1"), ("bf16", "0"), ("fp8", "1")])
+def test_grouped_small_with_empty_group(sqf, branch, tile):
+    """Ragged expert groups, one of them empty, on both grouped tile shapes."""
     moe = _moe_small()
     lays = moe.up
     # force one empty expert group
     lays[2] = synth.Layer(name="empty", m=0, k=lays[2].k, n=lays[2].n, k_out=lays[2].k_out,
                           x=lays[2].x[:0], x_cal=lays[2].x_cal, w=lays[2].w,
                           scaled=lays[2].scaled)
-    _grouped_check(sqf, lays, branch)
+    os.environ["SQF_GEMM_TILE"] = tile
+    try:
+        _grouped_check(sqf, lays, branch)
+    finally:
+        del os.environ["SQF_GEMM_TILE"]
 
 
 def _grouped_check(sqf, lays, branch, rows_per_group=None):
