@@ -165,6 +165,106 @@ def cpu_baseline(runs, rows_per_layer):
                        f"(act quantise/split + dual GEMM), {total_s:.1f} s")
 
 
+def time_call(torch, stream, fn, iters=10, warmup=2):
+    """Average time (ms) of fn() on `stream`, measured with events on that stream."""
+    for _ in range(warmup):
+        fn()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(iters):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def rows_section(sqf, torch, stream):
+    """Every hot-path row on its own workload, each against its roofline:
+    offline selection and packing (timed once), the activation split
+    (HBM-bound), the grouped MoE expert path (HBM-bound: the fp32 outputs
+    dominate its bytes) and the weight-side SQ-format GEMM (MFMA-bound: the
+    low and the masked pass are two int8 passes over K_low, plus the int8
+    branch)."""
+    from outlier_split_mixed_amd import synth
+
+    out = []
+    with torch.cuda.stream(stream):
+        # a0/a1 offline, on the widest layer of the step
+        lay = synth.llama3_70b(1, 16)
+        x_cal = torch.from_numpy(lay.x_cal).cuda()
+        w = torch.from_numpy(lay.w).cuda()
+        k_out = lay.k // 16
+        t = time_call(torch, stream, lambda: sqf.sqf_select_channels(x_cal, w, k_out, stream=stream),
+                      iters=3, warmup=1)
+        _, mp, _, _ = sqf.sqf_select_channels(x_cal, w, k_out, stream=stream)
+        out.append(dict(row="a0 select (offline)", shape=f"{lay.k}x{lay.n}, {lay.x_cal.shape[0]} cal rows",
+                        ms=round(t, 3)))
+        t = time_call(torch, stream, lambda: sqf.sqf_pack_weights(w, mp, stream=stream), iters=3, warmup=1)
+        out.append(dict(row="a1 pack (offline)", shape=f"{lay.k}x{lay.n}", ms=round(t, 3)))
+        del w, x_cal, mp
+        torch.cuda.empty_cache()
+
+        # a6: grouped experts (Qwen3-30B-A3B-shaped)
+        moe = synth.qwen3_moe()
+        ro = torch.from_numpy(moe.offsets).cuda()
+        rows = int(moe.offsets[-1])
+        for name, lays, br in (("up", moe.up, "bf16"), ("down", moe.down, "bf16"),
+                               ("down", moe.down, "fp8")):
+            k, n, ko = lays[0].k, lays[0].n, lays[0].k_out
+            maps = torch.stack([sqf.sqf_select_channels(torch.from_numpy(l.x_cal).cuda(),
+                                                        torch.from_numpy(l.w).cuda(), ko,
+                                                        stream=stream)[1] for l in lays])
+            wt = sqf.sqf_pack_weights(torch.from_numpy(np.stack([l.w for l in lays])).cuda(), maps,
+                                      branch=br, stream=stream)
+            xt = torch.from_numpy(synth.to_bf16_bits(np.concatenate([l.x for l in lays])).view(np.int16))
+            xt = xt.view(torch.bfloat16).cuda()
+            a = sqf.alloc_acts(rows, k - ko, ko, branch=br)
+            y = torch.empty((rows, n), dtype=torch.float32, device="cuda")
+            ta = time_call(torch, stream, lambda: sqf.sqf_quantize_split_act_grouped(
+                xt, ro, maps, a, stream=stream))
+            tg = time_call(torch, stream, lambda: sqf.sqf_dual_gemm_grouped(a, wt, ro, y=y, stream=stream))
+            esz = 2 if br == "bf16" else 1
+            act_b = rows * (k * 2 + a.ldk + a.ldo * esz + 4)
+            gemm_b = rows * (a.ldk + a.ldo * esz + 8) + len(lays) * n * (a.ldk + a.ldo * esz + 8) + rows * n * 4
+            out.append(dict(row=f"a6 grouped {name} ({br} branch)",
+                            shape=f"{len(lays)} experts, {rows} rows, {k}->{n}, k_out {ko}",
+                            act_us=round(ta * 1e3, 1),
+                            act_frac_hbm=round(act_b / (ta * 1e-3) / 1e9 / PEAK_HBM_GBS, 3),
+                            gemm_us=round(tg * 1e3, 1),
+                            gemm_tops=round(2.0 * rows * n * k / (tg * 1e-3) / 1e12, 1),
+                            gemm_gbs=round(gemm_b / (tg * 1e-3) / 1e9, 1),
+                            gemm_frac_hbm=round(gemm_b / (tg * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)))
+            del wt, xt, a, y, maps
+            torch.cuda.empty_cache()
+        del moe
+
+        # a7: SQ-format weight side
+        lay = synth.sq_weight()
+        k_out = lay.k_out
+        k_low = lay.k - k_out
+        x_cal = torch.from_numpy(lay.x_cal).cuda()
+        w = torch.from_numpy(lay.w).cuda()
+        _, mp, _, hd = sqf.sqf_select_channels(x_cal, w, k_out, stream=stream)
+        wt = sqf.sqf_pack_weights(w, mp, branch="i8", hdiag=hd, sq_nnz=k_low // 8, stream=stream)
+        xt = torch.from_numpy(synth.to_bf16_bits(lay.x).view(np.int16)).view(torch.bfloat16).cuda()
+        a = sqf.alloc_acts(lay.m, k_low, k_out, low="i8", branch="i8")
+        y = torch.empty((lay.m, lay.n), dtype=torch.float32, device="cuda")
+        ta = time_call(torch, stream, lambda: sqf.sqf_quantize_split_act(xt, mp, a, stream=stream))
+        tg = time_call(torch, stream, lambda: sqf.sqf_dual_gemm(a, wt, y=y, stream=stream), iters=5)
+        mfma_ops = 2.0 * lay.m * lay.n * (2 * k_low + k_out)
+        out.append(dict(row="a7 SQ-format weight side (int8 acts, masked int8 part, int8 branch)",
+                        shape=f"{lay.m}x{lay.k}->{lay.n}, nnz {k_low // 8}/row",
+                        act_us=round(ta * 1e3, 1), gemm_us=round(tg * 1e3, 1),
+                        gemm_eff_tops=round(2.0 * lay.m * lay.n * lay.k / (tg * 1e-3) / 1e12, 1),
+                        mfma_tops=round(mfma_ops / (tg * 1e-3) / 1e12, 1),
+                        frac_int8_peak=round(mfma_ops / (tg * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4)))
+        del wt, xt, a, y, w, x_cal
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -173,6 +273,8 @@ def main():
     ap.add_argument("--sweep", action="store_true", help="also time outlier fractions 1/2..1/16")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=128)
+    ap.add_argument("--no-rows", action="store_true",
+                    help="skip the per-row section (offline steps, grouped experts, SQ-format)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after timing, copy a buffer of this many bytes (counter calibration)")
     args = ap.parse_args()
@@ -250,6 +352,8 @@ def main():
                 del r
                 torch.cuda.empty_cache()
         out["sweep"] = sweep
+    if not args.no_rows:
+        out["rows"] = rows_section(sqf, torch, stream)
     if args.copy_bytes:
         # plain device copy of a known size: the reference that scales the
         # memory-traffic counters of a profiled run to bytes
