@@ -143,7 +143,7 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_du
 
   // ---- block -> tile (XCD-aware) ----
   int64_t lid = blockIdx.x;
-  {
+  if constexpr (!GROUPED) {
     const int64_t nb = gridDim.x;
     if ((nb & 7) == 0) lid = (lid & 7) * (nb >> 3) + (lid >> 3);
   }
@@ -160,6 +160,25 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_du
     __shared__ int64_t s_part[NW];
     __shared__ int64_t s_found[2];  // group, first tile of the group
     if (tid == 0) s_found[0] = -1;
+    // The grid is an upper bound on the tile count, so the XCD remap runs over
+    // the real count T: XCD x (hardware blocks x, x + 8, ...) takes the
+    // logical tiles [x * ceil(T/8), (x + 1) * ceil(T/8)).
+    {
+      int64_t cnt = 0;
+      for (int g = tid; g < p.groups; g += NW * 64)
+        cnt += ((p.row_off[g + 1] - p.row_off[g] + BM - 1) / BM) * tiles_n;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
+      if (lane == 0) s_part[wave] = cnt;
+      __syncthreads();
+      int64_t total = 0;
+      for (int w = 0; w < NW; ++w) total += s_part[w];
+      __syncthreads();
+      const int64_t per = (total + 7) >> 3;
+      const int64_t j = lid >> 3;
+      lid = (lid & 7) * per + j;
+      if (j >= per || lid >= total) return;
+    }
     int64_t carry = 0;
     for (int g0 = 0; g0 < p.groups; g0 += NW * 64) {
       const int g = g0 + tid;
@@ -261,6 +280,15 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_du
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+  // A group's last row tile is mostly empty (its rows end inside it): there
+  // each wave runs the MFMAs of its 16-row fragments that hold rows and skips
+  // the rest (a wave-uniform branch per fragment; plain tiles never skip).
+  int live = TM;
+  if constexpr (GROUPED) {
+    const int64_t left = m_end - (m0 + wm * WM);
+    live = left <= 0 ? 0 : left >= TM * 16 ? TM : (int)((left + 15) >> 4);
+    live = __builtin_amdgcn_readfirstlane(live);
+  }
 
   // Pipeline.  A step computes its 64 bytes of K in two halves.  Between
   // them, mid_sync issues the LDS reads of step t+1's B fragments and first A
@@ -351,6 +379,7 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_du
       }
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
+        if (GROUPED && i >= live) break;
         const v4i aa = i == 0 ? a0w[half]
                               : widen((uint32_t)A[i][2 * half], (uint32_t)A[i][2 * half + 1]);
 #pragma unroll
@@ -408,17 +437,20 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_du
   auto br_mfma = [&](const v4i (&A)[TM], const v4i (&B)[TN]) {
     if constexpr (BR == kBF16) {
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < TM; ++i) {
+        if (GROUPED && i >= live) break;
 #pragma unroll
         for (int j = 0; j < TN; ++j)
           c[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
               __builtin_bit_cast(v8bf, A[i]), __builtin_bit_cast(v8bf, B[j]), c[i][j], 0, 0, 0);
+      }
     } else {
       // E4M3: two MFMAs (K = 32 each) per 16-byte fragment
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
+          if (GROUPED && i >= live) break;
           const long a8 = (long)(((uint64_t)(uint32_t)A[i][2 * h + 1] << 32) | (uint32_t)A[i][2 * h]);
 #pragma unroll
           for (int j = 0; j < TN; ++j) {
@@ -463,12 +495,16 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_du
   float* y = p.y + m_begin * p.ldy;
   auto fused = [&](int i, int j, int r, int row, int col) {
     float v = c[i][j][r];
-    if constexpr (BR == kFP8) v += (p.s_xo[m_begin + row] * s_wo[col]) * c2[i][j][r];
+    // rows past the end (staged path) read the last row's scale, unused
+    if constexpr (BR == kFP8)
+      v += (p.s_xo[m_begin + (row < mrows ? row : mrows - 1)] * s_wo[col]) * c2[i][j][r];
     return v;
   };
   const int wrow0 = (int)(m0 - m_begin) + wm * WM, wcol0 = (int)n0 + wn * WN;
-  const bool whole = wrow0 + WM <= mrows && wcol0 + WN <= ncols && (p.ldy & 3) == 0 &&
-                     (((uintptr_t)p.y) & 15) == 0;
+  // (grouped: also a tile that ends inside the wave's rows, skipping the
+  // rows past the end per 16-row fragment and per row)
+  const bool whole = (GROUPED || wrow0 + WM <= mrows) && wcol0 + WN <= ncols &&
+                     (p.ldy & 3) == 0 && (((uintptr_t)p.y) & 15) == 0;
   if (whole) {
     // Row-contiguous stores: each 16-row slice of the wave tile goes through
     // this wave's part of the pair buffer the K loop no longer uses (the one
@@ -480,6 +516,7 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_du
     float* stg = (float*)(smem + ((ST >> 1) & 1) * PAIR) + wave * (16 * LDW);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
+      if (GROUPED && wrow0 + i * 16 >= mrows) break;
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -490,7 +527,8 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_du
       for (int k = 0; k < WN / 16; ++k) {
         const int idx = k * 64 + lane, rr = idx / (WN / 4), c4 = idx % (WN / 4);
         const v4f v = *(const v4f*)(stg + rr * LDW + 4 * c4);
-        *(v4f*)(y + (int64_t)(wrow0 + i * 16 + rr) * p.ldy + wcol0 + 4 * c4) = v;
+        if (!GROUPED || wrow0 + i * 16 + rr < mrows)
+          *(v4f*)(y + (int64_t)(wrow0 + i * 16 + rr) * p.ldy + wcol0 + 4 * c4) = v;
       }
     }
   } else {
@@ -516,8 +554,8 @@ template <int BM, int BN, int WGM, int WGN, int OCC, int BR, bool GROUPED, bool 
 static hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   int64_t tiles_n = (a.n + BN - 1) / BN;
   int64_t blocks;
-  if (GROUPED)
-    blocks = ((a.m + BM - 1) / BM + a.groups) * tiles_n;
+  if (GROUPED)  // an upper bound on the tiles, a multiple of the 8 XCDs
+    blocks = (((a.m + BM - 1) / BM + a.groups) * tiles_n + 7) & ~(int64_t)7;
   else
     blocks = ((a.m + BM - 1) / BM) * tiles_n;
   if (blocks <= 0) return hipSuccess;
