@@ -101,7 +101,7 @@ typedef struct sqf_weights {
    * the sq_nnz most important low slots with nibble 0x8 and stores their
    * int8 values in ascending slot order.  groups must be 1. */
   int64_t sq_nnz;       /* 0 = channel-split (OSC) format */
-  int8_t* sq_val;       /* [n][sq_nnz] */
+  int8_t* sq_val;       /* [n][sq_nnz], 16-byte aligned */
   float* s_w8;          /* [n] scale of sq_val */
   int32_t* sq_tile_off; /* [n][ldk/128 + 1]: count of marked slots before
                            each 256-slot tile (derived, written by pack) */

@@ -48,7 +48,6 @@ namespace sqf {
 // swz(h, r) = r ^ 2h makes the 16 rows x one chunk of an MFMA operand read
 // hit 16 distinct 16-byte bank groups (and any 8 consecutive lanes distinct
 // ones).  Each wave owns PW consecutive halves (A rows first, then B rows).
-__host__ __device__ constexpr int pair_swz(int h, int r) { return r ^ (2 * h); }
 
 template <int BM, int BN, int NW>
 struct DmaLoader {
@@ -75,53 +74,6 @@ struct DmaLoader {
     }
   }
 };
-// s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt bits [3:0] and [15:14]; expcnt and
-// lgkmcnt left at their maximum, i.e. not waited on).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
-
-// One 16-byte-per-lane global -> LDS DMA (global_load_lds_dwordx4): lane l's
-// 16 bytes land at LDS byte address lds + 16*l.  Written as a two-instruction
-// asm block rather than the compiler builtin because the builtin is a FLAT
-// instruction that also counts as an LDS access, and while one is outstanding
-// the compiler's wait insertion can only wait for every LDS read at once
-// (lgkmcnt(0)); the ring keeps DMAs outstanding across the whole K loop.  The
-// block has no register outputs; completion is tracked by the explicit vmcnt
-// waits of the ring (wait_vmcnt), and the "memory" clobber keeps the compiler
-// from moving LDS accesses across it.
-__device__ __forceinline__ void dma_16B(const uint8_t* base, uint32_t voff, uint32_t lds) {
-  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds);
-  // base: wave-uniform 64-bit address (SGPR pair); voff: per-lane byte offset.
-  // M0 holds the LDS base; one wait state separates its write from the DMA.
-  asm volatile(
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, %1"
-      :
-      : "v"(voff), "s"(base), "{m0}"(m0v)
-      : "memory");
-}
-
-// Byte address of a __shared__ object inside the workgroup's LDS.
-__device__ __forceinline__ uint32_t lds_offset(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// Workgroup barrier that does not drain outstanding loads.  __syncthreads()
-// carries a workgroup fence, and the fence makes the compiler wait for every
-// outstanding LDS-DMA load (they count as LDS writes), which would cap the
-// ring at one stage in flight.  Here the caller has already waited for the
-// stage it needs (vmcnt) and for its own LDS reads (lgkmcnt), and the empty
-// asm statements keep the compiler from moving LDS accesses across the
-// barrier.
-__device__ __forceinline__ void stage_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // OCC: blocks meant to share a CU (sets the register budget so that
 // OCC * WGM * WGN waves fit: 2 waves per SIMD either way).
 template <int BM, int BN, int WGM, int WGN, int OCC, int BR, bool GROUPED, bool DEBUG, int GROUP_M>

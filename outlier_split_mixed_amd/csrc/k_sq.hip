@@ -10,38 +10,38 @@
 //   acc_o  [m,n] = sum_t xo[m,t] * wo[n,t]          (int8 outlier-channel branch)
 //   y = s_x*(s_w4*acc_low + s_w8*acc_sp) + s_xo*s_wo*acc_o
 //
-// gfx950 mapping.  The "gather unit" is the decode of each K stage of W into
-// LDS, done once per block: a 128-slot stage of a W row becomes
+// gfx950 mapping.  The "gather unit" is the decode of each 128-slot K stage of
+// a block's W rows into LDS: a stage of a W row becomes
 //   * an int4 low tile with the marks cleared to 0 (SWAR: a nibble is the
 //     mark iff its top bit is set and its low three bits are zero), widened
 //     to int8 at MFMA time with the x16 trick (w << 4 & 0xF0.. and
 //     w & 0xF0..), which puts a group of 8 slots in the order 0,2,4,6,1,3,5,7;
 //   * an int8 tile holding the row's sparse values at their marked slots
-//     (zero elsewhere), in that same slot order.  Only the marked slots (1/8)
-//     are written: a lane walks the marks of its 64 slots with find-first-set
-//     and copies each value from the row's value window, which was fetched
-//     into LDS with the stage (the row's running value index is carried from
-//     stage to stage, so the window is known before the stage is decoded).
-// The int8 activations are written to LDS with the same slot permutation, so
-// both tiles feed v_mfma_i32_16x16x64_i8 with one A fragment.  The low
-// accumulator carries the x16 factor (|acc| <= 16*127*7*k_low < 2^31 for the
-// k_low the host accepts); it is removed exactly in the epilogue.  Global
-// loads of stage s+1 are issued right after stage s is in LDS, so their
-// latency hides behind stage s's MFMAs; two blocks share a CU.
+//     (zero elsewhere), in that same slot order: every 8-slot group is
+//     expanded at once from a window of the row's values with byte permutes
+//     whose selectors come from a table indexed by the group's mark mask.
+// The int8 activations stay in their natural order in LDS; each A fragment is
+// permuted into the widened slot order in registers as it is read, so both
+// tiles feed v_mfma_i32_16x16x64_i8 with one A fragment.  The low accumulator
+// carries the x16 factor (|acc| <= 16*127*7*k_low < 2^31 for the k_low the
+// host accepts); it is removed exactly in the epilogue.
+//
+// Pipeline.  A block computes 256 x 128 outputs with 8 waves (4 x 2, each
+// 64 x 64).  Activations and raw W codes move global -> LDS by DMA
+// (global_load_lds_dwordx4) through two-stage rings; the values of a stage
+// are fetched the same way, as a 64-byte window per row that starts at the
+// row's running value index (known once the previous stage is decoded).
+// Iteration s decodes stage s+1 (waves 0-3, two lanes per W row) and runs the
+// MFMAs of stage s (all waves) in one basic block, so the decode's vector ALU
+// work can issue between the MFMAs; one barrier per stage.  The DMAs of A
+// stage s+2 and W stage s+3 start right after that barrier, and the value
+// window of stage s+2 right after stage s+1 is decoded.
 #include "sqf_device.h"
 #include "sqf_launch.h"
 
 namespace sqf {
 
 namespace {
-
-// LDS barrier that does not wait for outstanding global loads.
-__device__ __forceinline__ void lds_sync() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
   return __builtin_amdgcn_perm(hi, lo, sel);
@@ -53,45 +53,132 @@ __device__ __forceinline__ int perm_pos(int k) {
   return (k & 8) + ((k & 1) ? 4 + ((k & 7) >> 1) : ((k & 7) >> 1));
 }
 
+// natural slot order -> widened slot order, 16 int8 codes
+__device__ __forceinline__ v4i to_widened(v4i u) {
+  return v4i{(int)perm((uint32_t)u.y, (uint32_t)u.x, 0x06040200u),
+             (int)perm((uint32_t)u.y, (uint32_t)u.x, 0x07050301u),
+             (int)perm((uint32_t)u.w, (uint32_t)u.z, 0x06040200u),
+             (int)perm((uint32_t)u.w, (uint32_t)u.z, 0x07050301u)};
+}
+
+// LDS barrier that does not wait for outstanding global loads.
+__device__ __forceinline__ void sq_sync() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  stage_barrier();
+}
+
+// LDS map of one block (bytes).
+constexpr int kBM = 256, kBN = 128;
+constexpr int kStA = kBM * 128;  // activation stage: 16-row blocks of 16 x 128 B (swizzled)
+constexpr int kStW = kBN * 64;   // raw W stage: row-major, 64 B per row
+constexpr int kStV = kBN * 64;   // value windows: row-major, 64 B per row
+constexpr int kStL = kBN * 64;   // clean low tile: [row block][K half][lane] x 8 B
+constexpr int kStS = kBN * 128;  // sparse tile: [row block][K half][lane] x 16 B
+constexpr int kOffA = 0;
+constexpr int kOffW = kOffA + 2 * kStA;
+constexpr int kOffV = kOffW + 2 * kStW;
+constexpr int kOffL = kOffV + 2 * kStV;
+constexpr int kOffS = kOffL + 2 * kStL;
+constexpr int kOffSel = kOffS + 2 * kStS;
+constexpr int kSmem = kOffSel + 256 * 8;
+static_assert(kSmem <= 160 * 1024, "LDS budget");
+// the branch's W tile (128 rows x 128 B, swizzled like A) reuses the raw W
+// and value rings
+static_assert(kBN * 128 <= 2 * kStW + 2 * kStV, "branch W tile fits");
+
 }  // namespace
 
 template <bool DEBUG>
-__global__ __launch_bounds__(256, 2) void k_sq_gemm(SqArgs p) {
-  constexpr int BM = 128, BN = 128, TM = 4, TN = 4;
-  // stage = 128 low slots: A 128 B / row, W 64 B / row
-  __shared__ uint4 sA[BM * 8];            // [rb][f][lane] x 16 B (permuted slot order)
-  __shared__ uint2 sL[BN * 8];            // [rb][f][lane] x 8 B (clean int4)
-  __shared__ uint4 sS[BN * 8];            // [rb][f][lane] x 16 B (values at marks)
-  __shared__ __attribute__((aligned(16))) uint8_t sV[BN * 64 + 16];  // value windows (+ read slack)
-  __shared__ uint2 sSel[256];  // expand selectors per 8-slot mark mask
+__global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
+  constexpr int TM = 4, TN = 4;
+  __shared__ __attribute__((aligned(2048))) uint8_t smem[kSmem];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int64_t tiles_m = (p.m + BM - 1) / BM;
-  const int64_t tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
-  if (tn * BN >= p.n) return;
-  const int64_t m0 = tm * BM, n0 = tn * BN;
-  const int nst = (int)(p.ldkw / 64);  // 128-slot stages (ldkw is a multiple of 128)
+  // rows, columns, stages and byte offsets fit in 32 bits (host limits)
+  const int tiles_m = (int)((p.m + kBM - 1) / kBM);
+  int lid = blockIdx.x;
+  {
+    // XCD-aware: hardware block b runs on XCD b % 8; give every XCD a
+    // contiguous run of tiles (row tiles fastest: the W tile is shared)
+    const int nb = gridDim.x;
+    if ((nb & 7) == 0) lid = (lid & 7) * (nb >> 3) + (lid >> 3);
+  }
+  const int tm = lid % tiles_m, tn = lid / tiles_m;
+  const int m0 = tm * kBM, n0 = tn * kBN;
+  const int mm = (int)p.m, nn = (int)p.n, nnz = (int)p.nnz;
+  const int nst = (int)(p.ldkw / 64);  // 128-slot stages (ldkw is a multiple of 64)
+  const uint32_t sbase = lds_offset(smem);
 
-  // this thread's share of a stage: row r (of A and of W), half h = K64 chunk
-  const int r = tid >> 1, h = tid & 1;
-  const int64_t ga = (m0 + r < p.m ? m0 + r : p.m - 1);
-  const int64_t gn = (n0 + r < p.n ? n0 + r : p.n - 1);
-  const uint8_t* arow = p.x_low + ga * p.ldkx + h * 64;
-  const uint8_t* wrow = p.w_low + gn * p.ldkw + h * 32;
-  const int8_t* vrow = p.sq_val + gn * p.nnz;
-  const int64_t vtotal = p.n * p.nnz;  // bytes in the value buffer
-  // byte offset of the buffer start past the previous 16-byte boundary
-  const int vmis = (int)((uintptr_t)p.sq_val & 15);
+  // ---- DMA lanes ----
+  // A: wave w brings the 8-row halves 4w .. 4w+3 of each stage; lane l row
+  // 8q + l/8, chunk (l%8) ^ swz(q%2, l/8)
+  uint32_t a_off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = wave * 4 + i, rl = lane >> 3;
+    int row = m0 + q * 8 + rl;
+    if (row > mm - 1) row = mm - 1;
+    a_off[i] = (uint32_t)row * (uint32_t)p.ldkx + (uint32_t)(((lane & 7) ^ pair_swz(q & 1, rl)) * 16);
+  }
+  // raw W: wave w brings rows 16w .. 16w+15; lane l row l/4, 16 bytes l%4
+  uint32_t w_off;
+  {
+    int row = n0 + wave * 16 + (lane >> 2);
+    if (row > nn - 1) row = nn - 1;
+    w_off = (uint32_t)row * (uint32_t)p.ldkw + (uint32_t)((lane & 3) * 16);
+  }
+  auto issue_a = [&](int s) {
+    const uint32_t buf = sbase + kOffA + (uint32_t)((s & 1) * kStA);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      dma_16B(p.x_low, a_off[i] + (uint32_t)s * 128u, buf + (uint32_t)((wave * 4 + i) * 1024));
+  };
+  auto issue_w = [&](int s) {
+    dma_16B(p.w_low, w_off + (uint32_t)s * 64u,
+            sbase + kOffW + (uint32_t)((s & 1) * kStW) + (uint32_t)(wave * 1024));
+  };
+
+  // ---- decode lanes (waves 0-3): row r of the W tile, K half h ----
+  const bool decoder = wave < 4;
+  const int r = (tid >> 1) & 127, h = tid & 1;
   const int rb = r >> 4, rr = r & 15;
+  const int gn = n0 + r < nn ? n0 + r : nn - 1;
+  const int8_t* vrow = p.sq_val + (int64_t)gn * nnz;
+  // sq_val is 16-byte aligned (host check); a window starts at the 16-byte
+  // boundary at or below the row's next value, and only whole blocks inside
+  // the buffer are used.  The buffer has at least one whole block, else every
+  // value is read one by one.
+  const int64_t vtotal = p.n * p.nnz;
+  const bool vdma = vtotal >= 16;
+  const uint32_t vlast = (uint32_t)((vtotal & ~(int64_t)15) - 16);  // last whole block
+  int vi = 0;  // row r's value index at the next stage to decode
+  // value windows of stage s for this wave's 32 rows (decoders only): lane l
+  // brings 16 bytes (l%4) of row 32w + 16k + l/4, whose value index lives in
+  // lanes 2*(16k + l/4) and +1
+  auto issue_v = [&](int s) {
+    const uint32_t buf = sbase + kOffV + (uint32_t)((s & 1) * kStV);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int vsrc = __shfl(vi, 2 * (16 * k + (lane >> 2)), 64);
+      int grow = n0 + wave * 32 + 16 * k + (lane >> 2);
+      if (grow > nn - 1) grow = nn - 1;
+      const uint32_t start = (uint32_t)(((int64_t)grow * nnz + vsrc) & ~(int64_t)15);
+      uint32_t off = start + (uint32_t)((lane & 3) * 16);
+      if (off > vlast) off = vlast;  // past the buffer: any whole block (unused)
+      dma_16B(vdma ? (const uint8_t*)p.sq_val : p.x_low, vdma ? off : 0u,
+              buf + (uint32_t)((wave * 32 + 16 * k) * 64));
+    }
+  };
 
   // Expand selectors: for the mark mask m of an 8-slot group, byte p of the
   // group's operand bytes (slot order 0,2,4,6,1,3,5,7) takes value number
   // rank(slot) (a byte of the pool {hi, lo} of the group's values) if the
   // slot is marked, else zero (selector 0x0C).
-  {
-    const int m = tid;  // 256 threads, 256 masks
+  uint2* sSel = (uint2*)(smem + kOffSel);
+  if (tid < 256) {
+    const int m = tid;
     uint32_t sel[2] = {0, 0};
 #pragma unroll
     for (int pp = 0; pp < 8; ++pp) {
@@ -100,87 +187,48 @@ __global__ __launch_bounds__(256, 2) void k_sq_gemm(SqArgs p) {
       sel[pp >> 2] |= b << (8 * (pp & 3));
     }
     sSel[m] = make_uint2(sel[0], sel[1]);
-    if (tid < 4) ((uint32_t*)(sV + BN * 64))[tid] = 0;
-    lds_sync();
   }
 
-  // prefetched global data of one stage
-  uint4 ra[4], rw[2], rv[2];
-  int vi = 0;         // row r's value index at the current stage
-  int win_valid = 0;  // bytes of the fetched window that lie inside the buffer
-  int64_t win_lo = 0; // buffer offset of the window's first byte (may be < 0)
-  auto fetch = [&](int s) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) ra[q] = *(const uint4*)(arow + s * 128 + q * 16);
-#pragma unroll
-    for (int q = 0; q < 2; ++q) rw[q] = *(const uint4*)(wrow + s * 64 + q * 16);
-    // value window [win_lo, win_lo + 64) (16-byte aligned addresses) holding
-    // row r's values from vi on; this lane brings its half (32 bytes)
-    const int64_t a0 = gn * p.nnz + vi;
-    win_lo = ((a0 + vmis) & ~(int64_t)15) - vmis;
-    // whole 16-byte blocks inside the buffer (the rest is read byte by byte)
-    const int64_t room = vtotal - win_lo;
-    win_valid = room > 0 ? (int)(room < 64 ? room : 64) & ~15 : 0;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int off = h * 32 + q * 16;
-      rv[q] = (off + 16 <= win_valid && win_lo + off >= 0)
-                  ? *(const uint4*)(p.sq_val + win_lo + off) : make_uint4(0, 0, 0, 0);
-    }
-  };
-
-  v4i acc[TM][TN], acs[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = acs[i][j] = v4i{0, 0, 0, 0};
-
-  if (nst > 0) fetch(0);
-  for (int s = 0; s < nst; ++s) {
-    // ---- A: 64 bytes (chunk h of row r) in the widened slot order ----
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const uint4 u = ra[g];
-      sA[(rb * 2 + h) * 64 + g * 16 + rr] =
-          make_uint4(perm(u.y, u.x, 0x06040200u), perm(u.y, u.x, 0x07050301u),
-                     perm(u.w, u.z, 0x06040200u), perm(u.w, u.z, 0x07050301u));
-    }
-    // ---- value window of row r ----
-    *(uint4*)(sV + r * 64 + h * 32) = rv[0];
-    *(uint4*)(sV + r * 64 + h * 32 + 16) = rv[1];
-    // ---- W: 64 slots (chunk h of row r): clean low tile, marks ----
+  // decode stage s (decoders): raw W and value window from LDS -> clean low
+  // tile and sparse tile of buffer s % 2; advances vi
+  auto decode = [&](int s) {
+    const uint8_t* wsrc = smem + kOffW + (s & 1) * kStW + r * 64 + h * 32;
+    const uint4 rw0 = *(const uint4*)wsrc, rw1 = *(const uint4*)(wsrc + 16);
     uint32_t wd[8], mk[8];
     int cnt = 0;
+    {
+      const uint32_t d8[8] = {rw0.x, rw0.y, rw0.z, rw0.w, rw1.x, rw1.y, rw1.z, rw1.w};
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const uint32_t d4[4] = {rw[q].x, rw[q].y, rw[q].z, rw[q].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t x = d4[e];
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t x = d8[e];
         const uint32_t nz = ((x & 0x77777777u) + 0x77777777u) & 0x88888888u;
         const uint32_t m8 = x & 0x88888888u & ~nz;  // bit 3 of each marked nibble
-        mk[q * 4 + e] = m8;
-        wd[q * 4 + e] = x & ~((m8 - (m8 >> 3)) | m8);
+        mk[e] = m8;
+        wd[e] = x & ~((m8 - (m8 >> 3)) | m8);
         cnt += __builtin_popcount(m8);
       }
     }
+    uint2* sL = (uint2*)(smem + kOffL + (s & 1) * kStL);
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
-      sL[(rb * 2 + h) * 64 + g * 16 + rr] = make_uint2(wd[2 * g], wd[2 * g + 1]);
-    uint4* srow = sS + (rb * 2 + h) * 64 + rr;  // this lane's sparse-tile bytes
+    for (int g = 0; g < 4; ++g) sL[(rb * 2 + h) * 64 + g * 16 + rr] = make_uint2(wd[2 * g], wd[2 * g + 1]);
+      // this lane's sparse-tile entries: 16-slot group g at + g * 256
+    uint8_t* srow = smem + kOffS + (s & 1) * kStS + ((rb * 2 + h) * 64 + rr) * 16;
     // marks of the first half of the row precede this lane's (partner lane ^ 1)
     const int cnt_other = __shfl_xor(cnt, 1, 64);
-    const int v0 = vi + (h ? cnt_other : 0);         // value index of this lane's first mark
-    const int wo0 = (int)(gn * p.nnz + v0 - win_lo);  // its offset in the value window
-    // ---- sparse tile: every 8-slot group expanded from its values at once ----
+    const int v0 = vi + (h ? cnt_other : 0);  // value index of this lane's first mark
+    const int64_t a0 = (int64_t)gn * nnz + vi;
+    const int64_t win_lo = a0 & ~(int64_t)15;  // the window the DMA brought
+    const int64_t room = vtotal - win_lo;
+    const int win_valid = !vdma ? 0 : room >= 64 ? 64 : (int)room & ~15;
+    const int wo0 = (int)(a0 - win_lo) + (v0 - vi);  // offset of this lane's first value
     {
-      const uint32_t* vw = (const uint32_t*)sV;
+      const uint32_t* vw = (const uint32_t*)(smem + kOffV + (s & 1) * kStV);
       int pre = 0;
 #pragma unroll
       for (int d = 0; d < 8; ++d) {
         // byte offset of the group's first value; past the row's window the
         // bytes are not used (those lanes take the path below), so the read
-        // only has to stay inside the array
+        // only has to stay inside LDS
         const int off = min(r * 64 + wo0 + pre, r * 64 + 64);
         const uint32_t d0 = vw[off >> 2], d1 = vw[(off >> 2) + 1], d2 = vw[(off >> 2) + 2];
         const uint32_t lo = __builtin_amdgcn_alignbyte(d1, d0, off & 3);
@@ -190,12 +238,12 @@ __global__ __launch_bounds__(256, 2) void k_sq_gemm(SqArgs p) {
         x = (x | (x >> 6)) & 0x000F000Fu;
         x = (x | (x >> 12)) & 0xFFu;
         const uint2 sl = sSel[x];
-        *(uint2*)((uint8_t*)(srow + (d >> 1) * 16) + (d & 1) * 8) = make_uint2(perm(hi, lo, sl.x), perm(hi, lo, sl.y));
+        *(uint2*)(srow + (d >> 1) * 256 + (d & 1) * 8) = make_uint2(perm(hi, lo, sl.x), perm(hi, lo, sl.y));
         pre += __builtin_popcount(mk[d]);
       }
     }
     // rare: values beyond the window (or more marks than values) -> one by one
-    if (wo0 + cnt > win_valid || v0 + cnt > p.nnz) {
+    if (wo0 + cnt > win_valid || v0 + cnt > nnz) {
       int j = 0;
 #pragma unroll
       for (int d = 0; d < 8; ++d) {
@@ -203,22 +251,40 @@ __global__ __launch_bounds__(256, 2) void k_sq_gemm(SqArgs p) {
         while (m8) {
           const int k = d * 8 + (__builtin_ctz(m8) >> 2);
           m8 &= m8 - 1;
-          const int8_t v = v0 + j >= p.nnz ? (int8_t)0 : vrow[v0 + j];
-          ((uint8_t*)(srow + (k >> 4) * 16))[perm_pos(k & 15)] = (uint8_t)v;
+          const int8_t v = v0 + j >= nnz ? (int8_t)0 : vrow[v0 + j];
+          srow[(k >> 4) * 256 + perm_pos(k & 15)] = (uint8_t)v;
           ++j;
         }
       }
     }
     vi += cnt + cnt_other;
-    lds_sync();
-    // ---- next stage's global data (its latency hides behind the MFMAs) ----
-    if (s + 1 < nst) fetch(s + 1);
-    // ---- MFMAs: two K64 chunks ----
+  };
+
+  // this lane's read offset inside a 2 KiB block of 16 rows x 128 B for K
+  // half f: row R = lane % 16, chunk C = lane / 16 + 4 * f
+  uint32_t rd_off[2];
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    const int R = lane & 15, C = (lane >> 4) + 4 * f;
+    rd_off[f] = (uint32_t)((R >> 3) * 1024 + (R & 7) * 128 + 16 * (C ^ pair_swz(R >> 3, R & 7)));
+  }
+
+  v4i acc[TM][TN], acs[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = acs[i][j] = v4i{0, 0, 0, 0};
+
+  // MFMAs of stage s: both K halves, low and sparse tiles on the same A
+  auto mfma_stage = [&](int s) {
+    const uint8_t* abuf = smem + kOffA + (s & 1) * kStA;
+    const uint2* sL = (const uint2*)(smem + kOffL + (s & 1) * kStL);
+    const uint4* sS = (const uint4*)(smem + kOffS + (s & 1) * kStS);
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
       v4i a[TM];
 #pragma unroll
-      for (int i = 0; i < TM; ++i) a[i] = __builtin_bit_cast(v4i, sA[((wm * TM + i) * 2 + f) * 64 + lane]);
+      for (int i = 0; i < TM; ++i) a[i] = to_widened(*(const v4i*)(abuf + (wm * TM + i) * 2048 + rd_off[f]));
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const int idx = ((wn * TN + j) * 2 + f) * 64 + lane;
@@ -233,7 +299,38 @@ __global__ __launch_bounds__(256, 2) void k_sq_gemm(SqArgs p) {
         }
       }
     }
-    lds_sync();
+  };
+
+  // ---- prologue: stage 0 decoded, A 1 and W 2 in flight ----
+  if (nst > 0) {
+    issue_a(0);
+    issue_w(0);
+    if (nst > 1) issue_w(1);
+    if (decoder) issue_v(0);
+    wait_vmcnt<0>();
+    sq_sync();  // selector table, A 0, W 0 and 1, values 0
+    if (decoder) {
+      decode(0);
+      if (nst > 1) issue_v(1);
+    }
+    wait_vmcnt<0>();
+    sq_sync();  // decoded stage 0, values 1; W 0 is free
+    if (nst > 1) issue_a(1);
+    if (nst > 2) issue_w(2);
+  }
+  // Iteration s: decode s+1 and the MFMAs of s; one barrier; then the DMAs of
+  // A s+2 (into the buffer of A s) and W s+3 (into the buffer of W s+1).
+  for (int s = 0; s < nst; ++s) {
+    if (decoder && s + 1 < nst) {
+      decode(s + 1);
+      if (s + 2 < nst) issue_v(s + 2);
+    }
+    mfma_stage(s);
+    // A s+1, W s+2 (issued one iteration ago) and values s+2 have landed
+    wait_vmcnt<0>();
+    sq_sync();
+    if (s + 2 < nst) issue_a(s + 2);
+    if (s + 3 < nst) issue_w(s + 3);
   }
 
   // ---- low + masked parts -> fp32 partial (the low accumulator is x16) ----
@@ -245,39 +342,61 @@ __global__ __launch_bounds__(256, 2) void k_sq_gemm(SqArgs p) {
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int64_t row = m0 + wm * 64 + i * 16 + lr + q, col = n0 + wn * 64 + j * 16 + lc;
-        const int64_t rc = row < p.m ? row : p.m - 1, cc = col < p.n ? col : p.n - 1;
+        const int row = m0 + wm * 64 + i * 16 + lr + q, col = n0 + wn * 64 + j * 16 + lc;
+        const int rc = row < mm ? row : mm - 1, cc = col < nn ? col : nn - 1;
         const int32_t lo = acc[i][j][q] >> 4;
-        if (DEBUG && row < p.m && col < p.n) {
-          p.dbg_low[row * p.n + col] = lo;
-          p.dbg_sp[row * p.n + col] = acs[i][j][q];
+        if (DEBUG && row < mm && col < nn) {
+          p.dbg_low[(int64_t)row * nn + col] = lo;
+          p.dbg_sp[(int64_t)row * nn + col] = acs[i][j][q];
         }
         acc[i][j][q] = __float_as_int(p.s_x[rc] * (p.s_w4[cc] * (float)lo + p.s_w8[cc] * (float)acs[i][j][q]));
         acs[i][j][q] = 0;
       }
 
   // ---- int8 branch (outlier channels), 128 bytes per row per stage ----
-  for (int s = 0; s < p.s_out; ++s) {
+  // A rows into A buffer 0, W rows (16-row blocks like A) over the raw W and
+  // value rings; the operands are in natural order on both sides.
+  if (p.s_out > 0) {
+    uint32_t o_off[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      sA[(rb * 2 + h) * 64 + q * 16 + rr] = *(const uint4*)(p.x_out + ga * p.ldo + s * 128 + h * 64 + q * 16);
-      sS[(rb * 2 + h) * 64 + q * 16 + rr] = *(const uint4*)(p.w_out + gn * p.ldo + s * 128 + h * 64 + q * 16);
+    for (int i = 0; i < 4; ++i) {
+      const int q = wave * 4 + i, rl = lane >> 3;
+      int row = m0 + q * 8 + rl;
+      if (row > mm - 1) row = mm - 1;
+      o_off[i] = (uint32_t)row * (uint32_t)p.ldo + (uint32_t)(((lane & 7) ^ pair_swz(q & 1, rl)) * 16);
     }
-    __syncthreads();
+    uint32_t wo_off[2];
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {
-      v4i b[TN];
+    for (int i = 0; i < 2; ++i) {
+      const int q = wave * 2 + i, rl = lane >> 3;
+      int row = n0 + q * 8 + rl;
+      if (row > nn - 1) row = nn - 1;
+      wo_off[i] = (uint32_t)row * (uint32_t)p.ldo + (uint32_t)(((lane & 7) ^ pair_swz(q & 1, rl)) * 16);
+    }
+    for (int t = 0; t < p.s_out; ++t) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j) b[j] = __builtin_bit_cast(v4i, sS[((wn * TN + j) * 2 + f) * 64 + lane]);
+      for (int i = 0; i < 4; ++i)
+        dma_16B(p.x_out, o_off[i] + (uint32_t)t * 128u, sbase + kOffA + (uint32_t)((wave * 4 + i) * 1024));
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const v4i a = __builtin_bit_cast(v4i, sA[((wm * TM + i) * 2 + f) * 64 + lane]);
+      for (int i = 0; i < 2; ++i)
+        dma_16B(p.w_out, wo_off[i] + (uint32_t)t * 128u, sbase + kOffW + (uint32_t)((wave * 2 + i) * 1024));
+      wait_vmcnt<0>();
+      sq_sync();
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acs[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[j], acs[i][j], 0, 0, 0);
+      for (int f = 0; f < 2; ++f) {
+        v4i b[TN];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) b[j] = *(const v4i*)(smem + kOffW + (wn * TN + j) * 2048 + rd_off[f]);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const v4i a = *(const v4i*)(smem + kOffA + (wm * TM + i) * 2048 + rd_off[f]);
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acs[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[j], acs[i][j], 0, 0, 0);
+        }
       }
+      sq_sync();
     }
-    __syncthreads();
   }
 
 #pragma unroll
@@ -286,20 +405,20 @@ __global__ __launch_bounds__(256, 2) void k_sq_gemm(SqArgs p) {
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int64_t row = m0 + wm * 64 + i * 16 + lr + q, col = n0 + wn * 64 + j * 16 + lc;
-        if (row >= p.m || col >= p.n) continue;
-        if (DEBUG) p.dbg_o[row * p.n + col] = acs[i][j][q];
+        const int row = m0 + wm * 64 + i * 16 + lr + q, col = n0 + wn * 64 + j * 16 + lc;
+        if (row >= mm || col >= nn) continue;
+        if (DEBUG) p.dbg_o[(int64_t)row * nn + col] = acs[i][j][q];
         float v = __int_as_float(acc[i][j][q]);
         if (p.s_out > 0) v += (p.s_xo[row] * p.s_wo[col]) * (float)acs[i][j][q];
-        p.y[row * p.ldy + col] = v;
+        p.y[(int64_t)row * p.ldy + col] = v;
       }
 }
 
 hipError_t launch_sq_gemm(const SqArgs& a, bool debug, hipStream_t s) {
-  int64_t blocks = ((a.m + 127) / 128) * ((a.n + 127) / 128);
+  const int64_t blocks = ((a.m + kBM - 1) / kBM) * ((a.n + kBN - 1) / kBN);
   if (blocks <= 0) return hipSuccess;
-  if (debug) hipLaunchKernelGGL(k_sq_gemm<true>, dim3((unsigned)blocks), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(k_sq_gemm<false>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  if (debug) hipLaunchKernelGGL(k_sq_gemm<true>, dim3((unsigned)blocks), dim3(512), 0, s, a);
+  else hipLaunchKernelGGL(k_sq_gemm<false>, dim3((unsigned)blocks), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

@@ -104,6 +104,8 @@ sqf_status check_weights(const sqf_weights* wt, const char* who) {
       return fail(SQF_ERR_UNSUPPORTED, "%s: the weight-side format needs an SQF_I8 branch", who);
     if (!wt->sq_val || !wt->s_w8 || !wt->sq_tile_off)
       return fail(SQF_ERR_INVALID_ARG, "%s: sq_val, s_w8 and sq_tile_off are required", who);
+    if (!aligned16(wt->sq_val))
+      return fail(SQF_ERR_ALIGN, "%s: sq_val must be 16-byte aligned", who);
   } else if (wt->branch == SQF_I8) {
     return fail(SQF_ERR_UNSUPPORTED,
                 "%s: an int8 branch is only built for the weight-side format", who);

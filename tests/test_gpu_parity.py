@@ -145,9 +145,26 @@ def test_sq_weight_side_small(sqf):
     """Weight-side SQ-format: int8 activations, int4 weights with reserved
     marks, int8 sparse values, int8 branch; three exact accumulators."""
     lay = _ragged(m=140, k=1280, n=300, n_scaled=80, seed=85)
+    _sq_check(sqf, lay, (lay.k - lay.k_out) // 8, "sq small")
+
+
+@pytest.mark.parametrize("m,k,n,den", [
+    (300, 1280, 260, 2),    # ~64 marks per 128-slot stage: past the value window
+    (70, 640, 130, 1),      # every low slot marked
+    (257, 2048, 129, 64),   # sparse marks, one row past a tile edge on both sides
+    (5, 256, 3, 128),       # a few values in total (below one 16-byte block)
+])
+def test_sq_weight_side_mark_density(sqf, m, k, n, den):
+    """Weight-side SQ-format at mark densities and sizes that exercise the
+    value windows' edges and the one-by-one path."""
+    lay = _ragged(m=m, k=k, n=n, n_scaled=max(1, k // 16), seed=90 + den)
+    _print(f"sq density m={m} k={k} n={n} nnz=k_low/{den}")
+    _sq_check(sqf, lay, max(1, (lay.k - lay.k_out) // den), f"sq m{m} k{k} n{n} 1/{den}")
+
+
+def _sq_check(sqf, lay, nnz, label):
     k_out = lay.k_out
     k_low = lay.k - k_out
-    nnz = k_low // 8
     x_cal = torch.from_numpy(lay.x_cal).cuda()
     w = torch.from_numpy(lay.w).cuda()
     idx, mp, score, hdiag = sqf.sqf_select_channels(x_cal, w, k_out)
@@ -180,7 +197,10 @@ def test_sq_weight_side_small(sqf):
     assert np.array_equal(al.cpu().numpy().astype(np.int64), o_al)
     assert np.array_equal(asp.cpu().numpy().astype(np.int64), o_asp)
     assert np.array_equal(ao.cpu().numpy().astype(np.int64), o_ao)
-    assert_rows_close(y.cpu().numpy(), o_y, "sq small")
+    assert_rows_close(y.cpu().numpy(), o_y, label)
+    y_fast = sqf.sqf_dual_gemm(acts, wts)
+    torch.cuda.synchronize()
+    assert_rows_close(y_fast.cpu().numpy(), o_y, label + " (timed launch)")
 
 
 def _moe_small(experts=6, tokens=96, topk=2, hidden=512, inter=256, seed=86):
