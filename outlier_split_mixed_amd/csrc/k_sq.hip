@@ -31,9 +31,9 @@
 // (global_load_lds_dwordx4) through two-stage rings; the values of a stage
 // are fetched the same way, as a 64-byte window per row that starts at the
 // row's running value index (known once the previous stage is decoded).
-// Iteration s decodes stage s+1 (waves 0-3, two lanes per W row) and runs the
-// MFMAs of stage s (all waves) in one basic block, so the decode's vector ALU
-// work can issue between the MFMAs; one barrier per stage.  The DMAs of A
+// Iteration s decodes stage s+1 (every wave its own 16 W rows, four lanes per
+// row) and runs the MFMAs of stage s in one basic block, so the decode's
+// vector ALU work can issue between the MFMAs; one barrier per stage.  The DMAs of A
 // stage s+2 and W stage s+3 start right after that barrier, and the value
 // window of stage s+2 right after stage s+1 is decoded.
 #include "sqf_device.h"
@@ -72,8 +72,8 @@ constexpr int kBM = 256, kBN = 128;
 constexpr int kStA = kBM * 128;  // activation stage: 16-row blocks of 16 x 128 B (swizzled)
 constexpr int kStW = kBN * 64;   // raw W stage: row-major, 64 B per row
 constexpr int kStV = kBN * 64;   // value windows: row-major, 64 B per row
-constexpr int kStL = kBN * 64;   // clean low tile: [row block][K half][lane] x 8 B
-constexpr int kStS = kBN * 128;  // sparse tile: [row block][K half][lane] x 16 B
+constexpr int kStL = kBN * 64;   // clean low tile: [row block][K half][entry] x 8 B
+constexpr int kStS = kBN * 128;  // sparse tile: [row block][K half][entry] x 16 B
 constexpr int kOffA = 0;
 constexpr int kOffW = kOffA + 2 * kStA;
 constexpr int kOffV = kOffW + 2 * kStW;
@@ -140,9 +140,11 @@ __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
             sbase + kOffW + (uint32_t)((s & 1) * kStW) + (uint32_t)(wave * 1024));
   };
 
-  // ---- decode lanes (waves 0-3): row r of the W tile, K half h ----
-  const bool decoder = wave < 4;
-  const int r = (tid >> 1) & 127, h = tid & 1;
+  // ---- decode lanes: every wave decodes its own 16 W rows (the rows its
+  // raw-W DMA brings), four lanes per row: lane l takes row 16w + l/4 and its
+  // 32 slots qq = l % 4 (K half f = qq / 2, 16-slot groups 2(qq%2), +1) ----
+  const int r = tid >> 2, qq = tid & 3;
+  const int f_own = qq >> 1, g0 = 2 * (qq & 1);
   const int rb = r >> 4, rr = r & 15;
   const int gn = n0 + r < nn ? n0 + r : nn - 1;
   const int8_t* vrow = p.sq_val + (int64_t)gn * nnz;
@@ -153,23 +155,14 @@ __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
   const int64_t vtotal = p.n * p.nnz;
   const bool vdma = vtotal >= 16;
   const uint32_t vlast = (uint32_t)((vtotal & ~(int64_t)15) - 16);  // last whole block
-  int vi = 0;  // row r's value index at the next stage to decode
-  // value windows of stage s for this wave's 32 rows (decoders only): lane l
-  // brings 16 bytes (l%4) of row 32w + 16k + l/4, whose value index lives in
-  // lanes 2*(16k + l/4) and +1
+  int vi = 0;  // row r's value index at the next stage to decode (same in its 4 lanes)
+  // value window of stage s: lane l brings 16-byte block l % 4 of its own row
   auto issue_v = [&](int s) {
-    const uint32_t buf = sbase + kOffV + (uint32_t)((s & 1) * kStV);
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int vsrc = __shfl(vi, 2 * (16 * k + (lane >> 2)), 64);
-      int grow = n0 + wave * 32 + 16 * k + (lane >> 2);
-      if (grow > nn - 1) grow = nn - 1;
-      const uint32_t start = (uint32_t)(((int64_t)grow * nnz + vsrc) & ~(int64_t)15);
-      uint32_t off = start + (uint32_t)((lane & 3) * 16);
-      if (off > vlast) off = vlast;  // past the buffer: any whole block (unused)
-      dma_16B(vdma ? (const uint8_t*)p.sq_val : p.x_low, vdma ? off : 0u,
-              buf + (uint32_t)((wave * 32 + 16 * k) * 64));
-    }
+    const uint32_t start = (uint32_t)(((int64_t)gn * nnz + vi) & ~(int64_t)15);
+    uint32_t off = start + (uint32_t)(qq * 16);
+    if (off > vlast) off = vlast;  // past the buffer: any whole block (unused)
+    dma_16B(vdma ? (const uint8_t*)p.sq_val : p.x_low, vdma ? off : 0u,
+            sbase + kOffV + (uint32_t)((s & 1) * kStV) + (uint32_t)(wave * 1024));
   };
 
   // Expand selectors: for the mark mask m of an 8-slot group, byte p of the
@@ -189,18 +182,24 @@ __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
     sSel[m] = make_uint2(sel[0], sel[1]);
   }
 
-  // decode stage s (decoders): raw W and value window from LDS -> clean low
-  // tile and sparse tile of buffer s % 2; advances vi
+  // Decoded-tile entry of MFMA lane (16-slot group g, row rr) in a K-half
+  // block: g * 16 + (rr ^ 8 (g / 2)), for the clean low tile also with g ^ f
+  // (f = K half); the sparse tile's 8-byte halves are swapped for f = 1.  The
+  // four lanes of a row write at once: these swizzles spread them over banks.
+  auto lpos = [](int g, int rr_, int f) { return ((g ^ f) << 4) + (rr_ ^ ((g >> 1) << 3)); };
+  auto spos = [](int g, int rr_) { return (g << 4) + (rr_ ^ ((g >> 1) << 3)); };
+
+  // decode stage s: raw W and value window from LDS -> clean low tile and
+  // sparse tile of buffer s % 2; advances vi
   auto decode = [&](int s) {
-    const uint8_t* wsrc = smem + kOffW + (s & 1) * kStW + r * 64 + h * 32;
-    const uint4 rw0 = *(const uint4*)wsrc, rw1 = *(const uint4*)(wsrc + 16);
-    uint32_t wd[8], mk[8];
+    const uint4 rw = *(const uint4*)(smem + kOffW + (s & 1) * kStW + r * 64 + qq * 16);
+    uint32_t wd[4], mk[4];
     int cnt = 0;
     {
-      const uint32_t d8[8] = {rw0.x, rw0.y, rw0.z, rw0.w, rw1.x, rw1.y, rw1.z, rw1.w};
+      const uint32_t d4[4] = {rw.x, rw.y, rw.z, rw.w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t x = d8[e];
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t x = d4[e];
         const uint32_t nz = ((x & 0x77777777u) + 0x77777777u) & 0x88888888u;
         const uint32_t m8 = x & 0x88888888u & ~nz;  // bit 3 of each marked nibble
         mk[e] = m8;
@@ -208,29 +207,37 @@ __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
         cnt += __builtin_popcount(m8);
       }
     }
-    uint2* sL = (uint2*)(smem + kOffL + (s & 1) * kStL);
+    uint2* sL = (uint2*)(smem + kOffL + (s & 1) * kStL) + (rb * 2 + f_own) * 64;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) sL[(rb * 2 + h) * 64 + g * 16 + rr] = make_uint2(wd[2 * g], wd[2 * g + 1]);
-      // this lane's sparse-tile entries: 16-slot group g at + g * 256
-    uint8_t* srow = smem + kOffS + (s & 1) * kStS + ((rb * 2 + h) * 64 + rr) * 16;
-    // marks of the first half of the row precede this lane's (partner lane ^ 1)
-    const int cnt_other = __shfl_xor(cnt, 1, 64);
-    const int v0 = vi + (h ? cnt_other : 0);  // value index of this lane's first mark
+    for (int e = 0; e < 2; ++e) sL[lpos(g0 + e, rr, f_own)] = make_uint2(wd[2 * e], wd[2 * e + 1]);
+    uint8_t* sblk = smem + kOffS + (s & 1) * kStS + (rb * 2 + f_own) * 1024;
+    // marks of the row's earlier lanes precede this lane's
+    int incl = cnt;
+    {
+      const int c1 = __shfl_up(incl, 1, 4);
+      if (qq >= 1) incl += c1;
+      const int c2 = __shfl_up(incl, 2, 4);
+      if (qq >= 2) incl += c2;
+    }
+    const int tot = __shfl(incl, 3, 4);
+    const int v0 = vi + incl - cnt;  // value index of this lane's first mark
     const int64_t a0 = (int64_t)gn * nnz + vi;
     const int64_t win_lo = a0 & ~(int64_t)15;  // the window the DMA brought
     const int64_t room = vtotal - win_lo;
     const int win_valid = !vdma ? 0 : room >= 64 ? 64 : (int)room & ~15;
     const int wo0 = (int)(a0 - win_lo) + (v0 - vi);  // offset of this lane's first value
     {
-      const uint32_t* vw = (const uint32_t*)(smem + kOffV + (s & 1) * kStV);
+      const uint8_t* vw = smem + kOffV + (s & 1) * kStV + r * 64;
+      auto vdw = [&](int o) { return *(const uint32_t*)(vw + o); };
       int pre = 0;
 #pragma unroll
-      for (int d = 0; d < 8; ++d) {
+      for (int d = 0; d < 4; ++d) {
         // byte offset of the group's first value; past the row's window the
         // bytes are not used (those lanes take the path below), so the read
         // only has to stay inside LDS
-        const int off = min(r * 64 + wo0 + pre, r * 64 + 64);
-        const uint32_t d0 = vw[off >> 2], d1 = vw[(off >> 2) + 1], d2 = vw[(off >> 2) + 2];
+        const int off = min(wo0 + pre, 64);
+        const int o4 = off & ~3;
+        const uint32_t d0 = vdw(o4), d1 = vdw(o4 + 4), d2 = vdw(o4 + 8);
         const uint32_t lo = __builtin_amdgcn_alignbyte(d1, d0, off & 3);
         const uint32_t hi = __builtin_amdgcn_alignbyte(d2, d1, off & 3);
         uint32_t x = mk[d] >> 3;  // mark bits at 4i -> bit i
@@ -238,7 +245,8 @@ __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
         x = (x | (x >> 6)) & 0x000F000Fu;
         x = (x | (x >> 12)) & 0xFFu;
         const uint2 sl = sSel[x];
-        *(uint2*)(srow + (d >> 1) * 256 + (d & 1) * 8) = make_uint2(perm(hi, lo, sl.x), perm(hi, lo, sl.y));
+        *(uint2*)(sblk + spos(g0 + (d >> 1), rr) * 16 + ((d & 1) ^ f_own) * 8) =
+            make_uint2(perm(hi, lo, sl.x), perm(hi, lo, sl.y));
         pre += __builtin_popcount(mk[d]);
       }
     }
@@ -246,18 +254,18 @@ __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
     if (wo0 + cnt > win_valid || v0 + cnt > nnz) {
       int j = 0;
 #pragma unroll
-      for (int d = 0; d < 8; ++d) {
+      for (int d = 0; d < 4; ++d) {
         uint32_t m8 = mk[d];
         while (m8) {
-          const int k = d * 8 + (__builtin_ctz(m8) >> 2);
+          const int k = d * 8 + (__builtin_ctz(m8) >> 2);  // slot within the lane's 32
           m8 &= m8 - 1;
           const int8_t v = v0 + j >= nnz ? (int8_t)0 : vrow[v0 + j];
-          srow[(k >> 4) * 256 + perm_pos(k & 15)] = (uint8_t)v;
+          sblk[spos(g0 + (k >> 4), rr) * 16 + (perm_pos(k & 15) ^ (f_own * 8))] = (uint8_t)v;
           ++j;
         }
       }
     }
-    vi += cnt + cnt_other;
+    vi += tot;
   };
 
   // this lane's read offset inside a 2 KiB block of 16 rows x 128 B for K
@@ -287,11 +295,12 @@ __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
       for (int i = 0; i < TM; ++i) a[i] = to_widened(*(const v4i*)(abuf + (wm * TM + i) * 2048 + rd_off[f]));
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int idx = ((wn * TN + j) * 2 + f) * 64 + lane;
-        const uint2 x = sL[idx];
+        const int blk = ((wn * TN + j) * 2 + f) * 64;
+        const uint2 x = sL[blk + lpos(lane >> 4, lane & 15, f)];
         const v4i bl = v4i{(int)((x.x << 4) & 0xF0F0F0F0u), (int)(x.x & 0xF0F0F0F0u),
                            (int)((x.y << 4) & 0xF0F0F0F0u), (int)(x.y & 0xF0F0F0F0u)};
-        const v4i bs = __builtin_bit_cast(v4i, sS[idx]);
+        v4i bs = __builtin_bit_cast(v4i, sS[blk + spos(lane >> 4, lane & 15)]);
+        if (f == 1) bs = v4i{bs.z, bs.w, bs.x, bs.y};
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
           acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], bl, acc[i][j], 0, 0, 0);
@@ -301,27 +310,54 @@ __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
     }
   };
 
+  // ---- int8 branch (outlier channels), 128 bytes per row per stage ----
+  // Branch stage t takes the A buffer (nst + t) % 2 and, for its W rows (16-row
+  // blocks swizzled like A), the raw W ring (t even) or the value ring (t odd):
+  // stages 0 and 1 load while the last low stages compute.  Both operands are
+  // in natural slot order.
+  auto br_a = [&](int t) { return kOffA + ((nst + t) & 1) * kStA; };
+  auto br_w = [&](int t) { return (t & 1) ? kOffV : kOffW; };
+  // (lane offsets formed here: they are needed at most a few times)
+  auto issue_branch = [&](int t) {
+    const int rl = lane >> 3;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = wave * 4 + i;
+      int row = m0 + q * 8 + rl;
+      if (row > mm - 1) row = mm - 1;
+      const uint32_t off = (uint32_t)row * (uint32_t)p.ldo + (uint32_t)(((lane & 7) ^ pair_swz(q & 1, rl)) * 16);
+      dma_16B(p.x_out, off + (uint32_t)t * 128u, sbase + (uint32_t)br_a(t) + (uint32_t)(q * 1024));
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int q = wave * 2 + i;
+      int row = n0 + q * 8 + rl;
+      if (row > nn - 1) row = nn - 1;
+      const uint32_t off = (uint32_t)row * (uint32_t)p.ldo + (uint32_t)(((lane & 7) ^ pair_swz(q & 1, rl)) * 16);
+      dma_16B(p.w_out, off + (uint32_t)t * 128u, sbase + (uint32_t)br_w(t) + (uint32_t)(q * 1024));
+    }
+  };
+
   // ---- prologue: stage 0 decoded, A 1 and W 2 in flight ----
   if (nst > 0) {
     issue_a(0);
     issue_w(0);
     if (nst > 1) issue_w(1);
-    if (decoder) issue_v(0);
+    issue_v(0);
     wait_vmcnt<0>();
     sq_sync();  // selector table, A 0, W 0 and 1, values 0
-    if (decoder) {
-      decode(0);
-      if (nst > 1) issue_v(1);
-    }
+    decode(0);
+    if (nst > 1) issue_v(1);
     wait_vmcnt<0>();
     sq_sync();  // decoded stage 0, values 1; W 0 is free
     if (nst > 1) issue_a(1);
+    else if (p.s_out > 0) issue_branch(0);
     if (nst > 2) issue_w(2);
   }
   // Iteration s: decode s+1 and the MFMAs of s; one barrier; then the DMAs of
   // A s+2 (into the buffer of A s) and W s+3 (into the buffer of W s+1).
   for (int s = 0; s < nst; ++s) {
-    if (decoder && s + 1 < nst) {
+    if (s + 1 < nst) {
       decode(s + 1);
       if (s + 2 < nst) issue_v(s + 2);
     }
@@ -330,6 +366,7 @@ __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
     wait_vmcnt<0>();
     sq_sync();
     if (s + 2 < nst) issue_a(s + 2);
+    else if (s + 2 - nst < p.s_out) issue_branch(s + 2 - nst);
     if (s + 3 < nst) issue_w(s + 3);
   }
 
@@ -353,65 +390,90 @@ __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
         acs[i][j][q] = 0;
       }
 
-  // ---- int8 branch (outlier channels), 128 bytes per row per stage ----
-  // A rows into A buffer 0, W rows (16-row blocks like A) over the raw W and
-  // value rings; the operands are in natural order on both sides.
-  if (p.s_out > 0) {
-    uint32_t o_off[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = wave * 4 + i, rl = lane >> 3;
-      int row = m0 + q * 8 + rl;
-      if (row > mm - 1) row = mm - 1;
-      o_off[i] = (uint32_t)row * (uint32_t)p.ldo + (uint32_t)(((lane & 7) ^ pair_swz(q & 1, rl)) * 16);
-    }
-    uint32_t wo_off[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int q = wave * 2 + i, rl = lane >> 3;
-      int row = n0 + q * 8 + rl;
-      if (row > nn - 1) row = nn - 1;
-      wo_off[i] = (uint32_t)row * (uint32_t)p.ldo + (uint32_t)(((lane & 7) ^ pair_swz(q & 1, rl)) * 16);
-    }
+  // ---- int8 branch stages (the first two are already in flight) ----
+  {
+    int bn = nst >= 1 ? (p.s_out < 2 ? p.s_out : 2) : 0;  // stages issued so far
     for (int t = 0; t < p.s_out; ++t) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        dma_16B(p.x_out, o_off[i] + (uint32_t)t * 128u, sbase + kOffA + (uint32_t)((wave * 4 + i) * 1024));
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        dma_16B(p.w_out, wo_off[i] + (uint32_t)t * 128u, sbase + kOffW + (uint32_t)((wave * 2 + i) * 1024));
+      if (bn == t) {
+        issue_branch(t);
+        ++bn;
+      }
       wait_vmcnt<0>();
       sq_sync();
 #pragma unroll
       for (int f = 0; f < 2; ++f) {
         v4i b[TN];
 #pragma unroll
-        for (int j = 0; j < TN; ++j) b[j] = *(const v4i*)(smem + kOffW + (wn * TN + j) * 2048 + rd_off[f]);
+        for (int j = 0; j < TN; ++j) b[j] = *(const v4i*)(smem + br_w(t) + (wn * TN + j) * 2048 + rd_off[f]);
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-          const v4i a = *(const v4i*)(smem + kOffA + (wm * TM + i) * 2048 + rd_off[f]);
+          const v4i a = *(const v4i*)(smem + br_a(t) + (wm * TM + i) * 2048 + rd_off[f]);
 #pragma unroll
           for (int j = 0; j < TN; ++j)
             acs[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[j], acs[i][j], 0, 0, 0);
         }
       }
       sq_sync();
+      // the buffers just read take stage t+2
+      if (bn == t + 2 && bn < p.s_out) {
+        issue_branch(bn);
+        ++bn;
+      }
     }
   }
 
+  // ---- fuse and store ----
+  // (the fused values replace the float partials in acc)
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int j = 0; j < TN; ++j) {
+    const int col = n0 + wn * 64 + j * 16 + lc;
+    const int cc = col < nn ? col : nn - 1;
+    const float swo = p.s_out > 0 ? p.s_wo[cc] : 0.0f;
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int row = m0 + wm * 64 + i * 16 + lr + q, col = n0 + wn * 64 + j * 16 + lc;
-        if (row >= mm || col >= nn) continue;
-        if (DEBUG) p.dbg_o[(int64_t)row * nn + col] = acs[i][j][q];
+        const int row = m0 + wm * 64 + i * 16 + lr + q;
+        const int rc = row < mm ? row : mm - 1;
+        if (DEBUG && row < mm && col < nn) p.dbg_o[(int64_t)row * nn + col] = acs[i][j][q];
         float v = __int_as_float(acc[i][j][q]);
-        if (p.s_out > 0) v += (p.s_xo[row] * p.s_wo[col]) * (float)acs[i][j][q];
-        p.y[(int64_t)row * p.ldy + col] = v;
+        if (p.s_out > 0) v += (p.s_xo[rc] * swo) * (float)acs[i][j][q];
+        acc[i][j][q] = __float_as_int(v);
       }
+  }
+  const int wrow0 = m0 + wm * 64, wcol0 = n0 + wn * 64;
+  const bool whole = wcol0 + 64 <= nn && (p.ldy & 3) == 0 && (((uintptr_t)p.y) & 15) == 0;
+  if (whole) {
+    // Row-contiguous 16-byte stores: each 16-row slice of the wave tile goes
+    // through this wave's rows of the (now free) A ring, padded by 4 floats
+    // per row (4-byte writes and 16-byte reads free of bank conflicts).
+    constexpr int LDW = 64 + 4;
+    float* stg = (float*)(smem + kOffA) + wave * (16 * LDW);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) stg[(lr + q) * LDW + j * 16 + lc] = __int_as_float(acc[i][j][q]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int idx = k * 64 + lane, rr2 = idx >> 4, c4 = idx & 15;
+        const v4f v = *(const v4f*)(stg + rr2 * LDW + 4 * c4);
+        const int row = wrow0 + i * 16 + rr2;
+        if (row < mm) *(v4f*)(p.y + (int64_t)row * p.ldy + wcol0 + 4 * c4) = v;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = wrow0 + i * 16 + lr + q, col = wcol0 + j * 16 + lc;
+          if (row < mm && col < nn) p.y[(int64_t)row * p.ldy + col] = __int_as_float(acc[i][j][q]);
+        }
+  }
 }
 
 hipError_t launch_sq_gemm(const SqArgs& a, bool debug, hipStream_t s) {
