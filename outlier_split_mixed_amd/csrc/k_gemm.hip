@@ -458,6 +458,8 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_du
   const bool whole = (GROUPED || wrow0 + WM <= mrows) && wcol0 + WN <= ncols &&
                      (p.ldy & 3) == 0 && (((uintptr_t)p.y) & 15) == 0;
   if (whole) {
+    // Y is written once and not read here: non-temporal stores keep it from
+    // evicting the operand panels other tiles still stream from L2.
     // Row-contiguous stores: each 16-row slice of the wave tile goes through
     // this wave's part of the pair buffer the K loop no longer uses (the one
     // that held pair NP-2; no DMA targets it any more), padded by 4 floats
@@ -480,7 +482,7 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_du
         const int idx = k * 64 + lane, rr = idx / (WN / 4), c4 = idx % (WN / 4);
         const v4f v = *(const v4f*)(stg + rr * LDW + 4 * c4);
         if (!GROUPED || wrow0 + i * 16 + rr < mrows)
-          *(v4f*)(y + (int64_t)(wrow0 + i * 16 + rr) * p.ldy + wcol0 + 4 * c4) = v;
+          __builtin_nontemporal_store(v, (v4f*)(y + (int64_t)(wrow0 + i * 16 + rr) * p.ldy + wcol0 + 4 * c4));
       }
     }
   } else {
@@ -494,7 +496,7 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_du
         for (int j = 0; j < TN; ++j) {
           const int col = col0 + j * 16;
           if (col >= ncols) continue;
-          y[(int64_t)row * p.ldy + col] = fused(i, j, r, row, col);
+          __builtin_nontemporal_store(fused(i, j, r, row, col), y + (int64_t)row * p.ldy + col);
         }
       }
     }

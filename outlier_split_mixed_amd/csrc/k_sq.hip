@@ -444,6 +444,7 @@ __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
   const int wrow0 = m0 + wm * 64, wcol0 = n0 + wn * 64;
   const bool whole = wcol0 + 64 <= nn && (p.ldy & 3) == 0 && (((uintptr_t)p.y) & 15) == 0;
   if (whole) {
+    // (non-temporal: Y is written once and not read here)
     // Row-contiguous 16-byte stores: each 16-row slice of the wave tile goes
     // through this wave's rows of the (now free) A ring, padded by 4 floats
     // per row (4-byte writes and 16-byte reads free of bank conflicts).
@@ -460,7 +461,7 @@ __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
         const int idx = k * 64 + lane, rr2 = idx >> 4, c4 = idx & 15;
         const v4f v = *(const v4f*)(stg + rr2 * LDW + 4 * c4);
         const int row = wrow0 + i * 16 + rr2;
-        if (row < mm) *(v4f*)(p.y + (int64_t)row * p.ldy + wcol0 + 4 * c4) = v;
+        if (row < mm) __builtin_nontemporal_store(v, (v4f*)(p.y + (int64_t)row * p.ldy + wcol0 + 4 * c4));
       }
     }
   } else {
@@ -471,7 +472,7 @@ __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int row = wrow0 + i * 16 + lr + q, col = wcol0 + j * 16 + lc;
-          if (row < mm && col < nn) p.y[(int64_t)row * p.ldy + col] = __int_as_float(acc[i][j][q]);
+          if (row < mm && col < nn) __builtin_nontemporal_store(__int_as_float(acc[i][j][q]), p.y + (int64_t)row * p.ldy + col);
         }
   }
 }
