@@ -196,10 +196,8 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
     if (m_first + f * m_step < m_stop) load_raw(m_first + f * m_step, ring[f]);
   lds_barrier();  // outlier list and zeroed images in place
 
-  auto row_body = [&](int64_t m, int it, uint32_t (&raw)[CPT][WPC]) {
-    const int buf = it & 1;
-    uint8_t* img = img0 + buf * img_bytes;
-    float* rd = red + buf * 2 * NW;
+  // the group of row m (expert groups): the map and outlier list follow it
+  auto enter_row = [&](int64_t m) {
     if constexpr (GROUPED) {
       // rows of a block are contiguous: advance to the group holding m
       while (m >= g_end) {
@@ -213,15 +211,21 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
         lds_barrier();
       }
     }
-    // ---- outlier channels: gathered from the row (cache-resident).  Issued
-    // before the next-row prefetch: loads retire in order, so waiting for
-    // these does not wait for the prefetch. ----
-    float ov[OPT];
+  };
+  // outlier channels of row m, gathered from the row (cache-resident).  The
+  // row loop issues these before the next-row prefetch: loads retire in
+  // order, so waiting for them does not wait for the prefetch.
+  auto gather = [&](int64_t m, float (&ov)[OPT]) {
 #pragma unroll
     for (int u = 0; u < OPT; ++u) {
       const int t = tid + u * NT;
       ov[u] = t < k_out ? xval(m, oidx[t]) : 0.0f;
     }
+  };
+  auto row_body = [&](int64_t m, int it, uint32_t (&raw)[CPT][WPC], const float (&ov)[OPT]) {
+    const int buf = it & 1;
+    uint8_t* img = img0 + buf * img_bytes;
+    float* rd = red + buf * 2 * NW;
     // Register pressure: the per-chunk constants are row-invariant and the
     // raw words are read twice; without these opaque redefinitions the
     // compiler keeps every derived value live across the whole loop.
@@ -358,9 +362,12 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
 #pragma unroll
     for (int u = 0; u <= PF; ++u) {
       if (m >= m_stop) break;
+      enter_row(m);
+      float ov[OPT];
+      gather(m, ov);
       // refill the buffer the previous row used with the row PF ahead
       if (m + PF * m_step < m_stop) load_raw(m + PF * m_step, ring[(u + PF) % (PF + 1)]);
-      row_body(m, it, ring[u]);
+      row_body(m, it, ring[u], ov);
       m += m_step;
       ++it;
     }
