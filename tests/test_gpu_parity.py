@@ -51,16 +51,30 @@ def test_row_width_extremes(sqf, k):
     _print("row width", k, st)
 
 
-@pytest.mark.parametrize("tile", ["0", "1", "2"])
-def test_ragged_every_tile_config(sqf, tile):
+@pytest.mark.parametrize("tile,branch", [("0", "bf16"), ("1", "bf16"), ("2", "bf16"),
+                                         ("0", "fp8"), ("1", "fp8"), ("2", "fp8")])
+def test_ragged_every_tile_config(sqf, tile, branch):
     """M, N and K_low are not multiples of any tile; K_out is not a multiple of 64."""
     lay = _ragged()
     os.environ["SQF_GEMM_TILE"] = tile
     try:
-        st, _ = run_layer(sqf, lay, lay.k_out)
+        st, _ = run_layer(sqf, lay, lay.k_out, branch=branch)
     finally:
         del os.environ["SQF_GEMM_TILE"]
-    _print("ragged tile", tile, st)
+    _print("ragged tile", tile, branch, st)
+
+
+@pytest.mark.parametrize("tile", ["0", "1"])
+def test_e4m3_every_channel_each_tile(sqf, tile):
+    """Every channel in the E4M3 branch (a long branch loop, no low stage) on
+    the 256x256 and 128x128 tiles."""
+    lay = _ragged(m=300, k=1024, n=520, n_scaled=64, seed=83)
+    os.environ["SQF_GEMM_TILE"] = tile
+    try:
+        st, _ = run_layer(sqf, lay, lay.k, branch="fp8")
+    finally:
+        del os.environ["SQF_GEMM_TILE"]
+    _print("k_out=k fp8 tile", tile, st)
 
 
 @pytest.mark.parametrize("branch", ["bf16", "fp8"])
@@ -208,7 +222,7 @@ def _moe_small(experts=6, tokens=96, topk=2, hidden=512, inter=256, seed=86):
                            inter=inter, cal_rows=64)
 
 
-@pytest.mark.parametrize("branch,tile", [("bf16", "1"), ("bf16", "0"), ("fp8", "1")])
+@pytest.mark.parametrize("branch,tile", [("bf16", "1"), ("bf16", "0"), ("fp8", "1"), ("fp8", "0")])
 def test_grouped_small_with_empty_group(sqf, branch, tile):
     """Ragged expert groups, one of them empty, on both grouped tile shapes."""
     moe = _moe_small()
