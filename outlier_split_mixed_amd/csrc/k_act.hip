@@ -377,9 +377,10 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
 template <int XT, int LOW, int BR, bool GROUPED, int NT, int CPT>
 static hipError_t launch_one(const ActArgs& a, int64_t cap, size_t lds, hipStream_t s) {
   auto kern = k_act_split<XT, LOW, BR, GROUPED, NT, CPT>;
-  // about 16 waves per CU over the 256 CUs; each block walks a strided set
-  // of rows, so the per-block setup (the channel map) is amortised
-  int64_t grid = (int64_t)256 * 16 * 64 / NT;
+  // about 16 waves per CU over the 256 CUs (32 single-wave blocks); each
+  // block walks a set of rows, so the per-block setup (the channel map) is
+  // amortised
+  int64_t grid = NT == 64 ? (int64_t)256 * 32 : (int64_t)256 * 16 * 64 / NT;
   if (cap > 0) grid = cap;
   if (grid > a.m) grid = a.m;
   if (lds > 65536) {
@@ -394,8 +395,12 @@ static hipError_t launch_one(const ActArgs& a, int64_t cap, size_t lds, hipStrea
 template <int XT, int LOW, int BR, bool GROUPED>
 static hipError_t launch_shape(const ActArgs& a, int64_t cap, size_t lds, hipStream_t s) {
   const int64_t chunks = a.k / 8;
-  if (chunks <= 128) return launch_one<XT, LOW, BR, GROUPED, 128, 1>(a, cap, lds, s);
-  if (chunks <= 256) return launch_one<XT, LOW, BR, GROUPED, 256, 1>(a, cap, lds, s);
+  // rows of up to 2048 channels: one wave per block, so that the per-row
+  // reduction and image hand-off need no cross-wave barrier wait and many
+  // more rows are in flight per CU
+  if (chunks <= 64) return launch_one<XT, LOW, BR, GROUPED, 64, 1>(a, cap, lds, s);
+  if (chunks <= 128) return launch_one<XT, LOW, BR, GROUPED, 64, 2>(a, cap, lds, s);
+  if (chunks <= 256) return launch_one<XT, LOW, BR, GROUPED, 64, 4>(a, cap, lds, s);
   if (chunks <= 512) return launch_one<XT, LOW, BR, GROUPED, 256, 2>(a, cap, lds, s);
   if (chunks <= 1024) return launch_one<XT, LOW, BR, GROUPED, 256, 4>(a, cap, lds, s);
   if (chunks <= 2048) return launch_one<XT, LOW, BR, GROUPED, 512, 4>(a, cap, lds, s);
