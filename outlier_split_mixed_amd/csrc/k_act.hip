@@ -402,7 +402,7 @@ static hipError_t launch_shape(const ActArgs& a, int64_t cap, size_t lds, hipStr
   if (chunks <= 128) return launch_one<XT, LOW, BR, GROUPED, 64, 2>(a, cap, lds, s);
   if (chunks <= 256) return launch_one<XT, LOW, BR, GROUPED, 64, 4>(a, cap, lds, s);
   if (chunks <= 512) return launch_one<XT, LOW, BR, GROUPED, 256, 2>(a, cap, lds, s);
-  if (chunks <= 1024) return launch_one<XT, LOW, BR, GROUPED, 256, 4>(a, cap, lds, s);
+  if (chunks <= 1024) return launch_one<XT, LOW, BR, GROUPED, 512, 2>(a, cap, lds, s);
   if (chunks <= 2048) return launch_one<XT, LOW, BR, GROUPED, 512, 4>(a, cap, lds, s);
   if (chunks <= 4096) return launch_one<XT, LOW, BR, GROUPED, 1024, 4>(a, cap, lds, s);
   return launch_one<XT, LOW, BR, GROUPED, 1024, 8>(a, cap, lds, s);
