@@ -203,7 +203,7 @@ __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
         const uint32_t nz = ((x & 0x77777777u) + 0x77777777u) & 0x88888888u;
         const uint32_t m8 = x & 0x88888888u & ~nz;  // bit 3 of each marked nibble
         mk[e] = m8;
-        wd[e] = x & ~((m8 - (m8 >> 3)) | m8);
+        wd[e] = x ^ m8;  // a marked nibble is exactly 0x8
         cnt += __builtin_popcount(m8);
       }
     }
@@ -240,10 +240,10 @@ __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
         const uint32_t d0 = vdw(o4), d1 = vdw(o4 + 4), d2 = vdw(o4 + 8);
         const uint32_t lo = __builtin_amdgcn_alignbyte(d1, d0, off & 3);
         const uint32_t hi = __builtin_amdgcn_alignbyte(d2, d1, off & 3);
-        uint32_t x = mk[d] >> 3;  // mark bits at 4i -> bit i
-        x = (x | (x >> 3)) & 0x03030303u;
-        x = (x | (x >> 6)) & 0x000F000Fu;
-        x = (x | (x >> 12)) & 0xFFu;
+        // mark bits at 4i + 3 -> bit i: two per byte, then one 4-way
+        // weighted byte sum (weights 1, 4, 16, 64)
+        const uint32_t t2 = ((mk[d] >> 3) | (mk[d] >> 6)) & 0x03030303u;
+        const uint32_t x = __builtin_amdgcn_udot4(t2, 0x40100401u, 0u, false);
         const uint2 sl = sSel[x];
         *(uint2*)(sblk + spos(g0 + (d >> 1), rr) * 16 + ((d & 1) ^ f_own) * 8) =
             make_uint2(perm(hi, lo, sl.x), perm(hi, lo, sl.y));
