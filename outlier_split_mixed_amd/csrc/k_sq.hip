@@ -33,9 +33,9 @@
 // row's running value index (known once the previous stage is decoded).
 // Iteration s decodes stage s+1 (every wave its own 16 W rows, four lanes per
 // row) and runs the MFMAs of stage s in one basic block, so the decode's
-// vector ALU work can issue between the MFMAs; one barrier per stage.  The DMAs of A
-// stage s+2 and W stage s+3 start right after that barrier, and the value
-// window of stage s+2 right after stage s+1 is decoded.
+// vector ALU work can issue between the MFMAs; one barrier per stage.  The
+// DMAs of A stage s+2 and W stage s+3 start right after that barrier, and the
+// value window of stage s+2 right after stage s+1 is decoded.
 #include "sqf_device.h"
 #include "sqf_launch.h"
 

@@ -238,6 +238,20 @@ def test_grouped_small_with_empty_group(sqf, branch, tile):
         del os.environ["SQF_GEMM_TILE"]
 
 
+@pytest.mark.parametrize("tile", ["0", "1"])
+def test_grouped_many_groups(sqf, tile):
+    """600 expert groups of 0-4 rows: more groups than one block-wide pass of
+    the tile lookup covers (256 or 512 per pass), many of them empty."""
+    moe = synth.qwen3_moe(seed=87, experts=600, tokens=300, topk=2, hidden=256, inter=128,
+                          cal_rows=32)
+    assert any(l.m == 0 for l in moe.up)
+    os.environ["SQF_GEMM_TILE"] = tile
+    try:
+        _grouped_check(sqf, moe.up, "bf16")
+    finally:
+        del os.environ["SQF_GEMM_TILE"]
+
+
 def _grouped_check(sqf, lays, branch, rows_per_group=None):
     g = len(lays)
     k, n, k_out = lays[0].k, lays[0].n, lays[0].k_out
