@@ -19,57 +19,138 @@
 
 namespace sqf {
 
-// One thread per output channel; reads of W[c][n] are coalesced across the
-// wave, map[c] is wave-uniform.  Two passes over the column: absmax, codes.
+// Channel-split packer.  A block of 1024 threads (16 waves) owns 64 output
+// channels: lane l of every wave works on column n0 + l, so each wave-wide
+// load of one weight row W[c][n0 .. n0+63] is 256 contiguous bytes.  Pass 1:
+// the waves split the K rows (wave w takes rows w, w+16, ...) for the low and
+// outlier absmax of their columns, combined across waves through LDS.  Pass 2
+// walks the slot space in chunks of kPackChunk slots: the block scatters the
+// map into an LDS slot -> channel list for the chunk, then each wave packs
+// 32-slot groups (one 16-byte store per lane) from the listed rows.  The
+// branch rows are packed the same way, 16 bytes per lane per store.  Every
+// code is a function of its own value and its column's absmax alone, so the
+// result is the same as a sequential walk over the column.
+constexpr int kPackCols = 64;
+constexpr int kPackWaves = 16;
+constexpr int kPackChunk = 8192;
+
 template <int BR>
-__global__ __launch_bounds__(256) void k_pack_osc(PackArgs p) {
+__global__ __launch_bounds__(1024) void k_pack_osc(PackArgs p) {
+  __shared__ int32_t list[kPackChunk];
+  __shared__ float red[2][kPackWaves][kPackCols];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t g = blockIdx.y;
-  const int64_t nn = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (nn >= p.n) return;
-  const float* w = p.w + g * p.k * p.n;
+  const int64_t nn = (int64_t)blockIdx.x * kPackCols + lane;
+  const bool live = nn < p.n;
+  const float* w = p.w + g * p.k * p.n + (live ? nn : 0);
   const int32_t* map = p.map + g * p.k;
-  uint8_t* wl = p.w_low + (g * p.n + nn) * p.ldk;
   constexpr int ESZ = BR == kBF16 ? 2 : 1;
-  uint8_t* wo = p.w_out ? p.w_out + (g * p.n + nn) * p.ldo * ESZ : nullptr;
 
+  // pass 1: absmax over the low and the outlier channels of the column
   float alo = 0.0f, ahi = 0.0f;
-  for (int64_t c = 0; c < p.k; ++c) {
-    float a = fabsf(w[c * p.n + nn]);
-    if (map[c] >= 0) alo = fmaxf(alo, a); else ahi = fmaxf(ahi, a);
-  }
-  const float inv = quant_inv(alo, 7.0f);
-  p.s_w[g * p.n + nn] = quant_scale(alo, 7.0f);
-  const float qhi = BR == kFP8 ? 448.0f : 127.0f;
-  const float inv_hi = BR == kBF16 ? 0.0f : quant_inv(ahi, qhi);
-  if (BR != kBF16 && p.s_wo) p.s_wo[g * p.n + nn] = quant_scale(ahi, qhi);
-
-  uint32_t buf[4] = {0, 0, 0, 0};
-  int cnt = 0;
-  int64_t grp = 0;
-  for (int64_t c = 0; c < p.k; ++c) {
-    const int32_t s = map[c];
-    const float v = w[c * p.n + nn];
-    if (s >= 0) {
-      uint32_t nib = (uint32_t)quant_code(v, inv, 7.0f) & 0xFu;
-      buf[cnt >> 3] |= nib << ((cnt & 7) * 4);
-      if (++cnt == 32) {
-        *(uint4*)(wl + grp * 16) = make_uint4(buf[0], buf[1], buf[2], buf[3]);
-        buf[0] = buf[1] = buf[2] = buf[3] = 0;
-        cnt = 0;
-        ++grp;
+  {
+    int64_t c = wv;
+    for (; c + 7 * kPackWaves < p.k; c += 8 * kPackWaves) {
+      float v[8];
+      int32_t m[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        m[u] = map[c + u * kPackWaves];
+        v[u] = fabsf(w[(c + u * kPackWaves) * p.n]);
       }
-    } else {
-      const int t = -s - 1;
-      if constexpr (BR == kBF16) ((uint16_t*)wo)[t] = (uint16_t)bf16_rne(v);
-      else if constexpr (BR == kFP8) wo[t] = (uint8_t)e4m3_rne_sat(v * inv_hi);
-      else wo[t] = (uint8_t)quant_code(v, inv_hi, 127.0f);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (m[u] >= 0) alo = fmaxf(alo, v[u]); else ahi = fmaxf(ahi, v[u]);
+      }
+    }
+    for (; c < p.k; c += kPackWaves) {
+      const float v = fabsf(w[c * p.n]);
+      if (map[c] >= 0) alo = fmaxf(alo, v); else ahi = fmaxf(ahi, v);
     }
   }
-  for (; grp < p.ldk / 16; ++grp) {  // flush the partial group, then zero padding
-    *(uint4*)(wl + grp * 16) = make_uint4(buf[0], buf[1], buf[2], buf[3]);
-    buf[0] = buf[1] = buf[2] = buf[3] = 0;
+  red[0][wv][lane] = alo;
+  red[1][wv][lane] = ahi;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kPackWaves; ++i) {
+    alo = fmaxf(alo, red[0][i][lane]);
+    ahi = fmaxf(ahi, red[1][i][lane]);
   }
-  for (int64_t t = p.k_out * ESZ; t < p.ldo * ESZ; ++t) wo[t] = 0;
+  const float inv = quant_inv(alo, 7.0f);
+  const float qhi = BR == kFP8 ? 448.0f : 127.0f;
+  const float inv_hi = BR == kBF16 ? 0.0f : quant_inv(ahi, qhi);
+  if (wv == 0 && live) {
+    p.s_w[g * p.n + nn] = quant_scale(alo, 7.0f);
+    if (BR != kBF16 && p.s_wo) p.s_wo[g * p.n + nn] = quant_scale(ahi, qhi);
+  }
+
+  // slot -> channel list for slots [s0, s0 + kPackChunk) of one kind (low:
+  // map value s, outlier: map value -(t+1)); unlisted slots read as value 0
+  auto build_list = [&](int64_t s0, bool low) {
+    __syncthreads();  // the previous chunk's readers are done
+    for (int i = threadIdx.x; i < kPackChunk; i += 1024) list[i] = -1;
+    __syncthreads();
+    const int64_t lim = low ? p.k_low : p.k_out;
+    for (int64_t c = threadIdx.x; c < p.k; c += 1024) {
+      const int32_t m = map[c];
+      const int64_t s = low ? (int64_t)m : -(int64_t)m - 1;
+      if (s >= s0 && s < s0 + kPackChunk && s < lim) list[s - s0] = (int32_t)c;
+    }
+    __syncthreads();
+  };
+
+  // pass 2a: int4 codes, 32 slots per 16-byte group, zero past k_low
+  uint8_t* wl = p.w_low + (g * p.n + nn) * p.ldk;
+  const int64_t slots = p.ldk * 2;
+  for (int64_t s0 = 0; s0 < slots; s0 += kPackChunk) {
+    const int64_t s1 = s0 + kPackChunk < slots ? s0 + kPackChunk : slots;
+    if (s0 < p.k_low) build_list(s0, true);
+    for (int64_t q = s0 / 32 + wv; q < s1 / 32; q += kPackWaves) {
+      uint32_t ow[4] = {0, 0, 0, 0};
+      if (q * 32 < p.k_low) {
+        float v[32];
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+          const int32_t c = list[q * 32 - s0 + e];  // -1 past k_low (cleared)
+          v[e] = c >= 0 ? w[(int64_t)c * p.n] : 0.0f;
+        }
+#pragma unroll
+        for (int e = 0; e < 32; ++e)
+          ow[e >> 3] |= ((uint32_t)quant_code(v[e], inv, 7.0f) & 0xFu) << ((e & 7) * 4);
+      }
+      if (live) *(uint4*)(wl + q * 16) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+    }
+  }
+
+  // pass 2b: branch codes, 16 bytes per store, zero past k_out
+  if (p.w_out == nullptr || p.ldo == 0) return;
+  constexpr int PER = 16 / ESZ;  // elements per 16-byte store
+  uint8_t* wo = p.w_out + (g * p.n + nn) * p.ldo * ESZ;
+  for (int64_t s0 = 0; s0 < p.ldo; s0 += kPackChunk) {
+    const int64_t s1 = s0 + kPackChunk < p.ldo ? s0 + kPackChunk : p.ldo;
+    if (s0 < p.k_out) build_list(s0, false);
+    for (int64_t q = s0 / PER + wv; q < s1 / PER; q += kPackWaves) {
+      uint32_t ow[4] = {0, 0, 0, 0};
+      if (q * PER < p.k_out) {
+        float v[PER];
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+          const int32_t c = list[q * PER - s0 + e];
+          v[e] = c >= 0 ? w[(int64_t)c * p.n] : 0.0f;
+        }
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+          uint32_t code;
+          if constexpr (BR == kBF16) code = bf16_rne(v[e]);
+          else if constexpr (BR == kFP8) code = e4m3_rne_sat(v[e] * inv_hi);
+          else code = (uint32_t)quant_code(v[e], inv_hi, 127.0f) & 0xFFu;
+          ow[e / (4 / ESZ)] |= code << ((e % (4 / ESZ)) * 8 * ESZ);
+        }
+      }
+      if (live) *(uint4*)(wo + q * 16) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+    }
+  }
 }
 
 // Block-wide helpers for the weight-side kernel (256 threads).
@@ -221,10 +302,11 @@ hipError_t launch_pack(const PackArgs& a, int branch, int groups, hipStream_t s)
     hipLaunchKernelGGL(k_pack_sq, dim3((unsigned)a.n), dim3(256), lds, s, a);
     return hipGetLastError();
   }
-  dim3 grid((unsigned)((a.n + 255) / 256), (unsigned)groups);
-  if (branch == kBF16) hipLaunchKernelGGL(k_pack_osc<kBF16>, grid, dim3(256), 0, s, a);
-  else if (branch == kFP8) hipLaunchKernelGGL(k_pack_osc<kFP8>, grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(k_pack_osc<kI8>, grid, dim3(256), 0, s, a);
+  dim3 grid((unsigned)((a.n + kPackCols - 1) / kPackCols), (unsigned)groups);
+  dim3 block(kPackCols * kPackWaves);
+  if (branch == kBF16) hipLaunchKernelGGL(k_pack_osc<kBF16>, grid, block, 0, s, a);
+  else if (branch == kFP8) hipLaunchKernelGGL(k_pack_osc<kFP8>, grid, block, 0, s, a);
+  else hipLaunchKernelGGL(k_pack_osc<kI8>, grid, block, 0, s, a);
   return hipGetLastError();
 }
 
