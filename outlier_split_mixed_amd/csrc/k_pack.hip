@@ -185,11 +185,17 @@ __device__ __forceinline__ int block_excl_scan(int v, int* scratch) {
 
 // One block (256 threads) per output channel.  Thread t owns the contiguous
 // slot range [t*per, (t+1)*per) so block scans give slot order directly.
+// A block reads one column of W (one 4-byte value per row); consecutive
+// blocks run on different XCDs (block b on XCD b mod 8), so XCD x is given the
+// contiguous column range [x*per_x, (x+1)*per_x): its concurrently running
+// blocks then share the 128-byte lines of W in their XCD's L2.
 __global__ __launch_bounds__(256) void k_pack_sq(PackArgs p) {
   extern __shared__ uint8_t sm[];
   __shared__ int iscr[8];
   __shared__ float fscr[8];
-  const int64_t nn = blockIdx.x;
+  const int64_t per_x = gridDim.x >> 3;  // the grid is a multiple of 8
+  const int64_t nn = (int64_t)(blockIdx.x & 7) * per_x + (blockIdx.x >> 3);
+  if (nn >= p.n) return;
   const int tid = threadIdx.x;
   const int64_t kl = p.k_low;
   float* vals = (float*)sm;                   // [k_low]
@@ -258,9 +264,10 @@ __global__ __launch_bounds__(256) void k_pack_sq(PackArgs p) {
   int kc = 0;
   for (int64_t j = j0; j < j1; ++j) kc += keep[j];
   int pos = block_excl_scan(kc, iscr);
+  const int before = pos;
   for (int64_t j = j0; j < j1; ++j)
     if (keep[j]) p.sq_val[nn * p.nnz + pos++] = (int8_t)quant_code(vals[j], inv8, 127.0f);
-  __syncthreads();
+  const int total = block_sum_i(kc, iscr);
   // packed row: 16-byte groups of 32 slots
   uint8_t* wl = p.w_low + nn * p.ldk;
   for (int64_t q = tid; q < p.ldk / 16; q += 256) {
@@ -273,14 +280,17 @@ __global__ __launch_bounds__(256) void k_pack_sq(PackArgs p) {
     }
     *(uint4*)(wl + q * 16) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
   }
-  // marked-slot count before each 256-slot tile
+  // marked-slot count before each 256-slot tile: the thread whose slot range
+  // holds a tile's first slot counts from its own prefix; tiles that start
+  // past k_low get the row total
   const int64_t ntiles = p.ldk / 128;
-  for (int64_t t = tid; t <= ntiles; t += 256) {
-    int cnt = 0;
-    int64_t lim = t * 256 < kl ? t * 256 : kl;
-    for (int64_t j = 0; j < lim; ++j) cnt += keep[j];
-    p.tile_off[nn * (ntiles + 1) + t] = cnt;
+  int32_t* toff = p.tile_off + nn * (ntiles + 1);
+  for (int64_t b = (j0 + 255) / 256 * 256; b < j1; b += 256) {
+    int cnt = before;
+    for (int64_t j = j0; j < b; ++j) cnt += keep[j];
+    toff[b / 256] = cnt;
   }
+  for (int64_t t = (kl + 255) / 256 + tid; t <= ntiles; t += 256) toff[t] = total;
   // int8 branch over the outlier channels
   float ao = 0.0f;
   for (int64_t t = tid; t < p.k_out; t += 256) ao = fmaxf(ao, fabsf(ov[t]));
@@ -299,7 +309,7 @@ hipError_t launch_pack(const PackArgs& a, int branch, int groups, hipStream_t s)
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k_pack_sq, dim3((unsigned)a.n), dim3(256), lds, s, a);
+    hipLaunchKernelGGL(k_pack_sq, dim3((unsigned)((a.n + 7) / 8 * 8)), dim3(256), lds, s, a);
     return hipGetLastError();
   }
   dim3 grid((unsigned)((a.n + kPackCols - 1) / kPackCols), (unsigned)groups);

@@ -113,6 +113,45 @@ def test_zero_token_rows_and_single_row(sqf):
     run_layer(sqf, one, one.k_out)
 
 
+@pytest.mark.parametrize("k,n", [(2500, 517), (1030, 1536)])
+def test_selection_ties_and_ragged_rows(sqf, k, n):
+    """Groups of channels with equal scores straddle the k_out boundary (the
+    lower channel must win), K spans several rank slices with a ragged last
+    one, and the weight rows are either not a multiple of 4 long (scalar
+    loads) or several 512-column stages long.  The map, idx, fp64 scores and
+    hdiag must match the oracle bit for bit; the packed weights too."""
+    lay = synth.draw_layer("ties", 88, 0, 8, k, n, 40, k // 16, draw_x=False)
+    x_cal, w = lay.x_cal.copy(), lay.w.copy()
+    k_out = k // 16
+    o_score = oracle.select_channels(x_cal, w, k_out)[2]
+    order = np.argsort(-o_score, kind="stable")
+    # copy channel order[k_out - 1] into four channels around the boundary and
+    # channel order[3] into two others: equal columns of x_cal and equal rows of
+    # W give equal scores
+    src_a, src_b = int(order[k_out - 1]), int(order[3])
+    for dst in (int(order[k_out - 3]), int(order[k_out]), int(order[k_out + 2]), int(order[-1])):
+        x_cal[:, dst], w[dst] = x_cal[:, src_a], w[src_a]
+    for dst in (int(order[k_out + 5]), int(order[0])):
+        x_cal[:, dst], w[dst] = x_cal[:, src_b], w[src_b]
+    idx, mp, score, hdiag = sqf.sqf_select_channels(torch.from_numpy(x_cal).cuda(),
+                                                    torch.from_numpy(w).cuda(), k_out)
+    wts = sqf.sqf_pack_weights(torch.from_numpy(w).cuda(), mp)
+    torch.cuda.synchronize()
+    o_idx, o_mp, o_sc, o_hd = oracle.select_channels(x_cal, w, k_out)
+    sc = o_sc[o_idx]
+    assert (sc == o_sc[src_a]).any() and (o_sc[np.setdiff1d(np.arange(k), o_idx)] == o_sc[src_a]).any(), \
+        "the tie group must straddle the boundary"
+    assert np.array_equal(score.cpu().numpy().view(np.uint64), o_sc.view(np.uint64))
+    assert np.array_equal(idx.cpu().numpy(), o_idx)
+    assert np.array_equal(mp.cpu().numpy(), o_mp)
+    assert f32_bits_equal(hdiag.cpu().numpy(), o_hd)
+    o_w = oracle.pack_weights(w, o_mp)
+    assert np.array_equal(wts.t["w_low"][0].cpu().numpy(), o_w["w_low"])
+    assert f32_bits_equal(wts.t["s_w"][0].cpu().numpy(), o_w["s_w"])
+    assert np.array_equal(wts.t["w_out"][0].cpu().numpy().view(o_w["w_out"].dtype), o_w["w_out"])
+    _print("ties", k, n, "boundary score", o_sc[src_a])
+
+
 def test_m_zero_is_a_no_op(sqf):
     acts = sqf.alloc_acts(0, 480, 32)
     w = sqf.alloc_weights(512, 64, 32)
