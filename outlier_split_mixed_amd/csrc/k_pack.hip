@@ -193,6 +193,8 @@ __global__ __launch_bounds__(256) void k_pack_sq(PackArgs p) {
   extern __shared__ uint8_t sm[];
   __shared__ int iscr[8];
   __shared__ float fscr[8];
+  __shared__ int hist[256];
+  __shared__ int sel[2];
   const int64_t per_x = gridDim.x >> 3;  // the grid is a multiple of 8
   const int64_t nn = (int64_t)(blockIdx.x & 7) * per_x + (blockIdx.x >> 3);
   if (nn >= p.n) return;
@@ -221,14 +223,49 @@ __global__ __launch_bounds__(256) void k_pack_sq(PackArgs p) {
     double key = wv * wv * (double)hd[j];  // >= 0: bit pattern is monotone
     return (uint64_t)__double_as_longlong(key);
   };
-  // threshold T = nnz-th largest key (bitwise binary search over the keys)
+  // threshold T = nnz-th largest key (0 when there are fewer keys): radix
+  // select over the 64-bit patterns, 8 bits per pass from the top.  Each pass
+  // histograms the next byte of the keys that match the bytes chosen so far,
+  // then takes the largest byte d whose keys at or above it still cover the
+  // `need` keys not yet accounted for above the matching range.
   uint64_t T = 0;
   if (p.nnz > 0) {
-    for (int bit = 63; bit >= 0; --bit) {
-      uint64_t cand = T | (1ull << bit);
-      int cnt = 0;
-      for (int64_t j = j0; j < j1; ++j) cnt += keybits(j) >= cand;
-      if (block_sum_i(cnt, iscr) >= p.nnz) T = cand;
+    uint64_t mask = 0;
+    int need = (int)p.nnz;
+    for (int shift = 56; shift >= 0; shift -= 8) {
+      hist[tid] = 0;
+      __syncthreads();
+      for (int64_t j = j0; j < j1; ++j) {
+        const uint64_t kb = keybits(j);
+        if ((kb & mask) == T) atomicAdd(&hist[(kb >> shift) & 255], 1);
+      }
+      __syncthreads();
+      if (tid < 64) {  // wave 0: lane l holds bins 4l .. 4l+3
+        const int h0 = hist[4 * tid], h1 = hist[4 * tid + 1], h2 = hist[4 * tid + 2],
+                  h3 = hist[4 * tid + 3];
+        const int s_l = h0 + h1 + h2 + h3;
+        const int incl = wave_inclusive_scan(s_l);
+        const int above = __shfl(incl, 63, 64) - incl;  // keys in the bins of lanes > l
+        const int s3 = above + h3, s2 = s3 + h2, s1 = s2 + h1, s0 = s1 + h0;
+        int d = -1, cover = 0, hd_d = 0;
+        if (s3 >= need) { d = 4 * tid + 3; cover = s3; hd_d = h3; }
+        else if (s2 >= need) { d = 4 * tid + 2; cover = s2; hd_d = h2; }
+        else if (s1 >= need) { d = 4 * tid + 1; cover = s1; hd_d = h1; }
+        else if (s0 >= need) { d = 4 * tid; cover = s0; hd_d = h0; }
+        int best = d;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) best = max(best, __shfl_xor(best, off, 64));
+        if (best < 0) {
+          if (tid == 0) { sel[0] = 0; sel[1] = need; }
+        } else if (d == best) {
+          sel[0] = best;
+          sel[1] = need - (cover - hd_d);  // keys above byte d are already in
+        }
+      }
+      __syncthreads();
+      T |= (uint64_t)sel[0] << shift;
+      need = sel[1];
+      mask |= 255ull << shift;
     }
   }
   // keep = key > T, plus the lowest-slot keys equal to T until nnz are kept
