@@ -329,15 +329,24 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_du
         mid_sync(t);
         __builtin_amdgcn_sched_barrier(0);
       }
+      // Wave priority: the two waves of a SIMD cross the same barriers and
+      // so tend to reach their MFMA runs together.  Each wave raises its
+      // priority after its first 16-row fragment and drops it before the
+      // last: the raised wave issues its MFMAs back to back while the other
+      // one, at the lower level, widens operands and reads LDS (+4-6% on
+      // the whole kernel against no priority change, measured).
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         if (GROUPED && i >= live) break;
+        if (i == 1) __builtin_amdgcn_s_setprio(1);
+        if (i == TM - 1) __builtin_amdgcn_s_setprio(0);
         const v4i aa = i == 0 ? a0w[half]
                               : widen((uint32_t)A[i][2 * half], (uint32_t)A[i][2 * half + 1]);
 #pragma unroll
         for (int j = 0; j < TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aa, bw[half][j], acc[i][j], 0, 0, 0);
       }
+      __builtin_amdgcn_s_setprio(0);
     }
   }
 
