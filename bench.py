@@ -199,10 +199,17 @@ def rows_section(sqf, torch, stream):
         t = time_call(torch, stream, lambda: sqf.sqf_select_channels(x_cal, w, k_out, stream=stream),
                       iters=3, warmup=1)
         _, mp, _, _ = sqf.sqf_select_channels(x_cal, w, k_out, stream=stream)
+        # algorithmic bytes: x_cal and W read once, scores / hdiag / map / idx written
+        b0 = 4 * lay.x_cal.size + 4 * lay.k * lay.n + (8 + 4 + 4) * lay.k + 4 * k_out
         out.append(dict(row="a0 select (offline)", shape=f"{lay.k}x{lay.n}, {lay.x_cal.shape[0]} cal rows",
-                        ms=round(t, 3)))
+                        ms=round(t, 3), gbs=round(b0 / t / 1e6, 1), frac_hbm=round(b0 / t / 1e6 / PEAK_HBM_GBS, 3)))
         t = time_call(torch, stream, lambda: sqf.sqf_pack_weights(w, mp, stream=stream), iters=3, warmup=1)
-        out.append(dict(row="a1 pack (offline)", shape=f"{lay.k}x{lay.n}", ms=round(t, 3)))
+        # W and the map read once; int4 rows, bf16 branch rows and scales written
+        ldk = sqf.sqf_pad_k_low(lay.k - k_out) // 2
+        ldo = sqf.sqf_pad_k_out(k_out, "bf16")
+        b1 = 4 * lay.k * lay.n + 4 * lay.k + lay.n * (ldk + 2 * ldo + 4)
+        out.append(dict(row="a1 pack (offline)", shape=f"{lay.k}x{lay.n}", ms=round(t, 3),
+                        gbs=round(b1 / t / 1e6, 1), frac_hbm=round(b1 / t / 1e6 / PEAK_HBM_GBS, 3)))
         del w, x_cal, mp
         torch.cuda.empty_cache()
 
