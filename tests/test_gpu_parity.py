@@ -215,6 +215,21 @@ def test_sq_weight_side_mark_density(sqf, m, k, n, den):
     _sq_check(sqf, lay, max(1, (lay.k - lay.k_out) // den), f"sq m{m} k{k} n{n} 1/{den}")
 
 
+@pytest.mark.parametrize("frac", [0.125, 0.9])
+def test_sq_weight_side_key_ties(sqf, frac):
+    """Many equal importance keys: W on a coarse grid of 5 values (a fifth of
+    them zero) and calibration columns repeated in groups of 4 channels, so
+    the nnz-th largest key sits inside a group of equal keys (lowest slots
+    win); at 0.9 of the low slots the threshold is the zero key itself."""
+    lay = _ragged(m=96, k=1024, n=136, n_scaled=64, seed=93)
+    lay.w[:] = np.clip(np.rint(lay.w / 0.01), -2, 2).astype(np.float32) * np.float32(0.01)
+    for c in range(0, lay.k - 3, 4):
+        lay.x_cal[:, c + 1:c + 4] = lay.x_cal[:, c:c + 1]
+    nnz = int((lay.k - lay.k_out) * frac)
+    _print(f"sq key ties nnz={nnz}")
+    _sq_check(sqf, lay, nnz, f"sq ties {frac}")
+
+
 def _sq_check(sqf, lay, nnz, label):
     k_out = lay.k_out
     k_low = lay.k - k_out
