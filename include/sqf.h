@@ -145,7 +145,8 @@ int64_t sqf_pad_k_out(int64_t k_out, int32_t branch);
  *   hdiag[c] = (float) sum_m x_cal[m,c]^2                            (fp64 sum)
  * The k_out channels of highest score (ties: lower index) become outliers.
  * Outputs: idx_out [k_out] ascending (may be NULL if k_out == 0), map_out
- * [k], score_out [k] (required: also used as workspace), hdiag_out [k] or
+ * [k] (required: holds the rank counts until the map is written),
+ * score_out [k] (required: also used as workspace), hdiag_out [k] or
  * NULL.  Asynchronous; k <= 1048576, m_cal >= 1, 0 <= k_out <= k. */
 sqf_status sqf_select_channels(const float* x_cal, int64_t m_cal, int64_t k, const float* w,
                                int64_t n, int64_t k_out, int32_t* idx_out, int32_t* map_out,
