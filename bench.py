@@ -91,6 +91,7 @@ class LayerRun:
             self.x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
             self.acts = sqf.alloc_acts(lay.m, lay.k - k_out, k_out)
             self.y = torch.empty((lay.m, lay.n), dtype=torch.float32, device="cuda")
+            self.yb = None  # bf16 Y buffer when the step writes bf16
             del w, x_cal
         stream.synchronize()
         self.sqf = sqf
@@ -101,7 +102,10 @@ class LayerRun:
         self.sqf.sqf_quantize_split_act(self.x, self.map, self.acts, stream=stream)
         if ev is not None:
             ev[1].record(stream)
-        self.sqf.sqf_dual_gemm(self.acts, self.w, y=self.y, stream=stream)
+        if self.yb is None:
+            self.sqf.sqf_dual_gemm(self.acts, self.w, y=self.y, stream=stream)
+        else:
+            self.sqf.sqf_dual_gemm(self.acts, self.w, y=self.yb, stream=stream, y_dtype="bf16")
         if ev is not None:
             ev[2].record(stream)
 
@@ -243,7 +247,14 @@ def rows_section(sqf, torch, stream):
                             gemm_tops=round(2.0 * rows * n * k / (tg * 1e-3) / 1e12, 1),
                             gemm_gbs=round(gemm_b / (tg * 1e-3) / 1e9, 1),
                             gemm_frac_hbm=round(gemm_b / (tg * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)))
-            del wt, xt, a, y, maps
+            # the same GEMM writing bf16 Y (half the output bytes)
+            yb = torch.empty((rows, n), dtype=torch.bfloat16, device="cuda")
+            tb = time_call(torch, stream, lambda: sqf.sqf_dual_gemm_grouped(a, wt, ro, y=yb, stream=stream,
+                                                                           y_dtype="bf16"))
+            gemm_bb = gemm_b - rows * n * 2
+            out[-1].update(gemm_bf16y_us=round(tb * 1e3, 1),
+                           gemm_bf16y_frac_hbm=round(gemm_bb / (tb * 1e-3) / 1e9 / PEAK_HBM_GBS, 3))
+            del wt, xt, a, y, yb, maps
             torch.cuda.empty_cache()
         del moe
 
@@ -315,6 +326,19 @@ def main():
                            pct_int8_peak=round(100 * tops / PEAK_INT8_TOPS, 2),
                            pct_dual_bound=round(100 * tops / (PEAK_INT8_TOPS * dual_bound_frac(
                                r.k - r.k_out, r.k_out)), 2)))
+    # the same step with bf16 Y (an output-type option, not the measured
+    # configuration; with the rows section): its GEMM times per layer
+    bf16_y = None
+    if not args.no_rows:
+        for r in runs:
+            r.yb = torch.empty((r.m, r.n), dtype=torch.bfloat16, device="cuda")
+        step_b, _, gemm_b = time_layers(torch, runs, stream, args.steps, args.warmup)
+        for r, d, g in zip(runs, detail, gemm_b):
+            d["gemm_bf16y_us"] = round(float(g) * 1e3, 2)
+            r.yb = None
+        torch.cuda.empty_cache()
+        bf16_y = {"ms_per_step": round(step_b, 4), "tops": round(total_ops / (step_b * 1e-3) / 1e12, 2),
+                  "gemm_top_s": round(gemm_ops / (gemm_b.sum() * 1e-3) / 1e12, 1)}
     traffic = read_traffic()
     out = {
         "metric": METRIC,
@@ -341,6 +365,7 @@ def main():
                      "avg_launch_us": round(float(gemm_ms.mean()) * 1e3, 2),
                      "ops_per_launch": gemm_ops / 3},
         "detail": detail,
+        "bf16_y_step": bf16_y,
         "setup_s": round(setup_s, 1),
     }
     if args.sweep:

@@ -195,6 +195,19 @@ sqf_status sqf_dual_gemm_grouped(const sqf_acts* a, const sqf_weights* w, int64_
                                  const int64_t* row_off, float* y, int64_t ldy,
                                  int32_t* acc_low_dbg, void* stream);
 
+/* The same fused epilogue ([OSC] result fusion) with a choice of output
+ * type: y_dtype SQF_F32 (y is float*, as above) or SQF_BF16 (y holds bf16
+ * bit patterns, each the round-to-nearest-even of the fp32 value the fp32
+ * call writes: half the output bytes, for a consumer that reads bf16).
+ * ldy counts elements of y's type.  No debug outputs.  Channel-split format
+ * only for SQF_BF16 (the weight-side format returns SQF_ERR_UNSUPPORTED);
+ * any other y_dtype returns SQF_ERR_INVALID_ARG. */
+sqf_status sqf_dual_gemm_y(const sqf_acts* a, const sqf_weights* w, void* y, int32_t y_dtype,
+                           int64_t ldy, void* stream);
+sqf_status sqf_dual_gemm_grouped_y(const sqf_acts* a, const sqf_weights* w, int64_t groups,
+                                   const int64_t* row_off, void* y, int32_t y_dtype, int64_t ldy,
+                                   void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -76,7 +76,9 @@ struct DmaLoader {
 };
 // OCC: blocks meant to share a CU (sets the register budget so that
 // OCC * WGM * WGN waves fit: 2 waves per SIMD either way).
-template <int BM, int BN, int WGM, int WGN, int OCC, int BR, bool GROUPED, bool DEBUG, int GROUP_M>
+// YB: Y is written as bf16 (round to nearest even of the fused fp32 value).
+template <int BM, int BN, int WGM, int WGN, int OCC, int BR, bool GROUPED, bool DEBUG, int GROUP_M,
+          bool YB>
 __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_dual_gemm(GemmArgs p) {
   constexpr int NW = WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;
@@ -85,6 +87,7 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_du
   constexpr int PW = DmaLoader<BM, BN, NW>::PW;
   static_assert(TM >= 1 && TN >= 1, "wave tile too small");
   static_assert(2 * PAIR * OCC <= 160 * 1024, "LDS budget");
+  static_assert(!(DEBUG && YB), "the accumulator dump comes with fp32 Y");
   __shared__ __attribute__((aligned(2048))) uint8_t smem[2 * PAIR];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -454,6 +457,7 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_du
 
   // ---------------- epilogue part 2: fuse and store ----------------
   float* y = p.y + m_begin * p.ldy;
+  uint16_t* yb = (uint16_t*)p.y + m_begin * p.ldy;  // (bf16 Y)
   auto fused = [&](int i, int j, int r, int row, int col) {
     float v = c[i][j][r];
     // rows past the end (staged path) read the last row's scale, unused
@@ -465,7 +469,7 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_du
   // (grouped: also a tile that ends inside the wave's rows, skipping the
   // rows past the end per 16-row fragment and per row)
   const bool whole = (GROUPED || wrow0 + WM <= mrows) && wcol0 + WN <= ncols &&
-                     (p.ldy & 3) == 0 && (((uintptr_t)p.y) & 15) == 0;
+                     (p.ldy & 3) == 0 && (((uintptr_t)p.y) & (YB ? 7 : 15)) == 0;
   if (whole) {
     // Y is written once and not read here: non-temporal stores keep it from
     // evicting the operand panels other tiles still stream from L2.
@@ -490,8 +494,17 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_du
       for (int k = 0; k < WN / 16; ++k) {
         const int idx = k * 64 + lane, rr = idx / (WN / 4), c4 = idx % (WN / 4);
         const v4f v = *(const v4f*)(stg + rr * LDW + 4 * c4);
-        if (!GROUPED || wrow0 + i * 16 + rr < mrows)
-          __builtin_nontemporal_store(v, (v4f*)(y + (int64_t)(wrow0 + i * 16 + rr) * p.ldy + wcol0 + 4 * c4));
+        if (!GROUPED || wrow0 + i * 16 + rr < mrows) {
+          const int64_t o = (int64_t)(wrow0 + i * 16 + rr) * p.ldy + wcol0 + 4 * c4;
+          if constexpr (YB) {
+            // v_cvt_pk_bf16_f32: two values per instruction, nearest even
+            const v2u h = v2u{__builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{v.x, v.y}, v2bf)),
+                              __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{v.z, v.w}, v2bf))};
+            __builtin_nontemporal_store(h, (v2u*)(yb + o));
+          } else {
+            __builtin_nontemporal_store(v, (v4f*)(y + o));
+          }
+        }
       }
     }
   } else {
@@ -505,7 +518,11 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_du
         for (int j = 0; j < TN; ++j) {
           const int col = col0 + j * 16;
           if (col >= ncols) continue;
-          __builtin_nontemporal_store(fused(i, j, r, row, col), y + (int64_t)row * p.ldy + col);
+          const float v = fused(i, j, r, row, col);
+          if constexpr (YB)
+            __builtin_nontemporal_store(__builtin_bit_cast(uint16_t, (__bf16)v), yb + (int64_t)row * p.ldy + col);
+          else
+            __builtin_nontemporal_store(v, y + (int64_t)row * p.ldy + col);
         }
       }
     }
@@ -513,7 +530,7 @@ __global__ __launch_bounds__(WGM* WGN * 64, (WGM * WGN * OCC + 3) / 4) void k_du
 }
 
 // ------------------------------------------------------------------ launch
-template <int BM, int BN, int WGM, int WGN, int OCC, int BR, bool GROUPED, bool DEBUG>
+template <int BM, int BN, int WGM, int WGN, int OCC, int BR, bool GROUPED, bool DEBUG, bool YB>
 static hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   int64_t tiles_n = (a.n + BN - 1) / BN;
   int64_t blocks;
@@ -522,44 +539,52 @@ static hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   else
     blocks = ((a.m + BM - 1) / BM) * tiles_n;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((k_dual_gemm<BM, BN, WGM, WGN, OCC, BR, GROUPED, DEBUG, 8>),
+  hipLaunchKernelGGL((k_dual_gemm<BM, BN, WGM, WGN, OCC, BR, GROUPED, DEBUG, 8, YB>),
                      dim3((unsigned)blocks), dim3(WGM * WGN * 64), 0, s, a);
   return hipGetLastError();
 }
 
-template <int BR, bool GROUPED, bool DEBUG>
+template <int BR, bool GROUPED, bool DEBUG, bool YB>
 static hipError_t launch_br(const GemmArgs& a, int cfg, hipStream_t s) {
   if constexpr (GROUPED) {
     // expert groups hold a few hundred rows each: 256x256 or 128x128 tiles
     if (BR != kFP8 && cfg == 0) {
-      if constexpr (BR != kFP8) return launch_cfg<256, 256, 2, 4, 1, BR, GROUPED, DEBUG>(a, s);
+      if constexpr (BR != kFP8) return launch_cfg<256, 256, 2, 4, 1, BR, GROUPED, DEBUG, YB>(a, s);
     }
-    return launch_cfg<128, 128, 2, 2, 2, BR, GROUPED, DEBUG>(a, s);
+    return launch_cfg<128, 128, 2, 2, 2, BR, GROUPED, DEBUG, YB>(a, s);
   } else {
     // an E4M3 branch keeps a second accumulator set: no 256x256 tile for it
     if (BR == kFP8 && cfg == 0) cfg = 1;
     switch (cfg) {
       case 0:
-        if constexpr (BR != kFP8) return launch_cfg<256, 256, 2, 4, 1, BR, GROUPED, DEBUG>(a, s);
+        if constexpr (BR != kFP8) return launch_cfg<256, 256, 2, 4, 1, BR, GROUPED, DEBUG, YB>(a, s);
         [[fallthrough]];
       case 1:
-        return launch_cfg<128, 128, 2, 2, 2, BR, GROUPED, DEBUG>(a, s);
+        return launch_cfg<128, 128, 2, 2, 2, BR, GROUPED, DEBUG, YB>(a, s);
       default:
-        return launch_cfg<64, 64, 2, 2, 2, BR, GROUPED, DEBUG>(a, s);
+        return launch_cfg<64, 64, 2, 2, 2, BR, GROUPED, DEBUG, YB>(a, s);
     }
   }
 }
 
 // cfg: 0 = 256x256 (8 waves), 1 = 128x128 (4 waves, two blocks per CU),
-// 2 = 64x64 (4 waves, two blocks per CU).
+// 2 = 64x64 (4 waves, two blocks per CU).  ybf16: bf16 Y (not with debug).
+template <int BR, bool GROUPED>
+static hipError_t launch_mode(const GemmArgs& a, bool debug, bool ybf16, int cfg, hipStream_t s) {
+  if (debug) return launch_br<BR, GROUPED, true, false>(a, cfg, s);
+  if (ybf16) return launch_br<BR, GROUPED, false, true>(a, cfg, s);
+  return launch_br<BR, GROUPED, false, false>(a, cfg, s);
+}
+
 hipError_t launch_dual_gemm(const GemmArgs& a, int branch, bool grouped, bool debug, int cfg,
-                            hipStream_t s) {
+                            hipStream_t s, bool ybf16) {
+  if (debug && ybf16) return hipErrorInvalidValue;
   if (branch == kFP8) {
-    if (grouped) return debug ? launch_br<kFP8, true, true>(a, cfg, s) : launch_br<kFP8, true, false>(a, cfg, s);
-    return debug ? launch_br<kFP8, false, true>(a, cfg, s) : launch_br<kFP8, false, false>(a, cfg, s);
+    if (grouped) return launch_mode<kFP8, true>(a, debug, ybf16, cfg, s);
+    return launch_mode<kFP8, false>(a, debug, ybf16, cfg, s);
   }
-  if (grouped) return debug ? launch_br<kBF16, true, true>(a, cfg, s) : launch_br<kBF16, true, false>(a, cfg, s);
-  return debug ? launch_br<kBF16, false, true>(a, cfg, s) : launch_br<kBF16, false, false>(a, cfg, s);
+  if (grouped) return launch_mode<kBF16, true>(a, debug, ybf16, cfg, s);
+  return launch_mode<kBF16, false>(a, debug, ybf16, cfg, s);
 }
 
 }  // namespace sqf

@@ -182,7 +182,7 @@ sqf_status quantize_common(const void* x, int32_t x_dtype, int64_t ldx, int64_t 
       sqf::launch_act_split(args, x_dtype, a->low, a->branch, grouped, (hipStream_t)stream), who);
 }
 
-sqf_status check_pair(const sqf_acts* a, const sqf_weights* w, float* y, int64_t ldy,
+sqf_status check_pair(const sqf_acts* a, const sqf_weights* w, const void* y, int64_t ldy,
                       const char* who) {
   sqf_status st = check_acts(a, who);
   if (st != SQF_OK) return st;
@@ -198,6 +198,66 @@ sqf_status check_pair(const sqf_acts* a, const sqf_weights* w, float* y, int64_t
   if (ldy < w->n) return fail(SQF_ERR_SHAPE, "%s: ldy=%lld < n=%lld", who, (long long)ldy,
                               (long long)w->n);
   return SQF_OK;
+}
+
+// Y is fp32 (float*) or, with ybf16, bf16 (uint16_t* bit patterns); ldy in
+// elements of Y's type.
+sqf_status dual_gemm_impl(const sqf_acts* a, const sqf_weights* w, void* y, bool ybf16,
+                          int64_t ldy, int32_t* acc_low_dbg, int32_t* acc_sp_dbg,
+                          int32_t* acc_out_dbg, void* stream, const char* who) {
+  sqf_status st = check_pair(a, w, y, ldy, who);
+  if (st != SQF_OK) return st;
+  if (w->groups != 1) return fail(SQF_ERR_INVALID_ARG, "%s: use sqf_dual_gemm_grouped", who);
+  if (a->m == 0) return SQF_OK;
+  const bool debug = acc_low_dbg || acc_sp_dbg || acc_out_dbg;
+  if (w->sq_nnz > 0) {
+    if (ybf16) return fail(SQF_ERR_UNSUPPORTED, "%s: the weight-side format writes fp32 Y", who);
+    // int8 activations x (16 x int4 weights) in an int32 accumulator
+    if (w->k_low > kMaxKLowSq)
+      return fail(SQF_ERR_UNSUPPORTED, "%s: k_low=%lld exceeds %lld for the weight-side format", who,
+                  (long long)w->k_low, (long long)kMaxKLowSq);
+    if (debug && !(acc_low_dbg && acc_sp_dbg && acc_out_dbg))
+      return fail(SQF_ERR_INVALID_ARG, "%s: the weight-side debug path writes all three accumulators", who);
+    sqf::SqArgs sa{a->x_low, a->s_x, (const uint8_t*)a->x_out, a->s_xo, w->w_low, w->s_w,
+                   w->sq_val, w->s_w8, w->sq_tile_off, (const uint8_t*)w->w_out, w->s_wo, (float*)y,
+                   acc_low_dbg, acc_sp_dbg, acc_out_dbg, a->m, w->n, a->ldk, w->ldk, w->ldo, ldy,
+                   w->sq_nnz, (int32_t)(w->ldk / 128), (int32_t)(w->ldo / 128)};
+    return hip_status(sqf::launch_sq_gemm(sa, debug, (hipStream_t)stream), who);
+  }
+  if (acc_sp_dbg || acc_out_dbg)
+    return fail(SQF_ERR_INVALID_ARG, "%s: acc_sp/acc_out debug outputs need the weight-side format", who);
+  const int64_t ldo_b = w->ldo * branch_esz(w->branch);
+  sqf::GemmArgs ga{a->x_low, a->s_x, (const uint8_t*)a->x_out, a->s_xo, w->w_low, w->s_w,
+                   (const uint8_t*)w->w_out, w->s_wo, (float*)y, acc_low_dbg, nullptr, a->m, w->n, w->ldk,
+                   ldo_b, ldy, 0, 0, 0, (int32_t)(w->ldk / 64), (int32_t)(ldo_b / 64), 1};
+  return hip_status(sqf::launch_dual_gemm(ga, w->branch, false, debug,
+                                          pick_cfg(a->m, w->n, w->branch), (hipStream_t)stream, ybf16),
+                    who);
+}
+
+sqf_status grouped_impl(const sqf_acts* a, const sqf_weights* w, int64_t groups,
+                        const int64_t* row_off, void* y, bool ybf16, int64_t ldy,
+                        int32_t* acc_low_dbg, void* stream, const char* who) {
+  sqf_status st = check_pair(a, w, y, ldy, who);
+  if (st != SQF_OK) return st;
+  if (groups < 1 || w->groups != groups || !row_off)
+    return fail(SQF_ERR_INVALID_ARG, "%s: need groups >= 1 == w->groups and row_off", who);
+  if (w->sq_nnz > 0) return fail(SQF_ERR_UNSUPPORTED, "%s: channel-split format only", who);
+  if (a->m == 0) return SQF_OK;
+  const int64_t ldo_b = w->ldo * branch_esz(w->branch);
+  // 256x256 tiles when the groups average 384 rows or more (bf16 branch),
+  // else 128x128; SQF_GEMM_TILE=0/1 forces one
+  sqf::GemmArgs ga{a->x_low, a->s_x, (const uint8_t*)a->x_out, a->s_xo, w->w_low, w->s_w,
+                   (const uint8_t*)w->w_out, w->s_wo, (float*)y, acc_low_dbg, row_off, a->m, w->n,
+                   w->ldk, ldo_b, ldy, w->n * w->ldk, w->n * ldo_b, w->n,
+                   (int32_t)(w->ldk / 64), (int32_t)(ldo_b / 64), (int32_t)groups};
+  const char* env = getenv("SQF_GEMM_TILE");
+  int cfg = (a->m / groups >= 384) ? 0 : 1;
+  if (env && (atoi(env) == 0 || atoi(env) == 1)) cfg = atoi(env);
+  if (w->branch == SQF_FP8_E4M3) cfg = 1;
+  return hip_status(sqf::launch_dual_gemm(ga, w->branch, true, acc_low_dbg != nullptr, cfg,
+                                          (hipStream_t)stream, ybf16),
+                    who);
 }
 
 }  // namespace
@@ -274,61 +334,35 @@ sqf_status sqf_dual_gemm(const sqf_acts* a, const sqf_weights* w, float* y, int6
                          int32_t* acc_low_dbg, int32_t* acc_sp_dbg, int32_t* acc_out_dbg,
                          void* stream) {
   g_err.clear();
-  const char* who = "sqf_dual_gemm";
-  sqf_status st = check_pair(a, w, y, ldy, who);
-  if (st != SQF_OK) return st;
-  if (w->groups != 1) return fail(SQF_ERR_INVALID_ARG, "%s: use sqf_dual_gemm_grouped", who);
-  if (a->m == 0) return SQF_OK;
-  const bool debug = acc_low_dbg || acc_sp_dbg || acc_out_dbg;
-  if (w->sq_nnz > 0) {
-    // int8 activations x (16 x int4 weights) in an int32 accumulator
-    if (w->k_low > kMaxKLowSq)
-      return fail(SQF_ERR_UNSUPPORTED, "%s: k_low=%lld exceeds %lld for the weight-side format", who,
-                  (long long)w->k_low, (long long)kMaxKLowSq);
-    if (debug && !(acc_low_dbg && acc_sp_dbg && acc_out_dbg))
-      return fail(SQF_ERR_INVALID_ARG, "%s: the weight-side debug path writes all three accumulators", who);
-    sqf::SqArgs sa{a->x_low, a->s_x, (const uint8_t*)a->x_out, a->s_xo, w->w_low, w->s_w,
-                   w->sq_val, w->s_w8, w->sq_tile_off, (const uint8_t*)w->w_out, w->s_wo, y,
-                   acc_low_dbg, acc_sp_dbg, acc_out_dbg, a->m, w->n, a->ldk, w->ldk, w->ldo, ldy,
-                   w->sq_nnz, (int32_t)(w->ldk / 128), (int32_t)(w->ldo / 128)};
-    return hip_status(sqf::launch_sq_gemm(sa, debug, (hipStream_t)stream), who);
-  }
-  if (acc_sp_dbg || acc_out_dbg)
-    return fail(SQF_ERR_INVALID_ARG, "%s: acc_sp/acc_out debug outputs need the weight-side format", who);
-  const int64_t ldo_b = w->ldo * branch_esz(w->branch);
-  sqf::GemmArgs ga{a->x_low, a->s_x, (const uint8_t*)a->x_out, a->s_xo, w->w_low, w->s_w,
-                   (const uint8_t*)w->w_out, w->s_wo, y, acc_low_dbg, nullptr, a->m, w->n, w->ldk,
-                   ldo_b, ldy, 0, 0, 0, (int32_t)(w->ldk / 64), (int32_t)(ldo_b / 64), 1};
-  return hip_status(sqf::launch_dual_gemm(ga, w->branch, false, debug,
-                                          pick_cfg(a->m, w->n, w->branch), (hipStream_t)stream),
-                    who);
+  return dual_gemm_impl(a, w, y, false, ldy, acc_low_dbg, acc_sp_dbg, acc_out_dbg, stream,
+                        "sqf_dual_gemm");
+}
+
+sqf_status sqf_dual_gemm_y(const sqf_acts* a, const sqf_weights* w, void* y, int32_t y_dtype,
+                           int64_t ldy, void* stream) {
+  g_err.clear();
+  const char* who = "sqf_dual_gemm_y";
+  if (y_dtype != SQF_F32 && y_dtype != SQF_BF16)
+    return fail(SQF_ERR_INVALID_ARG, "%s: y_dtype %d is neither SQF_F32 nor SQF_BF16", who, y_dtype);
+  return dual_gemm_impl(a, w, y, y_dtype == SQF_BF16, ldy, nullptr, nullptr, nullptr, stream, who);
 }
 
 sqf_status sqf_dual_gemm_grouped(const sqf_acts* a, const sqf_weights* w, int64_t groups,
                                  const int64_t* row_off, float* y, int64_t ldy,
                                  int32_t* acc_low_dbg, void* stream) {
   g_err.clear();
-  const char* who = "sqf_dual_gemm_grouped";
-  sqf_status st = check_pair(a, w, y, ldy, who);
-  if (st != SQF_OK) return st;
-  if (groups < 1 || w->groups != groups || !row_off)
-    return fail(SQF_ERR_INVALID_ARG, "%s: need groups >= 1 == w->groups and row_off", who);
-  if (w->sq_nnz > 0) return fail(SQF_ERR_UNSUPPORTED, "%s: channel-split format only", who);
-  if (a->m == 0) return SQF_OK;
-  const int64_t ldo_b = w->ldo * branch_esz(w->branch);
-  // 256x256 tiles when the groups average 384 rows or more (bf16 branch),
-  // else 128x128; SQF_GEMM_TILE=0/1 forces one
-  sqf::GemmArgs ga{a->x_low, a->s_x, (const uint8_t*)a->x_out, a->s_xo, w->w_low, w->s_w,
-                   (const uint8_t*)w->w_out, w->s_wo, y, acc_low_dbg, row_off, a->m, w->n,
-                   w->ldk, ldo_b, ldy, w->n * w->ldk, w->n * ldo_b, w->n,
-                   (int32_t)(w->ldk / 64), (int32_t)(ldo_b / 64), (int32_t)groups};
-  const char* env = getenv("SQF_GEMM_TILE");
-  int cfg = (a->m / groups >= 384) ? 0 : 1;
-  if (env && (atoi(env) == 0 || atoi(env) == 1)) cfg = atoi(env);
-  if (w->branch == SQF_FP8_E4M3) cfg = 1;
-  return hip_status(sqf::launch_dual_gemm(ga, w->branch, true, acc_low_dbg != nullptr, cfg,
-                                          (hipStream_t)stream),
-                    who);
+  return grouped_impl(a, w, groups, row_off, y, false, ldy, acc_low_dbg, stream,
+                      "sqf_dual_gemm_grouped");
+}
+
+sqf_status sqf_dual_gemm_grouped_y(const sqf_acts* a, const sqf_weights* w, int64_t groups,
+                                   const int64_t* row_off, void* y, int32_t y_dtype, int64_t ldy,
+                                   void* stream) {
+  g_err.clear();
+  const char* who = "sqf_dual_gemm_grouped_y";
+  if (y_dtype != SQF_F32 && y_dtype != SQF_BF16)
+    return fail(SQF_ERR_INVALID_ARG, "%s: y_dtype %d is neither SQF_F32 nor SQF_BF16", who, y_dtype);
+  return grouped_impl(a, w, groups, row_off, y, y_dtype == SQF_BF16, ldy, nullptr, stream, who);
 }
 
 }  // extern "C"

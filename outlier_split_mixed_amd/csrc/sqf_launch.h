@@ -79,8 +79,9 @@ hipError_t launch_act_split(const ActArgs& a, int x_dtype, int low, int branch, 
 // dynamic LDS bytes the activation kernel needs for one block
 size_t act_split_lds_bytes(int64_t ldk, int64_t k_out);
 // cfg: 0 = 256x256 tiles (8 waves), 1 = 128x128 (4 waves), 2 = 64x64 (4 waves)
+// ybf16: Y written as bf16 (not together with debug)
 hipError_t launch_dual_gemm(const GemmArgs& a, int branch, bool grouped, bool debug, int cfg,
-                            hipStream_t s);
+                            hipStream_t s, bool ybf16);
 hipError_t launch_sq_gemm(const SqArgs& a, bool debug, hipStream_t s);
 
 }  // namespace sqf

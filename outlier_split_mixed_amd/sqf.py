@@ -66,6 +66,9 @@ _decl("sqf_quantize_split_act_grouped", [P, I32, I64, I64, P, P, ctypes.POINTER(
 _decl("sqf_dual_gemm", [ctypes.POINTER(sqf_acts), ctypes.POINTER(sqf_weights), P, I64, P, P, P, P])
 _decl("sqf_dual_gemm_grouped", [ctypes.POINTER(sqf_acts), ctypes.POINTER(sqf_weights), I64, P, P,
                                 I64, P, P])
+_decl("sqf_dual_gemm_y", [ctypes.POINTER(sqf_acts), ctypes.POINTER(sqf_weights), P, I32, I64, P])
+_decl("sqf_dual_gemm_grouped_y", [ctypes.POINTER(sqf_acts), ctypes.POINTER(sqf_weights), I64, P, P,
+                                  I32, I64, P])
 
 if _lib.sqf_abi_version() != ABI_VERSION:
     raise ImportError(f"libsqf ABI {_lib.sqf_abi_version()} != binding ABI {ABI_VERSION}")
@@ -242,12 +245,28 @@ def sqf_quantize_split_act_grouped(x: torch.Tensor, row_off: torch.Tensor, maps:
     return out
 
 
-def sqf_dual_gemm(a: Acts, w: Weights, y: torch.Tensor | None = None, debug: bool = False,
-                  stream=None):
-    """a3-a5: returns y [m][n] fp32 (and int32 accumulators with ``debug``)."""
-    dev = a.t["s_x"].device
+def _y_out(a, w, y, y_dtype):
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16}[y_dtype]
     if y is None:
-        y = torch.empty((a.m, w.n), dtype=torch.float32, device=dev)
+        y = torch.empty((a.m, w.n), dtype=dt, device=a.t["s_x"].device)
+    if y.dtype != dt:
+        raise ValueError(f"y is {y.dtype}, y_dtype {y_dtype}")
+    return y
+
+
+def sqf_dual_gemm(a: Acts, w: Weights, y: torch.Tensor | None = None, debug: bool = False,
+                  stream=None, y_dtype: str = "f32"):
+    """a3-a5: returns y [m][n] (fp32, or bf16 with ``y_dtype="bf16"``), and the
+    int32 accumulators with ``debug`` (fp32 y only)."""
+    dev = a.t["s_x"].device
+    y = _y_out(a, w, y, y_dtype)
+    if y_dtype != "f32":
+        if debug:
+            raise ValueError("the accumulator dump comes with fp32 y")
+        da, dw = a.desc(), w.desc()
+        _check(_lib.sqf_dual_gemm_y(ctypes.byref(da), ctypes.byref(dw), _ptr(y), DTYPES[y_dtype],
+                                    y.stride(0), _stream(stream)))
+        return y
     dbg = [None, None, None]
     if debug:
         dbg[0] = torch.empty((a.m, w.n), dtype=torch.int32, device=dev)
@@ -261,10 +280,17 @@ def sqf_dual_gemm(a: Acts, w: Weights, y: torch.Tensor | None = None, debug: boo
 
 
 def sqf_dual_gemm_grouped(a: Acts, w: Weights, row_off: torch.Tensor, y=None, debug=False,
-                          stream=None):
+                          stream=None, y_dtype: str = "f32"):
     dev = a.t["s_x"].device
-    if y is None:
-        y = torch.empty((a.m, w.n), dtype=torch.float32, device=dev)
+    y = _y_out(a, w, y, y_dtype)
+    if y_dtype != "f32":
+        if debug:
+            raise ValueError("the accumulator dump comes with fp32 y")
+        da, dw = a.desc(), w.desc()
+        _check(_lib.sqf_dual_gemm_grouped_y(ctypes.byref(da), ctypes.byref(dw), row_off.numel() - 1,
+                                            _ptr(row_off), _ptr(y), DTYPES[y_dtype], y.stride(0),
+                                            _stream(stream)))
+        return y
     dbg = torch.empty((a.m, w.n), dtype=torch.int32, device=dev) if debug else None
     da, dw = a.desc(), w.desc()
     _check(_lib.sqf_dual_gemm_grouped(ctypes.byref(da), ctypes.byref(dw), row_off.numel() - 1,

@@ -26,7 +26,7 @@ def _declared_functions():
 
 def test_every_declared_symbol_is_exported(sqf):
     names = _declared_functions()
-    assert len(names) == 10
+    assert len(names) == 12
     for name in names:
         assert hasattr(sqf._lib, name), name
 
@@ -182,3 +182,25 @@ def test_grouped_argument_errors(sqf):
     w.groups = 1
     assert sqf._lib.sqf_dual_gemm(ctypes.byref(a), ctypes.byref(_weights(sqf, mem, **{})), None,
                                   256, None, None, None, None) == 1
+
+
+def test_output_type_argument_errors(sqf):
+    """The bf16-output entry points: an unknown output type, the weight-side
+    format (fp32 output only) and the shared checks fail before any launch."""
+    mem = FakeMem()
+    a = _acts(sqf, mem)
+    w = _weights(sqf, mem)
+    f = sqf._lib.sqf_dual_gemm_y
+    assert f(ctypes.byref(a), ctypes.byref(w), mem(), sqf.SQF_FP8_E4M3, 256, None) == 1
+    assert f(ctypes.byref(a), ctypes.byref(w), mem(), sqf.SQF_BF16, 10, None) == 2  # ldy < n
+    assert f(ctypes.byref(a), ctypes.byref(w), None, sqf.SQF_BF16, 256, None) == 1
+    assert sqf.sqf_last_error() != ""
+    a8 = _acts(sqf, mem, low="i8", branch="i8")
+    w8 = _weights(sqf, mem)
+    w8.branch, w8.ldo, w8.s_wo = sqf.SQF_I8, 128, mem()
+    w8.sq_nnz, w8.sq_val, w8.s_w8, w8.sq_tile_off = 60, mem(), mem(), mem()
+    assert f(ctypes.byref(a8), ctypes.byref(w8), mem(), sqf.SQF_BF16, 256, None) == 3
+    g = sqf._lib.sqf_dual_gemm_grouped_y
+    w.groups = 4
+    assert g(ctypes.byref(a), ctypes.byref(w), 4, mem(), mem(), 7, 256, None) == 1
+    assert g(ctypes.byref(a), ctypes.byref(w), 3, mem(), mem(), sqf.SQF_BF16, 256, None) == 1

@@ -152,6 +152,42 @@ def test_selection_ties_and_ragged_rows(sqf, k, n):
     _print("ties", k, n, "boundary score", o_sc[src_a])
 
 
+@pytest.mark.parametrize("tile,branch", [("0", "bf16"), ("1", "bf16"), ("2", "bf16"), ("1", "fp8")])
+def test_bf16_output(sqf, tile, branch):
+    """bf16 Y: each element is the round-to-nearest-even of the fp32 Y the
+    fp32 launch writes (same accumulators, same epilogue arithmetic), within
+    the fp32 tolerance plus one bf16 step of the oracle; both the 16-byte
+    store path and, with an odd row stride, the element-wise one (the
+    columns past n stay untouched)."""
+    lay = _ragged(m=300, k=1000, n=520, n_scaled=37, seed=95)
+    x_cal = torch.from_numpy(lay.x_cal).cuda()
+    w = torch.from_numpy(lay.w).cuda()
+    _, mp, _, _ = sqf.sqf_select_channels(x_cal, w, lay.k_out)
+    wts = sqf.sqf_pack_weights(w, mp, branch=branch)
+    ox, ofmt, xt = x_inputs(lay, "bf16")
+    acts = sqf.alloc_acts(lay.m, lay.k - lay.k_out, lay.k_out, branch=branch)
+    sqf.sqf_quantize_split_act(xt, mp, acts)
+    os.environ["SQF_GEMM_TILE"] = tile
+    try:
+        y32 = sqf.sqf_dual_gemm(acts, wts)
+        yb = sqf.sqf_dual_gemm(acts, wts, y_dtype="bf16")
+        big = torch.full((lay.m, lay.n + 3), float("nan"), dtype=torch.bfloat16, device="cuda")
+        sqf.sqf_dual_gemm(acts, wts, y=big[:, :lay.n], y_dtype="bf16")
+    finally:
+        del os.environ["SQF_GEMM_TILE"]
+    torch.cuda.synchronize()
+    want = _bf16_bits(y32.to(torch.bfloat16))
+    assert np.array_equal(_bf16_bits(yb), want)
+    assert np.array_equal(_bf16_bits(big[:, :lay.n]), want)
+    assert torch.isnan(big[:, lay.n:]).all()
+    o_mp = oracle.select_channels(lay.x_cal, lay.w, lay.k_out)[1]
+    o_a = oracle.quantize_split_act(ox, o_mp, branch=branch, x_fmt=ofmt)
+    o_w = oracle.pack_weights(lay.w, o_mp, branch=branch)
+    o_y = oracle.dual_gemm(o_a, o_w)
+    _assert_bf16_close(yb.float().cpu().numpy(), o_y, f"bf16 Y tile {tile} {branch}")
+    _print("bf16 Y", tile, branch)
+
+
 def test_m_zero_is_a_no_op(sqf):
     acts = sqf.alloc_acts(0, 480, 32)
     w = sqf.alloc_weights(512, 64, 32)
@@ -287,7 +323,7 @@ def test_grouped_small_with_empty_group(sqf, branch, tile):
                           scaled=lays[2].scaled)
     os.environ["SQF_GEMM_TILE"] = tile
     try:
-        _grouped_check(sqf, lays, branch)
+        _grouped_check(sqf, lays, branch, y_bf16=True)
     finally:
         del os.environ["SQF_GEMM_TILE"]
 
@@ -306,7 +342,21 @@ def test_grouped_many_groups(sqf, tile):
         del os.environ["SQF_GEMM_TILE"]
 
 
-def _grouped_check(sqf, lays, branch, rows_per_group=None):
+def _bf16_bits(t):
+    return t.contiguous().view(torch.int16).cpu().numpy()
+
+
+def _assert_bf16_close(yb, o_y, label):
+    """bf16 Y against the oracle's fp32 Y: the fp32 tolerance plus one bf16
+    step (2^-8 relative) for the final rounding."""
+    yb = np.asarray(yb, dtype=np.float64)
+    o_y = np.asarray(o_y, dtype=np.float64)
+    tol = 1e-3 * np.abs(o_y).max(axis=1, keepdims=True) + np.abs(o_y) * 2.0 ** -8
+    bad = np.abs(yb - o_y) > tol
+    assert not bad.any(), f"{label}: {int(bad.sum())} bf16 outputs beyond tolerance"
+
+
+def _grouped_check(sqf, lays, branch, rows_per_group=None, y_bf16=False):
     g = len(lays)
     k, n, k_out = lays[0].k, lays[0].n, lays[0].k_out
     counts = [l.m for l in lays]
@@ -328,7 +378,12 @@ def _grouped_check(sqf, lays, branch, rows_per_group=None):
     sqf.sqf_quantize_split_act_grouped(xt, row_off, maps_t, acts)
     y, acc = sqf.sqf_dual_gemm_grouped(acts, wts, row_off, debug=True)
     y_fast = sqf.sqf_dual_gemm_grouped(acts, wts, row_off)
+    yb = sqf.sqf_dual_gemm_grouped(acts, wts, row_off, y_dtype="bf16") if y_bf16 else None
     torch.cuda.synchronize()
+    if y_bf16:
+        # the bf16 launch rounds exactly the values the fp32 launch writes
+        assert np.array_equal(_bf16_bits(yb), _bf16_bits(y_fast.to(torch.bfloat16)))
+        ybf = yb.float().cpu().numpy()
     yg, ag = y.cpu().numpy(), acc.cpu().numpy().astype(np.int64)
     yf = y_fast.cpu().numpy()
     xl, xo = acts.t["x_low"].cpu().numpy(), acts.t["x_out"].cpu().numpy()
@@ -350,3 +405,5 @@ def _grouped_check(sqf, lays, branch, rows_per_group=None):
         assert np.array_equal(ag[r0:r1][sel], o_acc), f"expert {e} accumulators"
         assert_rows_close(yg[r0:r1][sel], o_y, f"expert {e}")
         assert_rows_close(yf[r0:r1][sel], o_y, f"expert {e} (no debug outputs)")
+        if y_bf16:
+            _assert_bf16_close(ybf[r0:r1][sel], o_y, f"expert {e} (bf16 Y)")
