@@ -5,6 +5,7 @@ Bit-exact: outlier set, channel map, fp64 scores, hdiag, packed int4 bytes,
 fp32 scale patterns, branch codes, int32 low-path accumulators.  Tolerance:
 per row, max |y_gpu - y_oracle| <= 1e-3 * max |y_oracle|.
 """
+import ctypes
 import os
 
 import numpy as np
@@ -171,11 +172,18 @@ def test_bf16_output(sqf, tile, branch):
     try:
         y32 = sqf.sqf_dual_gemm(acts, wts)
         yb = sqf.sqf_dual_gemm(acts, wts, y_dtype="bf16")
+        # the output-type entry point with SQF_F32 is the plain fp32 call
+        y32b = torch.empty_like(y32)
+        da, dw = acts.desc(), wts.desc()
+        assert sqf._lib.sqf_dual_gemm_y(ctypes.byref(da), ctypes.byref(dw), ctypes.c_void_p(y32b.data_ptr()),
+                                        sqf.SQF_F32, y32b.stride(0),
+                                        ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)) == 0
         big = torch.full((lay.m, lay.n + 3), float("nan"), dtype=torch.bfloat16, device="cuda")
         sqf.sqf_dual_gemm(acts, wts, y=big[:, :lay.n], y_dtype="bf16")
     finally:
         del os.environ["SQF_GEMM_TILE"]
     torch.cuda.synchronize()
+    assert torch.equal(y32b.view(torch.int32), y32.view(torch.int32))
     want = _bf16_bits(y32.to(torch.bfloat16))
     assert np.array_equal(_bf16_bits(yb), want)
     assert np.array_equal(_bf16_bits(big[:, :lay.n]), want)
