@@ -43,6 +43,15 @@ def test_tiny_fp32_input(sqf):
     _print("tiny", st)
 
 
+@pytest.mark.parametrize("k", [1000, 4096, 16384])
+def test_fp32_input_row_widths(sqf, k):
+    """fp32 activations (not only bf16) through the activation layouts for
+    narrow, medium and wide rows, ragged M and N."""
+    lay = synth.draw_layer("f32in", 1020 + k % 97, 0, 45, k, 136, 64, max(1, k // 16), x_dtype="f32")
+    st, _ = run_layer(sqf, lay, lay.k_out, x_dtype="f32")
+    _print("fp32 input", k, st)
+
+
 @pytest.mark.parametrize("k", [512, 40960])
 def test_row_width_extremes(sqf, k):
     """The narrowest and widest rows the activation kernel lays out differently
