@@ -43,6 +43,19 @@ def test_tiny_fp32_input(sqf):
     _print("tiny", st)
 
 
+@pytest.mark.parametrize("tile", ["0", "1", "2"])
+def test_tiny_m_and_n_every_tile(sqf, tile):
+    """7 tokens x 5 outputs: one partial tile on every configuration, almost
+    every row and column of it past the ends."""
+    lay = synth.draw_layer("tinymn", 1030, 0, 7, 512, 5, 32, 32)
+    os.environ["SQF_GEMM_TILE"] = tile
+    try:
+        st, _ = run_layer(sqf, lay, lay.k_out)
+    finally:
+        del os.environ["SQF_GEMM_TILE"]
+    _print("tiny m n", tile, st)
+
+
 @pytest.mark.parametrize("k", [1000, 4096, 16384])
 def test_fp32_input_row_widths(sqf, k):
     """fp32 activations (not only bf16) through the activation layouts for
