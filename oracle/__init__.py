@@ -249,6 +249,13 @@ def dual_gemm(a: dict, w: dict, rows=None, debug: bool = False):
     dbg = [np.zeros((nr, n), dtype=np.int64) for _ in range(3)] if debug else [None] * 3
     assert a["k_low"] == w["k_low"] and a["k_out"] == w["k_out"] and a["branch"] == w["branch"]
     sq = w.get("sq_nnz", 0)
+    # The integer sums are exact in int64 here; the GPU keeps them in int32.
+    # Their worst case |acc| is the code range product times the length.
+    qx = 7 if a["low"] == "i4" else 127
+    worst = max(qx * 7 * a["k_low"], qx * 127 * sq,
+                127 * 127 * a["k_out"] if a["branch"] == "i8" else 0)
+    if worst >= 2 ** 31:
+        raise ValueError(f"integer accumulators may exceed int32 (worst case {worst})")
     _load().orc_dual_gemm(
         n, a["k_low"], a["k_out"], _p(rows), nr,
         _p(a["x_low"]) if a["x_low"].size else None, a["ldk"], _FMT[a["low"]], _p(a["s_x"]),
@@ -258,5 +265,7 @@ def dual_gemm(a: dict, w: dict, rows=None, debug: bool = False):
         sq, _p(w["sq_val"]) if sq else None, _p(w["s_w8"]) if sq else None,
         _p(y), n, _p(dbg[0]), _p(dbg[1]), _p(dbg[2]))
     if debug:
+        for d in dbg:
+            assert np.abs(d).max(initial=0) < 2 ** 31
         return y, dbg[0], dbg[1], dbg[2]
     return y

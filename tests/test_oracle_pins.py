@@ -402,3 +402,121 @@ def test_sq_mask_is_top_key_per_row():
         key = lay.w[low, nn].astype(np.float64) ** 2 * hd[low].astype(np.float64)
         top = np.lexsort((np.arange(len(low)), -key))[:nnz]
         assert set(np.nonzero(nib[nn] == 8)[0].tolist()) == set(top.tolist())
+
+
+# ------------------------------------------------------------------ SQ-format whole op
+def test_hand_case_sq_with_int8_branch(golden):
+    """Hand-worked weight-side SQ-format case with a static int8 outlier branch
+    and a different scale on every term: s_x = 0.5, s_xo = 2, s_w4 = 1/16,
+    s_w8 = 1/32, s_wo = 1/64 (SQ-format article, sections 三 and 九; OSC
+    abstract).  Fixes y = s_x (s_w4 acc_low + s_w8 acc_sp) + s_xo s_wo acc_o
+    to the bit: dropping the branch, swapping any two of the scales or
+    mixing the two weight scales changes y."""
+    g = golden("sq_full_hand_case.txt")
+    mp = np.array([int(v) for v in g["map"][0]], np.int32)
+    hd = _floats(g["hdiag"])[0]
+    nnz = int(g["nnz"][0][0])
+    x = _floats(g["x"])
+    w = _floats(g["w"]).reshape(-1, 1)
+    a = oracle.quantize_split_act(x, mp, low="i8", branch="i8")
+    assert a["x_low"][0, :8].view(np.int8).tolist() == [int(v) for v in g["x_low_i8"][0]]
+    assert not a["x_low"][0, 8:].any()
+    assert a["s_x"][0] == np.float32(g["s_x"][0][0])
+    assert a["x_out"][0, :2].view(np.int8).tolist() == [int(v) for v in g["x_out_i8"][0]]
+    assert not a["x_out"][0, 2:].any()
+    assert a["s_xo"][0] == np.float32(g["s_xo"][0][0])
+    wp = oracle.pack_weights_sq(w, mp, hd, nnz)
+    assert wp["w_low"][0, :4].tolist() == _hexbytes(g["packed"])[0].tolist()
+    assert not wp["w_low"][0, 4:].any()
+    assert wp["sq_val"][0].tolist() == [int(v) for v in g["v8"][0]]
+    assert wp["s_w"][0] == np.float32(g["s_w4"][0][0])
+    assert wp["s_w8"][0] == np.float32(g["s_w8"][0][0])
+    assert wp["w_out"][0, :2].view(np.int8).tolist() == [int(v) for v in g["w_out_i8"][0]]
+    assert wp["s_wo"][0] == np.float32(g["s_wo"][0][0])
+    y, al, asp, ao = oracle.dual_gemm(a, wp, debug=True)
+    assert al[0, 0] == int(g["acc_low"][0][0])
+    assert asp[0, 0] == int(g["acc_sp"][0][0])
+    assert ao[0, 0] == int(g["acc_o"][0][0])
+    assert y[0, 0] == np.float32(g["y"][0][0])
+
+
+def test_sq_error_within_quantisation_bound():
+    """Weight-side SQ-format on the tiny layer: |Y - X.W| stays within the sum
+    of the per-element rounding errors (half a step of each int8 activation,
+    int4 weight, int8 marked value and int8 branch operand).  The outlier
+    channels and the marked weights carry most of |X.W|, so dropping the
+    branch, scaling it with the low activation scale, or scaling the marked
+    values with the int4 weight scale all break the bound."""
+    lay = synth.tiny()
+    idx, mp, _, hd = oracle.select_channels(lay.x_cal, lay.w, lay.k_out)
+    nnz = (lay.k - lay.k_out) // 8
+    a = oracle.quantize_split_act(lay.x, mp, low="i8", branch="i8")
+    wp = oracle.pack_weights_sq(lay.w, mp, hd, nnz)
+    y = oracle.dual_gemm(a, wp).astype(np.float64)
+    x, w = lay.x.astype(np.float64), lay.w.astype(np.float64)
+    low = mp >= 0
+    ch_low = np.nonzero(low)[0]               # channel of each low slot
+    # per-weight error: half a step of whichever part (int4 or int8) holds it
+    nib = np.stack([wp["w_low"] & 0xF, wp["w_low"] >> 4], -1).reshape(lay.n, -1)[:, : len(ch_low)]
+    marked = (nib == 8).T                     # [k_low][n]
+    ew = np.zeros_like(w)
+    ew[ch_low, :] = np.where(marked, 0.5 * wp["s_w8"][None, :].astype(np.float64),
+                             0.5 * wp["s_w"][None, :].astype(np.float64))
+    ew[~low, :] = 0.5 * wp["s_wo"][None, :].astype(np.float64)
+    ex = np.zeros_like(x)
+    ex[:, low] = 0.5 * a["s_x"][:, None].astype(np.float64)
+    ex[:, ~low] = 0.5 * a["s_xo"][:, None].astype(np.float64)
+    bound = np.abs(x) @ ew + ex @ np.abs(w) + ex @ ew
+    err = np.abs(y - x @ w)
+    assert (err <= bound + 1e-9).all()
+    # Sensitivity: each slip named above moves some output by more than twice
+    # its bound.  (A dropped marked part is below this worst-case bound here;
+    # the hand-worked case with an int8 branch fixes that term to the bit.)  The accumulators are decoded from the format here, not taken
+    # from the oracle.
+    k_low = a["k_low"]
+    cx = a["x_low"].view(np.int8).astype(np.int64)[:, :k_low]
+    dense_sp = np.zeros((lay.n, k_low), np.int64)
+    for nn in range(lay.n):
+        dense_sp[nn, np.nonzero(marked[:, nn])[0]] = wp["sq_val"][nn]
+    acc_sp = (cx @ dense_sp.T).astype(np.float64)
+    xo = a["x_out"].view(np.int8).astype(np.int64)[:, : lay.k_out]
+    wo = wp["w_out"].view(np.int8).astype(np.int64)[:, : lay.k_out]
+    acc_o = (xo @ wo.T).astype(np.float64)
+    sx, sxo = a["s_x"].astype(np.float64)[:, None], a["s_xo"].astype(np.float64)[:, None]
+    sw4, sw8 = wp["s_w"].astype(np.float64)[None, :], wp["s_w8"].astype(np.float64)[None, :]
+    swo = wp["s_wo"].astype(np.float64)[None, :]
+    slips = {
+        "branch dropped": np.abs(sxo * swo * acc_o),
+        "branch scaled by s_x": np.abs((sxo - sx) * swo * acc_o),
+        "marked part scaled by s_w4": np.abs(sx * (sw4 - sw8) * acc_sp),
+    }
+    for name, delta in slips.items():
+        assert (delta > 2 * bound + 1e-9).any(), name
+
+
+# ------------------------------------------------------------------ FP8 quantiser range
+def test_fp8_quantizer_maps_absmax_to_448():
+    """OCP E4M3 (the FP8 fallback of the OSC abstract): the largest finite
+    value is 448 (code 0x7E).  The symmetric quantiser scales a vector so its
+    absmax lands on 448, i.e. scale = absmax / 448 and the absmax element
+    gets 0x7E (0xFE when negative); every other code is the round-to-nearest
+    E4M3 value of v * 448 / absmax (torch's float8_e4m3fn cast as the
+    independent routine)."""
+    rng = np.random.default_rng(13)
+    for sign in (1.0, -1.0):
+        v = rng.standard_normal(257).astype(np.float32)
+        i = int(np.argmax(np.abs(v)))
+        v[i] = sign * (np.abs(v).max() + np.float32(0.75))
+        codes, s = oracle.quantize_vec(v, "fp8")
+        a = np.float32(np.abs(v).max())
+        assert s == np.float32(a / np.float32(448.0))
+        assert int(codes[i]) == (0x7E if sign > 0 else 0xFE)
+        inv = np.float32(448.0) / a
+        p = (v * inv).astype(np.float32)
+        ref = torch.from_numpy(p).to(torch.float8_e4m3fn).view(torch.uint8).numpy().astype(np.int64)
+        zero = (ref & 0x7F) == 0
+        got = codes.astype(np.int64) & 0xFF
+        assert (got[~zero] == ref[~zero]).all() and (got[zero] == 0).all()
+        # the dequantised vector is within half an E4M3 step of v
+        deq = np.array([oracle.e4m3_to_float(c) for c in got]) * float(s)
+        assert np.all(np.abs(deq - v) <= np.abs(v) * 2.0 ** -4 + float(s) * 2.0 ** -10)
