@@ -17,6 +17,8 @@ the method:
 * :func:`quantize_split_act` -- per-token int4/int8 quantisation plus the
   outlier sub-tensor gather (OSC abstract).
 * :func:`dual_gemm`        -- low path + masked path + branch + fused output.
+* :func:`i4x2_to_e2m3`     -- the same int4 codes stored in 6-bit E2M3 fields,
+  K-blocked (the storage a 6-bit matrix unit reads).
 """
 from __future__ import annotations
 
@@ -76,6 +78,10 @@ def _declare(lib):
     lib.orc_sq_row.restype = None
     lib.orc_pack_weights_sq.argtypes = [P, I64, I64, P, P, I64, I64, I64, I64, I64, P, P, P, P, P, P]
     lib.orc_pack_weights_sq.restype = None
+    lib.orc_e2m3_field_of_code.argtypes = [INT]
+    lib.orc_e2m3_field_of_code.restype = ctypes.c_uint8
+    lib.orc_i4x2_to_e2m3.argtypes = [P, I64, I64, I64, P]
+    lib.orc_i4x2_to_e2m3.restype = None
     lib.orc_quantize_split_act.argtypes = [P, INT, I64, I64, I64, P, I64, I64, I64, I64, INT, INT,
                                            P, P, P, P]
     lib.orc_quantize_split_act.restype = None
@@ -124,6 +130,27 @@ def e4m3_from_float(v: float) -> int:
 
 def e4m3_to_float(c: int) -> float:
     return float(_load().orc_e4m3_to_double(int(c) & 0xFF))
+
+
+def e2m3_field_of_code(code: int) -> int:
+    return int(_load().orc_e2m3_field_of_code(int(code)))
+
+
+def pad_rows(rows: int) -> int:
+    """Row count of the K-blocked 6-bit layout: rows rounded up to 256."""
+    return -(-rows // 256) * 256
+
+
+def i4x2_to_e2m3(packed: np.ndarray, rows_pad: int | None = None) -> np.ndarray:
+    """Packed int4 rows [rows][ldk] -> the K-blocked E2M3 array
+    [2*ldk/128][rows_pad][96] holding the same codes."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    rows, ldk = packed.shape
+    rp = pad_rows(rows) if rows_pad is None else rows_pad
+    out = np.zeros((2 * ldk // 128, rp, 96), dtype=np.uint8)
+    if rows and ldk:
+        _load().orc_i4x2_to_e2m3(_p(packed), rows, ldk, rp, _p(out))
+    return out
 
 
 def quantize_vec(v: np.ndarray, fmt: str):

@@ -446,6 +446,45 @@ void orc_quantize_split_act(const void* x, int x_fmt, int64_t m, int64_t k, int6
 }
 
 /* ------------------------------------------------------------------ */
+/* Storage of int4 codes in 6-bit OCP E2M3 fields (K-blocked layout)   */
+/* ------------------------------------------------------------------ */
+
+/* OCP MX E2M3: 1 sign bit (bit 5), 2 exponent bits (bits 4..3, bias 1), 3
+ * mantissa bits (bits 2..0); exponent 0 is subnormal with value
+ * (-1)^s * 2^(1-1) * m/8.  An int4 code c in [-7, 7] is held as the
+ * subnormal of magnitude |c|/8: field = (c < 0) << 5 | |c|.  The arithmetic
+ * on the codes is unchanged: this is how the same integers are stored for
+ * a 6-bit matrix unit (the product of two fields is c_x * c_w / 64). */
+uint8_t orc_e2m3_field_of_code(int code) {
+  int a = code < 0 ? -code : code;
+  return (uint8_t)(((code < 0) ? 0x20 : 0) | (a & 7));
+}
+
+/* Re-encode packed int4 rows (the layout of orc_quantize_split_act /
+ * orc_pack_weights: [rows][ldk], slot 2i in the low nibble of byte i) into
+ * the K-blocked E2M3 layout [pad/128][rows_pad][96]: slot j of row r sits in
+ * block j/128, 24-byte group (j%128)/32, field j%32 at bits 6*(j%32) of that
+ * group, little-endian.  pad = 2*ldk slots per row; rows_pad >= rows; the
+ * rows past `rows` are left zero. */
+void orc_i4x2_to_e2m3(const uint8_t* packed, int64_t rows, int64_t ldk, int64_t rows_pad,
+                      uint8_t* out) {
+  const int64_t pad = 2 * ldk, nblk = pad / 128;
+  memset(out, 0, (size_t)(nblk * rows_pad * 96));
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t j = 0; j < pad; ++j) {
+      uint8_t b = packed[r * ldk + (j >> 1)];
+      uint8_t nib = (uint8_t)(((j & 1) ? (b >> 4) : b) & 0xF);
+      int code = (nib & 0x8) ? (int)nib - 16 : (int)nib;
+      uint32_t f = orc_e2m3_field_of_code(code);
+      uint8_t* grp = out + ((j / 128) * rows_pad + r) * 96 + ((j % 128) / 32) * 24;
+      int64_t bit = 6 * (j % 32);
+      for (int t = 0; t < 6; ++t)
+        if ((f >> t) & 1u) grp[(bit + t) >> 3] |= (uint8_t)(1u << ((bit + t) & 7));
+    }
+  }
+}
+
+/* ------------------------------------------------------------------ */
 /* Steps a3-a5 (and the weight-side masked path): the dual GEMM        */
 /* ------------------------------------------------------------------ */
 

@@ -520,3 +520,56 @@ def test_fp8_quantizer_maps_absmax_to_448():
         # the dequantised vector is within half an E4M3 step of v
         deq = np.array([oracle.e4m3_to_float(c) for c in got]) * float(s)
         assert np.all(np.abs(deq - v) <= np.abs(v) * 2.0 ** -4 + float(s) * 2.0 ** -10)
+
+
+# ------------------------------------------------------------------ int4 codes in E2M3 fields
+def _e2m3_value(field):
+    """OCP MX E2M3 by its definition: sign bit 5, exponent bits 4..3 (bias 1),
+    mantissa bits 2..0; exponent 0 is subnormal."""
+    s, e, m = (field >> 5) & 1, (field >> 3) & 3, field & 7
+    v = (m / 8.0) if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 1)
+    return -v if s else v
+
+
+def test_e2m3_field_holds_code_over_8():
+    for c in range(-7, 8):
+        f = oracle.e2m3_field_of_code(c)
+        assert 0 <= f < 64
+        assert _e2m3_value(f) == c / 8.0
+
+
+def test_e2m3_storage_hand_case(golden):
+    g = golden("e2m3_storage_hand_case.txt")
+    codes = [int(v) for v in g["row0_codes"][0]]
+    packed = np.zeros((2, 128), np.uint8)
+    for j, c in enumerate(codes):
+        packed[0, j >> 1] |= (c & 0xF) << (4 * (j & 1))
+    assert packed[0, :4].tolist() == _hexbytes(g["row0_packed"])[0].tolist()
+    j1, c1 = int(g["row1_slot"][0][0]), int(g["row1_code"][0][0])
+    packed[1, j1 >> 1] |= (c1 & 0xF) << (4 * (j1 & 1))
+    out = oracle.i4x2_to_e2m3(packed)
+    assert out.shape == (2, 256, 96)
+    assert out[0, 0, :6].tolist() == _hexbytes(g["row0_block0"])[0].tolist()
+    assert not out[0, 0, 6:].any() and not out[1, 0].any()
+    assert out[1, 1, :3].tolist() == _hexbytes(g["row1_block1"])[0].tolist()
+    assert not out[1, 1, 3:].any() and not out[0, 1].any() and not out[:, 2:].any()
+
+
+def test_e2m3_storage_brute_force_reader():
+    """Random packed rows: every slot read back from the K-blocked array by
+    its position formula decodes (OCP E2M3) to the nibble's code / 8."""
+    rng = np.random.default_rng(31)
+    rows, pad = 5, 512
+    codes = rng.integers(-7, 8, (rows, pad))
+    packed = np.zeros((rows, pad // 2), np.uint8)
+    for r in range(rows):
+        for j in range(pad):
+            packed[r, j >> 1] |= (int(codes[r, j]) & 0xF) << (4 * (j & 1))
+    out = oracle.i4x2_to_e2m3(packed)
+    bits = np.unpackbits(out, axis=-1, bitorder="little")  # [blk][row][768]
+    for r in range(rows):
+        for j in range(pad):
+            grp = bits[j // 128, r, ((j % 128) // 32) * 192:]
+            f = int(sum(int(grp[6 * (j % 32) + t]) << t for t in range(6)))
+            assert _e2m3_value(f) * 8 == codes[r, j]
+    assert not out[:, rows:].any()
