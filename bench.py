@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the dual-path outlier-separated GEMM on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--sweep] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--no-sweep] [--no-rows] [--no-cpu]
 
 Workload: the Llama-3-70B-shaped prefill linears (M = 4096 tokens;
 8192->8192, 8192->28672, 28672->8192) at outlier fraction 1/16, bf16 input
@@ -14,11 +14,14 @@ step of the path, inputs resident in HBM.
 Prints ONE JSON line.  ``value`` is effective TOPS = sum(2*M*N*K) / step
 time.  ``roofline`` describes the dominant kernel (the dual GEMM): achieved
 algorithmic ops (2*M*N*K per launch) / its average launch time measured with
-HIP events on the stream it runs on, against the int8 MFMA peak;
-``traffic`` is HBM bytes per GEMM launch from the committed rocprofv3
-counter summary, or null if the kernel source changed since it was taken.
-``cpu_baseline`` times the scalar CPU oracle on a bounded row sample of the
-same step.  ``--sweep`` adds the outlier-fraction sweep (1/2 ... 1/16).
+HIP events on the stream it runs on, against the kernel's own matrix-core
+ceiling (the low path's operations at the int8 peak plus the branch's at the
+bf16 peak); ``traffic`` is HBM bytes per GEMM launch from the committed
+rocprofv3 counter summary, or null if the kernel source changed since it was
+taken.  ``cpu_baseline`` times the scalar CPU oracle on a bounded row sample
+of the same step.  ``sweep`` holds the outlier-fraction sweep (1/2 ... 1/16)
+of the same layers and the Llama-3-8B-shaped layers; ``rows`` every other
+row of the path on its own workload.
 """
 from __future__ import annotations
 
@@ -74,6 +77,17 @@ def dual_bound_frac(k_low, k_out):
     """Largest share of the int8 peak the dual path can reach when the bf16
     branch runs at half the int8 rate: K / (K_low + 2 K_out)."""
     return (k_low + k_out) / (k_low + 2.0 * k_out)
+
+
+def mfma_bound_us(m, n, k_low, k_out, low_peak=PEAK_INT8_TOPS, branch_peak=PEAK_BF16_TFLOPS):
+    """Shortest time the method's own arithmetic can take on the matrix cores:
+    2*M*N*K_low low-path operations at the low path's peak plus 2*M*N*K_out
+    branch operations at the branch's peak (TOP/s in, microseconds out)."""
+    return 2.0 * m * n * (k_low / low_peak + k_out / branch_peak) / 1e6
+
+
+def pct(v, q):
+    return round(float(np.percentile(np.asarray(v), q)), 2)
 
 
 class LayerRun:
@@ -135,17 +149,18 @@ def time_layers(torch, runs, stream, steps, warmup):
     t1.record(stream)
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
-    act_ms = np.zeros(len(runs))
-    gemm_ms = np.zeros(len(runs))
+    act = np.zeros((steps, len(runs)))
+    gemm = np.zeros((steps, len(runs)))
     for s in range(steps):
         for i in range(len(runs)):
             e = evs[s][i]
-            act_ms[i] += e[0].elapsed_time(e[1])
-            gemm_ms[i] += e[1].elapsed_time(e[2])
-    return total_ms / steps, act_ms / steps, gemm_ms / steps
+            act[s, i] = e[0].elapsed_time(e[1])
+            gemm[s, i] = e[1].elapsed_time(e[2])
+    time_layers.samples = (act, gemm)
+    return total_ms / steps, act.mean(0), gemm.mean(0)
 
 
-def cpu_baseline(runs, rows_per_layer):
+def cpu_baseline(lays, rows_per_layer):
     """The oracle (untuned) on a bounded sample of the same step: the online
     stages (activation quantise/split + dual GEMM) for `rows_per_layer` token
     rows of each layer.  Offline packing is outside the step, as on the GPU."""
@@ -153,20 +168,40 @@ def cpu_baseline(runs, rows_per_layer):
     from outlier_split_mixed_amd import synth
 
     total_ops, total_s = 0.0, 0.0
-    for r in runs:
-        lay = r.lay
-        _, o_mp, _, _ = oracle.select_channels(lay.x_cal, lay.w, r.k_out)
+    for lay in lays:
+        _, o_mp, _, _ = oracle.select_channels(lay.x_cal, lay.w, lay.k_out)
         o_w = oracle.pack_weights(lay.w, o_mp)
         xs = synth.to_bf16_bits(lay.x[:rows_per_layer])
         t = time.perf_counter()
         o_a = oracle.quantize_split_act(xs, o_mp, x_fmt="bf16")
         oracle.dual_gemm(o_a, o_w)
         total_s += time.perf_counter() - t
-        total_ops += 2.0 * rows_per_layer * r.n * r.k
+        total_ops += 2.0 * rows_per_layer * lay.n * lay.k
     return dict(value=round(total_ops / total_s / 1e12, 6), unit="TOPS", cores=oracle.num_threads(),
-                kind="oracle",
+                kind="oracle", cpu_model=cpu_model(),
                 sample=f"{rows_per_layer} token rows x all outputs of each of the 3 layers "
                        f"(act quantise/split + dual GEMM), {total_s:.1f} s")
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def progress(msg):
+    """One line per finished section on stderr (stdout carries only the JSON)."""
+    print(f"# bench: {msg}", file=sys.stderr, flush=True)
+
+
+def _add(out, row):
+    out.append(row)
+    progress(row["row"])
 
 
 def time_call(torch, stream, fn, iters=10, warmup=2):
@@ -205,14 +240,14 @@ def rows_section(sqf, torch, stream):
         _, mp, _, _ = sqf.sqf_select_channels(x_cal, w, k_out, stream=stream)
         # algorithmic bytes: x_cal and W read once, scores / hdiag / map / idx written
         b0 = 4 * lay.x_cal.size + 4 * lay.k * lay.n + (8 + 4 + 4) * lay.k + 4 * k_out
-        out.append(dict(row="a0 select (offline)", shape=f"{lay.k}x{lay.n}, {lay.x_cal.shape[0]} cal rows",
+        _add(out, dict(row="a0 select (offline)", shape=f"{lay.k}x{lay.n}, {lay.x_cal.shape[0]} cal rows",
                         ms=round(t, 3), gbs=round(b0 / t / 1e6, 1), frac_hbm=round(b0 / t / 1e6 / PEAK_HBM_GBS, 3)))
         t = time_call(torch, stream, lambda: sqf.sqf_pack_weights(w, mp, stream=stream), iters=3, warmup=1)
         # W and the map read once; int4 rows, bf16 branch rows and scales written
         ldk = sqf.sqf_pad_k_low(lay.k - k_out) // 2
         ldo = sqf.sqf_pad_k_out(k_out, "bf16")
         b1 = 4 * lay.k * lay.n + 4 * lay.k + lay.n * (ldk + 2 * ldo + 4)
-        out.append(dict(row="a1 pack (offline)", shape=f"{lay.k}x{lay.n}", ms=round(t, 3),
+        _add(out, dict(row="a1 pack (offline)", shape=f"{lay.k}x{lay.n}", ms=round(t, 3),
                         gbs=round(b1 / t / 1e6, 1), frac_hbm=round(b1 / t / 1e6 / PEAK_HBM_GBS, 3)))
         del w, x_cal, mp
         torch.cuda.empty_cache()
@@ -239,7 +274,7 @@ def rows_section(sqf, torch, stream):
             esz = 2 if br == "bf16" else 1
             act_b = rows * (k * 2 + a.ldk + a.ldo * esz + 4)
             gemm_b = rows * (a.ldk + a.ldo * esz + 8) + len(lays) * n * (a.ldk + a.ldo * esz + 8) + rows * n * 4
-            out.append(dict(row=f"a6 grouped {name} ({br} branch)",
+            _add(out, dict(row=f"a6 grouped {name} ({br} branch)",
                             shape=f"{len(lays)} experts, {rows} rows, {k}->{n}, k_out {ko}",
                             act_us=round(ta * 1e3, 1),
                             act_frac_hbm=round(act_b / (ta * 1e-3) / 1e9 / PEAK_HBM_GBS, 3),
@@ -271,13 +306,19 @@ def rows_section(sqf, torch, stream):
         y = torch.empty((lay.m, lay.n), dtype=torch.float32, device="cuda")
         ta = time_call(torch, stream, lambda: sqf.sqf_quantize_split_act(xt, mp, a, stream=stream))
         tg = time_call(torch, stream, lambda: sqf.sqf_dual_gemm(a, wt, y=y, stream=stream), iters=5)
+        # the method's own work: every low slot, every marked value and every
+        # branch channel once (2*M*N*(K_low + nnz + K_out) int8 operations)
+        nnz = k_low // 8
+        own_ops = 2.0 * lay.m * lay.n * (k_low + nnz + k_out)
+        # what the kernel issues: two dense int8 passes over K_low plus the branch
         mfma_ops = 2.0 * lay.m * lay.n * (2 * k_low + k_out)
-        out.append(dict(row="a7 SQ-format weight side (int8 acts, masked int8 part, int8 branch)",
-                        shape=f"{lay.m}x{lay.k}->{lay.n}, nnz {k_low // 8}/row",
+        _add(out, dict(row="a7 SQ-format weight side (int8 acts, masked int8 part, int8 branch)",
+                        shape=f"{lay.m}x{lay.k}->{lay.n}, nnz {nnz}/row",
                         act_us=round(ta * 1e3, 1), gemm_us=round(tg * 1e3, 1),
                         gemm_eff_tops=round(2.0 * lay.m * lay.n * lay.k / (tg * 1e-3) / 1e12, 1),
-                        mfma_tops=round(mfma_ops / (tg * 1e-3) / 1e12, 1),
-                        frac_int8_peak=round(mfma_ops / (tg * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4)))
+                        own_work_tops=round(own_ops / (tg * 1e-3) / 1e12, 1),
+                        frac_int8_peak=round(own_ops / (tg * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
+                        issued_mfma_tops=round(mfma_ops / (tg * 1e-3) / 1e12, 1)))
         del wt, xt, a, y, w, x_cal
         torch.cuda.empty_cache()
     return out
@@ -288,7 +329,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--sweep", action="store_true", help="also time outlier fractions 1/2..1/16")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the outlier-fraction sweep and the Llama-3-8B-shaped layers")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=128)
     ap.add_argument("--no-rows", action="store_true",
@@ -312,20 +354,32 @@ def main():
     runs = [LayerRun(sqf, torch, synth.llama3_70b(i, 16), 8192 // 16 if i < 2 else 28672 // 16,
                      stream) for i in range(3)]
     setup_s = time.time() - t_setup
+    progress(f"setup of the three layers done ({setup_s:.1f} s)")
     step_ms, act_ms, gemm_ms = time_layers(torch, runs, stream, args.steps, args.warmup)
+    act_s, gemm_s = time_layers.samples
+    progress(f"step timed: {step_ms:.4f} ms")
     total_ops = sum(r.ops for r in runs)
     value = total_ops / (step_ms * 1e-3) / 1e12
     gemm_ops = sum(r.ops for r in runs)
     achieved = gemm_ops / (gemm_ms.sum() * 1e-3) / 1e12
+    # the GEMM's own ceiling: each layer's low part at the int8 peak and its
+    # bf16 branch at the bf16 peak, summed over the three launches
+    bound_us = sum(mfma_bound_us(r.m, r.n, r.k - r.k_out, r.k_out) for r in runs)
+    peak_eff = gemm_ops / (bound_us * 1e-6) / 1e12
     detail = []
-    for r, a, g in zip(runs, act_ms, gemm_ms):
+    for i, (r, a, g) in enumerate(zip(runs, act_ms, gemm_ms)):
         tops = r.ops / (g * 1e-3) / 1e12
+        b_us = mfma_bound_us(r.m, r.n, r.k - r.k_out, r.k_out)
         detail.append(dict(shape=f"{r.m}x{r.k}->{r.n}", k_out=r.k_out, act_us=round(a * 1e3, 2),
+                           act_us_p10_p50_p90=[pct(act_s[:, i] * 1e3, q) for q in (10, 50, 90)],
                            act_gbs=round(r.act_bytes / (a * 1e-3) / 1e9, 1),
-                           gemm_us=round(g * 1e3, 2), gemm_tops=round(tops, 1),
+                           act_frac_hbm=round(r.act_bytes / (a * 1e-3) / 1e9 / PEAK_HBM_GBS, 3),
+                           gemm_us=round(g * 1e3, 2),
+                           gemm_us_p10_p50_p90=[pct(gemm_s[:, i] * 1e3, q) for q in (10, 50, 90)],
+                           gemm_tops=round(tops, 1),
                            pct_int8_peak=round(100 * tops / PEAK_INT8_TOPS, 2),
-                           pct_dual_bound=round(100 * tops / (PEAK_INT8_TOPS * dual_bound_frac(
-                               r.k - r.k_out, r.k_out)), 2)))
+                           mfma_bound_us=round(b_us, 1),
+                           frac_mfma_bound=round(b_us / (g * 1e3), 4)))
     # the same step with bf16 Y (an output-type option, not the measured
     # configuration; with the rows section): its GEMM times per layer
     bf16_y = None
@@ -359,33 +413,47 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "pct_int8_peak": round(100 * value / PEAK_INT8_TOPS, 2),
         "roofline": {"bound": "mfma", "kernel": "k_dual_gemm", "achieved": round(achieved, 1),
-                     "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
-                     "frac": round(achieved / PEAK_INT8_TOPS, 4),
+                     "peak": round(peak_eff, 1), "unit": "TOP/s",
+                     "frac": round(achieved / peak_eff, 4),
                      "traffic": traffic, "traffic_unit": "bytes per launch",
+                     "peak_basis": "2MN*K_low at the 5.0 POP/s int8 peak + 2MN*K_out at the "
+                                   "2.5 PFLOP/s bf16 peak, over the three launches",
+                     "frac_int8_peak": round(achieved / PEAK_INT8_TOPS, 4),
                      "avg_launch_us": round(float(gemm_ms.mean()) * 1e3, 2),
                      "ops_per_launch": gemm_ops / 3},
         "detail": detail,
         "bf16_y_step": bf16_y,
         "setup_s": round(setup_s, 1),
     }
-    if args.sweep:
+    lays = [r.lay for r in runs]
+    del runs
+    torch.cuda.empty_cache()
+    if not args.no_sweep:
+        # the Llama-3-70B-shaped layers at outlier fractions 1/2 ... 1/16, and
+        # the Llama-3-8B-shaped layers at 1/16 (M = 2048)
         sweep = []
-        for den in (2, 4, 8, 16):
-            for i in range(3):
-                lay = synth.llama3_70b(i, den)
-                r = LayerRun(sqf, torch, lay, lay.k // den, stream)
-                s_ms, a_ms, g_ms = time_layers(torch, [r], stream, max(5, args.steps // 2), 2)
-                tops = r.ops / (g_ms[0] * 1e-3) / 1e12
-                sweep.append(dict(frac=f"1/{den}", shape=f"{r.m}x{r.k}->{r.n}",
-                                  gemm_us=round(float(g_ms[0]) * 1e3, 1), gemm_tops=round(tops, 1),
-                                  pct_int8_peak=round(100 * tops / PEAK_INT8_TOPS, 2),
-                                  pct_dual_bound=round(100 * tops / (PEAK_INT8_TOPS * dual_bound_frac(
-                                      r.k - r.k_out, r.k_out)), 2)))
-                del r
-                torch.cuda.empty_cache()
+        cases = [(f"1/{den}", synth.llama3_70b(i, den)) for den in (2, 4, 8, 16) for i in range(3)]
+        cases += [("1/16", synth.llama3_8b(i)) for i in range(3)]
+        for frac, lay in cases:
+            r = LayerRun(sqf, torch, lay, lay.k_out, stream)
+            s_ms, a_ms, g_ms = time_layers(torch, [r], stream, max(5, args.steps // 2), 2)
+            g_us = float(g_ms[0]) * 1e3
+            tops = r.ops / (g_us * 1e-6) / 1e12
+            b_us = mfma_bound_us(r.m, r.n, r.k - r.k_out, r.k_out)
+            sweep.append(dict(workload=lay.name.split(".")[0], frac=frac,
+                              shape=f"{r.m}x{r.k}->{r.n}", k_out=r.k_out,
+                              act_us=round(float(a_ms[0]) * 1e3, 1),
+                              gemm_us=round(g_us, 1), gemm_tops=round(tops, 1),
+                              layer_us=round(float(a_ms[0] + g_ms[0]) * 1e3, 1),
+                              pct_int8_peak=round(100 * tops / PEAK_INT8_TOPS, 2),
+                              frac_mfma_bound=round(b_us / g_us, 4)))
+            del r
+            torch.cuda.empty_cache()
+            progress(f"sweep {lay.name} {frac}: {g_us:.1f} us")
         out["sweep"] = sweep
     if not args.no_rows:
         out["rows"] = rows_section(sqf, torch, stream)
+        progress("rows section done")
     if args.copy_bytes:
         # plain device copy of a known size: the reference that scales the
         # memory-traffic counters of a profiled run to bytes
@@ -396,7 +464,7 @@ def main():
         torch.cuda.synchronize()
         out["copy_calibration_bytes"] = args.copy_bytes
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(runs, args.cpu_rows)
+        out["cpu_baseline"] = cpu_baseline(lays, args.cpu_rows)
     print(json.dumps(out), flush=True)
 
 

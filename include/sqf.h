@@ -26,8 +26,20 @@
  *   x_low  [m][ldk] bytes: int4 codes in [-7,7], two's complement, slot 2i in
  *          the low nibble of byte i, slot 2i+1 in the high nibble (SQF_I4X2);
  *          or one int8 code per byte (SQF_I8).  Padding slots are 0.
- *   w_low  [n][ldk] bytes: int4 codes, same packing; nibble 0x8 is the
- *          reserved "high precision here" mark (weight-side format only).
+ *          SQF_I4_E2M3 holds the same int4 codes, each in a 6-bit OCP E2M3
+ *          field read as a subnormal (value code/8: field = sign << 5 | |code|),
+ *          32 slots per 24 bytes (slot i of a 32-group at bits 6i..6i+5,
+ *          little-endian) in a K-blocked array [ldk/96][sqf_pad_rows(m)][96]:
+ *          the 96 bytes of 128 consecutive slots of a row are contiguous, and
+ *          block kb of every row follows block kb of the row before.  Rows
+ *          beyond m are never written and never reach an output.
+ *          SQF_MXFP4 holds OCP MXFP4: E2M1 codes packed like SQF_I4X2
+ *          ([m][ldk], ldk = pad/2) plus one E8M0 scale byte per 32 slots in
+ *          s_xb [m][pad/32].
+ *   w_low  [n][ldk] bytes: int4 codes, same packings (SQF_I4_E2M3: [ldk/96]
+ *          [sqf_pad_rows(n)][96]; SQF_MXFP4: E2M1 with s_wb [n][pad/32]);
+ *          nibble 0x8 is the reserved "high precision here" mark
+ *          (weight-side format only).
  *   x_out  [m][ldo], w_out [n][ldo]: branch operands (bf16, E4M3 or int8).
  *   Y      [m][ldy] fp32.
  *   Low slots are padded to sqf_pad_k_low(k_low) (a multiple of 256); branch
@@ -62,7 +74,7 @@
 extern "C" {
 #endif
 
-#define SQF_ABI_VERSION 1
+#define SQF_ABI_VERSION 2
 
 typedef enum {
   SQF_OK = 0,
@@ -78,8 +90,21 @@ typedef enum {
   SQF_BF16 = 1,
   SQF_FP8_E4M3 = 2, /* OCP E4M3 (max 448, no infinities) */
   SQF_I8 = 3,
-  SQF_I4X2 = 4 /* two int4 codes per byte */
+  SQF_I4X2 = 4,    /* two int4 codes per byte */
+  SQF_I4_E2M3 = 5, /* int4 codes, one per 6-bit E2M3 field, K-blocked (see above) */
+  SQF_MXFP4 = 6    /* OCP MXFP4: E2M1 codes + one E8M0 scale per 32 slots */
 } sqf_dtype;
+
+/* GEMM tile choice of the *_ex calls.  SQF_TILE_AUTO picks by problem size;
+ * the others force 256x256, 128x128 or 64x64 output tiles (the E4M3 branch
+ * and the SQF_I4_E2M3 / SQF_MXFP4 low paths have one tile shape each: a
+ * forced tile they do not have returns SQF_ERR_UNSUPPORTED). */
+typedef enum {
+  SQF_TILE_AUTO = -1,
+  SQF_TILE_256 = 0,
+  SQF_TILE_128 = 1,
+  SQF_TILE_64 = 2
+} sqf_tile;
 
 /* Quantised weights, caller-allocated.  `groups` weight sets of identical
  * shape may be stacked back to back (grouped GEMM); every array then gains a
@@ -93,18 +118,26 @@ typedef struct sqf_weights {
   int64_t ldo;    /* elements per w_out row = sqf_pad_k_out(k_out, branch) */
   int32_t branch; /* SQF_BF16 | SQF_FP8_E4M3 | SQF_I8 */
   int32_t groups; /* >= 1 */
-  uint8_t* w_low; /* [groups][n][ldk] int4 codes */
-  float* s_w;     /* [groups][n] low scale (s_w4 of the weight-side format) */
+  int32_t low;    /* SQF_I4X2 | SQF_I4_E2M3 | SQF_MXFP4 */
+  int32_t reserved0;
+  uint8_t* w_low; /* [groups][n][ldk] int4 codes (see the layouts above) */
+  float* s_w;     /* [groups][n] low scale (s_w4 of the weight-side format);
+                     unused (may be NULL) for SQF_MXFP4 */
+  uint8_t* s_wb;  /* SQF_MXFP4 only: [n][pad/32] E8M0 block scales */
   void* w_out;    /* [groups][n][ldo] branch codes; NULL when k_out == 0 */
   float* s_wo;    /* [groups][n] branch scale; NULL for SQF_BF16 */
-  /* weight-side SQ-format ([SQF-art] 九): sq_nnz > 0 marks, per output row,
-   * the sq_nnz most important low slots with nibble 0x8 and stores their
-   * int8 values in ascending slot order.  groups must be 1. */
-  int64_t sq_nnz;       /* 0 = channel-split (OSC) format */
-  int8_t* sq_val;       /* [n][sq_nnz], 16-byte aligned */
-  float* s_w8;          /* [n] scale of sq_val */
-  int32_t* sq_tile_off; /* [n][ldk/128 + 1]: count of marked slots before
-                           each 256-slot tile (derived, written by pack) */
+  /* weight-side SQ-format ([SQF-art] 六, 七, 九): sq_nnz > 0 marks, per
+   * output row, the most important low slots of every bank with nibble 0x8
+   * and stores their int8 values in ascending slot order.  groups must be 1,
+   * low SQF_I4X2. */
+  int64_t sq_nnz;  /* 0 = channel-split (OSC) format; else marked slots per
+                      row, an equal share in every bank */
+  int64_t sq_bank; /* slots per bank: 0 = the whole row (k_low slots) is one
+                      bank; else a multiple of 64 that divides k_low, with
+                      sq_nnz * sq_bank / k_low marks in every bank */
+  int8_t* sq_val;  /* [n][sq_nnz], 16-byte aligned, in ascending slot order
+                      (so bank by bank) */
+  float* s_w8;     /* [n] scale of sq_val */
 } sqf_weights;
 
 /* Quantised activations, caller-allocated. */
@@ -114,10 +147,12 @@ typedef struct sqf_acts {
   int64_t k_out;  /* outlier channels */
   int64_t ldk;    /* bytes per x_low row: pad/2 (SQF_I4X2) or pad (SQF_I8) */
   int64_t ldo;    /* elements per x_out row */
-  int32_t low;    /* SQF_I4X2 | SQF_I8 (SQF_I8 only with weight-side format) */
+  int32_t low;    /* SQF_I4X2 | SQF_I8 (weight-side format only) |
+                     SQF_I4_E2M3 | SQF_MXFP4 */
   int32_t branch; /* SQF_BF16 | SQF_FP8_E4M3 | SQF_I8 */
-  uint8_t* x_low; /* [m][ldk] */
-  float* s_x;     /* [m] */
+  uint8_t* x_low; /* [m][ldk], or K-blocked for SQF_I4_E2M3 (see above) */
+  float* s_x;     /* [m]; unused (may be NULL) for SQF_MXFP4 */
+  uint8_t* s_xb;  /* SQF_MXFP4 only: [m][pad/32] E8M0 block scales */
   void* x_out;    /* [m][ldo]; NULL when k_out == 0 */
   float* s_xo;    /* [m]; NULL for SQF_BF16 */
 } sqf_acts;
@@ -131,6 +166,10 @@ const char* sqf_last_error(void);
 
 /* Padded low-slot count: round_up(k_low, 256); 0 stays 0; -1 if k_low < 0. */
 int64_t sqf_pad_k_low(int64_t k_low);
+
+/* Row count of the K-blocked SQF_I4_E2M3 arrays: round_up(rows, 256); 0
+ * stays 0; -1 if rows < 0. */
+int64_t sqf_pad_rows(int64_t rows);
 
 /* Padded branch row length in elements: round_up(k_out, 64) for SQF_BF16,
  * round_up(k_out, 128) for SQF_FP8_E4M3 / SQF_I8 (128 bytes per stage);
@@ -146,8 +185,11 @@ int64_t sqf_pad_k_out(int64_t k_out, int32_t branch);
  * The k_out channels of highest score (ties: lower index) become outliers.
  * Outputs: idx_out [k_out] ascending (may be NULL if k_out == 0), map_out
  * [k] (required: holds the rank counts until the map is written),
- * score_out [k] (required: also used as workspace), hdiag_out [k] or
- * NULL.  Asynchronous; k <= 1048576, m_cal >= 1, 0 <= k_out <= k. */
+ * score_out [k] or NULL, hdiag_out [k] or NULL.  The scores double as the
+ * call's workspace; with score_out == NULL the call takes k doubles from
+ * the stream-ordered allocator (hipMallocAsync on `stream`) and returns
+ * them (hipFreeAsync) before it returns.  Asynchronous on `stream` either
+ * way; k <= 1048576, m_cal >= 1, 0 <= k_out <= k. */
 sqf_status sqf_select_channels(const float* x_cal, int64_t m_cal, int64_t k, const float* w,
                                int64_t n, int64_t k_out, int32_t* idx_out, int32_t* map_out,
                                double* score_out, float* hdiag_out, void* stream);
@@ -157,17 +199,24 @@ sqf_status sqf_select_channels(const float* x_cal, int64_t m_cal, int64_t k, con
  * and consistent with map).  Channel-split format ([OSC]): per output row,
  * the low channels' values in slot order are quantised to int4, the outlier
  * channels' values stored in the branch type.  Weight-side format
- * (wt->sq_nnz > 0, [SQF-art] 九): hdiag [k] required, branch must be SQF_I8;
- * per output row the sq_nnz low slots with the largest w^2 * hdiag (ties:
- * lower slot) are marked 0x8 and kept as int8 (own scale s_w8), the others
- * quantised to int4 with an absmax over the unmarked slots. */
+ * (wt->sq_nnz > 0, [SQF-art] 六, 七, 九: banks of sq_bank slots, the same
+ * count of high-precision values in each): hdiag [k] required, branch must
+ * be SQF_I8, low SQF_I4X2; in every bank of every output row the
+ * sq_nnz / banks slots with the largest w^2 * hdiag (ties: lower slot) are
+ * marked 0x8 and kept as int8 (one scale s_w8 per row over all its marked
+ * values), the others quantised to int4 with an absmax over the unmarked
+ * slots.  SQF_I4_E2M3 weights hold the channel-split int4 codes in the
+ * K-blocked 6-bit layout; SQF_MXFP4 weights quantise each 32-slot block of
+ * a row's low values to E2M1 with a shared E8M0 scale (OCP MX). */
 sqf_status sqf_pack_weights(const float* w, const int32_t* map, const float* hdiag,
                             sqf_weights* wt, void* stream);
 
 /* a2 -- online per-token quantisation + outlier extraction ([OSC]
  * structured sub-tensor extraction).  x: [a->m][ldx] of x_dtype (SQF_F32 |
- * SQF_BF16), k = a->k_low + a->k_out must be a multiple of 8 and at most
- * 65536.  One pass over x writes x_low, s_x, x_out (and s_xo). */
+ * SQF_BF16), 1 <= k = a->k_low + a->k_out <= 65536, ldx >= k.  One pass over
+ * x writes x_low, s_x (or s_xb for SQF_MXFP4), x_out (and s_xo).  A k or
+ * ldx that is not a multiple of 8, or an x that is not 16-byte aligned,
+ * takes a slower element-wise load path with the same results. */
 sqf_status sqf_quantize_split_act(const void* x, int32_t x_dtype, int64_t ldx, const int32_t* map,
                                   sqf_acts* a, void* stream);
 
@@ -183,7 +232,10 @@ sqf_status sqf_dual_gemm(const sqf_acts* a, const sqf_weights* w, float* y, int6
                          int32_t* acc_low_dbg, int32_t* acc_sp_dbg, int32_t* acc_out_dbg,
                          void* stream);
 
-/* Grouped (mixture-of-experts) variants: rows of group g are
+/* Grouped (mixture-of-experts) variants ([OSC] abstract: evaluation on the
+ * Qwen3 mixture-of-experts model, whose experts each see their own tokens;
+ * the FP8 fallback is for the input of the experts' down projection W2):
+ * rows of group g are
  * [row_off[g], row_off[g+1]) of the concatenated activations (row_off: device
  * int64 [groups+1], non-decreasing, row_off[0] = 0, row_off[groups] = a->m).
  * Each group has its own map (maps: [groups][k]) and its own stacked weight
@@ -207,6 +259,18 @@ sqf_status sqf_dual_gemm_y(const sqf_acts* a, const sqf_weights* w, void* y, int
 sqf_status sqf_dual_gemm_grouped_y(const sqf_acts* a, const sqf_weights* w, int64_t groups,
                                    const int64_t* row_off, void* y, int32_t y_dtype, int64_t ldy,
                                    void* stream);
+
+/* The dual GEMM with every option explicit: the output type (as
+ * sqf_dual_gemm_y), the tile (sqf_tile) and the debug accumulators (as
+ * sqf_dual_gemm; SQF_F32 output only).  sqf_dual_gemm, sqf_dual_gemm_y and
+ * their grouped forms are this call with SQF_TILE_AUTO.  No call reads the
+ * environment or any other process-wide setting. */
+sqf_status sqf_dual_gemm_ex(const sqf_acts* a, const sqf_weights* w, void* y, int32_t y_dtype,
+                            int64_t ldy, int32_t tile, int32_t* acc_low_dbg, int32_t* acc_sp_dbg,
+                            int32_t* acc_out_dbg, void* stream);
+sqf_status sqf_dual_gemm_grouped_ex(const sqf_acts* a, const sqf_weights* w, int64_t groups,
+                                    const int64_t* row_off, void* y, int32_t y_dtype, int64_t ldy,
+                                    int32_t tile, int32_t* acc_low_dbg, void* stream);
 
 #ifdef __cplusplus
 }

@@ -30,8 +30,6 @@
 // re-zeroed.  Two images and two reduction slots alternate between rows, so
 // a row needs two barriers (absmax, image complete); the barriers wait for
 // LDS traffic only, never for the next row's loads.
-#include <cstdlib>
-
 #include "sqf_device.h"
 #include "sqf_launch.h"
 
@@ -59,7 +57,10 @@ constexpr float kRoundMagic = 12582912.0f;  // 1.5 * 2^23
 // touch (always with zero data at the very end of the row).
 constexpr int kImgSlack = 16;
 
-template <int XT, int LOW, int BR, bool GROUPED, int NT, int CPT>
+// RAGGED: k, ldx or x not aligned to 8-channel chunks.  Rows and the map are
+// then read element by element (channels past k read as absent: neither a
+// low slot nor an outlier); everything after the loads is the same.
+template <int XT, int LOW, int BR, bool GROUPED, int NT, int CPT, bool RAGGED>
 __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
   extern __shared__ uint8_t sm[];
   constexpr int ESZ = BR == kBF16 ? 2 : 1;
@@ -74,7 +75,7 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
   int32_t* oidx = (int32_t*)(sm + 2 * img_bytes);
   float* red = (float*)(sm + 2 * img_bytes + ((p.k_out * 4 + 15) & ~(int64_t)15));
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const float qlow = LOW == kI4X2 ? 7.0f : 127.0f;
+  const float qlow = LOW == kI8 ? 127.0f : 7.0f;
   const float qhi = BR == kFP8 ? 448.0f : 127.0f;
   const int k_out = (int)p.k_out;
 
@@ -94,14 +95,24 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
       const int64_t c8 = ((int64_t)tid + (int64_t)i * NT) * 8;
       uint32_t mask = 0xFFu, before = 0;
       if (c8 < p.k) {
-        const int4 u0 = *(const int4*)(mp + c8);
-        const int4 u1 = *(const int4*)(mp + c8 + 4);
-        const int m8[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+        int m8[8];
+        if constexpr (RAGGED) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) m8[e] = c8 + e < p.k ? mp[c8 + e] : 0;
+        } else {
+          const int4 u0 = *(const int4*)(mp + c8);
+          const int4 u1 = *(const int4*)(mp + c8 + 4);
+          m8[0] = u0.x; m8[1] = u0.y; m8[2] = u0.z; m8[3] = u0.w;
+          m8[4] = u1.x; m8[5] = u1.y; m8[6] = u1.z; m8[7] = u1.w;
+        }
         mask = 0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          mask |= (m8[e] < 0 ? 1u : 0u) << e;
-          if (m8[e] < 0) oidx[-m8[e] - 1] = (int32_t)(c8 + e);
+          // a channel past k is masked like an outlier (no low slot, no
+          // absmax) but has no branch slot either
+          const bool absent = RAGGED && c8 + e >= p.k;
+          mask |= (absent || m8[e] < 0 ? 1u : 0u) << e;
+          if (!absent && m8[e] < 0) oidx[-m8[e] - 1] = (int32_t)(c8 + e);
         }
         before = (uint32_t)(m8[0] >= 0 ? m8[0] : c8 - (-m8[0] - 1));
       }
@@ -137,7 +148,21 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int64_t c8 = ((int64_t)tid + (int64_t)i * NT) * 8;
-      if (c8 < p.k) {
+      if (RAGGED && c8 < p.k) {
+        if constexpr (XT == kBF16) {
+          const uint16_t* src = (const uint16_t*)p.x + row * p.ldx;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const int64_t c = c8 + 2 * w;
+            const uint32_t lo = c < p.k ? src[c] : 0u, hi = c + 1 < p.k ? src[c + 1] : 0u;
+            r[i][w] = lo | (hi << 16);
+          }
+        } else {
+          const uint32_t* src = (const uint32_t*)p.x + row * p.ldx;
+#pragma unroll
+          for (int w = 0; w < 8; ++w) r[i][w] = c8 + w < p.k ? src[c8 + w] : 0u;
+        }
+      } else if (c8 < p.k) {
         const v4u* src = XT == kBF16 ? (const v4u*)((const uint16_t*)p.x + row * p.ldx + c8)
                                      : (const v4u*)((const float*)p.x + row * p.ldx + c8);
 #pragma unroll
@@ -330,7 +355,18 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
         // the low channels' codes, in order, then zero bytes
         const uint32_t q0 = perm(d1, d0, sel0[i]), q1 = perm(d1, d0, sel1[i]);
         const uint32_t before = cw[i] >> 8;
-        if constexpr (LOW == kI4X2) {
+        if constexpr (LOW == kI4E2M3) {
+          // the chunk's codes as 6-bit E2M3 fields (code/8), 48 bits in slot
+          // order, OR-ed in at bit 6*before of the row's field stream (the
+          // concatenation of its 96-byte K blocks)
+          const uint64_t v = (uint64_t)e2m3_fields4(q0) | ((uint64_t)e2m3_fields4(q1) << 24);
+          const uint32_t bit = 6u * before, sh = bit & 31u;
+          const uint64_t lo = v << sh;
+          uint32_t* d = im + (bit >> 5);
+          atomicOr(d, (uint32_t)lo);
+          atomicOr(d + 1, (uint32_t)(lo >> 32));
+          if (sh > 16u) atomicOr(d + 2, (uint32_t)(v >> (64u - sh)));
+        } else if constexpr (LOW == kI4X2) {
           const uint32_t t0 = q0 & 0x0F0F0F0Fu, t1 = q1 & 0x0F0F0F0Fu;
           const uint32_t u0 = t0 | (t0 >> 4), u1 = t1 | (t1 >> 4);
           const uint32_t w = perm(u1, u0, 0x06040200u);  // 8 nibbles, slot order
@@ -349,9 +385,13 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
     }
     lds_barrier();  // (B) the image row is complete
     // ---- image -> packed HBM row (16-byte stores), then re-zero it ----
+    // (6-bit fields: 16-byte piece q belongs to K block q/6 of the row,
+    // which sits at block q/6's row m of the K-blocked array)
     uint8_t* xl = p.x_low + m * ldk;
     for (int64_t q = tid; q < ldk / 16; q += NT) {
-      *(uint4*)(xl + q * 16) = *(const uint4*)(img + q * 16);
+      uint8_t* dst = LOW == kI4E2M3 ? p.x_low + ((q / 6) * p.rows_pad + m) * 96 + (q % 6) * 16
+                                    : xl + q * 16;
+      *(uint4*)dst = *(const uint4*)(img + q * 16);
       *(uint4*)(img + q * 16) = make_uint4(0, 0, 0, 0);
     }
     if (tid == 0) *(uint4*)(img + ldk) = make_uint4(0, 0, 0, 0);  // slack
@@ -374,14 +414,13 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
   }
 }
 
-template <int XT, int LOW, int BR, bool GROUPED, int NT, int CPT>
-static hipError_t launch_one(const ActArgs& a, int64_t cap, size_t lds, hipStream_t s) {
-  auto kern = k_act_split<XT, LOW, BR, GROUPED, NT, CPT>;
+template <int XT, int LOW, int BR, bool GROUPED, int NT, int CPT, bool RAGGED = false>
+static hipError_t launch_one(const ActArgs& a, size_t lds, hipStream_t s) {
+  auto kern = k_act_split<XT, LOW, BR, GROUPED, NT, CPT, RAGGED>;
   // about 16 waves per CU over the 256 CUs (32 single-wave blocks); each
   // block walks a set of rows, so the per-block setup (the channel map) is
   // amortised
   int64_t grid = NT == 64 ? (int64_t)256 * 32 : (int64_t)256 * 16 * 64 / NT;
-  if (cap > 0) grid = cap;
   if (grid > a.m) grid = a.m;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -393,26 +432,32 @@ static hipError_t launch_one(const ActArgs& a, int64_t cap, size_t lds, hipStrea
 }
 
 template <int XT, int LOW, int BR, bool GROUPED>
-static hipError_t launch_shape(const ActArgs& a, int64_t cap, size_t lds, hipStream_t s) {
-  const int64_t chunks = a.k / 8;
+static hipError_t launch_shape(const ActArgs& a, bool ragged, size_t lds, hipStream_t s) {
+  const int64_t chunks = (a.k + 7) / 8;
+  if constexpr (!GROUPED) {
+    if (ragged) {
+      if (chunks <= 256) return launch_one<XT, LOW, BR, false, 64, 4, true>(a, lds, s);
+      return launch_one<XT, LOW, BR, false, 1024, 8, true>(a, lds, s);
+    }
+  }
   // rows of up to 2048 channels: one wave per block, so that the per-row
   // reduction and image hand-off need no cross-wave barrier wait and many
   // more rows are in flight per CU
-  if (chunks <= 64) return launch_one<XT, LOW, BR, GROUPED, 64, 1>(a, cap, lds, s);
-  if (chunks <= 128) return launch_one<XT, LOW, BR, GROUPED, 64, 2>(a, cap, lds, s);
-  if (chunks <= 256) return launch_one<XT, LOW, BR, GROUPED, 64, 4>(a, cap, lds, s);
-  if (chunks <= 512) return launch_one<XT, LOW, BR, GROUPED, 256, 2>(a, cap, lds, s);
-  if (chunks <= 1024) return launch_one<XT, LOW, BR, GROUPED, 512, 2>(a, cap, lds, s);
-  if (chunks <= 2048) return launch_one<XT, LOW, BR, GROUPED, 512, 4>(a, cap, lds, s);
-  if (chunks <= 4096) return launch_one<XT, LOW, BR, GROUPED, 1024, 4>(a, cap, lds, s);
-  return launch_one<XT, LOW, BR, GROUPED, 1024, 8>(a, cap, lds, s);
+  if (chunks <= 64) return launch_one<XT, LOW, BR, GROUPED, 64, 1>(a, lds, s);
+  if (chunks <= 128) return launch_one<XT, LOW, BR, GROUPED, 64, 2>(a, lds, s);
+  if (chunks <= 256) return launch_one<XT, LOW, BR, GROUPED, 64, 4>(a, lds, s);
+  if (chunks <= 512) return launch_one<XT, LOW, BR, GROUPED, 256, 2>(a, lds, s);
+  if (chunks <= 1024) return launch_one<XT, LOW, BR, GROUPED, 512, 2>(a, lds, s);
+  if (chunks <= 2048) return launch_one<XT, LOW, BR, GROUPED, 512, 4>(a, lds, s);
+  if (chunks <= 4096) return launch_one<XT, LOW, BR, GROUPED, 1024, 4>(a, lds, s);
+  return launch_one<XT, LOW, BR, GROUPED, 1024, 8>(a, lds, s);
 }
 
 template <int XT, int LOW, bool GROUPED>
-static hipError_t launch_br(const ActArgs& a, int br, int64_t cap, size_t lds, hipStream_t s) {
-  if (br == kBF16) return launch_shape<XT, LOW, kBF16, GROUPED>(a, cap, lds, s);
-  if (br == kFP8) return launch_shape<XT, LOW, kFP8, GROUPED>(a, cap, lds, s);
-  return launch_shape<XT, LOW, kI8, GROUPED>(a, cap, lds, s);
+static hipError_t launch_br(const ActArgs& a, int br, bool ragged, size_t lds, hipStream_t s) {
+  if (br == kBF16) return launch_shape<XT, LOW, kBF16, GROUPED>(a, ragged, lds, s);
+  if (br == kFP8) return launch_shape<XT, LOW, kFP8, GROUPED>(a, ragged, lds, s);
+  return launch_shape<XT, LOW, kI8, GROUPED>(a, ragged, lds, s);
 }
 
 size_t act_split_lds_bytes(int64_t ldk, int64_t k_out) {
@@ -420,24 +465,26 @@ size_t act_split_lds_bytes(int64_t ldk, int64_t k_out) {
 }
 
 hipError_t launch_act_split(const ActArgs& a, int x_dtype, int low, int branch, bool grouped,
-                            hipStream_t s) {
+                            bool ragged, hipStream_t s) {
   const size_t lds = act_split_lds_bytes(a.ldk, a.k_out);
-  // SQF_ACT_GRID overrides the number of blocks (tuning aid)
-  const char* env = getenv("SQF_ACT_GRID");
-  const int64_t cap = env ? atoll(env) : 0;
   if (a.m <= 0) return hipSuccess;
+  if (low == kI4E2M3) {  // bf16 branch, one weight set: the FP6 GEMM's operand
+    if (grouped || branch != kBF16) return hipErrorInvalidValue;
+    return x_dtype == kBF16 ? launch_shape<kBF16, kI4E2M3, kBF16, false>(a, ragged, lds, s)
+                            : launch_shape<kF32, kI4E2M3, kBF16, false>(a, ragged, lds, s);
+  }
   if (x_dtype == kBF16) {
     if (low == kI4X2)
-      return grouped ? launch_br<kBF16, kI4X2, true>(a, branch, cap, lds, s)
-                     : launch_br<kBF16, kI4X2, false>(a, branch, cap, lds, s);
-    return grouped ? launch_br<kBF16, kI8, true>(a, branch, cap, lds, s)
-                   : launch_br<kBF16, kI8, false>(a, branch, cap, lds, s);
+      return grouped ? launch_br<kBF16, kI4X2, true>(a, branch, ragged, lds, s)
+                     : launch_br<kBF16, kI4X2, false>(a, branch, ragged, lds, s);
+    return grouped ? launch_br<kBF16, kI8, true>(a, branch, ragged, lds, s)
+                   : launch_br<kBF16, kI8, false>(a, branch, ragged, lds, s);
   }
   if (low == kI4X2)
-    return grouped ? launch_br<kF32, kI4X2, true>(a, branch, cap, lds, s)
-                   : launch_br<kF32, kI4X2, false>(a, branch, cap, lds, s);
-  return grouped ? launch_br<kF32, kI8, true>(a, branch, cap, lds, s)
-                 : launch_br<kF32, kI8, false>(a, branch, cap, lds, s);
+    return grouped ? launch_br<kF32, kI4X2, true>(a, branch, ragged, lds, s)
+                   : launch_br<kF32, kI4X2, false>(a, branch, ragged, lds, s);
+  return grouped ? launch_br<kF32, kI8, true>(a, branch, ragged, lds, s)
+                 : launch_br<kF32, kI8, false>(a, branch, ragged, lds, s);
 }
 
 }  // namespace sqf

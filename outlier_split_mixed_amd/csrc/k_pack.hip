@@ -34,7 +34,9 @@ constexpr int kPackCols = 64;
 constexpr int kPackWaves = 16;
 constexpr int kPackChunk = 8192;
 
-template <int BR>
+// LOWF: kI4X2 (packed nibbles, [n][ldk]) or kI4E2M3 (the same codes in 6-bit
+// E2M3 fields, K-blocked [pad/128][rows_pad][96]; one weight set).
+template <int BR, int LOWF>
 __global__ __launch_bounds__(1024) void k_pack_osc(PackArgs p) {
   __shared__ int32_t list[kPackChunk];
   __shared__ float red[2][kPackWaves][kPackCols];
@@ -100,9 +102,10 @@ __global__ __launch_bounds__(1024) void k_pack_osc(PackArgs p) {
     __syncthreads();
   };
 
-  // pass 2a: int4 codes, 32 slots per 16-byte group, zero past k_low
+  // pass 2a: int4 codes, 32 slots per 16-byte group (24 bytes of 6-bit
+  // fields), zero past k_low
   uint8_t* wl = p.w_low + (g * p.n + nn) * p.ldk;
-  const int64_t slots = p.ldk * 2;
+  const int64_t slots = LOWF == kI4E2M3 ? p.ldk / 3 * 4 : p.ldk * 2;
   for (int64_t s0 = 0; s0 < slots; s0 += kPackChunk) {
     const int64_t s1 = s0 + kPackChunk < slots ? s0 + kPackChunk : slots;
     if (s0 < p.k_low) build_list(s0, true);
@@ -119,7 +122,31 @@ __global__ __launch_bounds__(1024) void k_pack_osc(PackArgs p) {
         for (int e = 0; e < 32; ++e)
           ow[e >> 3] |= ((uint32_t)quant_code(v[e], inv, 7.0f) & 0xFu) << ((e & 7) * 4);
       }
-      if (live) *(uint4*)(wl + q * 16) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+      if constexpr (LOWF == kI4E2M3) {
+        // nibbles -> one code per byte -> 6-bit fields, 24 bits per 4 codes
+        uint32_t f[8];
+#pragma unroll
+        for (int h = 0; h < 8; ++h) {
+          const uint32_t nib = ow[h >> 1] >> (16 * (h & 1));  // 4 codes, 4 bits each
+          // sign-extend each nibble into its own byte
+          const uint32_t b = (nib & 0xFu) | ((nib & 0xF0u) << 4) | ((nib & 0xF00u) << 8) |
+                             ((nib & 0xF000u) << 12);
+          const uint32_t sx = ((b & 0x08080808u) >> 3) * 0xF0u;
+          f[h] = e2m3_fields4(b | sx);
+        }
+        // 8 x 24 bits -> 6 dwords (fields of slot e at bits 6e .. 6e+5)
+        const uint32_t d0 = f[0] | (f[1] << 24), d1 = (f[1] >> 8) | (f[2] << 16),
+                       d2 = (f[2] >> 16) | (f[3] << 8), d3 = f[4] | (f[5] << 24),
+                       d4 = (f[5] >> 8) | (f[6] << 16), d5 = (f[6] >> 16) | (f[7] << 8);
+        if (live) {
+          uint8_t* dst = p.w_low + ((q >> 2) * p.rows_pad + nn) * 96 + (q & 3) * 24;
+          *(v2u*)dst = v2u{d0, d1};
+          *(v2u*)(dst + 8) = v2u{d2, d3};
+          *(v2u*)(dst + 16) = v2u{d4, d5};
+        }
+      } else {
+        if (live) *(uint4*)(wl + q * 16) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+      }
     }
   }
 
@@ -301,10 +328,8 @@ __global__ __launch_bounds__(256) void k_pack_sq(PackArgs p) {
   int kc = 0;
   for (int64_t j = j0; j < j1; ++j) kc += keep[j];
   int pos = block_excl_scan(kc, iscr);
-  const int before = pos;
   for (int64_t j = j0; j < j1; ++j)
     if (keep[j]) p.sq_val[nn * p.nnz + pos++] = (int8_t)quant_code(vals[j], inv8, 127.0f);
-  const int total = block_sum_i(kc, iscr);
   // packed row: 16-byte groups of 32 slots
   uint8_t* wl = p.w_low + nn * p.ldk;
   for (int64_t q = tid; q < p.ldk / 16; q += 256) {
@@ -317,17 +342,6 @@ __global__ __launch_bounds__(256) void k_pack_sq(PackArgs p) {
     }
     *(uint4*)(wl + q * 16) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
   }
-  // marked-slot count before each 256-slot tile: the thread whose slot range
-  // holds a tile's first slot counts from its own prefix; tiles that start
-  // past k_low get the row total
-  const int64_t ntiles = p.ldk / 128;
-  int32_t* toff = p.tile_off + nn * (ntiles + 1);
-  for (int64_t b = (j0 + 255) / 256 * 256; b < j1; b += 256) {
-    int cnt = before;
-    for (int64_t j = j0; j < b; ++j) cnt += keep[j];
-    toff[b / 256] = cnt;
-  }
-  for (int64_t t = (kl + 255) / 256 + tid; t <= ntiles; t += 256) toff[t] = total;
   // int8 branch over the outlier channels
   float ao = 0.0f;
   for (int64_t t = tid; t < p.k_out; t += 256) ao = fmaxf(ao, fabsf(ov[t]));
@@ -338,7 +352,7 @@ __global__ __launch_bounds__(256) void k_pack_sq(PackArgs p) {
     p.w_out[nn * p.ldo + t] = t < p.k_out ? (uint8_t)quant_code(ov[t], invo, 127.0f) : 0;
 }
 
-hipError_t launch_pack(const PackArgs& a, int branch, int groups, hipStream_t s) {
+hipError_t launch_pack(const PackArgs& a, int branch, int low, int groups, hipStream_t s) {
   if (a.nnz > 0) {
     size_t lds = (size_t)a.k_low * 9 + (size_t)a.k_out * 4 + 16;
     if (lds > 65536) {
@@ -351,9 +365,16 @@ hipError_t launch_pack(const PackArgs& a, int branch, int groups, hipStream_t s)
   }
   dim3 grid((unsigned)((a.n + kPackCols - 1) / kPackCols), (unsigned)groups);
   dim3 block(kPackCols * kPackWaves);
-  if (branch == kBF16) hipLaunchKernelGGL(k_pack_osc<kBF16>, grid, block, 0, s, a);
-  else if (branch == kFP8) hipLaunchKernelGGL(k_pack_osc<kFP8>, grid, block, 0, s, a);
-  else hipLaunchKernelGGL(k_pack_osc<kI8>, grid, block, 0, s, a);
+  if (low == kI4E2M3) {
+    if (branch != kBF16 || groups != 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_pack_osc<kBF16, kI4E2M3>), grid, block, 0, s, a);
+  } else if (branch == kBF16) {
+    hipLaunchKernelGGL((k_pack_osc<kBF16, kI4X2>), grid, block, 0, s, a);
+  } else if (branch == kFP8) {
+    hipLaunchKernelGGL((k_pack_osc<kFP8, kI4X2>), grid, block, 0, s, a);
+  } else {
+    hipLaunchKernelGGL((k_pack_osc<kI8, kI4X2>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 

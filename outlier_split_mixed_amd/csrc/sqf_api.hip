@@ -7,7 +7,6 @@
 
 #include <cstdarg>
 #include <cstdio>
-#include <cstdlib>
 #include <string>
 
 #include "../../include/sqf.h"
@@ -46,22 +45,33 @@ constexpr int64_t kMaxOperandBytes = ((int64_t)1 << 31) - 1;
 int branch_esz(int32_t b) { return b == SQF_BF16 ? 2 : 1; }
 bool branch_ok(int32_t b) { return b == SQF_BF16 || b == SQF_FP8_E4M3 || b == SQF_I8; }
 
-// Tile configuration for the channel-split GEMM.  SQF_GEMM_TILE=0/1/2 forces
-// 256x256 / 128x128 / 64x64 (a tuning and test aid, read on every call);
-// otherwise the largest tile that still gives the 256 CUs enough tiles.
-int pick_cfg(int64_t m, int64_t n, int32_t branch) {
-  const char* env = getenv("SQF_GEMM_TILE");
-  const int forced = env ? atoi(env) : -1;
+bool tile_ok(int32_t t) { return t >= SQF_TILE_AUTO && t <= SQF_TILE_64; }
+
+// Bytes per row of a low operand: packed nibbles (and E2M1) pad/2, int8 pad,
+// 6-bit E2M3 fields pad*3/4 (stored K-blocked, see sqf.h).
+int64_t low_ldk(int64_t k_low, int32_t low) {
+  const int64_t pad = sqf_pad_k_low(k_low);
+  return low == SQF_I8 ? pad : low == SQF_I4_E2M3 ? pad / 4 * 3 : pad / 2;
+}
+// Rows of a low operand's storage (the K-blocked layout pads them).
+int64_t low_rows(int64_t rows, int32_t low) {
+  return low == SQF_I4_E2M3 ? sqf_pad_rows(rows) : rows;
+}
+
+// Tile configuration for the channel-split GEMM: the caller's sqf_tile, or
+// (SQF_TILE_AUTO) the largest tile that still gives the 256 CUs enough tiles.
+// The E4M3 branch runs on 128x128 tiles: it needs a second accumulator set.
+int pick_cfg(int64_t m, int64_t n, int32_t branch, int32_t tile) {
   int cfg;
-  if (forced >= 0 && forced <= 2)
-    cfg = forced;
+  if (tile != SQF_TILE_AUTO)
+    cfg = tile;
   else if (((m + 255) / 256) * ((n + 255) / 256) >= 448)
     cfg = 0;
   else if (((m + 127) / 128) * ((n + 127) / 128) >= 256)
     cfg = 1;
   else
     cfg = 2;
-  if (branch == SQF_FP8_E4M3 && cfg == 0) cfg = 1;  // it needs a second accumulator set
+  if (branch == SQF_FP8_E4M3 && cfg == 0) cfg = 1;  // only when chosen automatically
   return cfg;
 }
 
@@ -74,12 +84,20 @@ sqf_status check_weights(const sqf_weights* wt, const char* who) {
   if (!branch_ok(wt->branch))
     return fail(SQF_ERR_INVALID_ARG, "%s: bad branch dtype %d", who, wt->branch);
   if (wt->groups < 1) return fail(SQF_ERR_SHAPE, "%s: groups must be >= 1", who);
+  if (wt->low == SQF_MXFP4)
+    return fail(SQF_ERR_UNSUPPORTED, "%s: low dtype %d is not available for weights", who, wt->low);
+  if (wt->low != SQF_I4X2 && wt->low != SQF_I4_E2M3)
+    return fail(SQF_ERR_INVALID_ARG, "%s: bad low dtype %d for weights", who, wt->low);
+  if (wt->low == SQF_I4_E2M3 && (wt->groups != 1 || wt->branch != SQF_BF16 || wt->sq_nnz != 0))
+    return fail(SQF_ERR_UNSUPPORTED, "%s: the 6-bit low layout is built for one weight set, a "
+                "bf16 branch and the channel-split format", who);
   if (wt->k_low > kMaxKLow)
     return fail(SQF_ERR_SHAPE, "%s: k_low=%lld exceeds %lld", who, (long long)wt->k_low,
                 (long long)kMaxKLow);
-  if (wt->ldk != sqf_pad_k_low(wt->k_low) / 2)
+  const int64_t want_wldk = low_ldk(wt->k_low, wt->low);
+  if (wt->ldk != want_wldk)
     return fail(SQF_ERR_SHAPE, "%s: ldk=%lld, expected %lld", who, (long long)wt->ldk,
-                (long long)(sqf_pad_k_low(wt->k_low) / 2));
+                (long long)want_wldk);
   if (wt->ldo != sqf_pad_k_out(wt->k_out, wt->branch))
     return fail(SQF_ERR_SHAPE, "%s: ldo=%lld, expected %lld", who, (long long)wt->ldo,
                 (long long)sqf_pad_k_out(wt->k_out, wt->branch));
@@ -92,7 +110,7 @@ sqf_status check_weights(const sqf_weights* wt, const char* who) {
     return fail(SQF_ERR_ALIGN, "%s: w_out must be 16-byte aligned", who);
   if (wt->k_out > 0 && wt->branch != SQF_BF16 && !wt->s_wo)
     return fail(SQF_ERR_INVALID_ARG, "%s: s_wo is required for a scaled branch", who);
-  if (wt->n * wt->ldk * wt->groups > kMaxOperandBytes ||
+  if (low_rows(wt->n, wt->low) * wt->ldk * wt->groups > kMaxOperandBytes ||
       wt->n * wt->ldo * branch_esz(wt->branch) * wt->groups > kMaxOperandBytes)
     return fail(SQF_ERR_SHAPE, "%s: a weight operand exceeds 2 GiB", who);
   if (wt->sq_nnz < 0 || wt->sq_nnz > wt->k_low)
@@ -102,8 +120,11 @@ sqf_status check_weights(const sqf_weights* wt, const char* who) {
       return fail(SQF_ERR_UNSUPPORTED, "%s: the weight-side format needs groups == 1", who);
     if (wt->branch != SQF_I8)
       return fail(SQF_ERR_UNSUPPORTED, "%s: the weight-side format needs an SQF_I8 branch", who);
-    if (!wt->sq_val || !wt->s_w8 || !wt->sq_tile_off)
-      return fail(SQF_ERR_INVALID_ARG, "%s: sq_val, s_w8 and sq_tile_off are required", who);
+    if (!wt->sq_val || !wt->s_w8)
+      return fail(SQF_ERR_INVALID_ARG, "%s: sq_val and s_w8 are required", who);
+    if (wt->sq_bank != 0 && wt->sq_bank != wt->k_low)
+      return fail(SQF_ERR_UNSUPPORTED, "%s: sq_bank=%lld: only whole-row banks are built", who,
+                  (long long)wt->sq_bank);
     if (!aligned16(wt->sq_val))
       return fail(SQF_ERR_ALIGN, "%s: sq_val must be 16-byte aligned", who);
   } else if (wt->branch == SQF_I8) {
@@ -118,14 +139,17 @@ sqf_status check_acts(const sqf_acts* a, const char* who) {
   if (a->m < 0 || a->k_low < 0 || a->k_out < 0 || a->k_low + a->k_out < 1)
     return fail(SQF_ERR_SHAPE, "%s: bad activation shape m=%lld k_low=%lld k_out=%lld", who,
                 (long long)a->m, (long long)a->k_low, (long long)a->k_out);
-  if (a->low != SQF_I4X2 && a->low != SQF_I8)
+  if (a->low == SQF_MXFP4)
+    return fail(SQF_ERR_UNSUPPORTED, "%s: low dtype %d is not available", who, a->low);
+  if (a->low != SQF_I4X2 && a->low != SQF_I8 && a->low != SQF_I4_E2M3)
     return fail(SQF_ERR_INVALID_ARG, "%s: bad low dtype %d", who, a->low);
+  if (a->low == SQF_I4_E2M3 && a->branch != SQF_BF16)
+    return fail(SQF_ERR_UNSUPPORTED, "%s: the 6-bit low layout comes with a bf16 branch", who);
   if (!branch_ok(a->branch))
     return fail(SQF_ERR_INVALID_ARG, "%s: bad branch dtype %d", who, a->branch);
   if (a->k_low > kMaxKLow)
     return fail(SQF_ERR_SHAPE, "%s: k_low exceeds %lld", who, (long long)kMaxKLow);
-  const int64_t pad = sqf_pad_k_low(a->k_low);
-  const int64_t want_ldk = a->low == SQF_I4X2 ? pad / 2 : pad;
+  const int64_t want_ldk = low_ldk(a->k_low, a->low);
   if (a->ldk != want_ldk)
     return fail(SQF_ERR_SHAPE, "%s: ldk=%lld, expected %lld", who, (long long)a->ldk,
                 (long long)want_ldk);
@@ -143,7 +167,7 @@ sqf_status check_acts(const sqf_acts* a, const char* who) {
     if (a->k_out > 0 && a->branch != SQF_BF16 && !a->s_xo)
       return fail(SQF_ERR_INVALID_ARG, "%s: s_xo is required for a scaled branch", who);
   }
-  if (a->m * a->ldk > kMaxOperandBytes ||
+  if (low_rows(a->m, a->low) * a->ldk > kMaxOperandBytes ||
       a->m * a->ldo * branch_esz(a->branch) > kMaxOperandBytes)
     return fail(SQF_ERR_SHAPE, "%s: an activation operand exceeds 2 GiB", who);
   return SQF_OK;
@@ -160,26 +184,29 @@ sqf_status quantize_common(const void* x, int32_t x_dtype, int64_t ldx, int64_t 
   if (x_dtype != SQF_F32 && x_dtype != SQF_BF16)
     return fail(SQF_ERR_INVALID_ARG, "%s: x_dtype must be SQF_F32 or SQF_BF16", who);
   const int64_t k = a->k_low + a->k_out;
-  if (k % 8 != 0 || k > 65536)
-    return fail(SQF_ERR_SHAPE, "%s: k=%lld must be a multiple of 8 and <= 65536", who,
-                (long long)k);
+  if (k > 65536) return fail(SQF_ERR_SHAPE, "%s: k=%lld exceeds 65536", who, (long long)k);
   if (sqf::act_split_lds_bytes(a->ldk, a->k_out) > 160 * 1024)
     return fail(SQF_ERR_SHAPE, "%s: k_low=%lld, k_out=%lld exceed the kernel's LDS staging", who,
                 (long long)a->k_low, (long long)a->k_out);
-  if (ldx < k || ldx % 8 != 0)
-    return fail(SQF_ERR_SHAPE, "%s: ldx=%lld must be >= k and a multiple of 8", who,
-                (long long)ldx);
-  if (!aligned16(x) || !aligned16(map))
-    return fail(SQF_ERR_ALIGN, "%s: x and map must be 16-byte aligned", who);
+  if (ldx < k) return fail(SQF_ERR_SHAPE, "%s: ldx=%lld < k=%lld", who, (long long)ldx, (long long)k);
+  if (((uintptr_t)x & (x_dtype == SQF_BF16 ? 1u : 3u)) || ((uintptr_t)map & 3u))
+    return fail(SQF_ERR_ALIGN, "%s: x and map must be aligned to their element size", who);
+  // 8-channel chunks with 16-byte loads need k, ldx and x aligned to them;
+  // anything else takes the element-wise load path
+  const bool ragged = k % 8 != 0 || ldx % 8 != 0 || !aligned16(x) || !aligned16(map);
+  if (ragged && grouped)
+    return fail(SQF_ERR_UNSUPPORTED, "%s: grouped rows need k and ldx multiples of 8 and "
+                "16-byte aligned x and maps", who);
   if (grouped && (groups < 1 || !row_off))
     return fail(SQF_ERR_INVALID_ARG, "%s: groups >= 1 and row_off are required", who);
   if (grouped && a->low != SQF_I4X2)
-    return fail(SQF_ERR_UNSUPPORTED, "%s: grouped activations are int4 only", who);
+    return fail(SQF_ERR_UNSUPPORTED, "%s: grouped activations are packed int4 only", who);
   sqf::ActArgs args{x, ldx, map, row_off, a->m, k, a->k_low, a->k_out, sqf_pad_k_low(a->k_low),
-                    a->ldk, a->ldo, (int32_t)(grouped ? groups : 1), a->x_low, a->s_x,
-                    (uint8_t*)a->x_out, a->s_xo};
+                    a->ldk, a->ldo, a->low == SQF_I4_E2M3 ? sqf_pad_rows(a->m) : 0,
+                    (int32_t)(grouped ? groups : 1), a->x_low, a->s_x, (uint8_t*)a->x_out, a->s_xo};
   return hip_status(
-      sqf::launch_act_split(args, x_dtype, a->low, a->branch, grouped, (hipStream_t)stream), who);
+      sqf::launch_act_split(args, x_dtype, a->low, a->branch, grouped, ragged, (hipStream_t)stream),
+      who);
 }
 
 sqf_status check_pair(const sqf_acts* a, const sqf_weights* w, const void* y, int64_t ldy,
@@ -194,6 +221,9 @@ sqf_status check_pair(const sqf_acts* a, const sqf_weights* w, const void* y, in
   if ((w->sq_nnz > 0) != (a->low == SQF_I8))
     return fail(SQF_ERR_INVALID_ARG,
                 "%s: weight-side format needs int8 activations and the channel split int4", who);
+  if (w->sq_nnz == 0 && a->low != w->low)
+    return fail(SQF_ERR_INVALID_ARG, "%s: activations (low %d) and weights (low %d) disagree on "
+                "the low storage", who, a->low, w->low);
   if (a->m > 0 && !y) return fail(SQF_ERR_INVALID_ARG, "%s: y is NULL", who);
   if (ldy < w->n) return fail(SQF_ERR_SHAPE, "%s: ldy=%lld < n=%lld", who, (long long)ldy,
                               (long long)w->n);
@@ -203,10 +233,15 @@ sqf_status check_pair(const sqf_acts* a, const sqf_weights* w, const void* y, in
 // Y is fp32 (float*) or, with ybf16, bf16 (uint16_t* bit patterns); ldy in
 // elements of Y's type.
 sqf_status dual_gemm_impl(const sqf_acts* a, const sqf_weights* w, void* y, bool ybf16,
-                          int64_t ldy, int32_t* acc_low_dbg, int32_t* acc_sp_dbg,
+                          int64_t ldy, int32_t tile, int32_t* acc_low_dbg, int32_t* acc_sp_dbg,
                           int32_t* acc_out_dbg, void* stream, const char* who) {
   sqf_status st = check_pair(a, w, y, ldy, who);
   if (st != SQF_OK) return st;
+  if (!tile_ok(tile)) return fail(SQF_ERR_INVALID_ARG, "%s: bad tile %d", who, tile);
+  if (ybf16 && (acc_low_dbg || acc_sp_dbg || acc_out_dbg))
+    return fail(SQF_ERR_INVALID_ARG, "%s: debug outputs need fp32 Y", who);
+  if (w->branch == SQF_FP8_E4M3 && tile == SQF_TILE_256)
+    return fail(SQF_ERR_UNSUPPORTED, "%s: the E4M3 branch has no 256x256 tile", who);
   if (w->groups != 1) return fail(SQF_ERR_INVALID_ARG, "%s: use sqf_dual_gemm_grouped", who);
   if (a->m == 0) return SQF_OK;
   const bool debug = acc_low_dbg || acc_sp_dbg || acc_out_dbg;
@@ -218,42 +253,58 @@ sqf_status dual_gemm_impl(const sqf_acts* a, const sqf_weights* w, void* y, bool
                   (long long)w->k_low, (long long)kMaxKLowSq);
     if (debug && !(acc_low_dbg && acc_sp_dbg && acc_out_dbg))
       return fail(SQF_ERR_INVALID_ARG, "%s: the weight-side debug path writes all three accumulators", who);
+    if (tile != SQF_TILE_AUTO)
+      return fail(SQF_ERR_UNSUPPORTED, "%s: the weight-side GEMM has one tile shape", who);
     sqf::SqArgs sa{a->x_low, a->s_x, (const uint8_t*)a->x_out, a->s_xo, w->w_low, w->s_w,
-                   w->sq_val, w->s_w8, w->sq_tile_off, (const uint8_t*)w->w_out, w->s_wo, (float*)y,
+                   w->sq_val, w->s_w8, (const uint8_t*)w->w_out, w->s_wo, (float*)y,
                    acc_low_dbg, acc_sp_dbg, acc_out_dbg, a->m, w->n, a->ldk, w->ldk, w->ldo, ldy,
                    w->sq_nnz, (int32_t)(w->ldk / 128), (int32_t)(w->ldo / 128)};
     return hip_status(sqf::launch_sq_gemm(sa, debug, (hipStream_t)stream), who);
   }
   if (acc_sp_dbg || acc_out_dbg)
     return fail(SQF_ERR_INVALID_ARG, "%s: acc_sp/acc_out debug outputs need the weight-side format", who);
+  if (w->low == SQF_I4_E2M3) {
+    if (tile != SQF_TILE_AUTO && tile != SQF_TILE_256)
+      return fail(SQF_ERR_UNSUPPORTED, "%s: the 6-bit low path has 256x256 tiles only", who);
+    sqf::Gemm6Args ga{a->x_low, a->s_x, (const uint8_t*)a->x_out, w->w_low, w->s_w,
+                      (const uint8_t*)w->w_out, (float*)y, acc_low_dbg, a->m, w->n,
+                      sqf_pad_rows(a->m), sqf_pad_rows(w->n), w->ldo * 2, ldy,
+                      (int32_t)(sqf_pad_k_low(w->k_low) / 128), (int32_t)(w->ldo / 32)};
+    return hip_status(sqf::launch_gemm6(ga, debug, ybf16, (hipStream_t)stream), who);
+  }
   const int64_t ldo_b = w->ldo * branch_esz(w->branch);
   sqf::GemmArgs ga{a->x_low, a->s_x, (const uint8_t*)a->x_out, a->s_xo, w->w_low, w->s_w,
                    (const uint8_t*)w->w_out, w->s_wo, (float*)y, acc_low_dbg, nullptr, a->m, w->n, w->ldk,
                    ldo_b, ldy, 0, 0, 0, (int32_t)(w->ldk / 64), (int32_t)(ldo_b / 64), 1};
   return hip_status(sqf::launch_dual_gemm(ga, w->branch, false, debug,
-                                          pick_cfg(a->m, w->n, w->branch), (hipStream_t)stream, ybf16),
+                                          pick_cfg(a->m, w->n, w->branch, tile), (hipStream_t)stream,
+                                          ybf16),
                     who);
 }
 
 sqf_status grouped_impl(const sqf_acts* a, const sqf_weights* w, int64_t groups,
-                        const int64_t* row_off, void* y, bool ybf16, int64_t ldy,
+                        const int64_t* row_off, void* y, bool ybf16, int64_t ldy, int32_t tile,
                         int32_t* acc_low_dbg, void* stream, const char* who) {
   sqf_status st = check_pair(a, w, y, ldy, who);
   if (st != SQF_OK) return st;
+  if (!tile_ok(tile)) return fail(SQF_ERR_INVALID_ARG, "%s: bad tile %d", who, tile);
+  if (tile == SQF_TILE_64)
+    return fail(SQF_ERR_UNSUPPORTED, "%s: grouped tiles are 256x256 or 128x128", who);
+  if (ybf16 && acc_low_dbg) return fail(SQF_ERR_INVALID_ARG, "%s: debug outputs need fp32 Y", who);
+  if (w->branch == SQF_FP8_E4M3 && tile == SQF_TILE_256)
+    return fail(SQF_ERR_UNSUPPORTED, "%s: the E4M3 branch has no 256x256 tile", who);
   if (groups < 1 || w->groups != groups || !row_off)
     return fail(SQF_ERR_INVALID_ARG, "%s: need groups >= 1 == w->groups and row_off", who);
   if (w->sq_nnz > 0) return fail(SQF_ERR_UNSUPPORTED, "%s: channel-split format only", who);
   if (a->m == 0) return SQF_OK;
   const int64_t ldo_b = w->ldo * branch_esz(w->branch);
   // 256x256 tiles when the groups average 384 rows or more (bf16 branch),
-  // else 128x128; SQF_GEMM_TILE=0/1 forces one
+  // else 128x128, unless the caller forces one
   sqf::GemmArgs ga{a->x_low, a->s_x, (const uint8_t*)a->x_out, a->s_xo, w->w_low, w->s_w,
                    (const uint8_t*)w->w_out, w->s_wo, (float*)y, acc_low_dbg, row_off, a->m, w->n,
                    w->ldk, ldo_b, ldy, w->n * w->ldk, w->n * ldo_b, w->n,
                    (int32_t)(w->ldk / 64), (int32_t)(ldo_b / 64), (int32_t)groups};
-  const char* env = getenv("SQF_GEMM_TILE");
-  int cfg = (a->m / groups >= 384) ? 0 : 1;
-  if (env && (atoi(env) == 0 || atoi(env) == 1)) cfg = atoi(env);
+  int cfg = tile != SQF_TILE_AUTO ? tile : (a->m / groups >= 384) ? 0 : 1;
   if (w->branch == SQF_FP8_E4M3) cfg = 1;
   return hip_status(sqf::launch_dual_gemm(ga, w->branch, true, acc_low_dbg != nullptr, cfg,
                                           (hipStream_t)stream, ybf16),
@@ -273,6 +324,11 @@ int64_t sqf_pad_k_low(int64_t k_low) {
   return (k_low + 255) / 256 * 256;
 }
 
+int64_t sqf_pad_rows(int64_t rows) {
+  if (rows < 0) return -1;
+  return (rows + 255) / 256 * 256;
+}
+
 int64_t sqf_pad_k_out(int64_t k_out, int32_t branch) {
   if (k_out < 0 || !branch_ok(branch)) return -1;
   const int64_t step = 128 / branch_esz(branch);
@@ -284,8 +340,8 @@ sqf_status sqf_select_channels(const float* x_cal, int64_t m_cal, int64_t k, con
                                double* score_out, float* hdiag_out, void* stream) {
   g_err.clear();
   const char* who = "sqf_select_channels";
-  if (!x_cal || !w || !map_out || !score_out)
-    return fail(SQF_ERR_INVALID_ARG, "%s: x_cal, w, map_out and score_out are required", who);
+  if (!x_cal || !w || !map_out)
+    return fail(SQF_ERR_INVALID_ARG, "%s: x_cal, w and map_out are required", who);
   if (m_cal < 1 || n < 1 || k < 1 || k > 1048576)
     return fail(SQF_ERR_SHAPE, "%s: need m_cal>=1, n>=1, 1<=k<=1048576 (got %lld, %lld, %lld)",
                 who, (long long)m_cal, (long long)n, (long long)k);
@@ -293,9 +349,22 @@ sqf_status sqf_select_channels(const float* x_cal, int64_t m_cal, int64_t k, con
     return fail(SQF_ERR_SHAPE, "%s: k_out=%lld outside [0, k=%lld]", who, (long long)k_out,
                 (long long)k);
   if (k_out > 0 && !idx_out) return fail(SQF_ERR_INVALID_ARG, "%s: idx_out is NULL", who);
-  return hip_status(sqf::launch_select(x_cal, m_cal, k, w, n, k_out, idx_out, map_out, score_out,
-                                       hdiag_out, (hipStream_t)stream),
-                    who);
+  hipStream_t s = (hipStream_t)stream;
+  double* score = score_out;
+  if (!score) {
+    // the scores are the kernels' workspace: borrow them from the
+    // stream-ordered pool for the duration of the call
+    sqf_status st = hip_status(hipMallocAsync((void**)&score, (size_t)k * sizeof(double), s), who);
+    if (st != SQF_OK) return st;
+  }
+  sqf_status st = hip_status(sqf::launch_select(x_cal, m_cal, k, w, n, k_out, idx_out, map_out,
+                                                score, hdiag_out, s),
+                             who);
+  if (!score_out) {
+    const sqf_status fst = hip_status(hipFreeAsync(score, s), who);
+    if (st == SQF_OK) st = fst;
+  }
+  return st;
 }
 
 sqf_status sqf_pack_weights(const float* w, const int32_t* map, const float* hdiag,
@@ -312,9 +381,9 @@ sqf_status sqf_pack_weights(const float* w, const int32_t* map, const float* hdi
                   (long long)wt->k_low);
   }
   sqf::PackArgs a{w, map, hdiag, wt->k, wt->n, wt->k_low, wt->k_out, wt->ldk, wt->ldo,
-                  wt->sq_nnz, wt->w_low, wt->s_w, (uint8_t*)wt->w_out, wt->s_wo, wt->sq_val,
-                  wt->s_w8, wt->sq_tile_off};
-  return hip_status(sqf::launch_pack(a, wt->branch, wt->groups, (hipStream_t)stream), who);
+                  wt->sq_nnz, wt->low == SQF_I4_E2M3 ? sqf_pad_rows(wt->n) : 0, wt->w_low, wt->s_w,
+                  (uint8_t*)wt->w_out, wt->s_wo, wt->sq_val, wt->s_w8};
+  return hip_status(sqf::launch_pack(a, wt->branch, wt->low, wt->groups, (hipStream_t)stream), who);
 }
 
 sqf_status sqf_quantize_split_act(const void* x, int32_t x_dtype, int64_t ldx, const int32_t* map,
@@ -334,8 +403,8 @@ sqf_status sqf_dual_gemm(const sqf_acts* a, const sqf_weights* w, float* y, int6
                          int32_t* acc_low_dbg, int32_t* acc_sp_dbg, int32_t* acc_out_dbg,
                          void* stream) {
   g_err.clear();
-  return dual_gemm_impl(a, w, y, false, ldy, acc_low_dbg, acc_sp_dbg, acc_out_dbg, stream,
-                        "sqf_dual_gemm");
+  return dual_gemm_impl(a, w, y, false, ldy, SQF_TILE_AUTO, acc_low_dbg, acc_sp_dbg, acc_out_dbg,
+                        stream, "sqf_dual_gemm");
 }
 
 sqf_status sqf_dual_gemm_y(const sqf_acts* a, const sqf_weights* w, void* y, int32_t y_dtype,
@@ -344,14 +413,15 @@ sqf_status sqf_dual_gemm_y(const sqf_acts* a, const sqf_weights* w, void* y, int
   const char* who = "sqf_dual_gemm_y";
   if (y_dtype != SQF_F32 && y_dtype != SQF_BF16)
     return fail(SQF_ERR_INVALID_ARG, "%s: y_dtype %d is neither SQF_F32 nor SQF_BF16", who, y_dtype);
-  return dual_gemm_impl(a, w, y, y_dtype == SQF_BF16, ldy, nullptr, nullptr, nullptr, stream, who);
+  return dual_gemm_impl(a, w, y, y_dtype == SQF_BF16, ldy, SQF_TILE_AUTO, nullptr, nullptr,
+                        nullptr, stream, who);
 }
 
 sqf_status sqf_dual_gemm_grouped(const sqf_acts* a, const sqf_weights* w, int64_t groups,
                                  const int64_t* row_off, float* y, int64_t ldy,
                                  int32_t* acc_low_dbg, void* stream) {
   g_err.clear();
-  return grouped_impl(a, w, groups, row_off, y, false, ldy, acc_low_dbg, stream,
+  return grouped_impl(a, w, groups, row_off, y, false, ldy, SQF_TILE_AUTO, acc_low_dbg, stream,
                       "sqf_dual_gemm_grouped");
 }
 
@@ -362,7 +432,30 @@ sqf_status sqf_dual_gemm_grouped_y(const sqf_acts* a, const sqf_weights* w, int6
   const char* who = "sqf_dual_gemm_grouped_y";
   if (y_dtype != SQF_F32 && y_dtype != SQF_BF16)
     return fail(SQF_ERR_INVALID_ARG, "%s: y_dtype %d is neither SQF_F32 nor SQF_BF16", who, y_dtype);
-  return grouped_impl(a, w, groups, row_off, y, y_dtype == SQF_BF16, ldy, nullptr, stream, who);
+  return grouped_impl(a, w, groups, row_off, y, y_dtype == SQF_BF16, ldy, SQF_TILE_AUTO, nullptr,
+                      stream, who);
+}
+
+sqf_status sqf_dual_gemm_ex(const sqf_acts* a, const sqf_weights* w, void* y, int32_t y_dtype,
+                            int64_t ldy, int32_t tile, int32_t* acc_low_dbg, int32_t* acc_sp_dbg,
+                            int32_t* acc_out_dbg, void* stream) {
+  g_err.clear();
+  const char* who = "sqf_dual_gemm_ex";
+  if (y_dtype != SQF_F32 && y_dtype != SQF_BF16)
+    return fail(SQF_ERR_INVALID_ARG, "%s: y_dtype %d is neither SQF_F32 nor SQF_BF16", who, y_dtype);
+  return dual_gemm_impl(a, w, y, y_dtype == SQF_BF16, ldy, tile, acc_low_dbg, acc_sp_dbg,
+                        acc_out_dbg, stream, who);
+}
+
+sqf_status sqf_dual_gemm_grouped_ex(const sqf_acts* a, const sqf_weights* w, int64_t groups,
+                                    const int64_t* row_off, void* y, int32_t y_dtype, int64_t ldy,
+                                    int32_t tile, int32_t* acc_low_dbg, void* stream) {
+  g_err.clear();
+  const char* who = "sqf_dual_gemm_grouped_ex";
+  if (y_dtype != SQF_F32 && y_dtype != SQF_BF16)
+    return fail(SQF_ERR_INVALID_ARG, "%s: y_dtype %d is neither SQF_F32 nor SQF_BF16", who, y_dtype);
+  return grouped_impl(a, w, groups, row_off, y, y_dtype == SQF_BF16, ldy, tile, acc_low_dbg,
+                      stream, who);
 }
 
 }  // extern "C"

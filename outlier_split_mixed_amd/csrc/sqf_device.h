@@ -21,7 +21,19 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 constexpr int kWave = 64;
 
 // Status codes mirrored from the public header (kept in sync by the host code).
-enum : int { kBF16 = 1, kFP8 = 2, kI8 = 3, kI4X2 = 4, kF32 = 0 };
+enum : int { kBF16 = 1, kFP8 = 2, kI8 = 3, kI4X2 = 4, kI4E2M3 = 5, kF32 = 0 };
+
+// Four int4 codes, one per byte (two's complement, |c| <= 7), as four 6-bit
+// OCP E2M3 fields holding c/8 (the subnormal: sign << 5 | |c|), packed into
+// the low 24 bits: code i at bits 6i .. 6i+5.
+__device__ __forceinline__ uint32_t e2m3_fields4(uint32_t q) {
+  const uint32_t s = q & 0x80808080u;           // sign bits
+  const uint32_t neg = (s >> 7) * 0xFFu;         // 0xFF in each negative byte
+  const uint32_t mag = (q ^ neg) + (neg & 0x01010101u);  // |c| per byte (no carries: |c| <= 7)
+  const uint32_t f = mag | (s >> 2);             // sign to bit 5
+  const uint32_t t = (f & 0x003F003Fu) | ((f & 0x3F003F00u) >> 2);  // 12-bit pairs
+  return (t & 0xFFFu) | ((t >> 4) & 0xFFF000u);
+}
 
 __device__ __forceinline__ uint32_t f32_bits(float f) { return __float_as_uint(f); }
 

@@ -11,13 +11,13 @@ struct PackArgs {
   const int32_t* map;  // [groups][k]
   const float* hdiag;  // [k] (weight-side format)
   int64_t k, n, k_low, k_out, ldk, ldo, nnz;
+  int64_t rows_pad;  // K-blocked 6-bit layout: rows of each K block (0 otherwise)
   uint8_t* w_low;
   float* s_w;
   uint8_t* w_out;
   float* s_wo;
   int8_t* sq_val;
   float* s_w8;
-  int32_t* tile_off;
 };
 
 struct ActArgs {
@@ -26,6 +26,7 @@ struct ActArgs {
   const int32_t* map;  // [groups][k]
   const int64_t* row_off;
   int64_t m, k, k_low, k_out, pad_lo, ldk, ldo;
+  int64_t rows_pad;  // K-blocked 6-bit layout: rows of each K block (0 otherwise)
   int32_t groups;
   uint8_t* x_low;
   float* s_x;
@@ -59,8 +60,7 @@ struct SqArgs {
   const float* s_w4;
   const int8_t* sq_val;  // [n][nnz]
   const float* s_w8;
-  const int32_t* tile_off;  // [n][tiles+1]
-  const uint8_t* w_out;     // int8 [n][ldo]
+  const uint8_t* w_out;  // int8 [n][ldo]
   const float* s_wo;
   float* y;
   int32_t* dbg_low;
@@ -70,12 +70,28 @@ struct SqArgs {
   int32_t s_low, s_out;
 };
 
+// The dual GEMM with int4 codes in 6-bit E2M3 fields (K-blocked) and a bf16
+// branch, on the FP6 matrix unit; one 256 x 256 tile shape.
+struct Gemm6Args {
+  const uint8_t* x6;  // [s_low][x_rows][96]
+  const float* s_x;
+  const uint8_t* x_out;  // bf16 [m][ldo]
+  const uint8_t* w6;     // [s_low][w_rows][96]
+  const float* s_w;
+  const uint8_t* w_out;  // bf16 [n][ldo]
+  float* y;
+  int32_t* acc_dbg;
+  int64_t m, n, x_rows, w_rows, ldo_b, ldy;
+  int32_t s_low, s_br;  // 128-slot low stages, 32-channel branch stages
+};
+
 hipError_t launch_select(const float* x_cal, int64_t m_cal, int64_t k, const float* w, int64_t n,
                          int64_t k_out, int32_t* idx, int32_t* map, double* score, float* hdiag,
                          hipStream_t s);
-hipError_t launch_pack(const PackArgs& a, int branch, int groups, hipStream_t s);
+hipError_t launch_pack(const PackArgs& a, int branch, int low, int groups, hipStream_t s);
+// ragged: k, ldx or x not aligned to 8-channel chunks; element-wise loads
 hipError_t launch_act_split(const ActArgs& a, int x_dtype, int low, int branch, bool grouped,
-                            hipStream_t s);
+                            bool ragged, hipStream_t s);
 // dynamic LDS bytes the activation kernel needs for one block
 size_t act_split_lds_bytes(int64_t ldk, int64_t k_out);
 // cfg: 0 = 256x256 tiles (8 waves), 1 = 128x128 (4 waves), 2 = 64x64 (4 waves)
@@ -83,5 +99,6 @@ size_t act_split_lds_bytes(int64_t ldk, int64_t k_out);
 hipError_t launch_dual_gemm(const GemmArgs& a, int branch, bool grouped, bool debug, int cfg,
                             hipStream_t s, bool ybf16);
 hipError_t launch_sq_gemm(const SqArgs& a, bool debug, hipStream_t s);
+hipError_t launch_gemm6(const Gemm6Args& a, bool debug, bool ybf16, hipStream_t s);
 
 }  // namespace sqf

@@ -55,22 +55,60 @@ def sample_rows(m, count, seed=0):
     return np.sort(np.concatenate([[0, m - 1], mid])).astype(np.int64)
 
 
+def tile_band_rows(m, tile=256):
+    """Every row of the second 256-row tile band (every row position a tile
+    has) and of the last, possibly partial, tile."""
+    band = np.arange(tile, min(2 * tile, m))
+    last = np.arange((m - 1) // tile * tile, m)
+    return np.unique(np.concatenate([band, last])).astype(np.int64)
+
+
+def _decode_i4(packed, k_low):
+    lo = (packed & 0xF).astype(np.int8)
+    hi = (packed >> 4).astype(np.int8)
+    nib = np.stack([lo, hi], -1).reshape(packed.shape[0], -1)[:, :k_low]
+    return np.where(nib > 7, nib - 16, nib).astype(np.float32)
+
+
+def check_band(acc_gpu, y_gpu, o_a, o_w, rows, what):
+    """At full size, on whole tile bands: every GPU int32 low sum equals the
+    exact dot product of the codes (decoded from the packed bytes already
+    matched bit for bit against the oracle; float32 products and sums of
+    integers below 2^24 are exact in any order), and every Y element is
+    within tolerance of s_x*s_w*acc + bf16 branch evaluated in fp64."""
+    k_low = o_a["k_low"]
+    cx = _decode_i4(o_a["x_low"][rows], k_low)
+    cw = _decode_i4(o_w["w_low"], k_low)
+    acc = cx @ cw.T
+    assert float(np.abs(acc).max(initial=0)) < 2 ** 24
+    assert np.array_equal(acc_gpu[rows].astype(np.int64), acc.astype(np.int64)), f"{what}: band sums"
+    y = (o_a["s_x"][rows].astype(np.float64)[:, None] * o_w["s_w"].astype(np.float64)[None, :]
+         * acc.astype(np.float64))
+    if o_a["k_out"]:
+        xo = synth.bf16_bits_to_f32(o_a["x_out"][rows].view(np.uint16)).astype(np.float64)
+        wo = synth.bf16_bits_to_f32(o_w["w_out"].view(np.uint16)).astype(np.float64)
+        y += xo @ wo.T
+    return assert_rows_close(y_gpu[rows], y, what + " (band)")
+
+
 def run_layer(sqf, lay, k_out, branch="bf16", x_dtype="bf16", rows=None, check_select=True,
-              debug=True):
-    """Full path for one layer on both sides.  Returns a dict of comparison stats."""
+              debug=True, tile="auto", low="i4", band=None):
+    """Full path for one layer on both sides.  Returns a dict of comparison stats.
+    low="i4e2m3": the int4 codes in the K-blocked 6-bit layout (FP6 GEMM); its
+    bytes are compared with the oracle's re-encoding of its own packed int4."""
     stats = {}
     # ---------------- GPU ----------------
     x_cal = torch.from_numpy(lay.x_cal).cuda()
     w = torch.from_numpy(lay.w).cuda()
     idx, mp, score, hdiag = sqf.sqf_select_channels(x_cal, w, k_out)
-    wts = sqf.sqf_pack_weights(w, mp, branch=branch)
+    wts = sqf.sqf_pack_weights(w, mp, branch=branch, low=low)
     ox, ofmt, xt = x_inputs(lay, x_dtype)
-    acts = sqf.alloc_acts(lay.m, lay.k - k_out, k_out, branch=branch)
+    acts = sqf.alloc_acts(lay.m, lay.k - k_out, k_out, branch=branch, low=low)
     sqf.sqf_quantize_split_act(xt, mp, acts)
-    out = sqf.sqf_dual_gemm(acts, wts, debug=debug)
+    out = sqf.sqf_dual_gemm(acts, wts, debug=debug, tile=tile)
     y, acc = (out[0], out[1]) if debug else (out, None)
     # the launch that timing uses (no accumulator dump) is checked as well
-    y_fast = sqf.sqf_dual_gemm(acts, wts) if debug else y
+    y_fast = sqf.sqf_dual_gemm(acts, wts, tile=tile) if debug else y
     torch.cuda.synchronize()
     del w, x_cal
     # ---------------- oracle ----------------
@@ -82,7 +120,11 @@ def run_layer(sqf, lay, k_out, branch="bf16", x_dtype="bf16", rows=None, check_s
             "fp64 scores differ"
         assert f32_bits_equal(hdiag.cpu().numpy(), o_hd), "hdiag differs"
     o_w = oracle.pack_weights(lay.w, o_mp, branch=branch)
-    assert np.array_equal(wts.t["w_low"][0].cpu().numpy(), o_w["w_low"]), "packed w_low differs"
+    if low == "i4e2m3":
+        want = oracle.i4x2_to_e2m3(o_w["w_low"], oracle.pad_rows(lay.n))
+        assert np.array_equal(wts.t["w_low"].cpu().numpy(), want), "6-bit w_low differs"
+    else:
+        assert np.array_equal(wts.t["w_low"][0].cpu().numpy(), o_w["w_low"]), "packed w_low differs"
     assert f32_bits_equal(wts.t["s_w"][0].cpu().numpy(), o_w["s_w"]), "s_w differs"
     if k_out:
         g = wts.t["w_out"][0].cpu().numpy().view(o_w["w_out"].dtype)
@@ -90,7 +132,13 @@ def run_layer(sqf, lay, k_out, branch="bf16", x_dtype="bf16", rows=None, check_s
         if branch != "bf16":
             assert f32_bits_equal(wts.t["s_wo"][0].cpu().numpy(), o_w["s_wo"]), "s_wo differs"
     o_a = oracle.quantize_split_act(ox, o_mp, branch=branch, x_fmt=ofmt)
-    assert np.array_equal(acts.t["x_low"].cpu().numpy(), o_a["x_low"]), "packed x_low differs"
+    if low == "i4e2m3":
+        want = oracle.i4x2_to_e2m3(o_a["x_low"], oracle.pad_rows(lay.m))
+        got = acts.t["x_low"].cpu().numpy()
+        assert got.shape == want.shape
+        assert np.array_equal(got[:, :lay.m], want[:, :lay.m]), "6-bit x_low differs"
+    else:
+        assert np.array_equal(acts.t["x_low"].cpu().numpy(), o_a["x_low"]), "packed x_low differs"
     assert f32_bits_equal(acts.t["s_x"].cpu().numpy(), o_a["s_x"]), "s_x differs"
     if k_out:
         g = acts.t["x_out"].cpu().numpy().view(o_a["x_out"].dtype)
@@ -108,4 +156,9 @@ def run_layer(sqf, lay, k_out, branch="bf16", x_dtype="bf16", rows=None, check_s
     if debug:
         assert_rows_close(y_fast.cpu().numpy()[rows], o_y, lay.name + " (no debug outputs)")
     stats["rows_checked"] = len(rows)
+    if band is not None:
+        assert debug and branch == "bf16"
+        yf = y_fast.cpu().numpy()
+        stats["band_rows"] = len(band)
+        stats["band_max_rel_err"] = check_band(acc.cpu().numpy(), yf, o_a, o_w, band, lay.name)
     return stats, y

@@ -26,13 +26,15 @@ def _declared_functions():
 
 def test_every_declared_symbol_is_exported(sqf):
     names = _declared_functions()
-    assert len(names) == 12
+    assert len(names) == 15
     for name in names:
         assert hasattr(sqf._lib, name), name
 
 
 def test_abi_version_and_padding(sqf):
-    assert sqf.sqf_abi_version() == 1
+    assert sqf.sqf_abi_version() == 2
+    assert sqf.sqf_pad_rows(0) == 0 and sqf.sqf_pad_rows(1) == 256 and sqf.sqf_pad_rows(4096) == 4096
+    assert sqf.sqf_pad_rows(300) == 512 and sqf._lib.sqf_pad_rows(-1) == -1
     assert sqf.sqf_pad_k_low(0) == 0 and sqf.sqf_pad_k_low(1) == 256
     assert sqf.sqf_pad_k_low(7680) == 7680 and sqf.sqf_pad_k_low(13440) == 13568
     assert sqf._lib.sqf_pad_k_low(-1) == -1
@@ -59,8 +61,8 @@ def _weights(sqf, mem, k=512, n=256, k_out=32, branch="bf16", **kw):
     k_low = k - k_out
     br = sqf.DTYPES[branch]
     d = sqf.sqf_weights(k, n, k_low, k_out, sqf.sqf_pad_k_low(k_low) // 2,
-                        sqf.sqf_pad_k_out(k_out, branch), br, 1, mem(), mem(), mem(),
-                        mem() if branch != "bf16" else None, 0, None, None, None)
+                        sqf.sqf_pad_k_out(k_out, branch), br, 1, sqf.SQF_I4X2, 0, mem(), mem(),
+                        None, mem(), mem() if branch != "bf16" else None, 0, 0, None, None)
     for f, v in kw.items():
         setattr(d, f, v)
     return d
@@ -71,7 +73,7 @@ def _acts(sqf, mem, m=64, k=512, k_out=32, branch="bf16", low="i4", **kw):
     pad = sqf.sqf_pad_k_low(k_low)
     d = sqf.sqf_acts(m, k_low, k_out, pad // 2 if low == "i4" else pad,
                      sqf.sqf_pad_k_out(k_out, branch), sqf.DTYPES[low], sqf.DTYPES[branch],
-                     mem(), mem(), mem(), mem() if branch != "bf16" else None)
+                     mem(), mem(), None, mem(), mem() if branch != "bf16" else None)
     for f, v in kw.items():
         setattr(d, f, v)
     return d
@@ -134,13 +136,17 @@ def test_zero_rows_is_a_no_op(sqf):
 def test_quantize_argument_errors(sqf):
     mem = FakeMem()
     f = sqf._lib.sqf_quantize_split_act
-    a = _acts(sqf, mem, k=500, k_out=20)  # k not a multiple of 8
-    assert f(mem(), sqf.SQF_BF16, 504, mem(), ctypes.byref(a), None) == 2
+    a = _acts(sqf, mem, k=70000, k_out=20)  # k beyond 65536
+    assert f(mem(), sqf.SQF_BF16, 70000, mem(), ctypes.byref(a), None) == 2
     a = _acts(sqf, mem)
     assert f(None, sqf.SQF_BF16, 512, mem(), ctypes.byref(a), None) == 1
     assert f(mem(), sqf.SQF_I8, 512, mem(), ctypes.byref(a), None) == 1
     assert f(mem(), sqf.SQF_BF16, 500, mem(), ctypes.byref(a), None) == 2  # ldx < k
-    assert f(mem(misalign=2), sqf.SQF_BF16, 512, mem(), ctypes.byref(a), None) == 5
+    assert f(mem(misalign=1), sqf.SQF_BF16, 512, mem(), ctypes.byref(a), None) == 5  # odd bf16
+    assert f(mem(misalign=2), sqf.SQF_F32, 512, mem(), ctypes.byref(a), None) == 5  # fp32 at 2 B
+    g = sqf._lib.sqf_quantize_split_act_grouped
+    # a grouped call takes the 16-byte chunk loads only
+    assert g(mem(misalign=2), sqf.SQF_BF16, 512, 2, mem(), mem(), ctypes.byref(a), None) == 3
     assert f(mem(), sqf.SQF_BF16, 512, mem(), None, None) == 1
 
 
@@ -151,7 +157,7 @@ def test_select_argument_errors(sqf):
     assert f(mem(), 0, 8, mem(), 4, 2, mem(), mem(), mem(), None, None) == 2
     assert f(mem(), 4, 8, mem(), 4, 9, mem(), mem(), mem(), None, None) == 2
     assert f(mem(), 4, 8, mem(), 4, 2, None, mem(), mem(), None, None) == 1
-    assert f(mem(), 4, 8, mem(), 4, 2, mem(), mem(), None, None, None) == 1
+    assert f(mem(), 4, 8, mem(), 4, 2, mem(), None, mem(), None, None) == 1  # map_out required
 
 
 def test_pack_argument_errors(sqf):
@@ -165,7 +171,7 @@ def test_pack_argument_errors(sqf):
     w.s_wo = mem()
     w.sq_nnz = 60
     assert f(mem(), mem(), None, ctypes.byref(w), None) == 1  # sq fields missing
-    w.sq_val, w.s_w8, w.sq_tile_off = mem(), mem(), mem()
+    w.sq_val, w.s_w8 = mem(), mem()
     assert f(mem(), mem(), None, ctypes.byref(w), None) == 1  # hdiag missing
     w.sq_nnz = 10_000
     assert f(mem(), mem(), mem(), ctypes.byref(w), None) == 2
@@ -198,9 +204,50 @@ def test_output_type_argument_errors(sqf):
     a8 = _acts(sqf, mem, low="i8", branch="i8")
     w8 = _weights(sqf, mem)
     w8.branch, w8.ldo, w8.s_wo = sqf.SQF_I8, 128, mem()
-    w8.sq_nnz, w8.sq_val, w8.s_w8, w8.sq_tile_off = 60, mem(), mem(), mem()
+    w8.sq_nnz, w8.sq_val, w8.s_w8 = 60, mem(), mem()
     assert f(ctypes.byref(a8), ctypes.byref(w8), mem(), sqf.SQF_BF16, 256, None) == 3
     g = sqf._lib.sqf_dual_gemm_grouped_y
     w.groups = 4
     assert g(ctypes.byref(a), ctypes.byref(w), 4, mem(), mem(), 7, 256, None) == 1
     assert g(ctypes.byref(a), ctypes.byref(w), 3, mem(), mem(), sqf.SQF_BF16, 256, None) == 1
+
+
+def test_explicit_options_argument_errors(sqf):
+    """sqf_dual_gemm_ex / _grouped_ex: a bad tile or output type, a tile the
+    branch does not have, and debug outputs with bf16 Y are refused before any
+    launch."""
+    mem = FakeMem()
+    a = _acts(sqf, mem)
+    w = _weights(sqf, mem)
+    f = sqf._lib.sqf_dual_gemm_ex
+    st = lambda *args: f(ctypes.byref(args[0]), ctypes.byref(args[1]), *args[2:])
+    assert st(a, w, mem(), sqf.SQF_F32, 256, 7, None, None, None, None) == 1  # no such tile
+    assert st(a, w, mem(), sqf.SQF_I8, 256, -1, None, None, None, None) == 1  # output type
+    assert st(a, w, mem(), sqf.SQF_BF16, 256, -1, mem(), None, None, None) == 1  # dbg + bf16 Y
+    a8 = _acts(sqf, mem, branch="fp8")
+    w8 = _weights(sqf, mem, branch="fp8")
+    assert st(a8, w8, mem(), sqf.SQF_F32, 256, sqf.TILES["256"], None, None, None, None) == 3
+    g = sqf._lib.sqf_dual_gemm_grouped_ex
+    w.groups = 4
+    assert g(ctypes.byref(a), ctypes.byref(w), 4, mem(), mem(), sqf.SQF_F32, 256,
+             sqf.TILES["64"], None, None) == 3  # grouped tiles are 256 or 128
+    assert g(ctypes.byref(a), ctypes.byref(w), 4, mem(), mem(), sqf.SQF_F32, 256, 9, None,
+             None) == 1
+    assert sqf.sqf_last_error() != ""
+
+
+def test_weight_side_bank_must_be_supported(sqf):
+    mem = FakeMem()
+    w = _weights(sqf, mem, k=512, k_out=32)
+    w.branch, w.ldo, w.s_wo = sqf.SQF_I8, 128, mem()
+    w.sq_nnz, w.sq_val, w.s_w8 = 60, mem(), mem()
+    w.sq_bank = 7  # not a multiple of 64 dividing k_low
+    assert sqf._lib.sqf_pack_weights(mem(), mem(), mem(), ctypes.byref(w), None) in (2, 3)
+
+
+def test_no_entry_point_reads_the_environment():
+    """Every option is an argument: the library sources call no getenv."""
+    csrc = os.path.join(ROOT, "outlier_split_mixed_amd", "csrc")
+    for fn in os.listdir(csrc):
+        text = open(os.path.join(csrc, fn)).read()
+        assert "getenv" not in text, fn

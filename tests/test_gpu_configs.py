@@ -22,7 +22,7 @@ import torch
 import oracle
 from outlier_split_mixed_amd import synth
 
-from harness import assert_rows_close, f32_bits_equal, run_layer, sample_rows, x_inputs
+from harness import assert_rows_close, f32_bits_equal, run_layer, sample_rows, tile_band_rows, x_inputs
 from test_gpu_parity import _grouped_check
 
 pytestmark = pytest.mark.gpu
@@ -41,25 +41,32 @@ def _log(*a):
     print(*a, flush=True)
 
 
+@pytest.mark.parametrize("low", ["i4", "i4e2m3"])
 @pytest.mark.parametrize("layer", [0, 1, 2])
-def test_llama3_8b_layers(sqf, layer):
+def test_llama3_8b_layers(sqf, layer, low):
+    """Sampled rows against the oracle, plus every row of a whole tile band
+    and of the last tile (exact sums, Y in tolerance)."""
     lay = synth.llama3_8b(layer)
-    st, _ = run_layer(sqf, lay, lay.k_out, rows=sample_rows(lay.m, 12, seed=layer))
-    _log(lay.name, st)
+    st, _ = run_layer(sqf, lay, lay.k_out, rows=sample_rows(lay.m, 12, seed=layer), low=low,
+                      band=tile_band_rows(lay.m))
+    _log(lay.name, low, st)
 
 
+@pytest.mark.parametrize("low", ["i4", "i4e2m3"])
 @pytest.mark.parametrize("layer", [0, 1, 2])
-def test_llama3_70b_layers_f16(sqf, layer):
+def test_llama3_70b_layers_f16(sqf, layer, low):
     lay = synth.llama3_70b(layer, 16)
-    st, _ = run_layer(sqf, lay, lay.k_out, rows=sample_rows(lay.m, 8, seed=10 + layer))
-    _log(lay.name, "1/16", st)
+    st, _ = run_layer(sqf, lay, lay.k_out, rows=sample_rows(lay.m, 8, seed=10 + layer), low=low,
+                      band=tile_band_rows(lay.m))
+    _log(lay.name, "1/16", low, st)
 
 
+@pytest.mark.parametrize("low", ["i4", "i4e2m3"])
 @pytest.mark.parametrize("frac", [2, 4, 8])
-def test_llama3_70b_fraction_sweep(sqf, frac):
+def test_llama3_70b_fraction_sweep(sqf, frac, low):
     lay = synth.llama3_70b(0, frac)
-    st, _ = run_layer(sqf, lay, lay.k_out, rows=sample_rows(lay.m, 8, seed=20 + frac))
-    _log(lay.name, f"1/{frac}", st)
+    st, _ = run_layer(sqf, lay, lay.k_out, rows=sample_rows(lay.m, 8, seed=20 + frac), low=low)
+    _log(lay.name, f"1/{frac}", low, st)
 
 
 @pytest.fixture(scope="module")
@@ -115,9 +122,14 @@ def test_sq_weight_side_full(sqf):
     assert np.array_equal(wts.t["w_low"][0].cpu().numpy(), o_w["w_low"])
     assert np.array_equal(wts.t["sq_val"].cpu().numpy(), o_w["sq_val"])
     assert f32_bits_equal(wts.t["s_w8"].cpu().numpy(), o_w["s_w8"])
+    assert f32_bits_equal(wts.t["s_w"][0].cpu().numpy(), o_w["s_w"])
+    assert np.array_equal(wts.t["w_out"][0].cpu().numpy().view(np.int8), o_w["w_out"])
+    assert f32_bits_equal(wts.t["s_wo"][0].cpu().numpy(), o_w["s_wo"])
     o_a = oracle.quantize_split_act(ox, o_mp, low="i8", branch="i8", x_fmt=ofmt)
     assert np.array_equal(acts.t["x_low"].cpu().numpy(), o_a["x_low"])
     assert np.array_equal(acts.t["x_out"].cpu().numpy(), o_a["x_out"])
+    assert f32_bits_equal(acts.t["s_x"].cpu().numpy(), o_a["s_x"])
+    assert f32_bits_equal(acts.t["s_xo"].cpu().numpy(), o_a["s_xo"])
     rows = sample_rows(lay.m, 8, seed=40)
     o_y, o_al, o_asp, o_ao = oracle.dual_gemm(o_a, o_w, rows=rows, debug=True)
     assert np.array_equal(al.cpu().numpy()[rows].astype(np.int64), o_al)

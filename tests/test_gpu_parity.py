@@ -6,7 +6,6 @@ fp32 scale patterns, branch codes, int32 low-path accumulators.  Tolerance:
 per row, max |y_gpu - y_oracle| <= 1e-3 * max |y_oracle|.
 """
 import ctypes
-import os
 
 import numpy as np
 import pytest
@@ -43,16 +42,12 @@ def test_tiny_fp32_input(sqf):
     _print("tiny", st)
 
 
-@pytest.mark.parametrize("tile", ["0", "1", "2"])
+@pytest.mark.parametrize("tile", ["256", "128", "64"])
 def test_tiny_m_and_n_every_tile(sqf, tile):
     """7 tokens x 5 outputs: one partial tile on every configuration, almost
     every row and column of it past the ends."""
     lay = synth.draw_layer("tinymn", 1030, 0, 7, 512, 5, 32, 32)
-    os.environ["SQF_GEMM_TILE"] = tile
-    try:
-        st, _ = run_layer(sqf, lay, lay.k_out)
-    finally:
-        del os.environ["SQF_GEMM_TILE"]
+    st, _ = run_layer(sqf, lay, lay.k_out, tile=tile)
     _print("tiny m n", tile, st)
 
 
@@ -74,30 +69,41 @@ def test_row_width_extremes(sqf, k):
     _print("row width", k, st)
 
 
-@pytest.mark.parametrize("tile,branch", [("0", "bf16"), ("1", "bf16"), ("2", "bf16"),
-                                         ("0", "fp8"), ("1", "fp8"), ("2", "fp8")])
+@pytest.mark.parametrize("tile,branch", [("256", "bf16"), ("128", "bf16"), ("64", "bf16"),
+                                         ("128", "fp8"), ("64", "fp8")])
 def test_ragged_every_tile_config(sqf, tile, branch):
     """M, N and K_low are not multiples of any tile; K_out is not a multiple of 64."""
     lay = _ragged()
-    os.environ["SQF_GEMM_TILE"] = tile
-    try:
-        st, _ = run_layer(sqf, lay, lay.k_out, branch=branch)
-    finally:
-        del os.environ["SQF_GEMM_TILE"]
+    st, _ = run_layer(sqf, lay, lay.k_out, branch=branch, tile=tile)
     _print("ragged tile", tile, branch, st)
 
 
-@pytest.mark.parametrize("tile", ["0", "1"])
+@pytest.mark.parametrize("tile", ["128", "64"])
 def test_e4m3_every_channel_each_tile(sqf, tile):
     """Every channel in the E4M3 branch (a long branch loop, no low stage) on
-    the 256x256 and 128x128 tiles."""
+    both of its tiles, 128x128 and 64x64."""
     lay = _ragged(m=300, k=1024, n=520, n_scaled=64, seed=83)
-    os.environ["SQF_GEMM_TILE"] = tile
-    try:
-        st, _ = run_layer(sqf, lay, lay.k, branch="fp8")
-    finally:
-        del os.environ["SQF_GEMM_TILE"]
+    st, _ = run_layer(sqf, lay, lay.k, branch="fp8", tile=tile)
     _print("k_out=k fp8 tile", tile, st)
+
+
+def test_forced_tile_the_e4m3_branch_lacks(sqf):
+    """The E4M3 branch has no 256x256 tile: forcing one is refused with
+    SQF_ERR_UNSUPPORTED (nothing runs), the automatic choice runs 128x128."""
+    lay = _ragged(m=64, k=512, n=128, n_scaled=32, seed=88)
+    x_cal = torch.from_numpy(lay.x_cal).cuda()
+    w = torch.from_numpy(lay.w).cuda()
+    _, mp, _, _ = sqf.sqf_select_channels(x_cal, w, lay.k_out)
+    wts = sqf.sqf_pack_weights(w, mp, branch="fp8")
+    acts = sqf.alloc_acts(lay.m, lay.k - lay.k_out, lay.k_out, branch="fp8")
+    sqf.sqf_quantize_split_act(x_inputs(lay, "bf16")[2], mp, acts)
+    with pytest.raises(sqf.SqfError) as ei:
+        sqf.sqf_dual_gemm(acts, wts, tile="256")
+    assert ei.value.status == sqf.SQF_ERR_UNSUPPORTED
+    y_auto = sqf.sqf_dual_gemm(acts, wts)
+    y_128 = sqf.sqf_dual_gemm(acts, wts, tile="128")
+    torch.cuda.synchronize()
+    assert torch.equal(y_auto.view(torch.int32), y_128.view(torch.int32))
 
 
 @pytest.mark.parametrize("branch", ["bf16", "fp8"])
@@ -175,7 +181,7 @@ def test_selection_ties_and_ragged_rows(sqf, k, n):
     _print("ties", k, n, "boundary score", o_sc[src_a])
 
 
-@pytest.mark.parametrize("tile,branch", [("0", "bf16"), ("1", "bf16"), ("2", "bf16"), ("1", "fp8")])
+@pytest.mark.parametrize("tile,branch", [("256", "bf16"), ("128", "bf16"), ("64", "bf16"), ("128", "fp8")])
 def test_bf16_output(sqf, tile, branch):
     """bf16 Y: each element is the round-to-nearest-even of the fp32 Y the
     fp32 launch writes (same accumulators, same epilogue arithmetic), within
@@ -190,20 +196,16 @@ def test_bf16_output(sqf, tile, branch):
     ox, ofmt, xt = x_inputs(lay, "bf16")
     acts = sqf.alloc_acts(lay.m, lay.k - lay.k_out, lay.k_out, branch=branch)
     sqf.sqf_quantize_split_act(xt, mp, acts)
-    os.environ["SQF_GEMM_TILE"] = tile
-    try:
-        y32 = sqf.sqf_dual_gemm(acts, wts)
-        yb = sqf.sqf_dual_gemm(acts, wts, y_dtype="bf16")
-        # the output-type entry point with SQF_F32 is the plain fp32 call
-        y32b = torch.empty_like(y32)
-        da, dw = acts.desc(), wts.desc()
-        assert sqf._lib.sqf_dual_gemm_y(ctypes.byref(da), ctypes.byref(dw), ctypes.c_void_p(y32b.data_ptr()),
-                                        sqf.SQF_F32, y32b.stride(0),
-                                        ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)) == 0
-        big = torch.full((lay.m, lay.n + 3), float("nan"), dtype=torch.bfloat16, device="cuda")
-        sqf.sqf_dual_gemm(acts, wts, y=big[:, :lay.n], y_dtype="bf16")
-    finally:
-        del os.environ["SQF_GEMM_TILE"]
+    y32 = sqf.sqf_dual_gemm(acts, wts, tile=tile)
+    yb = sqf.sqf_dual_gemm(acts, wts, y_dtype="bf16", tile=tile)
+    # the output-type entry point with SQF_F32 is the plain fp32 call
+    y32b = torch.empty_like(y32)
+    da, dw = acts.desc(), wts.desc()
+    assert sqf._lib.sqf_dual_gemm_ex(ctypes.byref(da), ctypes.byref(dw), ctypes.c_void_p(y32b.data_ptr()),
+                                     sqf.SQF_F32, y32b.stride(0), sqf.TILES[tile], None, None, None,
+                                     ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)) == 0
+    big = torch.full((lay.m, lay.n + 3), float("nan"), dtype=torch.bfloat16, device="cuda")
+    sqf.sqf_dual_gemm(acts, wts, y=big[:, :lay.n], y_dtype="bf16", tile=tile)
     torch.cuda.synchronize()
     assert torch.equal(y32b.view(torch.int32), y32.view(torch.int32))
     want = _bf16_bits(y32.to(torch.bfloat16))
@@ -317,11 +319,6 @@ def _sq_check(sqf, lay, nnz, label):
     assert f32_bits_equal(wts.t["s_w8"].cpu().numpy(), o_w["s_w8"])
     assert np.array_equal(wts.t["w_out"][0].cpu().numpy().view(np.int8), o_w["w_out"])
     assert f32_bits_equal(wts.t["s_wo"][0].cpu().numpy(), o_w["s_wo"])
-    # tile offsets: marks before each 256-slot tile, from the oracle's bytes
-    nib = np.stack([o_w["w_low"] & 0xF, o_w["w_low"] >> 4], -1).reshape(lay.n, -1)
-    marks = np.concatenate([np.zeros((lay.n, 1), np.int64), np.cumsum(nib == 8, 1)], 1)
-    want = marks[:, ::256]
-    assert np.array_equal(wts.t["sq_tile_off"].cpu().numpy(), want)
     o_a = oracle.quantize_split_act(ox, o_mp, low="i8", branch="i8", x_fmt=ofmt)
     assert np.array_equal(acts.t["x_low"].cpu().numpy(), o_a["x_low"])
     assert np.array_equal(acts.t["x_out"].cpu().numpy(), o_a["x_out"])
@@ -342,7 +339,7 @@ def _moe_small(experts=6, tokens=96, topk=2, hidden=512, inter=256, seed=86):
                            inter=inter, cal_rows=64)
 
 
-@pytest.mark.parametrize("branch,tile", [("bf16", "1"), ("bf16", "0"), ("fp8", "1"), ("fp8", "0")])
+@pytest.mark.parametrize("branch,tile", [("bf16", "128"), ("bf16", "256"), ("fp8", "128")])
 def test_grouped_small_with_empty_group(sqf, branch, tile):
     """Ragged expert groups, one of them empty, on both grouped tile shapes."""
     moe = _moe_small()
@@ -351,25 +348,17 @@ def test_grouped_small_with_empty_group(sqf, branch, tile):
     lays[2] = synth.Layer(name="empty", m=0, k=lays[2].k, n=lays[2].n, k_out=lays[2].k_out,
                           x=lays[2].x[:0], x_cal=lays[2].x_cal, w=lays[2].w,
                           scaled=lays[2].scaled)
-    os.environ["SQF_GEMM_TILE"] = tile
-    try:
-        _grouped_check(sqf, lays, branch, y_bf16=True)
-    finally:
-        del os.environ["SQF_GEMM_TILE"]
+    _grouped_check(sqf, lays, branch, y_bf16=True, tile=tile)
 
 
-@pytest.mark.parametrize("tile", ["0", "1"])
+@pytest.mark.parametrize("tile", ["256", "128"])
 def test_grouped_many_groups(sqf, tile):
     """600 expert groups of 0-4 rows: more groups than one block-wide pass of
     the tile lookup covers (256 or 512 per pass), many of them empty."""
     moe = synth.qwen3_moe(seed=87, experts=600, tokens=300, topk=2, hidden=256, inter=128,
                           cal_rows=32)
     assert any(l.m == 0 for l in moe.up)
-    os.environ["SQF_GEMM_TILE"] = tile
-    try:
-        _grouped_check(sqf, moe.up, "bf16")
-    finally:
-        del os.environ["SQF_GEMM_TILE"]
+    _grouped_check(sqf, moe.up, "bf16", tile=tile)
 
 
 def _bf16_bits(t):
@@ -386,7 +375,7 @@ def _assert_bf16_close(yb, o_y, label):
     assert not bad.any(), f"{label}: {int(bad.sum())} bf16 outputs beyond tolerance"
 
 
-def _grouped_check(sqf, lays, branch, rows_per_group=None, y_bf16=False):
+def _grouped_check(sqf, lays, branch, rows_per_group=None, y_bf16=False, tile="auto"):
     g = len(lays)
     k, n, k_out = lays[0].k, lays[0].n, lays[0].k_out
     counts = [l.m for l in lays]
@@ -406,9 +395,9 @@ def _grouped_check(sqf, lays, branch, rows_per_group=None, y_bf16=False):
     row_off = torch.from_numpy(off).cuda()
     acts = sqf.alloc_acts(int(off[-1]), k - k_out, k_out, branch=branch)
     sqf.sqf_quantize_split_act_grouped(xt, row_off, maps_t, acts)
-    y, acc = sqf.sqf_dual_gemm_grouped(acts, wts, row_off, debug=True)
-    y_fast = sqf.sqf_dual_gemm_grouped(acts, wts, row_off)
-    yb = sqf.sqf_dual_gemm_grouped(acts, wts, row_off, y_dtype="bf16") if y_bf16 else None
+    y, acc = sqf.sqf_dual_gemm_grouped(acts, wts, row_off, debug=True, tile=tile)
+    y_fast = sqf.sqf_dual_gemm_grouped(acts, wts, row_off, tile=tile)
+    yb = sqf.sqf_dual_gemm_grouped(acts, wts, row_off, y_dtype="bf16", tile=tile) if y_bf16 else None
     torch.cuda.synchronize()
     if y_bf16:
         # the bf16 launch rounds exactly the values the fp32 launch writes
@@ -417,17 +406,27 @@ def _grouped_check(sqf, lays, branch, rows_per_group=None, y_bf16=False):
     yg, ag = y.cpu().numpy(), acc.cpu().numpy().astype(np.int64)
     yf = y_fast.cpu().numpy()
     xl, xo = acts.t["x_low"].cpu().numpy(), acts.t["x_out"].cpu().numpy()
+    sx = acts.t["s_x"].cpu().numpy()
+    sxo = acts.t["s_xo"].cpu().numpy() if branch != "bf16" else None
     for e, l in enumerate(lays):
         o_idx, o_mp, _, _ = oracle.select_channels(l.x_cal, l.w, k_out)
         assert np.array_equal(maps_t[e].cpu().numpy(), o_mp)
         o_w = oracle.pack_weights(l.w, o_mp, branch=branch)
         assert np.array_equal(wts.t["w_low"][e].cpu().numpy(), o_w["w_low"])
+        assert f32_bits_equal(wts.t["s_w"][e].cpu().numpy(), o_w["s_w"]), f"expert {e} s_w"
+        assert np.array_equal(wts.t["w_out"][e].cpu().numpy().view(o_w["w_out"].dtype), o_w["w_out"]), \
+            f"expert {e} branch weights"
+        if branch != "bf16":
+            assert f32_bits_equal(wts.t["s_wo"][e].cpu().numpy(), o_w["s_wo"]), f"expert {e} s_wo"
         if l.m == 0:
             continue
         r0, r1 = off[e], off[e + 1]
         o_a = oracle.quantize_split_act(bits[r0:r1], o_mp, branch=branch, x_fmt="bf16")
         assert np.array_equal(xl[r0:r1], o_a["x_low"])
+        assert f32_bits_equal(sx[r0:r1], o_a["s_x"]), f"expert {e} s_x"
         assert np.array_equal(xo[r0:r1].view(o_a["x_out"].dtype), o_a["x_out"])
+        if branch != "bf16":
+            assert f32_bits_equal(sxo[r0:r1], o_a["s_xo"]), f"expert {e} s_xo"
         rows = None if rows_per_group is None else np.unique(
             np.linspace(0, l.m - 1, min(rows_per_group, l.m)).astype(np.int64))
         o_y, o_acc, _, _ = oracle.dual_gemm(o_a, o_w, rows=rows, debug=True)
@@ -437,3 +436,112 @@ def _grouped_check(sqf, lays, branch, rows_per_group=None, y_bf16=False):
         assert_rows_close(yf[r0:r1][sel], o_y, f"expert {e} (no debug outputs)")
         if y_bf16:
             _assert_bf16_close(ybf[r0:r1][sel], o_y, f"expert {e} (bf16 Y)")
+
+
+def test_hand_case_through_the_abi(sqf, golden):
+    """The hand-worked case (K = 4 channels, one outlier) through every entry
+    point on the GPU, against the values worked by hand: k = 4 is not a
+    multiple of the 8-channel chunk, so the activation kernel takes its
+    element-wise load path; the selection runs without a score buffer."""
+    g = golden("osc_hand_case.txt")
+    f = lambda key: np.array([[float(v) for v in r] for r in g[key]], np.float32)
+    x_cal = torch.from_numpy(f("x_cal")).cuda()
+    w = torch.from_numpy(f("w")).cuda()
+    idx, mp, score, _ = sqf.sqf_select_channels(x_cal, w, int(g["k_out"][0][0]), want_score=False)
+    assert score is None
+    wts = sqf.sqf_pack_weights(w, mp)
+    x = torch.from_numpy(f("x")).cuda()
+    acts = sqf.alloc_acts(1, 3, 1)
+    sqf.sqf_quantize_split_act(x, mp, acts)
+    y, acc = sqf.sqf_dual_gemm(acts, wts, debug=True)[:2]
+    torch.cuda.synchronize()
+    assert idx.cpu().tolist() == [int(v) for v in g["idx"][0]]
+    assert mp.cpu().tolist() == [int(v) for v in g["map"][0]]
+    xl = acts.t["x_low"][0].cpu().numpy()
+    assert xl[:2].tolist() == [int(v, 16) for v in g["x_low_bytes"][0]] and not xl[2:].any()
+    assert acts.t["s_x"][0].item() == float(g["s_x"][0][0])
+    assert int(acts.t["x_out"][0, 0].item()) & 0xFFFF == int(g["x_out_bf16"][0][0], 16)
+    wl = wts.t["w_low"][0].cpu().numpy()
+    assert wl[:, :2].tolist() == [[int(v, 16) for v in r] for r in g["w_low_bytes"]]
+    assert wts.t["s_w"][0].cpu().numpy().tolist() == f("s_w")[0].tolist()
+    assert acc[0].cpu().tolist() == [int(v) for v in g["acc"][0]]
+    assert y[0].cpu().numpy().tolist() == f("y")[0].tolist()
+
+
+@pytest.mark.parametrize("x_dtype", ["bf16", "f32"])
+def test_k_not_a_multiple_of_8(sqf, x_dtype):
+    """k = 1003 channels (k_low 940, k_out 63), rows of exactly k elements:
+    neither k nor the row stride is a multiple of the 8-channel chunk, so the
+    activation kernel reads element by element; every stage against the
+    oracle."""
+    lay = _ragged(m=37, k=1003, n=200, n_scaled=63, seed=97)
+    st, _ = run_layer(sqf, lay, lay.k_out, x_dtype=x_dtype)
+    _print("k=1003", x_dtype, st)
+
+
+def test_selection_without_score_buffer(sqf):
+    """score_out == NULL: the library borrows the workspace; idx and map are
+    those of the call with a score buffer (and of the oracle)."""
+    lay = _ragged(m=16, k=3000, n=300, n_scaled=100, seed=98)
+    x_cal = torch.from_numpy(lay.x_cal).cuda()
+    w = torch.from_numpy(lay.w).cuda()
+    i0, m0, s0, h0 = sqf.sqf_select_channels(x_cal, w, 187)
+    i1, m1, s1, h1 = sqf.sqf_select_channels(x_cal, w, 187, want_score=False)
+    torch.cuda.synchronize()
+    assert s1 is None
+    assert torch.equal(i0, i1) and torch.equal(m0, m1) and torch.equal(h0, h1)
+    o_idx, o_mp, _, _ = oracle.select_channels(lay.x_cal, lay.w, 187)
+    assert np.array_equal(i1.cpu().numpy(), o_idx) and np.array_equal(m1.cpu().numpy(), o_mp)
+
+
+# ------------------------------------------------------------------ int4 codes on the 6-bit matrix unit
+@pytest.mark.parametrize("x_dtype", ["bf16", "f32"])
+def test_e2m3_low_path_ragged(sqf, x_dtype):
+    """The int4 codes in 6-bit E2M3 fields through the FP6 GEMM: M, N and
+    K_low past any tile multiple, K_out not a multiple of the branch stage.
+    Bytes, scales and the exact int32 low sums against the oracle; Y within
+    tolerance."""
+    lay = _ragged(m=300, k=1000, n=520, n_scaled=37, seed=101)
+    st, _ = run_layer(sqf, lay, lay.k_out, x_dtype=x_dtype, low="i4e2m3")
+    _print("e2m3 ragged", x_dtype, st)
+
+
+@pytest.mark.parametrize("k_out_kind", ["none", "all", "half"])
+def test_e2m3_extreme_fractions(sqf, k_out_kind):
+    """No outlier channel (no branch stage), every channel an outlier (no low
+    stage: the bf16 branch alone), and half of them (f = 1/2)."""
+    lay = _ragged(m=260, k=640, n=300, n_scaled=40, seed=102)
+    k_out = {"none": 0, "all": lay.k, "half": lay.k // 2}[k_out_kind]
+    st, _ = run_layer(sqf, lay, k_out, low="i4e2m3", check_select=k_out not in (0, lay.k))
+    _print("e2m3 k_out", k_out_kind, st)
+
+
+def test_e2m3_matches_packed_int4_kernel_bit_for_bit(sqf):
+    """Same codes, same scales, same bf16 branch order: the FP6 kernel's fp32 Y
+    equals the packed-int4 kernel's Y to the bit (the low sums are exact on
+    both, and the fused epilogue rounds identically), and its bf16 Y is the
+    nearest-even rounding of that Y."""
+    lay = _ragged(m=512, k=2048, n=768, n_scaled=128, seed=103)
+    x_cal = torch.from_numpy(lay.x_cal).cuda()
+    w = torch.from_numpy(lay.w).cuda()
+    _, mp, _, _ = sqf.sqf_select_channels(x_cal, w, lay.k_out)
+    xt = x_inputs(lay, "bf16")[2]
+    w4 = sqf.sqf_pack_weights(w, mp)
+    w6 = sqf.sqf_pack_weights(w, mp, low="i4e2m3")
+    a4 = sqf.alloc_acts(lay.m, lay.k - lay.k_out, lay.k_out)
+    a6 = sqf.alloc_acts(lay.m, lay.k - lay.k_out, lay.k_out, low="i4e2m3")
+    sqf.sqf_quantize_split_act(xt, mp, a4)
+    sqf.sqf_quantize_split_act(xt, mp, a6)
+    y4 = sqf.sqf_dual_gemm(a4, w4, tile="256")
+    y6, acc6 = sqf.sqf_dual_gemm(a6, w6, debug=True)[:2]
+    y4d, acc4 = sqf.sqf_dual_gemm(a4, w4, debug=True, tile="256")[:2]
+    y6b = sqf.sqf_dual_gemm(a6, w6, y_dtype="bf16")
+    torch.cuda.synchronize()
+    assert torch.equal(acc6, acc4)
+    assert torch.equal(y6.view(torch.int32), y4.view(torch.int32))
+    assert torch.equal(y6b.view(torch.int16), y6.to(torch.bfloat16).view(torch.int16))
+    with pytest.raises(sqf.SqfError) as ei:
+        sqf.sqf_dual_gemm(a6, w6, tile="128")
+    assert ei.value.status == sqf.SQF_ERR_UNSUPPORTED
+    with pytest.raises(sqf.SqfError):
+        sqf.sqf_dual_gemm(a6, w4)  # activations and weights in different storage
