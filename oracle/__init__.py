@@ -142,12 +142,13 @@ def pad_rows(rows: int) -> int:
 
 
 def i4x2_to_e2m3(packed: np.ndarray, rows_pad: int | None = None) -> np.ndarray:
-    """Packed int4 rows [rows][ldk] -> the K-blocked E2M3 array
-    [2*ldk/128][rows_pad][96] holding the same codes."""
+    """Packed int4 rows [rows][ldk] -> the K-blocked E2M3 array holding the
+    same codes, shaped [2*ldk/128][rows_pad/16][4][16][24] (K block, 16-row
+    group, 32-slot group, row in the group, 24 bytes of 6-bit fields)."""
     packed = np.ascontiguousarray(packed, dtype=np.uint8)
     rows, ldk = packed.shape
     rp = pad_rows(rows) if rows_pad is None else rows_pad
-    out = np.zeros((2 * ldk // 128, rp, 96), dtype=np.uint8)
+    out = np.zeros((2 * ldk // 128, rp // 16, 4, 16, 24), dtype=np.uint8)
     if rows and ldk:
         _load().orc_i4x2_to_e2m3(_p(packed), rows, ldk, rp, _p(out))
     return out

@@ -462,13 +462,16 @@ uint8_t orc_e2m3_field_of_code(int code) {
 
 /* Re-encode packed int4 rows (the layout of orc_quantize_split_act /
  * orc_pack_weights: [rows][ldk], slot 2i in the low nibble of byte i) into
- * the K-blocked E2M3 layout [pad/128][rows_pad][96]: slot j of row r sits in
- * block j/128, 24-byte group (j%128)/32, field j%32 at bits 6*(j%32) of that
- * group, little-endian.  pad = 2*ldk slots per row; rows_pad >= rows; the
- * rows past `rows` are left zero. */
+ * the K-blocked E2M3 layout [pad/128][rows_pad/16][4][16][24]: the 32 slots
+ * 32g .. 32g+31 of K block kb (slots 128kb .. 128kb+127) of row r are 24
+ * bytes at (((kb * rows_pad/16 + r/16) * 4 + g) * 16 + r%16) * 24, field j%32
+ * at bits 6*(j%32) of those bytes, little-endian.  (Within a 16-row group and
+ * a K block the 24-byte pieces are ordered slot group first, row second.)
+ * pad = 2*ldk slots per row; rows_pad >= rows, a multiple of 16; the rows
+ * past `rows` are left zero. */
 void orc_i4x2_to_e2m3(const uint8_t* packed, int64_t rows, int64_t ldk, int64_t rows_pad,
                       uint8_t* out) {
-  const int64_t pad = 2 * ldk, nblk = pad / 128;
+  const int64_t pad = 2 * ldk, nblk = pad / 128, rg = rows_pad / 16;
   memset(out, 0, (size_t)(nblk * rows_pad * 96));
   for (int64_t r = 0; r < rows; ++r) {
     for (int64_t j = 0; j < pad; ++j) {
@@ -476,7 +479,8 @@ void orc_i4x2_to_e2m3(const uint8_t* packed, int64_t rows, int64_t ldk, int64_t 
       uint8_t nib = (uint8_t)(((j & 1) ? (b >> 4) : b) & 0xF);
       int code = (nib & 0x8) ? (int)nib - 16 : (int)nib;
       uint32_t f = orc_e2m3_field_of_code(code);
-      uint8_t* grp = out + ((j / 128) * rows_pad + r) * 96 + ((j % 128) / 32) * 24;
+      int64_t kb = j / 128, g = (j % 128) / 32;
+      uint8_t* grp = out + (((kb * rg + r / 16) * 4 + g) * 16 + r % 16) * 24;
       int64_t bit = 6 * (j % 32);
       for (int t = 0; t < 6; ++t)
         if ((f >> t) & 1u) grp[(bit + t) >> 3] |= (uint8_t)(1u << ((bit + t) & 7));

@@ -548,11 +548,12 @@ def test_e2m3_storage_hand_case(golden):
     j1, c1 = int(g["row1_slot"][0][0]), int(g["row1_code"][0][0])
     packed[1, j1 >> 1] |= (c1 & 0xF) << (4 * (j1 & 1))
     out = oracle.i4x2_to_e2m3(packed)
-    assert out.shape == (2, 256, 96)
-    assert out[0, 0, :6].tolist() == _hexbytes(g["row0_block0"])[0].tolist()
-    assert not out[0, 0, 6:].any() and not out[1, 0].any()
-    assert out[1, 1, :3].tolist() == _hexbytes(g["row1_block1"])[0].tolist()
-    assert not out[1, 1, 3:].any() and not out[0, 1].any() and not out[:, 2:].any()
+    assert out.shape == (2, 16, 4, 16, 24)  # [K block][16-row group][slot group][row][24 B]
+    assert out[0, 0, 0, 0, :6].tolist() == _hexbytes(g["row0_block0"])[0].tolist()
+    out[0, 0, 0, 0, :6] = 0
+    assert out[1, 0, 0, 1, :3].tolist() == _hexbytes(g["row1_block1"])[0].tolist()
+    out[1, 0, 0, 1, :3] = 0
+    assert not out.any()
 
 
 def test_e2m3_storage_brute_force_reader():
@@ -565,11 +566,14 @@ def test_e2m3_storage_brute_force_reader():
     for r in range(rows):
         for j in range(pad):
             packed[r, j >> 1] |= (int(codes[r, j]) & 0xF) << (4 * (j & 1))
-    out = oracle.i4x2_to_e2m3(packed)
-    bits = np.unpackbits(out, axis=-1, bitorder="little")  # [blk][row][768]
+    rows_pad = 32
+    out = oracle.i4x2_to_e2m3(packed, rows_pad).reshape(-1)
+    bits = np.unpackbits(out, bitorder="little")
     for r in range(rows):
         for j in range(pad):
-            grp = bits[j // 128, r, ((j % 128) // 32) * 192:]
-            f = int(sum(int(grp[6 * (j % 32) + t]) << t for t in range(6)))
+            kb, g = j // 128, (j % 128) // 32
+            piece = (((kb * (rows_pad // 16) + r // 16) * 4 + g) * 16 + r % 16) * 24
+            f = int(sum(int(bits[8 * piece + 6 * (j % 32) + t]) << t for t in range(6)))
             assert _e2m3_value(f) * 8 == codes[r, j]
-    assert not out[:, rows:].any()
+    view = out.reshape(pad // 128, rows_pad // 16, 4, 16, 24)
+    assert not view[:, 0, :, rows:].any() and not view[:, 1:].any()
