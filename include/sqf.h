@@ -29,15 +29,17 @@
  *          SQF_I4_E2M3 holds the same int4 codes, each in a 6-bit OCP E2M3
  *          field read as a subnormal (value code/8: field = sign << 5 | |code|),
  *          32 slots per 24 bytes (slot i of a 32-group at bits 6i..6i+5,
- *          little-endian) in a K-blocked array [ldk/96][sqf_pad_rows(m)][96]:
- *          the 96 bytes of 128 consecutive slots of a row are contiguous, and
- *          block kb of every row follows block kb of the row before.  Rows
- *          beyond m are never written and never reach an output.
+ *          little-endian) in a K-blocked array [ldk/96][P/16][4][16][24] with
+ *          P = sqf_pad_rows(m): the 24 bytes of slots 32g..32g+31 of K block kb
+ *          (slots 128kb..128kb+127) of row r sit at
+ *          (((kb*P/16 + r/16)*4 + g)*16 + r%16)*24 (the 6-bit matrix unit's
+ *          lane order).  Rows beyond m are never written and never reach an
+ *          output.
  *          SQF_MXFP4 holds OCP MXFP4: E2M1 codes packed like SQF_I4X2
  *          ([m][ldk], ldk = pad/2) plus one E8M0 scale byte per 32 slots in
  *          s_xb [m][pad/32].
- *   w_low  [n][ldk] bytes: int4 codes, same packings (SQF_I4_E2M3: [ldk/96]
- *          [sqf_pad_rows(n)][96]; SQF_MXFP4: E2M1 with s_wb [n][pad/32]);
+ *   w_low  [n][ldk] bytes: int4 codes, same packings (SQF_I4_E2M3: K-blocked
+ *          with P = sqf_pad_rows(n); SQF_MXFP4: E2M1 with s_wb [n][pad/32]);
  *          nibble 0x8 is the reserved "high precision here" mark
  *          (weight-side format only).
  *   x_out  [m][ldo], w_out [n][ldo]: branch operands (bf16, E4M3 or int8).

@@ -385,14 +385,23 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
     }
     lds_barrier();  // (B) the image row is complete
     // ---- image -> packed HBM row (16-byte stores), then re-zero it ----
-    // (6-bit fields: 16-byte piece q belongs to K block q/6 of the row,
-    // which sits at block q/6's row m of the K-blocked array)
     uint8_t* xl = p.x_low + m * ldk;
-    for (int64_t q = tid; q < ldk / 16; q += NT) {
-      uint8_t* dst = LOW == kI4E2M3 ? p.x_low + ((q / 6) * p.rows_pad + m) * 96 + (q % 6) * 16
-                                    : xl + q * 16;
-      *(uint4*)dst = *(const uint4*)(img + q * 16);
-      *(uint4*)(img + q * 16) = make_uint4(0, 0, 0, 0);
+    if constexpr (LOW == kI4E2M3) {
+      // 6-bit fields: 8-byte piece q is bytes 8*(q%3) .. +7 of slot group
+      // (q/3)%4 of K block q/12, stored at that block's 16-row group m/16,
+      // slot group, row m%16 (the matrix unit's lane order)
+      const int64_t rg = p.rows_pad / 16;
+      for (int64_t q = tid; q < ldk / 8; q += NT) {
+        const int64_t kb = q / 12, g = (q / 3) & 3;
+        uint8_t* dst = p.x_low + (((kb * rg + m / 16) * 4 + g) * 16 + (m & 15)) * 24 + (q % 3) * 8;
+        *(v2u*)dst = *(const v2u*)(img + q * 8);
+        *(v2u*)(img + q * 8) = v2u{0u, 0u};
+      }
+    } else {
+      for (int64_t q = tid; q < ldk / 16; q += NT) {
+        *(uint4*)(xl + q * 16) = *(const uint4*)(img + q * 16);
+        *(uint4*)(img + q * 16) = make_uint4(0, 0, 0, 0);
+      }
     }
     if (tid == 0) *(uint4*)(img + ldk) = make_uint4(0, 0, 0, 0);  // slack
   };

@@ -16,11 +16,16 @@
 // fp32 accumulation is exact in any order: the accumulator times 64 is the
 // int32 sum of the int4 path, bit for bit.
 //
-// Layout.  Both low operands are K-blocked: block kb of 128 slots of every
-// row is 96 contiguous bytes, and block kb of row r+1 follows block kb of
-// row r.  A 256-row panel of one K block is therefore one contiguous 24 KiB
-// run, which the stage's DMAs move as whole cache lines.  The rows are
-// padded to a multiple of 256, so the panel never leaves its block.
+// Layout.  Both low operands are K-blocked and stored in the matrix unit's
+// lane order: for K block kb (128 slots) and 16-row group rg, 1536 bytes
+// hold slot group g (32 slots, 24 bytes) of row r at (g*16 + r%16)*24, which
+// is exactly lane 16g + r%16's share of one 16 x 128 FP6 operand.  A 256-row
+// panel of one K block is one contiguous 24 KiB run (moved by the stage's
+// DMAs as whole cache lines), and each lane's fragment read is 24 bytes at
+// 24*lane: consecutive lanes, consecutive banks.  (A plain row pitch of 96
+// bytes put rows r, r+4, r+8, r+12 on the same banks: 73% of the LDS cycles
+// were bank conflicts.)  The rows are padded to a multiple of 256, so a
+// panel never leaves its block.
 //
 // Tiles.  A block computes 256 x 256 outputs with 8 waves (2 x 4), each
 // wave 128 x 64 (8 x 4 fragments of 16 x 16, 128 accumulator registers), two
@@ -53,7 +58,8 @@ constexpr int kGroupM = 8;
 typedef int v8i __attribute__((ext_vector_type(8)));
 
 // Three 8-byte LDS reads -> the 6 registers of one FP6 operand (32 fields of
-// lane l: row l%16 of the fragment, slots 32*(l/16) .. +31 of the stage).
+// lane l: row l%16 of the fragment, slots 32*(l/16) .. +31 of the stage,
+// stored at byte 24*l of the fragment's 1536 bytes).
 __device__ __forceinline__ v8i ld_fp6(const uint8_t* p) {
   const v2u a = *(const v2u*)p, b = *(const v2u*)(p + 8), c = *(const v2u*)(p + 16);
   return v8i{(int)a.x, (int)a.y, (int)b.x, (int)b.y, (int)c.x, (int)c.y, 0, 0};
@@ -151,10 +157,12 @@ __global__ __launch_bounds__(kNW * 64, 2) void k_gemm6(Gemm6Args p) {
 #pragma unroll
     for (int j = 0; j < kTN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // this lane's byte offsets inside a low stage's panels
+  // this lane's byte offsets inside a low stage's panels: fragment (16 rows)
+  // f of a panel is bytes f*1536 .. +1535, lane l's share at 24*l
   const int fr = lane & 15, fg = lane >> 4;
-  const uint32_t a_off = (uint32_t)((wm * kTM * 16 + fr) * kLowRowB + fg * 24);
-  const uint32_t b_off = (uint32_t)(kBM * kLowRowB + (wn * kTN * 16 + fr) * kLowRowB + fg * 24);
+  constexpr int kFragB = 16 * kLowRowB;  // 1536
+  const uint32_t a_off = (uint32_t)(wm * kTM * kFragB + lane * 24);
+  const uint32_t b_off = (uint32_t)(kBM * kLowRowB + wn * kTN * kFragB + lane * 24);
 
   issue(0);
   if (ST > 1) issue(1);
@@ -162,15 +170,22 @@ __global__ __launch_bounds__(kNW * 64, 2) void k_gemm6(Gemm6Args p) {
   // ---------------- low path: int4 codes on the 6-bit matrix unit ----------------
   for (int t = 0; t < S; ++t) {
     wait_dmas(dmas_of(t + 1));
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS reads are done
     stage_barrier();
     if (t + 2 < ST) issue(t + 2);
     const uint8_t* sl = smem + (t % kRing) * kSlot;
     v8i B[kTN];
 #pragma unroll
-    for (int j = 0; j < kTN; ++j) B[j] = ld_fp6(sl + b_off + j * 16 * kLowRowB);
+    for (int j = 0; j < kTN; ++j) B[j] = ld_fp6(sl + b_off + j * kFragB);
 #pragma unroll
     for (int i = 0; i < kTM; ++i) {
-      const v8i A = ld_fp6(sl + a_off + i * 16 * kLowRowB);
+      const v8i A = ld_fp6(sl + a_off + i * kFragB);
+      // Wave priority: the two waves of a SIMD cross the same barrier and
+      // reach their MFMA runs together; raising it after the first fragment
+      // and dropping it before the last lets one issue back to back while
+      // the other reads LDS.
+      if (i == 1) __builtin_amdgcn_s_setprio(1);
+      if (i == kTM - 1) __builtin_amdgcn_s_setprio(0);
 #pragma unroll
       for (int j = 0; j < kTN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B[j], acc[i][j], 2, 2, 0, 0,
@@ -206,6 +221,7 @@ __global__ __launch_bounds__(kNW * 64, 2) void k_gemm6(Gemm6Args p) {
   auto br_off = [&](int r) { return (uint32_t)(r * kBrRowB + 16 * (bc ^ ((r >> 2) & 3))); };
   for (int t = S; t < ST; ++t) {
     wait_dmas(dmas_of(t + 1));
+    __builtin_amdgcn_s_waitcnt(0xC07F);
     stage_barrier();
     if (t + 2 < ST) issue(t + 2);
     const uint8_t* sl = smem + (t % kRing) * kSlot;
@@ -228,17 +244,18 @@ __global__ __launch_bounds__(kNW * 64, 2) void k_gemm6(Gemm6Args p) {
   constexpr int WN = kTN * 16, LDW = WN + 4;
   const bool whole = wrow0 + kTM * 16 <= mrows && wcol0 + WN <= ncols && (p.ldy & 3) == 0 &&
                      (((uintptr_t)p.y) & (YB ? 7 : 15)) == 0;
+  // every wave is past its last LDS read of the ring (and no DMA is in
+  // flight: the last stage waited for all of them)
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  stage_barrier();
   float* y = p.y;
   uint16_t* yb = (uint16_t*)p.y;
   if (whole) {
-    // Each 16-row slice of the wave tile goes through this wave's part of a
-    // ring slot (no DMA is in flight any more: the last stage's wait drained
-    // them, and every wave has passed the last stage barrier before the
-    // slot the staging uses was last read) and leaves as 16-byte
-    // non-temporal stores of whole row segments.
+    // Each 16-row slice of the wave tile goes through this wave's part of
+    // the (now idle) ring and leaves as 16-byte non-temporal stores of
+    // whole row segments.
     static_assert(kNW * 16 * LDW * 4 <= kSlot, "staging fits one ring slot");
-    __syncthreads();
-    float* stg = (float*)(smem + (ST % kRing) * kSlot) + wave * (16 * LDW);
+    float* stg = (float*)smem + wave * (16 * LDW);
 #pragma unroll
     for (int i = 0; i < kTM; ++i) {
 #pragma unroll

@@ -35,7 +35,7 @@ constexpr int kPackWaves = 16;
 constexpr int kPackChunk = 8192;
 
 // LOWF: kI4X2 (packed nibbles, [n][ldk]) or kI4E2M3 (the same codes in 6-bit
-// E2M3 fields, K-blocked [pad/128][rows_pad][96]; one weight set).
+// E2M3 fields, K-blocked [pad/128][rows_pad/16][4][16][24]; one weight set).
 template <int BR, int LOWF>
 __global__ __launch_bounds__(1024) void k_pack_osc(PackArgs p) {
   __shared__ int32_t list[kPackChunk];
@@ -139,7 +139,9 @@ __global__ __launch_bounds__(1024) void k_pack_osc(PackArgs p) {
                        d2 = (f[2] >> 16) | (f[3] << 8), d3 = f[4] | (f[5] << 24),
                        d4 = (f[5] >> 8) | (f[6] << 16), d5 = (f[6] >> 16) | (f[7] << 8);
         if (live) {
-          uint8_t* dst = p.w_low + ((q >> 2) * p.rows_pad + nn) * 96 + (q & 3) * 24;
+          // K block q/4, 16-row group nn/16, slot group q%4, row nn%16
+          uint8_t* dst =
+              p.w_low + ((((q >> 2) * (p.rows_pad / 16) + nn / 16) * 4 + (q & 3)) * 16 + (nn & 15)) * 24;
           *(v2u*)dst = v2u{d0, d1};
           *(v2u*)(dst + 8) = v2u{d2, d3};
           *(v2u*)(dst + 16) = v2u{d4, d5};

@@ -132,11 +132,11 @@ def low_ldk(k_low: int, low: str) -> int:
 
 def _low_tensor(rows: int, k_low: int, low: str, device, zero: bool):
     """The low operand in its layout: [rows][ldk], or for the K-blocked 6-bit
-    layout [pad/128][sqf_pad_rows(rows)][96]."""
+    layout [pad/128][P/16][4][16][24] with P = sqf_pad_rows(rows)."""
     mk = torch.zeros if zero else torch.empty
     if low == "i4e2m3":
         p = sqf_pad_k_low(k_low)
-        return mk((p // 128, sqf_pad_rows(rows), 96), dtype=torch.uint8, device=device)
+        return mk((p // 128, sqf_pad_rows(rows) // 16, 4, 16, 24), dtype=torch.uint8, device=device)
     return mk((rows, low_ldk(k_low, low)), dtype=torch.uint8, device=device)
 
 

@@ -136,7 +136,10 @@ def run_layer(sqf, lay, k_out, branch="bf16", x_dtype="bf16", rows=None, check_s
         want = oracle.i4x2_to_e2m3(o_a["x_low"], oracle.pad_rows(lay.m))
         got = acts.t["x_low"].cpu().numpy()
         assert got.shape == want.shape
-        assert np.array_equal(got[:, :lay.m], want[:, :lay.m]), "6-bit x_low differs"
+        # rows past m are never written: compare the m real rows
+        rows_of = lambda t: t.transpose(0, 1, 3, 2, 4).reshape(t.shape[0], t.shape[1] * 16, 4, 24)
+        gv, wv = rows_of(got)[:, :lay.m], rows_of(want)[:, :lay.m]
+        assert np.array_equal(gv, wv), "6-bit x_low differs"
     else:
         assert np.array_equal(acts.t["x_low"].cpu().numpy(), o_a["x_low"]), "packed x_low differs"
     assert f32_bits_equal(acts.t["s_x"].cpu().numpy(), o_a["s_x"]), "s_x differs"
