@@ -9,13 +9,18 @@ activations, bf16 outlier branch, seeded synthetic data (no model weights or
 datasets exist here).  Channel selection and weight packing are offline and
 run once before timing.  One step = for each of the three layers: the online
 activation quantise/split kernel, then the fused dual GEMM -- every online
-step of the path, inputs resident in HBM.
+step of the path, inputs resident in HBM.  The int4 codes are stored in
+6-bit E2M3 fields (the value c/8) and multiplied on the FP6 matrix unit,
+whose fp32 sums of these products are exact (every partial sum is a multiple
+of 1/64 far below 2^24), so the results are those of an int32 accumulation;
+the same step with the codes packed two per byte on the int8 matrix unit is
+timed beside it (``packed_int4_step``).
 
 Prints ONE JSON line.  ``value`` is effective TOPS = sum(2*M*N*K) / step
 time.  ``roofline`` describes the dominant kernel (the dual GEMM): achieved
 algorithmic ops (2*M*N*K per launch) / its average launch time measured with
 HIP events on the stream it runs on, against the kernel's own matrix-core
-ceiling (the low path's operations at the int8 peak plus the branch's at the
+ceiling (the low path's operations at the FP6 peak plus the branch's at the
 bf16 peak); ``traffic`` is HBM bytes per GEMM launch from the committed
 rocprofv3 counter summary, or null if the kernel source changed since it was
 taken.  ``cpu_baseline`` times the scalar CPU oracle on a bounded row sample
@@ -40,10 +45,13 @@ if ROOT not in sys.path:
 
 METRIC = "dual-path W4A4+outlier GEMM effective TOPS and % of int8 MFMA peak, 1 GPU"
 PEAK_INT8_TOPS = 5000.0  # MI355X dense int8 MFMA, 5.0 POP/s
+PEAK_FP6_TFLOPS = 10100.0  # MI355X dense FP6 / FP4 MFMA, 10.1 PFLOP/s
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
-GEMM_SOURCES = ["outlier_split_mixed_amd/csrc/k_gemm.hip", "outlier_split_mixed_amd/csrc/sqf_device.h"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_dual_gemm_llama3_70b_f16.txt")
+GEMM_SOURCES = ["outlier_split_mixed_amd/csrc/k_gemm6.hip", "outlier_split_mixed_amd/csrc/sqf_device.h"]
+HEADLINE_LOW = "i4e2m3"  # the int4 codes in 6-bit E2M3 fields on the FP6 matrix unit
+LOW_PEAK = {"i4": PEAK_INT8_TOPS, "i4e2m3": PEAK_FP6_TFLOPS}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_gemm6_llama3_70b_f16.txt")
 
 
 def kernel_sha() -> str:
@@ -91,19 +99,20 @@ def pct(v, q):
 
 
 class LayerRun:
-    def __init__(self, sqf, torch, lay, k_out, stream):
+    def __init__(self, sqf, torch, lay, k_out, stream, low=HEADLINE_LOW):
         self.lay = lay
         self.m, self.k, self.n, self.k_out = lay.m, lay.k, lay.n, k_out
         with torch.cuda.stream(stream):
             x_cal = torch.from_numpy(lay.x_cal).cuda()
             w = torch.from_numpy(lay.w).cuda()
             _, self.map, _, _ = sqf.sqf_select_channels(x_cal, w, k_out, stream=stream)
-            self.w = sqf.sqf_pack_weights(w, self.map, stream=stream)
+            self.low = low
+            self.w = sqf.sqf_pack_weights(w, self.map, stream=stream, low=low)
             from outlier_split_mixed_amd import synth
 
             bits = synth.to_bf16_bits(lay.x)
             self.x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
-            self.acts = sqf.alloc_acts(lay.m, lay.k - k_out, k_out)
+            self.acts = sqf.alloc_acts(lay.m, lay.k - k_out, k_out, low=low)
             self.y = torch.empty((lay.m, lay.n), dtype=torch.float32, device="cuda")
             self.yb = None  # bf16 Y buffer when the step writes bf16
             del w, x_cal
@@ -362,14 +371,15 @@ def main():
     value = total_ops / (step_ms * 1e-3) / 1e12
     gemm_ops = sum(r.ops for r in runs)
     achieved = gemm_ops / (gemm_ms.sum() * 1e-3) / 1e12
-    # the GEMM's own ceiling: each layer's low part at the int8 peak and its
+    # the GEMM's own ceiling: each layer's low part at the FP6 peak and its
     # bf16 branch at the bf16 peak, summed over the three launches
-    bound_us = sum(mfma_bound_us(r.m, r.n, r.k - r.k_out, r.k_out) for r in runs)
+    low_peak = LOW_PEAK[HEADLINE_LOW]
+    bound_us = sum(mfma_bound_us(r.m, r.n, r.k - r.k_out, r.k_out, low_peak) for r in runs)
     peak_eff = gemm_ops / (bound_us * 1e-6) / 1e12
     detail = []
     for i, (r, a, g) in enumerate(zip(runs, act_ms, gemm_ms)):
         tops = r.ops / (g * 1e-3) / 1e12
-        b_us = mfma_bound_us(r.m, r.n, r.k - r.k_out, r.k_out)
+        b_us = mfma_bound_us(r.m, r.n, r.k - r.k_out, r.k_out, low_peak)
         detail.append(dict(shape=f"{r.m}x{r.k}->{r.n}", k_out=r.k_out, act_us=round(a * 1e3, 2),
                            act_us_p10_p50_p90=[pct(act_s[:, i] * 1e3, q) for q in (10, 50, 90)],
                            act_gbs=round(r.act_bytes / (a * 1e-3) / 1e9, 1),
@@ -393,6 +403,25 @@ def main():
         torch.cuda.empty_cache()
         bf16_y = {"ms_per_step": round(step_b, 4), "tops": round(total_ops / (step_b * 1e-3) / 1e12, 2),
                   "gemm_top_s": round(gemm_ops / (gemm_b.sum() * 1e-3) / 1e12, 1)}
+    progress("bf16-Y step timed")
+    lays = [r.lay for r in runs]
+    del runs
+    torch.cuda.empty_cache()
+    # the same step with the int4 codes packed two per byte (the int8 matrix
+    # unit, codes unpacked in registers): same layers, same results
+    runs4 = [LayerRun(sqf, torch, l, l.k_out, stream, low="i4") for l in lays]
+    step4, act4, gemm4 = time_layers(torch, runs4, stream, args.steps, args.warmup)
+    i4_step = {"low": "packed int4 (two codes per byte) on the int8 MFMA",
+               "ms_per_step": round(step4, 4),
+               "tops": round(total_ops / (step4 * 1e-3) / 1e12, 2),
+               "act_us": [round(float(v) * 1e3, 2) for v in act4],
+               "gemm_us": [round(float(v) * 1e3, 2) for v in gemm4],
+               "gemm_frac_mfma_bound": [round(mfma_bound_us(r.m, r.n, r.k - r.k_out, r.k_out,
+                                                            PEAK_INT8_TOPS) / (float(g) * 1e3), 4)
+                                        for r, g in zip(runs4, gemm4)]}
+    del runs4
+    torch.cuda.empty_cache()
+    progress(f"packed-int4 step timed: {step4:.4f} ms")
     traffic = read_traffic()
     out = {
         "metric": METRIC,
@@ -405,29 +434,28 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4*int4->int32 + bf16->fp32",
+        "dtype": "int4 codes (as E2M3 values c/8, FP6 MFMA, exact fp32 sums) + bf16 -> fp32",
         "data": "synthetic (seeded Gaussian, token-persistent outlier channels)",
         "config": {"workload": "llama3_70b_prefill_linears_f1/16", "m": 4096,
                    "shapes_k_n": [[8192, 8192], [8192, 28672], [28672, 8192]],
                    "outlier_fraction": "1/16", "x_dtype": "bf16", "branch": "bf16",
+                   "low_storage": "int4 codes in 6-bit E2M3 fields (K-blocked, lane order)",
                    "parallelism": "none (1 GPU)"},
         "pct_int8_peak": round(100 * value / PEAK_INT8_TOPS, 2),
-        "roofline": {"bound": "mfma", "kernel": "k_dual_gemm", "achieved": round(achieved, 1),
+        "roofline": {"bound": "mfma", "kernel": "k_gemm6", "achieved": round(achieved, 1),
                      "peak": round(peak_eff, 1), "unit": "TOP/s",
                      "frac": round(achieved / peak_eff, 4),
                      "traffic": traffic, "traffic_unit": "bytes per launch",
-                     "peak_basis": "2MN*K_low at the 5.0 POP/s int8 peak + 2MN*K_out at the "
+                     "peak_basis": "2MN*K_low at the 10.1 PFLOP/s FP6 peak + 2MN*K_out at the "
                                    "2.5 PFLOP/s bf16 peak, over the three launches",
                      "frac_int8_peak": round(achieved / PEAK_INT8_TOPS, 4),
                      "avg_launch_us": round(float(gemm_ms.mean()) * 1e3, 2),
                      "ops_per_launch": gemm_ops / 3},
         "detail": detail,
         "bf16_y_step": bf16_y,
+        "packed_int4_step": i4_step,
         "setup_s": round(setup_s, 1),
     }
-    lays = [r.lay for r in runs]
-    del runs
-    torch.cuda.empty_cache()
     if not args.no_sweep:
         # the Llama-3-70B-shaped layers at outlier fractions 1/2 ... 1/16, and
         # the Llama-3-8B-shaped layers at 1/16 (M = 2048)
@@ -436,10 +464,10 @@ def main():
         cases += [("1/16", synth.llama3_8b(i)) for i in range(3)]
         for frac, lay in cases:
             r = LayerRun(sqf, torch, lay, lay.k_out, stream)
-            s_ms, a_ms, g_ms = time_layers(torch, [r], stream, max(5, args.steps // 2), 2)
+            s_ms, a_ms, g_ms = time_layers(torch, [r], stream, max(5, args.steps // 2), 5)
             g_us = float(g_ms[0]) * 1e3
             tops = r.ops / (g_us * 1e-6) / 1e12
-            b_us = mfma_bound_us(r.m, r.n, r.k - r.k_out, r.k_out)
+            b_us = mfma_bound_us(r.m, r.n, r.k - r.k_out, r.k_out, low_peak)
             sweep.append(dict(workload=lay.name.split(".")[0], frac=frac,
                               shape=f"{r.m}x{r.k}->{r.n}", k_out=r.k_out,
                               act_us=round(float(a_ms[0]) * 1e3, 1),

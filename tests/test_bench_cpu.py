@@ -27,7 +27,7 @@ def test_kernel_sha_covers_the_gemm_sources():
     b = _bench()
     sha = b.kernel_sha()
     assert len(sha) == 16 and int(sha, 16) >= 0
-    assert any(p.endswith("k_gemm.hip") for p in b.GEMM_SOURCES)
+    assert any(p.endswith("k_gemm6.hip") for p in b.GEMM_SOURCES)
     assert any(p.endswith("sqf_device.h") for p in b.GEMM_SOURCES)
 
 
