@@ -19,6 +19,10 @@ the method:
 * :func:`dual_gemm`        -- low path + masked path + branch + fused output.
 * :func:`i4x2_to_e2m3`     -- the same int4 codes stored in 6-bit E2M3 fields,
   K-blocked (the storage a 6-bit matrix unit reads).
+* :func:`pack_weights_mx`, :func:`quantize_split_act_mx`, :func:`dual_gemm_mx`
+  -- the MXFP4 low path (OCP Microscaling: E2M1 elements, one E8M0 scale
+  per 32 slots; OSC abstract, 4-bit micro-scaling hardware), and
+  :func:`mx_storage`, the K-blocked storage of those rows.
 """
 from __future__ import annotations
 
@@ -94,6 +98,20 @@ def _declare(lib):
     lib.orc_e4m3_from_float.restype = ctypes.c_uint8
     lib.orc_e4m3_to_double.argtypes = [ctypes.c_uint8]
     lib.orc_e4m3_to_double.restype = ctypes.c_double
+    lib.orc_e2m1_to_double.argtypes = [ctypes.c_uint8]
+    lib.orc_e2m1_to_double.restype = ctypes.c_double
+    lib.orc_e2m1_from_double.argtypes = [ctypes.c_double]
+    lib.orc_e2m1_from_double.restype = ctypes.c_uint8
+    lib.orc_mx_block.argtypes = [P, I64, P]
+    lib.orc_mx_block.restype = ctypes.c_uint8
+    lib.orc_pack_weights_mx.argtypes = [P, I64, I64, P, I64, I64, I64, I64, P, P, P]
+    lib.orc_pack_weights_mx.restype = None
+    lib.orc_quantize_split_act_mx.argtypes = [P, INT, I64, I64, I64, P, I64, I64, I64, I64, P, P, P]
+    lib.orc_quantize_split_act_mx.restype = None
+    lib.orc_mx_storage.argtypes = [P, P, I64, I64, I64, P, P]
+    lib.orc_mx_storage.restype = None
+    lib.orc_dual_gemm_mx.argtypes = [I64, I64, I64, I64, P, I64, P, P, P, I64, P, P, P, P, I64]
+    lib.orc_dual_gemm_mx.restype = None
     lib.orc_num_threads.argtypes = []
     lib.orc_num_threads.restype = ctypes.c_int
 
@@ -296,4 +314,100 @@ def dual_gemm(a: dict, w: dict, rows=None, debug: bool = False):
         for d in dbg:
             assert np.abs(d).max(initial=0) < 2 ** 31
         return y, dbg[0], dbg[1], dbg[2]
+    return y
+
+
+# ---------------------------------------------------------------- MXFP4 low path
+def e2m1_to_float(c: int) -> float:
+    """Value of a 4-bit OCP E2M1 code."""
+    return float(_load().orc_e2m1_to_double(int(c) & 0xF))
+
+
+def e2m1_from_float(t: float) -> int:
+    """Nearest E2M1 code (ties to mantissa bit 0, saturating at +-6)."""
+    return int(_load().orc_e2m1_from_double(float(t)))
+
+
+def mx_block(v: np.ndarray):
+    """One MX block (<= 32 values) -> (E8M0 scale byte, E2M1 codes u8)."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    codes = np.zeros(max(len(v), 1), dtype=np.uint8)
+    b = _load().orc_mx_block(_p(v), len(v), _p(codes))
+    return int(b), codes[: len(v)]
+
+
+def pack_weights_mx(w: np.ndarray, mp: np.ndarray):
+    """Weights [k][n] -> dict(w_low u8 [n][pad/2] E2M1 pairs, s_wb u8 [n][pad/32]
+    E8M0, w_out u16 [n][ldo] bf16) for the MXFP4 low path."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    mp = np.ascontiguousarray(mp, dtype=np.int32)
+    k, n = w.shape
+    k_out = int((mp < 0).sum())
+    k_low = k - k_out
+    pad = pad_k_low(k_low)
+    ldo = pad_k_out(k_out, "bf16")
+    w_low = np.zeros((n, pad // 2), dtype=np.uint8)
+    s_wb = np.zeros((n, pad // 32), dtype=np.uint8)
+    w_out = np.zeros((n, ldo), dtype=np.uint16)
+    _load().orc_pack_weights_mx(_p(w), k, n, _p(mp), k_low, k_out, pad, ldo,
+                                _p(w_low) if pad else None, _p(s_wb) if pad else None,
+                                _p(w_out) if ldo else None)
+    return dict(w_low=w_low, s_wb=s_wb, w_out=w_out, k_low=k_low, k_out=k_out, pad=pad, ldo=ldo,
+                low="mxfp4", branch="bf16")
+
+
+def quantize_split_act_mx(x: np.ndarray, mp: np.ndarray, x_fmt: str = "f32"):
+    """Activations [m][k] -> dict(x_low u8 [m][pad/2], s_xb u8 [m][pad/32],
+    x_out u16 [m][ldo] bf16) for the MXFP4 low path."""
+    x = np.ascontiguousarray(x)
+    mp = np.ascontiguousarray(mp, dtype=np.int32)
+    m, k = x.shape
+    assert x.dtype == (np.uint16 if x_fmt == "bf16" else np.float32)
+    k_out = int((mp < 0).sum())
+    k_low = k - k_out
+    pad = pad_k_low(k_low)
+    ldo = pad_k_out(k_out, "bf16")
+    x_low = np.zeros((m, pad // 2), dtype=np.uint8)
+    s_xb = np.zeros((m, pad // 32), dtype=np.uint8)
+    x_out = np.zeros((m, ldo), dtype=np.uint16)
+    _load().orc_quantize_split_act_mx(_p(x), _FMT[x_fmt], m, k, k, _p(mp), k_low, k_out, pad, ldo,
+                                      _p(x_low) if pad else None, _p(s_xb) if pad else None,
+                                      _p(x_out) if ldo else None)
+    return dict(x_low=x_low, s_xb=s_xb, x_out=x_out, k_low=k_low, k_out=k_out, pad=pad, ldo=ldo,
+                low="mxfp4", branch="bf16")
+
+
+def mx_storage(codes: np.ndarray, scales: np.ndarray, rows_pad: int | None = None):
+    """MXFP4 rows (codes [rows][pad/2], scales [rows][pad/32]) -> the K-blocked
+    storage: codes [pad/128][rows_pad/16][4][16][16], scales
+    [pad/128][rows_pad/64][4][16][4] (see orc_mx_storage)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    rows, half = codes.shape
+    pad = 2 * half
+    assert scales.shape == (rows, pad // 32)
+    rp = pad_rows(rows) if rows_pad is None else rows_pad
+    c = np.zeros((pad // 128, rp // 16, 4, 16, 16), dtype=np.uint8)
+    sc = np.zeros((pad // 128, rp // 64, 4, 16, 4), dtype=np.uint8)
+    if rows and pad:
+        _load().orc_mx_storage(_p(codes), _p(scales), rows, pad, rp, _p(c), _p(sc))
+    return c, sc
+
+
+def dual_gemm_mx(a: dict, w: dict, rows=None):
+    """Y rows of the MXFP4 dual GEMM for token indices ``rows`` (default all)."""
+    m = a["x_low"].shape[0] if a["x_low"].size else a["x_out"].shape[0]
+    if rows is None:
+        rows = np.arange(m, dtype=np.int64)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    n = w["w_low"].shape[0] if w["w_low"].size else w["w_out"].shape[0]
+    assert a["k_low"] == w["k_low"] and a["k_out"] == w["k_out"] and a["pad"] == w["pad"]
+    y = np.zeros((len(rows), n), dtype=np.float32)
+    _load().orc_dual_gemm_mx(n, a["k_low"], a["k_out"], a["pad"], _p(rows), len(rows),
+                             _p(a["x_low"]) if a["x_low"].size else None,
+                             _p(a["s_xb"]) if a["s_xb"].size else None,
+                             _p(a["x_out"]) if a["x_out"].size else None, a["ldo"],
+                             _p(w["w_low"]) if w["w_low"].size else None,
+                             _p(w["s_wb"]) if w["s_wb"].size else None,
+                             _p(w["w_out"]) if w["w_out"].size else None, _p(y), n)
     return y

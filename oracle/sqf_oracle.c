@@ -489,6 +489,194 @@ void orc_i4x2_to_e2m3(const uint8_t* packed, int64_t rows, int64_t ldk, int64_t 
 }
 
 /* ------------------------------------------------------------------ */
+/* MXFP4 low path (OCP Microscaling: E2M1 elements, E8M0 block scales) */
+/* ------------------------------------------------------------------ */
+
+/* [OSC-abs: the low path fits 4-bit micro-scaling hardware.]  The pages do
+ * not define the format; the plain reading is the OCP Microscaling (MX)
+ * specification's MXFP4: blocks of 32 consecutive values share one E8M0
+ * scale 2^X, and each value is stored as an FP4 E2M1 element.
+ *
+ * E2M1: 1 sign bit (bit 3), 2 exponent bits (bits 2..1, bias 1), 1 mantissa
+ * bit (bit 0), no infinities or NaN; exponent 0 is subnormal with value
+ * (-1)^s * m/2, otherwise (-1)^s * 2^(e-1) * (1 + m/2).  The value of a code
+ * is computed from that definition. */
+double orc_e2m1_to_double(uint8_t c) {
+  int s = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+  double v = e == 0 ? (double)m / 2.0 : ldexp(1.0 + (double)m / 2.0, e - 1);
+  return s ? -v : v;
+}
+
+/* Nearest E2M1 value to t, ties to the code with mantissa bit 0, saturating
+ * to +-6 (the largest finite element); written as a search over the eight
+ * non-negative codes.  A value that rounds to zero gives +0 (0x0). */
+uint8_t orc_e2m1_from_double(double t) {
+  double a = fabs(t);
+  int best = 0;
+  double best_err = a;
+  for (int c = 1; c <= 7; ++c) {
+    double err = fabs(orc_e2m1_to_double((uint8_t)c) - a);
+    if (err < best_err || (err == best_err && (c & 1) == 0 && (best & 1) == 1)) {
+      best = c;
+      best_err = err;
+    }
+  }
+  if (a > 6.0) best = 7; /* saturate */
+  return (uint8_t)(best | ((t < 0.0 && best != 0) ? 0x8 : 0));
+}
+
+/* One MX block v[0..len) (len <= 32; absent positions count as 0): the
+ * shared exponent is X = floor(log2(max|v|)) - 2, 2 being the exponent of
+ * the largest E2M1 normal (6 = 1.5 * 2^2), clamped to the E8M0 range
+ * [-127, 127]; an all-zero block takes X = -127.  Element i is the E2M1
+ * code of v_i / 2^X (so the block's absmax lands in [4, 8) and saturates
+ * to 6 above 6).  codes[i] receives the 4-bit code; the return value is the
+ * E8M0 byte X + 127. */
+uint8_t orc_mx_block(const float* v, int64_t len, uint8_t* codes) {
+  double amax = 0.0;
+  for (int64_t i = 0; i < len; ++i)
+    if (fabs((double)v[i]) > amax) amax = fabs((double)v[i]);
+  int x = -127;
+  if (amax > 0.0) {
+    int e;
+    frexp(amax, &e); /* amax = f * 2^e, f in [0.5, 1): floor(log2 amax) = e - 1 */
+    x = (e - 1) - 2;
+    if (x < -127) x = -127;
+    if (x > 127) x = 127;
+  }
+  for (int64_t i = 0; i < len; ++i) codes[i] = orc_e2m1_from_double(ldexp((double)v[i], -x));
+  return (uint8_t)(x + 127);
+}
+
+/* Quantise a row of `len` values in slot order into MXFP4 over `pad` slots
+ * (pad a multiple of 32; slots >= len are 0): codes packed two per byte
+ * (slot 2i in the low nibble of byte i) into row[pad/2], scales[pad/32]. */
+static void mx_row(const float* vals, int64_t len, int64_t pad, uint8_t* row, uint8_t* scales) {
+  float blk[32];
+  uint8_t c[32];
+  memset(row, 0, (size_t)(pad / 2));
+  for (int64_t b = 0; b < pad / 32; ++b) {
+    for (int i = 0; i < 32; ++i) {
+      int64_t j = b * 32 + i;
+      blk[i] = j < len ? vals[j] : 0.0f;
+    }
+    scales[b] = orc_mx_block(blk, 32, c);
+    for (int i = 0; i < 32; ++i) {
+      int64_t j = b * 32 + i;
+      row[j >> 1] |= (uint8_t)((j & 1) ? (c[i] << 4) : c[i]);
+    }
+  }
+}
+
+/* Weights for the MXFP4 low path: per output channel nn, the low channels'
+ * values in slot order -> MXFP4 (codes w_low[nn][pad/2], scales
+ * s_wb[nn][pad/32]); the outlier channels -> bf16 branch row w_out[nn][ldo]. */
+void orc_pack_weights_mx(const float* w, int64_t k, int64_t n, const int32_t* map, int64_t k_low,
+                         int64_t k_out, int64_t pad, int64_t ldo, uint8_t* w_low, uint8_t* s_wb,
+                         uint16_t* w_out) {
+  float* lo = (float*)malloc(sizeof(float) * (size_t)(k_low + 1));
+  float* hi = (float*)malloc(sizeof(float) * (size_t)(k_out + 1));
+  int32_t* tmp = (int32_t*)malloc(sizeof(int32_t) * (size_t)(k_out + 1));
+  for (int64_t nn = 0; nn < n; ++nn) {
+    for (int64_t c = 0; c < k; ++c) {
+      int32_t s = map[c];
+      float v = w[c * n + nn];
+      if (s >= 0)
+        lo[s] = v;
+      else
+        hi[-s - 1] = v;
+    }
+    if (pad > 0) mx_row(lo, k_low, pad, w_low + nn * (pad / 2), s_wb + nn * (pad / 32));
+    if (ldo > 0) store_branch_row(hi, k_out, ORC_BF16, w_out + nn * ldo, ldo, tmp);
+  }
+  free(tmp);
+  free(hi);
+  free(lo);
+}
+
+/* Activations for the MXFP4 low path: per token, the low channels' values in
+ * slot order -> MXFP4 (x_low[m][pad/2], s_xb[m][pad/32]); the outlier
+ * channels -> bf16 branch row x_out[m][ldo] (no scale).  x as in
+ * orc_quantize_split_act. */
+void orc_quantize_split_act_mx(const void* x, int x_fmt, int64_t m, int64_t k, int64_t ldx,
+                               const int32_t* map, int64_t k_low, int64_t k_out, int64_t pad,
+                               int64_t ldo, uint8_t* x_low, uint8_t* s_xb, uint16_t* x_out) {
+  float* lo = (float*)malloc(sizeof(float) * (size_t)(k_low + 1));
+  float* hi = (float*)malloc(sizeof(float) * (size_t)(k_out + 1));
+  int32_t* tmp = (int32_t*)malloc(sizeof(int32_t) * (size_t)(k_out + 1));
+  for (int64_t mm = 0; mm < m; ++mm) {
+    for (int64_t c = 0; c < k; ++c) {
+      float v = x_fmt == ORC_BF16 ? (float)orc_bf16_to_double(((const uint16_t*)x)[mm * ldx + c])
+                                  : ((const float*)x)[mm * ldx + c];
+      if (map[c] >= 0)
+        lo[map[c]] = v;
+      else
+        hi[-map[c] - 1] = v;
+    }
+    if (pad > 0) mx_row(lo, k_low, pad, x_low + mm * (pad / 2), s_xb + mm * (pad / 32));
+    if (ldo > 0) store_branch_row(hi, k_out, ORC_BF16, x_out + mm * ldo, ldo, tmp);
+  }
+  free(tmp);
+  free(hi);
+  free(lo);
+}
+
+/* The MXFP4 rows in the K-blocked storage the 4-bit matrix unit reads:
+ *   codes  [pad/128][rows_pad/16][4][16][16]: the 16 bytes of slots
+ *          32g .. 32g+31 of K block kb of row r (bytes 64kb+16g .. +15 of
+ *          the packed row) at (((kb * rows_pad/16 + r/16) * 4 + g) * 16 +
+ *          r%16) * 16;
+ *   scales [pad/128][rows_pad/64][4][16][4]: the scale of that block of
+ *          row r at (((kb * rows_pad/64 + r/64) * 4 + g) * 16 + r%16) * 4 +
+ *          (r/16)%4.
+ * rows_pad >= rows, a multiple of 64; rows past `rows` are left zero. */
+void orc_mx_storage(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t pad,
+                    int64_t rows_pad, uint8_t* codes_out, uint8_t* scales_out) {
+  const int64_t nblk = pad / 128;
+  memset(codes_out, 0, (size_t)(nblk * rows_pad * 64));
+  memset(scales_out, 0, (size_t)(nblk * rows_pad * 4));
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t kb = 0; kb < nblk; ++kb)
+      for (int64_t g = 0; g < 4; ++g) {
+        memcpy(codes_out + (((kb * (rows_pad / 16) + r / 16) * 4 + g) * 16 + r % 16) * 16,
+               codes + r * (pad / 2) + kb * 64 + g * 16, 16);
+        scales_out[(((kb * (rows_pad / 64) + r / 64) * 4 + g) * 16 + r % 16) * 4 + (r / 16) % 4] =
+            scales[r * (pad / 32) + kb * 4 + g];
+      }
+}
+
+/* y[r][nn] of the MXFP4 dual GEMM for the token rows rows[0..nr):
+ *   y = sum_j (2^(X_x(b)) * e2m1(cx_j)) * (2^(X_w(b)) * e2m1(cw_j))
+ *       + sum_t xo[t] * wo[t]                   (b = block of slot j = j/32)
+ * in fp64, rounded once to fp32.  [OSC-abs: 4-bit path plus 16-bit branch,
+ * results summed; the micro-scaling block scales multiply each block's
+ * products.]  Codes packed [rows][pad/2], scales [rows][pad/32] (the
+ * logical layout of orc_quantize_split_act_mx / orc_pack_weights_mx). */
+void orc_dual_gemm_mx(int64_t n, int64_t k_low, int64_t k_out, int64_t pad, const int64_t* rows,
+                      int64_t nr, const uint8_t* x_low, const uint8_t* s_xb,
+                      const uint16_t* x_out, int64_t ldo, const uint8_t* w_low,
+                      const uint8_t* s_wb, const uint16_t* w_out, float* y, int64_t ldy) {
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int64_t r = 0; r < nr; ++r) {
+    for (int64_t nn = 0; nn < n; ++nn) {
+      int64_t mm = rows[r];
+      double acc = 0.0;
+      for (int64_t j = 0; j < k_low; ++j) {
+        uint8_t bx = x_low[mm * (pad / 2) + (j >> 1)], bw = w_low[nn * (pad / 2) + (j >> 1)];
+        uint8_t cx = (uint8_t)(((j & 1) ? bx >> 4 : bx) & 0xF);
+        uint8_t cw = (uint8_t)(((j & 1) ? bw >> 4 : bw) & 0xF);
+        double vx = ldexp(orc_e2m1_to_double(cx), (int)s_xb[mm * (pad / 32) + j / 32] - 127);
+        double vw = ldexp(orc_e2m1_to_double(cw), (int)s_wb[nn * (pad / 32) + j / 32] - 127);
+        acc += vx * vw;
+      }
+      for (int64_t t = 0; t < k_out; ++t)
+        acc += orc_bf16_to_double(x_out[mm * ldo + t]) * orc_bf16_to_double(w_out[nn * ldo + t]);
+      y[r * ldy + nn] = (float)acc;
+    }
+  }
+}
+
+/* ------------------------------------------------------------------ */
 /* Steps a3-a5 (and the weight-side masked path): the dual GEMM        */
 /* ------------------------------------------------------------------ */
 

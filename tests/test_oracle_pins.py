@@ -577,3 +577,154 @@ def test_e2m3_storage_brute_force_reader():
             assert _e2m3_value(f) * 8 == codes[r, j]
     view = out.reshape(pad // 128, rows_pad // 16, 4, 16, 24)
     assert not view[:, 0, :, rows:].any() and not view[:, 1:].any()
+
+
+# ------------------------------------------------------------------ MXFP4
+# OCP Microscaling MXFP4: the E2M1 element values and the scale rule are
+# the specification's; the cases below are worked by hand from it.
+E2M1_TABLE = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def test_e2m1_value_table():
+    for c in range(16):
+        v = E2M1_TABLE[c & 7]
+        assert oracle.e2m1_to_float(c) == (-v if c & 8 else v)
+        assert math.copysign(1.0, oracle.e2m1_to_float(c)) == (-1.0 if c & 8 else 1.0)
+
+
+def test_e2m1_rounding_ties_and_saturation():
+    cases = {0.0: 0, 0.24: 0, 0.25: 0, 0.26: 1, 0.75: 2, 1.25: 2, 1.75: 4, 2.5: 4, 3.5: 6,
+             5.0: 6, 5.01: 7, 6.0: 7, 7.9: 7, 100.0: 7, -0.75: 0xA, -5.0: 0xE, -0.1: 0}
+    for t, c in cases.items():
+        assert oracle.e2m1_from_float(t) == c, t
+
+
+def test_mx_block_hand_cases(golden):
+    g = golden("mx_hand_case.txt")
+    for name in ("blockA", "blockB"):
+        v = np.zeros(32, np.float32)
+        vals = [float(s) for s in g[name][0]]
+        v[: len(vals)] = vals
+        b, codes = oracle.mx_block(v)
+        assert b == int(g[name + "_scale"][0][0], 16)
+        exp = [int(s, 16) for s in g[name + "_codes"][0]]
+        assert codes[: len(exp)].tolist() == exp and not codes[len(exp):].any()
+    assert oracle.mx_block(np.zeros(32, np.float32))[0] == 0
+    for name, val in (("blockD", 2.0 ** -125), ("blockE", 2.0 ** -130), ("blockF", 2.0 ** 100)):
+        b, codes = oracle.mx_block(np.array([val], np.float32))
+        assert b == int(g[name + "_scale"][0][0], 16)
+        assert codes[0] == int(g[name + "_code"][0][0])
+
+
+def test_mx_whole_path_hand_case(golden):
+    g = golden("mx_hand_case.txt")
+    x = _floats(g["path_x"])
+    w = _floats(g["path_w"]).reshape(4, 1)
+    mp = np.array([int(v) for v in g["path_map"][0]], np.int32)
+    a = oracle.quantize_split_act_mx(x, mp)
+    assert a["x_low"][0, :2].tolist() == _hexbytes(g["path_x_low"])[0].tolist()
+    assert not a["x_low"][0, 2:].any()
+    assert a["s_xb"][0, 0] == int(g["path_s_xb"][0][0], 16)
+    assert int(a["x_out"][0, 0]) == int(g["path_x_out"][0][0], 16) and not a["x_out"][0, 1:].any()
+    wp = oracle.pack_weights_mx(w, mp)
+    assert wp["w_low"][0, :2].tolist() == _hexbytes(g["path_w_low"])[0].tolist()
+    assert wp["s_wb"][0, 0] == int(g["path_s_wb"][0][0], 16)
+    assert int(wp["w_out"][0, 0]) == int(g["path_w_out"][0][0], 16)
+    y = oracle.dual_gemm_mx(a, wp)
+    assert y[0, 0] == np.float32(g["path_y"][0][0])
+
+
+def _mx_representable(rng, rows, k_low):
+    """Rows whose every 32-slot block is exact in MXFP4: E2M1 values times
+    2^X with a +-4 or +-6 in the block (so the block's own X is X)."""
+    out = np.zeros((rows, k_low), np.float64)
+    for r in range(rows):
+        for b in range(0, k_low, 32):
+            n = min(32, k_low - b)
+            x = int(rng.integers(-3, 4))
+            v = rng.choice(E2M1_TABLE, n) * rng.choice([-1.0, 1.0], n)
+            v[int(rng.integers(0, n))] = rng.choice([4.0, 6.0, -4.0, -6.0])
+            out[r, b:b + n] = v * 2.0 ** x
+    return out
+
+
+def test_mx_gemm_equals_exact_product_when_representable():
+    """Inputs exact in MXFP4 (low part) and bf16 (branch): the oracle's Y is
+    X.W exactly (every product and partial sum is a short dyadic number),
+    and quantisation returns the inputs bit for bit."""
+    rng = np.random.default_rng(5)
+    m, k, n, k_out = 6, 300, 5, 20
+    perm = rng.permutation(k)
+    out_ch = np.sort(perm[:k_out])
+    mp = np.zeros(k, np.int32)
+    low_ch = [c for c in range(k) if c not in set(out_ch)]
+    for j, c in enumerate(low_ch):
+        mp[c] = j
+    for t, c in enumerate(out_ch):
+        mp[c] = -(t + 1)
+    k_low = k - k_out
+    xl, wl = _mx_representable(rng, m, k_low), _mx_representable(rng, n, k_low)
+    x = np.zeros((m, k)); w = np.zeros((k, n))
+    x[:, low_ch] = xl; w[low_ch, :] = wl.T
+    x[:, out_ch] = rng.integers(-64, 64, (m, k_out)) / 8.0  # exact in bf16
+    w[out_ch, :] = rng.integers(-64, 64, (k_out, n)) / 16.0
+    a = oracle.quantize_split_act_mx(x.astype(np.float32), mp)
+    wp = oracle.pack_weights_mx(w.astype(np.float32), mp)
+    deq = lambda codes, sc, j: oracle.e2m1_to_float((codes[j >> 1] >> (4 * (j & 1))) & 0xF) * 2.0 ** (int(sc[j // 32]) - 127)
+    for r in range(m):
+        assert [deq(a["x_low"][r], a["s_xb"][r], j) for j in range(k_low)] == xl[r].tolist()
+    for c in range(n):
+        assert [deq(wp["w_low"][c], wp["s_wb"][c], j) for j in range(k_low)] == wl[c].tolist()
+    y = oracle.dual_gemm_mx(a, wp)
+    assert np.array_equal(y, (x @ w).astype(np.float32))
+
+
+def test_mx_quantisation_error_bound():
+    """Gaussian rows: each block's scale is 2^(floor(log2 max) - 2) and every
+    element is within 2^(X+1) of its input (half a quantum of at most 2^(X+1)
+    below 6 * 2^X, saturation above)."""
+    rng = np.random.default_rng(9)
+    v = (rng.standard_normal((40, 32)) * np.exp(rng.uniform(-8, 8, (40, 1)))).astype(np.float32)
+    for row in v:
+        b, codes = oracle.mx_block(row)
+        amax = float(np.abs(row).max())
+        assert b - 127 == math.floor(math.log2(amax)) - 2
+        q = np.array([oracle.e2m1_to_float(c) for c in codes]) * 2.0 ** (b - 127)
+        assert np.all(np.abs(q - row) <= 2.0 ** (b - 127 + 1))
+        assert np.abs(q).max() >= 4 * 2.0 ** (b - 127)
+
+
+def test_mx_storage_hand_case(golden):
+    g = golden("mx_hand_case.txt")
+    codes = np.zeros((17, 128), np.uint8)
+    scales = np.zeros((17, 8), np.uint8)
+    codes[0, 0] = int(g["store_row0_byte0"][0][0], 16)
+    scales[0, 0] = int(g["store_row0_scale0"][0][0], 16)
+    codes[16, 100] = int(g["store_row16_slot200"][0][0])  # slot 200: low nibble of byte 100
+    scales[16, 6] = int(g["store_row16_scale6"][0][0], 16)
+    c, s = oracle.mx_storage(codes, scales)
+    assert c.shape == (2, 16, 4, 16, 16) and s.shape == (2, 4, 4, 16, 4)
+    assert c[0, 0, 0, 0, 0] == 0xA4 and c[1, 1, 2, 0, 4] == 0x07
+    c[0, 0, 0, 0, 0] = 0; c[1, 1, 2, 0, 4] = 0
+    assert not c.any()
+    assert s[0, 0, 0, 0, 0] == 0x7E and s[1, 0, 2, 0, 1] == 0x85
+    s[0, 0, 0, 0, 0] = 0; s[1, 0, 2, 0, 1] = 0
+    assert not s.any()
+
+
+def test_mx_storage_brute_force_reader():
+    rng = np.random.default_rng(13)
+    rows, pad, rp = 70, 384, 256
+    codes = rng.integers(0, 256, (rows, pad // 2)).astype(np.uint8)
+    scales = rng.integers(0, 255, (rows, pad // 32)).astype(np.uint8)
+    c, s = oracle.mx_storage(codes, scales, rp)
+    cf, sf = c.reshape(-1), s.reshape(-1)
+    for r in range(rows):
+        for j in range(pad):
+            kb, g = j // 128, (j % 128) // 32
+            piece = (((kb * (rp // 16) + r // 16) * 4 + g) * 16 + r % 16) * 16
+            byte = cf[piece + (j % 32) // 2]
+            assert (byte >> (4 * (j & 1))) & 0xF == (codes[r, j >> 1] >> (4 * (j & 1))) & 0xF
+            if j % 32 == 0:
+                sidx = (((kb * (rp // 64) + r // 64) * 4 + g) * 16 + r % 16) * 4 + (r // 16) % 4
+                assert sf[sidx] == scales[r, j // 32]
