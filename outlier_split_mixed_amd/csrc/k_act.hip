@@ -192,7 +192,19 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
   // Rows of a block: a strided set (one map for all rows), or, for expert
   // groups, a contiguous run, so that the group (and its map) rarely changes
   // between consecutive rows of a block.
+  // Strided rows: block b takes rows sigma(b) + i * G (G = gridDim.x).  When
+  // G is a multiple of 128, sigma places the 16 rows of each aligned 16-row
+  // group on 16 blocks of one XCD (blocks go to the XCDs round robin, block b
+  // to XCD b % 8), so the K-blocked layouts, whose smallest pieces are one
+  // row's 8..24 bytes inside a 16-row run, fill each cache line within one
+  // L2 in the same pass instead of leaving partial lines in eight.
   int64_t m_first = blockIdx.x, m_stop = p.m, m_step = gridDim.x;
+  if constexpr (!GROUPED) {
+    if ((gridDim.x & 127) == 0) {
+      const int64_t xcd = blockIdx.x & 7, s = blockIdx.x >> 3;
+      m_first = ((s >> 4) * 8 + xcd) * 16 + (s & 15);
+    }
+  }
   int g_cur = 0;      // group of the current row (expert groups)
   int64_t g_end = 0;  // first row after it
   if constexpr (GROUPED) {
