@@ -50,7 +50,7 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 GEMM_SOURCES = ["outlier_split_mixed_amd/csrc/k_gemm6.hip", "outlier_split_mixed_amd/csrc/sqf_device.h"]
 HEADLINE_LOW = "i4e2m3"  # the int4 codes in 6-bit E2M3 fields on the FP6 matrix unit
-LOW_PEAK = {"i4": PEAK_INT8_TOPS, "i4e2m3": PEAK_FP6_TFLOPS}
+LOW_PEAK = {"i4": PEAK_INT8_TOPS, "i4e2m3": PEAK_FP6_TFLOPS, "mxfp4": PEAK_FP6_TFLOPS}  # FP4 = FP6 rate
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_gemm6_llama3_70b_f16.txt")
 
 
@@ -422,6 +422,23 @@ def main():
     del runs4
     torch.cuda.empty_cache()
     progress(f"packed-int4 step timed: {step4:.4f} ms")
+    # the MXFP4 low path (E2M1 codes, one E8M0 scale per 32 slots) on the same
+    # layers: a different number format (its own quantisation), same shapes
+    runs_mx = [LayerRun(sqf, torch, l, l.k_out, stream, low="mxfp4") for l in lays]
+    step_mx, act_mx, gemm_mx = time_layers(torch, runs_mx, stream, args.steps, args.warmup)
+    mx_bound = [mfma_bound_us(r.m, r.n, r.k - r.k_out, r.k_out, LOW_PEAK["mxfp4"]) for r in runs_mx]
+    mx_step = {"low": "MXFP4 (E2M1 codes, E8M0 scale per 32 slots) on the FP4 MFMA",
+               "ms_per_step": round(step_mx, 4),
+               "tops": round(total_ops / (step_mx * 1e-3) / 1e12, 2),
+               "act_us": [round(float(v) * 1e3, 2) for v in act_mx],
+               "gemm_us": [round(float(v) * 1e3, 2) for v in gemm_mx],
+               "gemm_tops": round(gemm_ops / (gemm_mx.sum() * 1e-3) / 1e12, 1),
+               "gemm_frac_mfma_bound": [round(b / (float(g) * 1e3), 4) for b, g in zip(mx_bound, gemm_mx)],
+               "roofline_frac": round(sum(mx_bound) / (gemm_mx.sum() * 1e3), 4),
+               "peak_basis": "2MN*K_low at the 10.1 PFLOP/s FP4 peak + 2MN*K_out at 2.5 PFLOP/s bf16"}
+    del runs_mx
+    torch.cuda.empty_cache()
+    progress(f"MXFP4 step timed: {step_mx:.4f} ms")
     traffic = read_traffic()
     out = {
         "metric": METRIC,
@@ -454,6 +471,7 @@ def main():
         "detail": detail,
         "bf16_y_step": bf16_y,
         "packed_int4_step": i4_step,
+        "mxfp4_step": mx_step,
         "setup_s": round(setup_s, 1),
     }
     if not args.no_sweep:

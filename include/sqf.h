@@ -35,11 +35,18 @@
  *          (((kb*P/16 + r/16)*4 + g)*16 + r%16)*24 (the 6-bit matrix unit's
  *          lane order).  Rows beyond m are never written and never reach an
  *          output.
- *          SQF_MXFP4 holds OCP MXFP4: E2M1 codes packed like SQF_I4X2
- *          ([m][ldk], ldk = pad/2) plus one E8M0 scale byte per 32 slots in
- *          s_xb [m][pad/32].
- *   w_low  [n][ldk] bytes: int4 codes, same packings (SQF_I4_E2M3: K-blocked
- *          with P = sqf_pad_rows(n); SQF_MXFP4: E2M1 with s_wb [n][pad/32]);
+ *          SQF_MXFP4 holds OCP MXFP4 ([OSC] abstract: the low path on 4-bit
+ *          micro-scaling hardware): every 32 slots 32b..32b+31 of a row are
+ *          one block of E2M1 codes (sign bit 3, exponent bits 2..1 with bias
+ *          1, mantissa bit 0) sharing one E8M0 scale byte (value 2^(s-127)).
+ *          Codes two per byte (slot 2i in the low nibble), K-blocked
+ *          [ldk/64][P/16][4][16][16]: the 16 bytes of slot group g (slots
+ *          32g..32g+31) of K block kb of row r at
+ *          (((kb*P/16 + r/16)*4 + g)*16 + r%16)*16.  Scales K-blocked
+ *          [ldk/64][P/64][4][16][4]: the scale of that block of row r at
+ *          (((kb*P/64 + r/64)*4 + g)*16 + r%16)*4 + (r/16)%4 (s_xb / s_wb).
+ *   w_low  [n][ldk] bytes: int4 codes, same packings (SQF_I4_E2M3 and
+ *          SQF_MXFP4: K-blocked with P = sqf_pad_rows(n));
  *          nibble 0x8 is the reserved "high precision here" mark
  *          (weight-side format only).
  *   x_out  [m][ldo], w_out [n][ldo]: branch operands (bf16, E4M3 or int8).
@@ -50,12 +57,18 @@
  * Quantisation: symmetric, per token (activations) and per output channel
  * (weights): a = max|v| over the vector, inv = Q/a in fp32, code =
  * clamp(rint(v*inv), -Q, Q), scale = a/Q; a = 0 gives codes 0, scale 0.
+ * MXFP4 instead quantises each 32-slot block of a row: X = floor(log2
+ * max|v|) - 2 clamped to >= -127 (an all-zero block: -127), scale byte X+127,
+ * code = the E2M1 value nearest v / 2^X (ties to the even code, saturating
+ * at 6).
  * Q = 7 (int4), 127 (int8); E4M3 codes are the nearest-even E4M3 value of
  * v*448/a, saturated.  The low absmax excludes the outlier channels (and the
  * marked weight positions).  The bf16 branch is unscaled (round to nearest
  * even); E4M3 / int8 branches carry per-token and per-output-channel scales.
  * Output:  y = s_x[m]*s_w[n]*acc_low (+ s_x[m]*s_w8[n]*acc_sp)
  *              + (s_xo[m]*s_wo[n]) * acc_out           (bf16: s = 1)
+ *          MXFP4: y = sum_j 2^Xx(j/32) e2m1(cx_j) * 2^Xw(j/32) e2m1(cw_j)
+ *              + acc_out  (fp32 sums, not exact)
  *
  * Ownership: every buffer is caller-allocated device memory unless stated;
  * the library keeps no pointer after a call returns and allocates nothing.
@@ -76,7 +89,7 @@
 extern "C" {
 #endif
 
-#define SQF_ABI_VERSION 2
+#define SQF_ABI_VERSION 3
 
 typedef enum {
   SQF_OK = 0,
@@ -125,7 +138,8 @@ typedef struct sqf_weights {
   uint8_t* w_low; /* [groups][n][ldk] int4 codes (see the layouts above) */
   float* s_w;     /* [groups][n] low scale (s_w4 of the weight-side format);
                      unused (may be NULL) for SQF_MXFP4 */
-  uint8_t* s_wb;  /* SQF_MXFP4 only: [n][pad/32] E8M0 block scales */
+  uint8_t* s_wb;  /* SQF_MXFP4 only: E8M0 block scales, K-blocked (see above),
+                     16-byte aligned */
   void* w_out;    /* [groups][n][ldo] branch codes; NULL when k_out == 0 */
   float* s_wo;    /* [groups][n] branch scale; NULL for SQF_BF16 */
   /* weight-side SQ-format ([SQF-art] 六, 七, 九): sq_nnz > 0 marks, per
@@ -154,7 +168,8 @@ typedef struct sqf_acts {
   int32_t branch; /* SQF_BF16 | SQF_FP8_E4M3 | SQF_I8 */
   uint8_t* x_low; /* [m][ldk], or K-blocked for SQF_I4_E2M3 (see above) */
   float* s_x;     /* [m]; unused (may be NULL) for SQF_MXFP4 */
-  uint8_t* s_xb;  /* SQF_MXFP4 only: [m][pad/32] E8M0 block scales */
+  uint8_t* s_xb;  /* SQF_MXFP4 only: E8M0 block scales, K-blocked (see above),
+                     16-byte aligned */
   void* x_out;    /* [m][ldo]; NULL when k_out == 0 */
   float* s_xo;    /* [m]; NULL for SQF_BF16 */
 } sqf_acts;
@@ -209,7 +224,8 @@ sqf_status sqf_select_channels(const float* x_cal, int64_t m_cal, int64_t k, con
  * values), the others quantised to int4 with an absmax over the unmarked
  * slots.  SQF_I4_E2M3 weights hold the channel-split int4 codes in the
  * K-blocked 6-bit layout; SQF_MXFP4 weights quantise each 32-slot block of
- * a row's low values to E2M1 with a shared E8M0 scale (OCP MX). */
+ * a row's low values to E2M1 with a shared E8M0 scale (OCP MX), K-blocked.
+ * Both need groups == 1 and a bf16 branch. */
 sqf_status sqf_pack_weights(const float* w, const int32_t* map, const float* hdiag,
                             sqf_weights* wt, void* stream);
 
@@ -224,9 +240,12 @@ sqf_status sqf_quantize_split_act(const void* x, int32_t x_dtype, int64_t ldx, c
 
 /* a3-a5 (and the weight-side masked path) -- the fused dual GEMM.
  * y: [a->m][ldy] fp32, ldy >= n.  The low path runs on int8 MFMA with exact
- * int32 accumulation (int4 codes unpacked in registers); the branch on
- * bf16 / FP8 / int8 MFMA; the epilogue applies the scales and sums the paths
- * ([SQF-art] 三 two paths and fusion; [OSC] result fusion).
+ * int32 accumulation (SQF_I4X2: int4 codes unpacked in registers), on the
+ * FP6 matrix unit with exact sums (SQF_I4_E2M3) or on the FP4 matrix unit
+ * with the block scales applied per product (SQF_MXFP4, no debug output:
+ * SQF_ERR_UNSUPPORTED); the branch on bf16 / FP8 / int8 MFMA; the epilogue
+ * applies the scales and sums the paths ([SQF-art] 三 two paths and fusion;
+ * [OSC] result fusion).
  * Debug outputs (NULL in normal use) receive the exact int32 accumulators
  * [m][n] (row stride n): acc_low_dbg (low path), acc_sp_dbg (weight-side
  * masked path), acc_out_dbg (int8 branch only). */

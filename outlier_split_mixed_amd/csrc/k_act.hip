@@ -70,24 +70,30 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
   const int64_t ldk = p.ldk;
   const int img_bytes = (int)ldk + kImgSlack;  // a multiple of 16
   // LDS: image[2][ldk + slack] | outlier channel list int32[k_out] |
-  // reduction slots float[2][2 * NW]
+  // reduction slots float[2][2 * 16] | MXFP4 block maxima uint32[2][ldk/16]
   uint8_t* img0 = sm;
   int32_t* oidx = (int32_t*)(sm + 2 * img_bytes);
   float* red = (float*)(sm + 2 * img_bytes + ((p.k_out * 4 + 15) & ~(int64_t)15));
+  uint32_t* bmax0 = (uint32_t*)(red + 2 * 2 * 16);
+  const int nblk = LOW == kMXFP4 ? (int)(ldk / 16) : 0;  // 32-slot blocks per row
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const float qlow = LOW == kI8 ? 127.0f : 7.0f;
   const float qhi = BR == kFP8 ? 448.0f : 127.0f;
   const int k_out = (int)p.k_out;
 
-  // both images start zeroed
+  // both images (and the block maxima) start zeroed
   for (int j = tid * 16; j < 2 * img_bytes; j += NT * 16) *(uint4*)(img0 + j) = make_uint4(0, 0, 0, 0);
+  for (int j = tid; j < 2 * nblk; j += NT) bmax0[j] = 0u;
 
   // Per-chunk constants (chunk i of this thread = channels 8*(tid + i*NT) ..+7):
   //   cw   (low slots before the chunk) << 8 | outlier mask (bit e = channel e)
   //   am   absmax masks: 0x7FFF per low channel's bf16 half, 0 for outliers
   //   sel  byte-permute selectors taking the low channels' code bytes, in
   //        order, to bytes 0.. of the compacted pair (zero beyond them)
-  uint32_t cw[CPT], sel0[CPT], sel1[CPT], am[CPT][XT == kBF16 ? 4 : 1];
+  //   b0m  (MXFP4) bit e set when channel e is a low channel whose slot lies in
+  //        the 32-slot block of the chunk's first low slot (the others fall
+  //        in the next block: a chunk's at most 8 slots span at most two)
+  uint32_t cw[CPT], sel0[CPT], sel1[CPT], am[CPT][XT == kBF16 ? 4 : 1], b0m[CPT];
   auto load_map = [&](int g) {
     const int32_t* mp = p.map + (int64_t)g * p.k;
 #pragma unroll
@@ -117,6 +123,17 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
         before = (uint32_t)(m8[0] >= 0 ? m8[0] : c8 - (-m8[0] - 1));
       }
       cw[i] = (before << 8) | mask;
+      {
+        uint32_t bm = 0, rank = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (!((mask >> e) & 1u)) {
+            if ((before + rank) / 32 == before / 32) bm |= 1u << e;
+            ++rank;
+          }
+        }
+        b0m[i] = bm;
+      }
       uint64_t sel = 0x0C0C0C0C0C0C0C0Cull;
       int j = 0;
 #pragma unroll
@@ -273,8 +290,32 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
       for (int d = 0; d < (XT == kBF16 ? 4 : 1); ++d) asm volatile("" : "+v"(am[i][d]));
     }
     // ---- absmax over the low channels (and the outlier channels) ----
-    float alo, ahi = 0.0f;
-    if constexpr (XT == kBF16) {
+    float alo = 0.0f, ahi = 0.0f;
+    uint32_t* bmax = bmax0 + buf * nblk;
+    if constexpr (LOW == kMXFP4) {
+      // MXFP4: the |x| maxima of each 32-slot block, as fp32 bit patterns
+      // (integer order = float order for |x|), two blocks per chunk at most,
+      // combined with LDS atomic max
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        asm volatile("" : "+v"(b0m[i]));
+        const int64_t c8 = ((int64_t)tid + (int64_t)i * NT) * 8;
+        const uint32_t lowm = ~cw[i] & 0xFFu;
+        if (c8 < p.k && lowm != 0u) {
+          uint32_t m0 = 0, m1 = 0;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t a = __float_as_uint(val(raw, i, e)) & 0x7FFFFFFFu;
+            const uint32_t in0 = (b0m[i] >> e) & 1u, in1 = ((lowm & ~b0m[i]) >> e) & 1u;
+            m0 = in0 && a > m0 ? a : m0;
+            m1 = in1 && a > m1 ? a : m1;
+          }
+          const uint32_t b = (cw[i] >> 8) / 32u;
+          atomicMax(bmax + b, m0);
+          if (lowm & ~b0m[i]) atomicMax(bmax + b + 1, m1);
+        }
+      }
+    } else if constexpr (XT == kBF16) {
       typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
       u16x2 mx = {0, 0};
 #pragma unroll
@@ -299,7 +340,7 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
       for (int u = 0; u < OPT; ++u) ahi = fmaxf(ahi, fabsf(ov[u]));
       for (int t = OPT * NT + tid; t < k_out; t += NT) ahi = fmaxf(ahi, fabsf(xval(m, oidx[t])));
     }
-    alo = wave_max(alo);
+    if constexpr (LOW != kMXFP4) alo = wave_max(alo);
     if constexpr (BR != kBF16) ahi = wave_max(ahi);
     if (lane == 0) {
       rd[wv] = alo;
@@ -316,8 +357,17 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
     const float inv_lo = quant_inv(alo, qlow);
     const float inv_hi = BR == kBF16 ? 0.0f : quant_inv(ahi, qhi);
     if (tid == 0) {
-      p.s_x[m] = quant_scale(alo, qlow);
+      if constexpr (LOW != kMXFP4) p.s_x[m] = quant_scale(alo, qlow);
       if constexpr (BR != kBF16) p.s_xo[m] = quant_scale(ahi, qhi);
+    }
+    if constexpr (LOW == kMXFP4) {
+      // E8M0 scale of each block: X = floor(log2 max) - 2, clamped at -127
+      // (byte max(biased exponent - 2, 0)), stored in the matrix unit's
+      // K-blocked scale order
+      const int64_t r64 = p.rows_pad / 64;
+      for (int b = tid; b < nblk; b += NT)
+        p.s_xb[(((int64_t)(b >> 2) * r64 + m / 64) * 4 + (b & 3)) * 64 + (m & 15) * 4 + ((m >> 4) & 3)] =
+            (uint8_t)mx_scale_byte(bmax[b]);
     }
     // ---- branch row: coalesced direct stores, zero padding up to ldo ----
     uint8_t* xo = p.x_out + m * p.ldo * ESZ;
@@ -354,7 +404,16 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
         // must be rounded on its own (a fused multiply-add would round the
         // exact product instead and differ at ties)
         uint32_t y[8];
-        {
+        if constexpr (LOW == kMXFP4) {
+          // E2M1 code of x / 2^X (exact scaling by a power of two), with the
+          // scale of the slot's block
+          const uint32_t b = (cw[i] >> 8) / 32u;
+          const float f0 = mx_inv_scale(mx_scale_byte(bmax[b]));
+          float f1 = f0;
+          if ((~cw[i] & 0xFFu) & ~b0m[i]) f1 = mx_inv_scale(mx_scale_byte(bmax[b + 1]));
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[e] = e2m1_code(val(raw, i, e), ((b0m[i] >> e) & 1u) ? f0 : f1);
+        } else {
 #pragma clang fp contract(off)
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
@@ -378,7 +437,7 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
           atomicOr(d, (uint32_t)lo);
           atomicOr(d + 1, (uint32_t)(lo >> 32));
           if (sh > 16u) atomicOr(d + 2, (uint32_t)(v >> (64u - sh)));
-        } else if constexpr (LOW == kI4X2) {
+        } else if constexpr (LOW == kI4X2 || LOW == kMXFP4) {
           const uint32_t t0 = q0 & 0x0F0F0F0Fu, t1 = q1 & 0x0F0F0F0Fu;
           const uint32_t u0 = t0 | (t0 >> 4), u1 = t1 | (t1 >> 4);
           const uint32_t w = perm(u1, u0, 0x06040200u);  // 8 nibbles, slot order
@@ -408,6 +467,18 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
         uint8_t* dst = p.x_low + (((kb * rg + m / 16) * 4 + g) * 16 + (m & 15)) * 24 + (q % 3) * 8;
         *(v2u*)dst = *(const v2u*)(img + q * 8);
         *(v2u*)(img + q * 8) = v2u{0u, 0u};
+      }
+    } else if constexpr (LOW == kMXFP4) {
+      // E2M1 pairs: 16-byte piece q is slot group q%4 of K block q/4, stored
+      // at that block's 16-row group m/16, slot group, row m%16 (the matrix
+      // unit's lane order); the block maxima are cleared for the row after
+      // next
+      const int64_t rg = p.rows_pad / 16;
+      for (int64_t q = tid; q < ldk / 16; q += NT) {
+        uint8_t* dst = p.x_low + ((((q >> 2) * rg + m / 16) * 4 + (q & 3)) * 16 + (m & 15)) * 16;
+        *(uint4*)dst = *(const uint4*)(img + q * 16);
+        *(uint4*)(img + q * 16) = make_uint4(0, 0, 0, 0);
+        bmax[q] = 0u;
       }
     } else {
       for (int64_t q = tid; q < ldk / 16; q += NT) {
@@ -481,18 +552,24 @@ static hipError_t launch_br(const ActArgs& a, int br, bool ragged, size_t lds, h
   return launch_shape<XT, LOW, kI8, GROUPED>(a, ragged, lds, s);
 }
 
-size_t act_split_lds_bytes(int64_t ldk, int64_t k_out) {
-  return (size_t)(2 * (ldk + kImgSlack) + ((k_out * 4 + 15) & ~(int64_t)15) + 2 * 2 * 16 * sizeof(float));
+size_t act_split_lds_bytes(int64_t ldk, int64_t k_out, int low) {
+  return (size_t)(2 * (ldk + kImgSlack) + ((k_out * 4 + 15) & ~(int64_t)15) + 2 * 2 * 16 * sizeof(float) +
+                  (low == kMXFP4 ? 2 * (ldk / 16) * 4 : 0));
 }
 
 hipError_t launch_act_split(const ActArgs& a, int x_dtype, int low, int branch, bool grouped,
                             bool ragged, hipStream_t s) {
-  const size_t lds = act_split_lds_bytes(a.ldk, a.k_out);
+  const size_t lds = act_split_lds_bytes(a.ldk, a.k_out, low);
   if (a.m <= 0) return hipSuccess;
   if (low == kI4E2M3) {  // bf16 branch, one weight set: the FP6 GEMM's operand
     if (grouped || branch != kBF16) return hipErrorInvalidValue;
     return x_dtype == kBF16 ? launch_shape<kBF16, kI4E2M3, kBF16, false>(a, ragged, lds, s)
                             : launch_shape<kF32, kI4E2M3, kBF16, false>(a, ragged, lds, s);
+  }
+  if (low == kMXFP4) {  // bf16 branch, one weight set: the FP4 GEMM's operand
+    if (grouped || branch != kBF16) return hipErrorInvalidValue;
+    return x_dtype == kBF16 ? launch_shape<kBF16, kMXFP4, kBF16, false>(a, ragged, lds, s)
+                            : launch_shape<kF32, kMXFP4, kBF16, false>(a, ragged, lds, s);
   }
   if (x_dtype == kBF16) {
     if (low == kI4X2)

@@ -1,5 +1,7 @@
-// k_gemm6.hip -- the fused dual-path GEMM on gfx950's 6-bit matrix unit.
+// k_gemm6.hip -- the fused dual-path GEMM on gfx950's 6-/4-bit matrix unit
+// (v_mfma_scale_f32_16x16x128_f8f6f4), in two forms sharing one pipeline:
 //
+// int4 codes in E2M3 fields (FP6 operands):
 //   y[m,n] = s_x[m]*s_w[n]*sum_j qx[m,j]*qw[n,j]  +  sum_t xo[m,t]*wo[n,t]
 // The dual-path computation of OSC (abstract and method framework: a 4-bit
 // GEMM over the ordinary channels, a 16-bit GEMM over the compact outlier
@@ -16,6 +18,17 @@
 // fp32 accumulation is exact in any order: the accumulator times 64 is the
 // int32 sum of the int4 path, bit for bit.
 //
+// MXFP4 (FP4 operands; OSC abstract: the low path on 4-bit micro-scaling
+// hardware, read as OCP MXFP4):
+//   y[m,n] = sum_j 2^Xx(m,j/32) e2m1(cx[m,j]) * 2^Xw(n,j/32) e2m1(cw[n,j])
+//            + sum_t xo[m,t]*wo[n,t]
+// Lane l of a 16 x 128 operand holds the 32 slots of one block, so the
+// block's E8M0 scale is that lane's scale operand: the matrix unit applies
+// both block scales to every product; sums are fp32 (not exact).  The scale
+// bytes of four 16-row fragments (rows r, r+16, r+32, r+48 of a 64-row
+// group) share one dword per lane and the instruction's opsel picks the
+// fragment's byte.
+//
 // Layout.  Both low operands are K-blocked and stored in the matrix unit's
 // lane order: for K block kb (128 slots) and 16-row group rg, 1536 bytes
 // hold slot group g (32 slots, 24 bytes) of row r at (g*16 + r%16)*24, which
@@ -27,11 +40,14 @@
 // were bank conflicts.)  The rows are padded to a multiple of 256, so a
 // panel never leaves its block.
 //
+// (MXFP4: 16 bytes per lane, 1 KiB per 16-row fragment, 16 KiB per panel;
+// the scales of a panel's K block are one contiguous KiB.)
+//
 // Tiles.  A block computes 256 x 256 outputs with 8 waves (2 x 4), each
 // wave 128 x 64 (8 x 4 fragments of 16 x 16, 128 accumulator registers), two
-// waves per SIMD.  K runs as one stream of stages through a ring of three
-// 48 KiB LDS slots: low stages (128 slots: A panel 24 KiB, B panel 24 KiB),
-// then branch stages (32 bf16 channels: 16 KiB + 16 KiB, rows 64 bytes with
+// waves per SIMD.  K runs as one stream of stages through a ring of LDS
+// slots (three of 48 KiB for E2M3, four of 34 KiB for MXFP4): low stages
+// (128 slots: A panel, B panel, MXFP4 also their scales), then branch stages (32 bf16 channels: 16 KiB + 16 KiB, rows 64 bytes with
 // their 16-byte chunks XOR-swizzled by row so the MFMA operand reads hit
 // distinct banks).  At the top of stage t every wave waits for its own DMAs
 // of stage t, crosses one barrier, and issues stage t+2 into the slot stage
@@ -47,37 +63,110 @@ namespace {
 constexpr int kBM = 256, kBN = 256;
 constexpr int kWGM = 2, kWGN = 4, kNW = kWGM * kWGN;
 constexpr int kTM = kBM / kWGM / 16, kTN = kBN / kWGN / 16;  // 8 x 4 fragments
-constexpr int kSlot = 48 * 1024;                               // bytes per ring slot
-constexpr int kRing = 3;
-constexpr int kLowRowB = 96;                                   // bytes per row per low stage
 constexpr int kBrRowB = 64;                                    // bytes per row per branch stage
-constexpr int kLowDmaPerWave = (kBM + kBN) * kLowRowB / 1024 / kNW;  // 6
-constexpr int kBrDmaPerWave = (kBM + kBN) * kBrRowB / 1024 / kNW;    // 4
+constexpr int kBrDmaPerWave = (kBM + kBN) * kBrRowB / 1024 / kNW;  // 4
 constexpr int kGroupM = 8;
+constexpr int kStageWN = kTN * 16, kLDW = kStageWN + 4;         // epilogue staging (floats)
+constexpr int kStageBytes = kNW * 16 * kLDW * 4;                // 34816
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 
-// Three 8-byte LDS reads -> the 6 registers of one FP6 operand (32 fields of
-// lane l: row l%16 of the fragment, slots 32*(l/16) .. +31 of the stage,
-// stored at byte 24*l of the fragment's 1536 bytes).
-__device__ __forceinline__ v8i ld_fp6(const uint8_t* p) {
-  const v2u a = *(const v2u*)p, b = *(const v2u*)(p + 8), c = *(const v2u*)(p + 16);
-  return v8i{(int)a.x, (int)a.y, (int)b.x, (int)b.y, (int)c.x, (int)c.y, 0, 0};
+// Per low-format constants.
+template <int LF>
+struct LowFmt;
+template <>
+struct LowFmt<kI4E2M3> {
+  static constexpr int kRowB = 96;                           // bytes per row per low stage
+  static constexpr int kPanelB = kBM * kRowB;                // 24 KiB
+  static constexpr int kDma = (kBM + kBN) * kRowB / 1024 / kNW;  // 6 per wave
+  static constexpr int kScaleB = 0;
+  static constexpr int kSlot = 48 * 1024;
+  static constexpr int kRing = 3;
+  static constexpr int kType = 2;  // FP6 E2M3 operands
+};
+template <>
+struct LowFmt<kMXFP4> {
+  static constexpr int kRowB = 64;
+  static constexpr int kPanelB = kBM * kRowB;                // 16 KiB
+  static constexpr int kDma = (kBM + kBN) * kRowB / 1024 / kNW;  // 4 per wave (+1 scale DMA on waves 0, 1)
+  static constexpr int kScaleB = 1024;                       // E8M0 bytes per panel per K block
+  static constexpr int kSlot = 34 * 1024;
+  static constexpr int kRing = 4;
+  static constexpr int kType = 4;  // FP4 E2M1 operands
+};
+
+// One operand fragment of lane l (32 fields: row l%16 of the fragment, slots
+// 32*(l/16) .. +31 of the stage): E2M3, three 8-byte LDS reads into 6
+// registers; E2M1, one 16-byte read into 4 (the rest of the tuple unused).
+template <int LF>
+__device__ __forceinline__ v8i ld_frag(const uint8_t* p) {
+  if constexpr (LF == kI4E2M3) {
+    const v2u a = *(const v2u*)p, b = *(const v2u*)(p + 8), c = *(const v2u*)(p + 16);
+    return v8i{(int)a.x, (int)a.y, (int)b.x, (int)b.y, (int)c.x, (int)c.y, 0, 0};
+  } else {
+    const v4i a = *(const v4i*)p;
+    return v8i{a.x, a.y, a.z, a.w, 0, 0, 0, 0};
+  }
 }
 
-// s_waitcnt vmcnt for a wave-uniform count of DMAs still allowed in flight.
+// s_waitcnt vmcnt for a wave-uniform count n of DMAs still allowed in
+// flight, rounded down to one of the counts a wave can have outstanding.
+template <int LF>
 __device__ __forceinline__ void wait_dmas(int n) {
-  if (n >= kLowDmaPerWave) wait_vmcnt<kLowDmaPerWave>();
-  else if (n >= kBrDmaPerWave) wait_vmcnt<kBrDmaPerWave>();
-  else wait_vmcnt<0>();
+  if constexpr (LF == kI4E2M3) {
+    if (n >= 6) wait_vmcnt<6>();
+    else if (n >= 4) wait_vmcnt<4>();
+    else wait_vmcnt<0>();
+  } else {
+    if (n >= 10) wait_vmcnt<10>();
+    else if (n >= 9) wait_vmcnt<9>();
+    else if (n >= 8) wait_vmcnt<8>();
+    else if (n >= 5) wait_vmcnt<5>();
+    else if (n >= 4) wait_vmcnt<4>();
+    else wait_vmcnt<0>();
+  }
+}
+
+// FP4 x FP4 with per-lane E8M0 scales; OA / OB pick the byte of the scale
+// dwords (the builtin takes them as constants: the switch folds once the
+// fragment loops are unrolled).
+template <int OA, int OB>
+__device__ __forceinline__ v4f mfma_fp4(v8i a, v8i b, v4f c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, OA, sa, OB, sb);
+}
+__device__ __forceinline__ v4f mfma_fp4_sel(int oa, int ob, v8i a, v8i b, v4f c, int sa, int sb) {
+  switch (oa * 4 + ob) {
+    case 0: return mfma_fp4<0, 0>(a, b, c, sa, sb);
+    case 1: return mfma_fp4<0, 1>(a, b, c, sa, sb);
+    case 2: return mfma_fp4<0, 2>(a, b, c, sa, sb);
+    case 3: return mfma_fp4<0, 3>(a, b, c, sa, sb);
+    case 4: return mfma_fp4<1, 0>(a, b, c, sa, sb);
+    case 5: return mfma_fp4<1, 1>(a, b, c, sa, sb);
+    case 6: return mfma_fp4<1, 2>(a, b, c, sa, sb);
+    case 7: return mfma_fp4<1, 3>(a, b, c, sa, sb);
+    case 8: return mfma_fp4<2, 0>(a, b, c, sa, sb);
+    case 9: return mfma_fp4<2, 1>(a, b, c, sa, sb);
+    case 10: return mfma_fp4<2, 2>(a, b, c, sa, sb);
+    case 11: return mfma_fp4<2, 3>(a, b, c, sa, sb);
+    case 12: return mfma_fp4<3, 0>(a, b, c, sa, sb);
+    case 13: return mfma_fp4<3, 1>(a, b, c, sa, sb);
+    case 14: return mfma_fp4<3, 2>(a, b, c, sa, sb);
+    default: return mfma_fp4<3, 3>(a, b, c, sa, sb);
+  }
 }
 
 }  // namespace
 
-template <bool DEBUG, bool YB>
+template <int LF, bool DEBUG, bool YB>
 __global__ __launch_bounds__(kNW * 64, 2) void k_gemm6(Gemm6Args p) {
+  using F = LowFmt<LF>;
   static_assert(!(DEBUG && YB), "the accumulator dump comes with fp32 Y");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kRing * kSlot];
+  static_assert(!(DEBUG && LF == kMXFP4), "MXFP4 sums are not integers");
+  static_assert(2 * F::kPanelB + 2 * F::kScaleB <= F::kSlot && kBM * kBrRowB * 2 <= F::kSlot,
+                "a stage fits its slot");
+  static_assert(kStageBytes <= F::kSlot, "the epilogue staging fits one ring slot");
+  constexpr int kRing = F::kRing;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kRing * F::kSlot];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -101,25 +190,33 @@ __global__ __launch_bounds__(kNW * 64, 2) void k_gemm6(Gemm6Args p) {
   const int S = p.s_low, SB = p.s_br, ST = S + SB;
   const uint32_t smem_lds = lds_offset(smem);
 
-  // DMA of stage t into ring slot t % 3.  Low stage: the A panel (rows
-  // m0..m0+255 of K block t) and the B panel are contiguous 24 KiB runs;
-  // instruction q of 48 moves bytes q*1024 .. +1023 of the pair of panels.
+  // DMA of stage t into ring slot t % kRing.  Low stage: the A panel (rows
+  // m0..m0+255 of K block t) and the B panel are contiguous runs; instruction
+  // q moves bytes q*1024 .. +1023 of the pair.  MXFP4: waves 0 and 1 also
+  // move the A and B panels' scale KiB (after the panels in the slot).
   // Branch stage: row-major bf16 rows; instruction q of 32 covers 16 rows x
   // 4 chunks of 16 bytes, lane l -> row q*16 + l/4 (clamped to the last
   // real row), chunk (l%4) ^ ((row/4)%4) of the stage's 64 bytes.
   const int br_r = lane >> 2, br_c = lane & 3;
   auto issue = [&](int t) {
-    const uint32_t slot = smem_lds + (uint32_t)((t % kRing) * kSlot);
+    const uint32_t slot = smem_lds + (uint32_t)((t % kRing) * F::kSlot);
     if (t < S) {
-      const uint8_t* a = p.x6 + ((int64_t)t * p.x_rows + m0) * kLowRowB;
-      const uint8_t* b = p.w6 + ((int64_t)t * p.w_rows + n0) * kLowRowB;
+      const uint8_t* a = p.x6 + ((int64_t)t * p.x_rows + m0) * F::kRowB;
+      const uint8_t* b = p.w6 + ((int64_t)t * p.w_rows + n0) * F::kRowB;
+      constexpr int kPanelDma = F::kPanelB / 1024;
 #pragma unroll
-      for (int i = 0; i < kLowDmaPerWave; ++i) {
-        const int q = wave * kLowDmaPerWave + i;  // wave-uniform
-        const bool is_a = q < kBM * kLowRowB / 1024;
-        const int ql = is_a ? q : q - kBM * kLowRowB / 1024;
-        dma_16B(is_a ? a : b, (uint32_t)(ql * 1024 + lane * 16),
-                slot + (uint32_t)(q * 1024));
+      for (int i = 0; i < F::kDma; ++i) {
+        const int q = wave * F::kDma + i;  // wave-uniform
+        const bool is_a = q < kPanelDma;
+        const int ql = is_a ? q : q - kPanelDma;
+        dma_16B(is_a ? a : b, (uint32_t)(ql * 1024 + lane * 16), slot + (uint32_t)(q * 1024));
+      }
+      if constexpr (F::kScaleB > 0) {
+        if (wave < 2) {
+          const uint8_t* sc = wave == 0 ? p.x_sc + ((int64_t)t * p.x_rows + m0) * 4
+                                        : p.w_sc + ((int64_t)t * p.w_rows + n0) * 4;
+          dma_16B(sc, (uint32_t)(lane * 16), slot + (uint32_t)(2 * F::kPanelB + wave * 1024));
+        }
       }
     } else {
       const uint32_t kb = (uint32_t)(t - S) * kBrRowB;
@@ -137,8 +234,16 @@ __global__ __launch_bounds__(kNW * 64, 2) void k_gemm6(Gemm6Args p) {
       }
     }
   };
-  // DMAs per wave of stage t (0 past the end)
-  auto dmas_of = [&](int t) { return t >= ST ? 0 : (t < S ? kLowDmaPerWave : kBrDmaPerWave); };
+  // DMAs this wave issues for stage t (0 past the end)
+  const int low_dmas = F::kDma + ((F::kScaleB > 0 && wave < 2) ? 1 : 0);
+  auto dmas_of = [&](int t) { return t >= ST ? 0 : (t < S ? low_dmas : kBrDmaPerWave); };
+  // DMAs allowed in flight at the top of stage t: those of the stages after it
+  auto ahead = [&](int t) {
+    int n = 0;
+#pragma unroll
+    for (int d = 1; d < kRing - 1; ++d) n += dmas_of(t + d);
+    return n;
+  };
 
   // The epilogue's arguments are read with scalar loads; landing them before
   // the loop keeps the LDS read counter waits of the loop in order.
@@ -158,28 +263,38 @@ __global__ __launch_bounds__(kNW * 64, 2) void k_gemm6(Gemm6Args p) {
     for (int j = 0; j < kTN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
   // this lane's byte offsets inside a low stage's panels: fragment (16 rows)
-  // f of a panel is bytes f*1536 .. +1535, lane l's share at 24*l
+  // f of a panel is bytes f*16*kRowB .. , lane l's share at (kRowB/4)*l
   const int fr = lane & 15, fg = lane >> 4;
-  constexpr int kFragB = 16 * kLowRowB;  // 1536
-  const uint32_t a_off = (uint32_t)(wm * kTM * kFragB + lane * 24);
-  const uint32_t b_off = (uint32_t)(kBM * kLowRowB + wn * kTN * kFragB + lane * 24);
+  constexpr int kFragB = 16 * F::kRowB;
+  const uint32_t a_off = (uint32_t)(wm * kTM * kFragB + lane * (F::kRowB / 4));
+  const uint32_t b_off = (uint32_t)(F::kPanelB + wn * kTN * kFragB + lane * (F::kRowB / 4));
+  // MXFP4 scale dwords: 64-row group h of the panel, lane l at 4*l
+  const uint32_t as_off = (uint32_t)(2 * F::kPanelB + wm * 2 * 256 + 4 * lane);
+  const uint32_t bs_off = (uint32_t)(2 * F::kPanelB + 1024 + wn * 256 + 4 * lane);
 
-  issue(0);
-  if (ST > 1) issue(1);
+#pragma unroll
+  for (int d = 0; d < kRing - 1; ++d)
+    if (d < ST) issue(d);
 
-  // ---------------- low path: int4 codes on the 6-bit matrix unit ----------------
+  // ---------------- low path on the 6-/4-bit matrix unit ----------------
   for (int t = 0; t < S; ++t) {
-    wait_dmas(dmas_of(t + 1));
+    wait_dmas<LF>(ahead(t));
     __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS reads are done
     stage_barrier();
-    if (t + 2 < ST) issue(t + 2);
-    const uint8_t* sl = smem + (t % kRing) * kSlot;
+    if (t + kRing - 1 < ST) issue(t + kRing - 1);
+    const uint8_t* sl = smem + (t % kRing) * F::kSlot;
     v8i B[kTN];
 #pragma unroll
-    for (int j = 0; j < kTN; ++j) B[j] = ld_fp6(sl + b_off + j * kFragB);
+    for (int j = 0; j < kTN; ++j) B[j] = ld_frag<LF>(sl + b_off + j * kFragB);
+    int sa0 = 0, sa1 = 0, sb = 0;
+    if constexpr (LF == kMXFP4) {
+      sa0 = *(const int*)(sl + as_off);
+      sa1 = *(const int*)(sl + as_off + 256);
+      sb = *(const int*)(sl + bs_off);
+    }
 #pragma unroll
     for (int i = 0; i < kTM; ++i) {
-      const v8i A = ld_fp6(sl + a_off + i * kFragB);
+      const v8i A = ld_frag<LF>(sl + a_off + i * kFragB);
       // Wave priority: the two waves of a SIMD cross the same barrier and
       // reach their MFMA runs together; raising it after the first fragment
       // and dropping it before the last lets one issue back to back while
@@ -187,32 +302,40 @@ __global__ __launch_bounds__(kNW * 64, 2) void k_gemm6(Gemm6Args p) {
       if (i == 1) __builtin_amdgcn_s_setprio(1);
       if (i == kTM - 1) __builtin_amdgcn_s_setprio(0);
 #pragma unroll
-      for (int j = 0; j < kTN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B[j], acc[i][j], 2, 2, 0, 0,
-                                                                      0, 0);
+      for (int j = 0; j < kTN; ++j) {
+        if constexpr (LF == kI4E2M3) {
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B[j], acc[i][j], 2, 2, 0, 0,
+                                                                        0, 0);
+        } else {
+          // opsel picks the fragment's byte of the scale dwords
+          acc[i][j] = mfma_fp4_sel(i & 3, j & 3, A, B[j], acc[i][j], i < 4 ? sa0 : sa1, sb);
+        }
+      }
     }
   }
 
-  // ---------------- exact sums -> scaled fp32 ----------------
   // Lane l holds rows 4*(l/16)+r (r < 4) and column l%16 of each fragment.
   const int row0 = (int)m0 + wm * kTM * 16 + (lane >> 4) * 4;
   const int col0 = (int)n0 + wn * kTN * 16 + (lane & 15);
   const int mrows = (int)p.m, ncols = (int)p.n;
+  if constexpr (LF == kI4E2M3) {
+    // ---------------- exact sums -> scaled fp32 ----------------
 #pragma unroll
-  for (int j = 0; j < kTN; ++j) {
-    const int col = col0 + j * 16;
-    const float sw = p.s_w[col < ncols ? col : ncols - 1] * 64.0f;
+    for (int j = 0; j < kTN; ++j) {
+      const int col = col0 + j * 16;
+      const float sw = p.s_w[col < ncols ? col : ncols - 1] * 64.0f;
 #pragma unroll
-    for (int i = 0; i < kTM; ++i)
+      for (int i = 0; i < kTM; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = row0 + i * 16 + r;
-        if constexpr (DEBUG) {
-          if (row < mrows && col < ncols)
-            p.acc_dbg[(int64_t)row * p.n + col] = (int32_t)(acc[i][j][r] * 64.0f);
+        for (int r = 0; r < 4; ++r) {
+          const int row = row0 + i * 16 + r;
+          if constexpr (DEBUG) {
+            if (row < mrows && col < ncols)
+              p.acc_dbg[(int64_t)row * p.n + col] = (int32_t)(acc[i][j][r] * 64.0f);
+          }
+          acc[i][j][r] *= p.s_x[row < mrows ? row : mrows - 1] * sw;
         }
-        acc[i][j][r] *= p.s_x[row < mrows ? row : mrows - 1] * sw;
-      }
+    }
   }
 
   // ---------------- branch: bf16 outlier sub-tensor GEMM ----------------
@@ -220,11 +343,11 @@ __global__ __launch_bounds__(kNW * 64, 2) void k_gemm6(Gemm6Args p) {
   const int bc = fg;
   auto br_off = [&](int r) { return (uint32_t)(r * kBrRowB + 16 * (bc ^ ((r >> 2) & 3))); };
   for (int t = S; t < ST; ++t) {
-    wait_dmas(dmas_of(t + 1));
+    wait_dmas<LF>(ahead(t));
     __builtin_amdgcn_s_waitcnt(0xC07F);
     stage_barrier();
-    if (t + 2 < ST) issue(t + 2);
-    const uint8_t* sl = smem + (t % kRing) * kSlot;
+    if (t + kRing - 1 < ST) issue(t + kRing - 1);
+    const uint8_t* sl = smem + (t % kRing) * F::kSlot;
     v4i B[kTN];
 #pragma unroll
     for (int j = 0; j < kTN; ++j)
@@ -241,7 +364,7 @@ __global__ __launch_bounds__(kNW * 64, 2) void k_gemm6(Gemm6Args p) {
 
   // ---------------- store ----------------
   const int wrow0 = (int)m0 + wm * kTM * 16, wcol0 = (int)n0 + wn * kTN * 16;
-  constexpr int WN = kTN * 16, LDW = WN + 4;
+  constexpr int WN = kStageWN, LDW = kLDW;
   const bool whole = wrow0 + kTM * 16 <= mrows && wcol0 + WN <= ncols && (p.ldy & 3) == 0 &&
                      (((uintptr_t)p.y) & (YB ? 7 : 15)) == 0;
   // every wave is past its last LDS read of the ring (and no DMA is in
@@ -254,7 +377,6 @@ __global__ __launch_bounds__(kNW * 64, 2) void k_gemm6(Gemm6Args p) {
     // Each 16-row slice of the wave tile goes through this wave's part of
     // the (now idle) ring and leaves as 16-byte non-temporal stores of
     // whole row segments.
-    static_assert(kNW * 16 * LDW * 4 <= kSlot, "staging fits one ring slot");
     float* stg = (float*)smem + wave * (16 * LDW);
 #pragma unroll
     for (int i = 0; i < kTM; ++i) {
@@ -298,16 +420,25 @@ __global__ __launch_bounds__(kNW * 64, 2) void k_gemm6(Gemm6Args p) {
   }
 }
 
-hipError_t launch_gemm6(const Gemm6Args& a, bool debug, bool ybf16, hipStream_t s) {
+hipError_t launch_gemm6(const Gemm6Args& a, int low, bool debug, bool ybf16, hipStream_t s) {
   if (debug && ybf16) return hipErrorInvalidValue;
+  if (low != kI4E2M3 && low != kMXFP4) return hipErrorInvalidValue;
+  if (low == kMXFP4 && debug) return hipErrorInvalidValue;
   const int64_t blocks = ((a.m + kBM - 1) / kBM) * ((a.n + kBN - 1) / kBN);
   if (blocks <= 0) return hipSuccess;
-  if (debug)
-    hipLaunchKernelGGL((k_gemm6<true, false>), dim3((unsigned)blocks), dim3(kNW * 64), 0, s, a);
-  else if (ybf16)
-    hipLaunchKernelGGL((k_gemm6<false, true>), dim3((unsigned)blocks), dim3(kNW * 64), 0, s, a);
-  else
-    hipLaunchKernelGGL((k_gemm6<false, false>), dim3((unsigned)blocks), dim3(kNW * 64), 0, s, a);
+  const dim3 grid((unsigned)blocks), block(kNW * 64);
+  if (low == kMXFP4) {
+    if (ybf16)
+      hipLaunchKernelGGL((k_gemm6<kMXFP4, false, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((k_gemm6<kMXFP4, false, false>), grid, block, 0, s, a);
+  } else if (debug) {
+    hipLaunchKernelGGL((k_gemm6<kI4E2M3, true, false>), grid, block, 0, s, a);
+  } else if (ybf16) {
+    hipLaunchKernelGGL((k_gemm6<kI4E2M3, false, true>), grid, block, 0, s, a);
+  } else {
+    hipLaunchKernelGGL((k_gemm6<kI4E2M3, false, false>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 

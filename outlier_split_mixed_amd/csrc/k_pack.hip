@@ -34,8 +34,12 @@ constexpr int kPackCols = 64;
 constexpr int kPackWaves = 16;
 constexpr int kPackChunk = 8192;
 
-// LOWF: kI4X2 (packed nibbles, [n][ldk]) or kI4E2M3 (the same codes in 6-bit
-// E2M3 fields, K-blocked [pad/128][rows_pad/16][4][16][24]; one weight set).
+// LOWF: kI4X2 (packed nibbles, [n][ldk]), kI4E2M3 (the same codes in 6-bit
+// E2M3 fields, K-blocked [pad/128][rows_pad/16][4][16][24]; one weight set)
+// or kMXFP4 (OSC abstract: the low path on 4-bit micro-scaling hardware,
+// read as OCP MXFP4: each 32-slot group of a row is one block with its own
+// E8M0 scale and E2M1 codes, K-blocked [pad/128][rows_pad/16][4][16][16],
+// scales [pad/128][rows_pad/64][4][16][4]; one weight set).
 template <int BR, int LOWF>
 __global__ __launch_bounds__(1024) void k_pack_osc(PackArgs p) {
   __shared__ int32_t list[kPackChunk];
@@ -83,7 +87,7 @@ __global__ __launch_bounds__(1024) void k_pack_osc(PackArgs p) {
   const float qhi = BR == kFP8 ? 448.0f : 127.0f;
   const float inv_hi = BR == kBF16 ? 0.0f : quant_inv(ahi, qhi);
   if (wv == 0 && live) {
-    p.s_w[g * p.n + nn] = quant_scale(alo, 7.0f);
+    if (LOWF != kMXFP4) p.s_w[g * p.n + nn] = quant_scale(alo, 7.0f);
     if (BR != kBF16 && p.s_wo) p.s_wo[g * p.n + nn] = quant_scale(ahi, qhi);
   }
 
@@ -111,6 +115,7 @@ __global__ __launch_bounds__(1024) void k_pack_osc(PackArgs p) {
     if (s0 < p.k_low) build_list(s0, true);
     for (int64_t q = s0 / 32 + wv; q < s1 / 32; q += kPackWaves) {
       uint32_t ow[4] = {0, 0, 0, 0};
+      uint32_t sbyte = 0;  // MXFP4 scale (an all-zero block: 0)
       if (q * 32 < p.k_low) {
         float v[32];
 #pragma unroll
@@ -118,11 +123,33 @@ __global__ __launch_bounds__(1024) void k_pack_osc(PackArgs p) {
           const int32_t c = list[q * 32 - s0 + e];  // -1 past k_low (cleared)
           v[e] = c >= 0 ? w[(int64_t)c * p.n] : 0.0f;
         }
+        if constexpr (LOWF == kMXFP4) {
+          uint32_t amax = 0;
 #pragma unroll
-        for (int e = 0; e < 32; ++e)
-          ow[e >> 3] |= ((uint32_t)quant_code(v[e], inv, 7.0f) & 0xFu) << ((e & 7) * 4);
+          for (int e = 0; e < 32; ++e) {
+            const uint32_t a = __float_as_uint(v[e]) & 0x7FFFFFFFu;
+            amax = a > amax ? a : amax;
+          }
+          sbyte = mx_scale_byte(amax);
+          const float f = mx_inv_scale(sbyte);
+#pragma unroll
+          for (int e = 0; e < 32; ++e) ow[e >> 3] |= e2m1_code(v[e], f) << ((e & 7) * 4);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 32; ++e)
+            ow[e >> 3] |= ((uint32_t)quant_code(v[e], inv, 7.0f) & 0xFu) << ((e & 7) * 4);
+        }
       }
-      if constexpr (LOWF == kI4E2M3) {
+      if constexpr (LOWF == kMXFP4) {
+        if (live) {
+          // K block q/4, 16-row group nn/16, slot group q%4, row nn%16; the
+          // scale byte with the 64-row group's other three fragments
+          *(uint4*)(p.w_low + ((((q >> 2) * (p.rows_pad / 16) + nn / 16) * 4 + (q & 3)) * 16 + (nn & 15)) * 16) =
+              make_uint4(ow[0], ow[1], ow[2], ow[3]);
+          p.s_wb[((((q >> 2) * (p.rows_pad / 64) + nn / 64) * 4 + (q & 3)) * 16 + (nn & 15)) * 4 +
+                 ((nn >> 4) & 3)] = (uint8_t)sbyte;
+        }
+      } else if constexpr (LOWF == kI4E2M3) {
         // nibbles -> one code per byte -> 6-bit fields, 24 bits per 4 codes
         uint32_t f[8];
 #pragma unroll
@@ -370,6 +397,9 @@ hipError_t launch_pack(const PackArgs& a, int branch, int low, int groups, hipSt
   if (low == kI4E2M3) {
     if (branch != kBF16 || groups != 1) return hipErrorInvalidValue;
     hipLaunchKernelGGL((k_pack_osc<kBF16, kI4E2M3>), grid, block, 0, s, a);
+  } else if (low == kMXFP4) {
+    if (branch != kBF16 || groups != 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_pack_osc<kBF16, kMXFP4>), grid, block, 0, s, a);
   } else if (branch == kBF16) {
     hipLaunchKernelGGL((k_pack_osc<kBF16, kI4X2>), grid, block, 0, s, a);
   } else if (branch == kFP8) {

@@ -47,16 +47,18 @@ bool branch_ok(int32_t b) { return b == SQF_BF16 || b == SQF_FP8_E4M3 || b == SQ
 
 bool tile_ok(int32_t t) { return t >= SQF_TILE_AUTO && t <= SQF_TILE_64; }
 
-// Bytes per row of a low operand: packed nibbles (and E2M1) pad/2, int8 pad,
-// 6-bit E2M3 fields pad*3/4 (stored K-blocked, see sqf.h).
+// Bytes per row of a low operand: packed nibbles (and E2M1 pairs) pad/2, int8
+// pad, 6-bit E2M3 fields pad*3/4 (E2M3 and E2M1 stored K-blocked, see sqf.h).
 int64_t low_ldk(int64_t k_low, int32_t low) {
   const int64_t pad = sqf_pad_k_low(k_low);
   return low == SQF_I8 ? pad : low == SQF_I4_E2M3 ? pad / 4 * 3 : pad / 2;
 }
 // Rows of a low operand's storage (the K-blocked layout pads them).
-int64_t low_rows(int64_t rows, int32_t low) {
-  return low == SQF_I4_E2M3 ? sqf_pad_rows(rows) : rows;
-}
+bool low_kblocked(int32_t low) { return low == SQF_I4_E2M3 || low == SQF_MXFP4; }
+int64_t low_rows(int64_t rows, int32_t low) { return low_kblocked(low) ? sqf_pad_rows(rows) : rows; }
+// Bytes of an MXFP4 operand's E8M0 scale array: one per 32 slots of every
+// stored row.
+int64_t mx_scale_bytes(int64_t k_low, int64_t rows) { return sqf_pad_k_low(k_low) / 32 * sqf_pad_rows(rows); }
 
 // Tile configuration for the channel-split GEMM: the caller's sqf_tile, or
 // (SQF_TILE_AUTO) the largest tile that still gives the 256 CUs enough tiles.
@@ -84,13 +86,11 @@ sqf_status check_weights(const sqf_weights* wt, const char* who) {
   if (!branch_ok(wt->branch))
     return fail(SQF_ERR_INVALID_ARG, "%s: bad branch dtype %d", who, wt->branch);
   if (wt->groups < 1) return fail(SQF_ERR_SHAPE, "%s: groups must be >= 1", who);
-  if (wt->low == SQF_MXFP4)
-    return fail(SQF_ERR_UNSUPPORTED, "%s: low dtype %d is not available for weights", who, wt->low);
-  if (wt->low != SQF_I4X2 && wt->low != SQF_I4_E2M3)
+  if (wt->low != SQF_I4X2 && wt->low != SQF_I4_E2M3 && wt->low != SQF_MXFP4)
     return fail(SQF_ERR_INVALID_ARG, "%s: bad low dtype %d for weights", who, wt->low);
-  if (wt->low == SQF_I4_E2M3 && (wt->groups != 1 || wt->branch != SQF_BF16 || wt->sq_nnz != 0))
-    return fail(SQF_ERR_UNSUPPORTED, "%s: the 6-bit low layout is built for one weight set, a "
-                "bf16 branch and the channel-split format", who);
+  if (low_kblocked(wt->low) && (wt->groups != 1 || wt->branch != SQF_BF16 || wt->sq_nnz != 0))
+    return fail(SQF_ERR_UNSUPPORTED, "%s: the K-blocked low layouts (E2M3, MXFP4) are built for "
+                "one weight set, a bf16 branch and the channel-split format", who);
   if (wt->k_low > kMaxKLow)
     return fail(SQF_ERR_SHAPE, "%s: k_low=%lld exceeds %lld", who, (long long)wt->k_low,
                 (long long)kMaxKLow);
@@ -104,7 +104,15 @@ sqf_status check_weights(const sqf_weights* wt, const char* who) {
   if (wt->k_low > 0 && !wt->w_low) return fail(SQF_ERR_INVALID_ARG, "%s: w_low is NULL", who);
   if (wt->k_low > 0 && !aligned16(wt->w_low))
     return fail(SQF_ERR_ALIGN, "%s: w_low must be 16-byte aligned", who);
-  if (!wt->s_w) return fail(SQF_ERR_INVALID_ARG, "%s: s_w is NULL", who);
+  if (wt->low == SQF_MXFP4) {
+    if (wt->k_low > 0 && !wt->s_wb) return fail(SQF_ERR_INVALID_ARG, "%s: s_wb is NULL", who);
+    if (wt->k_low > 0 && !aligned16(wt->s_wb))
+      return fail(SQF_ERR_ALIGN, "%s: s_wb must be 16-byte aligned", who);
+    if (mx_scale_bytes(wt->k_low, wt->n) > kMaxOperandBytes)
+      return fail(SQF_ERR_SHAPE, "%s: the weight scales exceed 2 GiB", who);
+  } else if (!wt->s_w) {
+    return fail(SQF_ERR_INVALID_ARG, "%s: s_w is NULL", who);
+  }
   if (wt->k_out > 0 && !wt->w_out) return fail(SQF_ERR_INVALID_ARG, "%s: w_out is NULL", who);
   if (wt->k_out > 0 && !aligned16(wt->w_out))
     return fail(SQF_ERR_ALIGN, "%s: w_out must be 16-byte aligned", who);
@@ -139,12 +147,11 @@ sqf_status check_acts(const sqf_acts* a, const char* who) {
   if (a->m < 0 || a->k_low < 0 || a->k_out < 0 || a->k_low + a->k_out < 1)
     return fail(SQF_ERR_SHAPE, "%s: bad activation shape m=%lld k_low=%lld k_out=%lld", who,
                 (long long)a->m, (long long)a->k_low, (long long)a->k_out);
-  if (a->low == SQF_MXFP4)
-    return fail(SQF_ERR_UNSUPPORTED, "%s: low dtype %d is not available", who, a->low);
-  if (a->low != SQF_I4X2 && a->low != SQF_I8 && a->low != SQF_I4_E2M3)
+  if (a->low != SQF_I4X2 && a->low != SQF_I8 && a->low != SQF_I4_E2M3 && a->low != SQF_MXFP4)
     return fail(SQF_ERR_INVALID_ARG, "%s: bad low dtype %d", who, a->low);
-  if (a->low == SQF_I4_E2M3 && a->branch != SQF_BF16)
-    return fail(SQF_ERR_UNSUPPORTED, "%s: the 6-bit low layout comes with a bf16 branch", who);
+  if (low_kblocked(a->low) && a->branch != SQF_BF16)
+    return fail(SQF_ERR_UNSUPPORTED, "%s: the K-blocked low layouts (E2M3, MXFP4) come with a "
+                "bf16 branch", who);
   if (!branch_ok(a->branch))
     return fail(SQF_ERR_INVALID_ARG, "%s: bad branch dtype %d", who, a->branch);
   if (a->k_low > kMaxKLow)
@@ -160,7 +167,13 @@ sqf_status check_acts(const sqf_acts* a, const char* who) {
     if (a->k_low > 0 && !a->x_low) return fail(SQF_ERR_INVALID_ARG, "%s: x_low is NULL", who);
     if (a->k_low > 0 && !aligned16(a->x_low))
       return fail(SQF_ERR_ALIGN, "%s: x_low must be 16-byte aligned", who);
-    if (!a->s_x) return fail(SQF_ERR_INVALID_ARG, "%s: s_x is NULL", who);
+    if (a->low == SQF_MXFP4) {
+      if (a->k_low > 0 && !a->s_xb) return fail(SQF_ERR_INVALID_ARG, "%s: s_xb is NULL", who);
+      if (a->k_low > 0 && !aligned16(a->s_xb))
+        return fail(SQF_ERR_ALIGN, "%s: s_xb must be 16-byte aligned", who);
+    } else if (!a->s_x) {
+      return fail(SQF_ERR_INVALID_ARG, "%s: s_x is NULL", who);
+    }
     if (a->k_out > 0 && !a->x_out) return fail(SQF_ERR_INVALID_ARG, "%s: x_out is NULL", who);
     if (a->k_out > 0 && !aligned16(a->x_out))
       return fail(SQF_ERR_ALIGN, "%s: x_out must be 16-byte aligned", who);
@@ -168,7 +181,8 @@ sqf_status check_acts(const sqf_acts* a, const char* who) {
       return fail(SQF_ERR_INVALID_ARG, "%s: s_xo is required for a scaled branch", who);
   }
   if (low_rows(a->m, a->low) * a->ldk > kMaxOperandBytes ||
-      a->m * a->ldo * branch_esz(a->branch) > kMaxOperandBytes)
+      a->m * a->ldo * branch_esz(a->branch) > kMaxOperandBytes ||
+      (a->low == SQF_MXFP4 && mx_scale_bytes(a->k_low, a->m) > kMaxOperandBytes))
     return fail(SQF_ERR_SHAPE, "%s: an activation operand exceeds 2 GiB", who);
   return SQF_OK;
 }
@@ -185,7 +199,7 @@ sqf_status quantize_common(const void* x, int32_t x_dtype, int64_t ldx, int64_t 
     return fail(SQF_ERR_INVALID_ARG, "%s: x_dtype must be SQF_F32 or SQF_BF16", who);
   const int64_t k = a->k_low + a->k_out;
   if (k > 65536) return fail(SQF_ERR_SHAPE, "%s: k=%lld exceeds 65536", who, (long long)k);
-  if (sqf::act_split_lds_bytes(a->ldk, a->k_out) > 160 * 1024)
+  if (sqf::act_split_lds_bytes(a->ldk, a->k_out, a->low) > 160 * 1024)
     return fail(SQF_ERR_SHAPE, "%s: k_low=%lld, k_out=%lld exceed the kernel's LDS staging", who,
                 (long long)a->k_low, (long long)a->k_out);
   if (ldx < k) return fail(SQF_ERR_SHAPE, "%s: ldx=%lld < k=%lld", who, (long long)ldx, (long long)k);
@@ -202,8 +216,9 @@ sqf_status quantize_common(const void* x, int32_t x_dtype, int64_t ldx, int64_t 
   if (grouped && a->low != SQF_I4X2)
     return fail(SQF_ERR_UNSUPPORTED, "%s: grouped activations are packed int4 only", who);
   sqf::ActArgs args{x, ldx, map, row_off, a->m, k, a->k_low, a->k_out, sqf_pad_k_low(a->k_low),
-                    a->ldk, a->ldo, a->low == SQF_I4_E2M3 ? sqf_pad_rows(a->m) : 0,
-                    (int32_t)(grouped ? groups : 1), a->x_low, a->s_x, (uint8_t*)a->x_out, a->s_xo};
+                    a->ldk, a->ldo, low_kblocked(a->low) ? sqf_pad_rows(a->m) : 0,
+                    (int32_t)(grouped ? groups : 1), a->x_low, a->s_x, (uint8_t*)a->x_out, a->s_xo,
+                    a->s_xb};
   return hip_status(
       sqf::launch_act_split(args, x_dtype, a->low, a->branch, grouped, ragged, (hipStream_t)stream),
       who);
@@ -263,14 +278,18 @@ sqf_status dual_gemm_impl(const sqf_acts* a, const sqf_weights* w, void* y, bool
   }
   if (acc_sp_dbg || acc_out_dbg)
     return fail(SQF_ERR_INVALID_ARG, "%s: acc_sp/acc_out debug outputs need the weight-side format", who);
-  if (w->low == SQF_I4_E2M3) {
+  if (low_kblocked(w->low)) {
     if (tile != SQF_TILE_AUTO && tile != SQF_TILE_256)
-      return fail(SQF_ERR_UNSUPPORTED, "%s: the 6-bit low path has 256x256 tiles only", who);
-    sqf::Gemm6Args ga{a->x_low, a->s_x, (const uint8_t*)a->x_out, w->w_low, w->s_w,
-                      (const uint8_t*)w->w_out, (float*)y, acc_low_dbg, a->m, w->n,
+      return fail(SQF_ERR_UNSUPPORTED, "%s: the K-blocked low paths have 256x256 tiles only", who);
+    if (w->low == SQF_MXFP4 && acc_low_dbg)
+      return fail(SQF_ERR_UNSUPPORTED, "%s: the MXFP4 low path has no integer accumulators", who);
+    sqf::Gemm6Args ga{a->x_low, a->s_x, a->s_xb, (const uint8_t*)a->x_out, w->w_low, w->s_w,
+                      w->s_wb, (const uint8_t*)w->w_out, (float*)y, acc_low_dbg, a->m, w->n,
                       sqf_pad_rows(a->m), sqf_pad_rows(w->n), w->ldo * 2, ldy,
                       (int32_t)(sqf_pad_k_low(w->k_low) / 128), (int32_t)(w->ldo / 32)};
-    return hip_status(sqf::launch_gemm6(ga, debug, ybf16, (hipStream_t)stream), who);
+    return hip_status(sqf::launch_gemm6(ga, w->low == SQF_MXFP4 ? sqf::kMXFP4 : sqf::kI4E2M3, debug,
+                                        ybf16, (hipStream_t)stream),
+                      who);
   }
   const int64_t ldo_b = w->ldo * branch_esz(w->branch);
   sqf::GemmArgs ga{a->x_low, a->s_x, (const uint8_t*)a->x_out, a->s_xo, w->w_low, w->s_w,
@@ -296,6 +315,8 @@ sqf_status grouped_impl(const sqf_acts* a, const sqf_weights* w, int64_t groups,
   if (groups < 1 || w->groups != groups || !row_off)
     return fail(SQF_ERR_INVALID_ARG, "%s: need groups >= 1 == w->groups and row_off", who);
   if (w->sq_nnz > 0) return fail(SQF_ERR_UNSUPPORTED, "%s: channel-split format only", who);
+  if (w->low != SQF_I4X2)
+    return fail(SQF_ERR_UNSUPPORTED, "%s: grouped weights are packed int4 only", who);
   if (a->m == 0) return SQF_OK;
   const int64_t ldo_b = w->ldo * branch_esz(w->branch);
   // 256x256 tiles when the groups average 384 rows or more (bf16 branch),
@@ -381,8 +402,8 @@ sqf_status sqf_pack_weights(const float* w, const int32_t* map, const float* hdi
                   (long long)wt->k_low);
   }
   sqf::PackArgs a{w, map, hdiag, wt->k, wt->n, wt->k_low, wt->k_out, wt->ldk, wt->ldo,
-                  wt->sq_nnz, wt->low == SQF_I4_E2M3 ? sqf_pad_rows(wt->n) : 0, wt->w_low, wt->s_w,
-                  (uint8_t*)wt->w_out, wt->s_wo, wt->sq_val, wt->s_w8};
+                  wt->sq_nnz, low_kblocked(wt->low) ? sqf_pad_rows(wt->n) : 0, wt->w_low, wt->s_w,
+                  wt->s_wb, (uint8_t*)wt->w_out, wt->s_wo, wt->sq_val, wt->s_w8};
   return hip_status(sqf::launch_pack(a, wt->branch, wt->low, wt->groups, (hipStream_t)stream), who);
 }
 

@@ -21,7 +21,7 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 constexpr int kWave = 64;
 
 // Status codes mirrored from the public header (kept in sync by the host code).
-enum : int { kBF16 = 1, kFP8 = 2, kI8 = 3, kI4X2 = 4, kI4E2M3 = 5, kF32 = 0 };
+enum : int { kBF16 = 1, kFP8 = 2, kI8 = 3, kI4X2 = 4, kI4E2M3 = 5, kMXFP4 = 6, kF32 = 0 };
 
 // Four int4 codes, one per byte (two's complement, |c| <= 7), as four 6-bit
 // OCP E2M3 fields holding c/8 (the subnormal: sign << 5 | |c|), packed into
@@ -36,6 +36,28 @@ __device__ __forceinline__ uint32_t e2m3_fields4(uint32_t q) {
 }
 
 __device__ __forceinline__ uint32_t f32_bits(float f) { return __float_as_uint(f); }
+
+// OCP MXFP4.  E8M0 scale byte of a 32-value block from its max |v| (fp32
+// bits): X = floor(log2 max) - 2 (2 = exponent of the largest E2M1 value, 6),
+// clamped at -127; the byte is X + 127 = max(biased exponent - 2, 0) (a zero
+// or subnormal max gives 0).
+__device__ __forceinline__ uint32_t mx_scale_byte(uint32_t amax_bits) {
+  const int e = (int)(amax_bits >> 23) - 2;
+  return (uint32_t)(e > 0 ? e : 0);
+}
+// 2^-X for scale byte b (b <= 252: a normal float, exact scaling)
+__device__ __forceinline__ float mx_inv_scale(uint32_t b) { return __uint_as_float((254u - b) << 23); }
+// E2M1 code (sign bit 3) of v * inv: the nearest of 0, 0.5, 1, 1.5, 2, 3, 4,
+// 6 with ties to the even code, saturating at 6.  The code is the count of
+// midpoints below |t|; at a midpoint the even neighbour wins (down at 0.25,
+// 1.25, 2.5, 5; up at 0.75, 1.75, 3.5).  A zero code has no sign.
+__device__ __forceinline__ uint32_t e2m1_code(float v, float inv) {
+  const float t = fabsf(v) * inv;
+  uint32_t c = (uint32_t)(t > 0.25f) + (uint32_t)(t >= 0.75f) + (uint32_t)(t > 1.25f) +
+               (uint32_t)(t >= 1.75f) + (uint32_t)(t > 2.5f) + (uint32_t)(t >= 3.5f) + (uint32_t)(t > 5.0f);
+  if (c != 0u && v < 0.0f) c |= 8u;
+  return c;
+}
 
 // fp32 -> bf16 bits, round to nearest even (finite inputs).
 __device__ __forceinline__ uint32_t bf16_rne(float f) {

@@ -11,9 +11,10 @@ struct PackArgs {
   const int32_t* map;  // [groups][k]
   const float* hdiag;  // [k] (weight-side format)
   int64_t k, n, k_low, k_out, ldk, ldo, nnz;
-  int64_t rows_pad;  // K-blocked 6-bit layout: rows of each K block (0 otherwise)
+  int64_t rows_pad;  // K-blocked layouts: rows of each K block (0 otherwise)
   uint8_t* w_low;
   float* s_w;
+  uint8_t* s_wb;  // MXFP4: E8M0 block scales, K-blocked [pad/128][rows_pad/64][4][16][4]
   uint8_t* w_out;
   float* s_wo;
   int8_t* sq_val;
@@ -32,6 +33,7 @@ struct ActArgs {
   float* s_x;
   uint8_t* x_out;
   float* s_xo;
+  uint8_t* s_xb;  // MXFP4: E8M0 block scales, K-blocked [pad/128][rows_pad/64][4][16][4]
 };
 
 struct GemmArgs {
@@ -73,11 +75,13 @@ struct SqArgs {
 // The dual GEMM with int4 codes in 6-bit E2M3 fields (K-blocked) and a bf16
 // branch, on the FP6 matrix unit; one 256 x 256 tile shape.
 struct Gemm6Args {
-  const uint8_t* x6;  // [s_low][x_rows][96]
-  const float* s_x;
+  const uint8_t* x6;     // K-blocked low codes: E2M3 [s_low][x_rows][96] or E2M1 [s_low][x_rows][64]
+  const float* s_x;      // E2M3: per-token scale
+  const uint8_t* x_sc;   // E2M1: E8M0 block scales [s_low][x_rows/64][4][16][4]
   const uint8_t* x_out;  // bf16 [m][ldo]
-  const uint8_t* w6;     // [s_low][w_rows][96]
+  const uint8_t* w6;
   const float* s_w;
+  const uint8_t* w_sc;
   const uint8_t* w_out;  // bf16 [n][ldo]
   float* y;
   int32_t* acc_dbg;
@@ -93,12 +97,14 @@ hipError_t launch_pack(const PackArgs& a, int branch, int low, int groups, hipSt
 hipError_t launch_act_split(const ActArgs& a, int x_dtype, int low, int branch, bool grouped,
                             bool ragged, hipStream_t s);
 // dynamic LDS bytes the activation kernel needs for one block
-size_t act_split_lds_bytes(int64_t ldk, int64_t k_out);
+size_t act_split_lds_bytes(int64_t ldk, int64_t k_out, int low);
 // cfg: 0 = 256x256 tiles (8 waves), 1 = 128x128 (4 waves), 2 = 64x64 (4 waves)
 // ybf16: Y written as bf16 (not together with debug)
 hipError_t launch_dual_gemm(const GemmArgs& a, int branch, bool grouped, bool debug, int cfg,
                             hipStream_t s, bool ybf16);
 hipError_t launch_sq_gemm(const SqArgs& a, bool debug, hipStream_t s);
-hipError_t launch_gemm6(const Gemm6Args& a, bool debug, bool ybf16, hipStream_t s);
+// low: kI4E2M3 (int4 codes as E2M3 subnormals, exact sums; debug dumps them)
+// or kMXFP4 (E2M1 with E8M0 block scales; no debug output)
+hipError_t launch_gemm6(const Gemm6Args& a, int low, bool debug, bool ybf16, hipStream_t s);
 
 }  // namespace sqf

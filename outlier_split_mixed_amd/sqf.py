@@ -30,7 +30,7 @@ SQF_F32, SQF_BF16, SQF_FP8_E4M3, SQF_I8, SQF_I4X2, SQF_I4_E2M3, SQF_MXFP4 = rang
 DTYPES = {"f32": SQF_F32, "bf16": SQF_BF16, "fp8": SQF_FP8_E4M3, "i8": SQF_I8, "i4": SQF_I4X2,
           "i4e2m3": SQF_I4_E2M3, "mxfp4": SQF_MXFP4}
 TILES = {"auto": -1, "256": 0, "128": 1, "64": 2}
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 P = ctypes.c_void_p
 I64 = ctypes.c_int64
@@ -131,13 +131,21 @@ def low_ldk(k_low: int, low: str) -> int:
 
 
 def _low_tensor(rows: int, k_low: int, low: str, device, zero: bool):
-    """The low operand in its layout: [rows][ldk], or for the K-blocked 6-bit
-    layout [pad/128][P/16][4][16][24] with P = sqf_pad_rows(rows)."""
+    """The low operand in its layout: [rows][ldk], or K-blocked with
+    P = sqf_pad_rows(rows): 6-bit E2M3 [pad/128][P/16][4][16][24], MXFP4 E2M1
+    pairs [pad/128][P/16][4][16][16]."""
     mk = torch.zeros if zero else torch.empty
-    if low == "i4e2m3":
-        p = sqf_pad_k_low(k_low)
-        return mk((p // 128, sqf_pad_rows(rows) // 16, 4, 16, 24), dtype=torch.uint8, device=device)
+    p = sqf_pad_k_low(k_low)
+    if low in ("i4e2m3", "mxfp4"):
+        piece = 24 if low == "i4e2m3" else 16
+        return mk((p // 128, sqf_pad_rows(rows) // 16, 4, 16, piece), dtype=torch.uint8, device=device)
     return mk((rows, low_ldk(k_low, low)), dtype=torch.uint8, device=device)
+
+
+def _mx_scales(rows: int, k_low: int, device):
+    """MXFP4 E8M0 block scales, K-blocked [pad/128][P/64][4][16][4]."""
+    p = sqf_pad_k_low(k_low)
+    return torch.zeros((p // 128, sqf_pad_rows(rows) // 64, 4, 16, 4), dtype=torch.uint8, device=device)
 
 
 # ------------------------------------------------------------------ buffers
@@ -204,13 +212,13 @@ def alloc_weights(k, n, k_out, branch="bf16", groups=1, sq_nnz=0, sq_bank=0, low
                 sq_bank=sq_bank, low=low)
     g = groups
     t = w.t
-    if low == "i4e2m3":
-        assert g == 1, "the K-blocked 6-bit layout is built for one weight set"
+    if low in ("i4e2m3", "mxfp4"):
+        assert g == 1, "the K-blocked layouts are built for one weight set"
         t["w_low"] = _low_tensor(n, w.k_low, low, device, zero=True)
     else:
         t["w_low"] = torch.zeros((g, n, w.ldk), dtype=torch.uint8, device=device)
     if low == "mxfp4":
-        t["s_wb"] = torch.zeros((g, n, sqf_pad_k_low(w.k_low) // 32), dtype=torch.uint8, device=device)
+        t["s_wb"] = _mx_scales(n, w.k_low, device)
     else:
         t["s_w"] = torch.zeros((g, n), dtype=torch.float32, device=device)
     t["w_out"] = torch.zeros((g, n, w.ldo), dtype=_BR_TORCH[branch], device=device)
@@ -225,7 +233,7 @@ def alloc_acts(m, k_low, k_out, low="i4", branch="bf16", device="cuda") -> Acts:
     a = Acts(m=m, k_low=k_low, k_out=k_out, low=low, branch=branch)
     a.t["x_low"] = _low_tensor(m, k_low, low, device, zero=False)
     if low == "mxfp4":
-        a.t["s_xb"] = torch.empty((m, sqf_pad_k_low(k_low) // 32), dtype=torch.uint8, device=device)
+        a.t["s_xb"] = _mx_scales(m, k_low, device)
     else:
         a.t["s_x"] = torch.empty(m, dtype=torch.float32, device=device)
     a.t["x_out"] = torch.empty((m, a.ldo), dtype=_BR_TORCH[branch], device=device)

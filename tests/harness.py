@@ -165,3 +165,77 @@ def run_layer(sqf, lay, k_out, branch="bf16", x_dtype="bf16", rows=None, check_s
         stats["band_rows"] = len(band)
         stats["band_max_rel_err"] = check_band(acc.cpu().numpy(), yf, o_a, o_w, band, lay.name)
     return stats, y
+
+
+# ---------------------------------------------------------------- MXFP4 low path
+E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0])
+
+
+def _mx_rows(codes_kb, scales_kb, rows):
+    """K-blocked MXFP4 storage -> (codes [P][pad/2], scales [P][pad/32]) by row."""
+    nkb = codes_kb.shape[0]
+    c = codes_kb.transpose(1, 3, 0, 2, 4).reshape(-1, nkb * 64)[:rows]
+    s = scales_kb.transpose(1, 4, 3, 0, 2).reshape(-1, nkb * 4)[:rows]
+    return c, s
+
+
+def _mx_dequant(codes, scales, k_low):
+    """Packed E2M1 rows and their E8M0 scales -> float64 values [rows][k_low]."""
+    nib = np.stack([codes & 0xF, codes >> 4], -1).reshape(codes.shape[0], -1)[:, :k_low]
+    sc = np.repeat(scales.astype(np.int64), 32, axis=1)[:, :k_low]
+    return E2M1[nib] * np.ldexp(1.0, sc - 127)
+
+
+def run_layer_mx(sqf, lay, k_out, x_dtype="bf16", rows=None, band=None, check_select=True):
+    """The MXFP4 low path for one layer on both sides: selection, the K-blocked
+    codes and block scales of weights and activations (bit for bit, real rows),
+    the bf16 branch, and Y on the sampled rows (oracle, fp64) and on the band
+    rows (the plain product of the dequantised operands already matched bit
+    for bit, fp64)."""
+    stats = {}
+    x_cal = torch.from_numpy(lay.x_cal).cuda()
+    w = torch.from_numpy(lay.w).cuda()
+    idx, mp, score, hdiag = sqf.sqf_select_channels(x_cal, w, k_out)
+    wts = sqf.sqf_pack_weights(w, mp, low="mxfp4")
+    ox, ofmt, xt = x_inputs(lay, x_dtype)
+    acts = sqf.alloc_acts(lay.m, lay.k - k_out, k_out, low="mxfp4")
+    sqf.sqf_quantize_split_act(xt, mp, acts)
+    y = sqf.sqf_dual_gemm(acts, wts)
+    torch.cuda.synchronize()
+    del w, x_cal
+    o_idx, o_mp, _, _ = oracle.select_channels(lay.x_cal, lay.w, k_out)
+    if check_select:
+        assert np.array_equal(mp.cpu().numpy(), o_mp), "channel map differs"
+    o_w = oracle.pack_weights_mx(lay.w, o_mp)
+    wc, ws = oracle.mx_storage(o_w["w_low"], o_w["s_wb"], oracle.pad_rows(lay.n))
+    assert np.array_equal(wts.t["w_low"].cpu().numpy(), wc), "MXFP4 w_low differs"
+    assert np.array_equal(wts.t["s_wb"].cpu().numpy(), ws), "MXFP4 weight scales differ"
+    if k_out:
+        assert np.array_equal(wts.t["w_out"][0].cpu().numpy().view(np.uint16), o_w["w_out"]), \
+            "branch weights differ"
+    o_a = oracle.quantize_split_act_mx(ox, o_mp, x_fmt=ofmt)
+    if o_a["pad"]:
+        gc, gs = _mx_rows(acts.t["x_low"].cpu().numpy(), acts.t["s_xb"].cpu().numpy(), lay.m)
+        assert np.array_equal(gc, o_a["x_low"]), "MXFP4 x_low differs"
+        assert np.array_equal(gs, o_a["s_xb"]), "MXFP4 activation scales differ"
+    if k_out:
+        assert np.array_equal(acts.t["x_out"].cpu().numpy().view(np.uint16), o_a["x_out"]), \
+            "branch activations differ"
+    if rows is None:
+        rows = np.arange(lay.m, dtype=np.int64)
+    o_y = oracle.dual_gemm_mx(o_a, o_w, rows=rows)
+    yg = y.cpu().numpy()
+    stats["max_rel_err"] = assert_rows_close(yg[rows], o_y, lay.name + " (mxfp4)")
+    stats["rows_checked"] = len(rows)
+    if band is not None:
+        k_low = o_a["k_low"]
+        xq = _mx_dequant(o_a["x_low"][band], o_a["s_xb"][band], k_low)
+        wq = _mx_dequant(o_w["w_low"], o_w["s_wb"], k_low)
+        yb = xq @ wq.T
+        if k_out:
+            xo = synth.bf16_bits_to_f32(o_a["x_out"][band]).astype(np.float64)
+            wo = synth.bf16_bits_to_f32(o_w["w_out"]).astype(np.float64)
+            yb += xo @ wo.T
+        stats["band_rows"] = len(band)
+        stats["band_max_rel_err"] = assert_rows_close(yg[band], yb, lay.name + " (mxfp4 band)")
+    return stats, y

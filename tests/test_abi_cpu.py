@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported(sqf):
 
 
 def test_abi_version_and_padding(sqf):
-    assert sqf.sqf_abi_version() == 2
+    assert sqf.sqf_abi_version() == 3
     assert sqf.sqf_pad_rows(0) == 0 and sqf.sqf_pad_rows(1) == 256 and sqf.sqf_pad_rows(4096) == 4096
     assert sqf.sqf_pad_rows(300) == 512 and sqf._lib.sqf_pad_rows(-1) == -1
     assert sqf.sqf_pad_k_low(0) == 0 and sqf.sqf_pad_k_low(1) == 256
@@ -233,6 +233,49 @@ def test_explicit_options_argument_errors(sqf):
              sqf.TILES["64"], None, None) == 3  # grouped tiles are 256 or 128
     assert g(ctypes.byref(a), ctypes.byref(w), 4, mem(), mem(), sqf.SQF_F32, 256, 9, None,
              None) == 1
+    assert sqf.sqf_last_error() != ""
+
+
+def _mx_pair(sqf, mem, m=64, k=512, k_out=32, n=256):
+    k_low = k - k_out
+    a = _acts(sqf, mem, m=m, k=k, k_out=k_out)
+    a.low, a.s_x, a.s_xb = sqf.SQF_MXFP4, None, mem()
+    w = _weights(sqf, mem, k=k, n=n, k_out=k_out)
+    w.low, w.s_w, w.s_wb = sqf.SQF_MXFP4, None, mem()
+    assert a.ldk == w.ldk == sqf.sqf_pad_k_low(k_low) // 2
+    return a, w
+
+
+def test_mxfp4_contract_errors(sqf):
+    """The MXFP4 low path: block scales required and 16-byte aligned, one
+    weight set, a bf16 branch, the 256x256 tile only, no integer debug
+    accumulators, no grouped form -- all refused before any launch."""
+    mem = FakeMem()
+    ex = lambda a, w, y, yd, ldy, tile, dbg: sqf._lib.sqf_dual_gemm_ex(
+        ctypes.byref(a), ctypes.byref(w), y, yd, ldy, tile, dbg, None, None, None)
+    a, w = _mx_pair(sqf, mem)
+    assert ex(a, w, mem(), sqf.SQF_F32, 256, sqf.TILES["256"], mem()) == 3  # debug accumulators
+    assert ex(a, w, mem(), sqf.SQF_F32, 256, sqf.TILES["128"], None) == 3  # one tile shape
+    w.s_wb = None
+    assert ex(a, w, mem(), sqf.SQF_F32, 256, -1, None) == 1
+    w.s_wb = mem(misalign=4)
+    assert ex(a, w, mem(), sqf.SQF_F32, 256, -1, None) == 5
+    a, w = _mx_pair(sqf, mem)
+    a.s_xb = None
+    assert ex(a, w, mem(), sqf.SQF_F32, 256, -1, None) == 1
+    a, w = _mx_pair(sqf, mem)
+    w.groups = 2
+    assert sqf._lib.sqf_pack_weights(mem(), mem(), None, ctypes.byref(w), None) == 3
+    a, w = _mx_pair(sqf, mem)
+    assert sqf._lib.sqf_dual_gemm_grouped(ctypes.byref(a), ctypes.byref(w), 1, mem(), mem(), 256,
+                                          None, None) == 3
+    a, w = _mx_pair(sqf, mem)
+    w.branch, w.ldo, w.s_wo = sqf.SQF_FP8_E4M3, 128, mem()
+    assert sqf._lib.sqf_pack_weights(mem(), mem(), None, ctypes.byref(w), None) == 3
+    a, w = _mx_pair(sqf, mem)
+    w.low = sqf.SQF_I4X2  # storages disagree
+    w.s_w = mem()
+    assert ex(a, w, mem(), sqf.SQF_F32, 256, -1, None) == 1
     assert sqf.sqf_last_error() != ""
 
 

@@ -22,7 +22,8 @@ import torch
 import oracle
 from outlier_split_mixed_amd import synth
 
-from harness import assert_rows_close, f32_bits_equal, run_layer, sample_rows, tile_band_rows, x_inputs
+from harness import (assert_rows_close, f32_bits_equal, run_layer, run_layer_mx, sample_rows,
+                     tile_band_rows, x_inputs)
 from test_gpu_parity import _grouped_check
 
 pytestmark = pytest.mark.gpu
@@ -67,6 +68,25 @@ def test_llama3_70b_fraction_sweep(sqf, frac, low):
     lay = synth.llama3_70b(0, frac)
     st, _ = run_layer(sqf, lay, lay.k_out, rows=sample_rows(lay.m, 8, seed=20 + frac), low=low)
     _log(lay.name, f"1/{frac}", low, st)
+
+
+@pytest.mark.parametrize("layer", [0, 1, 2])
+def test_llama3_70b_layers_mxfp4(sqf, layer):
+    """The MXFP4 low path at full size: every code and block scale, sampled
+    rows against the oracle, a whole tile band plus the last tile against the
+    product of the dequantised operands."""
+    lay = synth.llama3_70b(layer, 16)
+    st, _ = run_layer_mx(sqf, lay, lay.k_out, rows=sample_rows(lay.m, 4, seed=30 + layer),
+                         band=tile_band_rows(lay.m))
+    _log(lay.name, "mxfp4", st)
+
+
+@pytest.mark.parametrize("layer", [0, 1, 2])
+def test_llama3_8b_layers_mxfp4(sqf, layer):
+    lay = synth.llama3_8b(layer)
+    st, _ = run_layer_mx(sqf, lay, lay.k_out, rows=sample_rows(lay.m, 6, seed=40 + layer),
+                         band=tile_band_rows(lay.m))
+    _log(lay.name, "mxfp4", st)
 
 
 @pytest.fixture(scope="module")

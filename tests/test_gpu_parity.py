@@ -14,7 +14,7 @@ import torch
 import oracle
 from outlier_split_mixed_amd import synth
 
-from harness import assert_rows_close, f32_bits_equal, run_layer, x_inputs
+from harness import assert_rows_close, f32_bits_equal, run_layer, run_layer_mx, x_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -545,3 +545,63 @@ def test_e2m3_matches_packed_int4_kernel_bit_for_bit(sqf):
     assert ei.value.status == sqf.SQF_ERR_UNSUPPORTED
     with pytest.raises(sqf.SqfError):
         sqf.sqf_dual_gemm(a6, w4)  # activations and weights in different storage
+
+
+# ------------------------------------------------------------------ MXFP4 low path
+@pytest.mark.parametrize("x_dtype", ["bf16", "f32"])
+def test_mxfp4_low_path_ragged(sqf, x_dtype):
+    """MXFP4 codes and block scales (K-blocked) from the packer and the
+    activation kernel against the oracle bit for bit; Y within tolerance on
+    every row.  M, N and K_low past any tile multiple, K_out not a multiple
+    of the branch stage."""
+    lay = _ragged(m=300, k=1000, n=520, n_scaled=37, seed=111)
+    st, _ = run_layer_mx(sqf, lay, lay.k_out, x_dtype=x_dtype)
+    _print("mxfp4 ragged", x_dtype, st)
+
+
+@pytest.mark.parametrize("k_out_kind", ["none", "all", "half"])
+def test_mxfp4_extreme_fractions(sqf, k_out_kind):
+    lay = _ragged(m=260, k=640, n=300, n_scaled=40, seed=112)
+    k_out = {"none": 0, "all": lay.k, "half": lay.k // 2}[k_out_kind]
+    st, _ = run_layer_mx(sqf, lay, k_out, check_select=k_out not in (0, lay.k))
+    _print("mxfp4 k_out", k_out_kind, st)
+
+
+def test_mxfp4_block_scales_over_a_wide_range(sqf):
+    """Blocks whose magnitudes span 2^-140 .. 2^60 (fp32 subnormals, the
+    E8M0 clamp at -127, all-zero blocks, exact ties of the E2M1 grid): every
+    code and scale byte bit for bit, Y within tolerance."""
+    rng = np.random.default_rng(113)
+    lay = _ragged(m=520, k=1536, n=264, n_scaled=24, seed=113)
+    x = lay.x.astype(np.float64) * np.exp2(rng.integers(-140, 60, (lay.m, lay.k // 32)).repeat(32, 1))
+    x[rng.random(lay.m) < 0.1, :] = 0.0
+    x[:, 64:96] = 0.0  # a zero block in every row (before the permutation)
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0]) * 0.5
+    x[::7, :8] = ties
+    w = lay.w.astype(np.float64) * np.exp2(rng.integers(-30, 30, (lay.k // 32, lay.n)).repeat(32, 0))
+    lay2 = synth.Layer(name="wide", m=lay.m, k=lay.k, n=lay.n, k_out=lay.k_out,
+                       x=x.astype(np.float32), x_cal=lay.x_cal, w=w.astype(np.float32), scaled=lay.scaled)
+    st, _ = run_layer_mx(sqf, lay2, lay2.k_out, x_dtype="f32")
+    _print("mxfp4 wide", st)
+
+
+def test_mxfp4_bf16_output_and_errors(sqf):
+    """bf16 Y is the nearest-even rounding of the fp32 Y; the MXFP4 path has
+    one tile shape and no integer accumulators."""
+    lay = _ragged(m=512, k=2048, n=768, n_scaled=128, seed=114)
+    x_cal = torch.from_numpy(lay.x_cal).cuda()
+    w = torch.from_numpy(lay.w).cuda()
+    _, mp, _, _ = sqf.sqf_select_channels(x_cal, w, lay.k_out)
+    wm = sqf.sqf_pack_weights(w, mp, low="mxfp4")
+    am = sqf.alloc_acts(lay.m, lay.k - lay.k_out, lay.k_out, low="mxfp4")
+    sqf.sqf_quantize_split_act(x_inputs(lay, "bf16")[2], mp, am)
+    y = sqf.sqf_dual_gemm(am, wm)
+    yb = sqf.sqf_dual_gemm(am, wm, y_dtype="bf16")
+    y2 = sqf.sqf_dual_gemm(am, wm, tile="256")
+    torch.cuda.synchronize()
+    assert torch.equal(yb.view(torch.int16), y.to(torch.bfloat16).view(torch.int16))
+    assert torch.equal(y2.view(torch.int32), y.view(torch.int32))
+    for kw in (dict(tile="128"), dict(debug=True)):
+        with pytest.raises(sqf.SqfError) as ei:
+            sqf.sqf_dual_gemm(am, wm, **kw)
+        assert ei.value.status == sqf.SQF_ERR_UNSUPPORTED
