@@ -211,6 +211,20 @@ sqf_status sqf_select_channels(const float* x_cal, int64_t m_cal, int64_t k, con
                                int64_t n, int64_t k_out, int32_t* idx_out, int32_t* map_out,
                                double* score_out, float* hdiag_out, void* stream);
 
+/* a0 without allocation, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same channel choice and outputs as sqf_select_channels
+ * (bit for bit), with the scores kept in a static array of the library
+ * (65536 fp64 values per GPU, held until the process ends) instead of
+ * score_out or a stream-ordered workspace.  No call allocates or frees
+ * memory.  k <= 65536, else SQF_ERR_SHAPE; other checks and the asynchrony
+ * as sqf_select_channels; `stream` must belong to the current device.  Every
+ * call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (other streams, other threads) race and must be ordered by the caller. */
+sqf_status sqf_select_channels_noalloc(const float* x_cal, int64_t m_cal, int64_t k,
+                                       const float* w, int64_t n, int64_t k_out, int32_t* idx_out,
+                                       int32_t* map_out, float* hdiag_out, void* stream);
+
 /* a1 -- offline weight conversion.  w: [groups][k][n] fp32, map: [groups][k]
  * (one map per group).  Fills every array of `wt` (shape fields must be set
  * and consistent with map).  Channel-split format ([OSC]): per output row,

@@ -7,11 +7,20 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/sqf.h"
 #include "sqf_device.h"
 #include "sqf_launch.h"
+
+// The allocation-free channel choice (sqf_select_channels_noalloc) keeps its
+// scores in this array: one copy per GPU, held from the library's first use
+// on that GPU until the process ends.  Host code never uses the array's name
+// as an address (on the host it is only a stand-in): the device address comes
+// from hipGetSymbolAddress, looked up once per device (scratch_scores below).
+constexpr int64_t kScratchScores = 65536;  // channels (512 KiB of fp64 scores)
+static __device__ __align__(256) double scratch[kScratchScores];
 
 namespace {
 
@@ -332,6 +341,46 @@ sqf_status grouped_impl(const sqf_acts* a, const sqf_weights* w, int64_t groups,
                     who);
 }
 
+sqf_status check_select(const float* x_cal, int64_t m_cal, int64_t k, const float* w, int64_t n,
+                        int64_t k_out, const int32_t* idx_out, const int32_t* map_out,
+                        const char* who) {
+  if (!x_cal || !w || !map_out)
+    return fail(SQF_ERR_INVALID_ARG, "%s: x_cal, w and map_out are required", who);
+  if (m_cal < 1 || n < 1 || k < 1 || k > 1048576)
+    return fail(SQF_ERR_SHAPE, "%s: need m_cal>=1, n>=1, 1<=k<=1048576 (got %lld, %lld, %lld)",
+                who, (long long)m_cal, (long long)n, (long long)k);
+  if (k_out < 0 || k_out > k)
+    return fail(SQF_ERR_SHAPE, "%s: k_out=%lld outside [0, k=%lld]", who, (long long)k_out,
+                (long long)k);
+  if (k_out > 0 && !idx_out) return fail(SQF_ERR_INVALID_ARG, "%s: idx_out is NULL", who);
+  return SQF_OK;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+double* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of the current device's `scratch`, looked up on the
+// first call on that device (with that device current).
+sqf_status scratch_scores(double** out, const char* who) {
+  int dev = -1;
+  sqf_status st = hip_status(hipGetDevice(&dev), who);
+  if (st != SQF_OK) return st;
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SQF_ERR_UNSUPPORTED, "%s: device %d beyond the %d this library tracks", who, dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    st = hip_status(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), who);
+    if (st != SQF_OK) return st;
+    if (!ptr) return fail(SQF_ERR_HIP, "%s: no device address for the score array", who);
+    g_scratch_ptr[dev] = (double*)ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SQF_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -361,15 +410,8 @@ sqf_status sqf_select_channels(const float* x_cal, int64_t m_cal, int64_t k, con
                                double* score_out, float* hdiag_out, void* stream) {
   g_err.clear();
   const char* who = "sqf_select_channels";
-  if (!x_cal || !w || !map_out)
-    return fail(SQF_ERR_INVALID_ARG, "%s: x_cal, w and map_out are required", who);
-  if (m_cal < 1 || n < 1 || k < 1 || k > 1048576)
-    return fail(SQF_ERR_SHAPE, "%s: need m_cal>=1, n>=1, 1<=k<=1048576 (got %lld, %lld, %lld)",
-                who, (long long)m_cal, (long long)n, (long long)k);
-  if (k_out < 0 || k_out > k)
-    return fail(SQF_ERR_SHAPE, "%s: k_out=%lld outside [0, k=%lld]", who, (long long)k_out,
-                (long long)k);
-  if (k_out > 0 && !idx_out) return fail(SQF_ERR_INVALID_ARG, "%s: idx_out is NULL", who);
+  sqf_status vst = check_select(x_cal, m_cal, k, w, n, k_out, idx_out, map_out, who);
+  if (vst != SQF_OK) return vst;
   hipStream_t s = (hipStream_t)stream;
   double* score = score_out;
   if (!score) {
@@ -386,6 +428,27 @@ sqf_status sqf_select_channels(const float* x_cal, int64_t m_cal, int64_t k, con
     if (st == SQF_OK) st = fst;
   }
   return st;
+}
+
+sqf_status sqf_select_channels_noalloc(const float* x_cal, int64_t m_cal, int64_t k,
+                                       const float* w, int64_t n, int64_t k_out, int32_t* idx_out,
+                                       int32_t* map_out, float* hdiag_out, void* stream) {
+  g_err.clear();
+  const char* who = "sqf_select_channels_noalloc";
+  sqf_status vst = check_select(x_cal, m_cal, k, w, n, k_out, idx_out, map_out, who);
+  if (vst != SQF_OK) return vst;
+  if (k > kScratchScores)
+    return fail(SQF_ERR_SHAPE, "%s: k=%lld exceeds the %lld channels of the library's static "
+                "score array (use sqf_select_channels)", who, (long long)k,
+                (long long)kScratchScores);
+  double* score = nullptr;
+  sqf_status st = scratch_scores(&score, who);
+  if (st != SQF_OK) return st;
+  // every score[c], c < k, is written by the first kernel before it is read:
+  // nothing left by an earlier call needs clearing
+  return hip_status(sqf::launch_select(x_cal, m_cal, k, w, n, k_out, idx_out, map_out, score,
+                                       hdiag_out, (hipStream_t)stream),
+                    who);
 }
 
 sqf_status sqf_pack_weights(const float* w, const int32_t* map, const float* hdiag,

@@ -63,6 +63,7 @@ _decl("sqf_pad_k_low", [I64], I64)
 _decl("sqf_pad_k_out", [I64, I32], I64)
 _decl("sqf_pad_rows", [I64], I64)
 _decl("sqf_select_channels", [P, I64, I64, P, I64, I64, P, P, P, P, P])
+_decl("sqf_select_channels_noalloc", [P, I64, I64, P, I64, I64, P, P, P, P])
 _decl("sqf_pack_weights", [P, P, P, ctypes.POINTER(sqf_weights), P])
 _decl("sqf_quantize_split_act", [P, I32, I64, P, ctypes.POINTER(sqf_acts), P])
 _decl("sqf_quantize_split_act_grouped", [P, I32, I64, I64, P, P, ctypes.POINTER(sqf_acts), P])
@@ -259,6 +260,27 @@ def sqf_select_channels(x_cal: torch.Tensor, w: torch.Tensor, k_out: int, stream
     _check(_lib.sqf_select_channels(_ptr(x_cal), m_cal, k, _ptr(w), n, k_out, _ptr(idx), _ptr(mp),
                                     _ptr(score), _ptr(hdiag), _stream(stream)))
     return idx[:k_out], mp, score, hdiag
+
+
+def sqf_select_channels_noalloc(x_cal: torch.Tensor, w: torch.Tensor, k_out: int, idx=None,
+                                mp=None, hdiag=None, stream=None):
+    """a0 through the allocation-free entry point: the scores live in the
+    library's static per-GPU array.  Output tensors may be passed in (the
+    call itself allocates nothing); returns (idx, map, hdiag)."""
+    assert x_cal.is_cuda and w.is_cuda and x_cal.dtype == torch.float32 and w.dtype == torch.float32
+    assert x_cal.is_contiguous() and w.is_contiguous()
+    m_cal, k = x_cal.shape
+    n = w.shape[1]
+    dev = x_cal.device
+    if idx is None:
+        idx = torch.empty(max(k_out, 1), dtype=torch.int32, device=dev)
+    if mp is None:
+        mp = torch.empty(k, dtype=torch.int32, device=dev)
+    if hdiag is None:
+        hdiag = torch.empty(k, dtype=torch.float32, device=dev)
+    _check(_lib.sqf_select_channels_noalloc(_ptr(x_cal), m_cal, k, _ptr(w), n, k_out, _ptr(idx),
+                                            _ptr(mp), _ptr(hdiag), _stream(stream)))
+    return idx[:k_out], mp, hdiag
 
 
 def sqf_pack_weights(w: torch.Tensor, mp: torch.Tensor, branch="bf16", hdiag=None, sq_nnz=0,

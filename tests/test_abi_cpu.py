@@ -26,7 +26,7 @@ def _declared_functions():
 
 def test_every_declared_symbol_is_exported(sqf):
     names = _declared_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     for name in names:
         assert hasattr(sqf._lib, name), name
 
@@ -158,6 +158,18 @@ def test_select_argument_errors(sqf):
     assert f(mem(), 4, 8, mem(), 4, 9, mem(), mem(), mem(), None, None) == 2
     assert f(mem(), 4, 8, mem(), 4, 2, None, mem(), mem(), None, None) == 1
     assert f(mem(), 4, 8, mem(), 4, 2, mem(), None, mem(), None, None) == 1  # map_out required
+
+
+def test_noalloc_select_argument_errors(sqf):
+    """The allocation-free channel choice: the shared checks, and k beyond
+    its static score array, fail before any device call."""
+    mem = FakeMem()
+    f = sqf._lib.sqf_select_channels_noalloc
+    assert f(None, 4, 8, mem(), 4, 2, mem(), mem(), None, None) == 1
+    assert f(mem(), 4, 8, mem(), 4, 9, mem(), mem(), None, None) == 2
+    assert f(mem(), 4, 8, mem(), 4, 2, mem(), None, None, None) == 1
+    assert f(mem(), 4, 65537, mem(), 4, 2, mem(), mem(), None, None) == 2
+    assert "65536" in sqf.sqf_last_error()
 
 
 def test_pack_argument_errors(sqf):
