@@ -78,9 +78,10 @@ def _declare(lib):
     lib.orc_quantize_vec.restype = ctypes.c_float
     lib.orc_pack_weights.argtypes = [P, I64, I64, P, I64, I64, I64, I64, INT, P, P, P, P]
     lib.orc_pack_weights.restype = None
-    lib.orc_sq_row.argtypes = [P, P, I64, I64, INT, P, P, P, P]
+    lib.orc_sq_row.argtypes = [P, P, I64, I64, I64, INT, P, P, P, P]
     lib.orc_sq_row.restype = None
-    lib.orc_pack_weights_sq.argtypes = [P, I64, I64, P, P, I64, I64, I64, I64, I64, P, P, P, P, P, P]
+    lib.orc_pack_weights_sq.argtypes = [P, I64, I64, P, P, I64, I64, I64, I64, I64, I64, P, P, P, P,
+                                        P, P]
     lib.orc_pack_weights_sq.restype = None
     lib.orc_e2m3_field_of_code.argtypes = [INT]
     lib.orc_e2m3_field_of_code.restype = ctypes.c_uint8
@@ -221,8 +222,17 @@ def pack_weights(w: np.ndarray, mp: np.ndarray, branch: str = "bf16"):
                 ldo=ldo, branch=branch, sq_nnz=0)
 
 
-def sq_row(wrow: np.ndarray, hdiag: np.ndarray, nnz: int, bits: int = 4):
-    """One weight-side SQ-format row -> (fields u8 [k_low], v8 i8 [nnz], s8, s_low)."""
+def _check_bank(k_low: int, nnz: int, bank: int) -> int:
+    if bank <= 0 or bank >= k_low:
+        return 0
+    if k_low % bank or nnz % (k_low // bank):
+        raise ValueError(f"bank {bank} must divide k_low {k_low} and the bank count nnz {nnz}")
+    return bank
+
+
+def sq_row(wrow: np.ndarray, hdiag: np.ndarray, nnz: int, bits: int = 4, bank: int = 0):
+    """One weight-side SQ-format row -> (fields u8 [k_low], v8 i8 [nnz], s8, s_low).
+    ``bank`` > 0: banks of that many slots, nnz / banks marks in each."""
     wrow = np.ascontiguousarray(wrow, dtype=np.float32)
     hdiag = np.ascontiguousarray(hdiag, dtype=np.float32)
     k_low = len(wrow)
@@ -230,12 +240,15 @@ def sq_row(wrow: np.ndarray, hdiag: np.ndarray, nnz: int, bits: int = 4):
     v8 = np.zeros(max(nnz, 1), dtype=np.int8)
     s8 = np.zeros(1, dtype=np.float32)
     sl = np.zeros(1, dtype=np.float32)
-    _load().orc_sq_row(_p(wrow), _p(hdiag), k_low, nnz, bits, _p(fields), _p(v8), _p(s8), _p(sl))
+    bank = _check_bank(k_low, nnz, bank)
+    _load().orc_sq_row(_p(wrow), _p(hdiag), k_low, nnz, bank, bits, _p(fields), _p(v8), _p(s8),
+                       _p(sl))
     return fields[:k_low], v8[:nnz], s8[0], sl[0]
 
 
-def pack_weights_sq(w: np.ndarray, mp: np.ndarray, hdiag: np.ndarray, nnz: int):
-    """Weight-side SQ-format with an int8 branch over the outlier channels."""
+def pack_weights_sq(w: np.ndarray, mp: np.ndarray, hdiag: np.ndarray, nnz: int, bank: int = 0):
+    """Weight-side SQ-format with an int8 branch over the outlier channels
+    (``bank`` > 0: banks of that many slots with an equal count of marks)."""
     w = np.ascontiguousarray(w, dtype=np.float32)
     mp = np.ascontiguousarray(mp, dtype=np.int32)
     hdiag = np.ascontiguousarray(hdiag, dtype=np.float32)
@@ -250,11 +263,13 @@ def pack_weights_sq(w: np.ndarray, mp: np.ndarray, hdiag: np.ndarray, nnz: int):
     s_w8 = np.zeros(n, dtype=np.float32)
     w_out = np.zeros((n, ldo), dtype=np.int8)
     s_wo = np.zeros(n, dtype=np.float32)
-    _load().orc_pack_weights_sq(_p(w), k, n, _p(mp), _p(hdiag), k_low, k_out, ldk, ldo, nnz,
+    bank = _check_bank(k_low, nnz, bank)
+    _load().orc_pack_weights_sq(_p(w), k, n, _p(mp), _p(hdiag), k_low, k_out, ldk, ldo, nnz, bank,
                                 _p(w_low), _p(s_w4), _p(sq_val), _p(s_w8),
                                 _p(w_out) if ldo else None, _p(s_wo))
     return dict(w_low=w_low, s_w=s_w4, sq_val=sq_val[:, :nnz].copy(), s_w8=s_w8, w_out=w_out,
-                s_wo=s_wo, k_low=k_low, k_out=k_out, ldk=ldk, ldo=ldo, branch="i8", sq_nnz=nnz)
+                s_wo=s_wo, k_low=k_low, k_out=k_out, ldk=ldk, ldo=ldo, branch="i8", sq_nnz=nnz,
+                sq_bank=bank)
 
 
 def quantize_split_act(x: np.ndarray, mp: np.ndarray, low: str = "i4", branch: str = "bf16",

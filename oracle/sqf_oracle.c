@@ -290,16 +290,19 @@ void orc_pack_weights(const float* w, int64_t k, int64_t n, const int32_t* map, 
  * quantisation leaves the largest unsigned code unused and that code marks
  * the high-precision positions; the positions are the top fraction of each
  * bank by an importance score built from the weight and the Hessian
- * diagonal.]  The bank is the whole row here.
+ * diagonal; section 七: banks keep the work of every bank equal.]
  *   key_j = w_j^2 * hdiag_j in fp64 (orders exactly like |w_j| * sqrt(hdiag_j))
- * The nnz largest keys (lower slot first on ties) are kept at high
- * precision: int8 per-row quantisation of those values in ascending slot
- * order -> v8[0..nnz), scale *s8.  The remaining slots are quantised to
+ * The row is split into banks of `bank` consecutive slots (bank <= 0 or
+ * bank == k_low: one bank, the whole row; otherwise bank divides k_low and
+ * nnz is a multiple of the bank count); in every bank the nnz / banks
+ * largest keys (lower slot first on ties) are kept at high precision: int8
+ * per-row quantisation of all kept values in ascending slot order ->
+ * v8[0..nnz), scale *s8.  The remaining slots are quantised to
  * [-(2^(bits-1)-1), 2^(bits-1)-1] with their own scale *s_low; the kept
  * slots receive the reserved code 2^(bits-1) (as an unsigned field).
  * codes_out[j] holds the unsigned field value of slot j. */
-void orc_sq_row(const float* wrow, const float* hdiag, int64_t k_low, int64_t nnz, int bits,
-                uint8_t* codes_out, int8_t* v8, float* s8, float* s_low) {
+void orc_sq_row(const float* wrow, const float* hdiag, int64_t k_low, int64_t nnz, int64_t bank,
+                int bits, uint8_t* codes_out, int8_t* v8, float* s8, float* s_low) {
   double* key = (double*)malloc(sizeof(double) * (size_t)(k_low + 1));
   int32_t* order = (int32_t*)malloc(sizeof(int32_t) * (size_t)(k_low + 1));
   uint8_t* keep = (uint8_t*)calloc((size_t)(k_low + 1), 1);
@@ -310,9 +313,15 @@ void orc_sq_row(const float* wrow, const float* hdiag, int64_t k_low, int64_t nn
     key[j] = wj * wj * (double)hdiag[j];
     order[j] = (int32_t)j;
   }
+  if (bank <= 0 || bank > k_low) bank = k_low;
+  const int64_t banks = k_low > 0 ? k_low / bank : 0;
+  const int64_t per_bank = banks > 0 ? nnz / banks : 0;
   g_sort_score = key;
-  qsort(order, (size_t)k_low, sizeof(int32_t), cmp_rank);
-  for (int64_t i = 0; i < nnz; ++i) keep[order[i]] = 1;
+  for (int64_t b = 0; b < banks; ++b) {
+    /* rank the bank's slots on their own and keep its per_bank largest */
+    qsort(order + b * bank, (size_t)bank, sizeof(int32_t), cmp_rank);
+    for (int64_t i = 0; i < per_bank; ++i) keep[order[b * bank + i]] = 1;
+  }
   /* high-precision values, ascending slot order */
   int64_t c = 0;
   for (int64_t j = 0; j < k_low; ++j)
@@ -354,7 +363,7 @@ void orc_sq_row(const float* wrow, const float* hdiag, int64_t k_low, int64_t nn
  * channels -> int8 branch rows w_out[nn][ldo] with scale s_wo. */
 void orc_pack_weights_sq(const float* w, int64_t k, int64_t n, const int32_t* map,
                          const float* hdiag_k, int64_t k_low, int64_t k_out, int64_t ldk,
-                         int64_t ldo, int64_t nnz, uint8_t* w_low, float* s_w4, int8_t* sq_val,
+                         int64_t ldo, int64_t nnz, int64_t bank, uint8_t* w_low, float* s_w4, int8_t* sq_val,
                          float* s_w8, int8_t* w_out, float* s_wo) {
   float* lo = (float*)malloc(sizeof(float) * (size_t)(k_low + 1));
   float* hlo = (float*)malloc(sizeof(float) * (size_t)(k_low + 1));
@@ -372,7 +381,7 @@ void orc_pack_weights_sq(const float* w, int64_t k, int64_t n, const int32_t* ma
       else
         hi[-s - 1] = v;
     }
-    orc_sq_row(lo, hlo, k_low, nnz, 4, fields, sq_val + nn * nnz, &s_w8[nn], &s_w4[nn]);
+    orc_sq_row(lo, hlo, k_low, nnz, bank, 4, fields, sq_val + nn * nnz, &s_w8[nn], &s_w4[nn]);
     uint8_t* row = w_low + nn * ldk;
     memset(row, 0, (size_t)ldk);
     for (int64_t j = 0; j < k_low; ++j)

@@ -728,3 +728,67 @@ def test_mx_storage_brute_force_reader():
             if j % 32 == 0:
                 sidx = (((kb * (rp // 64) + r // 64) * 4 + g) * 16 + r % 16) * 4 + (r // 16) % 4
                 assert sf[sidx] == scales[r, j // 32]
+
+
+# ------------------------------------------------------------------ banked SQ-format
+def _sq_hand_row():
+    w = np.full(128, 0.1, np.float32)
+    for j, v in ((3, 9.0), (10, -8.0), (20, 7.0), (70, 6.0), (100, -0.5)):
+        w[j] = v
+    return w, np.ones(128, np.float32)
+
+
+def test_sq_banked_hand_case(golden):
+    g = golden("sq_bank_hand_case.txt")
+    w, hd = _sq_hand_row()
+    nnz, bank = int(g["nnz"][0][0]), int(g["bank"][0][0])
+    f, v8, s8, sl = oracle.sq_row(w, hd, nnz, bank=bank)
+    marks = [int(v) for v in g["banked_marks"][0]]
+    assert np.flatnonzero(f == 8).tolist() == marks
+    assert v8.tolist() == [int(v) for v in g["banked_v8"][0]]
+    assert s8 == np.float32(9.0) / np.float32(127.0)
+    assert sl == np.float32(g["banked_s_low"][0][0])
+    assert f[20] == int(g["banked_field20"][0][0])
+    others = [j for j in range(128) if j not in marks and j != 20]
+    assert (f[others] == int(g["banked_field_other"][0][0])).all()
+    f, v8, s8, sl = oracle.sq_row(w, hd, nnz, bank=0)
+    marks = [int(v) for v in g["row_marks"][0]]
+    assert np.flatnonzero(f == 8).tolist() == marks
+    assert v8.tolist() == [int(v) for v in g["row_v8"][0]]
+    assert f[100] == int(g["row_field100"][0][0])
+    others = [j for j in range(128) if j not in marks and j != 100]
+    assert (f[others] == int(g["row_field_other"][0][0])).all()
+
+
+def test_sq_banked_selection_brute_force():
+    """Tiny rows with distinct keys: in every bank the marked set is the
+    subset of per_bank slots with the largest total key (enumerated)."""
+    import itertools
+    rng = np.random.default_rng(17)
+    for trial in range(6):
+        k_low, bank, per = 24, 8, 1 + trial % 3
+        banks = k_low // bank
+        w = rng.standard_normal(k_low).astype(np.float32)
+        hd = rng.uniform(0.5, 2.0, k_low).astype(np.float32)
+        key = w.astype(np.float64) ** 2 * hd.astype(np.float64)
+        assert len(set(key.tolist())) == k_low
+        f, v8, _, _ = oracle.sq_row(w, hd, per * banks, bank=bank)
+        got = set(np.flatnonzero(f == 8).tolist())
+        want = set()
+        for b in range(banks):
+            sl = range(b * bank, (b + 1) * bank)
+            best = max(itertools.combinations(sl, per), key=lambda c: sum(key[j] for j in c))
+            want |= set(best)
+        assert got == want
+        assert len(v8) == per * banks
+
+
+def test_sq_one_bank_is_the_whole_row():
+    rng = np.random.default_rng(19)
+    w = rng.standard_normal(256).astype(np.float32)
+    hd = rng.uniform(0.1, 3.0, 256).astype(np.float32)
+    a = oracle.sq_row(w, hd, 32, bank=0)
+    b = oracle.sq_row(w, hd, 32, bank=256)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and a[2] == b[2] and a[3] == b[3]
+    with pytest.raises(ValueError):
+        oracle.sq_row(w, hd, 30, bank=64)  # 30 marks over 4 banks
