@@ -302,33 +302,39 @@ def rows_section(sqf, torch, stream):
             torch.cuda.empty_cache()
         del moe
 
-        # a7: SQ-format weight side
+        # a7: SQ-format weight side, one bank per row and banks of 64 slots
         lay = synth.sq_weight()
         k_out = lay.k_out
         k_low = lay.k - k_out
         x_cal = torch.from_numpy(lay.x_cal).cuda()
         w = torch.from_numpy(lay.w).cuda()
         _, mp, _, hd = sqf.sqf_select_channels(x_cal, w, k_out, stream=stream)
-        wt = sqf.sqf_pack_weights(w, mp, branch="i8", hdiag=hd, sq_nnz=k_low // 8, stream=stream)
         xt = torch.from_numpy(synth.to_bf16_bits(lay.x).view(np.int16)).view(torch.bfloat16).cuda()
         a = sqf.alloc_acts(lay.m, k_low, k_out, low="i8", branch="i8")
         y = torch.empty((lay.m, lay.n), dtype=torch.float32, device="cuda")
         ta = time_call(torch, stream, lambda: sqf.sqf_quantize_split_act(xt, mp, a, stream=stream))
-        tg = time_call(torch, stream, lambda: sqf.sqf_dual_gemm(a, wt, y=y, stream=stream), iters=5)
-        # the method's own work: every low slot, every marked value and every
-        # branch channel once (2*M*N*(K_low + nnz + K_out) int8 operations)
         nnz = k_low // 8
-        own_ops = 2.0 * lay.m * lay.n * (k_low + nnz + k_out)
-        # what the kernel issues: two dense int8 passes over K_low plus the branch
-        mfma_ops = 2.0 * lay.m * lay.n * (2 * k_low + k_out)
-        _add(out, dict(row="a7 SQ-format weight side (int8 acts, masked int8 part, int8 branch)",
-                        shape=f"{lay.m}x{lay.k}->{lay.n}, nnz {nnz}/row",
-                        act_us=round(ta * 1e3, 1), gemm_us=round(tg * 1e3, 1),
-                        gemm_eff_tops=round(2.0 * lay.m * lay.n * lay.k / (tg * 1e-3) / 1e12, 1),
-                        own_work_tops=round(own_ops / (tg * 1e-3) / 1e12, 1),
-                        frac_int8_peak=round(own_ops / (tg * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
-                        issued_mfma_tops=round(mfma_ops / (tg * 1e-3) / 1e12, 1)))
-        del wt, xt, a, y, w, x_cal
+        for bank in (0, 64):
+            tp = time_call(torch, stream, lambda: sqf.sqf_pack_weights(
+                w, mp, branch="i8", hdiag=hd, sq_nnz=nnz, sq_bank=bank, stream=stream), iters=2, warmup=1)
+            wt = sqf.sqf_pack_weights(w, mp, branch="i8", hdiag=hd, sq_nnz=nnz, sq_bank=bank, stream=stream)
+            tg = time_call(torch, stream, lambda: sqf.sqf_dual_gemm(a, wt, y=y, stream=stream), iters=5)
+            # the method's own work: every low slot, every marked value and
+            # every branch channel once (2*M*N*(K_low + nnz + K_out) int8 operations)
+            own_ops = 2.0 * lay.m * lay.n * (k_low + nnz + k_out)
+            # what the kernel issues: two dense int8 passes over K_low plus the branch
+            mfma_ops = 2.0 * lay.m * lay.n * (2 * k_low + k_out)
+            what = "one bank per row" if bank == 0 else f"banks of {bank} slots, {nnz * bank // k_low} marks each"
+            _add(out, dict(row=f"a7 SQ-format weight side ({what}; int8 acts, masked int8 part, int8 branch)",
+                            shape=f"{lay.m}x{lay.k}->{lay.n}, nnz {nnz}/row",
+                            pack_ms=round(tp, 3),
+                            act_us=round(ta * 1e3, 1), gemm_us=round(tg * 1e3, 1),
+                            gemm_eff_tops=round(2.0 * lay.m * lay.n * lay.k / (tg * 1e-3) / 1e12, 1),
+                            own_work_tops=round(own_ops / (tg * 1e-3) / 1e12, 1),
+                            frac_int8_peak=round(own_ops / (tg * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
+                            issued_mfma_tops=round(mfma_ops / (tg * 1e-3) / 1e12, 1)))
+            del wt
+        del xt, a, y, w, x_cal
         torch.cuda.empty_cache()
     return out
 

@@ -148,9 +148,12 @@ typedef struct sqf_weights {
    * low SQF_I4X2. */
   int64_t sq_nnz;  /* 0 = channel-split (OSC) format; else marked slots per
                       row, an equal share in every bank */
-  int64_t sq_bank; /* slots per bank: 0 = the whole row (k_low slots) is one
-                      bank; else a multiple of 64 that divides k_low, with
-                      sq_nnz * sq_bank / k_low marks in every bank */
+  int64_t sq_bank; /* slots per bank: 0 (or k_low) = the whole row is one
+                      bank; else a multiple of 64, at most 1024, that
+                      divides k_low, with sq_nnz a multiple of the bank count
+                      k_low / sq_bank: sq_nnz * sq_bank / k_low marks in
+                      every bank (SQF_ERR_SHAPE otherwise; larger banks
+                      SQF_ERR_UNSUPPORTED) */
   int8_t* sq_val;  /* [n][sq_nnz], 16-byte aligned, in ascending slot order
                       (so bank by bank) */
   float* s_w8;     /* [n] scale of sq_val */

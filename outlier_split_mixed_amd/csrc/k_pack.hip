@@ -245,6 +245,13 @@ __device__ __forceinline__ int block_excl_scan(int v, int* scratch) {
 // blocks run on different XCDs (block b on XCD b mod 8), so XCD x is given the
 // contiguous column range [x*per_x, (x+1)*per_x): its concurrently running
 // blocks then share the 128-byte lines of W in their XCD's L2.
+//
+// Banks (SQ-format article, section 九: the top fraction inside each bank;
+// section 七: equal work per bank): with p.bank > 0 the row is cut into banks
+// of p.bank consecutive slots and each keeps its nnz / banks largest keys.
+// Every slot then counts the keys of its bank that rank above it (larger,
+// or equal at a lower slot) and is kept when fewer than that many do; a
+// wave's 64 slots share a bank, so its reads of the bank are broadcasts.
 __global__ __launch_bounds__(256) void k_pack_sq(PackArgs p) {
   extern __shared__ uint8_t sm[];
   __shared__ int iscr[8];
@@ -284,8 +291,9 @@ __global__ __launch_bounds__(256) void k_pack_sq(PackArgs p) {
   // histograms the next byte of the keys that match the bytes chosen so far,
   // then takes the largest byte d whose keys at or above it still cover the
   // `need` keys not yet accounted for above the matching range.
+  const int64_t bank = p.bank > 0 && p.bank < kl ? p.bank : 0;
   uint64_t T = 0;
-  if (p.nnz > 0) {
+  if (p.nnz > 0 && bank == 0) {
     uint64_t mask = 0;
     int need = (int)p.nnz;
     for (int shift = 56; shift >= 0; shift -= 8) {
@@ -324,27 +332,44 @@ __global__ __launch_bounds__(256) void k_pack_sq(PackArgs p) {
       mask |= 255ull << shift;
     }
   }
-  // keep = key > T, plus the lowest-slot keys equal to T until nnz are kept
-  int gt = 0, eq = 0;
-  if (p.nnz > 0)
+  if (bank == 0) {
+    // keep = key > T, plus the lowest-slot keys equal to T until nnz are kept
+    int gt = 0, eq = 0;
+    if (p.nnz > 0)
+      for (int64_t j = j0; j < j1; ++j) {
+        uint64_t kb = keybits(j);
+        gt += kb > T;
+        eq += kb == T;
+      }
+    const int n_gt = block_sum_i(gt, iscr);
+    int eq_before = block_excl_scan(eq, iscr);
+    const int need = (int)p.nnz - n_gt;
     for (int64_t j = j0; j < j1; ++j) {
-      uint64_t kb = keybits(j);
-      gt += kb > T;
-      eq += kb == T;
+      uint8_t kp = 0;
+      if (p.nnz > 0) {
+        uint64_t kb = keybits(j);
+        if (kb > T) kp = 1;
+        else if (kb == T) kp = (eq_before++ < need) ? 1 : 0;
+      }
+      keep[j] = kp;
     }
-  const int n_gt = block_sum_i(gt, iscr);
-  int eq_before = block_excl_scan(eq, iscr);
-  const int need = (int)p.nnz - n_gt;
+  } else {
+    const int per_bank = (int)(p.nnz / (kl / bank));
+    for (int64_t j = tid; j < kl; j += 256) {
+      const int64_t b0 = j / bank * bank;
+      const uint64_t kj = keybits(j);
+      int above = 0;
+      for (int64_t i = b0; i < b0 + bank; ++i) {
+        const uint64_t ki = keybits(i);
+        above += (ki > kj) || (ki == kj && i < j);
+      }
+      keep[j] = above < per_bank ? 1 : 0;
+    }
+    __syncthreads();
+  }
   float a8 = 0.0f, a4 = 0.0f;
   for (int64_t j = j0; j < j1; ++j) {
-    uint8_t kp = 0;
-    if (p.nnz > 0) {
-      uint64_t kb = keybits(j);
-      if (kb > T) kp = 1;
-      else if (kb == T) kp = (eq_before++ < need) ? 1 : 0;
-    }
-    keep[j] = kp;
-    if (kp) a8 = fmaxf(a8, fabsf(vals[j])); else a4 = fmaxf(a4, fabsf(vals[j]));
+    if (keep[j]) a8 = fmaxf(a8, fabsf(vals[j])); else a4 = fmaxf(a4, fabsf(vals[j]));
   }
   a8 = block_max_f(a8, fscr);
   a4 = block_max_f(a4, fscr);

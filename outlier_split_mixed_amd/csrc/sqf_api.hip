@@ -48,6 +48,9 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 constexpr int64_t kMaxKLow = 171000;
 // weight-side format: |acc| <= 16 * 127 * 7 * k_low < 2^31
 constexpr int64_t kMaxKLowSq = 150000;
+// Banked weight-side format: each slot ranks itself within its bank (bank^2
+// work per bank in the packer).
+constexpr int64_t kMaxSqBank = 1024;
 // Kernels address operands with 32-bit byte offsets.
 constexpr int64_t kMaxOperandBytes = ((int64_t)1 << 31) - 1;
 
@@ -139,9 +142,17 @@ sqf_status check_weights(const sqf_weights* wt, const char* who) {
       return fail(SQF_ERR_UNSUPPORTED, "%s: the weight-side format needs an SQF_I8 branch", who);
     if (!wt->sq_val || !wt->s_w8)
       return fail(SQF_ERR_INVALID_ARG, "%s: sq_val and s_w8 are required", who);
-    if (wt->sq_bank != 0 && wt->sq_bank != wt->k_low)
-      return fail(SQF_ERR_UNSUPPORTED, "%s: sq_bank=%lld: only whole-row banks are built", who,
-                  (long long)wt->sq_bank);
+    if (wt->sq_bank != 0 && wt->sq_bank != wt->k_low) {
+      if (wt->sq_bank < 64 || wt->sq_bank % 64 != 0 || wt->k_low % wt->sq_bank != 0 ||
+          wt->sq_nnz % (wt->k_low / wt->sq_bank) != 0)
+        return fail(SQF_ERR_SHAPE, "%s: sq_bank=%lld must be a multiple of 64 dividing k_low=%lld, "
+                    "and sq_nnz=%lld a multiple of the %lld banks", who, (long long)wt->sq_bank,
+                    (long long)wt->k_low, (long long)wt->sq_nnz,
+                    (long long)(wt->sq_bank > 0 ? wt->k_low / wt->sq_bank : 0));
+      if (wt->sq_bank > kMaxSqBank)
+        return fail(SQF_ERR_UNSUPPORTED, "%s: sq_bank=%lld: banks of up to %lld slots (or the "
+                    "whole row) are built", who, (long long)wt->sq_bank, (long long)kMaxSqBank);
+    }
     if (!aligned16(wt->sq_val))
       return fail(SQF_ERR_ALIGN, "%s: sq_val must be 16-byte aligned", who);
   } else if (wt->branch == SQF_I8) {
@@ -465,7 +476,7 @@ sqf_status sqf_pack_weights(const float* w, const int32_t* map, const float* hdi
                   (long long)wt->k_low);
   }
   sqf::PackArgs a{w, map, hdiag, wt->k, wt->n, wt->k_low, wt->k_out, wt->ldk, wt->ldo,
-                  wt->sq_nnz, low_kblocked(wt->low) ? sqf_pad_rows(wt->n) : 0, wt->w_low, wt->s_w,
+                  wt->sq_nnz, wt->sq_bank == wt->k_low ? 0 : wt->sq_bank, low_kblocked(wt->low) ? sqf_pad_rows(wt->n) : 0, wt->w_low, wt->s_w,
                   wt->s_wb, (uint8_t*)wt->w_out, wt->s_wo, wt->sq_val, wt->s_w8};
   return hip_status(sqf::launch_pack(a, wt->branch, wt->low, wt->groups, (hipStream_t)stream), who);
 }

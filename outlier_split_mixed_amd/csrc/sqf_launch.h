@@ -11,6 +11,7 @@ struct PackArgs {
   const int32_t* map;  // [groups][k]
   const float* hdiag;  // [k] (weight-side format)
   int64_t k, n, k_low, k_out, ldk, ldo, nnz;
+  int64_t bank;      // weight-side format: slots per bank (0 = the whole row)
   int64_t rows_pad;  // K-blocked layouts: rows of each K block (0 otherwise)
   uint8_t* w_low;
   float* s_w;

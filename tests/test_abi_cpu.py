@@ -292,12 +292,22 @@ def test_mxfp4_contract_errors(sqf):
 
 
 def test_weight_side_bank_must_be_supported(sqf):
+    """Banks: a multiple of 64 slots that divides k_low, an equal count of
+    marks in each bank, at most 1024 slots (or the whole row)."""
     mem = FakeMem()
-    w = _weights(sqf, mem, k=512, k_out=32)
-    w.branch, w.ldo, w.s_wo = sqf.SQF_I8, 128, mem()
-    w.sq_nnz, w.sq_val, w.s_w8 = 60, mem(), mem()
-    w.sq_bank = 7  # not a multiple of 64 dividing k_low
-    assert sqf._lib.sqf_pack_weights(mem(), mem(), mem(), ctypes.byref(w), None) in (2, 3)
+
+    def st(k_low, nnz, bank):
+        w = _weights(sqf, mem, k=k_low + 32, k_out=32)
+        w.branch, w.ldo, w.s_wo = sqf.SQF_I8, 128, mem()
+        w.sq_nnz, w.sq_val, w.s_w8, w.sq_bank = nnz, mem(), mem(), bank
+        return sqf._lib.sqf_pack_weights(mem(), mem(), mem(), ctypes.byref(w), None)
+
+    assert st(480, 60, 7) == 2     # not a multiple of 64
+    assert st(512, 60, 64) == 2    # 60 marks over 8 banks
+    assert st(512, 64, 96) == 2    # 96 is not a multiple of 64
+    assert st(512, 64, 192) == 2   # does not divide 512
+    assert st(4096, 64, 2048) == 3  # beyond the largest bank built
+    assert "bank" in sqf.sqf_last_error()
 
 
 def test_no_entry_point_reads_the_environment():

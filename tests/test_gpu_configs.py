@@ -120,7 +120,8 @@ def test_moe_down_fp8_every_channel(sqf, moe):
     _log("moe down fp8 f=1 ok")
 
 
-def test_sq_weight_side_full(sqf):
+@pytest.mark.parametrize("bank", [0, 64, 256])
+def test_sq_weight_side_full(sqf, bank):
     lay = synth.sq_weight()
     k_out = lay.k_out
     k_low = lay.k - k_out
@@ -128,7 +129,7 @@ def test_sq_weight_side_full(sqf):
     x_cal = torch.from_numpy(lay.x_cal).cuda()
     w = torch.from_numpy(lay.w).cuda()
     idx, mp, score, hdiag = sqf.sqf_select_channels(x_cal, w, k_out)
-    wts = sqf.sqf_pack_weights(w, mp, branch="i8", hdiag=hdiag, sq_nnz=nnz)
+    wts = sqf.sqf_pack_weights(w, mp, branch="i8", hdiag=hdiag, sq_nnz=nnz, sq_bank=bank)
     ox, ofmt, xt = x_inputs(lay, "bf16")
     acts = sqf.alloc_acts(lay.m, k_low, k_out, low="i8", branch="i8")
     sqf.sqf_quantize_split_act(xt, mp, acts)
@@ -138,7 +139,7 @@ def test_sq_weight_side_full(sqf):
     o_idx, o_mp, _, o_hd = oracle.select_channels(lay.x_cal, lay.w, k_out)
     assert np.array_equal(mp.cpu().numpy(), o_mp)
     assert f32_bits_equal(hdiag.cpu().numpy(), o_hd)
-    o_w = oracle.pack_weights_sq(lay.w, o_mp, o_hd, nnz)
+    o_w = oracle.pack_weights_sq(lay.w, o_mp, o_hd, nnz, bank=bank)
     assert np.array_equal(wts.t["w_low"][0].cpu().numpy(), o_w["w_low"])
     assert np.array_equal(wts.t["sq_val"].cpu().numpy(), o_w["sq_val"])
     assert f32_bits_equal(wts.t["s_w8"].cpu().numpy(), o_w["s_w8"])
@@ -157,4 +158,4 @@ def test_sq_weight_side_full(sqf):
     assert np.array_equal(ao.cpu().numpy()[rows].astype(np.int64), o_ao)
     assert_rows_close(y.cpu().numpy()[rows], o_y, "sq full")
     assert_rows_close(y_fast.cpu().numpy()[rows], o_y, "sq full (no debug outputs)")
-    _log("sq full ok")
+    _log("sq full ok, bank", bank)

@@ -298,13 +298,13 @@ def test_sq_weight_side_key_ties(sqf, frac):
     _sq_check(sqf, lay, nnz, f"sq ties {frac}")
 
 
-def _sq_check(sqf, lay, nnz, label):
+def _sq_check(sqf, lay, nnz, label, bank=0):
     k_out = lay.k_out
     k_low = lay.k - k_out
     x_cal = torch.from_numpy(lay.x_cal).cuda()
     w = torch.from_numpy(lay.w).cuda()
     idx, mp, score, hdiag = sqf.sqf_select_channels(x_cal, w, k_out)
-    wts = sqf.sqf_pack_weights(w, mp, branch="i8", hdiag=hdiag, sq_nnz=nnz)
+    wts = sqf.sqf_pack_weights(w, mp, branch="i8", hdiag=hdiag, sq_nnz=nnz, sq_bank=bank)
     ox, ofmt, xt = x_inputs(lay, "bf16")
     acts = sqf.alloc_acts(lay.m, k_low, k_out, low="i8", branch="i8")
     sqf.sqf_quantize_split_act(xt, mp, acts)
@@ -312,7 +312,7 @@ def _sq_check(sqf, lay, nnz, label):
     torch.cuda.synchronize()
     o_idx, o_mp, _, o_hd = oracle.select_channels(lay.x_cal, lay.w, k_out)
     assert np.array_equal(mp.cpu().numpy(), o_mp)
-    o_w = oracle.pack_weights_sq(lay.w, o_mp, o_hd, nnz)
+    o_w = oracle.pack_weights_sq(lay.w, o_mp, o_hd, nnz, bank=bank)
     assert np.array_equal(wts.t["w_low"][0].cpu().numpy(), o_w["w_low"])
     assert np.array_equal(wts.t["sq_val"].cpu().numpy(), o_w["sq_val"])
     assert f32_bits_equal(wts.t["s_w"][0].cpu().numpy(), o_w["s_w"])
@@ -605,3 +605,32 @@ def test_mxfp4_bf16_output_and_errors(sqf):
         with pytest.raises(sqf.SqfError) as ei:
             sqf.sqf_dual_gemm(am, wm, **kw)
         assert ei.value.status == sqf.SQF_ERR_UNSUPPORTED
+
+
+# ------------------------------------------------------------------ banked SQ-format
+@pytest.mark.parametrize("bank", [64, 128, 256, 512])
+def test_sq_banked(sqf, bank):
+    """Banked weight-side format: the same count of marks in every bank of
+    `bank` slots; marks, values, scales, the three exact accumulators and Y
+    against the oracle (k_low = 1024, 1/8 of the slots marked)."""
+    lay = _ragged(m=200, k=1280, n=300, n_scaled=256, seed=121)
+    assert lay.k - lay.k_out == 1024
+    _sq_check(sqf, lay, 128, f"sq bank {bank}", bank=bank)
+
+
+@pytest.mark.parametrize("bank,den", [(64, 2), (64, 64), (1024, 8)])
+def test_sq_banked_densities(sqf, bank, den):
+    """Half of every bank marked, one mark per bank, and a bank equal to the
+    whole row (the unbanked choice)."""
+    lay = _ragged(m=130, k=1280, n=260, n_scaled=256, seed=122)
+    _sq_check(sqf, lay, 1024 // den, f"sq bank {bank} 1/{den}", bank=bank)
+
+
+def test_sq_banked_key_ties(sqf):
+    """Equal keys inside banks (W on a 5-value grid, calibration columns
+    repeated in groups of 4): the lower slot wins within each bank."""
+    lay = _ragged(m=96, k=1280, n=136, n_scaled=256, seed=123)
+    lay.w[:] = np.clip(np.rint(lay.w / 0.01), -2, 2).astype(np.float32) * np.float32(0.01)
+    for c in range(0, lay.k - 3, 4):
+        lay.x_cal[:, c + 1:c + 4] = lay.x_cal[:, c:c + 1]
+    _sq_check(sqf, lay, 256, "sq bank ties", bank=64)
