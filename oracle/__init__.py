@@ -19,6 +19,9 @@ the method:
 * :func:`dual_gemm`        -- low path + masked path + branch + fused output.
 * :func:`i4x2_to_e2m3`     -- the same int4 codes stored in 6-bit E2M3 fields,
   K-blocked (the storage a 6-bit matrix unit reads).
+* :func:`rmsnorm`, :func:`rmsnorm_quantize_split_act` -- the norm in front
+  of the split, and the two composed; :func:`slot_order` -- the channel
+  order that turns the split into a slice (SQ-format article, section 九).
 * :func:`pack_weights_mx`, :func:`quantize_split_act_mx`, :func:`dual_gemm_mx`
   -- the MXFP4 low path (OCP Microscaling: E2M1 elements, one E8M0 scale
   per 32 slots; OSC abstract, 4-bit micro-scaling hardware), and
@@ -113,6 +116,10 @@ def _declare(lib):
     lib.orc_mx_storage.restype = None
     lib.orc_dual_gemm_mx.argtypes = [I64, I64, I64, I64, P, I64, P, P, P, I64, P, P, P, P, I64]
     lib.orc_dual_gemm_mx.restype = None
+    lib.orc_rmsnorm.argtypes = [P, INT, I64, I64, I64, P, ctypes.c_float, P]
+    lib.orc_rmsnorm.restype = None
+    lib.orc_slot_order.argtypes = [P, I64, P, P]
+    lib.orc_slot_order.restype = None
     lib.orc_num_threads.argtypes = []
     lib.orc_num_threads.restype = ctypes.c_int
 
@@ -426,3 +433,32 @@ def dual_gemm_mx(a: dict, w: dict, rows=None):
                              _p(w["s_wb"]) if w["s_wb"].size else None,
                              _p(w["w_out"]) if w["w_out"].size else None, _p(y), n)
     return y
+
+
+# ---------------------------------------------------------------- producer side
+def rmsnorm(x: np.ndarray, gamma: np.ndarray, eps: float, x_fmt: str = "f32") -> np.ndarray:
+    """RMS normalisation of each row -> fp32 [m][k] (see orc_rmsnorm)."""
+    x = np.ascontiguousarray(x)
+    assert x.dtype == (np.uint16 if x_fmt == "bf16" else np.float32)
+    gamma = np.ascontiguousarray(gamma, dtype=np.float32)
+    m, k = x.shape
+    out = np.zeros((m, k), np.float32)
+    if m:
+        _load().orc_rmsnorm(_p(x), _FMT[x_fmt], m, k, k, _p(gamma), float(eps), _p(out))
+    return out
+
+
+def rmsnorm_quantize_split_act(x, gamma, eps, mp, low="i4", branch="bf16", x_fmt="f32"):
+    """The split of the normalised rows: quantize_split_act(rmsnorm(x))."""
+    return quantize_split_act(rmsnorm(x, gamma, eps, x_fmt), mp, low=low, branch=branch, x_fmt="f32")
+
+
+def slot_order(mp: np.ndarray):
+    """(perm, slice_map): position p of the reordered channel axis holds
+    channel perm[p] (low channels in slot order, then the outliers); the
+    consumer's map on that axis is slice_map."""
+    mp = np.ascontiguousarray(mp, dtype=np.int32)
+    perm = np.zeros(len(mp), np.int32)
+    sm = np.zeros(len(mp), np.int32)
+    _load().orc_slot_order(_p(mp), len(mp), _p(perm), _p(sm))
+    return perm, sm

@@ -455,6 +455,54 @@ void orc_quantize_split_act(const void* x, int x_fmt, int64_t m, int64_t k, int6
 }
 
 /* ------------------------------------------------------------------ */
+/* Producer side: the norm that feeds the split, and the channel order */
+/* ------------------------------------------------------------------ */
+
+/* RMS normalisation of each row (the norm in front of the linear layers of
+ * the Llama / Qwen models the workloads are shaped after; the pages name no
+ * norm, so this is a reading): out[m][c] = (x[m][c] * r_m) * gamma[c] in
+ * fp32, r_m = 1 / sqrt(mean_c x[m][c]^2 + eps) formed in fp64 (the squares of
+ * fp32 values are exact there) and rounded once to fp32.  x is fp32 (x_fmt
+ * ORC_F32) or bf16 patterns (ORC_BF16), row stride ldx; out is [m][k]. */
+void orc_rmsnorm(const void* x, int x_fmt, int64_t m, int64_t k, int64_t ldx, const float* gamma,
+                 float eps, float* out) {
+  for (int64_t mm = 0; mm < m; ++mm) {
+    double ss = 0.0;
+    for (int64_t c = 0; c < k; ++c) {
+      double v = x_fmt == ORC_BF16 ? orc_bf16_to_double(((const uint16_t*)x)[mm * ldx + c])
+                                   : (double)((const float*)x)[mm * ldx + c];
+      ss += v * v;
+    }
+    float r = (float)(1.0 / sqrt(ss / (double)k + (double)eps));
+    for (int64_t c = 0; c < k; ++c) {
+      float v = x_fmt == ORC_BF16 ? (float)orc_bf16_to_double(((const uint16_t*)x)[mm * ldx + c])
+                                  : ((const float*)x)[mm * ldx + c];
+      float t = v * r;
+      out[mm * k + c] = t * gamma[c];
+    }
+  }
+}
+
+/* The channel order that makes the split a slice [SQ-format article,
+ * section 九: weight columns reordered by the importance mask]: position p
+ * of the reordered axis holds channel perm[p]; the low channels first in slot
+ * order (p = map[c]), then the outlier channels in branch order (p = k_low +
+ * t for map[c] = -(t+1)).  Reordering the producer's output channels and the
+ * consumer's input channels this way leaves every product of the layer
+ * unchanged, and the consumer's map becomes the slice map: p -> p for
+ * p < k_low, p -> -(p - k_low + 1) after. */
+void orc_slot_order(const int32_t* map, int64_t k, int32_t* perm, int32_t* slice_map) {
+  int64_t k_low = 0;
+  for (int64_t c = 0; c < k; ++c)
+    if (map[c] >= 0) ++k_low;
+  for (int64_t c = 0; c < k; ++c) {
+    int64_t p = map[c] >= 0 ? map[c] : k_low + (-map[c] - 1);
+    perm[p] = (int32_t)c;
+  }
+  for (int64_t p = 0; p < k; ++p) slice_map[p] = p < k_low ? (int32_t)p : (int32_t)(-(p - k_low + 1));
+}
+
+/* ------------------------------------------------------------------ */
 /* Storage of int4 codes in 6-bit OCP E2M3 fields (K-blocked layout)   */
 /* ------------------------------------------------------------------ */
 

@@ -792,3 +792,49 @@ def test_sq_one_bank_is_the_whole_row():
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and a[2] == b[2] and a[3] == b[3]
     with pytest.raises(ValueError):
         oracle.sq_row(w, hd, 30, bank=64)  # 30 marks over 4 banks
+
+
+# ------------------------------------------------------------------ producer side
+def test_rmsnorm_hand_cases():
+    x = np.full((1, 4), 2.0, np.float32)
+    g = np.array([1.0, -3.0, 0.25, 8.0], np.float32)
+    # mean(x^2) = 4 -> r = 1/2 (a sum would give 1/4); eps inside the root
+    assert oracle.rmsnorm(x, g, 0.0).tolist() == [[1.0, -3.0, 0.25, 8.0]]
+    assert oracle.rmsnorm(x, g, 12.0).tolist() == [[0.5, -1.5, 0.125, 4.0]]
+    xb = synth.to_bf16_bits(x)
+    assert oracle.rmsnorm(xb, g, 12.0, x_fmt="bf16").tolist() == [[0.5, -1.5, 0.125, 4.0]]
+
+
+def test_rmsnorm_matches_torch_in_fp64():
+    rng = np.random.default_rng(23)
+    x = (rng.standard_normal((16, 300)) * 3).astype(np.float32)
+    g = rng.uniform(0.2, 2.0, 300).astype(np.float32)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x).double(), (300,),
+                                       weight=torch.from_numpy(g).double(), eps=1e-5).numpy()
+    got = oracle.rmsnorm(x, g, 1e-5)
+    assert np.abs(got - ref).max() <= 4e-7 * np.abs(ref).max()
+
+
+def test_slot_order_hand_case():
+    perm, sm = oracle.slot_order(np.array([0, -1, 1, -2, 2], np.int32))
+    assert perm.tolist() == [0, 2, 4, 1, 3]
+    assert sm.tolist() == [0, 1, 2, -1, -2]
+
+
+def test_slot_order_leaves_the_layer_unchanged():
+    """Reordering the activations' channels and the weights' input rows by
+    the slot order, with the slice map, gives the same codes, scales and Y
+    bit for bit."""
+    lay = synth.draw_layer("perm", 31, 0, 20, 640, 96, 64, 40)
+    _, mp, _, _ = oracle.select_channels(lay.x_cal, lay.w, lay.k_out)
+    perm, sm = oracle.slot_order(mp)
+    a0 = oracle.quantize_split_act(lay.x, mp)
+    w0 = oracle.pack_weights(lay.w, mp)
+    a1 = oracle.quantize_split_act(np.ascontiguousarray(lay.x[:, perm]), sm)
+    w1 = oracle.pack_weights(np.ascontiguousarray(lay.w[perm, :]), sm)
+    for key in ("x_low", "s_x", "x_out"):
+        assert np.array_equal(a0[key], a1[key])
+    for key in ("w_low", "s_w", "w_out"):
+        assert np.array_equal(w0[key], w1[key])
+    assert np.array_equal(oracle.dual_gemm(a0, w0), oracle.dual_gemm(a1, w1))
+    assert sorted(perm.tolist()) == list(range(lay.k))
