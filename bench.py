@@ -261,6 +261,29 @@ def rows_section(sqf, torch, stream):
         del w, x_cal, mp
         torch.cuda.empty_cache()
 
+        # f2: the RMS norm fused into the split (E2M3 storage, bf16 X), on the
+        # 70B step's two row widths, against the split alone; a separate norm
+        # kernel would add a read and a write of X (2 * M * K * 2 bytes)
+        for li in (0, 2):
+            lay = synth.llama3_70b(li, 16)
+            x_cal = torch.from_numpy(lay.x_cal).cuda()
+            w = torch.from_numpy(lay.w).cuda()
+            _, mp, _, _ = sqf.sqf_select_channels(x_cal, w, lay.k_out, stream=stream)
+            del w, x_cal
+            xt = torch.from_numpy(synth.to_bf16_bits(lay.x).view(np.int16)).view(torch.bfloat16).cuda()
+            g = torch.ones(lay.k, dtype=torch.float32, device="cuda")
+            a = sqf.alloc_acts(lay.m, lay.k - lay.k_out, lay.k_out, low=HEADLINE_LOW)
+            t0 = time_call(torch, stream, lambda: sqf.sqf_quantize_split_act(xt, mp, a, stream=stream))
+            t1 = time_call(torch, stream, lambda: sqf.sqf_rmsnorm_quantize_split_act(
+                xt, g, 1e-5, mp, a, stream=stream))
+            b = lay.m * (lay.k * 2 + a.ldk + a.ldo * 2 + 4)
+            _add(out, dict(row=f"f2 RMS norm fused into the split ({lay.m}x{lay.k}, E2M3 codes)",
+                           split_us=round(t0 * 1e3, 1), fused_us=round(t1 * 1e3, 1),
+                           fused_frac_hbm=round(b / (t1 * 1e-3) / 1e9 / PEAK_HBM_GBS, 3),
+                           separate_norm_min_us=round(2 * lay.m * lay.k * 2 / (PEAK_HBM_GBS * 1e9) * 1e6, 1)))
+            del xt, a, g, mp
+            torch.cuda.empty_cache()
+
         # a6: grouped experts (Qwen3-30B-A3B-shaped)
         moe = synth.qwen3_moe()
         ro = torch.from_numpy(moe.offsets).cuda()

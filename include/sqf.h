@@ -255,6 +255,41 @@ sqf_status sqf_pack_weights(const float* w, const int32_t* map, const float* hdi
 sqf_status sqf_quantize_split_act(const void* x, int32_t x_dtype, int64_t ldx, const int32_t* map,
                                   sqf_acts* a, void* stream);
 
+/* Producer-side reordering ([SQF-art] 九: weight columns reordered by the
+ * importance mask).  sqf_slot_order: from a channel map [k] (device),
+ * perm_out[p] = the channel at position p of the slot order (the low
+ * channels in slot order, then the outlier channels in branch order) and
+ * slice_map_out [k] = the map of the reordered axis (p for p < k_low,
+ * -(p - k_low + 1) after), with which the split is a slice.  Reordering the
+ * producer's output channels (its weight columns and its norm's gamma) and
+ * the consumer's input channels (the rows of W) by perm leaves every product
+ * unchanged: the packed weights, the quantised activations and Y are the
+ * same bit for bit.  1 <= k <= 1048576; the map must be a valid channel map.
+ * sqf_permute_channels: dst = src gathered along one axis of a row-major
+ * fp32 matrix [rows][cols]: axis 1, dst[r][p] = src[r][perm[p]]; axis 0,
+ * dst[p][j] = src[perm[p]][j] (perm has cols resp. rows entries); src and
+ * dst distinct, ld >= cols.  Both asynchronous on `stream`. */
+sqf_status sqf_slot_order(const int32_t* map, int64_t k, int32_t* perm_out, int32_t* slice_map_out,
+                          void* stream);
+sqf_status sqf_permute_channels(const float* src, int64_t rows, int64_t cols, int64_t ld_src,
+                                const int32_t* perm, int32_t axis, float* dst, int64_t ld_dst,
+                                void* stream);
+
+/* a2 fused with the norm in front of it (producer-side fusion): each row is
+ * RMS-normalised, xn[c] = (x[c] * r) * gamma[c] in fp32 with r = 1 /
+ * sqrt(mean_c x[c]^2 + eps) (the mean of squares in fp64, r rounded once to
+ * fp32), and xn is split and quantised exactly as sqf_quantize_split_act
+ * would quantise it (the norm that precedes the linear layers of the
+ * Llama / Qwen models is RMSNorm; [OSC] structured sub-tensor extraction).
+ * gamma: [k] fp32 device array, 4-byte aligned; 0 <= eps <= 1.  Bf16 branch
+ * and SQF_I4X2 / SQF_I4_E2M3 low codes only (SQF_ERR_UNSUPPORTED otherwise);
+ * gamma is staged in LDS, so k is bounded by the kernel's LDS budget
+ * (SQF_ERR_SHAPE beyond it; about 30000 channels).  Other arguments and
+ * errors as sqf_quantize_split_act. */
+sqf_status sqf_rmsnorm_quantize_split_act(const void* x, int32_t x_dtype, int64_t ldx,
+                                          const float* gamma, float eps, const int32_t* map,
+                                          sqf_acts* a, void* stream);
+
 /* a3-a5 (and the weight-side masked path) -- the fused dual GEMM.
  * y: [a->m][ldy] fp32, ldy >= n.  The low path runs on int8 MFMA with exact
  * int32 accumulation (SQF_I4X2: int4 codes unpacked in registers), on the

@@ -60,9 +60,16 @@ constexpr int kImgSlack = 16;
 // RAGGED: k, ldx or x not aligned to 8-channel chunks.  Rows and the map are
 // then read element by element (channels past k read as absent: neither a
 // low slot nor an outlier); everything after the loads is the same.
-template <int XT, int LOW, int BR, bool GROUPED, int NT, int CPT, bool RAGGED>
+// NORM: the rows are RMS-normalised first (the norm's epilogue fused into
+// the split): r = 1/sqrt(mean x^2 + eps) from an fp64 sum of squares across
+// the block, rounded once to fp32; every value the split reads is then
+// (x * r) * gamma[c] in fp32, gamma held in LDS.  One more barrier per row.
+template <int XT, int LOW, int BR, bool GROUPED, int NT, int CPT, bool RAGGED, bool NORM = false>
 __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
+  static_assert(!NORM || (!GROUPED && BR == kBF16 && (LOW == kI4X2 || LOW == kI4E2M3)),
+                "the fused norm comes with one map, a bf16 branch and int4 codes");
   extern __shared__ uint8_t sm[];
+  __shared__ double ss_red[2][16];  // NORM: per-wave sums of squares
   constexpr int ESZ = BR == kBF16 ? 2 : 1;
   constexpr int NW = NT / 64;
   constexpr int OPT = 4;  // outlier channels gathered per thread per pass
@@ -76,6 +83,8 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
   float* red = (float*)(sm + 2 * img_bytes + ((p.k_out * 4 + 15) & ~(int64_t)15));
   uint32_t* bmax0 = (uint32_t*)(red + 2 * 2 * 16);
   const int nblk = LOW == kMXFP4 ? (int)(ldk / 16) : 0;  // 32-slot blocks per row
+  // NORM: gamma[k] after the other regions (16-byte aligned)
+  float* gam = (float*)((uint8_t*)bmax0 + ((2 * nblk * 4 + 15) & ~15));
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const float qlow = LOW == kI8 ? 127.0f : 7.0f;
   const float qhi = BR == kFP8 ? 448.0f : 127.0f;
@@ -84,6 +93,8 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
   // both images (and the block maxima) start zeroed
   for (int j = tid * 16; j < 2 * img_bytes; j += NT * 16) *(uint4*)(img0 + j) = make_uint4(0, 0, 0, 0);
   for (int j = tid; j < 2 * nblk; j += NT) bmax0[j] = 0u;
+  if constexpr (NORM)
+    for (int64_t c = tid; c < (p.k + 7) / 8 * 8; c += NT) gam[c] = c < p.k ? p.gamma[c] : 0.0f;
 
   // Per-chunk constants (chunk i of this thread = channels 8*(tid + i*NT) ..+7):
   //   cw   (low slots before the chunk) << 8 | outlier mask (bit e = channel e)
@@ -289,10 +300,59 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
 #pragma unroll
       for (int d = 0; d < (XT == kBF16 ? 4 : 1); ++d) asm volatile("" : "+v"(am[i][d]));
     }
+    // ---- NORM: the row's r = 1/sqrt(mean x^2 + eps) ----
+    float rn = 1.0f;
+    if constexpr (NORM) {
+      double ss = 0.0;
+#pragma unroll
+      for (int i = 0; i < CPT; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const double v = (double)val(raw, i, e);  // absent channels read 0
+          ss += v * v;
+        }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, kWave);
+      if (lane == 0) ss_red[buf][wv] = ss;
+      lds_barrier();  // (N) per-wave sums in place
+      double tot = 0.0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) tot += ss_red[buf][w];
+      rn = (float)(1.0 / sqrt(tot / (double)p.k + (double)p.eps));
+    }
+    // NORM: the normalised row, (x * r) * gamma[c] in fp32, formed once
+    // (gamma from LDS, zero-padded to whole chunks)
+    float xn[NORM ? CPT : 1][8];
+    if constexpr (NORM) {
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const int64_t c8 = ((int64_t)tid + (int64_t)i * NT) * 8;
+        const int64_t cg = c8 < p.k ? c8 : 0;
+        const float4 g0 = *(const float4*)(gam + cg), g1 = *(const float4*)(gam + cg + 4);
+        const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float t = val(raw, i, e) * rn;
+          xn[i][e] = t * gv[e];
+        }
+      }
+    }
+    // the value the split quantises: x, or with NORM the normalised x
+    auto nval = [&](int i, int e) -> float {
+      if constexpr (NORM) return xn[i][e];
+      else return val(raw, i, e);
+    };
     // ---- absmax over the low channels (and the outlier channels) ----
     float alo = 0.0f, ahi = 0.0f;
     uint32_t* bmax = bmax0 + buf * nblk;
-    if constexpr (LOW == kMXFP4) {
+    if constexpr (NORM) {
+      // low channels only (outliers and absent channels carry a cw bit)
+#pragma unroll
+      for (int i = 0; i < CPT; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (!((cw[i] >> e) & 1u)) alo = fmaxf(alo, fabsf(nval(i, e)));
+    } else if constexpr (LOW == kMXFP4) {
       // MXFP4: the |x| maxima of each 32-slot block, as fp32 bit patterns
       // (integer order = float order for |x|), two blocks per chunk at most,
       // combined with LDS atomic max
@@ -375,13 +435,14 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
     for (int u = 0; u < OPT; ++u) {
       const int t = tid + u * NT;
       if (t < k_out) {
-        if constexpr (BR == kBF16) ((uint16_t*)xo)[t] = (uint16_t)bf16_rne(ov[u]);
+        if constexpr (NORM) ((uint16_t*)xo)[t] = (uint16_t)bf16_rne((ov[u] * rn) * gam[oidx[t]]);
+        else if constexpr (BR == kBF16) ((uint16_t*)xo)[t] = (uint16_t)bf16_rne(ov[u]);
         else if constexpr (BR == kFP8) xo[t] = (uint8_t)e4m3_rne_sat(ov[u] * inv_hi);
         else xo[t] = (uint8_t)quant_code(ov[u], inv_hi, qhi);
       }
     }
     for (int t = OPT * NT + tid; t < k_out; t += NT) {  // outliers beyond the registers
-      const float x = xval(m, oidx[t]);
+      const float x = NORM ? (xval(m, oidx[t]) * rn) * gam[oidx[t]] : xval(m, oidx[t]);
       if constexpr (BR == kBF16) ((uint16_t*)xo)[t] = (uint16_t)bf16_rne(x);
       else if constexpr (BR == kFP8) xo[t] = (uint8_t)e4m3_rne_sat(x * inv_hi);
       else xo[t] = (uint8_t)quant_code(x, inv_hi, qhi);
@@ -390,10 +451,12 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
       if constexpr (BR == kBF16) ((uint16_t*)xo)[t] = 0;
       else xo[t] = 0;
     }
+    if constexpr (!NORM) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i)
+      for (int i = 0; i < CPT; ++i)
 #pragma unroll
-      for (int w = 0; w < WPC; ++w) asm volatile("" : "+v"(raw[i][w]));
+        for (int w = 0; w < WPC; ++w) asm volatile("" : "+v"(raw[i][w]));
+    }
     // ---- low codes: compacted, packed and OR-ed into the image row ----
     uint32_t* im = (uint32_t*)img;
 #pragma unroll
@@ -417,7 +480,7 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
 #pragma clang fp contract(off)
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float prod = val(raw, i, e) * inv_lo;
+            const float prod = nval(i, e) * inv_lo;
             y[e] = __float_as_uint(prod + kRoundMagic);
           }
         }
@@ -506,9 +569,9 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
   }
 }
 
-template <int XT, int LOW, int BR, bool GROUPED, int NT, int CPT, bool RAGGED = false>
+template <int XT, int LOW, int BR, bool GROUPED, int NT, int CPT, bool RAGGED = false, bool NORM = false>
 static hipError_t launch_one(const ActArgs& a, size_t lds, hipStream_t s) {
-  auto kern = k_act_split<XT, LOW, BR, GROUPED, NT, CPT, RAGGED>;
+  auto kern = k_act_split<XT, LOW, BR, GROUPED, NT, CPT, RAGGED, NORM>;
   // about 16 waves per CU over the 256 CUs (32 single-wave blocks); each
   // block walks a set of rows, so the per-block setup (the channel map) is
   // amortised
@@ -523,26 +586,30 @@ static hipError_t launch_one(const ActArgs& a, size_t lds, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int XT, int LOW, int BR, bool GROUPED>
+template <int XT, int LOW, int BR, bool GROUPED, bool NORM = false>
 static hipError_t launch_shape(const ActArgs& a, bool ragged, size_t lds, hipStream_t s) {
   const int64_t chunks = (a.k + 7) / 8;
   if constexpr (!GROUPED) {
     if (ragged) {
-      if (chunks <= 256) return launch_one<XT, LOW, BR, false, 64, 4, true>(a, lds, s);
-      return launch_one<XT, LOW, BR, false, 1024, 8, true>(a, lds, s);
+      if (chunks <= 256) return launch_one<XT, LOW, BR, false, 64, 4, true, NORM>(a, lds, s);
+      if constexpr (NORM) return launch_one<XT, LOW, BR, false, 512, 8, true, NORM>(a, lds, s);
+      return launch_one<XT, LOW, BR, false, 1024, 8, true, NORM>(a, lds, s);
     }
   }
   // rows of up to 2048 channels: one wave per block, so that the per-row
   // reduction and image hand-off need no cross-wave barrier wait and many
   // more rows are in flight per CU
-  if (chunks <= 64) return launch_one<XT, LOW, BR, GROUPED, 64, 1>(a, lds, s);
-  if (chunks <= 128) return launch_one<XT, LOW, BR, GROUPED, 64, 2>(a, lds, s);
-  if (chunks <= 256) return launch_one<XT, LOW, BR, GROUPED, 64, 4>(a, lds, s);
-  if (chunks <= 512) return launch_one<XT, LOW, BR, GROUPED, 256, 2>(a, lds, s);
-  if (chunks <= 1024) return launch_one<XT, LOW, BR, GROUPED, 512, 2>(a, lds, s);
-  if (chunks <= 2048) return launch_one<XT, LOW, BR, GROUPED, 512, 4>(a, lds, s);
-  if (chunks <= 4096) return launch_one<XT, LOW, BR, GROUPED, 1024, 4>(a, lds, s);
-  return launch_one<XT, LOW, BR, GROUPED, 1024, 8>(a, lds, s);
+  if (chunks <= 64) return launch_one<XT, LOW, BR, GROUPED, 64, 1, false, NORM>(a, lds, s);
+  if (chunks <= 128) return launch_one<XT, LOW, BR, GROUPED, 64, 2, false, NORM>(a, lds, s);
+  if (chunks <= 256) return launch_one<XT, LOW, BR, GROUPED, 64, 4, false, NORM>(a, lds, s);
+  if (chunks <= 512) return launch_one<XT, LOW, BR, GROUPED, 256, 2, false, NORM>(a, lds, s);
+  if (chunks <= 1024) return launch_one<XT, LOW, BR, GROUPED, 512, 2, false, NORM>(a, lds, s);
+  if (chunks <= 2048) return launch_one<XT, LOW, BR, GROUPED, 512, 4, false, NORM>(a, lds, s);
+  // the fused norm's rows live in registers as fp32: 512 threads (up to 256
+  // VGPRs each) rather than 1024 (128)
+  if constexpr (NORM) return launch_one<XT, LOW, BR, GROUPED, 512, 8, false, NORM>(a, lds, s);
+  if (chunks <= 4096) return launch_one<XT, LOW, BR, GROUPED, 1024, 4, false, NORM>(a, lds, s);
+  return launch_one<XT, LOW, BR, GROUPED, 1024, 8, false, NORM>(a, lds, s);
 }
 
 template <int XT, int LOW, bool GROUPED>
@@ -552,15 +619,24 @@ static hipError_t launch_br(const ActArgs& a, int br, bool ragged, size_t lds, h
   return launch_shape<XT, LOW, kI8, GROUPED>(a, ragged, lds, s);
 }
 
-size_t act_split_lds_bytes(int64_t ldk, int64_t k_out, int low) {
+size_t act_split_lds_bytes(int64_t ldk, int64_t k_out, int low, int64_t norm_k) {
   return (size_t)(2 * (ldk + kImgSlack) + ((k_out * 4 + 15) & ~(int64_t)15) + 2 * 2 * 16 * sizeof(float) +
-                  (low == kMXFP4 ? 2 * (ldk / 16) * 4 : 0));
+                  (low == kMXFP4 ? (2 * (ldk / 16) * 4 + 15) & ~(int64_t)15 : 0) + (norm_k + 7) / 8 * 32);
 }
 
 hipError_t launch_act_split(const ActArgs& a, int x_dtype, int low, int branch, bool grouped,
-                            bool ragged, hipStream_t s) {
-  const size_t lds = act_split_lds_bytes(a.ldk, a.k_out, low);
+                            bool ragged, bool norm, hipStream_t s) {
+  const size_t lds = act_split_lds_bytes(a.ldk, a.k_out, low, norm ? a.k : 0);
   if (a.m <= 0) return hipSuccess;
+  if (norm) {  // one map, bf16 branch, int4 codes (packed or in E2M3 fields)
+    if (grouped || branch != kBF16 || (low != kI4X2 && low != kI4E2M3) || !a.gamma)
+      return hipErrorInvalidValue;
+    if (low == kI4X2)
+      return x_dtype == kBF16 ? launch_shape<kBF16, kI4X2, kBF16, false, true>(a, ragged, lds, s)
+                              : launch_shape<kF32, kI4X2, kBF16, false, true>(a, ragged, lds, s);
+    return x_dtype == kBF16 ? launch_shape<kBF16, kI4E2M3, kBF16, false, true>(a, ragged, lds, s)
+                            : launch_shape<kF32, kI4E2M3, kBF16, false, true>(a, ragged, lds, s);
+  }
   if (low == kI4E2M3) {  // bf16 branch, one weight set: the FP6 GEMM's operand
     if (grouped || branch != kBF16) return hipErrorInvalidValue;
     return x_dtype == kBF16 ? launch_shape<kBF16, kI4E2M3, kBF16, false>(a, ragged, lds, s)

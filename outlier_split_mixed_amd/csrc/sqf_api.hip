@@ -209,7 +209,8 @@ sqf_status check_acts(const sqf_acts* a, const char* who) {
 
 sqf_status quantize_common(const void* x, int32_t x_dtype, int64_t ldx, int64_t groups,
                            const int64_t* row_off, const int32_t* map, sqf_acts* a, bool grouped,
-                           void* stream, const char* who) {
+                           void* stream, const char* who, const float* gamma = nullptr,
+                           float eps = 0.0f) {
   g_err.clear();
   sqf_status st = check_acts(a, who);
   if (st != SQF_OK) return st;
@@ -219,9 +220,18 @@ sqf_status quantize_common(const void* x, int32_t x_dtype, int64_t ldx, int64_t 
     return fail(SQF_ERR_INVALID_ARG, "%s: x_dtype must be SQF_F32 or SQF_BF16", who);
   const int64_t k = a->k_low + a->k_out;
   if (k > 65536) return fail(SQF_ERR_SHAPE, "%s: k=%lld exceeds 65536", who, (long long)k);
-  if (sqf::act_split_lds_bytes(a->ldk, a->k_out, a->low) > 160 * 1024)
-    return fail(SQF_ERR_SHAPE, "%s: k_low=%lld, k_out=%lld exceed the kernel's LDS staging", who,
-                (long long)a->k_low, (long long)a->k_out);
+  const bool norm = gamma != nullptr;
+  if (norm) {
+    if (a->branch != SQF_BF16 || (a->low != SQF_I4X2 && a->low != SQF_I4_E2M3))
+      return fail(SQF_ERR_UNSUPPORTED, "%s: the fused norm comes with a bf16 branch and int4 codes "
+                  "(SQF_I4X2 or SQF_I4_E2M3)", who);
+    if (!(eps >= 0.0f) || eps > 1.0f)
+      return fail(SQF_ERR_INVALID_ARG, "%s: eps must be in [0, 1]", who);
+    if ((uintptr_t)gamma & 3u) return fail(SQF_ERR_ALIGN, "%s: gamma must be 4-byte aligned", who);
+  }
+  if (sqf::act_split_lds_bytes(a->ldk, a->k_out, a->low, norm ? k : 0) > 160 * 1024)
+    return fail(SQF_ERR_SHAPE, "%s: k_low=%lld, k_out=%lld exceed the kernel's LDS staging%s", who,
+                (long long)a->k_low, (long long)a->k_out, norm ? " (with gamma)" : "");
   if (ldx < k) return fail(SQF_ERR_SHAPE, "%s: ldx=%lld < k=%lld", who, (long long)ldx, (long long)k);
   if (((uintptr_t)x & (x_dtype == SQF_BF16 ? 1u : 3u)) || ((uintptr_t)map & 3u))
     return fail(SQF_ERR_ALIGN, "%s: x and map must be aligned to their element size", who);
@@ -238,10 +248,10 @@ sqf_status quantize_common(const void* x, int32_t x_dtype, int64_t ldx, int64_t 
   sqf::ActArgs args{x, ldx, map, row_off, a->m, k, a->k_low, a->k_out, sqf_pad_k_low(a->k_low),
                     a->ldk, a->ldo, low_kblocked(a->low) ? sqf_pad_rows(a->m) : 0,
                     (int32_t)(grouped ? groups : 1), a->x_low, a->s_x, (uint8_t*)a->x_out, a->s_xo,
-                    a->s_xb};
-  return hip_status(
-      sqf::launch_act_split(args, x_dtype, a->low, a->branch, grouped, ragged, (hipStream_t)stream),
-      who);
+                    a->s_xb, gamma, eps};
+  return hip_status(sqf::launch_act_split(args, x_dtype, a->low, a->branch, grouped, ragged, norm,
+                                          (hipStream_t)stream),
+                    who);
 }
 
 sqf_status check_pair(const sqf_acts* a, const sqf_weights* w, const void* y, int64_t ldy,
@@ -485,6 +495,46 @@ sqf_status sqf_quantize_split_act(const void* x, int32_t x_dtype, int64_t ldx, c
                                   sqf_acts* a, void* stream) {
   return quantize_common(x, x_dtype, ldx, 1, nullptr, map, a, false, stream,
                          "sqf_quantize_split_act");
+}
+
+sqf_status sqf_slot_order(const int32_t* map, int64_t k, int32_t* perm_out,
+                          int32_t* slice_map_out, void* stream) {
+  g_err.clear();
+  const char* who = "sqf_slot_order";
+  if (!map || !perm_out || !slice_map_out)
+    return fail(SQF_ERR_INVALID_ARG, "%s: map, perm_out and slice_map_out are required", who);
+  if (k < 1 || k > 1048576)
+    return fail(SQF_ERR_SHAPE, "%s: need 1 <= k <= 1048576 (got %lld)", who, (long long)k);
+  return hip_status(sqf::launch_slot_order(map, k, perm_out, slice_map_out, (hipStream_t)stream),
+                    who);
+}
+
+sqf_status sqf_permute_channels(const float* src, int64_t rows, int64_t cols, int64_t ld_src,
+                                const int32_t* perm, int32_t axis, float* dst, int64_t ld_dst,
+                                void* stream) {
+  g_err.clear();
+  const char* who = "sqf_permute_channels";
+  if (!src || !perm || !dst) return fail(SQF_ERR_INVALID_ARG, "%s: src, perm and dst are required", who);
+  if (axis != 0 && axis != 1) return fail(SQF_ERR_INVALID_ARG, "%s: axis must be 0 or 1", who);
+  if (rows < 0 || cols < 0 || ld_src < cols || ld_dst < cols)
+    return fail(SQF_ERR_SHAPE, "%s: bad shape rows=%lld cols=%lld ld_src=%lld ld_dst=%lld", who,
+                (long long)rows, (long long)cols, (long long)ld_src, (long long)ld_dst);
+  if ((const void*)src == (const void*)dst)
+    return fail(SQF_ERR_INVALID_ARG, "%s: src and dst must not be the same buffer", who);
+  return hip_status(sqf::launch_permute(src, rows, cols, ld_src, perm, axis, dst, ld_dst,
+                                        (hipStream_t)stream),
+                    who);
+}
+
+sqf_status sqf_rmsnorm_quantize_split_act(const void* x, int32_t x_dtype, int64_t ldx,
+                                          const float* gamma, float eps, const int32_t* map,
+                                          sqf_acts* a, void* stream) {
+  if (!gamma) {
+    g_err.clear();
+    return fail(SQF_ERR_INVALID_ARG, "sqf_rmsnorm_quantize_split_act: gamma is required");
+  }
+  return quantize_common(x, x_dtype, ldx, 1, nullptr, map, a, false, stream,
+                         "sqf_rmsnorm_quantize_split_act", gamma, eps);
 }
 
 sqf_status sqf_quantize_split_act_grouped(const void* x, int32_t x_dtype, int64_t ldx,

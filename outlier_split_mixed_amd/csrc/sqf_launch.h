@@ -35,6 +35,8 @@ struct ActArgs {
   uint8_t* x_out;
   float* s_xo;
   uint8_t* s_xb;  // MXFP4: E8M0 block scales, K-blocked [pad/128][rows_pad/64][4][16][4]
+  const float* gamma;  // fused RMS norm: [k] weights (NULL: no norm)
+  float eps;
 };
 
 struct GemmArgs {
@@ -95,10 +97,11 @@ hipError_t launch_select(const float* x_cal, int64_t m_cal, int64_t k, const flo
                          hipStream_t s);
 hipError_t launch_pack(const PackArgs& a, int branch, int low, int groups, hipStream_t s);
 // ragged: k, ldx or x not aligned to 8-channel chunks; element-wise loads
+// norm: RMS-normalise each row with a.gamma / a.eps first (fused)
 hipError_t launch_act_split(const ActArgs& a, int x_dtype, int low, int branch, bool grouped,
-                            bool ragged, hipStream_t s);
+                            bool ragged, bool norm, hipStream_t s);
 // dynamic LDS bytes the activation kernel needs for one block
-size_t act_split_lds_bytes(int64_t ldk, int64_t k_out, int low);
+size_t act_split_lds_bytes(int64_t ldk, int64_t k_out, int low, int64_t norm_k);
 // cfg: 0 = 256x256 tiles (8 waves), 1 = 128x128 (4 waves), 2 = 64x64 (4 waves)
 // ybf16: Y written as bf16 (not together with debug)
 hipError_t launch_dual_gemm(const GemmArgs& a, int branch, bool grouped, bool debug, int cfg,
@@ -107,5 +110,14 @@ hipError_t launch_sq_gemm(const SqArgs& a, bool debug, hipStream_t s);
 // low: kI4E2M3 (int4 codes as E2M3 subnormals, exact sums; debug dumps them)
 // or kMXFP4 (E2M1 with E8M0 block scales; no debug output)
 hipError_t launch_gemm6(const Gemm6Args& a, int low, bool debug, bool ybf16, hipStream_t s);
+
+// slot order of a channel map (perm[p] = channel at position p) and the
+// slice map of the reordered axis
+hipError_t launch_slot_order(const int32_t* map, int64_t k, int32_t* perm, int32_t* slice_map,
+                             hipStream_t s);
+// gather along one axis of a row-major fp32 matrix by perm (axis 1: columns,
+// axis 0: rows)
+hipError_t launch_permute(const float* src, int64_t rows, int64_t cols, int64_t ld_src,
+                          const int32_t* perm, int axis, float* dst, int64_t ld_dst, hipStream_t s);
 
 }  // namespace sqf

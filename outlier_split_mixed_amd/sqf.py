@@ -67,6 +67,9 @@ _decl("sqf_select_channels_noalloc", [P, I64, I64, P, I64, I64, P, P, P, P])
 _decl("sqf_pack_weights", [P, P, P, ctypes.POINTER(sqf_weights), P])
 _decl("sqf_quantize_split_act", [P, I32, I64, P, ctypes.POINTER(sqf_acts), P])
 _decl("sqf_quantize_split_act_grouped", [P, I32, I64, I64, P, P, ctypes.POINTER(sqf_acts), P])
+_decl("sqf_rmsnorm_quantize_split_act", [P, I32, I64, P, ctypes.c_float, P, ctypes.POINTER(sqf_acts), P])
+_decl("sqf_slot_order", [P, I64, P, P, P])
+_decl("sqf_permute_channels", [P, I64, I64, I64, P, I32, P, I64, P])
 _decl("sqf_dual_gemm", [ctypes.POINTER(sqf_acts), ctypes.POINTER(sqf_weights), P, I64, P, P, P, P])
 _decl("sqf_dual_gemm_grouped", [ctypes.POINTER(sqf_acts), ctypes.POINTER(sqf_weights), I64, P, P,
                                 I64, P, P])
@@ -306,6 +309,37 @@ def sqf_quantize_split_act(x: torch.Tensor, mp: torch.Tensor, out: Acts, stream=
     _check(_lib.sqf_quantize_split_act(_ptr(x), xd, x.stride(0), _ptr(mp), ctypes.byref(d),
                                        _stream(stream)))
     return out
+
+
+def sqf_rmsnorm_quantize_split_act(x: torch.Tensor, gamma: torch.Tensor, eps: float,
+                                   mp: torch.Tensor, out: Acts, stream=None) -> Acts:
+    """a2 with the RMS norm in front of it fused in: x [m][k] (fp32 or
+    bf16), gamma [k] fp32 -> fills ``out``."""
+    xd = SQF_BF16 if x.dtype == torch.bfloat16 else SQF_F32
+    assert gamma.dtype == torch.float32 and gamma.is_contiguous()
+    d = out.desc()
+    _check(_lib.sqf_rmsnorm_quantize_split_act(_ptr(x), xd, x.stride(0), _ptr(gamma), float(eps),
+                                               _ptr(mp), ctypes.byref(d), _stream(stream)))
+    return out
+
+
+def sqf_slot_order(mp: torch.Tensor, stream=None):
+    """(perm, slice_map) of a channel map: the slot order and the map of the
+    reordered axis."""
+    k = mp.numel()
+    perm = torch.empty(k, dtype=torch.int32, device=mp.device)
+    sm = torch.empty(k, dtype=torch.int32, device=mp.device)
+    _check(_lib.sqf_slot_order(_ptr(mp), k, _ptr(perm), _ptr(sm), _stream(stream)))
+    return perm, sm
+
+
+def sqf_permute_channels(src: torch.Tensor, perm: torch.Tensor, axis: int, stream=None):
+    """src [rows][cols] fp32 gathered along ``axis`` by perm (a new tensor)."""
+    assert src.dtype == torch.float32 and src.dim() == 2 and src.stride(1) == 1
+    dst = torch.empty(src.shape, dtype=torch.float32, device=src.device)
+    _check(_lib.sqf_permute_channels(_ptr(src), src.shape[0], src.shape[1], src.stride(0),
+                                     _ptr(perm), axis, _ptr(dst), dst.stride(0), _stream(stream)))
+    return dst
 
 
 def sqf_quantize_split_act_grouped(x: torch.Tensor, row_off: torch.Tensor, maps: torch.Tensor,

@@ -26,7 +26,7 @@ def _declared_functions():
 
 def test_every_declared_symbol_is_exported(sqf):
     names = _declared_functions()
-    assert len(names) == 16
+    assert len(names) == 19
     for name in names:
         assert hasattr(sqf._lib, name), name
 
@@ -170,6 +170,32 @@ def test_noalloc_select_argument_errors(sqf):
     assert f(mem(), 4, 8, mem(), 4, 2, mem(), None, None, None) == 1
     assert f(mem(), 4, 65537, mem(), 4, 2, mem(), mem(), None, None) == 2
     assert "65536" in sqf.sqf_last_error()
+
+
+def test_producer_side_argument_errors(sqf):
+    """The fused norm + split, the slot order and the channel permutation
+    refuse bad arguments before any launch."""
+    mem = FakeMem()
+    f = sqf._lib.sqf_rmsnorm_quantize_split_act
+    a = _acts(sqf, mem)
+    assert f(mem(), sqf.SQF_BF16, 512, None, 1e-5, mem(), ctypes.byref(a), None) == 1  # no gamma
+    assert f(mem(), sqf.SQF_BF16, 512, mem(), -1.0, mem(), ctypes.byref(a), None) == 1  # eps
+    assert f(mem(), sqf.SQF_BF16, 512, mem(misalign=2), 1e-5, mem(), ctypes.byref(a), None) == 5
+    a8 = _acts(sqf, mem, branch="fp8")
+    assert f(mem(), sqf.SQF_BF16, 512, mem(), 1e-5, mem(), ctypes.byref(a8), None) == 3
+    am, _ = _mx_pair(sqf, mem)
+    assert f(mem(), sqf.SQF_BF16, 512, mem(), 1e-5, mem(), ctypes.byref(am), None) == 3
+    big = _acts(sqf, mem, k=60000, k_out=64)  # gamma does not fit next to the images
+    assert f(mem(), sqf.SQF_BF16, 60000, mem(), 1e-5, mem(), ctypes.byref(big), None) == 2
+    so = sqf._lib.sqf_slot_order
+    assert so(None, 8, mem(), mem(), None) == 1
+    assert so(mem(), 0, mem(), mem(), None) == 2
+    pc = sqf._lib.sqf_permute_channels
+    assert pc(mem(), 4, 8, 8, mem(), 2, mem(), 8, None) == 1  # axis
+    assert pc(mem(), 4, 8, 4, mem(), 1, mem(), 8, None) == 2  # ld_src < cols
+    b = mem()
+    assert pc(b, 4, 8, 8, mem(), 1, b, 8, None) == 1  # in place
+    assert sqf.sqf_last_error() != ""
 
 
 def test_pack_argument_errors(sqf):
