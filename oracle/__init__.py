@@ -19,6 +19,9 @@ the method:
 * :func:`dual_gemm`        -- low path + masked path + branch + fused output.
 * :func:`i4x2_to_e2m3`     -- the same int4 codes stored in 6-bit E2M3 fields,
   K-blocked (the storage a 6-bit matrix unit reads).
+* :func:`sqf_row`, :func:`pack_weights_sqf`, :func:`dual_gemm_sqf` -- the
+  floating-point weight-side SQ-format (FP4 E2M1 low part with the 0x8 mark,
+  FP8 E4M3 sparse values; SQ-format article, section 八).
 * :func:`rmsnorm`, :func:`rmsnorm_quantize_split_act` -- the norm in front
   of the split, and the two composed; :func:`slot_order` -- the channel
   order that turns the split into a slice (SQ-format article, section 九).
@@ -120,6 +123,14 @@ def _declare(lib):
     lib.orc_rmsnorm.restype = None
     lib.orc_slot_order.argtypes = [P, I64, P, P]
     lib.orc_slot_order.restype = None
+    lib.orc_sqf_row.argtypes = [P, P, I64, I64, I64, P, P, P, P]
+    lib.orc_sqf_row.restype = None
+    lib.orc_pack_weights_sqf.argtypes = [P, I64, I64, P, P, I64, I64, I64, I64, I64, I64, P, P, P, P,
+                                         P, P]
+    lib.orc_pack_weights_sqf.restype = None
+    lib.orc_dual_gemm_sqf.argtypes = [I64, I64, I64, P, I64, P, I64, P, P, I64, P, P, I64, P, I64, P,
+                                      P, P, P, P, I64]
+    lib.orc_dual_gemm_sqf.restype = None
     lib.orc_num_threads.argtypes = []
     lib.orc_num_threads.restype = ctypes.c_int
 
@@ -462,3 +473,65 @@ def slot_order(mp: np.ndarray):
     sm = np.zeros(len(mp), np.int32)
     _load().orc_slot_order(_p(mp), len(mp), _p(perm), _p(sm))
     return perm, sm
+
+
+# ---------------------------------------------------------------- FP8/FP4 SQ-format
+def sqf_row(wrow: np.ndarray, hdiag: np.ndarray, nnz: int, bank: int = 0):
+    """One floating-point SQ-format row -> (fields u8 [k_low] (E2M1, 0x8 =
+    mark), v8 u8 [nnz] (E4M3), s8, s4)."""
+    wrow = np.ascontiguousarray(wrow, dtype=np.float32)
+    hdiag = np.ascontiguousarray(hdiag, dtype=np.float32)
+    k_low = len(wrow)
+    bank = _check_bank(k_low, nnz, bank)
+    fields = np.zeros(max(k_low, 1), np.uint8)
+    v8 = np.zeros(max(nnz, 1), np.uint8)
+    s8 = np.zeros(1, np.float32)
+    s4 = np.zeros(1, np.float32)
+    _load().orc_sqf_row(_p(wrow), _p(hdiag), k_low, nnz, bank, _p(fields), _p(v8), _p(s8), _p(s4))
+    return fields[:k_low], v8[:nnz], s8[0], s4[0]
+
+
+def pack_weights_sqf(w: np.ndarray, mp: np.ndarray, hdiag: np.ndarray, nnz: int, bank: int = 0):
+    """Floating-point SQ-format weights with an E4M3 branch over the outlier channels."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    mp = np.ascontiguousarray(mp, dtype=np.int32)
+    hdiag = np.ascontiguousarray(hdiag, dtype=np.float32)
+    k, n = w.shape
+    k_out = int((mp < 0).sum())
+    k_low = k - k_out
+    bank = _check_bank(k_low, nnz, bank)
+    ldk = pad_k_low(k_low) // 2
+    ldo = pad_k_out(k_out, "fp8")
+    w_low = np.zeros((n, ldk), np.uint8)
+    s_w4 = np.zeros(n, np.float32)
+    sq_val = np.zeros((n, max(nnz, 1)), np.uint8)
+    s_w8 = np.zeros(n, np.float32)
+    w_out = np.zeros((n, ldo), np.uint8)
+    s_wo = np.zeros(n, np.float32)
+    _load().orc_pack_weights_sqf(_p(w), k, n, _p(mp), _p(hdiag), k_low, k_out, ldk, ldo, nnz, bank,
+                                 _p(w_low), _p(s_w4), _p(sq_val), _p(s_w8),
+                                 _p(w_out) if ldo else None, _p(s_wo))
+    return dict(w_low=w_low, s_w=s_w4, sq_val=sq_val[:, :nnz].copy(), s_w8=s_w8, w_out=w_out,
+                s_wo=s_wo, k_low=k_low, k_out=k_out, ldk=ldk, ldo=ldo, branch="fp8", sq_nnz=nnz,
+                sq_bank=bank, low="fp4")
+
+
+def dual_gemm_sqf(a: dict, w: dict, rows=None):
+    """Y of the floating-point SQ-format (activations from
+    quantize_split_act(..., low="fp8", branch="fp8"))."""
+    assert a["low"] == "fp8" and a["branch"] == "fp8" and w["branch"] == "fp8"
+    m = a["x_low"].shape[0] if a["x_low"].size else a["x_out"].shape[0]
+    if rows is None:
+        rows = np.arange(m, dtype=np.int64)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    n = w["s_w"].shape[0]
+    assert a["k_low"] == w["k_low"] and a["k_out"] == w["k_out"]
+    y = np.zeros((len(rows), n), np.float32)
+    nnz = w["sq_nnz"]
+    _load().orc_dual_gemm_sqf(n, a["k_low"], a["k_out"], _p(rows), len(rows),
+                              _p(a["x_low"]) if a["x_low"].size else None, a["ldk"], _p(a["s_x"]),
+                              _p(a["x_out"]) if a["x_out"].size else None, a["ldo"], _p(a["s_xo"]),
+                              _p(w["w_low"]) if w["w_low"].size else None, w["ldk"], _p(w["s_w"]),
+                              nnz, _p(w["sq_val"]) if nnz else None, _p(w["s_w8"]),
+                              _p(w["w_out"]) if w["w_out"].size else None, _p(w["s_wo"]), _p(y), n)
+    return y

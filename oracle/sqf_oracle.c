@@ -102,6 +102,10 @@ uint8_t orc_e4m3_from_float(float v) {
   return (uint8_t)(best | ((v < 0.0f && best != 0) ? 0x80 : 0));
 }
 
+/* OCP E2M1 (FP4) conversions, defined with the MXFP4 steps below. */
+double orc_e2m1_to_double(uint8_t c);
+uint8_t orc_e2m1_from_double(double t);
+
 /* Signed int4 nibble -> code.  0x8 is the reserved mark; it contributes 0 to
  * the dense low-precision product [SQF-art section 三: the low part is
  * consumed by ordinary matrix units, the marked positions by a separate
@@ -397,6 +401,124 @@ void orc_pack_weights_sq(const float* w, int64_t k, int64_t n, const int32_t* ma
   free(hi);
   free(hlo);
   free(lo);
+}
+
+/* ------------------------------------------------------------------ */
+/* Floating-point weight-side SQ-format: FP4 low part, FP8 sparse part */
+/* ------------------------------------------------------------------ */
+
+/* [SQF-art section 八: the format with floating-point types, FP8 for the
+ * high-precision part and FP4 for the low part at 87.5% sparsity, about 5
+ * bits per weight.]  Readings: FP4 = OCP E2M1, FP8 = OCP E4M3; the reserved
+ * mark of the dense FP4 codes is 0x8 (E2M1 negative zero, which the encoder
+ * never produces: a value that rounds to zero is +0); one scale per output
+ * row for each part, as in the integer form: the kept values are E4M3 codes
+ * of v * 448/a8 (s_w8 = a8/448), the others E2M1 codes of v * inv4 with
+ * inv4 = 6/a4 as one fp32 division (s_w4 = a4/6), a4 the absmax over the
+ * unmarked slots.  The marks are chosen exactly as in the integer form
+ * (orc_sq_row: key w^2 * hdiag, banks, ties to the lower slot).  fields[j]
+ * receives the 4-bit field of slot j, v8[0..nnz) the E4M3 bytes in slot
+ * order. */
+void orc_sqf_row(const float* wrow, const float* hdiag, int64_t k_low, int64_t nnz, int64_t bank,
+                 uint8_t* fields, uint8_t* v8, float* s8, float* s4) {
+  int8_t* dummy8 = (int8_t*)malloc((size_t)(nnz + 1));
+  float* tmp = (float*)malloc(sizeof(float) * (size_t)(k_low + 1));
+  int32_t* codes = (int32_t*)malloc(sizeof(int32_t) * (size_t)(k_low + 1));
+  float s_int8, s_int4;
+  /* the marks: the integer form's choice (its codes are not used) */
+  orc_sq_row(wrow, hdiag, k_low, nnz, bank, 4, fields, dummy8, &s_int8, &s_int4);
+  int64_t c = 0;
+  for (int64_t j = 0; j < k_low; ++j)
+    if (fields[j] == 0x8) tmp[c++] = wrow[j];
+  *s8 = orc_quantize_vec(tmp, c, ORC_FP8, codes);
+  for (int64_t i = 0; i < c; ++i) v8[i] = (uint8_t)(codes[i] & 0xFF);
+  float a = 0.0f;
+  for (int64_t j = 0; j < k_low; ++j)
+    if (fields[j] != 0x8 && fabsf(wrow[j]) > a) a = fabsf(wrow[j]);
+  float inv = a == 0.0f ? 0.0f : 6.0f / a;
+  *s4 = a == 0.0f ? 0.0f : a / 6.0f;
+  for (int64_t j = 0; j < k_low; ++j)
+    if (fields[j] != 0x8) fields[j] = orc_e2m1_from_double((double)(wrow[j] * inv));
+  free(codes);
+  free(tmp);
+  free(dummy8);
+}
+
+/* Whole weight matrix in the floating-point SQ-format with an E4M3 branch
+ * over the outlier channels (scale s_wo per output row). */
+void orc_pack_weights_sqf(const float* w, int64_t k, int64_t n, const int32_t* map,
+                          const float* hdiag_k, int64_t k_low, int64_t k_out, int64_t ldk,
+                          int64_t ldo, int64_t nnz, int64_t bank, uint8_t* w_low, float* s_w4,
+                          uint8_t* sq_val, float* s_w8, uint8_t* w_out, float* s_wo) {
+  float* lo = (float*)malloc(sizeof(float) * (size_t)(k_low + 1));
+  float* hlo = (float*)malloc(sizeof(float) * (size_t)(k_low + 1));
+  float* hi = (float*)malloc(sizeof(float) * (size_t)(k_out + 1));
+  uint8_t* fields = (uint8_t*)malloc((size_t)(k_low + 1));
+  int32_t* codes = (int32_t*)malloc(sizeof(int32_t) * (size_t)(k + 1));
+  for (int64_t c = 0; c < k; ++c)
+    if (map[c] >= 0) hlo[map[c]] = hdiag_k[c];
+  for (int64_t nn = 0; nn < n; ++nn) {
+    for (int64_t c = 0; c < k; ++c) {
+      if (map[c] >= 0)
+        lo[map[c]] = w[c * n + nn];
+      else
+        hi[-map[c] - 1] = w[c * n + nn];
+    }
+    orc_sqf_row(lo, hlo, k_low, nnz, bank, fields, sq_val + nn * nnz, &s_w8[nn], &s_w4[nn]);
+    uint8_t* row = w_low + nn * ldk;
+    memset(row, 0, (size_t)ldk);
+    for (int64_t j = 0; j < k_low; ++j)
+      row[j >> 1] |= (uint8_t)((j & 1) ? (fields[j] << 4) : fields[j]);
+    if (ldo > 0)
+      s_wo[nn] = store_branch_row(hi, k_out, ORC_FP8, w_out + nn * ldo, ldo, codes);
+    else
+      s_wo[nn] = 0.0f;
+  }
+  free(codes);
+  free(fields);
+  free(hi);
+  free(hlo);
+  free(lo);
+}
+
+/* y of the floating-point SQ-format for the token rows rows[0..nr): E4M3
+ * activations (per-token scale s_x over the low channels), E2M1 weights with
+ * the 0x8 mark, E4M3 sparse values, E4M3 branch:
+ *   acc_low = sum_j e4m3(cx_j) * e2m1(cw_j)        (unmarked slots)
+ *   acc_sp  = sum_i e4m3(cx_pos_i) * e4m3(v8_i)     (i-th marked slot)
+ *   acc_o   = sum_t e4m3(xo_t) * e4m3(wo_t)
+ *   y = s_x * (s_w4 * acc_low + s_w8 * acc_sp) + (s_xo * s_wo) * acc_o
+ * in fp64 (every product and these sums are exact there), rounded once to
+ * fp32.  [SQF-art section 三: two paths summed; 八: the FP8/FP4 form.] */
+void orc_dual_gemm_sqf(int64_t n, int64_t k_low, int64_t k_out, const int64_t* rows, int64_t nr,
+                       const uint8_t* x_low, int64_t ldk_x, const float* s_x, const uint8_t* x_out,
+                       int64_t ldo, const float* s_xo, const uint8_t* w_low, int64_t ldk_w,
+                       const float* s_w4, int64_t nnz, const uint8_t* sq_val, const float* s_w8,
+                       const uint8_t* w_out, const float* s_wo, float* y, int64_t ldy) {
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int64_t r = 0; r < nr; ++r) {
+    for (int64_t nn = 0; nn < n; ++nn) {
+      int64_t mm = rows[r];
+      double acc = 0.0, acc_sp = 0.0, acc_o = 0.0;
+      int64_t i_sp = 0;
+      for (int64_t j = 0; j < k_low; ++j) {
+        double vx = orc_e4m3_to_double(x_low[mm * ldk_x + j]);
+        uint8_t b = w_low[nn * ldk_w + (j >> 1)];
+        uint8_t f = (uint8_t)(((j & 1) ? (b >> 4) : b) & 0xF);
+        if (f == 0x8) {
+          acc_sp += vx * orc_e4m3_to_double(sq_val[nn * nnz + i_sp]);
+          ++i_sp;
+        } else {
+          acc += vx * orc_e2m1_to_double(f);
+        }
+      }
+      for (int64_t t = 0; t < k_out; ++t)
+        acc_o += orc_e4m3_to_double(x_out[mm * ldo + t]) * orc_e4m3_to_double(w_out[nn * ldo + t]);
+      double out = (double)s_x[mm] * ((double)s_w4[nn] * acc + (double)s_w8[nn] * acc_sp);
+      if (k_out > 0) out += ((double)s_xo[mm] * (double)s_wo[nn]) * acc_o;
+      y[r * ldy + nn] = (float)out;
+    }
+  }
 }
 
 /* ------------------------------------------------------------------ */

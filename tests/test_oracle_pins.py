@@ -838,3 +838,63 @@ def test_slot_order_leaves_the_layer_unchanged():
         assert np.array_equal(w0[key], w1[key])
     assert np.array_equal(oracle.dual_gemm(a0, w0), oracle.dual_gemm(a1, w1))
     assert sorted(perm.tolist()) == list(range(lay.k))
+
+
+# ------------------------------------------------------------------ FP8/FP4 SQ-format
+def test_sqf_fp_hand_case(golden):
+    g = golden("sqf_fp_hand_case.txt")
+    wl = [float(v) for v in g["w_low"][0]]
+    w = np.array(wl + [float(g["w_out"][0][0])], np.float32).reshape(9, 1)
+    x = np.array([[float(v) for v in g["x_low"][0]] + [float(g["x_out"][0][0])]], np.float32)
+    mp = np.array([0, 1, 2, 3, 4, 5, 6, 7, -1], np.int32)
+    hd = np.ones(9, np.float32)
+    wp = oracle.pack_weights_sqf(w, mp, hd, 1)
+    assert wp["w_low"][0, :4].tolist() == _hexbytes(g["fields_bytes"])[0].tolist()
+    assert not wp["w_low"][0, 4:].any()
+    assert wp["sq_val"][0].tolist() == _hexbytes(g["v8"])[0].tolist()
+    assert wp["s_w8"][0] == np.float32(12.0) / np.float32(448.0)
+    assert wp["s_w"][0] == np.float32(0.5)
+    assert int(wp["w_out"][0, 0]) == int(g["wo_code"][0][0], 16)
+    a = oracle.quantize_split_act(x, mp, low="fp8", branch="fp8")
+    assert a["x_low"][0, :8].tolist() == _hexbytes(g["x_codes"])[0].tolist()
+    assert int(a["x_out"][0, 0]) == int(g["xo_code"][0][0], 16)
+    y = oracle.dual_gemm_sqf(a, wp)
+    assert abs(float(y[0, 0]) - float(g["y"][0][0])) <= 48.5 * 4e-7
+
+
+def test_sqf_fp_mark_never_a_value_and_five_bits():
+    """The FP4 encoder never produces 0x8 (a value rounding to zero is +0),
+    so every 0x8 field is a mark: exactly nnz per row; storage is 4 bits per
+    slot plus 8 per kept value, 5 bits per weight at 1/8 kept."""
+    lay = synth.draw_layer("sqf", 41, 0, 4, 2304, 48, 64, 256)
+    _, mp, _, hd = oracle.select_channels(lay.x_cal, lay.w, 256)
+    k_low = 2048
+    wp = oracle.pack_weights_sqf(lay.w, mp, hd, k_low // 8)
+    nib = np.stack([wp["w_low"] & 0xF, wp["w_low"] >> 4], -1).reshape(48, -1)[:, :k_low]
+    assert ((nib == 8).sum(axis=1) == k_low // 8).all()
+    f, _, _, _ = oracle.sqf_row(-np.abs(lay.w[:k_low, 0]) * 1e-3, np.ones(k_low, np.float32), 0)
+    assert not (f == 8).any()  # tiny negatives round to +0, never to the mark
+    bits = (wp["w_low"].nbytes * 8 + wp["sq_val"].nbytes * 8) / (48 * k_low)
+    assert bits == 5.0
+
+
+def test_sqf_fp_error_bound():
+    """|Y - XW| within the sum of the parts' rounding bounds: E4M3 (2^-4
+    relative) on activations and kept values, E2M1 (half a step at the
+    largest code: s4) on the low weights, E4M3 on the branch."""
+    lay = synth.draw_layer("sqfb", 42, 0, 6, 1280, 32, 64, 128)
+    _, mp, _, hd = oracle.select_channels(lay.x_cal, lay.w, 128)
+    wp = oracle.pack_weights_sqf(lay.w, mp, hd, 144)
+    a = oracle.quantize_split_act(lay.x, mp, low="fp8", branch="fp8")
+    y = oracle.dual_gemm_sqf(a, wp).astype(np.float64)
+    x64, w64 = lay.x.astype(np.float64), lay.w.astype(np.float64)
+    ref = x64 @ w64
+    # per-element bounds: |x| 2^-4 + s_x 2^-9 (subnormal step) ...; |w| low: s4; kept: 2^-4 |w|
+    low = mp >= 0
+    ex = np.abs(x64) * 2.0 ** -4 + a["s_x"][:, None] * 2.0 ** -9
+    ew = np.where(low[:, None], wp["s_w"][None, :] * 1.0, 0.0) + np.abs(w64) * 2.0 ** -4 \
+        + wp["s_w8"][None, :] * 2.0 ** -9
+    bound = (np.abs(x64) + ex) @ ew + ex @ np.abs(w64)
+    assert np.all(np.abs(y - ref) <= bound * 1.01 + 1e-6)
+    # a dropped branch or sparse part leaves that bound
+    assert np.abs(y - ref).max() < 0.5 * np.abs(ref).max()
