@@ -357,6 +357,24 @@ def rows_section(sqf, torch, stream):
                             frac_int8_peak=round(own_ops / (tg * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
                             issued_mfma_tops=round(mfma_ops / (tg * 1e-3) / 1e12, 1)))
             del wt
+        # f4: the floating-point form (E2M1 low codes with the mark, E4M3
+        # values, E4M3 activations and branch), one bank per row
+        af = sqf.alloc_acts(lay.m, k_low, k_out, low="fp8", branch="fp8")
+        taf = time_call(torch, stream, lambda: sqf.sqf_quantize_split_act(xt, mp, af, stream=stream))
+        tp = time_call(torch, stream, lambda: sqf.sqf_pack_weights(
+            w, mp, branch="fp8", hdiag=hd, sq_nnz=nnz, low="fp4", stream=stream), iters=2, warmup=1)
+        wt = sqf.sqf_pack_weights(w, mp, branch="fp8", hdiag=hd, sq_nnz=nnz, low="fp4", stream=stream)
+        tg = time_call(torch, stream, lambda: sqf.sqf_dual_gemm(af, wt, y=y, stream=stream), iters=5)
+        own_ops = 2.0 * lay.m * lay.n * (k_low + nnz + k_out)
+        bits = (wt.t["w_low"].numel() * 8 + wt.t["sq_val"].numel() * 8) / (lay.n * sqf.sqf_pad_k_low(k_low))
+        _add(out, dict(row="f4 SQ-format, FP8/FP4 (E2M1 low with the mark, E4M3 values, E4M3 acts and branch)",
+                        shape=f"{lay.m}x{lay.k}->{lay.n}, nnz {nnz}/row",
+                        bits_per_low_weight=round(bits, 3),
+                        pack_ms=round(tp, 3), act_us=round(taf * 1e3, 1), gemm_us=round(tg * 1e3, 1),
+                        gemm_eff_tops=round(2.0 * lay.m * lay.n * lay.k / (tg * 1e-3) / 1e12, 1),
+                        own_work_tops=round(own_ops / (tg * 1e-3) / 1e12, 1),
+                        frac_fp8_peak=round(own_ops / (tg * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4)))
+        del wt, af
         del xt, a, y, w, x_cal
         torch.cuda.empty_cache()
     return out

@@ -48,7 +48,8 @@
  *   w_low  [n][ldk] bytes: int4 codes, same packings (SQF_I4_E2M3 and
  *          SQF_MXFP4: K-blocked with P = sqf_pad_rows(n));
  *          nibble 0x8 is the reserved "high precision here" mark
- *          (weight-side format only).
+ *          (weight-side format only; in the floating-point form, SQF_FP4_E2M1,
+ *          the mark is 0x8 = E2M1 -0, which the encoder never produces).
  *   x_out  [m][ldo], w_out [n][ldo]: branch operands (bf16, E4M3 or int8).
  *   Y      [m][ldy] fp32.
  *   Low slots are padded to sqf_pad_k_low(k_low) (a multiple of 256); branch
@@ -89,7 +90,7 @@
 extern "C" {
 #endif
 
-#define SQF_ABI_VERSION 3
+#define SQF_ABI_VERSION 4
 
 typedef enum {
   SQF_OK = 0,
@@ -107,7 +108,9 @@ typedef enum {
   SQF_I8 = 3,
   SQF_I4X2 = 4,    /* two int4 codes per byte */
   SQF_I4_E2M3 = 5, /* int4 codes, one per 6-bit E2M3 field, K-blocked (see above) */
-  SQF_MXFP4 = 6    /* OCP MXFP4: E2M1 codes + one E8M0 scale per 32 slots */
+  SQF_MXFP4 = 6,   /* OCP MXFP4: E2M1 codes + one E8M0 scale per 32 slots */
+  SQF_FP4_E2M1 = 7 /* OCP E2M1 codes packed like SQF_I4X2, one scale per row
+                      (the floating-point weight-side format) */
 } sqf_dtype;
 
 /* GEMM tile choice of the *_ex calls.  SQF_TILE_AUTO picks by problem size;
@@ -133,7 +136,8 @@ typedef struct sqf_weights {
   int64_t ldo;    /* elements per w_out row = sqf_pad_k_out(k_out, branch) */
   int32_t branch; /* SQF_BF16 | SQF_FP8_E4M3 | SQF_I8 */
   int32_t groups; /* >= 1 */
-  int32_t low;    /* SQF_I4X2 | SQF_I4_E2M3 | SQF_MXFP4 */
+  int32_t low;    /* SQF_I4X2 | SQF_I4_E2M3 | SQF_MXFP4 | SQF_FP4_E2M1 (the
+                     floating-point weight-side format) */
   int32_t reserved0;
   uint8_t* w_low; /* [groups][n][ldk] int4 codes (see the layouts above) */
   float* s_w;     /* [groups][n] low scale (s_w4 of the weight-side format);
@@ -167,7 +171,9 @@ typedef struct sqf_acts {
   int64_t ldk;    /* bytes per x_low row: pad/2 (SQF_I4X2) or pad (SQF_I8) */
   int64_t ldo;    /* elements per x_out row */
   int32_t low;    /* SQF_I4X2 | SQF_I8 (weight-side format only) |
-                     SQF_I4_E2M3 | SQF_MXFP4 */
+                     SQF_I4_E2M3 | SQF_MXFP4 | SQF_FP8_E4M3 (E4M3 codes, one
+                     per byte, ldk = pad: the floating-point weight-side
+                     format, with an SQF_FP8_E4M3 branch) */
   int32_t branch; /* SQF_BF16 | SQF_FP8_E4M3 | SQF_I8 */
   uint8_t* x_low; /* [m][ldk], or K-blocked for SQF_I4_E2M3 (see above) */
   float* s_x;     /* [m]; unused (may be NULL) for SQF_MXFP4 */
@@ -239,7 +245,12 @@ sqf_status sqf_select_channels_noalloc(const float* x_cal, int64_t m_cal, int64_
  * sq_nnz / banks slots with the largest w^2 * hdiag (ties: lower slot) are
  * marked 0x8 and kept as int8 (one scale s_w8 per row over all its marked
  * values), the others quantised to int4 with an absmax over the unmarked
- * slots.  SQF_I4_E2M3 weights hold the channel-split int4 codes in the
+ * slots.  Floating-point weight-side format ([SQF-art] 八: FP8 high, FP4
+ * low): low SQF_FP4_E2M1 and an SQF_FP8_E4M3 branch; the same marks, the
+ * kept values as E4M3 codes of v*448/a8 (s_w8 = a8/448, sq_val holds the
+ * E4M3 bytes), the others as E2M1 codes of v*6/a4 (s_w = a4/6), the branch
+ * E4M3 per row; it pairs with E4M3 activations (low SQF_FP8_E4M3, per-token
+ * scale a/448) and its GEMM has fp32 sums (no debug outputs).  SQF_I4_E2M3 weights hold the channel-split int4 codes in the
  * K-blocked 6-bit layout; SQF_MXFP4 weights quantise each 32-slot block of
  * a row's low values to E2M1 with a shared E8M0 scale (OCP MX), K-blocked.
  * Both need groups == 1 and a bf16 branch. */

@@ -86,7 +86,8 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
   // NORM: gamma[k] after the other regions (16-byte aligned)
   float* gam = (float*)((uint8_t*)bmax0 + ((2 * nblk * 4 + 15) & ~15));
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const float qlow = LOW == kI8 ? 127.0f : 7.0f;
+  // low codes: int4 (7), int8 (127) or E4M3 (448, the floating-point weight-side form)
+  const float qlow = LOW == kI8 ? 127.0f : (LOW == kFP8 ? 448.0f : 7.0f);
   const float qhi = BR == kFP8 ? 448.0f : 127.0f;
   const int k_out = (int)p.k_out;
 
@@ -476,6 +477,9 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
           if ((~cw[i] & 0xFFu) & ~b0m[i]) f1 = mx_inv_scale(mx_scale_byte(bmax[b + 1]));
 #pragma unroll
           for (int e = 0; e < 8; ++e) y[e] = e2m1_code(val(raw, i, e), ((b0m[i] >> e) & 1u) ? f0 : f1);
+        } else if constexpr (LOW == kFP8) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[e] = e4m3_rne_sat(nval(i, e) * inv_lo);
         } else {
 #pragma clang fp contract(off)
 #pragma unroll
@@ -641,6 +645,11 @@ hipError_t launch_act_split(const ActArgs& a, int x_dtype, int low, int branch, 
     if (grouped || branch != kBF16) return hipErrorInvalidValue;
     return x_dtype == kBF16 ? launch_shape<kBF16, kI4E2M3, kBF16, false>(a, ragged, lds, s)
                             : launch_shape<kF32, kI4E2M3, kBF16, false>(a, ragged, lds, s);
+  }
+  if (low == kFP8) {  // E4M3 codes with an E4M3 branch: the floating-point weight-side form
+    if (grouped || branch != kFP8) return hipErrorInvalidValue;
+    return x_dtype == kBF16 ? launch_shape<kBF16, kFP8, kFP8, false>(a, ragged, lds, s)
+                            : launch_shape<kF32, kFP8, kFP8, false>(a, ragged, lds, s);
   }
   if (low == kMXFP4) {  // bf16 branch, one weight set: the FP4 GEMM's operand
     if (grouped || branch != kBF16) return hipErrorInvalidValue;

@@ -252,6 +252,12 @@ __device__ __forceinline__ int block_excl_scan(int v, int* scratch) {
 // Every slot then counts the keys of its bank that rank above it (larger,
 // or equal at a lower slot) and is kept when fewer than that many do; a
 // wave's 64 slots share a bank, so its reads of the bank are broadcasts.
+//
+// FP (SQ-format article, section 八: FP8 high-precision part, FP4 low part):
+// the same marks; the kept values become E4M3 codes of v * 448/a8 and the
+// other slots E2M1 codes of v * 6/a4 (0x8, E2M1 -0, is never produced by
+// the encoder and stays the mark); the branch is E4M3 with its own scale.
+template <bool FP>
 __global__ __launch_bounds__(256) void k_pack_sq(PackArgs p) {
   extern __shared__ uint8_t sm[];
   __shared__ int iscr[8];
@@ -373,17 +379,20 @@ __global__ __launch_bounds__(256) void k_pack_sq(PackArgs p) {
   }
   a8 = block_max_f(a8, fscr);
   a4 = block_max_f(a4, fscr);
-  const float inv8 = quant_inv(a8, 127.0f), inv4 = quant_inv(a4, 7.0f);
+  constexpr float Q8 = FP ? 448.0f : 127.0f, Q4 = FP ? 6.0f : 7.0f;
+  const float inv8 = quant_inv(a8, Q8), inv4 = quant_inv(a4, Q4);
   if (tid == 0) {
-    p.s_w8[nn] = quant_scale(a8, 127.0f);
-    p.s_w[nn] = quant_scale(a4, 7.0f);
+    p.s_w8[nn] = quant_scale(a8, Q8);
+    p.s_w[nn] = quant_scale(a4, Q4);
   }
   // int8 values in ascending slot order
   int kc = 0;
   for (int64_t j = j0; j < j1; ++j) kc += keep[j];
   int pos = block_excl_scan(kc, iscr);
   for (int64_t j = j0; j < j1; ++j)
-    if (keep[j]) p.sq_val[nn * p.nnz + pos++] = (int8_t)quant_code(vals[j], inv8, 127.0f);
+    if (keep[j])
+      p.sq_val[nn * p.nnz + pos++] =
+          FP ? (int8_t)e4m3_rne_sat(vals[j] * inv8) : (int8_t)quant_code(vals[j], inv8, 127.0f);
   // packed row: 16-byte groups of 32 slots
   uint8_t* wl = p.w_low + nn * p.ldk;
   for (int64_t q = tid; q < p.ldk / 16; q += 256) {
@@ -391,30 +400,41 @@ __global__ __launch_bounds__(256) void k_pack_sq(PackArgs p) {
     for (int e = 0; e < 32; ++e) {
       int64_t j = q * 32 + e;
       uint32_t nib = 0;
-      if (j < kl) nib = keep[j] ? 0x8u : ((uint32_t)quant_code(vals[j], inv4, 7.0f) & 0xFu);
+      if (j < kl)
+        nib = keep[j] ? 0x8u
+                      : (FP ? e2m1_code(vals[j], inv4) : ((uint32_t)quant_code(vals[j], inv4, 7.0f) & 0xFu));
       ow[e >> 3] |= nib << ((e & 7) * 4);
     }
     *(uint4*)(wl + q * 16) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
   }
-  // int8 branch over the outlier channels
+  // int8 (FP: E4M3) branch over the outlier channels
   float ao = 0.0f;
   for (int64_t t = tid; t < p.k_out; t += 256) ao = fmaxf(ao, fabsf(ov[t]));
   ao = block_max_f(ao, fscr);
-  const float invo = quant_inv(ao, 127.0f);
-  if (tid == 0 && p.s_wo) p.s_wo[nn] = quant_scale(ao, 127.0f);
+  const float invo = quant_inv(ao, Q8);
+  if (tid == 0 && p.s_wo) p.s_wo[nn] = quant_scale(ao, Q8);
   for (int64_t t = tid; t < p.ldo; t += 256)
-    p.w_out[nn * p.ldo + t] = t < p.k_out ? (uint8_t)quant_code(ov[t], invo, 127.0f) : 0;
+    p.w_out[nn * p.ldo + t] =
+        t < p.k_out ? (FP ? (uint8_t)e4m3_rne_sat(ov[t] * invo) : (uint8_t)quant_code(ov[t], invo, 127.0f))
+                    : 0;
 }
 
 hipError_t launch_pack(const PackArgs& a, int branch, int low, int groups, hipStream_t s) {
   if (a.nnz > 0) {
+    // integer form (int4 + int8) or floating-point form (E2M1 + E4M3)
+    const bool fp = low == kFP4E2M1;
+    if (fp != (branch == kFP8)) return hipErrorInvalidValue;
+    const void* kern = fp ? (const void*)k_pack_sq<true> : (const void*)k_pack_sq<false>;
     size_t lds = (size_t)a.k_low * 9 + (size_t)a.k_out * 4 + 16;
     if (lds > 65536) {
-      hipError_t e = hipFuncSetAttribute((const void*)k_pack_sq,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k_pack_sq, dim3((unsigned)((a.n + 7) / 8 * 8)), dim3(256), lds, s, a);
+    const dim3 grid((unsigned)((a.n + 7) / 8 * 8));
+    if (fp)
+      hipLaunchKernelGGL(k_pack_sq<true>, grid, dim3(256), lds, s, a);
+    else
+      hipLaunchKernelGGL(k_pack_sq<false>, grid, dim3(256), lds, s, a);
     return hipGetLastError();
   }
   dim3 grid((unsigned)((a.n + kPackCols - 1) / kPackCols), (unsigned)groups);

@@ -36,6 +36,22 @@
 // vector ALU work can issue between the MFMAs; one barrier per stage.  The
 // DMAs of A stage s+2 and W stage s+3 start right after that barrier, and the
 // value window of stage s+2 right after stage s+1 is decoded.
+//
+// Floating-point form (SQ-format article, section 八: FP8 high-precision
+// part, FP4 low part): E4M3 activations, E2M1 weight codes with the same
+// 0x8 mark, E4M3 sparse values and branch.  The same pipeline and decode;
+// the tiles are laid out for v_mfma_scale_f32_16x16x128_f8f6f4, whose lane
+// l of a 16 x 128 operand holds row l%16 and, for FP4, slots 32(l/16) ..
+// +31 (16 bytes), for FP8 slots 16(l/16) .. +15 and 64 + 16(l/16) .. +15
+// (32 bytes; measured: with one FP8 and one FP4 operand the layouts must
+// differ like this, with two FP8 operands any common order works).  The
+// clean tile is the raw E2M1 nibbles with the marks cleared (a cleared mark
+// is +0); the sparse tile holds the E4M3 values at their slots in the FP8
+// order.  The low pass is
+// E4M3 x E2M1, the sparse pass and the branch E4M3 x E4M3, all with fp32
+// accumulators (not exact).
+#include <type_traits>
+
 #include "sqf_device.h"
 #include "sqf_launch.h"
 
@@ -88,8 +104,12 @@ static_assert(kBN * 128 <= 2 * kStW + 2 * kStV, "branch W tile fits");
 
 }  // namespace
 
-template <bool DEBUG>
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+template <bool DEBUG, bool FP>
 __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
+  static_assert(!(DEBUG && FP), "the floating-point form has no integer accumulators");
+  using AccT = std::conditional_t<FP, v4f, v4i>;
   constexpr int TM = 4, TN = 4;
   __shared__ __attribute__((aligned(2048))) uint8_t smem[kSmem];
 
@@ -146,6 +166,14 @@ __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
   const int r = tid >> 2, qq = tid & 3;
   const int f_own = qq >> 1, g0 = 2 * (qq & 1);
   const int rb = r >> 4, rr = r & 15;
+  // floating-point tiles: entry of (row rr, slot group qq) in a 16-row block
+  // (clean E2M1 tile); the sparse E4M3 tile takes slots 32qq + 8d .. +7 of
+  // this lane to FP8 group g = 2(qq%2) + d/2, bytes 16(qq/2) + 8(d%2) ..
+  const int fpos_w = (qq << 4) + (rr ^ (qq << 2));
+  auto sp_off = [&](int d) {
+    const int g = 2 * (qq & 1) + (d >> 1);
+    return ((g << 4) + (rr ^ (g << 2))) * 32 + 16 * (qq >> 1) + 8 * (d & 1);
+  };
   const int gn = n0 + r < nn ? n0 + r : nn - 1;
   const int8_t* vrow = p.sq_val + (int64_t)gn * nnz;
   // sq_val is 16-byte aligned (host check); a window starts at the 16-byte
@@ -175,7 +203,7 @@ __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
     uint32_t sel[2] = {0, 0};
 #pragma unroll
     for (int pp = 0; pp < 8; ++pp) {
-      const int sl = pp < 4 ? 2 * pp : 2 * (pp - 4) + 1;
+      const int sl = FP ? pp : (pp < 4 ? 2 * pp : 2 * (pp - 4) + 1);
       const uint32_t b = ((m >> sl) & 1) ? (uint32_t)__builtin_popcount(m & ((1 << sl) - 1)) : 0x0Cu;
       sel[pp >> 2] |= b << (8 * (pp & 3));
     }
@@ -207,10 +235,19 @@ __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
         cnt += __builtin_popcount(m8);
       }
     }
-    uint2* sL = (uint2*)(smem + kOffL + (s & 1) * kStL) + (rb * 2 + f_own) * 64;
+    uint8_t* sblk;
+    if constexpr (FP) {
+      // lane-order entries of the 16-row block rb: (row rr, slot group qq)
+      // at fpos (swizzled so the 16 lanes of a row quad hit distinct banks)
+      *(uint4*)(smem + kOffL + (s & 1) * kStL + rb * 1024 + fpos_w * 16) =
+          make_uint4(wd[0], wd[1], wd[2], wd[3]);
+      sblk = smem + kOffS + (s & 1) * kStS + rb * 2048;
+    } else {
+      uint2* sL = (uint2*)(smem + kOffL + (s & 1) * kStL) + (rb * 2 + f_own) * 64;
 #pragma unroll
-    for (int e = 0; e < 2; ++e) sL[lpos(g0 + e, rr, f_own)] = make_uint2(wd[2 * e], wd[2 * e + 1]);
-    uint8_t* sblk = smem + kOffS + (s & 1) * kStS + (rb * 2 + f_own) * 1024;
+      for (int e = 0; e < 2; ++e) sL[lpos(g0 + e, rr, f_own)] = make_uint2(wd[2 * e], wd[2 * e + 1]);
+      sblk = smem + kOffS + (s & 1) * kStS + (rb * 2 + f_own) * 1024;
+    }
     // marks of the row's earlier lanes precede this lane's
     int incl = cnt;
     {
@@ -245,8 +282,11 @@ __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
         const uint32_t t2 = ((mk[d] >> 3) | (mk[d] >> 6)) & 0x03030303u;
         const uint32_t x = __builtin_amdgcn_udot4(t2, 0x40100401u, 0u, false);
         const uint2 sl = sSel[x];
-        *(uint2*)(sblk + spos(g0 + (d >> 1), rr) * 16 + ((d & 1) ^ f_own) * 8) =
-            make_uint2(perm(hi, lo, sl.x), perm(hi, lo, sl.y));
+        if constexpr (FP)
+          *(uint2*)(sblk + sp_off(d)) = make_uint2(perm(hi, lo, sl.x), perm(hi, lo, sl.y));
+        else
+          *(uint2*)(sblk + spos(g0 + (d >> 1), rr) * 16 + ((d & 1) ^ f_own) * 8) =
+              make_uint2(perm(hi, lo, sl.x), perm(hi, lo, sl.y));
         pre += __builtin_popcount(mk[d]);
       }
     }
@@ -260,7 +300,10 @@ __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
           const int k = d * 8 + (__builtin_ctz(m8) >> 2);  // slot within the lane's 32
           m8 &= m8 - 1;
           const int8_t v = v0 + j >= nnz ? (int8_t)0 : vrow[v0 + j];
-          sblk[spos(g0 + (k >> 4), rr) * 16 + (perm_pos(k & 15) ^ (f_own * 8))] = (uint8_t)v;
+          if constexpr (FP)
+            sblk[sp_off(k >> 3) + (k & 7)] = (uint8_t)v;
+          else
+            sblk[spos(g0 + (k >> 4), rr) * 16 + (perm_pos(k & 15) ^ (f_own * 8))] = (uint8_t)v;
           ++j;
         }
       }
@@ -277,14 +320,51 @@ __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
     rd_off[f] = (uint32_t)((R >> 3) * 1024 + (R & 7) * 128 + 16 * (C ^ pair_swz(R >> 3, R & 7)));
   }
 
-  v4i acc[TM][TN], acs[TM][TN];
+  AccT acc[TM][TN], acs[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = acs[i][j] = v4i{0, 0, 0, 0};
+    for (int j = 0; j < TN; ++j) acc[i][j] = acs[i][j] = AccT{0, 0, 0, 0};
 
-  // MFMAs of stage s: both K halves, low and sparse tiles on the same A
+  // floating-point form: this lane's FP8 fragment (row lane%16 of a 16-row
+  // block, chunks lane/16 and lane/16 + 4 of the swizzled 128-byte row) and
+  // its lane-order tile entry
+  uint32_t rdf[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int R = lane & 15, C = (lane >> 4) + 4 * h;
+    rdf[h] = (uint32_t)((R >> 3) * 1024 + (R & 7) * 128 + 16 * (C ^ pair_swz(R >> 3, R & 7)));
+  }
+  const int fpos_r = ((lane >> 4) << 4) + ((lane & 15) ^ ((lane >> 4) << 2));
+  auto ld_a8 = [&](const uint8_t* blk) {
+    const v4i lo = *(const v4i*)(blk + rdf[0]), hi = *(const v4i*)(blk + rdf[1]);
+    return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  };
+
+  // MFMAs of stage s: low and sparse tiles on the same A
   auto mfma_stage = [&](int s) {
+    if constexpr (FP) {
+      const uint8_t* abuf = smem + kOffA + (s & 1) * kStA;
+      const uint8_t* cb = smem + kOffL + (s & 1) * kStL;
+      const uint8_t* sb = smem + kOffS + (s & 1) * kStS;
+      v8i a[TM];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) a[i] = ld_a8(abuf + (wm * TM + i) * 2048);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int blk = wn * TN + j;
+        const v4i l4 = *(const v4i*)(cb + blk * 1024 + fpos_r * 16);
+        const v8i bl = v8i{l4.x, l4.y, l4.z, l4.w, 0, 0, 0, 0};
+        const v4i s0 = *(const v4i*)(sb + blk * 2048 + fpos_r * 32);
+        const v4i s1 = *(const v4i*)(sb + blk * 2048 + fpos_r * 32 + 16);
+        const v8i bs = v8i{s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], bl, acc[i][j], 0, 4, 0, 0, 0, 0);
+          acs[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], bs, acs[i][j], 0, 0, 0, 0, 0, 0);
+        }
+      }
+    } else {
     const uint8_t* abuf = smem + kOffA + (s & 1) * kStA;
     const uint2* sL = (const uint2*)(smem + kOffL + (s & 1) * kStL);
     const uint4* sS = (const uint4*)(smem + kOffS + (s & 1) * kStS);
@@ -308,7 +388,9 @@ __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
         }
       }
     }
+    }
   };
+
 
   // ---- int8 branch (outlier channels), 128 bytes per row per stage ----
   // Branch stage t takes the A buffer (nst + t) % 2 and, for its W rows (16-row
@@ -381,13 +463,18 @@ __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
       for (int q = 0; q < 4; ++q) {
         const int row = m0 + wm * 64 + i * 16 + lr + q, col = n0 + wn * 64 + j * 16 + lc;
         const int rc = row < mm ? row : mm - 1, cc = col < nn ? col : nn - 1;
-        const int32_t lo = acc[i][j][q] >> 4;
-        if (DEBUG && row < mm && col < nn) {
-          p.dbg_low[(int64_t)row * nn + col] = lo;
-          p.dbg_sp[(int64_t)row * nn + col] = acs[i][j][q];
+        if constexpr (FP) {
+          acc[i][j][q] = p.s_x[rc] * (p.s_w4[cc] * acc[i][j][q] + p.s_w8[cc] * acs[i][j][q]);
+          acs[i][j][q] = 0.0f;
+        } else {
+          const int32_t lo = acc[i][j][q] >> 4;
+          if (DEBUG && row < mm && col < nn) {
+            p.dbg_low[(int64_t)row * nn + col] = lo;
+            p.dbg_sp[(int64_t)row * nn + col] = acs[i][j][q];
+          }
+          acc[i][j][q] = __float_as_int(p.s_x[rc] * (p.s_w4[cc] * (float)lo + p.s_w8[cc] * (float)acs[i][j][q]));
+          acs[i][j][q] = 0;
         }
-        acc[i][j][q] = __float_as_int(p.s_x[rc] * (p.s_w4[cc] * (float)lo + p.s_w8[cc] * (float)acs[i][j][q]));
-        acs[i][j][q] = 0;
       }
 
   // ---- int8 branch stages (the first two are already in flight) ----
@@ -400,17 +487,31 @@ __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
       }
       wait_vmcnt<0>();
       sq_sync();
+      if constexpr (FP) {
+        // E4M3 x E4M3, one 128-byte K step per instruction
+        v8i b[TN];
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        v4i b[TN];
-#pragma unroll
-        for (int j = 0; j < TN; ++j) b[j] = *(const v4i*)(smem + br_w(t) + (wn * TN + j) * 2048 + rd_off[f]);
+        for (int j = 0; j < TN; ++j) b[j] = ld_a8(smem + br_w(t) + (wn * TN + j) * 2048);
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-          const v4i a = *(const v4i*)(smem + br_a(t) + (wm * TM + i) * 2048 + rd_off[f]);
+          const v8i a = ld_a8(smem + br_a(t) + (wm * TM + i) * 2048);
 #pragma unroll
           for (int j = 0; j < TN; ++j)
-            acs[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[j], acs[i][j], 0, 0, 0);
+            acs[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b[j], acs[i][j], 0, 0, 0, 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+          v4i b[TN];
+#pragma unroll
+          for (int j = 0; j < TN; ++j) b[j] = *(const v4i*)(smem + br_w(t) + (wn * TN + j) * 2048 + rd_off[f]);
+#pragma unroll
+          for (int i = 0; i < TM; ++i) {
+            const v4i a = *(const v4i*)(smem + br_a(t) + (wm * TM + i) * 2048 + rd_off[f]);
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+              acs[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[j], acs[i][j], 0, 0, 0);
+          }
         }
       }
       sq_sync();
@@ -435,12 +536,21 @@ __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
       for (int q = 0; q < 4; ++q) {
         const int row = m0 + wm * 64 + i * 16 + lr + q;
         const int rc = row < mm ? row : mm - 1;
-        if (DEBUG && row < mm && col < nn) p.dbg_o[(int64_t)row * nn + col] = acs[i][j][q];
-        float v = __int_as_float(acc[i][j][q]);
-        if (p.s_out > 0) v += (p.s_xo[rc] * swo) * (float)acs[i][j][q];
-        acc[i][j][q] = __float_as_int(v);
+        if constexpr (FP) {
+          if (p.s_out > 0) acc[i][j][q] += (p.s_xo[rc] * swo) * acs[i][j][q];
+        } else {
+          if (DEBUG && row < mm && col < nn) p.dbg_o[(int64_t)row * nn + col] = acs[i][j][q];
+          float v = __int_as_float(acc[i][j][q]);
+          if (p.s_out > 0) v += (p.s_xo[rc] * swo) * (float)acs[i][j][q];
+          acc[i][j][q] = __float_as_int(v);
+        }
       }
   }
+  // the fused value of an accumulator element (int form: fp32 bits)
+  auto outv = [](auto v) -> float {
+    if constexpr (FP) return v;
+    else return __int_as_float(v);
+  };
   const int wrow0 = m0 + wm * 64, wcol0 = n0 + wn * 64;
   const bool whole = wcol0 + 64 <= nn && (p.ldy & 3) == 0 && (((uintptr_t)p.y) & 15) == 0;
   if (whole) {
@@ -455,7 +565,7 @@ __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) stg[(lr + q) * LDW + j * 16 + lc] = __int_as_float(acc[i][j][q]);
+        for (int q = 0; q < 4; ++q) stg[(lr + q) * LDW + j * 16 + lc] = outv(acc[i][j][q]);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int idx = k * 64 + lane, rr2 = idx >> 4, c4 = idx & 15;
@@ -472,16 +582,18 @@ __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int row = wrow0 + i * 16 + lr + q, col = wcol0 + j * 16 + lc;
-          if (row < mm && col < nn) __builtin_nontemporal_store(__int_as_float(acc[i][j][q]), p.y + (int64_t)row * p.ldy + col);
+          if (row < mm && col < nn) __builtin_nontemporal_store(outv(acc[i][j][q]), p.y + (int64_t)row * p.ldy + col);
         }
   }
 }
 
-hipError_t launch_sq_gemm(const SqArgs& a, bool debug, hipStream_t s) {
+hipError_t launch_sq_gemm(const SqArgs& a, bool debug, bool fp, hipStream_t s) {
   const int64_t blocks = ((a.m + kBM - 1) / kBM) * ((a.n + kBN - 1) / kBN);
   if (blocks <= 0) return hipSuccess;
-  if (debug) hipLaunchKernelGGL(k_sq_gemm<true>, dim3((unsigned)blocks), dim3(512), 0, s, a);
-  else hipLaunchKernelGGL(k_sq_gemm<false>, dim3((unsigned)blocks), dim3(512), 0, s, a);
+  if (fp && debug) return hipErrorInvalidValue;
+  if (fp) hipLaunchKernelGGL((k_sq_gemm<false, true>), dim3((unsigned)blocks), dim3(512), 0, s, a);
+  else if (debug) hipLaunchKernelGGL((k_sq_gemm<true, false>), dim3((unsigned)blocks), dim3(512), 0, s, a);
+  else hipLaunchKernelGGL((k_sq_gemm<false, false>), dim3((unsigned)blocks), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

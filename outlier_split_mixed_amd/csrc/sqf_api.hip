@@ -63,7 +63,7 @@ bool tile_ok(int32_t t) { return t >= SQF_TILE_AUTO && t <= SQF_TILE_64; }
 // pad, 6-bit E2M3 fields pad*3/4 (E2M3 and E2M1 stored K-blocked, see sqf.h).
 int64_t low_ldk(int64_t k_low, int32_t low) {
   const int64_t pad = sqf_pad_k_low(k_low);
-  return low == SQF_I8 ? pad : low == SQF_I4_E2M3 ? pad / 4 * 3 : pad / 2;
+  return (low == SQF_I8 || low == SQF_FP8_E4M3) ? pad : low == SQF_I4_E2M3 ? pad / 4 * 3 : pad / 2;
 }
 // Rows of a low operand's storage (the K-blocked layout pads them).
 bool low_kblocked(int32_t low) { return low == SQF_I4_E2M3 || low == SQF_MXFP4; }
@@ -98,8 +98,12 @@ sqf_status check_weights(const sqf_weights* wt, const char* who) {
   if (!branch_ok(wt->branch))
     return fail(SQF_ERR_INVALID_ARG, "%s: bad branch dtype %d", who, wt->branch);
   if (wt->groups < 1) return fail(SQF_ERR_SHAPE, "%s: groups must be >= 1", who);
-  if (wt->low != SQF_I4X2 && wt->low != SQF_I4_E2M3 && wt->low != SQF_MXFP4)
+  if (wt->low != SQF_I4X2 && wt->low != SQF_I4_E2M3 && wt->low != SQF_MXFP4 &&
+      wt->low != SQF_FP4_E2M1)
     return fail(SQF_ERR_INVALID_ARG, "%s: bad low dtype %d for weights", who, wt->low);
+  if (wt->low == SQF_FP4_E2M1 && (wt->sq_nnz == 0 || wt->branch != SQF_FP8_E4M3 || wt->groups != 1))
+    return fail(SQF_ERR_UNSUPPORTED, "%s: SQF_FP4_E2M1 weights are the floating-point weight-side "
+                "format (sq_nnz > 0, SQF_FP8_E4M3 branch, one weight set)", who);
   if (low_kblocked(wt->low) && (wt->groups != 1 || wt->branch != SQF_BF16 || wt->sq_nnz != 0))
     return fail(SQF_ERR_UNSUPPORTED, "%s: the K-blocked low layouts (E2M3, MXFP4) are built for "
                 "one weight set, a bf16 branch and the channel-split format", who);
@@ -138,8 +142,10 @@ sqf_status check_weights(const sqf_weights* wt, const char* who) {
   if (wt->sq_nnz > 0) {
     if (wt->groups != 1)
       return fail(SQF_ERR_UNSUPPORTED, "%s: the weight-side format needs groups == 1", who);
-    if (wt->branch != SQF_I8)
-      return fail(SQF_ERR_UNSUPPORTED, "%s: the weight-side format needs an SQF_I8 branch", who);
+    if (!((wt->low == SQF_I4X2 && wt->branch == SQF_I8) ||
+          (wt->low == SQF_FP4_E2M1 && wt->branch == SQF_FP8_E4M3)))
+      return fail(SQF_ERR_UNSUPPORTED, "%s: the weight-side format is int4 codes with an SQF_I8 "
+                  "branch, or SQF_FP4_E2M1 codes with an SQF_FP8_E4M3 branch", who);
     if (!wt->sq_val || !wt->s_w8)
       return fail(SQF_ERR_INVALID_ARG, "%s: sq_val and s_w8 are required", who);
     if (wt->sq_bank != 0 && wt->sq_bank != wt->k_low) {
@@ -167,8 +173,12 @@ sqf_status check_acts(const sqf_acts* a, const char* who) {
   if (a->m < 0 || a->k_low < 0 || a->k_out < 0 || a->k_low + a->k_out < 1)
     return fail(SQF_ERR_SHAPE, "%s: bad activation shape m=%lld k_low=%lld k_out=%lld", who,
                 (long long)a->m, (long long)a->k_low, (long long)a->k_out);
-  if (a->low != SQF_I4X2 && a->low != SQF_I8 && a->low != SQF_I4_E2M3 && a->low != SQF_MXFP4)
+  if (a->low != SQF_I4X2 && a->low != SQF_I8 && a->low != SQF_I4_E2M3 && a->low != SQF_MXFP4 &&
+      a->low != SQF_FP8_E4M3)
     return fail(SQF_ERR_INVALID_ARG, "%s: bad low dtype %d", who, a->low);
+  if (a->low == SQF_FP8_E4M3 && a->branch != SQF_FP8_E4M3)
+    return fail(SQF_ERR_UNSUPPORTED, "%s: E4M3 low codes (the floating-point weight-side format) "
+                "come with an SQF_FP8_E4M3 branch", who);
   if (low_kblocked(a->low) && a->branch != SQF_BF16)
     return fail(SQF_ERR_UNSUPPORTED, "%s: the K-blocked low layouts (E2M3, MXFP4) come with a "
                 "bf16 branch", who);
@@ -263,9 +273,13 @@ sqf_status check_pair(const sqf_acts* a, const sqf_weights* w, const void* y, in
   if (a->k_low != w->k_low || a->k_out != w->k_out || a->branch != w->branch)
     return fail(SQF_ERR_INVALID_ARG, "%s: activations and weights disagree on k_low/k_out/branch",
                 who);
-  if ((w->sq_nnz > 0) != (a->low == SQF_I8))
-    return fail(SQF_ERR_INVALID_ARG,
-                "%s: weight-side format needs int8 activations and the channel split int4", who);
+  if (w->sq_nnz > 0 && !((w->low == SQF_I4X2 && a->low == SQF_I8) ||
+                         (w->low == SQF_FP4_E2M1 && a->low == SQF_FP8_E4M3)))
+    return fail(SQF_ERR_INVALID_ARG, "%s: the weight-side format needs int8 activations (int4 "
+                "weights) or E4M3 activations (E2M1 weights)", who);
+  if (w->sq_nnz == 0 && (a->low == SQF_I8 || a->low == SQF_FP8_E4M3))
+    return fail(SQF_ERR_INVALID_ARG, "%s: 8-bit low activations belong to the weight-side format",
+                who);
   if (w->sq_nnz == 0 && a->low != w->low)
     return fail(SQF_ERR_INVALID_ARG, "%s: activations (low %d) and weights (low %d) disagree on "
                 "the low storage", who, a->low, w->low);
@@ -292,6 +306,10 @@ sqf_status dual_gemm_impl(const sqf_acts* a, const sqf_weights* w, void* y, bool
   const bool debug = acc_low_dbg || acc_sp_dbg || acc_out_dbg;
   if (w->sq_nnz > 0) {
     if (ybf16) return fail(SQF_ERR_UNSUPPORTED, "%s: the weight-side format writes fp32 Y", who);
+    const bool fp = w->low == SQF_FP4_E2M1;
+    if (fp && debug)
+      return fail(SQF_ERR_UNSUPPORTED, "%s: the floating-point weight-side format has no integer "
+                  "accumulators", who);
     // int8 activations x (16 x int4 weights) in an int32 accumulator
     if (w->k_low > kMaxKLowSq)
       return fail(SQF_ERR_UNSUPPORTED, "%s: k_low=%lld exceeds %lld for the weight-side format", who,
@@ -304,7 +322,7 @@ sqf_status dual_gemm_impl(const sqf_acts* a, const sqf_weights* w, void* y, bool
                    w->sq_val, w->s_w8, (const uint8_t*)w->w_out, w->s_wo, (float*)y,
                    acc_low_dbg, acc_sp_dbg, acc_out_dbg, a->m, w->n, a->ldk, w->ldk, w->ldo, ldy,
                    w->sq_nnz, (int32_t)(w->ldk / 128), (int32_t)(w->ldo / 128)};
-    return hip_status(sqf::launch_sq_gemm(sa, debug, (hipStream_t)stream), who);
+    return hip_status(sqf::launch_sq_gemm(sa, debug, fp, (hipStream_t)stream), who);
   }
   if (acc_sp_dbg || acc_out_dbg)
     return fail(SQF_ERR_INVALID_ARG, "%s: acc_sp/acc_out debug outputs need the weight-side format", who);

@@ -21,7 +21,7 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 constexpr int kWave = 64;
 
 // Status codes mirrored from the public header (kept in sync by the host code).
-enum : int { kBF16 = 1, kFP8 = 2, kI8 = 3, kI4X2 = 4, kI4E2M3 = 5, kMXFP4 = 6, kF32 = 0 };
+enum : int { kBF16 = 1, kFP8 = 2, kI8 = 3, kI4X2 = 4, kI4E2M3 = 5, kMXFP4 = 6, kFP4E2M1 = 7, kF32 = 0 };
 
 // Four int4 codes, one per byte (two's complement, |c| <= 7), as four 6-bit
 // OCP E2M3 fields holding c/8 (the subnormal: sign << 5 | |c|), packed into

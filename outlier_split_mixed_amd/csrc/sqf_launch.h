@@ -106,7 +106,7 @@ size_t act_split_lds_bytes(int64_t ldk, int64_t k_out, int low, int64_t norm_k);
 // ybf16: Y written as bf16 (not together with debug)
 hipError_t launch_dual_gemm(const GemmArgs& a, int branch, bool grouped, bool debug, int cfg,
                             hipStream_t s, bool ybf16);
-hipError_t launch_sq_gemm(const SqArgs& a, bool debug, hipStream_t s);
+hipError_t launch_sq_gemm(const SqArgs& a, bool debug, bool fp, hipStream_t s);
 // low: kI4E2M3 (int4 codes as E2M3 subnormals, exact sums; debug dumps them)
 // or kMXFP4 (E2M1 with E8M0 block scales; no debug output)
 hipError_t launch_gemm6(const Gemm6Args& a, int low, bool debug, bool ybf16, hipStream_t s);

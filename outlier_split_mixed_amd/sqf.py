@@ -26,11 +26,11 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 SQF_OK, SQF_ERR_INVALID_ARG, SQF_ERR_SHAPE, SQF_ERR_UNSUPPORTED, SQF_ERR_HIP, SQF_ERR_ALIGN = range(6)
-SQF_F32, SQF_BF16, SQF_FP8_E4M3, SQF_I8, SQF_I4X2, SQF_I4_E2M3, SQF_MXFP4 = range(7)
+SQF_F32, SQF_BF16, SQF_FP8_E4M3, SQF_I8, SQF_I4X2, SQF_I4_E2M3, SQF_MXFP4, SQF_FP4_E2M1 = range(8)
 DTYPES = {"f32": SQF_F32, "bf16": SQF_BF16, "fp8": SQF_FP8_E4M3, "i8": SQF_I8, "i4": SQF_I4X2,
-          "i4e2m3": SQF_I4_E2M3, "mxfp4": SQF_MXFP4}
+          "i4e2m3": SQF_I4_E2M3, "mxfp4": SQF_MXFP4, "fp4": SQF_FP4_E2M1}
 TILES = {"auto": -1, "256": 0, "128": 1, "64": 2}
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 P = ctypes.c_void_p
 I64 = ctypes.c_int64
@@ -131,7 +131,7 @@ def sqf_pad_rows(rows: int) -> int:
 def low_ldk(k_low: int, low: str) -> int:
     """Bytes per row of the low operand (see the layouts in sqf.h)."""
     p = sqf_pad_k_low(k_low)
-    return {"i4": p // 2, "mxfp4": p // 2, "i8": p, "i4e2m3": p * 3 // 4}[low]
+    return {"i4": p // 2, "mxfp4": p // 2, "fp4": p // 2, "i8": p, "fp8": p, "i4e2m3": p * 3 // 4}[low]
 
 
 def _low_tensor(rows: int, k_low: int, low: str, device, zero: bool):

@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported(sqf):
 
 
 def test_abi_version_and_padding(sqf):
-    assert sqf.sqf_abi_version() == 3
+    assert sqf.sqf_abi_version() == 4
     assert sqf.sqf_pad_rows(0) == 0 and sqf.sqf_pad_rows(1) == 256 and sqf.sqf_pad_rows(4096) == 4096
     assert sqf.sqf_pad_rows(300) == 512 and sqf._lib.sqf_pad_rows(-1) == -1
     assert sqf.sqf_pad_k_low(0) == 0 and sqf.sqf_pad_k_low(1) == 256
@@ -314,6 +314,36 @@ def test_mxfp4_contract_errors(sqf):
     w.low = sqf.SQF_I4X2  # storages disagree
     w.s_w = mem()
     assert ex(a, w, mem(), sqf.SQF_F32, 256, -1, None) == 1
+    assert sqf.sqf_last_error() != ""
+
+
+def test_fp_weight_side_contract_errors(sqf):
+    """The floating-point weight-side format: E2M1 weights only with marks and
+    an E4M3 branch, E4M3 activations only with an E4M3 branch, and the two
+    forms never mixed -- refused before any launch."""
+    mem = FakeMem()
+
+    def wfp(**kw):
+        w = _weights(sqf, mem, k=544, k_out=32, branch="fp8")
+        w.low, w.sq_nnz, w.sq_val, w.s_w8, w.s_wo = sqf.SQF_FP4_E2M1, 64, mem(), mem(), mem()
+        for f, v in kw.items():
+            setattr(w, f, v)
+        return w
+
+    pack = lambda w: sqf._lib.sqf_pack_weights(mem(), mem(), mem(), ctypes.byref(w), None)
+    assert pack(wfp(sq_nnz=0)) == 3
+    w = wfp()
+    w.branch, w.ldo = sqf.SQF_I8, 128
+    assert pack(w) == 3
+    afp = _acts(sqf, mem, k=544, k_out=32, branch="fp8")
+    afp.low, afp.ldk = sqf.SQF_FP8_E4M3, 512
+    g = lambda a, w, dbg=(None, None, None): _gemm(sqf, a, w, mem(), 256, dbg)
+    assert g(afp, wfp(), (mem(), mem(), mem())) == 3  # no integer accumulators
+    a8 = _acts(sqf, mem, k=544, k_out=32, branch="fp8", low="i8")
+    assert g(a8, wfp()) == 1  # int8 activations with E2M1 weights
+    abf = _acts(sqf, mem, k=544, k_out=32)
+    abf.low, abf.ldk = sqf.SQF_FP8_E4M3, 512
+    assert sqf._lib.sqf_quantize_split_act(mem(), sqf.SQF_BF16, 544, mem(), ctypes.byref(abf), None) == 3
     assert sqf.sqf_last_error() != ""
 
 

@@ -24,7 +24,7 @@ from outlier_split_mixed_amd import synth
 
 from harness import (assert_rows_close, f32_bits_equal, run_layer, run_layer_mx, sample_rows,
                      tile_band_rows, x_inputs)
-from test_gpu_parity import _grouped_check
+from test_gpu_parity import _grouped_check, _sqf_fp_check
 
 pytestmark = pytest.mark.gpu
 
@@ -159,3 +159,13 @@ def test_sq_weight_side_full(sqf, bank):
     assert_rows_close(y.cpu().numpy()[rows], o_y, "sq full")
     assert_rows_close(y_fast.cpu().numpy()[rows], o_y, "sq full (no debug outputs)")
     _log("sq full ok, bank", bank)
+
+
+@pytest.mark.parametrize("bank", [0, 64])
+def test_sq_fp_weight_side_full(sqf, bank):
+    """The floating-point weight-side format (E2M1 low, E4M3 sparse values,
+    E4M3 activations and branch) at full size, 1/8 of the slots kept."""
+    lay = synth.sq_weight()
+    st = _sqf_fp_check(sqf, lay, (lay.k - lay.k_out) // 8, f"sq fp full bank {bank}", bank=bank,
+                       rows=sample_rows(lay.m, 8, seed=50 + bank))
+    _log("sq fp full", bank, st)

@@ -634,3 +634,73 @@ def test_sq_banked_key_ties(sqf):
     for c in range(0, lay.k - 3, 4):
         lay.x_cal[:, c + 1:c + 4] = lay.x_cal[:, c:c + 1]
     _sq_check(sqf, lay, 256, "sq bank ties", bank=64)
+
+
+# ------------------------------------------------------------------ floating-point SQ-format
+def _sqf_fp_check(sqf, lay, nnz, label, bank=0, x_dtype="bf16", rows=None):
+    """E4M3 activations, E2M1 weights with the 0x8 mark, E4M3 sparse values
+    and branch: every byte and scale bit for bit, Y within tolerance."""
+    k_out = lay.k_out
+    k_low = lay.k - k_out
+    x_cal = torch.from_numpy(lay.x_cal).cuda()
+    w = torch.from_numpy(lay.w).cuda()
+    _, mp, _, hdiag = sqf.sqf_select_channels(x_cal, w, k_out)
+    wts = sqf.sqf_pack_weights(w, mp, branch="fp8", hdiag=hdiag, sq_nnz=nnz, sq_bank=bank, low="fp4")
+    ox, ofmt, xt = x_inputs(lay, x_dtype)
+    acts = sqf.alloc_acts(lay.m, k_low, k_out, low="fp8", branch="fp8")
+    sqf.sqf_quantize_split_act(xt, mp, acts)
+    y = sqf.sqf_dual_gemm(acts, wts)
+    torch.cuda.synchronize()
+    o_mp = mp.cpu().numpy()
+    o_hd = hdiag.cpu().numpy()
+    o_w = oracle.pack_weights_sqf(lay.w, o_mp, o_hd, nnz, bank=bank)
+    assert np.array_equal(wts.t["w_low"][0].cpu().numpy(), o_w["w_low"]), "E2M1 codes differ"
+    assert np.array_equal(wts.t["sq_val"].cpu().numpy().view(np.uint8), o_w["sq_val"]), "E4M3 values differ"
+    assert f32_bits_equal(wts.t["s_w"][0].cpu().numpy(), o_w["s_w"])
+    assert f32_bits_equal(wts.t["s_w8"].cpu().numpy(), o_w["s_w8"])
+    assert np.array_equal(wts.t["w_out"][0].cpu().numpy(), o_w["w_out"])
+    assert f32_bits_equal(wts.t["s_wo"][0].cpu().numpy(), o_w["s_wo"])
+    o_a = oracle.quantize_split_act(ox, o_mp, low="fp8", branch="fp8", x_fmt=ofmt)
+    assert np.array_equal(acts.t["x_low"].cpu().numpy(), o_a["x_low"]), "E4M3 activations differ"
+    assert np.array_equal(acts.t["x_out"].cpu().numpy(), o_a["x_out"])
+    assert f32_bits_equal(acts.t["s_x"].cpu().numpy(), o_a["s_x"])
+    assert f32_bits_equal(acts.t["s_xo"].cpu().numpy(), o_a["s_xo"])
+    if rows is None:
+        rows = np.arange(lay.m, dtype=np.int64)
+    o_y = oracle.dual_gemm_sqf(o_a, o_w, rows=rows)
+    return assert_rows_close(y.cpu().numpy()[rows], o_y, label)
+
+
+@pytest.mark.parametrize("x_dtype", ["bf16", "f32"])
+def test_sq_fp_small(sqf, x_dtype):
+    lay = _ragged(m=300, k=1280, n=260, n_scaled=64, seed=141)
+    _print("sq fp small", x_dtype, _sqf_fp_check(sqf, lay, (lay.k - lay.k_out) // 8, "sq fp", x_dtype=x_dtype))
+
+
+@pytest.mark.parametrize("m,k,n,den,bank", [
+    (257, 1280, 129, 2, 0),     # dense marks: past the value window
+    (70, 640, 130, 1, 0),       # every low slot marked
+    (200, 1280, 300, 8, 64),    # banks of 64 (k_low = 1024)
+    (5, 256, 3, 128, 0),        # a few values in total
+])
+def test_sq_fp_densities_and_banks(sqf, m, k, n, den, bank):
+    n_scaled = 256 if bank else max(1, k // 16)
+    lay = _ragged(m=m, k=k, n=n, n_scaled=n_scaled, seed=142 + den)
+    nnz = max(1, (lay.k - lay.k_out) // den)
+    _print("sq fp", m, k, n, den, bank, _sqf_fp_check(sqf, lay, nnz, f"sq fp 1/{den} bank {bank}", bank=bank))
+
+
+def test_sq_fp_refuses_debug_and_mismatch(sqf):
+    lay = _ragged(m=64, k=512, n=64, n_scaled=32, seed=146)
+    x_cal = torch.from_numpy(lay.x_cal).cuda()
+    w = torch.from_numpy(lay.w).cuda()
+    _, mp, _, hd = sqf.sqf_select_channels(x_cal, w, lay.k_out)
+    wts = sqf.sqf_pack_weights(w, mp, branch="fp8", hdiag=hd, sq_nnz=60, low="fp4")
+    acts = sqf.alloc_acts(lay.m, lay.k - lay.k_out, lay.k_out, low="fp8", branch="fp8")
+    sqf.sqf_quantize_split_act(x_inputs(lay, "bf16")[2], mp, acts)
+    with pytest.raises(sqf.SqfError) as ei:
+        sqf.sqf_dual_gemm(acts, wts, debug=True)
+    assert ei.value.status == sqf.SQF_ERR_UNSUPPORTED
+    a8 = sqf.alloc_acts(lay.m, lay.k - lay.k_out, lay.k_out, low="i8", branch="fp8")
+    with pytest.raises(sqf.SqfError):
+        sqf.sqf_dual_gemm(a8, wts)
