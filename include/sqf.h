@@ -29,13 +29,14 @@
  *          SQF_I4_E2M3 holds the same int4 codes, each in a 6-bit OCP E2M3
  *          field read as a subnormal (value code/8: field = sign << 5 | |code|),
  *          32 slots per 24 bytes (slot i of a 32-group at bits 6i..6i+5,
- *          little-endian) in a K-blocked array [ldk/96][P/16][4][16][24] with
- *          P = sqf_pad_rows(m): the 24 bytes of slots 32g..32g+31 of K block kb
- *          (slots 128kb..128kb+127) of row r sit at
- *          (((kb*P/16 + r/16)*4 + g)*16 + r%16)*24 (the 6-bit matrix unit's
- *          lane order).  Rows beyond m are never written and never reach an
- *          output.
- *          SQF_MXFP4 holds OCP MXFP4 ([OSC] abstract: the low path on 4-bit
+ *          little-endian), K-blocked with P = sqf_pad_rows(m): for K block
+ *          kb (slots 128kb..128kb+127) and rows 32p..32p+31 the 3072 bytes at
+ *          (kb*P/32 + p)*3072 hold, for row r of them (h = (r/16)%2, lane =
+ *          16g + r%16, g the 32-slot group), bytes 0..15 of its 24 at
+ *          h*1024 + 16*lane and bytes 16..23 at 2048 + 16*lane + 8h (the
+ *          6-bit matrix unit's lane order).  Rows beyond m are never written
+ *          and never reach an output.
+          SQF_MXFP4 holds OCP MXFP4 ([OSC] abstract: the low path on 4-bit
  *          micro-scaling hardware): every 32 slots 32b..32b+31 of a row are
  *          one block of E2M1 codes (sign bit 3, exponent bits 2..1 with bias
  *          1, mantissa bit 0) sharing one E8M0 scale byte (value 2^(s-127)).
@@ -90,7 +91,7 @@
 extern "C" {
 #endif
 
-#define SQF_ABI_VERSION 4
+#define SQF_ABI_VERSION 5
 
 typedef enum {
   SQF_OK = 0,

@@ -179,16 +179,40 @@ def pad_rows(rows: int) -> int:
 
 
 def i4x2_to_e2m3(packed: np.ndarray, rows_pad: int | None = None) -> np.ndarray:
-    """Packed int4 rows [rows][ldk] -> the K-blocked E2M3 array holding the
-    same codes, shaped [2*ldk/128][rows_pad/16][4][16][24] (K block, 16-row
-    group, 32-slot group, row in the group, 24 bytes of 6-bit fields)."""
+    """Packed int4 rows [rows][ldk] -> the K-blocked E2M3 storage holding the
+    same codes, shaped [2*ldk/128][rows_pad/32][3072] (K block, pair of
+    16-row groups, the pair's two head KiB and tail KiB; see orc_i4x2_to_e2m3)."""
     packed = np.ascontiguousarray(packed, dtype=np.uint8)
     rows, ldk = packed.shape
     rp = pad_rows(rows) if rows_pad is None else rows_pad
-    out = np.zeros((2 * ldk // 128, rp // 16, 4, 16, 24), dtype=np.uint8)
+    out = np.zeros((2 * ldk // 128, rp // 32, 3072), dtype=np.uint8)
     if rows and ldk:
         _load().orc_i4x2_to_e2m3(_p(packed), rows, ldk, rp, _p(out))
     return out
+
+
+def e2m3_group(storage: np.ndarray, r: int, kb: int, g: int) -> np.ndarray:
+    """The 24 bytes (32 six-bit fields) of slot group g of K block kb of row r
+    in the K-blocked E2M3 storage (the layout's position formula)."""
+    lane, h = g * 16 + r % 16, (r // 16) % 2
+    blk = storage[kb, r // 32]
+    return np.concatenate([blk[h * 1024 + lane * 16: h * 1024 + lane * 16 + 16],
+                           blk[2048 + lane * 16 + 8 * h: 2048 + lane * 16 + 8 * h + 8]])
+
+
+def e2m3_row_of_byte(nkb: int, rows_pad: int) -> np.ndarray:
+    """For every byte of the K-blocked E2M3 storage, the row it belongs to."""
+    o = np.arange(3072)
+    row = np.empty(3072, np.int64)
+    head = o < 2048
+    h_head = o // 1024
+    lane_head = (o % 1024) // 16
+    row[head] = h_head[head] * 16 + lane_head[head] % 16
+    lane_tail = (o - 2048) // 16
+    h_tail = ((o - 2048) % 16) // 8
+    row[~head] = h_tail[~head] * 16 + lane_tail[~head] % 16
+    rows = (np.arange(rows_pad // 32) * 32)[:, None] + row[None, :]
+    return np.broadcast_to(rows, (nkb, rows_pad // 32, 3072))
 
 
 def quantize_vec(v: np.ndarray, fmt: str):

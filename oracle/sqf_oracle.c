@@ -641,28 +641,41 @@ uint8_t orc_e2m3_field_of_code(int code) {
 
 /* Re-encode packed int4 rows (the layout of orc_quantize_split_act /
  * orc_pack_weights: [rows][ldk], slot 2i in the low nibble of byte i) into
- * the K-blocked E2M3 layout [pad/128][rows_pad/16][4][16][24]: the 32 slots
- * 32g .. 32g+31 of K block kb (slots 128kb .. 128kb+127) of row r are 24
- * bytes at (((kb * rows_pad/16 + r/16) * 4 + g) * 16 + r%16) * 24, field j%32
- * at bits 6*(j%32) of those bytes, little-endian.  (Within a 16-row group and
- * a K block the 24-byte pieces are ordered slot group first, row second.)
- * pad = 2*ldk slots per row; rows_pad >= rows, a multiple of 16; the rows
- * past `rows` are left zero. */
+ * the K-blocked E2M3 storage.  The 32 slots 32g .. 32g+31 of K block kb
+ * (slots 128kb .. 128kb+127) of row r form a 24-byte group, field j%32 at
+ * bits 6*(j%32), little-endian.  Rows are taken in pairs of 16-row groups:
+ * for K block kb and rows 32p .. 32p+31 (p = r/32, h = (r/16)%2, lane =
+ * 16g + r%16) the 3072 bytes at (kb * rows_pad/32 + p) * 3072 hold
+ *   bytes 0..15 of the group at h*1024 + lane*16   (the two "head" KiB),
+ *   bytes 16..23 of the group at 2048 + lane*16 + 8h   (the "tail" KiB).
+ * (A storage convention of this implementation, not of the method: it lets
+ * each lane read its 24 bytes with 16-byte loads.)  pad = 2*ldk slots per
+ * row; rows_pad >= rows, a multiple of 32; the rows past `rows` are left
+ * zero. */
 void orc_i4x2_to_e2m3(const uint8_t* packed, int64_t rows, int64_t ldk, int64_t rows_pad,
                       uint8_t* out) {
-  const int64_t pad = 2 * ldk, nblk = pad / 128, rg = rows_pad / 16;
+  const int64_t pad = 2 * ldk, nblk = pad / 128, npair = rows_pad / 32;
   memset(out, 0, (size_t)(nblk * rows_pad * 96));
+  uint8_t grp[24];
   for (int64_t r = 0; r < rows; ++r) {
-    for (int64_t j = 0; j < pad; ++j) {
-      uint8_t b = packed[r * ldk + (j >> 1)];
-      uint8_t nib = (uint8_t)(((j & 1) ? (b >> 4) : b) & 0xF);
-      int code = (nib & 0x8) ? (int)nib - 16 : (int)nib;
-      uint32_t f = orc_e2m3_field_of_code(code);
-      int64_t kb = j / 128, g = (j % 128) / 32;
-      uint8_t* grp = out + (((kb * rg + r / 16) * 4 + g) * 16 + r % 16) * 24;
-      int64_t bit = 6 * (j % 32);
-      for (int t = 0; t < 6; ++t)
-        if ((f >> t) & 1u) grp[(bit + t) >> 3] |= (uint8_t)(1u << ((bit + t) & 7));
+    for (int64_t kb = 0; kb < nblk; ++kb) {
+      for (int64_t g = 0; g < 4; ++g) {
+        memset(grp, 0, sizeof grp);
+        for (int64_t i = 0; i < 32; ++i) {
+          int64_t j = kb * 128 + g * 32 + i;
+          uint8_t b = packed[r * ldk + (j >> 1)];
+          uint8_t nib = (uint8_t)(((j & 1) ? (b >> 4) : b) & 0xF);
+          int code = (nib & 0x8) ? (int)nib - 16 : (int)nib;
+          uint32_t f = orc_e2m3_field_of_code(code);
+          int64_t bit = 6 * i;
+          for (int t = 0; t < 6; ++t)
+            if ((f >> t) & 1u) grp[(bit + t) >> 3] |= (uint8_t)(1u << ((bit + t) & 7));
+        }
+        const int64_t lane = g * 16 + r % 16, h = (r / 16) % 2;
+        uint8_t* base = out + (kb * npair + r / 32) * 3072;
+        memcpy(base + h * 1024 + lane * 16, grp, 16);
+        memcpy(base + 2048 + lane * 16 + 8 * h, grp + 16, 8);
+      }
     }
   }
 }

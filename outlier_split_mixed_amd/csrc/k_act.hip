@@ -526,12 +526,17 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
     uint8_t* xl = p.x_low + m * ldk;
     if constexpr (LOW == kI4E2M3) {
       // 6-bit fields: 8-byte piece q is bytes 8*(q%3) .. +7 of slot group
-      // (q/3)%4 of K block q/12, stored at that block's 16-row group m/16,
-      // slot group, row m%16 (the matrix unit's lane order)
-      const int64_t rg = p.rows_pad / 16;
+      // g = (q/3)%4 of K block q/12; the group's bytes 0..15 (pieces 0, 1)
+      // go to the head KiB h = (m/16)%2 of the row pair m/32 at 16*lane,
+      // bytes 16..23 (piece 2) to the tail KiB at 16*lane + 8h, lane =
+      // 16g + m%16 (the matrix unit's lane order, read with 16-byte loads)
+      const int64_t npair = p.rows_pad / 32;
+      const int64_t h = (m >> 4) & 1;
       for (int64_t q = tid; q < ldk / 8; q += NT) {
-        const int64_t kb = q / 12, g = (q / 3) & 3;
-        uint8_t* dst = p.x_low + (((kb * rg + m / 16) * 4 + g) * 16 + (m & 15)) * 24 + (q % 3) * 8;
+        const int64_t kb = q / 12, g = (q / 3) & 3, part = q % 3;
+        const int64_t lane = g * 16 + (m & 15);
+        uint8_t* base = p.x_low + (kb * npair + m / 32) * 3072;
+        uint8_t* dst = part < 2 ? base + h * 1024 + lane * 16 + part * 8 : base + 2048 + lane * 16 + h * 8;
         *(v2u*)dst = *(const v2u*)(img + q * 8);
         *(v2u*)(img + q * 8) = v2u{0u, 0u};
       }

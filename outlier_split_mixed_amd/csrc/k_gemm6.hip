@@ -30,15 +30,19 @@
 // fragment's byte.
 //
 // Layout.  Both low operands are K-blocked and stored in the matrix unit's
-// lane order: for K block kb (128 slots) and 16-row group rg, 1536 bytes
-// hold slot group g (32 slots, 24 bytes) of row r at (g*16 + r%16)*24, which
-// is exactly lane 16g + r%16's share of one 16 x 128 FP6 operand.  A 256-row
-// panel of one K block is one contiguous 24 KiB run (moved by the stage's
-// DMAs as whole cache lines), and each lane's fragment read is 24 bytes at
-// 24*lane: consecutive lanes, consecutive banks.  (A plain row pitch of 96
-// bytes put rows r, r+4, r+8, r+12 on the same banks: 73% of the LDS cycles
-// were bank conflicts.)  The rows are padded to a multiple of 256, so a
-// panel never leaves its block.
+// lane order.  For K block kb (128 slots), slot group g (32 slots, 24 bytes
+// of fields) of row r belongs to lane 16g + r%16 of the 16 x 128 FP6 operand
+// of its 16-row group.  Rows go in pairs of 16-row groups (rows 32p ..
+// 32p+31, 3 KiB per K block): the first KiB holds bytes 0..15 of every lane
+// of the first group, the second KiB those of the second group, the third
+// KiB bytes 16..23 of both (lane l at 16l: the first group's 8, then the
+// second's).  Each lane's 24 bytes of two fragments are then three
+// conflict-free 16-byte reads; 8-byte reads moved ~40% fewer bytes per
+// clock and made the LDS the limit (and a plain 96-byte row pitch put rows
+// r, r+4, r+8, r+12 on the same banks: 73% of the LDS cycles were bank
+// conflicts).  A 256-row panel of one K block is one contiguous 24 KiB run,
+// moved by the stage's DMAs as whole cache lines; rows are padded to a
+// multiple of 256, so a panel never leaves its block.
 //
 // (MXFP4: 16 bytes per lane, 1 KiB per 16-row fragment, 16 KiB per panel;
 // the scales of a panel's K block are one contiguous KiB.)
@@ -95,18 +99,24 @@ struct LowFmt<kMXFP4> {
   static constexpr int kType = 4;  // FP4 E2M1 operands
 };
 
-// One operand fragment of lane l (32 fields: row l%16 of the fragment, slots
-// 32*(l/16) .. +31 of the stage): E2M3, three 8-byte LDS reads into 6
-// registers; E2M1, one 16-byte read into 4 (the rest of the tuple unused).
-template <int LF>
-__device__ __forceinline__ v8i ld_frag(const uint8_t* p) {
-  if constexpr (LF == kI4E2M3) {
-    const v2u a = *(const v2u*)p, b = *(const v2u*)(p + 8), c = *(const v2u*)(p + 16);
-    return v8i{(int)a.x, (int)a.y, (int)b.x, (int)b.y, (int)c.x, (int)c.y, 0, 0};
-  } else {
-    const v4i a = *(const v4i*)p;
-    return v8i{a.x, a.y, a.z, a.w, 0, 0, 0, 0};
-  }
+// Operand fragments of lane l (32 fields: row l%16 of the fragment, slots
+// 32*(l/16) .. +31 of the stage).  E2M1: one 16-byte read into 4 registers
+// (the rest of the tuple unused).  E2M3: fragments come in pairs (rows
+// 32p .. 32p+31); three 16-byte reads -- the two fragments' heads (bytes
+// 0..15 of each lane's 24) and their interleaved tails (bytes 16..23) --
+// fill 6 registers of each.  (ds_read_b128 moves about 1.6x the bytes per
+// clock of ds_read_b64 here, and 24-byte reads as b64 x 3 made the LDS the
+// limit of the stage.)
+__device__ __forceinline__ v8i ld_fp4(const uint8_t* p) {
+  const v4i a = *(const v4i*)p;
+  return v8i{a.x, a.y, a.z, a.w, 0, 0, 0, 0};
+}
+__device__ __forceinline__ void ld_fp6_pair(const uint8_t* pair, int lane, v8i& f0, v8i& f1) {
+  const v4i h0 = *(const v4i*)(pair + lane * 16);
+  const v4i h1 = *(const v4i*)(pair + 1024 + lane * 16);
+  const v4i t = *(const v4i*)(pair + 2048 + lane * 16);
+  f0 = v8i{h0.x, h0.y, h0.z, h0.w, t.x, t.y, 0, 0};
+  f1 = v8i{h1.x, h1.y, h1.z, h1.w, t.z, t.w, 0, 0};
 }
 
 // s_waitcnt vmcnt for a wave-uniform count n of DMAs still allowed in
@@ -262,12 +272,12 @@ __global__ __launch_bounds__(kNW * 64, 2) void k_gemm6(Gemm6Args p) {
 #pragma unroll
     for (int j = 0; j < kTN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // this lane's byte offsets inside a low stage's panels: fragment (16 rows)
-  // f of a panel is bytes f*16*kRowB .. , lane l's share at (kRowB/4)*l
+  // the wave's fragments inside a low stage's panels: fragment (16 rows) f of
+  // a panel is bytes f*16*kRowB .. +16*kRowB-1 (E2M3: fragment pairs of 3 KiB)
   const int fr = lane & 15, fg = lane >> 4;
   constexpr int kFragB = 16 * F::kRowB;
-  const uint32_t a_off = (uint32_t)(wm * kTM * kFragB + lane * (F::kRowB / 4));
-  const uint32_t b_off = (uint32_t)(F::kPanelB + wn * kTN * kFragB + lane * (F::kRowB / 4));
+  const uint32_t a_off = (uint32_t)(wm * kTM * kFragB);
+  const uint32_t b_off = (uint32_t)(F::kPanelB + wn * kTN * kFragB);
   // MXFP4 scale dwords: 64-row group h of the panel, lane l at 4*l
   const uint32_t as_off = (uint32_t)(2 * F::kPanelB + wm * 2 * 256 + 4 * lane);
   const uint32_t bs_off = (uint32_t)(2 * F::kPanelB + 1024 + wn * 256 + 4 * lane);
@@ -284,17 +294,29 @@ __global__ __launch_bounds__(kNW * 64, 2) void k_gemm6(Gemm6Args p) {
     if (t + kRing - 1 < ST) issue(t + kRing - 1);
     const uint8_t* sl = smem + (t % kRing) * F::kSlot;
     v8i B[kTN];
+    if constexpr (LF == kI4E2M3) {
 #pragma unroll
-    for (int j = 0; j < kTN; ++j) B[j] = ld_frag<LF>(sl + b_off + j * kFragB);
+      for (int j = 0; j < kTN; j += 2) ld_fp6_pair(sl + b_off + j * kFragB, lane, B[j], B[j + 1]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kTN; ++j) B[j] = ld_fp4(sl + b_off + j * kFragB + lane * 16);
+    }
     int sa0 = 0, sa1 = 0, sb = 0;
     if constexpr (LF == kMXFP4) {
       sa0 = *(const int*)(sl + as_off);
       sa1 = *(const int*)(sl + as_off + 256);
       sb = *(const int*)(sl + bs_off);
     }
+    v8i Anext;
 #pragma unroll
     for (int i = 0; i < kTM; ++i) {
-      const v8i A = ld_frag<LF>(sl + a_off + i * kFragB);
+      v8i A;
+      if constexpr (LF == kI4E2M3) {
+        if (i % 2 == 0) ld_fp6_pair(sl + a_off + i * kFragB, lane, A, Anext);
+        else A = Anext;
+      } else {
+        A = ld_fp4(sl + a_off + i * kFragB + lane * 16);
+      }
       // Wave priority: the two waves of a SIMD cross the same barrier and
       // reach their MFMA runs together; raising it after the first fragment
       // and dropping it before the last lets one issue back to back while

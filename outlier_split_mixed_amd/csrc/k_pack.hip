@@ -166,12 +166,13 @@ __global__ __launch_bounds__(1024) void k_pack_osc(PackArgs p) {
                        d2 = (f[2] >> 16) | (f[3] << 8), d3 = f[4] | (f[5] << 24),
                        d4 = (f[5] >> 8) | (f[6] << 16), d5 = (f[6] >> 16) | (f[7] << 8);
         if (live) {
-          // K block q/4, 16-row group nn/16, slot group q%4, row nn%16
-          uint8_t* dst =
-              p.w_low + ((((q >> 2) * (p.rows_pad / 16) + nn / 16) * 4 + (q & 3)) * 16 + (nn & 15)) * 24;
-          *(v2u*)dst = v2u{d0, d1};
-          *(v2u*)(dst + 8) = v2u{d2, d3};
-          *(v2u*)(dst + 16) = v2u{d4, d5};
+          // K block q/4, row pair nn/32, slot group q%4: bytes 0..15 to the
+          // head KiB (nn/16)%2 at 16*lane, bytes 16..23 to the tail KiB at
+          // 16*lane + 8*((nn/16)%2), lane = 16*(q%4) + nn%16
+          const int64_t lane = (q & 3) * 16 + (nn & 15), h = (nn >> 4) & 1;
+          uint8_t* base = p.w_low + ((q >> 2) * (p.rows_pad / 32) + nn / 32) * 3072;
+          *(uint4*)(base + h * 1024 + lane * 16) = make_uint4(d0, d1, d2, d3);
+          *(v2u*)(base + 2048 + lane * 16 + h * 8) = v2u{d4, d5};
         }
       } else {
         if (live) *(uint4*)(wl + q * 16) = make_uint4(ow[0], ow[1], ow[2], ow[3]);

@@ -30,7 +30,7 @@ SQF_F32, SQF_BF16, SQF_FP8_E4M3, SQF_I8, SQF_I4X2, SQF_I4_E2M3, SQF_MXFP4, SQF_F
 DTYPES = {"f32": SQF_F32, "bf16": SQF_BF16, "fp8": SQF_FP8_E4M3, "i8": SQF_I8, "i4": SQF_I4X2,
           "i4e2m3": SQF_I4_E2M3, "mxfp4": SQF_MXFP4, "fp4": SQF_FP4_E2M1}
 TILES = {"auto": -1, "256": 0, "128": 1, "64": 2}
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 P = ctypes.c_void_p
 I64 = ctypes.c_int64
@@ -136,13 +136,14 @@ def low_ldk(k_low: int, low: str) -> int:
 
 def _low_tensor(rows: int, k_low: int, low: str, device, zero: bool):
     """The low operand in its layout: [rows][ldk], or K-blocked with
-    P = sqf_pad_rows(rows): 6-bit E2M3 [pad/128][P/16][4][16][24], MXFP4 E2M1
-    pairs [pad/128][P/16][4][16][16]."""
+    P = sqf_pad_rows(rows): 6-bit E2M3 [pad/128][P/32][3072] (pairs of 16-row
+    groups), MXFP4 E2M1 pairs [pad/128][P/16][4][16][16]."""
     mk = torch.zeros if zero else torch.empty
     p = sqf_pad_k_low(k_low)
-    if low in ("i4e2m3", "mxfp4"):
-        piece = 24 if low == "i4e2m3" else 16
-        return mk((p // 128, sqf_pad_rows(rows) // 16, 4, 16, piece), dtype=torch.uint8, device=device)
+    if low == "i4e2m3":
+        return mk((p // 128, sqf_pad_rows(rows) // 32, 3072), dtype=torch.uint8, device=device)
+    if low == "mxfp4":
+        return mk((p // 128, sqf_pad_rows(rows) // 16, 4, 16, 16), dtype=torch.uint8, device=device)
     return mk((rows, low_ldk(k_low, low)), dtype=torch.uint8, device=device)
 
 

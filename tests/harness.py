@@ -63,6 +63,14 @@ def tile_band_rows(m, tile=256):
     return np.unique(np.concatenate([band, last])).astype(np.int64)
 
 
+def e2m3_rows_equal(got, want, m):
+    """K-blocked E2M3 storages equal on every byte of the m real rows (the
+    activation kernel never writes the padding rows)."""
+    rb = oracle.e2m3_row_of_byte(got.shape[0], got.shape[1] * 32)
+    keep = rb < m
+    return got.shape == want.shape and np.array_equal(got[keep], want[keep])
+
+
 def _decode_i4(packed, k_low):
     lo = (packed & 0xF).astype(np.int8)
     hi = (packed >> 4).astype(np.int8)
@@ -137,9 +145,7 @@ def run_layer(sqf, lay, k_out, branch="bf16", x_dtype="bf16", rows=None, check_s
         got = acts.t["x_low"].cpu().numpy()
         assert got.shape == want.shape
         # rows past m are never written: compare the m real rows
-        rows_of = lambda t: t.transpose(0, 1, 3, 2, 4).reshape(t.shape[0], t.shape[1] * 16, 4, 24)
-        gv, wv = rows_of(got)[:, :lay.m], rows_of(want)[:, :lay.m]
-        assert np.array_equal(gv, wv), "6-bit x_low differs"
+        assert e2m3_rows_equal(got, want, lay.m), "6-bit x_low differs"
     else:
         assert np.array_equal(acts.t["x_low"].cpu().numpy(), o_a["x_low"]), "packed x_low differs"
     assert f32_bits_equal(acts.t["s_x"].cpu().numpy(), o_a["s_x"]), "s_x differs"

@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported(sqf):
 
 
 def test_abi_version_and_padding(sqf):
-    assert sqf.sqf_abi_version() == 4
+    assert sqf.sqf_abi_version() == 5
     assert sqf.sqf_pad_rows(0) == 0 and sqf.sqf_pad_rows(1) == 256 and sqf.sqf_pad_rows(4096) == 4096
     assert sqf.sqf_pad_rows(300) == 512 and sqf._lib.sqf_pad_rows(-1) == -1
     assert sqf.sqf_pad_k_low(0) == 0 and sqf.sqf_pad_k_low(1) == 256

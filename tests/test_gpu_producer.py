@@ -10,7 +10,7 @@ import torch
 import oracle
 from outlier_split_mixed_amd import synth
 
-from harness import assert_rows_close, f32_bits_equal, x_inputs
+from harness import assert_rows_close, e2m3_rows_equal, f32_bits_equal, x_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -49,8 +49,7 @@ def _norm_case(sqf, lay, low, x_dtype, eps=1e-5, seed=0, rows=None):
     if low == "i4e2m3":
         want = oracle.i4x2_to_e2m3(o_a["x_low"], oracle.pad_rows(lay.m))
         got = acts.t["x_low"].cpu().numpy()
-        rows_of = lambda t: t.transpose(0, 1, 3, 2, 4).reshape(t.shape[0], t.shape[1] * 16, 4, 24)
-        assert np.array_equal(rows_of(got)[:, :lay.m], rows_of(want)[:, :lay.m]), "x_low differs"
+        assert e2m3_rows_equal(got, want, lay.m), "x_low differs"
     else:
         assert np.array_equal(acts.t["x_low"].cpu().numpy(), o_a["x_low"]), "x_low differs"
     assert f32_bits_equal(acts.t["s_x"].cpu().numpy(), o_a["s_x"]), "s_x differs"

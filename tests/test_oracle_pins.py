@@ -548,35 +548,42 @@ def test_e2m3_storage_hand_case(golden):
     j1, c1 = int(g["row1_slot"][0][0]), int(g["row1_code"][0][0])
     packed[1, j1 >> 1] |= (c1 & 0xF) << (4 * (j1 & 1))
     out = oracle.i4x2_to_e2m3(packed)
-    assert out.shape == (2, 16, 4, 16, 24)  # [K block][16-row group][slot group][row][24 B]
-    assert out[0, 0, 0, 0, :6].tolist() == _hexbytes(g["row0_block0"])[0].tolist()
-    out[0, 0, 0, 0, :6] = 0
-    assert out[1, 0, 0, 1, :3].tolist() == _hexbytes(g["row1_block1"])[0].tolist()
-    out[1, 0, 0, 1, :3] = 0
+    assert out.shape == (2, 8, 3072)  # [K block][pair of 16-row groups][3072 B]
+    assert out[0, 0, 0:6].tolist() == _hexbytes(g["row0_block0"])[0].tolist()  # row 0: lane 0, head
+    out[0, 0, 0:6] = 0
+    assert out[1, 0, 16:19].tolist() == _hexbytes(g["row1_block1"])[0].tolist()  # row 1: lane 1
+    out[1, 0, 16:19] = 0
     assert not out.any()
 
 
 def test_e2m3_storage_brute_force_reader():
-    """Random packed rows: every slot read back from the K-blocked array by
-    its position formula decodes (OCP E2M3) to the nibble's code / 8."""
+    """Random packed rows: every slot read back from the storage by the
+    documented position formula (head bytes 0..15 at h*1024 + 16*lane, tail
+    bytes 16..23 at 2048 + 16*lane + 8h) decodes (OCP E2M3) to the code / 8;
+    bytes of rows past the real ones stay zero."""
     rng = np.random.default_rng(31)
-    rows, pad = 5, 512
+    rows, pad = 37, 512
     codes = rng.integers(-7, 8, (rows, pad))
     packed = np.zeros((rows, pad // 2), np.uint8)
     for r in range(rows):
         for j in range(pad):
             packed[r, j >> 1] |= (int(codes[r, j]) & 0xF) << (4 * (j & 1))
-    rows_pad = 32
-    out = oracle.i4x2_to_e2m3(packed, rows_pad).reshape(-1)
-    bits = np.unpackbits(out, bitorder="little")
+    rows_pad = 64
+    out = oracle.i4x2_to_e2m3(packed, rows_pad)
     for r in range(rows):
-        for j in range(pad):
-            kb, g = j // 128, (j % 128) // 32
-            piece = (((kb * (rows_pad // 16) + r // 16) * 4 + g) * 16 + r % 16) * 24
-            f = int(sum(int(bits[8 * piece + 6 * (j % 32) + t]) << t for t in range(6)))
-            assert _e2m3_value(f) * 8 == codes[r, j]
-    view = out.reshape(pad // 128, rows_pad // 16, 4, 16, 24)
-    assert not view[:, 0, :, rows:].any() and not view[:, 1:].any()
+        for kb in range(pad // 128):
+            for gg in range(4):
+                lane, h = gg * 16 + r % 16, (r // 16) % 2
+                blk = out[kb, r // 32]
+                grp = np.concatenate([blk[h * 1024 + 16 * lane: h * 1024 + 16 * lane + 16],
+                                      blk[2048 + 16 * lane + 8 * h: 2048 + 16 * lane + 8 * h + 8]])
+                bits = np.unpackbits(grp, bitorder="little")
+                for i in range(32):
+                    f = int(sum(int(bits[6 * i + t]) << t for t in range(6)))
+                    assert _e2m3_value(f) * 8 == codes[r, kb * 128 + gg * 32 + i]
+    rb = oracle.e2m3_row_of_byte(pad // 128, rows_pad)
+    assert not out[rb >= rows].any()
+    assert np.bincount(rb.reshape(-1)).tolist() == [96 * (pad // 128)] * rows_pad
 
 
 # ------------------------------------------------------------------ MXFP4
