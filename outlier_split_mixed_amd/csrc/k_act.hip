@@ -222,17 +222,19 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
   // groups, a contiguous run, so that the group (and its map) rarely changes
   // between consecutive rows of a block.
   // Strided rows: block b takes rows sigma(b) + i * G (G = gridDim.x).  When
-  // G is a multiple of 128, sigma places the 16 rows of each aligned 16-row
-  // group on 16 blocks of one XCD (blocks go to the XCDs round robin, block b
-  // to XCD b % 8), so the K-blocked layouts, whose smallest pieces are one
-  // row's 8..24 bytes inside a 16-row run, fill each cache line within one
-  // L2 in the same pass instead of leaving partial lines in eight.
+  // G is a multiple of 256 (128), sigma places the rows of each aligned
+  // 32-row (16-row) group on blocks of one XCD (blocks go to the XCDs round
+  // robin, block b to XCD b % 8), so the K-blocked layouts, whose smallest
+  // pieces are one row's 8..24 bytes inside a 16- or 32-row run, fill each
+  // cache line within one L2 in the same pass instead of leaving partial
+  // lines in several.
   int64_t m_first = blockIdx.x, m_stop = p.m, m_step = gridDim.x;
   if constexpr (!GROUPED) {
-    if ((gridDim.x & 127) == 0) {
-      const int64_t xcd = blockIdx.x & 7, s = blockIdx.x >> 3;
+    const int64_t xcd = blockIdx.x & 7, s = blockIdx.x >> 3;
+    if ((gridDim.x & 255) == 0)
+      m_first = ((s >> 5) * 8 + xcd) * 32 + (s & 31);
+    else if ((gridDim.x & 127) == 0)
       m_first = ((s >> 4) * 8 + xcd) * 16 + (s & 15);
-    }
   }
   int g_cur = 0;      // group of the current row (expert groups)
   int64_t g_end = 0;  // first row after it
@@ -532,13 +534,17 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
       // 16g + m%16 (the matrix unit's lane order, read with 16-byte loads)
       const int64_t npair = p.rows_pad / 32;
       const int64_t h = (m >> 4) & 1;
-      for (int64_t q = tid; q < ldk / 8; q += NT) {
-        const int64_t kb = q / 12, g = (q / 3) & 3, part = q % 3;
+      for (int64_t q = tid; q < ldk / 24; q += NT) {  // one 24-byte group per step
+        const int64_t kb = q >> 2, g = q & 3;
         const int64_t lane = g * 16 + (m & 15);
         uint8_t* base = p.x_low + (kb * npair + m / 32) * 3072;
-        uint8_t* dst = part < 2 ? base + h * 1024 + lane * 16 + part * 8 : base + 2048 + lane * 16 + h * 8;
-        *(v2u*)dst = *(const v2u*)(img + q * 8);
-        *(v2u*)(img + q * 8) = v2u{0u, 0u};
+        const v2u a = *(const v2u*)(img + q * 24), b = *(const v2u*)(img + q * 24 + 8),
+                  c = *(const v2u*)(img + q * 24 + 16);
+        *(v4u*)(base + h * 1024 + lane * 16) = v4u{a.x, a.y, b.x, b.y};
+        *(v2u*)(base + 2048 + lane * 16 + h * 8) = c;
+        *(v2u*)(img + q * 24) = v2u{0u, 0u};
+        *(v2u*)(img + q * 24 + 8) = v2u{0u, 0u};
+        *(v2u*)(img + q * 24 + 16) = v2u{0u, 0u};
       }
     } else if constexpr (LOW == kMXFP4) {
       // E2M1 pairs: 16-byte piece q is slot group q%4 of K block q/4, stored
