@@ -50,13 +50,24 @@ K_ALIGN_LOW = 256  # low slots are padded to a multiple of this
 K_ALIGN_OUT_BYTES = 128  # branch rows are padded to a multiple of 128 bytes
 
 
-def build(force: bool = True) -> str:
-    """Compile liboracle.so with gcc (scalar C, no fast-math, no contraction)."""
-    if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
-        tmp = LIB + ".tmp"
-        subprocess.check_call(["gcc", *CFLAGS, SRC, "-o", tmp, "-lm"])
-        os.replace(tmp, LIB)
-    return LIB
+# AddressSanitizer + UndefinedBehaviorSanitizer build of the same source
+# (tests/test_sanitizers.py runs the oracle's pins against it, with gcc's
+# libasan preloaded into the interpreter)
+SAN_LIB = os.path.join(HERE, "liboracle_san.so")
+SAN_CFLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+              "-fno-sanitize-recover=undefined", "-fno-fast-math", "-ffp-contract=off", "-fopenmp",
+              "-fPIC", "-shared", "-std=c11"]
+
+
+def build(force: bool = True, sanitize: bool = False) -> str:
+    """Compile liboracle.so with gcc (scalar C, no fast-math, no contraction);
+    ``sanitize`` builds liboracle_san.so with ASan and UBSan instead."""
+    lib, flags = (SAN_LIB, SAN_CFLAGS) if sanitize else (LIB, CFLAGS)
+    if force or not os.path.exists(lib) or os.path.getmtime(lib) < os.path.getmtime(SRC):
+        tmp = lib + ".tmp"
+        subprocess.check_call(["gcc", *flags, SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, lib)
+    return lib
 
 
 _lib = None
@@ -65,9 +76,12 @@ _lib = None
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB):
+        # SQF_ORACLE_LIBRARY (read once, at the first call) names another
+        # build of this source, e.g. the sanitizer build
+        path = os.environ.get("SQF_ORACLE_LIBRARY") or LIB
+        if path == LIB and not os.path.exists(LIB):
             build(force=True)
-        _lib = ctypes.CDLL(LIB)
+        _lib = ctypes.CDLL(path)
         _declare(_lib)
     return _lib
 

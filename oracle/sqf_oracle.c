@@ -60,6 +60,12 @@ static uint32_t bits_from_f32(float f) {
   return b;
 }
 
+/* memset(p, 0, n) that is also defined for n == 0 with p == NULL (an empty
+ * array passed from the caller) */
+static void zero_bytes(void* p, int64_t n) {
+  if (n > 0) memset(p, 0, (size_t)n);
+}
+
 /* bf16 -> fp32 is exact: the bf16 pattern is the top half of the fp32 one. */
 double orc_bf16_to_double(uint16_t h) { return (double)f32_from_bits((uint32_t)h << 16); }
 
@@ -218,7 +224,7 @@ void orc_select_channels(const float* x_cal, int64_t m_cal, int64_t k, const flo
 /* ------------------------------------------------------------------ */
 
 static void pack_i4_row(const int32_t* codes, int64_t len, uint8_t* row, int64_t ldk) {
-  memset(row, 0, (size_t)ldk);
+  zero_bytes(row, ldk);
   for (int64_t j = 0; j < len; ++j) {
     uint8_t nib = (uint8_t)(codes[j] & 0xF);
     if (j & 1)
@@ -387,7 +393,7 @@ void orc_pack_weights_sq(const float* w, int64_t k, int64_t n, const int32_t* ma
     }
     orc_sq_row(lo, hlo, k_low, nnz, bank, 4, fields, sq_val + nn * nnz, &s_w8[nn], &s_w4[nn]);
     uint8_t* row = w_low + nn * ldk;
-    memset(row, 0, (size_t)ldk);
+    zero_bytes(row, ldk);
     for (int64_t j = 0; j < k_low; ++j)
       row[j >> 1] |= (uint8_t)((j & 1) ? (fields[j] << 4) : fields[j]);
     if (ldo > 0) {
@@ -466,7 +472,7 @@ void orc_pack_weights_sqf(const float* w, int64_t k, int64_t n, const int32_t* m
     }
     orc_sqf_row(lo, hlo, k_low, nnz, bank, fields, sq_val + nn * nnz, &s_w8[nn], &s_w4[nn]);
     uint8_t* row = w_low + nn * ldk;
-    memset(row, 0, (size_t)ldk);
+    zero_bytes(row, ldk);
     for (int64_t j = 0; j < k_low; ++j)
       row[j >> 1] |= (uint8_t)((j & 1) ? (fields[j] << 4) : fields[j]);
     if (ldo > 0)
@@ -559,7 +565,7 @@ void orc_quantize_split_act(const void* x, int x_fmt, int64_t m, int64_t k, int6
     if (low_fmt == ORC_I4) {
       pack_i4_row(codes, k_low, dst, ldk);
     } else {
-      memset(dst, 0, (size_t)ldk);
+      zero_bytes(dst, ldk);
       for (int64_t j = 0; j < k_low; ++j) dst[j] = (uint8_t)(codes[j] & 0xFF);
     }
     if (ldo > 0) {
@@ -655,7 +661,7 @@ uint8_t orc_e2m3_field_of_code(int code) {
 void orc_i4x2_to_e2m3(const uint8_t* packed, int64_t rows, int64_t ldk, int64_t rows_pad,
                       uint8_t* out) {
   const int64_t pad = 2 * ldk, nblk = pad / 128, npair = rows_pad / 32;
-  memset(out, 0, (size_t)(nblk * rows_pad * 96));
+  zero_bytes(out, nblk * rows_pad * 96);
   uint8_t grp[24];
   for (int64_t r = 0; r < rows; ++r) {
     for (int64_t kb = 0; kb < nblk; ++kb) {
@@ -746,7 +752,7 @@ uint8_t orc_mx_block(const float* v, int64_t len, uint8_t* codes) {
 static void mx_row(const float* vals, int64_t len, int64_t pad, uint8_t* row, uint8_t* scales) {
   float blk[32];
   uint8_t c[32];
-  memset(row, 0, (size_t)(pad / 2));
+  zero_bytes(row, pad / 2);
   for (int64_t b = 0; b < pad / 32; ++b) {
     for (int i = 0; i < 32; ++i) {
       int64_t j = b * 32 + i;
@@ -825,8 +831,8 @@ void orc_quantize_split_act_mx(const void* x, int x_fmt, int64_t m, int64_t k, i
 void orc_mx_storage(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t pad,
                     int64_t rows_pad, uint8_t* codes_out, uint8_t* scales_out) {
   const int64_t nblk = pad / 128;
-  memset(codes_out, 0, (size_t)(nblk * rows_pad * 64));
-  memset(scales_out, 0, (size_t)(nblk * rows_pad * 4));
+  zero_bytes(codes_out, nblk * rows_pad * 64);
+  zero_bytes(scales_out, nblk * rows_pad * 4);
   for (int64_t r = 0; r < rows; ++r)
     for (int64_t kb = 0; kb < nblk; ++kb)
       for (int64_t g = 0; g < 4; ++g) {

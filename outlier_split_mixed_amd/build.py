@@ -53,6 +53,38 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+SAN_LIB = os.path.join(BUILD, "libsqf_hostsan.so")
+# host-side sanitizers only: each -fsanitize= follows -Xarch_host, so the
+# device code is built exactly as in the product library
+SAN_HOST_FLAGS = ["-g", "-fno-omit-frame-pointer", "-Xarch_host", "-fsanitize=address,undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=undefined"]
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    """libsqf with AddressSanitizer and UBSan in the C-ABI host code
+    (sqf_api.hip: argument checks, workspace handling, launch set-up), linked
+    with the kernels' objects of the last build(); written to _build/.  A
+    process that loads it needs clang's ASan runtime preloaded."""
+    api = os.path.join(CSRC, "sqf_api.hip")
+    objs = sorted(glob.glob(os.path.join(BUILD, "*.hip.o")))
+    kern = [o for o in objs if os.path.basename(o) != "sqf_api.hip.o"]
+    if len(kern) != len(glob.glob(os.path.join(CSRC, "*.hip"))) - 1:
+        raise RuntimeError("build() first: the kernel objects are missing from _build/")
+    obj = os.path.join(BUILD, "sqf_api.hostsan.o")
+    cmd = [HIPCC, *FLAGS, *SAN_HOST_FLAGS, "-I", os.path.join(ROOT, "include"), "-c", api, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {api}:\n{r.stderr}")
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address,undefined",
+           "-shared-libsan", obj, *kern, "-o", SAN_LIB]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    if verbose:
+        print(f"built {SAN_LIB}")
+    return SAN_LIB
+
+
 if __name__ == "__main__":
     build(verbose=True)
     sys.exit(0)

@@ -18,11 +18,13 @@ from dataclasses import dataclass, field
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsqf.so")
+# SQF_LIBRARY (read once, at import) names another build of libsqf, e.g. the
+# one whose host code carries AddressSanitizer (build.build_host_sanitized)
+LIB_PATH = os.environ.get("SQF_LIBRARY") or os.path.join(_HERE, "libsqf.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"libsqf.so not found at {LIB_PATH}; build it with `python -m outlier_split_mixed_amd.build`")
+        f"libsqf not found at {LIB_PATH}; build it with `python -m outlier_split_mixed_amd.build`")
 _lib = ctypes.CDLL(LIB_PATH)
 
 SQF_OK, SQF_ERR_INVALID_ARG, SQF_ERR_SHAPE, SQF_ERR_UNSUPPORTED, SQF_ERR_HIP, SQF_ERR_ALIGN = range(6)
