@@ -169,6 +169,26 @@ def time_layers(torch, runs, stream, steps, warmup):
     return total_ms / steps, act.mean(0), gemm.mean(0)
 
 
+def time_cold(torch, runs, stream, steps, flush_bytes=1 << 30):
+    """Each step timed alone after overwriting a 1 GiB device buffer on the
+    same stream, which evicts the L2s and the 256 MiB last-level cache: no
+    operand of the step is resident in any cache when it starts."""
+    buf = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    for s in range(steps):
+        with torch.cuda.stream(stream):
+            buf.fill_(float(s))
+        evs[s][0].record(stream)
+        for r in runs:
+            r.step(stream)
+        evs[s][1].record(stream)
+    torch.cuda.synchronize()
+    del buf
+    return np.array([a.elapsed_time(b) for a, b in evs])
+
+
 def cpu_baseline(lays, rows_per_layer):
     """The oracle (untuned) on a bounded sample of the same step: the online
     stages (activation quantise/split + dual GEMM) for `rows_per_layer` token
@@ -414,6 +434,8 @@ def main():
     step_ms, act_ms, gemm_ms = time_layers(torch, runs, stream, args.steps, args.warmup)
     act_s, gemm_s = time_layers.samples
     progress(f"step timed: {step_ms:.4f} ms")
+    cold = time_cold(torch, runs, stream, max(5, args.steps // 2))
+    progress(f"cold steps timed: median {np.median(cold):.4f} ms")
     total_ops = sum(r.ops for r in runs)
     value = total_ops / (step_ms * 1e-3) / 1e12
     gemm_ops = sum(r.ops for r in runs)
@@ -516,6 +538,12 @@ def main():
                      "avg_launch_us": round(float(gemm_ms.mean()) * 1e3, 2),
                      "ops_per_launch": gemm_ops / 3},
         "detail": detail,
+        "cold_step": {"protocol": "each step timed alone (HIP events on its stream) after a 1 GiB device "
+                                  "buffer is overwritten on the same stream: L2s and the 256 MiB last-level "
+                                  "cache hold no operand; the steps above run back to back (warm)",
+                      "steps": int(cold.size),
+                      "ms_p10_p50_p90": [round(float(np.percentile(cold, q)), 4) for q in (10, 50, 90)],
+                      "tops_at_p50": round(total_ops / (float(np.median(cold)) * 1e-3) / 1e12, 2)},
         "bf16_y_step": bf16_y,
         "packed_int4_step": i4_step,
         "mxfp4_step": mx_step,

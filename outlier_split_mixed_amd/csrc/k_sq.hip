@@ -11,20 +11,20 @@
 //   y = s_x*(s_w4*acc_low + s_w8*acc_sp) + s_xo*s_wo*acc_o
 //
 // gfx950 mapping.  The "gather unit" is the decode of each 128-slot K stage of
-// a block's W rows into LDS: a stage of a W row becomes
-//   * an int4 low tile with the marks cleared to 0 (SWAR: a nibble is the
-//     mark iff its top bit is set and its low three bits are zero), widened
-//     to int8 at MFMA time with the x16 trick (w << 4 & 0xF0.. and
-//     w & 0xF0..), which puts a group of 8 slots in the order 0,2,4,6,1,3,5,7;
+// a block's W rows into LDS, once per block: a stage of a W row becomes
+//   * an int8 low tile: the int4 codes with the marks cleared to 0 (SWAR: a
+//     nibble is the mark iff its top bit is set and its low three bits are
+//     zero), widened to int8 as 16*code (w << 4 & 0xF0.. and w & 0xF0..) and
+//     put back in slot order with two byte permutes per 8 slots;
 //   * an int8 tile holding the row's sparse values at their marked slots
-//     (zero elsewhere), in that same slot order: every 8-slot group is
-//     expanded at once from a window of the row's values with byte permutes
-//     whose selectors come from a table indexed by the group's mark mask.
-// The int8 activations stay in their natural order in LDS; each A fragment is
-// permuted into the widened slot order in registers as it is read, so both
-// tiles feed v_mfma_i32_16x16x64_i8 with one A fragment.  The low accumulator
-// carries the x16 factor (|acc| <= 16*127*7*k_low < 2^31 for the k_low the
-// host accepts); it is removed exactly in the epilogue.
+//     (zero elsewhere): every 8-slot group is expanded at once from a window
+//     of the row's values with byte permutes whose selectors come from a
+//     table indexed by the group's mark mask.
+// Both tiles and the int8 activations are in natural slot order, so the MFMA
+// loop is LDS reads and v_mfma_i32_16x16x64_i8 only: the widening is done
+// once per W row per block rather than once per wave that reads it.  The low
+// accumulator carries the x16 factor (|acc| <= 16*127*7*k_low < 2^31 for the
+// k_low the host accepts); it is removed exactly in the epilogue.
 //
 // Pipeline.  A block computes 256 x 128 outputs with 8 waves (4 x 2, each
 // 64 x 64).  Activations and raw W codes move global -> LDS by DMA
@@ -63,18 +63,28 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
-// byte position, inside a lane's 16-byte MFMA operand, of slot k (0..15) in
-// the widened order 0,2,4,6,1,3,5,7 | 8,10,12,14,9,11,13,15
-__device__ __forceinline__ int perm_pos(int k) {
-  return (k & 8) + ((k & 1) ? 4 + ((k & 7) >> 1) : ((k & 7) >> 1));
+// eight int4 codes (natural nibble order: slot 2b in the low nibble of byte
+// b) -> eight int8 values 16*code in slot order
+__device__ __forceinline__ uint2 widen8(uint32_t w) {
+  const uint32_t lo = (w << 4) & 0xF0F0F0F0u;  // slots 0, 2, 4, 6
+  const uint32_t hi = w & 0xF0F0F0F0u;         // slots 1, 3, 5, 7
+  return make_uint2(perm(hi, lo, 0x05010400u), perm(hi, lo, 0x07030602u));
 }
 
-// natural slot order -> widened slot order, 16 int8 codes
-__device__ __forceinline__ v4i to_widened(v4i u) {
-  return v4i{(int)perm((uint32_t)u.y, (uint32_t)u.x, 0x06040200u),
-             (int)perm((uint32_t)u.y, (uint32_t)u.x, 0x07050301u),
-             (int)perm((uint32_t)u.w, (uint32_t)u.z, 0x06040200u),
-             (int)perm((uint32_t)u.w, (uint32_t)u.z, 0x07050301u)};
+// dma_16B for lanes 0..47 only: the exec mask is narrowed and restored inside
+// the statement (the wave is converged here), so the caller has no branch
+__device__ __forceinline__ void dma_16B_lanes48(const uint8_t* base, uint32_t voff, uint32_t lds) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds);
+  uint64_t saved;
+  asm volatile(
+      "s_mov_b64 %0, exec\n\t"
+      "s_and_b32 exec_hi, exec_hi, 0xffff\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b64 exec, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(base), "{m0}"(m0v)
+      : "memory");
 }
 
 // LDS barrier that does not wait for outstanding global loads.
@@ -85,22 +95,37 @@ __device__ __forceinline__ void sq_sync() {
 
 // LDS map of one block (bytes).
 constexpr int kBM = 256, kBN = 128;
-constexpr int kStA = kBM * 128;  // activation stage: 16-row blocks of 16 x 128 B (swizzled)
-constexpr int kStW = kBN * 64;   // raw W stage: row-major, 64 B per row
-constexpr int kStV = kBN * 64;   // value windows: row-major, 64 B per row
-constexpr int kStL = kBN * 64;   // clean low tile: [row block][K half][entry] x 8 B
-constexpr int kStS = kBN * 128;  // sparse tile: [row block][K half][entry] x 16 B
-constexpr int kOffA = 0;
-constexpr int kOffW = kOffA + 2 * kStA;
-constexpr int kOffV = kOffW + 2 * kStW;
-constexpr int kOffL = kOffV + 2 * kStV;
-constexpr int kOffS = kOffL + 2 * kStL;
-constexpr int kOffSel = kOffS + 2 * kStS;
-constexpr int kSmem = kOffSel + 256 * 8;
-static_assert(kSmem <= 160 * 1024, "LDS budget");
+constexpr int kStA = kBM * 128;    // activation stage: 16-row blocks of 16 x 128 B (swizzled)
+constexpr int kStW = kBN * 64;     // raw W stage: row-major, 64 B per row
+constexpr int kVRow = 48;          // value window per row: three 16-byte blocks
+constexpr int kStV = kBN * kVRow;  // value windows: row-major
+constexpr int kStS = kBN * 128;    // sparse tile: [row block][K half][entry] x 16 B
+template <bool FP>
+struct SqLds {
+  // clean low tile: E2M1 nibbles [row block][entry] x 16 B (FP), or int8
+  // 16*code [row block][K half][entry] x 16 B (integer form)
+  static constexpr int kStL = FP ? kBN * 64 : kBN * 128;
+  static constexpr int kOffA = 0;
+  static constexpr int kOffW = kOffA + 2 * kStA;
+  static constexpr int kOffV = kOffW + 2 * kStW;
+  static constexpr int kOffL = kOffV + 2 * kStV;
+  static constexpr int kOffS = kOffL + 2 * kStL;
+  static constexpr int kOffSel = kOffS + 2 * kStS;
+  static constexpr int kSmem = kOffSel + 256 * 8;
+};
+static_assert(SqLds<false>::kSmem <= 160 * 1024 && SqLds<true>::kSmem <= 160 * 1024, "LDS budget");
 // the branch's W tile (128 rows x 128 B, swizzled like A) reuses the raw W
-// and value rings
-static_assert(kBN * 128 <= 2 * kStW + 2 * kStV, "branch W tile fits");
+// ring (even branch stages) and the clean-tile ring (odd ones)
+static_assert(kBN * 128 <= 2 * kStW && kBN * 128 <= 2 * SqLds<true>::kStL, "branch W tile fits");
+
+// Entry of MFMA lane (16-slot group g, row rr) in a 1 KiB block of a decoded
+// integer tile (16 rows x 64 slots of one K half f): 16 g + (rr ^ 4 (g/2 +
+// 2 f)).  The 64 lanes of a read cover the 64 entries once; the four lanes of
+// a row that write at once (two K halves x two groups) land on four different
+// 16-byte bank groups for each of the row's 4 x 4 neighbours.
+__device__ __forceinline__ int tile_entry(int g, int rr, int f) {
+  return (g << 4) | (rr ^ ((((g >> 1) + 2 * f) << 2) & 15));
+}
 
 }  // namespace
 
@@ -110,8 +135,11 @@ template <bool DEBUG, bool FP>
 __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
   static_assert(!(DEBUG && FP), "the floating-point form has no integer accumulators");
   using AccT = std::conditional_t<FP, v4f, v4i>;
+  using L = SqLds<FP>;
+  constexpr int kOffA = L::kOffA, kOffW = L::kOffW, kOffV = L::kOffV, kOffL = L::kOffL,
+                kOffS = L::kOffS, kOffSel = L::kOffSel, kStL = L::kStL;
   constexpr int TM = 4, TN = 4;
-  __shared__ __attribute__((aligned(2048))) uint8_t smem[kSmem];
+  __shared__ __attribute__((aligned(2048))) uint8_t smem[L::kSmem];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -184,43 +212,58 @@ __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
   const bool vdma = vtotal >= 16;
   const uint32_t vlast = (uint32_t)((vtotal & ~(int64_t)15) - 16);  // last whole block
   int vi = 0;  // row r's value index at the next stage to decode (same in its 4 lanes)
-  // value window of stage s: lane l brings 16-byte block l % 4 of its own row
+  // value window of stage s: lane l < 48 brings 16-byte block l % 3 of row
+  // 16w + l / 3 (whose value index it takes from that row's first decode lane)
+  const int vr = lane / 3, vb = lane - 3 * vr;
+  const int gn_v = n0 + wave * 16 + vr < nn ? n0 + wave * 16 + vr : nn - 1;
+  // (lanes 48..63 are switched off inside the DMA statement itself, so the
+  // issue adds no branch to the iteration's basic block)
   auto issue_v = [&](int s) {
-    const uint32_t start = (uint32_t)(((int64_t)gn * nnz + vi) & ~(int64_t)15);
-    uint32_t off = start + (uint32_t)(qq * 16);
+    const int v_row = __shfl(vi, (4 * vr) & 63, kWave);
+    const uint32_t start = (uint32_t)(((int64_t)gn_v * nnz + v_row) & ~(int64_t)15);
+    uint32_t off = start + (uint32_t)(vb * 16);
     if (off > vlast) off = vlast;  // past the buffer: any whole block (unused)
-    dma_16B(vdma ? (const uint8_t*)p.sq_val : p.x_low, vdma ? off : 0u,
-            sbase + kOffV + (uint32_t)((s & 1) * kStV) + (uint32_t)(wave * 1024));
+    dma_16B_lanes48(vdma ? (const uint8_t*)p.sq_val : p.x_low, vdma ? off : 0u,
+                    sbase + kOffV + (uint32_t)((s & 1) * kStV) + (uint32_t)(wave * 16 * kVRow));
   };
 
   // Expand selectors: for the mark mask m of an 8-slot group, byte p of the
-  // group's operand bytes (slot order 0,2,4,6,1,3,5,7) takes value number
-  // rank(slot) (a byte of the pool {hi, lo} of the group's values) if the
-  // slot is marked, else zero (selector 0x0C).
+  // group's operand bytes (slot order) takes value number rank(p) (a byte of
+  // the pool {hi, lo} of the group's values) if slot p is marked, else zero
+  // (selector 0x0C).
   uint2* sSel = (uint2*)(smem + kOffSel);
   if (tid < 256) {
     const int m = tid;
     uint32_t sel[2] = {0, 0};
 #pragma unroll
     for (int pp = 0; pp < 8; ++pp) {
-      const int sl = FP ? pp : (pp < 4 ? 2 * pp : 2 * (pp - 4) + 1);
-      const uint32_t b = ((m >> sl) & 1) ? (uint32_t)__builtin_popcount(m & ((1 << sl) - 1)) : 0x0Cu;
+      const uint32_t b = ((m >> pp) & 1) ? (uint32_t)__builtin_popcount(m & ((1 << pp) - 1)) : 0x0Cu;
       sel[pp >> 2] |= b << (8 * (pp & 3));
     }
     sSel[m] = make_uint2(sel[0], sel[1]);
   }
-
-  // Decoded-tile entry of MFMA lane (16-slot group g, row rr) in a K-half
-  // block: g * 16 + (rr ^ 8 (g / 2)), for the clean low tile also with g ^ f
-  // (f = K half); the sparse tile's 8-byte halves are swapped for f = 1.  The
-  // four lanes of a row write at once: these swizzles spread them over banks.
-  auto lpos = [](int g, int rr_, int f) { return ((g ^ f) << 4) + (rr_ ^ ((g >> 1) << 3)); };
-  auto spos = [](int g, int rr_) { return (g << 4) + (rr_ ^ ((g >> 1) << 3)); };
+  // this decode lane's two tile entries (integer form): groups g0, g0 + 1 of
+  // K half f_own in row block rb, as LDS pointers into the clean tile of
+  // slot 0 (the sparse tile and slot 1 are fixed offsets from them, small
+  // enough for the instruction's immediate)
+  const int ent0 = (rb * 2 + f_own) * 1024 + 16 * tile_entry(g0, rr, f_own);
+  const int ent1 = (rb * 2 + f_own) * 1024 + 16 * tile_entry(g0 + 1, rr, f_own);
+  // (LDS-typed, so the stores stay ds_write: a generic pointer would become
+  // a flat store, which also makes every LDS wait a full drain)
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+  typedef uint32_t lds_v4u_t __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) lds_v4u_t lds_v4u;
+  lds_u8* wb0 = (lds_u8*)(smem + kOffL + ent0);
+  lds_u8* wb1 = (lds_u8*)(smem + kOffL + ent1);
+  asm volatile("" : "+v"(wb0), "+v"(wb1));
 
   // decode stage s: raw W and value window from LDS -> clean low tile and
   // sparse tile of buffer s % 2; advances vi
-  auto decode = [&](int s) {
-    const uint4 rw = *(const uint4*)(smem + kOffW + (s & 1) * kStW + r * 64 + qq * 16);
+  // (par: the stage's ring slot as a compile-time constant, so that every
+  // LDS address is a per-lane base plus an immediate)
+  auto decode = [&](auto par) {
+    constexpr int b = decltype(par)::value;
+    const uint4 rw = *(const uint4*)(smem + kOffW + b * kStW + r * 64 + qq * 16);
     uint32_t wd[4], mk[4];
     int cnt = 0;
     {
@@ -239,40 +282,43 @@ __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
     if constexpr (FP) {
       // lane-order entries of the 16-row block rb: (row rr, slot group qq)
       // at fpos (swizzled so the 16 lanes of a row quad hit distinct banks)
-      *(uint4*)(smem + kOffL + (s & 1) * kStL + rb * 1024 + fpos_w * 16) =
+      *(uint4*)(smem + kOffL + b * kStL + rb * 1024 + fpos_w * 16) =
           make_uint4(wd[0], wd[1], wd[2], wd[3]);
-      sblk = smem + kOffS + (s & 1) * kStS + rb * 2048;
+      sblk = smem + kOffS + b * kStS + rb * 2048;
     } else {
-      uint2* sL = (uint2*)(smem + kOffL + (s & 1) * kStL) + (rb * 2 + f_own) * 64;
-#pragma unroll
-      for (int e = 0; e < 2; ++e) sL[lpos(g0 + e, rr, f_own)] = make_uint2(wd[2 * e], wd[2 * e + 1]);
-      sblk = smem + kOffS + (s & 1) * kStS + (rb * 2 + f_own) * 1024;
+      // int8 16*code, slot order: 16 bytes per entry, one store each
+      const uint2 c0 = widen8(wd[0]), c1 = widen8(wd[1]), c2 = widen8(wd[2]), c3 = widen8(wd[3]);
+      *(lds_v4u*)(wb0 + b * kStL) = lds_v4u_t{c0.x, c0.y, c1.x, c1.y};
+      *(lds_v4u*)(wb1 + b * kStL) = lds_v4u_t{c2.x, c2.y, c3.x, c3.y};
+      sblk = smem + kOffS + b * kStS;
     }
-    // marks of the row's earlier lanes precede this lane's
+    // marks of the row's earlier lanes precede this lane's: an inclusive scan
+    // over the row's four lanes with DPP row shifts (no LDS round trip)
     int incl = cnt;
     {
-      const int c1 = __shfl_up(incl, 1, 4);
+      const int c1 = __builtin_amdgcn_update_dpp(0, incl, 0x111, 0xF, 0xF, true);  // row_shr:1
       if (qq >= 1) incl += c1;
-      const int c2 = __shfl_up(incl, 2, 4);
+      const int c2 = __builtin_amdgcn_update_dpp(0, incl, 0x112, 0xF, 0xF, true);  // row_shr:2
       if (qq >= 2) incl += c2;
     }
-    const int tot = __shfl(incl, 3, 4);
+    const int tot = __builtin_amdgcn_update_dpp(0, incl, 0xFF, 0xF, 0xF, true);  // quad_perm [3,3,3,3]
     const int v0 = vi + incl - cnt;  // value index of this lane's first mark
     const int64_t a0 = (int64_t)gn * nnz + vi;
     const int64_t win_lo = a0 & ~(int64_t)15;  // the window the DMA brought
     const int64_t room = vtotal - win_lo;
-    const int win_valid = !vdma ? 0 : room >= 64 ? 64 : (int)room & ~15;
+    const int win_valid = !vdma ? 0 : room >= kVRow ? kVRow : (int)room & ~15;
     const int wo0 = (int)(a0 - win_lo) + (v0 - vi);  // offset of this lane's first value
     {
-      const uint8_t* vw = smem + kOffV + (s & 1) * kStV + r * 64;
+      const uint8_t* vw = smem + kOffV + b * kStV + r * kVRow;
       auto vdw = [&](int o) { return *(const uint32_t*)(vw + o); };
       int pre = 0;
+      uint2 sp[4];  // integer form: the four groups' sparse bytes, stored in pairs
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         // byte offset of the group's first value; past the row's window the
         // bytes are not used (those lanes take the path below), so the read
         // only has to stay inside LDS
-        const int off = min(wo0 + pre, 64);
+        const int off = min(wo0 + pre, kVRow);
         const int o4 = off & ~3;
         const uint32_t d0 = vdw(o4), d1 = vdw(o4 + 4), d2 = vdw(o4 + 8);
         const uint32_t lo = __builtin_amdgcn_alignbyte(d1, d0, off & 3);
@@ -285,9 +331,12 @@ __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
         if constexpr (FP)
           *(uint2*)(sblk + sp_off(d)) = make_uint2(perm(hi, lo, sl.x), perm(hi, lo, sl.y));
         else
-          *(uint2*)(sblk + spos(g0 + (d >> 1), rr) * 16 + ((d & 1) ^ f_own) * 8) =
-              make_uint2(perm(hi, lo, sl.x), perm(hi, lo, sl.y));
+          sp[d] = make_uint2(perm(hi, lo, sl.x), perm(hi, lo, sl.y));
         pre += __builtin_popcount(mk[d]);
+      }
+      if constexpr (!FP) {
+        *(lds_v4u*)(wb0 + (kOffS - kOffL) + b * kStS) = lds_v4u_t{sp[0].x, sp[0].y, sp[1].x, sp[1].y};
+        *(lds_v4u*)(wb1 + (kOffS - kOffL) + b * kStS) = lds_v4u_t{sp[2].x, sp[2].y, sp[3].x, sp[3].y};
       }
     }
     // rare: values beyond the window (or more marks than values) -> one by one
@@ -303,7 +352,7 @@ __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
           if constexpr (FP)
             sblk[sp_off(k >> 3) + (k & 7)] = (uint8_t)v;
           else
-            sblk[spos(g0 + (k >> 4), rr) * 16 + (perm_pos(k & 15) ^ (f_own * 8))] = (uint8_t)v;
+            sblk[(k < 16 ? ent0 : ent1) + (k & 15)] = (uint8_t)v;
           ++j;
         }
       }
@@ -336,17 +385,25 @@ __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
     rdf[h] = (uint32_t)((R >> 3) * 1024 + (R & 7) * 128 + 16 * (C ^ pair_swz(R >> 3, R & 7)));
   }
   const int fpos_r = ((lane >> 4) << 4) + ((lane & 15) ^ ((lane >> 4) << 2));
+  // integer form: this lane's entry in the decoded-tile blocks of its wave's
+  // columns for K half f (clean tile, slot 0; the sparse tile and slot 1 at
+  // immediate offsets), and its A fragment base for K half f
+  const uint8_t* rlb[2] = {smem + kOffL + wn * TN * 2048 + 16 * tile_entry(lane >> 4, lane & 15, 0),
+                           smem + kOffL + wn * TN * 2048 + 1024 + 16 * tile_entry(lane >> 4, lane & 15, 1)};
+  const uint8_t* rab[2] = {smem + kOffA + wm * TM * 2048 + rd_off[0], smem + kOffA + wm * TM * 2048 + rd_off[1]};
+
   auto ld_a8 = [&](const uint8_t* blk) {
     const v4i lo = *(const v4i*)(blk + rdf[0]), hi = *(const v4i*)(blk + rdf[1]);
     return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
   };
 
   // MFMAs of stage s: low and sparse tiles on the same A
-  auto mfma_stage = [&](int s) {
+  auto mfma_stage = [&](auto par) {
+    constexpr int b = decltype(par)::value;
     if constexpr (FP) {
-      const uint8_t* abuf = smem + kOffA + (s & 1) * kStA;
-      const uint8_t* cb = smem + kOffL + (s & 1) * kStL;
-      const uint8_t* sb = smem + kOffS + (s & 1) * kStS;
+      const uint8_t* abuf = smem + kOffA + b * kStA;
+      const uint8_t* cb = smem + kOffL + b * kStL;
+      const uint8_t* sb = smem + kOffS + b * kStS;
       v8i a[TM];
 #pragma unroll
       for (int i = 0; i < TM; ++i) a[i] = ld_a8(abuf + (wm * TM + i) * 2048);
@@ -365,40 +422,47 @@ __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
         }
       }
     } else {
-    const uint8_t* abuf = smem + kOffA + (s & 1) * kStA;
-    const uint2* sL = (const uint2*)(smem + kOffL + (s & 1) * kStL);
-    const uint4* sS = (const uint4*)(smem + kOffS + (s & 1) * kStS);
+      // both decoded tiles and the activations are int8 in slot order: LDS
+      // reads (per-lane base + immediate) and MFMAs only.  Eight groups (K
+      // half f, column block j) of eight MFMAs; the B fragments of the next
+      // group and the A fragments of the next K half are read while the
+      // current group multiplies, so no group waits for its own reads.
+      v4i a[2][TM], bl[2], bs[2];
+      auto ld_b = [&](int g, int slot) {
+        const int f = g >> 2, j = g & 3;
+        bl[slot] = *(const v4i*)(rlb[f] + b * kStL + j * 2048);
+        bs[slot] = *(const v4i*)(rlb[f] + (kOffS - kOffL) + b * kStS + j * 2048);
+      };
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {
-      v4i a[TM];
+      for (int i = 0; i < TM; ++i) a[0][i] = *(const v4i*)(rab[0] + b * kStA + i * 2048);
+      ld_b(0, 0);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) a[i] = to_widened(*(const v4i*)(abuf + (wm * TM + i) * 2048 + rd_off[f]));
+      for (int g = 0; g < 8; ++g) {
+        const int f = g >> 2, j = g & 3;
+        if (g + 1 < 8) ld_b(g + 1, (g + 1) & 1);
+        if (g == 1) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int blk = ((wn * TN + j) * 2 + f) * 64;
-        const uint2 x = sL[blk + lpos(lane >> 4, lane & 15, f)];
-        const v4i bl = v4i{(int)((x.x << 4) & 0xF0F0F0F0u), (int)(x.x & 0xF0F0F0F0u),
-                           (int)((x.y << 4) & 0xF0F0F0F0u), (int)(x.y & 0xF0F0F0F0u)};
-        v4i bs = __builtin_bit_cast(v4i, sS[blk + spos(lane >> 4, lane & 15)]);
-        if (f == 1) bs = v4i{bs.z, bs.w, bs.x, bs.y};
+          for (int i = 0; i < TM; ++i) a[1][i] = *(const v4i*)(rab[1] + b * kStA + i * 2048);
+        }
+        // the reads above stay above this group's MFMAs
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], bl, acc[i][j], 0, 0, 0);
-          acs[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], bs, acs[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[f][i], bl[g & 1], acc[i][j], 0, 0, 0);
+          acs[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[f][i], bs[g & 1], acs[i][j], 0, 0, 0);
         }
       }
-    }
     }
   };
 
 
   // ---- int8 branch (outlier channels), 128 bytes per row per stage ----
   // Branch stage t takes the A buffer (nst + t) % 2 and, for its W rows (16-row
-  // blocks swizzled like A), the raw W ring (t even) or the value ring (t odd):
-  // stages 0 and 1 load while the last low stages compute.  Both operands are
-  // in natural slot order.
+  // blocks swizzled like A), the raw W ring (t even) or the clean-tile ring
+  // (t odd): stages 0 and 1 load while the last low stages compute.  Both
+  // operands are in natural slot order.
   auto br_a = [&](int t) { return kOffA + ((nst + t) & 1) * kStA; };
-  auto br_w = [&](int t) { return (t & 1) ? kOffV : kOffW; };
+  auto br_w = [&](int t) { return (t & 1) ? kOffL : kOffW; };
   // (lane offsets formed here: they are needed at most a few times)
   auto issue_branch = [&](int t) {
     const int rl = lane >> 3;
@@ -428,7 +492,7 @@ __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
     issue_v(0);
     wait_vmcnt<0>();
     sq_sync();  // selector table, A 0, W 0 and 1, values 0
-    decode(0);
+    decode(std::integral_constant<int, 0>{});
     if (nst > 1) issue_v(1);
     wait_vmcnt<0>();
     sq_sync();  // decoded stage 0, values 1; W 0 is free
@@ -438,18 +502,29 @@ __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
   }
   // Iteration s: decode s+1 and the MFMAs of s; one barrier; then the DMAs of
   // A s+2 (into the buffer of A s) and W s+3 (into the buffer of W s+1).
-  for (int s = 0; s < nst; ++s) {
+  // Unrolled by two, so that each iteration knows its ring slots.  The values
+  // of s+2 are fetched right after the decode of s+1 (for s + 2 == nst: a
+  // window nobody reads, into a free slot).  (Measured: having half the
+  // waves multiply first, so the two waves of a SIMD alternate decode and
+  // matrix work, is slower -- the decode's LDS chains then queue behind the
+  // other wave's fragment reads.)
+  auto iteration = [&](int s, auto par) {
+    constexpr int b = decltype(par)::value;
     if (s + 1 < nst) {
-      decode(s + 1);
-      if (s + 2 < nst) issue_v(s + 2);
+      decode(std::integral_constant<int, 1 - b>{});
+      issue_v(s + 2);
     }
-    mfma_stage(s);
+    mfma_stage(par);
     // A s+1, W s+2 (issued one iteration ago) and values s+2 have landed
     wait_vmcnt<0>();
     sq_sync();
     if (s + 2 < nst) issue_a(s + 2);
     else if (s + 2 - nst < p.s_out) issue_branch(s + 2 - nst);
     if (s + 3 < nst) issue_w(s + 3);
+  };
+  for (int s = 0; s < nst; s += 2) {
+    iteration(s, std::integral_constant<int, 0>{});
+    if (s + 1 < nst) iteration(s + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- low + masked parts -> fp32 partial (the low accumulator is x16) ----
