@@ -469,29 +469,46 @@ __global__ __launch_bounds__(NT) void k_act_split(ActArgs p) {
         // code byte e = low byte of fl(fl(x_e * inv) + 1.5*2^23); the product
         // must be rounded on its own (a fused multiply-add would round the
         // exact product instead and differ at ties)
-        uint32_t y[8];
+        uint32_t d0, d1;  // the chunk's eight codes, one byte each, channel order
         if constexpr (LOW == kMXFP4) {
-          // E2M1 code of x / 2^X (exact scaling by a power of two), with the
-          // scale of the slot's block
+          // E2M1 code of x / 2^X, with the scale of the slot's block: the
+          // exact product by the power of two 2^-X, converted by the
+          // hardware (round to nearest even, saturating at 6 -- the same
+          // codes as e2m1_code at every rounding boundary, checked on this
+          // GPU), two channels per instruction; a zero code is then made
+          // unsigned (the hardware keeps the sign of a negative value that
+          // rounds to zero)
           const uint32_t b = (cw[i] >> 8) / 32u;
           const float f0 = mx_inv_scale(mx_scale_byte(bmax[b]));
           float f1 = f0;
           if ((~cw[i] & 0xFFu) & ~b0m[i]) f1 = mx_inv_scale(mx_scale_byte(bmax[b + 1]));
+          float t[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) y[e] = e2m1_code(val(raw, i, e), ((b0m[i] >> e) & 1u) ? f0 : f1);
-        } else if constexpr (LOW == kFP8) {
+          for (int e = 0; e < 8; ++e) t[e] = val(raw, i, e) * (((b0m[i] >> e) & 1u) ? f0 : f1);
+          uint32_t pk = 0;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) y[e] = e4m3_rne_sat(nval(i, e) * inv_lo);
+          for (int e = 0; e < 8; e += 2)
+            pk |= (__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, t[e], t[e + 1], 1.0f, 0) & 0xFFu) << (4 * e);
+          pk &= 0x77777777u | (((pk & 0x77777777u) + 0x77777777u) & 0x88888888u);
+          const uint32_t lo = pk & 0x0F0F0F0Fu, hi = (pk >> 4) & 0x0F0F0F0Fu;  // even / odd channels
+          d0 = perm(hi, lo, 0x05010400u);
+          d1 = perm(hi, lo, 0x07030602u);
         } else {
+          uint32_t y[8];
+          if constexpr (LOW == kFP8) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = e4m3_rne_sat(nval(i, e) * inv_lo);
+          } else {
 #pragma clang fp contract(off)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float prod = nval(i, e) * inv_lo;
-            y[e] = __float_as_uint(prod + kRoundMagic);
+            for (int e = 0; e < 8; ++e) {
+              const float prod = nval(i, e) * inv_lo;
+              y[e] = __float_as_uint(prod + kRoundMagic);
+            }
           }
+          d0 = perm(y[1], y[0], 0x0C0C0400u) | (perm(y[3], y[2], 0x0C0C0400u) << 16);
+          d1 = perm(y[5], y[4], 0x0C0C0400u) | (perm(y[7], y[6], 0x0C0C0400u) << 16);
         }
-        const uint32_t d0 = perm(y[1], y[0], 0x0C0C0400u) | (perm(y[3], y[2], 0x0C0C0400u) << 16);
-        const uint32_t d1 = perm(y[5], y[4], 0x0C0C0400u) | (perm(y[7], y[6], 0x0C0C0400u) << 16);
         // the low channels' codes, in order, then zero bytes
         const uint32_t q0 = perm(d1, d0, sel0[i]), q1 = perm(d1, d0, sel1[i]);
         const uint32_t before = cw[i] >> 8;
