@@ -169,6 +169,65 @@ def time_layers(torch, runs, stream, steps, warmup):
     return total_ms / steps, act.mean(0), gemm.mean(0)
 
 
+def measured_peaks():
+    """Matrix-unit rates measured on this GPU (TOP/s): eight independent MFMA
+    chains per wave, two waves per SIMD, one 512-thread block per CU, as the
+    dual GEMM runs (libsqf_bench.so, built beside libsqf.so)."""
+    import ctypes
+
+    path = os.path.join(ROOT, "outlier_split_mixed_amd", "libsqf_bench.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build with __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    lib.sqfb_mfma_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.POINTER(ctypes.c_double)]
+    out = {}
+    for name, kind in (("fp6", 0), ("fp4", 1), ("int8", 2), ("bf16", 3)):
+        v = ctypes.c_double()
+        rc = lib.sqfb_mfma_rate(kind, 256, 4096, 5, ctypes.byref(v))
+        if rc != 0:
+            raise RuntimeError(f"sqfb_mfma_rate({name}) failed: {rc}")
+        out[name] = round(v.value, 1)
+    return out
+
+
+def clone_run(r):
+    """A LayerRun over fresh device copies of every buffer it touches (same
+    contents, different memory)."""
+    import copy
+
+    c = copy.copy(r)
+    c.x = r.x.clone()
+    c.map = r.map.clone()
+    c.y = r.y.clone()
+    c.w = copy.copy(r.w)
+    c.w.t = {k: (v.clone() if v is not None else None) for k, v in r.w.t.items()}
+    c.acts = copy.copy(r.acts)
+    c.acts.t = {k: (v.clone() if v is not None else None) for k, v in r.acts.t.items()}
+    return c
+
+
+def time_rotated(torch, sets, stream, steps, warmup):
+    """Steps back to back over rotating buffer sets: step s runs set s % len(sets),
+    so each step's operands were last touched len(sets) - 1 steps earlier."""
+    n = len(sets)
+    for s in range(warmup):
+        for r in sets[s % n]:
+            r.step(stream)
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in sets[0]] for _ in range(steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for s in range(steps):
+        for i, r in enumerate(sets[s % n]):
+            r.step(stream, evs[s][i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    act = np.array([[e[0].elapsed_time(e[1]) for e in row] for row in evs])
+    gemm = np.array([[e[1].elapsed_time(e[2]) for e in row] for row in evs])
+    return t0.elapsed_time(t1) / steps, act, gemm
+
+
 def time_cold(torch, runs, stream, steps, flush_bytes=1 << 30):
     """Each step timed alone after overwriting a 1 GiB device buffer on the
     same stream, which evicts the L2s and the 256 MiB last-level cache: no
@@ -403,8 +462,8 @@ def rows_section(sqf, torch, stream):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the outlier-fraction sweep and the Llama-3-8B-shaped layers")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -436,6 +495,14 @@ def main():
     progress(f"step timed: {step_ms:.4f} ms")
     cold = time_cold(torch, runs, stream, max(5, args.steps // 2))
     progress(f"cold steps timed: median {np.median(cold):.4f} ms")
+    # four buffer sets in rotation (every buffer of a step: X, codes, weights, Y)
+    sets = [runs] + [[clone_run(r) for r in runs] for _ in range(3)]
+    set_bytes = sum(t.numel() * t.element_size() for r in runs
+                    for t in [r.x, r.y, *r.w.t.values(), *r.acts.t.values()] if t is not None)
+    rot_ms, rot_act, rot_gemm = time_rotated(torch, sets, stream, args.steps, args.warmup)
+    del sets
+    torch.cuda.empty_cache()
+    progress(f"rotated steps timed: {rot_ms:.4f} ms")
     total_ops = sum(r.ops for r in runs)
     value = total_ops / (step_ms * 1e-3) / 1e12
     gemm_ops = sum(r.ops for r in runs)
@@ -474,6 +541,7 @@ def main():
                   "gemm_top_s": round(gemm_ops / (gemm_b.sum() * 1e-3) / 1e12, 1)}
     progress("bf16-Y step timed")
     lays = [r.lay for r in runs]
+    lays_shapes = [(r.m, r.n, r.k, r.k_out) for r in runs]
     del runs
     torch.cuda.empty_cache()
     # the same step with the int4 codes packed two per byte (the int8 matrix
@@ -509,6 +577,11 @@ def main():
     torch.cuda.empty_cache()
     progress(f"MXFP4 step timed: {step_mx:.4f} ms")
     traffic = read_traffic()
+    meas = measured_peaks()
+    progress(f"measured matrix-unit rates: {meas}")
+    # the same kernel bound with the measured rates in place of the spec peaks
+    bound_meas_us = sum(2.0 * m * n * ((k - ko) / meas["fp6"] + ko / meas["bf16"]) / 1e6
+                        for m, n, k, ko in lays_shapes)
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -536,7 +609,9 @@ def main():
                                    "2.5 PFLOP/s bf16 peak, over the three launches",
                      "frac_int8_peak": round(achieved / PEAK_INT8_TOPS, 4),
                      "avg_launch_us": round(float(gemm_ms.mean()) * 1e3, 2),
-                     "ops_per_launch": gemm_ops / 3},
+                     "ops_per_launch": gemm_ops / 3,
+                     "measured_peaks_tops": meas,
+                     "frac_of_measured_bound": round(bound_meas_us / (float(gemm_ms.sum()) * 1e3), 4)},
         "detail": detail,
         "cold_step": {"protocol": "each step timed alone (HIP events on its stream) after a 1 GiB device "
                                   "buffer is overwritten on the same stream: L2s and the 256 MiB last-level "
@@ -544,6 +619,15 @@ def main():
                       "steps": int(cold.size),
                       "ms_p10_p50_p90": [round(float(np.percentile(cold, q)), 4) for q in (10, 50, 90)],
                       "tops_at_p50": round(total_ops / (float(np.median(cold)) * 1e-3) / 1e12, 2)},
+        "rotated_step": {"protocol": "steps back to back over 4 buffer sets in rotation (X, codes, packed "
+                                     "weights, Y: every buffer of a step), each set "
+                                     f"{set_bytes / 2**30:.2f} GiB, so a step's operands were last touched "
+                                     "3 steps (about 4.5 GiB of traffic) earlier, beyond the 256 MiB "
+                                     "last-level cache",
+                         "ms_per_step": round(rot_ms, 4),
+                         "tops": round(total_ops / (rot_ms * 1e-3) / 1e12, 2),
+                         "act_us_p50": [pct(rot_act[:, i] * 1e3, 50) for i in range(rot_act.shape[1])],
+                         "gemm_us_p50": [pct(rot_gemm[:, i] * 1e3, 50) for i in range(rot_gemm.shape[1])]},
         "bf16_y_step": bf16_y,
         "packed_int4_step": i4_step,
         "mxfp4_step": mx_step,

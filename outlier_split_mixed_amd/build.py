@@ -50,7 +50,26 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
+    build_bench(verbose)
     return LIB
+
+
+BENCH_LIB = os.path.join(HERE, "libsqf_bench.so")
+
+
+def build_bench(verbose: bool = False) -> str:
+    """libsqf_bench.so: the matrix-unit rate micro-benchmark bench.py reports
+    beside the spec peaks (measurement only; not part of the path's ABI)."""
+    srcs = sorted(glob.glob(os.path.join(HERE, "csrc_bench", "*.hip")))
+    tmp = BENCH_LIB + ".tmp"
+    cmd = [HIPCC, *FLAGS, "-shared", *srcs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {srcs}:\n{r.stderr}")
+    os.replace(tmp, BENCH_LIB)
+    if verbose:
+        print(f"built {BENCH_LIB}")
+    return BENCH_LIB
 
 
 SAN_LIB = os.path.join(BUILD, "libsqf_hostsan.so")
