@@ -585,6 +585,25 @@ def test_mxfp4_block_scales_over_a_wide_range(sqf):
     _print("mxfp4 wide", st)
 
 
+def test_mxfp4_codes_at_rounding_boundaries(sqf):
+    """Every rounding boundary of the E2M1 grid (exact ties go to the even
+    code, values one bf16 step either side go to the nearer one), saturation
+    at 6, and negative values that round to zero -- whose code must be the
+    unsigned zero: codes and scale bytes bit for bit against the oracle.
+    Each row repeats a 16-value pattern whose largest magnitude is 7.5, so
+    every 32-slot block has the scale exponent of its row's power of two."""
+    pattern = np.array([6.0, 0.25, -0.25, 0.75, -0.75, 1.25, -1.75, 2.5, -3.5, 5.0, -0.125,
+                        -0.2490234375, 0.2509765625, -6.0, 7.5, -0.0])
+    lay = _ragged(m=272, k=1024, n=256, n_scaled=16, seed=211)
+    r = np.arange(lay.m)[:, None]
+    c = np.arange(lay.k)[None, :]
+    x = pattern[(c + r) % 16] * np.exp2((r % 41) - 20.0)
+    lay2 = synth.Layer(name="e2m1 boundaries", m=lay.m, k=lay.k, n=lay.n, k_out=lay.k_out,
+                       x=x.astype(np.float32), x_cal=lay.x_cal, w=lay.w, scaled=lay.scaled)
+    st, _ = run_layer_mx(sqf, lay2, lay2.k_out, x_dtype="f32")
+    _print("mxfp4 boundaries", st)
+
+
 def test_mxfp4_bf16_output_and_errors(sqf):
     """bf16 Y is the nearest-even rounding of the fp32 Y; the MXFP4 path has
     one tile shape and no integer accumulators."""
