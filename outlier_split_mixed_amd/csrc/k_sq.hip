@@ -312,7 +312,7 @@ __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
       const uint8_t* vw = smem + kOffV + b * kStV + r * kVRow;
       auto vdw = [&](int o) { return *(const uint32_t*)(vw + o); };
       int pre = 0;
-      uint2 sp[4];  // integer form: the four groups' sparse bytes, stored in pairs
+      uint2 sp[4];  // the four groups' sparse bytes, stored in pairs
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         // byte offset of the group's first value; past the row's window the
@@ -328,13 +328,14 @@ __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
         const uint32_t t2 = ((mk[d] >> 3) | (mk[d] >> 6)) & 0x03030303u;
         const uint32_t x = __builtin_amdgcn_udot4(t2, 0x40100401u, 0u, false);
         const uint2 sl = sSel[x];
-        if constexpr (FP)
-          *(uint2*)(sblk + sp_off(d)) = make_uint2(perm(hi, lo, sl.x), perm(hi, lo, sl.y));
-        else
-          sp[d] = make_uint2(perm(hi, lo, sl.x), perm(hi, lo, sl.y));
+        sp[d] = make_uint2(perm(hi, lo, sl.x), perm(hi, lo, sl.y));
         pre += __builtin_popcount(mk[d]);
       }
-      if constexpr (!FP) {
+      if constexpr (FP) {
+        // groups 2e and 2e+1 are the two halves of one 16-byte FP8 slot run
+        *(uint4*)(sblk + sp_off(0)) = make_uint4(sp[0].x, sp[0].y, sp[1].x, sp[1].y);
+        *(uint4*)(sblk + sp_off(2)) = make_uint4(sp[2].x, sp[2].y, sp[3].x, sp[3].y);
+      } else {
         *(lds_v4u*)(wb0 + (kOffS - kOffL) + b * kStS) = lds_v4u_t{sp[0].x, sp[0].y, sp[1].x, sp[1].y};
         *(lds_v4u*)(wb1 + (kOffS - kOffL) + b * kStS) = lds_v4u_t{sp[2].x, sp[2].y, sp[3].x, sp[3].y};
       }
