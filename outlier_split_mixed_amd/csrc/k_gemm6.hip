@@ -53,14 +53,24 @@
 // slots (three of 48 KiB for E2M3, four of 34 KiB for MXFP4): low stages
 // (128 slots: A panel, B panel, MXFP4 also their scales), then branch stages (32 bf16 channels: 16 KiB + 16 KiB, rows 64 bytes with
 // their 16-byte chunks XOR-swizzled by row so the MFMA operand reads hit
-// distinct banks).  At the top of stage t every wave waits for its own DMAs
-// of stage t, crosses one barrier, and issues stage t+2 into the slot stage
-// t-1 used.  Blocks are mapped XCD-aware (each XCD a contiguous run of tiles,
-// rastered in groups of 8 tile rows).
+// distinct banks).  The two waves of a SIMD take turns: while one multiplies
+// a stage from registers, the other reads its next stage's fragments from
+// LDS and issues a later stage's DMAs (two phases per stage, each ended by a
+// workgroup barrier; the schedule is spelled out at the loop).  Blocks are
+// mapped XCD-aware (each XCD a contiguous run of tiles, rastered in groups of
+// 8 tile rows).
 #include "sqf_device.h"
 #include "sqf_launch.h"
 
 namespace sqf {
+
+typedef int v6i __attribute__((ext_vector_type(6)));
+
+// The FP6 overload of the scaled f8f6f4 MFMA: an FP6 operand is six
+// registers (the clang builtin only takes the eight-register FP8 tuple, which
+// would hold two dead registers per fragment).
+__device__ v4f mfma_fp6(v6i a, v6i b, v4f c, int cbsz, int blgp, int opsel_a, int scale_a, int opsel_b,
+                        int scale_b) __asm("llvm.amdgcn.mfma.scale.f32.16x16x128.f8f6f4.v6i32.v6i32");
 
 namespace {
 
@@ -74,6 +84,7 @@ constexpr int kStageWN = kTN * 16, kLDW = kStageWN + 4;         // epilogue stag
 constexpr int kStageBytes = kNW * 16 * kLDW * 4;                // 34816
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f_a4 __attribute__((ext_vector_type(4), aligned(4)));  // s_x is only float-aligned
 
 // Per low-format constants.
 template <int LF>
@@ -109,14 +120,14 @@ struct LowFmt<kMXFP4> {
 // limit of the stage.)
 __device__ __forceinline__ v8i ld_fp4(const uint8_t* p) {
   const v4i a = *(const v4i*)p;
-  return v8i{a.x, a.y, a.z, a.w, 0, 0, 0, 0};
+  return __builtin_shufflevector(a, a, 0, 1, 2, 3, -1, -1, -1, -1);
 }
-__device__ __forceinline__ void ld_fp6_pair(const uint8_t* pair, int lane, v8i& f0, v8i& f1) {
+__device__ __forceinline__ void ld_fp6_pair(const uint8_t* pair, int lane, v6i& f0, v6i& f1) {
   const v4i h0 = *(const v4i*)(pair + lane * 16);
   const v4i h1 = *(const v4i*)(pair + 1024 + lane * 16);
   const v4i t = *(const v4i*)(pair + 2048 + lane * 16);
-  f0 = v8i{h0.x, h0.y, h0.z, h0.w, t.x, t.y, 0, 0};
-  f1 = v8i{h1.x, h1.y, h1.z, h1.w, t.z, t.w, 0, 0};
+  f0 = __builtin_shufflevector(h0, t, 0, 1, 2, 3, 4, 5);
+  f1 = __builtin_shufflevector(h1, t, 0, 1, 2, 3, 6, 7);
 }
 
 // s_waitcnt vmcnt for a wave-uniform count n of DMAs still allowed in
@@ -282,80 +293,119 @@ __global__ __launch_bounds__(kNW * 64, 2) void k_gemm6(Gemm6Args p) {
   const uint32_t as_off = (uint32_t)(2 * F::kPanelB + wm * 2 * 256 + 4 * lane);
   const uint32_t bs_off = (uint32_t)(2 * F::kPanelB + 1024 + wn * 256 + 4 * lane);
 
+  // Two wave groups with one wave of every SIMD in each: waves 0-3 and 4-7
+  // (a workgroup's waves go to the SIMDs round-robin; read back from HW_ID
+  // on this chip).  Every stage is a load phase (the stage's fragments from
+  // LDS into registers, then this wave's DMAs of stage t+kRing-1) and a
+  // multiply phase (the stage's MFMAs from registers only), each ended by a
+  // workgroup barrier.  Group 1 runs one phase behind group 0, so on every
+  // SIMD one wave multiplies while the other loads.  Stage t is read in
+  // phases 2t (group 0) and 2t+1 (group 1), so its slot is free from phase
+  // 2t+2 on, where the load phase of stage t+1 refills it (with stage
+  // t+kRing).  At the end of phase 2t+1 (group 0 after multiplying, group 1
+  // after loading) every wave waits for its own DMAs of stage t+1, so the
+  // barrier there hands group 0 a landed stage in phase 2t+2.
+  const int grp = wave >> 2;
 #pragma unroll
   for (int d = 0; d < kRing - 1; ++d)
     if (d < ST) issue(d);
+  wait_dmas<LF>(ahead(0));
+  stage_barrier();
+  if (grp == 1) stage_barrier();
+
+  // End of a load phase: the fragments are in registers (and, for group 1,
+  // the slot is free).  The multiply phase runs at raised wave priority, so
+  // when both waves of a SIMD can issue, the MFMA goes first.
+  auto load_end = [&](int t) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    if (grp == 1) wait_dmas<LF>(ahead(t + 1));
+    __builtin_amdgcn_sched_barrier(0);
+    stage_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
+  };
+  auto mul_end = [&](int t) {
+    __builtin_amdgcn_s_setprio(0);
+    if (grp == 0) wait_dmas<LF>(ahead(t + 1));
+    __builtin_amdgcn_sched_barrier(0);
+    stage_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
   // ---------------- low path on the 6-/4-bit matrix unit ----------------
   for (int t = 0; t < S; ++t) {
-    wait_dmas<LF>(ahead(t));
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS reads are done
-    stage_barrier();
-    if (t + kRing - 1 < ST) issue(t + kRing - 1);
     const uint8_t* sl = smem + (t % kRing) * F::kSlot;
-    v8i B[kTN];
+    // E2M3 fragments are six registers, FP4 ones four (of an eight-register tuple)
+    typedef typename std::conditional<LF == kI4E2M3, v6i, v8i>::type frag_t;
+    frag_t A[kTM], B[kTN];
+    int sa0 = 0, sa1 = 0, sb = 0;
     if constexpr (LF == kI4E2M3) {
 #pragma unroll
       for (int j = 0; j < kTN; j += 2) ld_fp6_pair(sl + b_off + j * kFragB, lane, B[j], B[j + 1]);
+#pragma unroll
+      for (int i = 0; i < kTM; i += 2) ld_fp6_pair(sl + a_off + i * kFragB, lane, A[i], A[i + 1]);
     } else {
 #pragma unroll
       for (int j = 0; j < kTN; ++j) B[j] = ld_fp4(sl + b_off + j * kFragB + lane * 16);
-    }
-    int sa0 = 0, sa1 = 0, sb = 0;
-    if constexpr (LF == kMXFP4) {
+#pragma unroll
+      for (int i = 0; i < kTM; ++i) A[i] = ld_fp4(sl + a_off + i * kFragB + lane * 16);
       sa0 = *(const int*)(sl + as_off);
       sa1 = *(const int*)(sl + as_off + 256);
       sb = *(const int*)(sl + bs_off);
     }
-    v8i Anext;
+    if (t + kRing - 1 < ST) issue(t + kRing - 1);
+    load_end(t);
 #pragma unroll
-    for (int i = 0; i < kTM; ++i) {
-      v8i A;
-      if constexpr (LF == kI4E2M3) {
-        if (i % 2 == 0) ld_fp6_pair(sl + a_off + i * kFragB, lane, A, Anext);
-        else A = Anext;
-      } else {
-        A = ld_fp4(sl + a_off + i * kFragB + lane * 16);
-      }
-      // Wave priority: the two waves of a SIMD cross the same barrier and
-      // reach their MFMA runs together; raising it after the first fragment
-      // and dropping it before the last lets one issue back to back while
-      // the other reads LDS.
-      if (i == 1) __builtin_amdgcn_s_setprio(1);
-      if (i == kTM - 1) __builtin_amdgcn_s_setprio(0);
+    for (int i = 0; i < kTM; ++i)
 #pragma unroll
       for (int j = 0; j < kTN; ++j) {
         if constexpr (LF == kI4E2M3) {
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B[j], acc[i][j], 2, 2, 0, 0,
-                                                                        0, 0);
+          acc[i][j] = mfma_fp6(A[i], B[j], acc[i][j], 2, 2, 0, 0, 0, 0);
         } else {
           // opsel picks the fragment's byte of the scale dwords
-          acc[i][j] = mfma_fp4_sel(i & 3, j & 3, A, B[j], acc[i][j], i < 4 ? sa0 : sa1, sb);
+          acc[i][j] = mfma_fp4_sel(i & 3, j & 3, A[i], B[j], acc[i][j], i < 4 ? sa0 : sa1, sb);
         }
       }
-    }
+    mul_end(t);
   }
 
-  // Lane l holds rows 4*(l/16)+r (r < 4) and column l%16 of each fragment.
-  const int row0 = (int)m0 + wm * kTM * 16 + (lane >> 4) * 4;
-  const int col0 = (int)n0 + wn * kTN * 16 + (lane & 15);
   const int mrows = (int)p.m, ncols = (int)p.n;
   if constexpr (LF == kI4E2M3) {
     // ---------------- exact sums -> scaled fp32 ----------------
+    // Lane l holds rows 4*(l/16)+r (r < 4) and column l%16 of each fragment:
+    // one 16-byte read of s_x per fragment row (clamped reads at the edge).
+    // The indices are derived from an opaque copy of the lane id so that
+    // they die here instead of living through the branch loop.
+    int ls = lane;
+    asm volatile("" : "+v"(ls));
+    const int srow0 = (int)m0 + wm * kTM * 16 + (ls >> 4) * 4;
+    const int scol0 = (int)n0 + wn * kTN * 16 + (ls & 15);
+    float sw[kTN];
 #pragma unroll
     for (int j = 0; j < kTN; ++j) {
-      const int col = col0 + j * 16;
-      const float sw = p.s_w[col < ncols ? col : ncols - 1] * 64.0f;
+      const int col = scol0 + j * 16;
+      sw[j] = p.s_w[col < ncols ? col : ncols - 1] * 64.0f;
+    }
 #pragma unroll
-      for (int i = 0; i < kTM; ++i)
+    for (int i = 0; i < kTM; ++i) {
+      const int row = srow0 + i * 16;
+      v4f sx;
+      if (row + 3 < mrows) {
+        sx = *(const v4f_a4*)(p.s_x + row);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sx[r] = p.s_x[row + r < mrows ? row + r : mrows - 1];
+      }
+#pragma unroll
+      for (int j = 0; j < kTN; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int row = row0 + i * 16 + r;
           if constexpr (DEBUG) {
-            if (row < mrows && col < ncols)
-              p.acc_dbg[(int64_t)row * p.n + col] = (int32_t)(acc[i][j][r] * 64.0f);
+            const int col = scol0 + j * 16;
+            if (row + r < mrows && col < ncols)
+              p.acc_dbg[(int64_t)(row + r) * p.n + col] = (int32_t)(acc[i][j][r] * 64.0f);
           }
-          acc[i][j][r] *= p.s_x[row < mrows ? row : mrows - 1] * sw;
+          acc[i][j][r] *= sx[r] * sw[j];
         }
     }
   }
@@ -365,26 +415,28 @@ __global__ __launch_bounds__(kNW * 64, 2) void k_gemm6(Gemm6Args p) {
   const int bc = fg;
   auto br_off = [&](int r) { return (uint32_t)(r * kBrRowB + 16 * (bc ^ ((r >> 2) & 3))); };
   for (int t = S; t < ST; ++t) {
-    wait_dmas<LF>(ahead(t));
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    stage_barrier();
-    if (t + kRing - 1 < ST) issue(t + kRing - 1);
     const uint8_t* sl = smem + (t % kRing) * F::kSlot;
-    v4i B[kTN];
+    v4i A[kTM], B[kTN];
 #pragma unroll
     for (int j = 0; j < kTN; ++j)
       B[j] = *(const v4i*)(sl + kBM * kBrRowB + br_off(wn * kTN * 16 + j * 16 + fr));
 #pragma unroll
-    for (int i = 0; i < kTM; ++i) {
-      const v4i A = *(const v4i*)(sl + br_off(wm * kTM * 16 + i * 16 + fr));
+    for (int i = 0; i < kTM; ++i) A[i] = *(const v4i*)(sl + br_off(wm * kTM * 16 + i * 16 + fr));
+    if (t + kRing - 1 < ST) issue(t + kRing - 1);
+    load_end(t);
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
 #pragma unroll
       for (int j = 0; j < kTN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(v8bf, A), __builtin_bit_cast(v8bf, B[j]), acc[i][j], 0, 0, 0);
-    }
+            __builtin_bit_cast(v8bf, A[i]), __builtin_bit_cast(v8bf, B[j]), acc[i][j], 0, 0, 0);
+    mul_end(t);
   }
-
+  if (grp == 0) stage_barrier();
   // ---------------- store ----------------
+  // Lane l holds rows 4*(l/16)+r (r < 4) and column l%16 of each fragment.
+  const int row0 = (int)m0 + wm * kTM * 16 + (lane >> 4) * 4;
+  const int col0 = (int)n0 + wn * kTN * 16 + (lane & 15);
   const int wrow0 = (int)m0 + wm * kTM * 16, wcol0 = (int)n0 + wn * kTN * 16;
   constexpr int WN = kStageWN, LDW = kLDW;
   const bool whole = wrow0 + kTM * 16 <= mrows && wcol0 + WN <= ncols && (p.ldy & 3) == 0 &&
