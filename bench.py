@@ -426,6 +426,11 @@ def rows_section(sqf, torch, stream):
                 w, mp, branch="i8", hdiag=hd, sq_nnz=nnz, sq_bank=bank, stream=stream), iters=2, warmup=1)
             wt = sqf.sqf_pack_weights(w, mp, branch="i8", hdiag=hd, sq_nnz=nnz, sq_bank=bank, stream=stream)
             tg = time_call(torch, stream, lambda: sqf.sqf_dual_gemm(a, wt, y=y, stream=stream), iters=5)
+            # the same product with the gather done once per call into a
+            # workspace (decode kernel + GEMM on the decoded tiles, both timed)
+            ws = torch.empty(sqf.sqf_sq_workspace_bytes(wt), dtype=torch.uint8, device="cuda")
+            tw = time_call(torch, stream, lambda: sqf.sqf_dual_gemm_sq_ws(a, wt, y=y, workspace=ws,
+                                                                          stream=stream), iters=5)
             # the method's own work: every low slot, every marked value and
             # every branch channel once (2*M*N*(K_low + nnz + K_out) int8 operations)
             own_ops = 2.0 * lay.m * lay.n * (k_low + nnz + k_out)
@@ -439,8 +444,11 @@ def rows_section(sqf, torch, stream):
                             gemm_eff_tops=round(2.0 * lay.m * lay.n * lay.k / (tg * 1e-3) / 1e12, 1),
                             own_work_tops=round(own_ops / (tg * 1e-3) / 1e12, 1),
                             frac_int8_peak=round(own_ops / (tg * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
-                            issued_mfma_tops=round(mfma_ops / (tg * 1e-3) / 1e12, 1)))
-            del wt
+                            issued_mfma_tops=round(mfma_ops / (tg * 1e-3) / 1e12, 1),
+                            ws_call_us=round(tw * 1e3, 1),
+                            ws_workspace_mib=round(ws.numel() / 2**20, 1),
+                            ws_frac_int8_peak=round(own_ops / (tw * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4)))
+            del wt, ws
         # f4: the floating-point form (E2M1 low codes with the mark, E4M3
         # values, E4M3 activations and branch), one bank per row
         af = sqf.alloc_acts(lay.m, k_low, k_out, low="fp8", branch="fp8")
@@ -449,6 +457,9 @@ def rows_section(sqf, torch, stream):
             w, mp, branch="fp8", hdiag=hd, sq_nnz=nnz, low="fp4", stream=stream), iters=2, warmup=1)
         wt = sqf.sqf_pack_weights(w, mp, branch="fp8", hdiag=hd, sq_nnz=nnz, low="fp4", stream=stream)
         tg = time_call(torch, stream, lambda: sqf.sqf_dual_gemm(af, wt, y=y, stream=stream), iters=5)
+        ws = torch.empty(sqf.sqf_sq_workspace_bytes(wt), dtype=torch.uint8, device="cuda")
+        tw = time_call(torch, stream, lambda: sqf.sqf_dual_gemm_sq_ws(af, wt, y=y, workspace=ws,
+                                                                      stream=stream), iters=5)
         own_ops = 2.0 * lay.m * lay.n * (k_low + nnz + k_out)
         bits = (wt.t["w_low"].numel() * 8 + wt.t["sq_val"].numel() * 8) / (lay.n * sqf.sqf_pad_k_low(k_low))
         _add(out, dict(row="f4 SQ-format, FP8/FP4 (E2M1 low with the mark, E4M3 values, E4M3 acts and branch)",
@@ -457,8 +468,11 @@ def rows_section(sqf, torch, stream):
                         pack_ms=round(tp, 3), act_us=round(taf * 1e3, 1), gemm_us=round(tg * 1e3, 1),
                         gemm_eff_tops=round(2.0 * lay.m * lay.n * lay.k / (tg * 1e-3) / 1e12, 1),
                         own_work_tops=round(own_ops / (tg * 1e-3) / 1e12, 1),
-                        frac_fp8_peak=round(own_ops / (tg * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4)))
-        del wt, af
+                        frac_fp8_peak=round(own_ops / (tg * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
+                        ws_call_us=round(tw * 1e3, 1),
+                        ws_workspace_mib=round(ws.numel() / 2**20, 1),
+                        ws_frac_fp8_peak=round(own_ops / (tw * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4)))
+        del wt, af, ws
         del xt, a, y, w, x_cal
         torch.cuda.empty_cache()
     return out

@@ -91,7 +91,7 @@
 extern "C" {
 #endif
 
-#define SQF_ABI_VERSION 5
+#define SQF_ABI_VERSION 6
 
 typedef enum {
   SQF_OK = 0,
@@ -316,6 +316,27 @@ sqf_status sqf_rmsnorm_quantize_split_act(const void* x, int32_t x_dtype, int64_
 sqf_status sqf_dual_gemm(const sqf_acts* a, const sqf_weights* w, float* y, int64_t ldy,
                          int32_t* acc_low_dbg, int32_t* acc_sp_dbg, int32_t* acc_out_dbg,
                          void* stream);
+
+/* a7 with the gather done once per call ([SQF-art] 三 and 七: the gather
+ * unit feeds the sparse high-precision values to the matrix units; 九: the
+ * format).  The same product, accumulators and Y as sqf_dual_gemm on
+ * weight-side (sq_nnz > 0) weights, bit for bit in the integer form (the FP8 /
+ * FP4 form sums in fp32 the same way).  The decode of every 128-slot K stage
+ * of every 128-row weight tile -- the clean low tile and the sparse tile --
+ * is written once into `workspace` by a first kernel, and the GEMM then
+ * reads the decoded tiles instead of decoding each stage in every
+ * 256-row activation tile; for m above a few hundred rows this is the faster
+ * call.  workspace: device memory of at least sqf_sq_workspace_bytes(w)
+ * bytes, 256-byte aligned, owned by the caller, overwritten by the call and
+ * free again once the call's work on `stream` is done (calls that share a
+ * workspace must be ordered).  Errors: SQF_ERR_INVALID_ARG for weights
+ * without the weight-side format or a NULL workspace, SQF_ERR_ALIGN,
+ * SQF_ERR_SHAPE for a workspace that is too small; the rest as
+ * sqf_dual_gemm.  Asynchronous on `stream`. */
+int64_t sqf_sq_workspace_bytes(const sqf_weights* w); /* -1: not weight-side weights */
+sqf_status sqf_dual_gemm_sq_ws(const sqf_acts* a, const sqf_weights* w, float* y, int64_t ldy,
+                               void* workspace, int64_t workspace_bytes, int32_t* acc_low_dbg,
+                               int32_t* acc_sp_dbg, int32_t* acc_out_dbg, void* stream);
 
 /* Grouped (mixture-of-experts) variants ([OSC] abstract: evaluation on the
  * Qwen3 mixture-of-experts model, whose experts each see their own tokens;

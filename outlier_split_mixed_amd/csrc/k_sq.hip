@@ -114,6 +114,11 @@ struct SqLds {
   static constexpr int kSmem = kOffSel + 256 * 8;
 };
 static_assert(SqLds<false>::kSmem <= 160 * 1024 && SqLds<true>::kSmem <= 160 * 1024, "LDS budget");
+// A decoded stage image in the workspace: the clean tile, then the sparse
+// tile, each exactly as the fused decode leaves it in LDS (24 KiB in the FP
+// form, whose clean tile is E2M1 nibbles; 32 KiB in the integer form).
+template <bool FP>
+constexpr int kImgBytes = SqLds<FP>::kStL + kStS;
 // the branch's W tile (128 rows x 128 B, swizzled like A) reuses the raw W
 // ring (even branch stages) and the clean-tile ring (odd ones)
 static_assert(kBN * 128 <= 2 * kStW && kBN * 128 <= 2 * SqLds<true>::kStL, "branch W tile fits");
@@ -131,7 +136,7 @@ __device__ __forceinline__ int tile_entry(int g, int rr, int f) {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 
-template <bool DEBUG, bool FP>
+template <bool DEBUG, bool FP, bool PRE>
 __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
   static_assert(!(DEBUG && FP), "the floating-point form has no integer accumulators");
   using AccT = std::conditional_t<FP, v4f, v4i>;
@@ -232,7 +237,7 @@ __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
   // the pool {hi, lo} of the group's values) if slot p is marked, else zero
   // (selector 0x0C).
   uint2* sSel = (uint2*)(smem + kOffSel);
-  if (tid < 256) {
+  if (!PRE && tid < 256) {
     const int m = tid;
     uint32_t sel[2] = {0, 0};
 #pragma unroll
@@ -485,6 +490,59 @@ __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
     }
   };
 
+  // ---- PRE: the decoded tiles of each stage come from the call's
+  // workspace (k_sq_expand wrote them there), one contiguous image per
+  // (column tile, stage): the clean tile, then the sparse tile, each exactly
+  // as the decode above would leave it in LDS ----
+  constexpr int kImg = kImgBytes<FP>;
+  constexpr int kDmaD = kImg / 8192;  // 16-byte DMAs per thread per stage image
+  const uint8_t* dec_tile = PRE ? p.dec + (int64_t)tn * nst * kImg : p.x_low;
+  auto issue_d = [&](int s) {
+    const uint32_t voff = (uint32_t)s * (uint32_t)kImg + (uint32_t)tid * 16u;
+#pragma unroll
+    for (int i = 0; i < kDmaD; ++i) {
+      const uint32_t dst = i * 8192 < kStL
+                               ? sbase + kOffL + (uint32_t)((s & 1) * kStL + i * 8192)
+                               : sbase + kOffS + (uint32_t)((s & 1) * kStS + i * 8192 - kStL);
+      dma_16B(dec_tile, voff + (uint32_t)(i * 8192), dst + (uint32_t)(wave * 1024));
+    }
+  };
+
+  if constexpr (PRE) {
+    // prologue: stages 0 and 1 in flight, wait for stage 0 only
+    if (nst > 0) {
+      issue_a(0);
+      issue_d(0);
+      if (nst > 1) {
+        issue_a(1);
+        issue_d(1);
+        wait_vmcnt<4 + kDmaD>();
+      } else if (p.s_out > 0) {
+        issue_branch(0);
+        wait_vmcnt<6>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      sq_sync();
+    }
+    // Iteration s: the MFMAs of stage s; wait for stage s+1; one barrier;
+    // then stage s+2 (or the first branch stages) into the slots of stage s.
+    auto iteration = [&](int s, auto par) {
+      mfma_stage(par);
+      wait_vmcnt<0>();
+      sq_sync();
+      if (s + 2 < nst) {
+        issue_a(s + 2);
+        issue_d(s + 2);
+      } else if (s + 2 - nst < p.s_out) {
+        issue_branch(s + 2 - nst);
+      }
+    };
+    for (int s = 0; s < nst; s += 2) {
+      iteration(s, std::integral_constant<int, 0>{});
+      if (s + 1 < nst) iteration(s + 1, std::integral_constant<int, 1>{});
+    }
+  } else {
   // ---- prologue: stage 0 decoded, A 1 and W 2 in flight ----
   if (nst > 0) {
     issue_a(0);
@@ -527,6 +585,7 @@ __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
     iteration(s, std::integral_constant<int, 0>{});
     if (s + 1 < nst) iteration(s + 1, std::integral_constant<int, 1>{});
   }
+  }  // !PRE
 
   // ---- low + masked parts -> fp32 partial (the low accumulator is x16) ----
   // (the fp32 partial reuses the low accumulator's registers)
@@ -663,13 +722,169 @@ __global__ __launch_bounds__(512, 1) void k_sq_gemm(SqArgs p) {
   }
 }
 
+// The gather done once per call (sqf_dual_gemm_sq_ws): every (column tile,
+// 128-slot stage) of the weights is decoded into the workspace as the image
+// the fused kernel's decode leaves in LDS for that stage -- the clean tile,
+// then the sparse tile, same entry order -- so that k_sq_gemm<.., PRE> moves
+// it with plain DMAs, and the decode runs once per weight tile instead of
+// once per (row tile, weight tile).  A workgroup takes one 16-row block of a
+// column tile; its wave w decodes stage 16 t + w of step t for the 16 rows,
+// four lanes per row (the fused decode's lane map), so each store
+// instruction of a wave writes whole 256-byte runs of the image.  A row's
+// value index at a lane comes from a scan over its four lanes, the row's
+// counts of the earlier stages of the step (an LDS table) and the steps
+// before.  Rows past n are written as zeros.
+template <bool FP>
+__global__ __launch_bounds__(1024) void k_sq_expand(SqArgs p) {
+  constexpr int kStL = SqLds<FP>::kStL, kImg = kImgBytes<FP>;
+  __shared__ uint2 sSel[256];
+  __shared__ int sCnt[2][16][16];  // [step parity][wave = stage of the step][row]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid < 256) {
+    // the expand selectors of the fused kernel (one 8-slot group's mark mask)
+    const int m = tid;
+    uint32_t sel[2] = {0, 0};
+#pragma unroll
+    for (int pp = 0; pp < 8; ++pp) {
+      const uint32_t b = ((m >> pp) & 1) ? (uint32_t)__builtin_popcount(m & ((1 << pp) - 1)) : 0x0Cu;
+      sel[pp >> 2] |= b << (8 * (pp & 3));
+    }
+    sSel[m] = make_uint2(sel[0], sel[1]);
+  }
+  const int blk16 = blockIdx.x, tn = blk16 >> 3, rb = blk16 & 7;
+  const int rr = lane >> 2, qq = lane & 3;
+  const int64_t row = (int64_t)blk16 * 16 + rr;
+  const bool live = row < p.n;
+  const int nst = (int)(p.ldkw / 64), nnz = (int)p.nnz;
+  const uint8_t* wrow = p.w_low + (live ? row : 0) * p.ldkw;
+  const int64_t vrow = (live ? row : 0) * p.nnz;  // offset of the row's first value
+  const int64_t vtotal = p.n * p.nnz;
+  uint8_t* img_tile = p.dec + (int64_t)tn * nst * kImg;
+  int carry = 0;  // marks of the row in the steps before
+  for (int t = 0; t * 16 < nst; ++t) {
+    const int s = t * 16 + wave;
+    const bool act = s < nst;
+    uint4 rw = make_uint4(0u, 0u, 0u, 0u);
+    if (act && live) rw = *(const uint4*)(wrow + s * 64 + qq * 16);
+    uint32_t wd[4], mk[4];
+    int cnt = 0;
+    {
+      const uint32_t d4[4] = {rw.x, rw.y, rw.z, rw.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t x = d4[e];
+        const uint32_t nz = ((x & 0x77777777u) + 0x77777777u) & 0x88888888u;
+        const uint32_t m8 = x & 0x88888888u & ~nz;  // bit 3 of each marked nibble
+        mk[e] = m8;
+        wd[e] = x ^ m8;
+        cnt += __builtin_popcount(m8);
+      }
+    }
+    // marks of the row's earlier lanes in this stage (DPP scan over the quad)
+    int incl = cnt;
+    {
+      const int c1 = __builtin_amdgcn_update_dpp(0, incl, 0x111, 0xF, 0xF, true);  // row_shr:1
+      if (qq >= 1) incl += c1;
+      const int c2 = __builtin_amdgcn_update_dpp(0, incl, 0x112, 0xF, 0xF, true);  // row_shr:2
+      if (qq >= 2) incl += c2;
+    }
+    const int tot = __builtin_amdgcn_update_dpp(0, incl, 0xFF, 0xF, 0xF, true);  // quad_perm [3,3,3,3]
+    if (qq == 0) sCnt[t & 1][wave][rr] = tot;
+    __syncthreads();  // (also orders the selector table before its first use)
+    int before = 0, all = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < 16; ++w2) {
+      const int c = sCnt[t & 1][w2][rr];
+      before += w2 < wave ? c : 0;
+      all += c;
+    }
+    const int v0 = carry + before + incl - cnt;  // value index of this lane's first mark
+    carry += all;
+    uint2 sp[4];
+    if (v0 + cnt <= nnz && vrow + v0 + cnt + 12 <= vtotal) {
+      // three aligned dwords cover a group's (at most 8) values
+      int pre = 0;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const int64_t off = vrow + v0 + pre;
+        const uint32_t* q = (const uint32_t*)(p.sq_val + (off & ~(int64_t)3));
+        const uint32_t d0 = q[0], d1 = q[1], d2 = q[2];
+        const uint32_t lo = __builtin_amdgcn_alignbyte(d1, d0, (uint32_t)(off & 3));
+        const uint32_t hi = __builtin_amdgcn_alignbyte(d2, d1, (uint32_t)(off & 3));
+        const uint32_t t2 = ((mk[d] >> 3) | (mk[d] >> 6)) & 0x03030303u;
+        const uint32_t x = __builtin_amdgcn_udot4(t2, 0x40100401u, 0u, false);
+        const uint2 sl = sSel[x];
+        sp[d] = make_uint2(perm(hi, lo, sl.x), perm(hi, lo, sl.y));
+        pre += __builtin_popcount(mk[d]);
+      }
+    } else {
+      // near the end of the value buffer, or more marks than values (those
+      // take 0): one value at a time
+      int j = 0;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        uint32_t w2[2] = {0u, 0u};
+#pragma unroll
+        for (int pp = 0; pp < 8; ++pp) {
+          if ((mk[d] >> (4 * pp + 3)) & 1u) {
+            const uint32_t v = v0 + j < nnz ? (uint8_t)p.sq_val[vrow + v0 + j] : 0u;
+            w2[pp >> 2] |= v << (8 * (pp & 3));
+            ++j;
+          }
+        }
+        sp[d] = make_uint2(w2[0], w2[1]);
+      }
+    }
+    if (act) {
+      uint8_t* img = img_tile + (int64_t)s * kImg;
+      if constexpr (FP) {
+        const int fpos = (qq << 4) + (rr ^ (qq << 2));
+        *(uint4*)(img + rb * 1024 + fpos * 16) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+        auto sp_off = [&](int d) {
+          const int g = 2 * (qq & 1) + (d >> 1);
+          return ((g << 4) + (rr ^ (g << 2))) * 32 + 16 * (qq >> 1) + 8 * (d & 1);
+        };
+        uint8_t* sblk = img + kStL + rb * 2048;
+        *(uint4*)(sblk + sp_off(0)) = make_uint4(sp[0].x, sp[0].y, sp[1].x, sp[1].y);
+        *(uint4*)(sblk + sp_off(2)) = make_uint4(sp[2].x, sp[2].y, sp[3].x, sp[3].y);
+      } else {
+        const int f = qq >> 1, g0 = 2 * (qq & 1);
+        const int e0 = (rb * 2 + f) * 1024 + 16 * tile_entry(g0, rr, f);
+        const int e1 = (rb * 2 + f) * 1024 + 16 * tile_entry(g0 + 1, rr, f);
+        const uint2 c0w = widen8(wd[0]), c1w = widen8(wd[1]), c2w = widen8(wd[2]), c3w = widen8(wd[3]);
+        *(uint4*)(img + e0) = make_uint4(c0w.x, c0w.y, c1w.x, c1w.y);
+        *(uint4*)(img + e1) = make_uint4(c2w.x, c2w.y, c3w.x, c3w.y);
+        *(uint4*)(img + kStL + e0) = make_uint4(sp[0].x, sp[0].y, sp[1].x, sp[1].y);
+        *(uint4*)(img + kStL + e1) = make_uint4(sp[2].x, sp[2].y, sp[3].x, sp[3].y);
+      }
+    }
+  }
+}
+
+int64_t sq_image_bytes(int64_t n, int64_t ldkw, bool fp) {
+  return (n + kBN - 1) / kBN * (ldkw / 64) * (fp ? kImgBytes<true> : kImgBytes<false>);
+}
+
 hipError_t launch_sq_gemm(const SqArgs& a, bool debug, bool fp, hipStream_t s) {
   const int64_t blocks = ((a.m + kBM - 1) / kBM) * ((a.n + kBN - 1) / kBN);
   if (blocks <= 0) return hipSuccess;
   if (fp && debug) return hipErrorInvalidValue;
-  if (fp) hipLaunchKernelGGL((k_sq_gemm<false, true>), dim3((unsigned)blocks), dim3(512), 0, s, a);
-  else if (debug) hipLaunchKernelGGL((k_sq_gemm<true, false>), dim3((unsigned)blocks), dim3(512), 0, s, a);
-  else hipLaunchKernelGGL((k_sq_gemm<false, false>), dim3((unsigned)blocks), dim3(512), 0, s, a);
+  const dim3 g((unsigned)blocks), b(512);
+  if (a.dec) {
+    // the gather into the workspace, then the GEMM on the decoded images
+    const dim3 ge((unsigned)(((a.n + kBN - 1) / kBN) * (kBN / 16)));
+    if (fp) hipLaunchKernelGGL((k_sq_expand<true>), ge, dim3(1024), 0, s, a);
+    else hipLaunchKernelGGL((k_sq_expand<false>), ge, dim3(1024), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (fp) hipLaunchKernelGGL((k_sq_gemm<false, true, true>), g, b, 0, s, a);
+    else if (debug) hipLaunchKernelGGL((k_sq_gemm<true, false, true>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((k_sq_gemm<false, false, true>), g, b, 0, s, a);
+    return hipGetLastError();
+  }
+  if (fp) hipLaunchKernelGGL((k_sq_gemm<false, true, false>), g, b, 0, s, a);
+  else if (debug) hipLaunchKernelGGL((k_sq_gemm<true, false, false>), g, b, 0, s, a);
+  else hipLaunchKernelGGL((k_sq_gemm<false, false, false>), g, b, 0, s, a);
   return hipGetLastError();
 }
 

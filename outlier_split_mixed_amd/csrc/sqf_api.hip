@@ -293,9 +293,21 @@ sqf_status check_pair(const sqf_acts* a, const sqf_weights* w, const void* y, in
 // elements of Y's type.
 sqf_status dual_gemm_impl(const sqf_acts* a, const sqf_weights* w, void* y, bool ybf16,
                           int64_t ldy, int32_t tile, int32_t* acc_low_dbg, int32_t* acc_sp_dbg,
-                          int32_t* acc_out_dbg, void* stream, const char* who) {
+                          int32_t* acc_out_dbg, void* stream, const char* who,
+                          void* ws = nullptr, int64_t ws_bytes = 0, bool ws_call = false) {
   sqf_status st = check_pair(a, w, y, ldy, who);
   if (st != SQF_OK) return st;
+  if (ws_call) {
+    if (w->sq_nnz <= 0)
+      return fail(SQF_ERR_INVALID_ARG, "%s: the workspace call is for the weight-side format", who);
+    const int64_t need = sqf::sq_image_bytes(w->n, w->ldk, w->low == SQF_FP4_E2M1);
+    if (!ws) return fail(SQF_ERR_INVALID_ARG, "%s: workspace is NULL", who);
+    if ((((uintptr_t)ws) & 255) != 0)
+      return fail(SQF_ERR_ALIGN, "%s: workspace must be 256-byte aligned", who);
+    if (ws_bytes < need)
+      return fail(SQF_ERR_SHAPE, "%s: workspace of %lld bytes, %lld needed", who, (long long)ws_bytes,
+                  (long long)need);
+  }
   if (!tile_ok(tile)) return fail(SQF_ERR_INVALID_ARG, "%s: bad tile %d", who, tile);
   if (ybf16 && (acc_low_dbg || acc_sp_dbg || acc_out_dbg))
     return fail(SQF_ERR_INVALID_ARG, "%s: debug outputs need fp32 Y", who);
@@ -321,7 +333,8 @@ sqf_status dual_gemm_impl(const sqf_acts* a, const sqf_weights* w, void* y, bool
     sqf::SqArgs sa{a->x_low, a->s_x, (const uint8_t*)a->x_out, a->s_xo, w->w_low, w->s_w,
                    w->sq_val, w->s_w8, (const uint8_t*)w->w_out, w->s_wo, (float*)y,
                    acc_low_dbg, acc_sp_dbg, acc_out_dbg, a->m, w->n, a->ldk, w->ldk, w->ldo, ldy,
-                   w->sq_nnz, (int32_t)(w->ldk / 128), (int32_t)(w->ldo / 128)};
+                   w->sq_nnz, (int32_t)(w->ldk / 128), (int32_t)(w->ldo / 128),
+                   ws_call ? (uint8_t*)ws : nullptr};
     return hip_status(sqf::launch_sq_gemm(sa, debug, fp, (hipStream_t)stream), who);
   }
   if (acc_sp_dbg || acc_out_dbg)
@@ -568,6 +581,18 @@ sqf_status sqf_dual_gemm(const sqf_acts* a, const sqf_weights* w, float* y, int6
   g_err.clear();
   return dual_gemm_impl(a, w, y, false, ldy, SQF_TILE_AUTO, acc_low_dbg, acc_sp_dbg, acc_out_dbg,
                         stream, "sqf_dual_gemm");
+}
+
+int64_t sqf_sq_workspace_bytes(const sqf_weights* w) {
+  if (!w || w->sq_nnz <= 0 || w->n < 1 || w->ldk < 0 || w->ldk % 64 != 0) return -1;
+  return sqf::sq_image_bytes(w->n, w->ldk, w->low == SQF_FP4_E2M1);
+}
+
+sqf_status sqf_dual_gemm_sq_ws(const sqf_acts* a, const sqf_weights* w, float* y, int64_t ldy,
+                               void* workspace, int64_t workspace_bytes, int32_t* acc_low_dbg,
+                               int32_t* acc_sp_dbg, int32_t* acc_out_dbg, void* stream) {
+  return dual_gemm_impl(a, w, y, false, ldy, SQF_TILE_AUTO, acc_low_dbg, acc_sp_dbg, acc_out_dbg,
+                        stream, "sqf_dual_gemm_sq_ws", workspace, workspace_bytes, true);
 }
 
 sqf_status sqf_dual_gemm_y(const sqf_acts* a, const sqf_weights* w, void* y, int32_t y_dtype,

@@ -73,6 +73,10 @@ struct SqArgs {
   int32_t* dbg_o;
   int64_t m, n, ldkx, ldkw, ldo, ldy, nnz;
   int32_t s_low, s_out;
+  // NULL: the GEMM decodes each stage itself; else the call's workspace of
+  // sq_image_bytes(n, ldkw, fp) bytes, which the decode fills first (once
+  // per call) and the GEMM then reads
+  uint8_t* dec;
 };
 
 // The dual GEMM with int4 codes in 6-bit E2M3 fields (K-blocked) and a bf16
@@ -107,6 +111,9 @@ size_t act_split_lds_bytes(int64_t ldk, int64_t k_out, int low, int64_t norm_k);
 hipError_t launch_dual_gemm(const GemmArgs& a, int branch, bool grouped, bool debug, int cfg,
                             hipStream_t s, bool ybf16);
 hipError_t launch_sq_gemm(const SqArgs& a, bool debug, bool fp, hipStream_t s);
+// Workspace bytes of the decoded stage images of an n-row weight-side operand
+// with ldkw bytes per row.
+int64_t sq_image_bytes(int64_t n, int64_t ldkw, bool fp);
 // low: kI4E2M3 (int4 codes as E2M3 subnormals, exact sums; debug dumps them)
 // or kMXFP4 (E2M1 with E8M0 block scales; no debug output)
 hipError_t launch_gemm6(const Gemm6Args& a, int low, bool debug, bool ybf16, hipStream_t s);

@@ -32,7 +32,7 @@ SQF_F32, SQF_BF16, SQF_FP8_E4M3, SQF_I8, SQF_I4X2, SQF_I4_E2M3, SQF_MXFP4, SQF_F
 DTYPES = {"f32": SQF_F32, "bf16": SQF_BF16, "fp8": SQF_FP8_E4M3, "i8": SQF_I8, "i4": SQF_I4X2,
           "i4e2m3": SQF_I4_E2M3, "mxfp4": SQF_MXFP4, "fp4": SQF_FP4_E2M1}
 TILES = {"auto": -1, "256": 0, "128": 1, "64": 2}
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 P = ctypes.c_void_p
 I64 = ctypes.c_int64
@@ -73,6 +73,9 @@ _decl("sqf_rmsnorm_quantize_split_act", [P, I32, I64, P, ctypes.c_float, P, ctyp
 _decl("sqf_slot_order", [P, I64, P, P, P])
 _decl("sqf_permute_channels", [P, I64, I64, I64, P, I32, P, I64, P])
 _decl("sqf_dual_gemm", [ctypes.POINTER(sqf_acts), ctypes.POINTER(sqf_weights), P, I64, P, P, P, P])
+_decl("sqf_sq_workspace_bytes", [ctypes.POINTER(sqf_weights)], I64)
+_decl("sqf_dual_gemm_sq_ws", [ctypes.POINTER(sqf_acts), ctypes.POINTER(sqf_weights), P, I64, P, I64,
+                              P, P, P, P])
 _decl("sqf_dual_gemm_grouped", [ctypes.POINTER(sqf_acts), ctypes.POINTER(sqf_weights), I64, P, P,
                                 I64, P, P])
 _decl("sqf_dual_gemm_y", [ctypes.POINTER(sqf_acts), ctypes.POINTER(sqf_weights), P, I32, I64, P])
@@ -391,6 +394,31 @@ def sqf_dual_gemm(a: Acts, w: Weights, y: torch.Tensor | None = None, debug: boo
     else:
         _check(_lib.sqf_dual_gemm(ctypes.byref(da), ctypes.byref(dw), _ptr(y), y.stride(0),
                                   _ptr(dbg[0]), _ptr(dbg[1]), _ptr(dbg[2]), _stream(stream)))
+    return (y, *dbg) if debug else y
+
+
+def sqf_sq_workspace_bytes(w: Weights) -> int:
+    dw = w.desc()
+    return _lib.sqf_sq_workspace_bytes(ctypes.byref(dw))
+
+
+def sqf_dual_gemm_sq_ws(a: Acts, w: Weights, y: torch.Tensor | None = None,
+                        workspace: torch.Tensor | None = None, debug: bool = False, stream=None):
+    """a7 with the gather done once per call into ``workspace`` (a uint8
+    device tensor of at least sqf_sq_workspace_bytes(w) bytes; allocated here
+    when None).  Returns y [m][n] fp32, and the three int32 accumulators with
+    ``debug``."""
+    dev = a.t["x_out"].device
+    y = _y_out(a, w, y, "f32")
+    if workspace is None:
+        workspace = torch.empty(max(sqf_sq_workspace_bytes(w), 1), dtype=torch.uint8, device=dev)
+    dbg = [None, None, None]
+    if debug:
+        dbg = [torch.empty((a.m, w.n), dtype=torch.int32, device=dev) for _ in range(3)]
+    da, dw = a.desc(), w.desc()
+    _check(_lib.sqf_dual_gemm_sq_ws(ctypes.byref(da), ctypes.byref(dw), _ptr(y), y.stride(0),
+                                    _ptr(workspace), workspace.numel(), _ptr(dbg[0]), _ptr(dbg[1]),
+                                    _ptr(dbg[2]), _stream(stream)))
     return (y, *dbg) if debug else y
 
 

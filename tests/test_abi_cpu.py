@@ -26,13 +26,13 @@ def _declared_functions():
 
 def test_every_declared_symbol_is_exported(sqf):
     names = _declared_functions()
-    assert len(names) == 19
+    assert len(names) == 21
     for name in names:
         assert hasattr(sqf._lib, name), name
 
 
 def test_abi_version_and_padding(sqf):
-    assert sqf.sqf_abi_version() == 5
+    assert sqf.sqf_abi_version() == 6
     assert sqf.sqf_pad_rows(0) == 0 and sqf.sqf_pad_rows(1) == 256 and sqf.sqf_pad_rows(4096) == 4096
     assert sqf.sqf_pad_rows(300) == 512 and sqf._lib.sqf_pad_rows(-1) == -1
     assert sqf.sqf_pad_k_low(0) == 0 and sqf.sqf_pad_k_low(1) == 256
@@ -372,3 +372,50 @@ def test_no_entry_point_reads_the_environment():
     for fn in os.listdir(csrc):
         text = open(os.path.join(csrc, fn)).read()
         assert "getenv" not in text, fn
+
+
+def test_weight_side_workspace_contract(sqf):
+    """sqf_dual_gemm_sq_ws: the workspace holds one decoded image per (128-row
+    weight tile, 128-slot stage) -- 32 KiB in the integer form (int8 clean and
+    sparse tiles), 24 KiB in the FP8/FP4 form (E2M1 clean tile) -- and the
+    call refuses, before any launch, channel-split weights, a NULL, misaligned
+    or too small workspace."""
+    mem = FakeMem()
+
+    def wsq(k_low=480, n=300, fp=False):
+        w = _weights(sqf, mem, k=k_low + 32, n=n, k_out=32, branch="fp8" if fp else "bf16")
+        w.branch, w.ldo, w.s_wo = (sqf.SQF_FP8_E4M3 if fp else sqf.SQF_I8), 128, mem()
+        w.sq_nnz, w.sq_val, w.s_w8 = k_low // 8, mem(), mem()
+        if fp:
+            w.low = sqf.SQF_FP4_E2M1
+        return w
+
+    ws = lambda w: sqf._lib.sqf_sq_workspace_bytes(ctypes.byref(w))
+    # k_low 480 -> 512 padded slots = 4 stages; 300 rows -> 3 tiles
+    assert ws(wsq()) == 3 * 4 * 32768
+    assert ws(wsq(fp=True)) == 3 * 4 * 24576
+    assert ws(wsq(k_low=3840, n=14336)) == 112 * 30 * 32768
+    assert ws(_weights(sqf, mem)) == -1  # channel-split weights
+    assert sqf._lib.sqf_sq_workspace_bytes(None) == -1
+
+    a = _acts(sqf, mem, k=512, k_out=32, branch="i8", low="i8")
+    a.ldo = 128
+    a.s_xo = mem()
+
+    def call(w, wsp, nbytes):
+        return sqf._lib.sqf_dual_gemm_sq_ws(ctypes.byref(a), ctypes.byref(w), mem(), 300, wsp,
+                                            nbytes, None, None, None, None)
+
+    w = wsq()
+    need = ws(w)
+    assert call(w, None, need) == 1
+    assert "NULL" in sqf.sqf_last_error()
+    assert call(w, mem(misalign=16), need) == 5
+    big = ctypes.create_string_buffer(need + 512)
+    aligned = ctypes.c_void_p((ctypes.addressof(big) + 255) // 256 * 256)
+    assert call(w, aligned, need - 1) == 2
+    assert "needed" in sqf.sqf_last_error()
+    ab = _acts(sqf, mem, k=512, k_out=32)
+    st = sqf._lib.sqf_dual_gemm_sq_ws(ctypes.byref(ab), ctypes.byref(_weights(sqf, mem)), mem(), 256,
+                                      aligned, need, None, None, None, None)
+    assert st == 1 and "weight-side" in sqf.sqf_last_error()

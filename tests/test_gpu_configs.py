@@ -24,7 +24,7 @@ from outlier_split_mixed_amd import synth
 
 from harness import (assert_rows_close, f32_bits_equal, run_layer, run_layer_mx, sample_rows,
                      tile_band_rows, x_inputs)
-from test_gpu_parity import _grouped_check, _sqf_fp_check
+from test_gpu_parity import _grouped_check, _poisoned_workspace, _sq_ws_same, _sqf_fp_check
 
 pytestmark = pytest.mark.gpu
 
@@ -158,6 +158,16 @@ def test_sq_weight_side_full(sqf, bank):
     assert np.array_equal(ao.cpu().numpy()[rows].astype(np.int64), o_ao)
     assert_rows_close(y.cpu().numpy()[rows], o_y, "sq full")
     assert_rows_close(y_fast.cpu().numpy()[rows], o_y, "sq full (no debug outputs)")
+    # the gather once per call into a workspace: the sampled rows' accumulators
+    # against the oracle, and the whole Y bit for bit against the fused call
+    ws = _poisoned_workspace(sqf, wts)
+    y_ws, al_w, asp_w, ao_w = sqf.sqf_dual_gemm_sq_ws(acts, wts, workspace=ws, debug=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(al_w.cpu().numpy()[rows].astype(np.int64), o_al)
+    assert np.array_equal(asp_w.cpu().numpy()[rows].astype(np.int64), o_asp)
+    assert np.array_equal(ao_w.cpu().numpy()[rows].astype(np.int64), o_ao)
+    assert torch.equal(al_w, al) and torch.equal(asp_w, asp) and torch.equal(ao_w, ao)
+    _sq_ws_same(sqf, acts, wts, y_fast, "sq full", ws=ws)
     _log("sq full ok, bank", bank)
 
 

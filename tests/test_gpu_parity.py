@@ -332,6 +332,33 @@ def _sq_check(sqf, lay, nnz, label, bank=0):
     y_fast = sqf.sqf_dual_gemm(acts, wts)
     torch.cuda.synchronize()
     assert_rows_close(y_fast.cpu().numpy(), o_y, label + " (timed launch)")
+    # the gather once per call into a workspace: the oracle's accumulators,
+    # and Y bit-identical to the fused decode's
+    ws = _poisoned_workspace(sqf, wts)
+    y_ws, al_w, asp_w, ao_w = sqf.sqf_dual_gemm_sq_ws(acts, wts, workspace=ws, debug=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(al_w.cpu().numpy().astype(np.int64), o_al)
+    assert np.array_equal(asp_w.cpu().numpy().astype(np.int64), o_asp)
+    assert np.array_equal(ao_w.cpu().numpy().astype(np.int64), o_ao)
+    _sq_ws_same(sqf, acts, wts, y, label, ws=ws)
+
+
+def _poisoned_workspace(sqf, wts):
+    """A workspace of the required size filled with 0xA5, so that any byte
+    the GEMM reads and the gather did not write shows up in Y."""
+    nb = sqf.sqf_sq_workspace_bytes(wts)
+    assert nb > 0
+    return torch.full((nb,), 0xA5, dtype=torch.uint8, device="cuda")
+
+
+def _sq_ws_same(sqf, acts, wts, y_ref, label, ws=None):
+    """sqf_dual_gemm_sq_ws (timed form) gives the fused call's Y bit for bit,
+    on a poisoned workspace and again on the same workspace reused."""
+    ws = _poisoned_workspace(sqf, wts) if ws is None else ws
+    for i in range(2):
+        y_ws = sqf.sqf_dual_gemm_sq_ws(acts, wts, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(y_ws.view(torch.int32), y_ref.view(torch.int32)), f"{label}: workspace call {i}"
 
 
 def _moe_small(experts=6, tokens=96, topk=2, hidden=512, inter=256, seed=86):
@@ -687,7 +714,9 @@ def _sqf_fp_check(sqf, lay, nnz, label, bank=0, x_dtype="bf16", rows=None):
     if rows is None:
         rows = np.arange(lay.m, dtype=np.int64)
     o_y = oracle.dual_gemm_sqf(o_a, o_w, rows=rows)
-    return assert_rows_close(y.cpu().numpy()[rows], o_y, label)
+    st = assert_rows_close(y.cpu().numpy()[rows], o_y, label)
+    _sq_ws_same(sqf, acts, wts, y, label)
+    return st
 
 
 @pytest.mark.parametrize("x_dtype", ["bf16", "f32"])
