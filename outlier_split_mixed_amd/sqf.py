@@ -414,7 +414,7 @@ def sqf_dual_gemm_sq_ws(a: Acts, w: Weights, y: torch.Tensor | None = None,
         workspace = torch.empty(max(sqf_sq_workspace_bytes(w), 1), dtype=torch.uint8, device=dev)
     dbg = [None, None, None]
     if debug:
-        dbg = [torch.empty((a.m, w.n), dtype=torch.int32, device=dev) for _ in range(3)]
+        dbg = [torch.full((a.m, w.n), -1, dtype=torch.int32, device=dev) for _ in range(3)]
     da, dw = a.desc(), w.desc()
     _check(_lib.sqf_dual_gemm_sq_ws(ctypes.byref(da), ctypes.byref(dw), _ptr(y), y.stride(0),
                                     _ptr(workspace), workspace.numel(), _ptr(dbg[0]), _ptr(dbg[1]),

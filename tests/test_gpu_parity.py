@@ -14,7 +14,7 @@ import torch
 import oracle
 from outlier_split_mixed_amd import synth
 
-from harness import assert_rows_close, f32_bits_equal, run_layer, run_layer_mx, x_inputs
+from harness import assert_rows_close, f32_bits_equal, run_layer, run_layer_mx, sample_rows, x_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -356,9 +356,54 @@ def _sq_ws_same(sqf, acts, wts, y_ref, label, ws=None):
     on a poisoned workspace and again on the same workspace reused."""
     ws = _poisoned_workspace(sqf, wts) if ws is None else ws
     for i in range(2):
-        y_ws = sqf.sqf_dual_gemm_sq_ws(acts, wts, workspace=ws)
+        y_ws = torch.full_like(y_ref, float("nan"))  # a tile nobody wrote shows
+        y_ws = sqf.sqf_dual_gemm_sq_ws(acts, wts, y=y_ws, workspace=ws)
         torch.cuda.synchronize()
         assert torch.equal(y_ws.view(torch.int32), y_ref.view(torch.int32)), f"{label}: workspace call {i}"
+
+
+@pytest.mark.parametrize("m,k,n", [
+    (2048, 640, 2048),   # 128 tiles
+    (1000, 640, 6400),   # 200 tiles, ragged last row tile
+    (300, 1152, 8300),   # 130 tiles, ragged rows and columns
+])
+def test_sq_workspace_many_tiles(sqf, m, k, n):
+    """The workspace call over a hundred or more tiles (most of a round of
+    the GPU): the oracle's three accumulators bit for bit on sampled rows,
+    and every accumulator and Y bit-identical to the fused call's, on a
+    poisoned workspace, with Y and the dumps prefilled so that a tile nobody
+    wrote shows."""
+    lay = _ragged(m=m, k=k, n=n, n_scaled=max(1, k // 16), seed=151 + m % 97)
+    k_out = lay.k_out
+    k_low = lay.k - k_out
+    nnz = k_low // 8
+    x_cal = torch.from_numpy(lay.x_cal).cuda()
+    w = torch.from_numpy(lay.w).cuda()
+    _, mp, _, hdiag = sqf.sqf_select_channels(x_cal, w, k_out)
+    wts = sqf.sqf_pack_weights(w, mp, branch="i8", hdiag=hdiag, sq_nnz=nnz)
+    ox, ofmt, xt = x_inputs(lay, "bf16")
+    acts = sqf.alloc_acts(lay.m, k_low, k_out, low="i8", branch="i8")
+    sqf.sqf_quantize_split_act(xt, mp, acts)
+    y, al, asp, ao = sqf.sqf_dual_gemm(acts, wts, debug=True)
+    ws = _poisoned_workspace(sqf, wts)
+    for i in range(2):  # the second call reuses the workspace
+        # Y and the accumulator dumps start as NaN / -1: a tile nobody wrote shows
+        y_w = torch.full_like(y, float("nan"))
+        y_w, al_w, asp_w, ao_w = sqf.sqf_dual_gemm_sq_ws(acts, wts, y=y_w, workspace=ws, debug=True)
+        torch.cuda.synchronize()
+        assert torch.equal(al_w, al) and torch.equal(asp_w, asp) and torch.equal(ao_w, ao), f"call {i}"
+        assert torch.equal(y_w.view(torch.int32), y.view(torch.int32)), f"call {i}"
+    _sq_ws_same(sqf, acts, wts, y, f"many tiles m{m} n{n}", ws=ws)
+    o_mp = mp.cpu().numpy()
+    o_w = oracle.pack_weights_sq(lay.w, o_mp, hdiag.cpu().numpy(), nnz)
+    o_a = oracle.quantize_split_act(ox, o_mp, low="i8", branch="i8", x_fmt=ofmt)
+    rows = sample_rows(lay.m, 6, seed=m)
+    o_y, o_al, o_asp, o_ao = oracle.dual_gemm(o_a, o_w, rows=rows, debug=True)
+    assert np.array_equal(al_w.cpu().numpy()[rows].astype(np.int64), o_al)
+    assert np.array_equal(asp_w.cpu().numpy()[rows].astype(np.int64), o_asp)
+    assert np.array_equal(ao_w.cpu().numpy()[rows].astype(np.int64), o_ao)
+    assert_rows_close(y_w.cpu().numpy()[rows], o_y, f"many tiles m{m} n{n}")
+    _print("sq workspace many tiles ok", m, k, n)
 
 
 def _moe_small(experts=6, tokens=96, topk=2, hidden=512, inter=256, seed=86):
